@@ -1,0 +1,332 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized MoE expert grouped GEMM on one MI355X.
+
+One step = the whole hot path over one batch of synthetic routed rows:
+quantize activations, expert weights and output gradients, then the
+grouped GEMMs (forward, dgrad, wgrad for both expert GEMMs) and, for
+delayed scaling, the amax-history update.
+
+Default workload: Mixtral-8x7B-shaped experts (8 experts, hidden 4096,
+ffn 14336, 8192 tokens top-2 = 16384 routed rows) with delayed scaling
+(history 1024, max), e4m3 activations / weights and e5m2 gradients,
+forward + dgrad + wgrad. ``--workload`` selects the other shapes.
+
+Prints one JSON line (rank 0, N = 1). ``value`` is the GEMM FLOPs of a
+step divided by the measured step time (quantization and the delayed
+update included) in TFLOP/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+WORKLOADS = {
+    "mixtral-dl": 3,   # default: Mixtral shapes, delayed hybrid, fwd + dgrad + wgrad
+    "mixtral-tw": 2,   # Mixtral shapes, tensorwise e4m3, forward only
+    "deepseek-block": 4,
+    "llama4-mx": 5,
+}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="mixtral-dl", choices=sorted(WORKLOADS))
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-rows", type=int, default=256)
+    p.add_argument("--cpu-sample-cols", type=int, default=4096)
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# synthetic inputs (generated on the GPU with torch's seeded generator; the
+# distributions and routing follow mx_scaled_grouped_amd.workloads)
+
+def make_inputs(cid, torch, W, sets=2):
+    spec = W.SPECS[cid]
+    r = W.routing_for(cid)
+    dev = "cuda"
+    g = torch.Generator(device=dev)
+    g.manual_seed(1000 + cid)
+    R = r.rows
+    row_token = torch.from_numpy(r.row_token).to(dev)
+
+    def normal(shape, std):
+        t = torch.randn(shape, generator=g, device=dev, dtype=torch.float32)
+        if std != 1.0:
+            t.mul_(std)
+        return t.to(torch.bfloat16)
+
+    def outliers(t):
+        if cid != 5:
+            return t
+        flat = t.view(-1)
+        idx = torch.randint(0, flat.numel(), (max(1, flat.numel() // 1000),), generator=g, device=dev)
+        flat[idx] = (flat[idx].float() * 50.0).to(torch.bfloat16)
+        return t
+
+    gu_k, gu_n = spec.gemm_shape("gu")
+    dn_k, dn_n = spec.gemm_shape("dn")
+    weights = {"gu": normal((spec.experts, gu_k, gu_n), 0.02)}
+    if "dn" in spec.gemms:
+        weights["dn"] = normal((spec.experts, dn_k, dn_n), 0.02)
+    sets_out = []
+    for s in range(sets):
+        drift = 1.01 ** s if cid == 3 else 1.0
+        x = outliers(normal((spec.tokens, gu_k), drift))
+        d = {"a_gu": x.index_select(0, row_token).contiguous()}
+        del x
+        if "dn" in spec.gemms:
+            d["a_dn"] = outliers(normal((R, dn_k), drift))
+        if "dgrad" in spec.modes:
+            d["dy_gu"] = normal((R, gu_n), 2.0 ** -10)
+            if "dn" in spec.gemms:
+                d["dy_dn"] = normal((R, dn_n), 2.0 ** -10)
+        sets_out.append(d)
+    ge = torch.from_numpy(r.group_ends).to(dev)
+    return spec, r, ge, weights, sets_out
+
+
+# ---------------------------------------------------------------------------
+
+class Step:
+    """One pass of the hot path; every call's duration is recorded with HIP
+    events on the stream the kernels run on (torch's current stream)."""
+
+    def __init__(self, torch, api, spec, ge, weights, recipe):
+        self.torch, self.api, self.spec, self.ge, self.weights = torch, api, spec, ge, weights
+        self.recipe = recipe
+        self.fa, self.fg = 0, (1 if recipe == "dl" else 0)     # hybrid: e5m2 gradients
+        self.E = spec.experts
+        self.bwd = "dgrad" in spec.modes
+        self.q = {}        # reused quantized outputs
+        self.out = {}      # reused GEMM outputs
+        self.timing = None
+        if recipe == "dl":
+            # e4m3 units: a_gu, a_dn, then E per weight; e5m2 units: dy_gu, dy_dn
+            ng = len(spec.gemms)
+            self.st_f = api.DelayedState.create(ng + ng * self.E, 0, 1024)
+            self.st_g = api.DelayedState.create(ng, 1, 1024)
+        self.flops = {}
+        self.bytes = {}
+
+    def _t(self, name, fn):
+        if self.timing is None:
+            return fn()
+        e0 = self.torch.cuda.Event(enable_timing=True)
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e0.record()
+        r = fn()
+        e1.record()
+        self.timing.append((name, e0, e1))
+        return r
+
+    def run(self, data, timing=None):
+        api, spec, r = self.api, self.spec, self.recipe
+        self.timing = timing
+        bwd = self.bwd
+        for gi, which in enumerate(spec.gemms):
+            K, N = spec.gemm_shape(which)
+            a, w = data["a_" + which], self.weights[which]
+            kw = {}
+            if r == "dl":
+                kw = dict(state=self.st_f, unit=gi)
+            qa = self._t(f"quant_a_{which}", lambda: api.quantize_act(
+                a, r, self.fa, self.ge, rowwise=True, colwise=bwd, out=self.q.get("a_" + which), **kw))
+            self.q["a_" + which] = qa
+            kw = {}
+            if r == "dl":
+                kw = dict(state=self.st_f, unit=len(spec.gemms) + gi * self.E)
+            qw = self._t(f"quant_w_{which}", lambda: api.quantize_weight(
+                w, r, 0, kmajor=True, nmajor=bwd, out=self.q.get("w_" + which), **kw))
+            self.q["w_" + which] = qw
+            self.out["y_" + which] = self._t(f"gemm_fwd_{which}", lambda: api.grouped_mm_fwd(
+                qa, qw, self.ge, out=self.out.get("y_" + which)))
+            if bwd:
+                dy = data["dy_" + which]
+                kw = dict(state=self.st_g, unit=gi) if r == "dl" else {}
+                qd = self._t(f"quant_dy_{which}", lambda: api.quantize_act(
+                    dy, r, self.fg, self.ge, rowwise=True, colwise=True, out=self.q.get("dy_" + which), **kw))
+                self.q["dy_" + which] = qd
+                self.out["da_" + which] = self._t(f"gemm_dgrad_{which}", lambda: api.grouped_mm_dgrad(
+                    qd, qw, self.ge, out=self.out.get("da_" + which)))
+                self.out["dw_" + which] = self._t(f"gemm_wgrad_{which}", lambda: api.grouped_mm_wgrad(
+                    qa, qd, self.ge, out=self.out.get("dw_" + which)))
+        if r == "dl":
+            self._t("delayed_update", lambda: (self.st_f.update(), self.st_g.update()))
+        self.timing = None
+
+    def work(self, R):
+        """Algorithmic GEMM FLOPs and quantization bytes per call name."""
+        spec, r = self.spec, self.recipe
+        flops, byts = {}, {}
+        per_layout = {"tw": 1.0, "dl": 1.0, "block": 1.0 + 4 / 128, "mx": 1.0 + 1 / 32}[r]
+        read = {"tw": 4.0, "dl": 2.0, "block": 2.0, "mx": 2.0}[r]   # tw reads twice (amax pass)
+        w_layout = {"block": 1.0 + 4 / 16384}.get(r, per_layout)
+        for which in spec.gemms:
+            K, N = spec.gemm_shape(which)
+            f = 2.0 * R * K * N
+            flops[f"gemm_fwd_{which}"] = f
+            nl = 2 if self.bwd else 1
+            byts[f"quant_a_{which}"] = R * K * (read + nl * per_layout)
+            byts[f"quant_w_{which}"] = self.E * K * N * (read + nl * w_layout)
+            if self.bwd:
+                flops[f"gemm_dgrad_{which}"] = f
+                flops[f"gemm_wgrad_{which}"] = f
+                byts[f"quant_dy_{which}"] = R * N * (read + 2 * per_layout)
+        return flops, byts
+
+
+def cpu_baseline(cid, rows, cols):
+    """The CPU oracle on a bounded sample of the same workload: one expert,
+    `rows` routed rows, the full K and the first `cols` output columns of the
+    gate/up GEMM; quantization
+    of the sampled operands plus the forward (and dgrad, wgrad) float64
+    GEMMs. Reported in TFLOP/s of the sampled GEMMs."""
+    import numpy as np
+    from oracle import quant as OQ, gemm as OG, formats as OF
+    from mx_scaled_grouped_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    spec = W.SPECS[cid]
+    r = W.routing_for(cid)
+    K, N = spec.gemm_shape("gu")
+    N = min(N, cols)
+    m = min(rows, int(r.group_sizes[0]))
+    rec = {"tw": "tw", "dl": "dl", "block": "block", "mx": "mx"}[spec.recipe]
+    a = W.normal_bf16(cid, W.T_X, (m, K))
+    w = W.normal_bf16(cid, W.T_W1, (1, K, N), std=0.02, chunk_rows=256)
+    ge = np.array([m], np.int32)
+    bwd = "dgrad" in spec.modes
+    fg = OF.E5M2 if rec == "dl" else OF.E4M3
+    dl = (np.float32(1.0), np.float32(1.0))
+    t0 = time.perf_counter()
+    qa = OQ.quantize_act(a, rec, OF.E4M3, ge, rowwise=True, colwise=bwd, dl_scale=dl)
+    qw = OQ.quantize_weight(w, rec, OF.E4M3, dl_scale=(np.ones(1, np.float32), np.ones(1, np.float32)))
+    A = OG.deq_act_rows(qa["row_codes"], qa["row_scales"], rec, OF.E4M3)
+    Y = OG.round_bf16(OG.grouped_fwd(A, OG.deq_weight(qw, rec, OF.E4M3, "k"), ge))
+    flops = 2.0 * m * K * N
+    if bwd:
+        dy = W.normal_bf16(cid, W.T_DY1, (m, N), std=2.0 ** -10)
+        qd = OQ.quantize_act(dy, rec, fg, ge, rowwise=True, colwise=True, dl_scale=dl)
+        D = OG.deq_act_rows(qd["row_codes"], qd["row_scales"], rec, fg)
+        dA = OG.round_bf16(OG.grouped_dgrad(D, OG.deq_weight(qw, rec, OF.E4M3, "n"), ge))
+        P = qa["padded_starts"]
+        At = OG.unpad_cols(OG.deq_act_cols(qa["col_codes"], qa["col_scales"], rec, OF.E4M3), P, ge)
+        Dt = OG.unpad_cols(OG.deq_act_cols(qd["col_codes"], qd["col_scales"], rec, fg), P, ge)
+        dW = OG.round_f32(OG.grouped_wgrad(At, Dt, ge, 1))
+        flops *= 3
+    dt = time.perf_counter() - t0
+    mode = "fwd+dgrad+wgrad" if bwd else "fwd"
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"expert 0 gate/up GEMM, {m} routed rows x K={K} x N={N}, {mode}, "
+                      f"oracle quantization + float64 GEMMs, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path shards by expert, "
+              "see the design notes", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from mx_scaled_grouped_amd import api, workloads as W
+
+    cid = WORKLOADS[args.workload]
+    print(f"# generating inputs for {W.SPECS[cid].name}", file=sys.stderr, flush=True)
+    spec, routing, ge, weights, sets = make_inputs(cid, torch, W)
+    R = routing.rows
+    step = Step(torch, api, spec, ge, weights, spec.recipe)
+    torch.cuda.synchronize()
+    print("# warmup", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step.run(sets[i % len(sets)])
+    torch.cuda.synchronize()
+
+    print("# timed steps", file=sys.stderr, flush=True)
+    timing = []
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e_start.record()
+    t_wall = time.perf_counter()
+    for i in range(args.steps):
+        step.run(sets[i % len(sets)], timing=timing)
+    e_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_total = e_start.elapsed_time(e_end)
+    ms_step = ms_total / args.steps
+
+    per = {}
+    for name, a, b in timing:
+        per.setdefault(name, []).append(a.elapsed_time(b))
+    flops, byts = step.work(R)
+    step_flops = sum(flops.values())
+    value = step_flops / (ms_step * 1e-3) / 1e12
+
+    gemm_ms = {k: sum(v) / len(v) for k, v in per.items() if k.startswith("gemm")}
+    quant_ms = {k: sum(v) / len(v) for k, v in per.items() if k.startswith("quant")}
+    gemm_tflops = {k: flops[k] / (gemm_ms[k] * 1e-3) / 1e12 for k in gemm_ms}
+    quant_gbs = {k: byts[k] / (quant_ms[k] * 1e-3) / 1e9 for k in quant_ms}
+    gemm_total_ms = sum(gemm_ms.values())
+    quant_total_ms = sum(quant_ms.values())
+    achieved = step_flops / (gemm_total_ms * 1e-3) / 1e12
+    quant_agg = sum(byts.values()) / (quant_total_ms * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cid, args.cpu_sample_rows, args.cpu_sample_cols)
+
+    out = {
+        "metric": "FP8 grouped-GEMM TFLOP/s fwd+bwd (% FP8 MFMA peak); quant GB/s (% HBM)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8(e4m3/e5m2) codes, fp32 accumulate, bf16/fp32 out",
+        "data": "synthetic (seeded torch generator on the GPU; routing seeded numpy)",
+        "config": {"workload": spec.name, "experts": spec.experts, "tokens": spec.tokens,
+                   "topk": spec.topk, "routed_rows": R, "hidden": spec.hidden, "ffn": spec.ffn,
+                   "recipe": spec.recipe, "modes": list(spec.modes),
+                   "group_sizes": [int(x) for x in routing.group_sizes]},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "breakdown": {
+            "gemm_ms": {k: round(v, 4) for k, v in gemm_ms.items()},
+            "gemm_tflops": {k: round(v, 1) for k, v in gemm_tflops.items()},
+            "quant_ms": {k: round(v, 4) for k, v in quant_ms.items()},
+            "quant_gbs": {k: round(v, 1) for k, v in quant_gbs.items()},
+            "quant_gbs_total": round(quant_agg, 1),
+            "quant_hbm_frac": round(quant_agg / PEAK_HBM_GBS, 4),
+            "gemm_ms_total": round(gemm_total_ms, 4),
+            "quant_ms_total": round(quant_total_ms, 4),
+            "wall_s": round(wall, 3),
+        },
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

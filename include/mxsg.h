@@ -1,0 +1,221 @@
+/*
+ * mxsg.h - C ABI of the MI355X (gfx950) quantized MoE expert grouped GEMM.
+ *
+ * What it computes. The float8 MoE training pages describe one hot path:
+ * quantize the routed-row activations, the expert weights and the output
+ * gradients to FP8 ("dynamic quant + scaled grouped mm", torchao float8 MoE
+ * training PR, Summary), then run a grouped matmul over per-expert token
+ * groups for the forward pass and both backward products (the same PR's
+ * Testing section checks outputs, input gradients and parameter gradients).
+ * Recipes: tensorwise dynamic; delayed with an amax history and the "max"
+ * algorithm (Megatron-LM FP8-vs-BF16 MoE bug report, reproduction flags);
+ * DeepSeek-style 1x128 / 128x1 / 128x128 blockwise with fp32 scales
+ * (Transformer Engine "FP8BlockQuantizer not work" issue, design note);
+ * MXFP8 with 32-element blocks and E8M0 scales (Megatron-LM single grouped
+ * weight PR, coverage table). Formats are OCP e4m3 and e5m2.
+ *
+ * Conventions for every call.
+ *  - All array pointers are DEVICE pointers of the current HIP device, owned
+ *    by the caller. The library never allocates, frees, copies between host
+ *    and device, or synchronizes. Work is enqueued on `stream` (a
+ *    hipStream_t passed as void*; NULL = the default stream) and runs in
+ *    stream order. Offsets stay on the device; no call reads them on the host.
+ *  - bf16 tensors are row-major uint16 bit patterns; FP8 codes are uint8 bit
+ *    patterns; fp32 scales are float; E8M0 scales are uint8 (2^(c-127)).
+ *  - Return value: MXSG_OK, or an error code and nothing enqueued. Argument
+ *    errors are detected on the host before any HIP call; mxsg_last_error()
+ *    then gives a message (per thread). A failed launch returns
+ *    MXSG_HIP_ERROR.
+ *  - Shapes: every feature dimension (C of a token tensor, K and N of a
+ *    weight) must be a positive multiple of 128. The token dimension M may
+ *    be any value >= 0, and groups may be empty or of any size. (The
+ *    blockwise issue's shape rule: the blocked dimension must divide by the
+ *    block; its correction: the other dimension is free.)
+ *  - Groups: `group_ends` is int32[E] of cumulative row ends, non-decreasing,
+ *    with group_ends[E-1] == M (group g = rows [group_ends[g-1],
+ *    group_ends[g]), group_ends[-1] = 0). Values outside [0, M] are clamped
+ *    on the device and a decreasing end makes that group empty, so malformed
+ *    offsets give wrong numbers but never out-of-bounds accesses.
+ *
+ * Layouts.
+ *  - Scale of a scaling unit: s = fp32(amax / fmax) (stored, the multiplier
+ *    that dequantizes), codes = sat_rne(fp32(x * inv)), inv = fp32(fmax /
+ *    amax); amax == 0 gives s = inv = 1. fmax = 448 (e4m3), 57344 (e5m2).
+ *    MX: E8M0 code k+127 with k the smallest integer such that amax <=
+ *    fmax * 2^k (clamped to [-127, 127]; 0 for amax == 0), inv = 2^-k.
+ *  - Column-wise (transposed) token layout, the wgrad operand: codes
+ *    [C, ld] where group g's tokens sit at columns [P_g, P_g + m_g),
+ *    P_0 = 0, P_{g+1} = P_g + ceil(m_g / 128) * 128, and columns
+ *    [P_g + m_g, P_{g+1}) hold code 0x00 (zero fill of partial blocks).
+ *    ld must be a multiple of 128 and >= mxsg_padded_capacity(M, E).
+ *    Columns >= P_E are not written.
+ */
+#ifndef MXSG_H
+#define MXSG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t mxsg_status;
+#define MXSG_OK 0
+#define MXSG_INVALID_ARGUMENT 1 /* null pointer, bad enum, negative size */
+#define MXSG_BAD_SHAPE 2        /* feature dim not a multiple of 128, ld too small, ... */
+#define MXSG_UNSUPPORTED 3      /* a recipe / format / mode combination not built */
+#define MXSG_HIP_ERROR 4        /* a HIP launch failed */
+
+/* recipes */
+#define MXSG_RECIPE_TENSORWISE 0 /* one unit per 2-D tensor (per expert for weights), dynamic amax */
+#define MXSG_RECIPE_DELAYED 1    /* as tensorwise, scale taken from a delayed-scaling state */
+#define MXSG_RECIPE_BLOCKWISE 2  /* tokens 1x128 rows / 128x1 columns; weights 128x128 tiles */
+#define MXSG_RECIPE_MX 3         /* 32-element blocks, E8M0 scales */
+
+/* element formats */
+#define MXSG_FMT_E4M3 0
+#define MXSG_FMT_E5M2 1
+
+/* grouped GEMM modes */
+#define MXSG_MODE_FWD 0   /* Y[M,N]    = A[M,K]  x W_g[K,N]   (bf16 out) */
+#define MXSG_MODE_DGRAD 1 /* dA[M,K]   = dY[M,N] x W_g[K,N]^T (bf16 out) */
+#define MXSG_MODE_WGRAD 2 /* dW[E,K,N] = A_g^T x dY_g         (fp32 out) */
+
+typedef void *mxsg_stream_t; /* hipStream_t */
+
+/* Static text of a status code. */
+const char *mxsg_status_str(mxsg_status s);
+/* Message of the last error returned on this thread ("" if none). */
+const char *mxsg_last_error(void);
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t mxsg_version(void);
+
+/* Columns needed by the column-wise layout of M tokens in E groups:
+ * the smallest multiple of 128 that is >= max over group sizes of P_E,
+ * i.e. 128 * ceil((M + 127 * E) / 128). Pure host function. */
+int64_t mxsg_padded_capacity(int64_t M, int32_t E);
+
+/*
+ * Quantize a token-major tensor x [M, C] (routed-row activations or output
+ * gradients), producing the row-wise operand (forward / dgrad) and/or the
+ * column-wise operand (wgrad).
+ *
+ *  recipe TENSORWISE: amax = max|x| is computed first (written to amax[0],
+ *    required), then s and inv. row_scales / col_scales (fp32[1], each
+ *    optional) receive s.
+ *  recipe DELAYED: quantizes with s = dl_scale[0], inv = dl_inv[0] (state of
+ *    mxsg_delayed_update) and max-reduces max|x| into amax[0] (required;
+ *    the caller or mxsg_delayed_update must have zeroed it). row_scales /
+ *    col_scales (optional) receive a copy of s.
+ *  recipe BLOCKWISE: row_scales fp32 [M, C/128] (1x128 units along C);
+ *    col_scales fp32 [C, ld/128] (128x1 units along the padded tokens,
+ *    restarting at each group). amax, dl_* unused.
+ *  recipe MX: row_scales uint8 [M, C/32]; col_scales uint8 [C, ld/32]; a
+ *    32-block made only of padding gets code 127.
+ *
+ *  row_codes uint8 [M, C] (NULL: no row-wise output).
+ *  col_codes uint8 [C, ld] (NULL: no column-wise output). When given, E >= 1,
+ *    group_ends and padded_starts (int32 [E+1], receives P_0..P_E) are required.
+ *  At least one of row_codes / col_codes must be non-NULL.
+ */
+mxsg_status mxsg_quantize_act(const void *x, int64_t M, int64_t C, int32_t recipe, int32_t fmt,
+                              int32_t E, const int32_t *group_ends, void *row_codes,
+                              void *row_scales, void *col_codes, void *col_scales, int64_t ld,
+                              int32_t *padded_starts, float *amax, const float *dl_scale,
+                              const float *dl_inv, mxsg_stream_t stream);
+
+/*
+ * Quantize expert weights w [E, K, N] (the single contiguous grouped weight
+ * of the Megatron-LM PR), into the forward operand (k-major codes
+ * [E, N, K], contiguous along K) and/or the dgrad operand (n-major codes
+ * [E, K, N], contiguous along N). Either code pointer may be NULL.
+ *
+ *  TENSORWISE: one unit per expert; amax fp32 [E] (required) receives
+ *    max|W_e|; scales fp32 [E] (same values for both layouts).
+ *  DELAYED: s = dl_scale[e], inv = dl_inv[e]; max|W_e| is max-reduced into
+ *    amax[e] (required, zeroed beforehand); scales fp32 [E] receive s.
+ *  BLOCKWISE: 128x128 tiles of each [K, N]; one code set in two layouts;
+ *    scales fp32 [E, K/128, N/128] (same array content for both layouts).
+ *  MX: two code sets. k-major: blocks of 32 along K, kmajor_scales uint8
+ *    [E, N, K/32]; n-major: blocks of 32 along N, nmajor_scales uint8
+ *    [E, K, N/32].
+ *  Scale pointers belonging to a non-NULL code pointer are required.
+ */
+mxsg_status mxsg_quantize_weight(const void *w, int32_t E, int64_t K, int64_t N, int32_t recipe,
+                                 int32_t fmt, void *kmajor_codes, void *kmajor_scales,
+                                 void *nmajor_codes, void *nmajor_scales, float *amax,
+                                 const float *dl_scale, const float *dl_inv,
+                                 mxsg_stream_t stream);
+
+/*
+ * Delayed-scaling update for `units` scaling units (the "max" amax algorithm
+ * with a history of length L, as in the Megatron-LM bug report's flags).
+ * State, all device arrays owned by the caller (zero-initialized history,
+ * pos, amax; scale = inv = 1 initially):
+ *   history fp32 [units, L], pos int32 [units], amax fp32 [units],
+ *   scale fp32 [units], inv fp32 [units].
+ * Per unit: history[pos] = amax; pos = (pos + 1) % L; a = max(history);
+ * if a is finite and > 0: scale = fp32(a / fmax), inv = fp32(fmax / a),
+ * otherwise both are kept; finally amax = 0 (ready for the next step).
+ * Margin is 0. fmt selects fmax.
+ */
+mxsg_status mxsg_delayed_update(float *history, int32_t *pos, float *amax, float *scale,
+                                float *inv, int32_t units, int32_t L, int32_t fmt,
+                                mxsg_stream_t stream);
+
+/*
+ * Grouped GEMM over per-expert token groups with FP8 operands and fp32
+ * accumulation. C[i, j] = sum_l A[i, l] * B[j, l]: both code operands are
+ * contiguous along the contraction index l.
+ *
+ *  FWD:   A = row-wise codes of x  [M, K] (row stride lda >= K),
+ *         B = k-major weight codes [E, N, K] (row stride ldb = K),
+ *         out = Y bf16 [M, N] (row stride N).
+ *  DGRAD: A = row-wise codes of dY [M, N] (lda >= N),
+ *         B = n-major weight codes [E, K, N] (ldb = N),
+ *         out = dA bf16 [M, K] (row stride K).
+ *  WGRAD: A = column-wise codes of x  [K, lda], B = column-wise codes of dY
+ *         [N, ldb] (both in the padded layout of the same groups),
+ *         padded_starts int32 [E+1] from mxsg_quantize_act,
+ *         out = dW fp32 [E, K, N]; accumulate != 0 adds into out.
+ *
+ *  Scales, by recipe (each operand's scales come from its quantize call):
+ *   TENSORWISE / DELAYED: a_scales fp32 [1]; b_scales fp32 [E] for weights
+ *     (FWD / DGRAD) or fp32 [1] (WGRAD). out = acc * sA * sB.
+ *   BLOCKWISE: FWD a_scales [M, K/128], b_scales [E, K/128, N/128];
+ *     DGRAD a_scales [M, N/128], same b_scales; WGRAD a_scales [K, lda/128],
+ *     b_scales [N, ldb/128]. Partial sums of each 128-long contraction block
+ *     are scaled by sA * sB and accumulated in fp32.
+ *   MX: uint8 E8M0 scales with one byte per 32 contraction elements:
+ *     FWD a [M, K/32], b [E, N, K/32]; DGRAD a [M, N/32], b [E, K, N/32];
+ *     WGRAD a [K, lda/32], b [N, ldb/32]; applied inside the MFMA.
+ *  fmt_a / fmt_b: element formats of A and B (e4m3 x e4m3, e5m2 x e4m3 and
+ *  e4m3 x e5m2 are supported; hybrid training uses e5m2 gradients).
+ *
+ *  Rows of FWD / DGRAD outputs belong to exactly one group and are all
+ *  written. WGRAD: an empty group's dW_g is written with zeros (left
+ *  unchanged when accumulating).
+ */
+mxsg_status mxsg_grouped_mm(int32_t mode, int32_t recipe, int32_t fmt_a, int32_t fmt_b, int32_t E,
+                            int64_t M, int64_t K, int64_t N, const int32_t *group_ends,
+                            const int32_t *padded_starts, const void *a_codes,
+                            const void *a_scales, int64_t lda, const void *b_codes,
+                            const void *b_scales, int64_t ldb, void *out, int32_t accumulate,
+                            mxsg_stream_t stream);
+
+/*
+ * The device FP8 cast used by every quantizer (saturating round to nearest
+ * even), applied to the n consecutive fp32 bit patterns start_bits,
+ * start_bits + 1, ... (wrapping modulo 2^32): out[i] = code(float(start_bits
+ * + i)). out uint8 [n]. NaN patterns give an unspecified code. Lets a
+ * caller check the cast exhaustively over all 2^32 inputs.
+ */
+mxsg_status mxsg_cast_sweep(uint32_t start_bits, int64_t n, int32_t fmt, void *out,
+                            mxsg_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXSG_H */

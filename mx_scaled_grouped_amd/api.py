@@ -1,0 +1,268 @@
+"""Torch-facing binding of the C ABI in include/mxsg.h.
+
+PyTorch supplies device memory and the current HIP stream; every step of
+the computation runs in the HIP kernels of libmxsg.so. Functions here
+only allocate outputs, check dtypes / devices and pass pointers.
+
+The calls follow the problem statement of the float8 MoE pages:
+``quantize(tensor, recipe)`` for routed-row activations, gradients and
+expert weights, and ``grouped_mm`` for the forward, dgrad and wgrad
+products over per-expert token groups.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+E4M3, E5M2 = 0, 1
+FMT = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
+RECIPES = {"tw": 0, "dl": 1, "block": 2, "mx": 3}
+MODE_FWD, MODE_DGRAD, MODE_WGRAD = 0, 1, 2
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("tensors must be on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+
+
+def _bits16(x: torch.Tensor) -> torch.Tensor:
+    if x.dtype == torch.bfloat16:
+        return x
+    if x.dtype in (torch.int16, torch.uint16):
+        return x
+    raise TypeError("expected bf16 (or its 16-bit bit pattern)")
+
+
+def padded_capacity(M: int, E: int) -> int:
+    """Columns of the column-wise layout for M tokens in E groups."""
+    return int(_lib.load().mxsg_padded_capacity(M, E))
+
+
+def _scale_blocks(recipe: str) -> int:
+    return {"block": 128, "mx": 32}.get(recipe, 0)
+
+
+@dataclasses.dataclass
+class DelayedState:
+    """Caller-owned delayed-scaling state for `units` scaling units of one format."""
+    history: torch.Tensor   # fp32 [units, L]
+    pos: torch.Tensor       # int32 [units]
+    amax: torch.Tensor      # fp32 [units]
+    scale: torch.Tensor     # fp32 [units]
+    inv: torch.Tensor       # fp32 [units]
+    fmt: int
+
+    @classmethod
+    def create(cls, units: int, fmt, history_len: int = 1024, device="cuda") -> "DelayedState":
+        f = torch.float32
+        return cls(torch.zeros(units, history_len, dtype=f, device=device),
+                   torch.zeros(units, dtype=torch.int32, device=device),
+                   torch.zeros(units, dtype=f, device=device),
+                   torch.ones(units, dtype=f, device=device),
+                   torch.ones(units, dtype=f, device=device), FMT[fmt])
+
+    @property
+    def units(self) -> int:
+        return self.history.shape[0]
+
+    def update(self) -> None:
+        """Push each unit's recorded amax and recompute its scale (mxsg_delayed_update)."""
+        _lib.call("mxsg_delayed_update", _ptr(self.history), _ptr(self.pos), _ptr(self.amax),
+                  _ptr(self.scale), _ptr(self.inv), self.units, self.history.shape[1], self.fmt,
+                  _stream())
+
+    def state_dict(self):
+        return {k: getattr(self, k).detach().cpu().clone() for k in ("history", "pos", "amax", "scale", "inv")}
+
+    def load_state_dict(self, d):
+        for k, v in d.items():
+            getattr(self, k).copy_(v)
+
+
+@dataclasses.dataclass
+class QuantAct:
+    recipe: str
+    fmt: int
+    M: int
+    C: int
+    row_codes: Optional[torch.Tensor] = None     # uint8 [M, C]
+    row_scales: Optional[torch.Tensor] = None
+    col_codes: Optional[torch.Tensor] = None     # uint8 [C, ld]
+    col_scales: Optional[torch.Tensor] = None
+    padded_starts: Optional[torch.Tensor] = None  # int32 [E+1]
+    amax: Optional[torch.Tensor] = None
+    ld: int = 0
+
+
+def quantize_act(x: torch.Tensor, recipe: str, fmt, group_ends: Optional[torch.Tensor] = None,
+                 rowwise: bool = True, colwise: bool = False,
+                 state: Optional[DelayedState] = None, unit: int = 0,
+                 out: Optional[QuantAct] = None) -> QuantAct:
+    """Quantize a token-major bf16 tensor [M, C] (mxsg_quantize_act).
+
+    recipe "dl" takes its scale from ``state`` unit ``unit`` and records
+    the amax there. Column-wise output needs ``group_ends`` (int32 [E]).
+    ``out`` reuses previously allocated outputs of the same shape.
+    """
+    x = _bits16(x)
+    _check_dev(x, group_ends)
+    M, C = x.shape
+    f = FMT[fmt]
+    dev = x.device
+    blk = _scale_blocks(recipe)
+    E = int(group_ends.numel()) if group_ends is not None else 0
+    q = out
+    if q is None:
+        q = QuantAct(recipe, f, M, C)
+        sdt = torch.uint8 if recipe == "mx" else torch.float32
+        if rowwise:
+            q.row_codes = torch.empty(M, C, dtype=torch.uint8, device=dev)
+            q.row_scales = (torch.empty(M, C // blk, dtype=sdt, device=dev) if blk
+                            else torch.empty(1, dtype=torch.float32, device=dev))
+        if colwise:
+            if group_ends is None:
+                raise ValueError("column-wise output needs group_ends")
+            q.ld = padded_capacity(M, E)
+            q.col_codes = torch.empty(C, q.ld, dtype=torch.uint8, device=dev)
+            q.col_scales = (torch.empty(C, q.ld // blk, dtype=sdt, device=dev) if blk
+                            else torch.empty(1, dtype=torch.float32, device=dev))
+            q.padded_starts = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        if recipe == "tw":
+            q.amax = torch.empty(1, dtype=torch.float32, device=dev)
+    amax = q.amax
+    dls = dli = None
+    if recipe == "dl":
+        if state is None:
+            raise ValueError("recipe 'dl' needs a DelayedState")
+        amax = state.amax[unit:unit + 1]
+        dls = state.scale[unit:unit + 1]
+        dli = state.inv[unit:unit + 1]
+    _lib.call("mxsg_quantize_act", _ptr(x), M, C, RECIPES[recipe], f, E, _ptr(group_ends),
+              _ptr(q.row_codes), _ptr(q.row_scales), _ptr(q.col_codes), _ptr(q.col_scales),
+              q.ld, _ptr(q.padded_starts), _ptr(amax), _ptr(dls), _ptr(dli), _stream())
+    return q
+
+
+@dataclasses.dataclass
+class QuantWeight:
+    recipe: str
+    fmt: int
+    E: int
+    K: int
+    N: int
+    kmajor_codes: Optional[torch.Tensor] = None   # uint8 [E, N, K]  (forward operand)
+    kmajor_scales: Optional[torch.Tensor] = None
+    nmajor_codes: Optional[torch.Tensor] = None   # uint8 [E, K, N]  (dgrad operand)
+    nmajor_scales: Optional[torch.Tensor] = None
+    amax: Optional[torch.Tensor] = None
+
+
+def quantize_weight(w: torch.Tensor, recipe: str, fmt, kmajor: bool = True, nmajor: bool = True,
+                    state: Optional[DelayedState] = None, unit: int = 0,
+                    out: Optional[QuantWeight] = None) -> QuantWeight:
+    """Quantize expert weights [E, K, N] (mxsg_quantize_weight)."""
+    w = _bits16(w)
+    _check_dev(w)
+    E, K, N = w.shape
+    f = FMT[fmt]
+    dev = w.device
+    q = out
+    if q is None:
+        q = QuantWeight(recipe, f, E, K, N)
+        if recipe in ("tw", "dl"):
+            ks = ns = torch.empty(E, dtype=torch.float32, device=dev)
+        elif recipe == "block":
+            ks = ns = torch.empty(E, K // 128, N // 128, dtype=torch.float32, device=dev)
+        else:
+            ks = torch.empty(E, N, K // 32, dtype=torch.uint8, device=dev)
+            ns = torch.empty(E, K, N // 32, dtype=torch.uint8, device=dev)
+        if kmajor:
+            q.kmajor_codes = torch.empty(E, N, K, dtype=torch.uint8, device=dev)
+            q.kmajor_scales = ks
+        if nmajor:
+            q.nmajor_codes = torch.empty(E, K, N, dtype=torch.uint8, device=dev)
+            q.nmajor_scales = ns
+        if recipe == "tw":
+            q.amax = torch.empty(E, dtype=torch.float32, device=dev)
+    amax = q.amax
+    dls = dli = None
+    if recipe == "dl":
+        if state is None:
+            raise ValueError("recipe 'dl' needs a DelayedState")
+        amax = state.amax[unit:unit + E]
+        dls = state.scale[unit:unit + E]
+        dli = state.inv[unit:unit + E]
+    _lib.call("mxsg_quantize_weight", _ptr(w), E, K, N, RECIPES[recipe], f,
+              _ptr(q.kmajor_codes), _ptr(q.kmajor_scales), _ptr(q.nmajor_codes),
+              _ptr(q.nmajor_scales), _ptr(amax), _ptr(dls), _ptr(dli), _stream())
+    return q
+
+
+def grouped_mm(mode: int, recipe: str, fmt_a, fmt_b, E: int, M: int, K: int, N: int,
+               group_ends: torch.Tensor, a: torch.Tensor, a_scales: torch.Tensor, lda: int,
+               b: torch.Tensor, b_scales: torch.Tensor, ldb: int,
+               padded_starts: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+               accumulate: bool = False) -> torch.Tensor:
+    """Raw grouped GEMM call (mxsg_grouped_mm); see the helpers below."""
+    _check_dev(group_ends, a, a_scales, b, b_scales, padded_starts, out)
+    dev = a.device
+    if out is None:
+        if mode == MODE_FWD:
+            out = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        elif mode == MODE_DGRAD:
+            out = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+        else:
+            out = torch.empty(E, K, N, dtype=torch.float32, device=dev)
+    _lib.call("mxsg_grouped_mm", mode, RECIPES[recipe], FMT[fmt_a], FMT[fmt_b], E, M, K, N,
+              _ptr(group_ends), _ptr(padded_starts), _ptr(a), _ptr(a_scales), lda, _ptr(b),
+              _ptr(b_scales), ldb, _ptr(out), int(bool(accumulate)), _stream())
+    return out
+
+
+def grouped_mm_fwd(qa: QuantAct, qw: QuantWeight, group_ends: torch.Tensor,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y [M, N] (bf16) = A_g @ W_g per group, from row-wise A and k-major W."""
+    return grouped_mm(MODE_FWD, qa.recipe, qa.fmt, qw.fmt, qw.E, qa.M, qw.K, qw.N, group_ends,
+                      qa.row_codes, qa.row_scales, qa.C, qw.kmajor_codes, qw.kmajor_scales, qw.K,
+                      out=out)
+
+
+def grouped_mm_dgrad(qdy: QuantAct, qw: QuantWeight, group_ends: torch.Tensor,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dA [M, K] (bf16) = dY_g @ W_g^T per group, from row-wise dY and n-major W."""
+    return grouped_mm(MODE_DGRAD, qdy.recipe, qdy.fmt, qw.fmt, qw.E, qdy.M, qw.K, qw.N, group_ends,
+                      qdy.row_codes, qdy.row_scales, qdy.C, qw.nmajor_codes, qw.nmajor_scales,
+                      qw.N, out=out)
+
+
+def grouped_mm_wgrad(qa: QuantAct, qdy: QuantAct, group_ends: torch.Tensor,
+                     out: Optional[torch.Tensor] = None, accumulate: bool = False) -> torch.Tensor:
+    """dW [E, K, N] (fp32) = A_g^T @ dY_g per group, from the column-wise operands."""
+    E = int(group_ends.numel())
+    return grouped_mm(MODE_WGRAD, qa.recipe, qa.fmt, qdy.fmt, E, qa.M, qa.C, qdy.C, group_ends,
+                      qa.col_codes, qa.col_scales, qa.ld, qdy.col_codes, qdy.col_scales, qdy.ld,
+                      padded_starts=qa.padded_starts, out=out, accumulate=accumulate)
+
+
+def cast_sweep(start_bits: int, n: int, fmt, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Codes of the fp32 bit patterns start_bits .. start_bits + n - 1 (mxsg_cast_sweep)."""
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device="cuda")
+    _lib.call("mxsg_cast_sweep", start_bits & 0xFFFFFFFF, n, FMT[fmt], _ptr(out), _stream())
+    return out

@@ -1,0 +1,150 @@
+// Device helpers shared by the quantization and GEMM kernels (gfx950 only).
+//
+// FP8 here is OCP e4m3 / e5m2, the formats the float8 MoE pages name
+// (e4m3 in the Megatron-LM single-grouped-weight PR's coverage table, hybrid
+// e4m3 / e5m2 in the Megatron-LM FP8-vs-BF16 bug report). On gfx950 the
+// v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 instructions convert to the OCP
+// formats with round-to-nearest-even; saturation is made explicit by
+// clamping to +-fmax first (for finite inputs, RNE of the clamped value
+// equals the saturating RNE of the value).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxsg {
+
+enum Recipe : int { kTensorwise = 0, kDelayed = 1, kBlockwise = 2, kMx = 3, kTile128 = 4 };
+enum Format : int { kE4M3 = 0, kE5M2 = 1 };
+enum Mode : int { kFwd = 0, kDgrad = 1, kWgrad = 2 };
+
+template <int FMT> struct Fp8;
+template <> struct Fp8<kE4M3> {
+  static constexpr float fmax = 448.0f;
+  static constexpr int emax = 8;  // 448 = 1.75 * 2^8
+};
+template <> struct Fp8<kE5M2> {
+  static constexpr float fmax = 57344.0f;
+  static constexpr int emax = 15;  // 57344 = 1.75 * 2^15
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// |bf16| bit magnitudes of the two halves; for non-negative floats the order
+// of the bit patterns is the order of the values, so max is exact.
+__device__ __forceinline__ uint32_t absmax_bits2(uint32_t w, uint32_t m) {
+  uint32_t lo = w & 0x7fffu, hi = (w >> 16) & 0x7fffu;
+  m = lo > m ? lo : m;
+  return hi > m ? hi : m;
+}
+
+__device__ __forceinline__ uint32_t absmax_bits8(uint4 v, uint32_t m) {
+  m = absmax_bits2(v.x, m);
+  m = absmax_bits2(v.y, m);
+  m = absmax_bits2(v.z, m);
+  return absmax_bits2(v.w, m);
+}
+
+// amax as float from a bf16 magnitude (exact)
+__device__ __forceinline__ float bits_to_amax(uint32_t m) { return __uint_as_float(m << 16); }
+
+// Four floats -> four FP8 codes in one dword (byte i = code of the i-th value).
+template <int FMT>
+__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
+  constexpr float m = Fp8<FMT>::fmax;
+  a = __builtin_fminf(__builtin_fmaxf(a, -m), m);
+  b = __builtin_fminf(__builtin_fmaxf(b, -m), m);
+  c = __builtin_fminf(__builtin_fmaxf(c, -m), m);
+  d = __builtin_fminf(__builtin_fmaxf(d, -m), m);
+  int r;
+  if constexpr (FMT == kE4M3) {
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  } else {
+    r = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    r = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, r, true);
+  }
+  return (uint32_t)r;
+}
+
+// 8 bf16 (one 16-byte vector) times inv -> 8 codes
+template <int FMT>
+__device__ __forceinline__ uint2 cvt8(uint4 v, float inv) {
+  uint2 r;
+  r.x = cvt4<FMT>(bf16_lo(v.x) * inv, bf16_hi(v.x) * inv, bf16_lo(v.y) * inv, bf16_hi(v.y) * inv);
+  r.y = cvt4<FMT>(bf16_lo(v.z) * inv, bf16_hi(v.z) * inv, bf16_lo(v.w) * inv, bf16_hi(v.w) * inv);
+  return r;
+}
+
+// fp32 scale pair of a unit: s = amax / fmax, inv = fmax / amax (IEEE
+// correctly rounded divisions); amax == 0 gives (1, 1).
+template <int FMT>
+__device__ __forceinline__ void scale_pair(float amax, float &s, float &inv) {
+  if (amax > 0.0f) {
+    s = __fdiv_rn(amax, Fp8<FMT>::fmax);
+    inv = __fdiv_rn(Fp8<FMT>::fmax, amax);
+  } else {
+    s = 1.0f;
+    inv = 1.0f;
+  }
+}
+
+// MX shared exponent: the smallest k with amax <= fmax * 2^k, clamped to
+// [-127, 127], from the bits of amax = f * 2^E (1 <= f < 2):
+// k = E - emax + (f > 1.75), because fmax = 1.75 * 2^emax.
+template <int FMT>
+__device__ __forceinline__ int mx_exponent(float amax) {
+  uint32_t u = __float_as_uint(amax) & 0x7fffffffu;
+  if (u == 0) return 0;
+  int eb = (int)(u >> 23);
+  uint32_t man = u & 0x7fffffu;
+  int E;
+  if (eb == 0) {  // subnormal amax: normalize the mantissa
+    int top = 31 - __clz(man);
+    E = top - 149;
+    man = (man << (23 - top)) & 0x7fffffu;
+  } else {
+    E = eb - 127;
+  }
+  int k = E - Fp8<FMT>::emax + (man > 0x600000u ? 1 : 0);
+  return k < -127 ? -127 : (k > 127 ? 127 : k);
+}
+
+// 2^-k as float (exact for k in [-127, 127]; 2^-127 is subnormal)
+__device__ __forceinline__ float exp2_neg(int k) {
+  int e = 127 - k;
+  if (e >= 1) return __uint_as_float((uint32_t)e << 23);
+  return __uint_as_float(1u << (22 + e));  // e == 0: 2^-127
+}
+
+// wave-wide max of a uint (64 lanes)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    uint32_t t = (uint32_t)__shfl_xor((int)v, o, 64);
+    v = t > v ? t : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// bf16 bits of a float, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Clamped group bounds: rows [lo, hi) of group g from int32 cumulative ends.
+__device__ __forceinline__ void group_bounds(const int32_t *__restrict__ ends, int g, int64_t M,
+                                             int64_t &lo, int64_t &hi) {
+  int64_t a = g > 0 ? (int64_t)ends[g - 1] : 0;
+  int64_t b = (int64_t)ends[g];
+  a = a < 0 ? 0 : (a > M ? M : a);
+  b = b < 0 ? 0 : (b > M ? M : b);
+  lo = a;
+  hi = b < a ? a : b;
+}
+
+}  // namespace mxsg

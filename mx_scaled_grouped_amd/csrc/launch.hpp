@@ -1,0 +1,62 @@
+// Internal launcher interface between the C ABI (mxsg.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxsg {
+
+struct QuantActParams {
+  const uint16_t *x;
+  int64_t M, C;
+  int recipe, fmt;
+  int E;
+  const int32_t *group_ends;
+  uint8_t *row_codes;
+  void *row_scales;
+  uint8_t *col_codes;
+  void *col_scales;
+  int64_t ld;
+  int32_t *padded_starts;
+  float *amax;
+  const float *dl_scale, *dl_inv;
+};
+
+struct QuantWeightParams {
+  const uint16_t *w;
+  int E;
+  int64_t K, N;
+  int recipe, fmt;
+  uint8_t *kmajor_codes;
+  void *kmajor_scales;
+  uint8_t *nmajor_codes;
+  void *nmajor_scales;
+  float *amax;
+  const float *dl_scale, *dl_inv;
+};
+
+struct GemmParams {
+  int mode, recipe, fmt_a, fmt_b;
+  int E;
+  int64_t M, K, N;
+  const int32_t *group_ends;
+  const int32_t *padded_starts;
+  const uint8_t *a;
+  const void *a_scales;
+  int64_t lda;
+  const uint8_t *b;
+  const void *b_scales;
+  int64_t ldb;
+  void *out;
+  int accumulate;
+};
+
+hipError_t launch_zero(float *p, int n, hipStream_t st);
+hipError_t launch_quantize_act(const QuantActParams &p, hipStream_t st);
+hipError_t launch_quantize_weight(const QuantWeightParams &p, hipStream_t st);
+hipError_t launch_delayed_update(float *hist, int32_t *pos, float *amax, float *scale, float *inv,
+                                 int units, int L, int fmt, hipStream_t st);
+hipError_t launch_cast_sweep(uint32_t start, int64_t n, int fmt, uint8_t *out, hipStream_t st);
+hipError_t launch_grouped_mm(const GemmParams &p, hipStream_t st);
+
+}  // namespace mxsg

@@ -1,0 +1,241 @@
+// C ABI of the quantized MoE expert grouped GEMM: host-side validation and
+// dispatch to the gfx950 kernels. Declarations and contracts: include/mxsg.h.
+//
+// Every argument check happens here, before any HIP call, so a malformed
+// call returns an error code and enqueues nothing. The library keeps no
+// mutable global state besides the per-thread error message.
+#include "mxsg.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mxsg_status fail(mxsg_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+mxsg_status from_hip(hipError_t e, const char *what) {
+  if (e == hipSuccess) {
+    g_err[0] = 0;
+    return MXSG_OK;
+  }
+  return fail(MXSG_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool recipe_ok(int32_t r) { return r >= MXSG_RECIPE_TENSORWISE && r <= MXSG_RECIPE_MX; }
+bool fmt_ok(int32_t f) { return f == MXSG_FMT_E4M3 || f == MXSG_FMT_E5M2; }
+
+#define REQUIRE(cond, code, ...) \
+  do {                           \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char *mxsg_status_str(mxsg_status s) {
+  switch (s) {
+    case MXSG_OK: return "ok";
+    case MXSG_INVALID_ARGUMENT: return "invalid argument";
+    case MXSG_BAD_SHAPE: return "bad shape";
+    case MXSG_UNSUPPORTED: return "unsupported";
+    case MXSG_HIP_ERROR: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char *mxsg_last_error(void) { return g_err; }
+
+int32_t mxsg_version(void) { return 100; }  // 0.1.0
+
+int64_t mxsg_padded_capacity(int64_t M, int32_t E) {
+  if (M < 0 || E < 0) return -1;
+  return ((M + 127 * (int64_t)E + 127) / 128) * 128;
+}
+
+mxsg_status mxsg_quantize_act(const void *x, int64_t M, int64_t C, int32_t recipe, int32_t fmt,
+                              int32_t E, const int32_t *group_ends, void *row_codes,
+                              void *row_scales, void *col_codes, void *col_scales, int64_t ld,
+                              int32_t *padded_starts, float *amax, const float *dl_scale,
+                              const float *dl_inv, mxsg_stream_t stream) {
+  REQUIRE(recipe_ok(recipe), MXSG_INVALID_ARGUMENT, "quantize_act: unknown recipe %d", recipe);
+  REQUIRE(fmt_ok(fmt), MXSG_INVALID_ARGUMENT, "quantize_act: unknown format %d", fmt);
+  REQUIRE(M >= 0 && C > 0, MXSG_INVALID_ARGUMENT, "quantize_act: M=%lld C=%lld", (long long)M,
+          (long long)C);
+  REQUIRE(C % 128 == 0, MXSG_BAD_SHAPE, "quantize_act: C=%lld is not a multiple of 128",
+          (long long)C);
+  REQUIRE(M <= ((int64_t)1 << 31) - 1, MXSG_BAD_SHAPE, "quantize_act: M too large");
+  REQUIRE(row_codes || col_codes, MXSG_INVALID_ARGUMENT, "quantize_act: no output requested");
+  REQUIRE(M == 0 || x, MXSG_INVALID_ARGUMENT, "quantize_act: x is NULL");
+  const bool scaled_unit = recipe == MXSG_RECIPE_BLOCKWISE || recipe == MXSG_RECIPE_MX;
+  if (row_codes && scaled_unit)
+    REQUIRE(row_scales, MXSG_INVALID_ARGUMENT, "quantize_act: row_scales is NULL");
+  if (col_codes) {
+    REQUIRE(E >= 1, MXSG_INVALID_ARGUMENT, "quantize_act: column-wise output needs E >= 1");
+    REQUIRE(group_ends && padded_starts, MXSG_INVALID_ARGUMENT,
+            "quantize_act: column-wise output needs group_ends and padded_starts");
+    REQUIRE(ld % 128 == 0 && ld >= mxsg_padded_capacity(M, E), MXSG_BAD_SHAPE,
+            "quantize_act: ld=%lld must be a multiple of 128 and >= %lld", (long long)ld,
+            (long long)mxsg_padded_capacity(M, E));
+    if (scaled_unit)
+      REQUIRE(col_scales, MXSG_INVALID_ARGUMENT, "quantize_act: col_scales is NULL");
+  }
+  if (recipe == MXSG_RECIPE_TENSORWISE || recipe == MXSG_RECIPE_DELAYED)
+    REQUIRE(amax, MXSG_INVALID_ARGUMENT, "quantize_act: amax is NULL");
+  if (recipe == MXSG_RECIPE_DELAYED)
+    REQUIRE(dl_scale && dl_inv, MXSG_INVALID_ARGUMENT, "quantize_act: dl_scale/dl_inv NULL");
+
+  mxsg::QuantActParams p{};
+  p.x = static_cast<const uint16_t *>(x);
+  p.M = M;
+  p.C = C;
+  p.recipe = recipe;
+  p.fmt = fmt;
+  p.E = col_codes ? E : 0;
+  p.group_ends = group_ends;
+  p.row_codes = static_cast<uint8_t *>(row_codes);
+  p.row_scales = row_scales;
+  p.col_codes = static_cast<uint8_t *>(col_codes);
+  p.col_scales = col_scales;
+  p.ld = ld;
+  p.padded_starts = padded_starts;
+  p.amax = amax;
+  p.dl_scale = dl_scale;
+  p.dl_inv = dl_inv;
+  return from_hip(mxsg::launch_quantize_act(p, static_cast<hipStream_t>(stream)), "quantize_act");
+}
+
+mxsg_status mxsg_quantize_weight(const void *w, int32_t E, int64_t K, int64_t N, int32_t recipe,
+                                 int32_t fmt, void *kmajor_codes, void *kmajor_scales,
+                                 void *nmajor_codes, void *nmajor_scales, float *amax,
+                                 const float *dl_scale, const float *dl_inv,
+                                 mxsg_stream_t stream) {
+  REQUIRE(recipe_ok(recipe), MXSG_INVALID_ARGUMENT, "quantize_weight: unknown recipe %d", recipe);
+  REQUIRE(fmt_ok(fmt), MXSG_INVALID_ARGUMENT, "quantize_weight: unknown format %d", fmt);
+  REQUIRE(E >= 1 && K > 0 && N > 0, MXSG_INVALID_ARGUMENT, "quantize_weight: E=%d K=%lld N=%lld",
+          E, (long long)K, (long long)N);
+  REQUIRE(K % 128 == 0 && N % 128 == 0, MXSG_BAD_SHAPE,
+          "quantize_weight: K=%lld and N=%lld must be multiples of 128", (long long)K, (long long)N);
+  REQUIRE(E <= 65535 && K / 128 <= 65535, MXSG_BAD_SHAPE, "quantize_weight: too large");
+  REQUIRE(w, MXSG_INVALID_ARGUMENT, "quantize_weight: w is NULL");
+  REQUIRE(kmajor_codes || nmajor_codes, MXSG_INVALID_ARGUMENT, "quantize_weight: no output");
+  if (kmajor_codes) REQUIRE(kmajor_scales, MXSG_INVALID_ARGUMENT, "quantize_weight: kmajor_scales NULL");
+  if (nmajor_codes) REQUIRE(nmajor_scales, MXSG_INVALID_ARGUMENT, "quantize_weight: nmajor_scales NULL");
+  if (recipe == MXSG_RECIPE_TENSORWISE || recipe == MXSG_RECIPE_DELAYED)
+    REQUIRE(amax, MXSG_INVALID_ARGUMENT, "quantize_weight: amax is NULL");
+  if (recipe == MXSG_RECIPE_DELAYED)
+    REQUIRE(dl_scale && dl_inv, MXSG_INVALID_ARGUMENT, "quantize_weight: dl_scale/dl_inv NULL");
+
+  mxsg::QuantWeightParams p{};
+  p.w = static_cast<const uint16_t *>(w);
+  p.E = E;
+  p.K = K;
+  p.N = N;
+  p.recipe = recipe;
+  p.fmt = fmt;
+  p.kmajor_codes = static_cast<uint8_t *>(kmajor_codes);
+  p.kmajor_scales = kmajor_scales;
+  p.nmajor_codes = static_cast<uint8_t *>(nmajor_codes);
+  p.nmajor_scales = nmajor_scales;
+  p.amax = amax;
+  p.dl_scale = dl_scale;
+  p.dl_inv = dl_inv;
+  return from_hip(mxsg::launch_quantize_weight(p, static_cast<hipStream_t>(stream)),
+                  "quantize_weight");
+}
+
+mxsg_status mxsg_delayed_update(float *history, int32_t *pos, float *amax, float *scale,
+                                float *inv, int32_t units, int32_t L, int32_t fmt,
+                                mxsg_stream_t stream) {
+  REQUIRE(fmt_ok(fmt), MXSG_INVALID_ARGUMENT, "delayed_update: unknown format %d", fmt);
+  REQUIRE(units >= 0 && L >= 1, MXSG_INVALID_ARGUMENT, "delayed_update: units=%d L=%d", units, L);
+  if (units > 0)
+    REQUIRE(history && pos && amax && scale && inv, MXSG_INVALID_ARGUMENT,
+            "delayed_update: NULL state array");
+  return from_hip(mxsg::launch_delayed_update(history, pos, amax, scale, inv, units, L, fmt,
+                                              static_cast<hipStream_t>(stream)),
+                  "delayed_update");
+}
+
+mxsg_status mxsg_grouped_mm(int32_t mode, int32_t recipe, int32_t fmt_a, int32_t fmt_b, int32_t E,
+                            int64_t M, int64_t K, int64_t N, const int32_t *group_ends,
+                            const int32_t *padded_starts, const void *a_codes,
+                            const void *a_scales, int64_t lda, const void *b_codes,
+                            const void *b_scales, int64_t ldb, void *out, int32_t accumulate,
+                            mxsg_stream_t stream) {
+  REQUIRE(mode >= MXSG_MODE_FWD && mode <= MXSG_MODE_WGRAD, MXSG_INVALID_ARGUMENT,
+          "grouped_mm: unknown mode %d", mode);
+  REQUIRE(recipe_ok(recipe), MXSG_INVALID_ARGUMENT, "grouped_mm: unknown recipe %d", recipe);
+  REQUIRE(fmt_ok(fmt_a) && fmt_ok(fmt_b), MXSG_INVALID_ARGUMENT, "grouped_mm: unknown format");
+  REQUIRE(!(fmt_a == MXSG_FMT_E5M2 && fmt_b == MXSG_FMT_E5M2), MXSG_UNSUPPORTED,
+          "grouped_mm: e5m2 x e5m2 is not built");
+  REQUIRE(E >= 1 && M >= 0 && K > 0 && N > 0, MXSG_INVALID_ARGUMENT,
+          "grouped_mm: E=%d M=%lld K=%lld N=%lld", E, (long long)M, (long long)K, (long long)N);
+  REQUIRE(K % 128 == 0 && N % 128 == 0, MXSG_BAD_SHAPE,
+          "grouped_mm: K=%lld and N=%lld must be multiples of 128", (long long)K, (long long)N);
+  REQUIRE(M <= ((int64_t)1 << 31) - 1 && E <= (1 << 20), MXSG_BAD_SHAPE, "grouped_mm: too large");
+  REQUIRE(a_codes && b_codes && out && a_scales && b_scales && group_ends, MXSG_INVALID_ARGUMENT,
+          "grouped_mm: NULL operand");
+  REQUIRE(accumulate == 0 || mode == MXSG_MODE_WGRAD, MXSG_INVALID_ARGUMENT,
+          "grouped_mm: accumulate is only defined for WGRAD");
+  if (mode == MXSG_MODE_WGRAD) {
+    REQUIRE(padded_starts, MXSG_INVALID_ARGUMENT, "grouped_mm: WGRAD needs padded_starts");
+    const int64_t cap = mxsg_padded_capacity(M, E);
+    REQUIRE(lda % 128 == 0 && ldb % 128 == 0 && lda >= cap && ldb >= cap, MXSG_BAD_SHAPE,
+            "grouped_mm: WGRAD lda=%lld ldb=%lld must be multiples of 128 and >= %lld",
+            (long long)lda, (long long)ldb, (long long)cap);
+  } else {
+    const int64_t L = mode == MXSG_MODE_FWD ? K : N;
+    REQUIRE(lda >= L && lda % 16 == 0, MXSG_BAD_SHAPE,
+            "grouped_mm: lda=%lld must be >= %lld and a multiple of 16", (long long)lda,
+            (long long)L);
+    REQUIRE(ldb == L, MXSG_BAD_SHAPE, "grouped_mm: ldb=%lld must equal %lld", (long long)ldb,
+            (long long)L);
+  }
+  mxsg::GemmParams p{};
+  p.mode = mode;
+  p.recipe = recipe;
+  p.fmt_a = fmt_a;
+  p.fmt_b = fmt_b;
+  p.E = E;
+  p.M = M;
+  p.K = K;
+  p.N = N;
+  p.group_ends = group_ends;
+  p.padded_starts = padded_starts;
+  p.a = static_cast<const uint8_t *>(a_codes);
+  p.a_scales = a_scales;
+  p.lda = lda;
+  p.b = static_cast<const uint8_t *>(b_codes);
+  p.b_scales = b_scales;
+  p.ldb = ldb;
+  p.out = out;
+  p.accumulate = accumulate;
+  return from_hip(mxsg::launch_grouped_mm(p, static_cast<hipStream_t>(stream)), "grouped_mm");
+}
+
+mxsg_status mxsg_cast_sweep(uint32_t start_bits, int64_t n, int32_t fmt, void *out,
+                            mxsg_stream_t stream) {
+  REQUIRE(fmt_ok(fmt), MXSG_INVALID_ARGUMENT, "cast_sweep: unknown format %d", fmt);
+  REQUIRE(n >= 0 && n <= ((int64_t)1 << 32), MXSG_INVALID_ARGUMENT, "cast_sweep: n=%lld",
+          (long long)n);
+  REQUIRE(n == 0 || out, MXSG_INVALID_ARGUMENT, "cast_sweep: out is NULL");
+  return from_hip(mxsg::launch_cast_sweep(start_bits, n, fmt, static_cast<uint8_t *>(out),
+                                          static_cast<hipStream_t>(stream)),
+                  "cast_sweep");
+}
+
+}  // extern "C"

@@ -1,0 +1,546 @@
+// Quantization kernels: amax reduction, scale computation, saturating RNE
+// cast to OCP e4m3 / e5m2, and the LDS-staged transposed (column-wise)
+// variant for wgrad, for the tensorwise, delayed, blockwise (1x128, 128x1,
+// 128x128) and MX (32-element, E8M0) recipes.
+//
+// Design (gfx950): HBM-bound, so each element is read once per pass with
+// 16-byte vector loads and each code written once with coalesced stores.
+// A 256-thread workgroup owns a 128 x 128 tile of the input (128 rows of
+// 128 features). Row-wise units (1x128, 1x32) are reduced across the 16 (or
+// 4) lanes that hold one row; the tile is staged in LDS and re-read by
+// columns for the column-wise units (128x1, 32x1), whose codes are written
+// through an LDS code tile as 128-byte rows of the transposed output. This
+// is the "128x1 block scaling and transpose in shared memory" of the
+// Transformer Engine blockwise issue's design note, with the partial-block
+// zero fill it describes: a tile that runs past a group's last token reads
+// zeros there, so padding never raises an amax and its codes are 0x00.
+//
+// Column-wise tiles are laid out in padded token space: group g owns padded
+// columns [P_g, P_{g+1}), P_{g+1} = P_g + ceil(m_g/128)*128, so every
+// 128-column tile lies inside one group and a 128x1 unit is one tile column.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace mxsg {
+
+constexpr int QT = 128;       // tile rows (tokens or K) and columns (features)
+constexpr int QTHREADS = 256;
+constexpr int CODE_LD = 144;  // LDS row stride (bytes) of the transposed code tile
+
+// ---------------------------------------------------------------------------
+// small kernels
+
+__global__ void zero_f32_kernel(float *__restrict__ p, int n) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
+// amax of `units` contiguous units of `unit_elems` bf16 each (unit_elems % 8
+// == 0); the result is max-reduced into amax_bits[u] (fp32 bit pattern; the
+// slot must start at 0).
+__global__ __launch_bounds__(256) void amax_kernel(const uint16_t *__restrict__ x,
+                                                   int64_t unit_elems,
+                                                   uint32_t *__restrict__ amax_bits) {
+  const int u = blockIdx.y;
+  const uint4 *p = reinterpret_cast<const uint4 *>(x + (int64_t)u * unit_elems);
+  const int64_t nvec = unit_elems / 8;
+  uint32_t m = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    m = absmax_bits8(p[i], m);
+  }
+  m = wave_max_u32(m);
+  __shared__ uint32_t red[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = umax(umax(red[0], red[1]), umax(red[2], red[3]));
+    if (m) atomicMax(amax_bits + u, m << 16);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// the 128x128 tile quantizer
+
+struct TileArgs {
+  const uint16_t *x;      // [batch][rows, C]
+  int64_t rows;           // M (tokens) or K (weights)
+  int64_t C;              // features
+  int32_t E;              // groups (column-wise token layout); 0 = one group of all rows
+  const int32_t *ends;    // [E]
+  uint8_t *row_codes;     // [batch][rows, C]
+  void *row_scales;
+  uint8_t *col_codes;     // [batch][C, ld]
+  void *col_scales;
+  int64_t ld;             // column-wise row stride (bytes)
+  int32_t *padded_out;    // [E+1] or null
+  float *amax;            // [batch]: TW read (computed before), DL max-reduced into
+  const float *dl_scale;  // [batch]
+  const float *dl_inv;    // [batch]
+  int64_t x_bstride, row_bstride, col_bstride;       // per batch element (elements / bytes)
+  int64_t rs_bstride, cs_bstride;                    // scale strides per batch element
+};
+
+// Padded start of the tile and its source rows. Returns false if the tile is
+// past the last group. Uses LDS `scan` (>= 65 ints).
+__device__ bool locate_padded_tile(const TileArgs &a, int64_t p0, int64_t &src0, int &nvalid,
+                                   int32_t *scan) {
+  // P_g prefix over groups, 64 groups per pass on wave 0, broadcast via LDS
+  const int lane = threadIdx.x & 63;
+  __shared__ int64_t s_src0;
+  __shared__ int s_nvalid, s_found;
+  if (threadIdx.x == 0) s_found = 0;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    int64_t base = 0;  // P of the first group of this pass
+    for (int g0 = 0; g0 < a.E; g0 += 64) {
+      const int g = g0 + lane;
+      int64_t lo = 0, hi = 0;
+      if (g < a.E) group_bounds(a.ends, g, a.rows, lo, hi);
+      const int64_t m = hi - lo;
+      const int64_t padm = ((m + QT - 1) / QT) * QT;
+      // inclusive scan of padm over the wave
+      int64_t incl = padm;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        int64_t t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+      }
+      const int64_t start = base + incl - padm;
+      if (g < a.E && p0 >= start && p0 < start + padm) {
+        s_src0 = lo + (p0 - start);
+        int64_t nv = m - (p0 - start);
+        s_nvalid = (int)(nv > QT ? QT : nv);
+        s_found = 1;
+      }
+      if (a.padded_out && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && g < a.E) {
+        a.padded_out[g + 1] = (int32_t)(start + padm);
+        if (g == 0) a.padded_out[0] = 0;
+      }
+      base += __shfl(incl, 63, 64);
+    }
+  }
+  __syncthreads();
+  src0 = s_src0;
+  nvalid = s_nvalid;
+  return s_found != 0;
+}
+
+template <int RECIPE, int FMT, bool ROW, bool COL>
+__global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[QT * QT];       // bf16, row stride 256 B
+  __shared__ __attribute__((aligned(16))) uint8_t ctile[QT * CODE_LD];  // codes [feature][pos]
+  __shared__ uint32_t colmax[4][QT];
+  __shared__ uint32_t red[4];
+  __shared__ int32_t scan[72];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int64_t b = blockIdx.z;
+  const int64_t c0 = (int64_t)blockIdx.y * QT;  // feature tile (grid.x walks the row tiles)
+  const uint16_t *x = a.x + b * a.x_bstride;
+
+  // the tensor scale (tensorwise / delayed) is written first, so that it is
+  // there even when no tile holds a row (an empty tensor or empty groups)
+  if ((RECIPE == kTensorwise || RECIPE == kDelayed) && blockIdx.x == 0 && blockIdx.y == 0 &&
+      t == 0) {
+    float s0 = 1.0f, i0 = 1.0f;
+    if (RECIPE == kTensorwise)
+      scale_pair<FMT>(a.amax[b], s0, i0);
+    else
+      s0 = a.dl_scale[b];
+    if (a.row_scales) reinterpret_cast<float *>(a.row_scales)[b] = s0;
+    if (a.col_scales) reinterpret_cast<float *>(a.col_scales)[b] = s0;
+  }
+
+  // which rows does this tile cover?
+  int64_t src0 = 0, p0 = 0;
+  int nvalid = 0;
+  if (COL) {
+    p0 = (int64_t)blockIdx.x * QT;
+    if (a.E > 0) {
+      if (!locate_padded_tile(a, p0, src0, nvalid, scan)) return;
+    } else {  // weights: one group of all rows, rows % 128 == 0
+      src0 = p0;
+      nvalid = 128;
+    }
+  } else {
+    src0 = (int64_t)blockIdx.x * QT;
+    int64_t nv = a.rows - src0;
+    nvalid = (int)(nv > QT ? QT : nv);
+  }
+
+  // ---- load: chunk id = u*256 + t, row = id / 16, 16-byte chunk = id % 16
+  const int cq = t & 15;   // chunk within the row (8 features)
+  const int rq = t >> 4;   // row offset within a 16-row slab
+  uint4 v[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int r = u * 16 + rq;
+    if (r < nvalid) {
+      v[u] = *reinterpret_cast<const uint4 *>(x + (src0 + r) * a.C + c0 + cq * 8);
+    } else {
+      v[u] = make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  // ---- tensor-level scale (tensorwise / delayed)
+  float t_s = 1.0f, t_inv = 1.0f;
+  if (RECIPE == kTensorwise) {
+    scale_pair<FMT>(a.amax[b], t_s, t_inv);
+  } else if (RECIPE == kDelayed) {
+    t_s = a.dl_scale[b];
+    t_inv = a.dl_inv[b];
+    uint32_t m = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m = absmax_bits8(v[u], m);
+    m = wave_max_u32(m);
+    if (lane == 0) red[wave] = m;
+  } else if (RECIPE == kTile128) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m = absmax_bits8(v[u], m);
+    m = wave_max_u32(m);
+    if (lane == 0) red[wave] = m;
+  }
+  if (RECIPE == kDelayed || RECIPE == kTile128) {
+    __syncthreads();
+    const uint32_t m = umax(umax(red[0], red[1]), umax(red[2], red[3]));
+    if (RECIPE == kDelayed) {
+      if (t == 0 && m) atomicMax(reinterpret_cast<uint32_t *>(a.amax + b), m << 16);
+    } else {
+      scale_pair<FMT>(bits_to_amax(m), t_s, t_inv);
+      if (t == 0) {
+        // 128x128 tile scale: [K/128, N/128] per expert, shared by both layouts
+        const int64_t idx = b * a.rs_bstride + (int64_t)blockIdx.x * (a.C / QT) + blockIdx.y;
+        if (a.row_scales) reinterpret_cast<float *>(a.row_scales)[idx] = t_s;
+        if (a.col_scales) reinterpret_cast<float *>(a.col_scales)[idx] = t_s;
+      }
+    }
+  }
+
+  // ---- row-wise output
+  if (ROW) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = u * 16 + rq;
+      float inv = t_inv;
+      if (RECIPE == kBlockwise) {  // 1x128: the 16 lanes holding this row
+        uint32_t m = absmax_bits8(v[u], 0);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) m = umax(m, (uint32_t)__shfl_xor((int)m, o, 64));
+        float s;
+        scale_pair<FMT>(bits_to_amax(m), s, inv);
+        if (cq == 0 && r < nvalid)
+          reinterpret_cast<float *>(a.row_scales)[b * a.rs_bstride + (src0 + r) * (a.C / QT) +
+                                                  blockIdx.y] = s;
+      } else if (RECIPE == kMx) {  // 1x32: the 4 lanes holding 32 features
+        uint32_t m = absmax_bits8(v[u], 0);
+        m = umax(m, (uint32_t)__shfl_xor((int)m, 1, 64));
+        m = umax(m, (uint32_t)__shfl_xor((int)m, 2, 64));
+        const int k = mx_exponent<FMT>(bits_to_amax(m));
+        inv = exp2_neg(k);
+        if ((cq & 3) == 0 && r < nvalid)
+          reinterpret_cast<uint8_t *>(a.row_scales)[b * a.rs_bstride + (src0 + r) * (a.C / 32) +
+                                                    (c0 / 32) + (cq >> 2)] = (uint8_t)(k + 127);
+      }
+      if (r < nvalid) {
+        const uint2 q = cvt8<FMT>(v[u], inv);
+        *reinterpret_cast<uint2 *>(a.row_codes + b * a.row_bstride + (src0 + r) * a.C + c0 +
+                                   cq * 8) = q;
+      }
+    }
+  }
+
+  if (!COL) return;
+
+  // ---- column-wise output: stage the bf16 tile in LDS
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int r = u * 16 + rq;
+    *reinterpret_cast<uint4 *>(&tile[r * QT + cq * 8]) = v[u];
+  }
+  __syncthreads();
+
+  // thread -> feature pair fp (features 2fp, 2fp+1), row quarter q (32 rows)
+  const int fp = t & 63;
+  const int q = t >> 6;
+  uint32_t w[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) w[i] = *reinterpret_cast<const uint32_t *>(&tile[(q * 32 + i) * QT + fp * 2]);
+
+  float inv0 = t_inv, inv1 = t_inv;
+  if (RECIPE == kBlockwise || RECIPE == kMx) {
+    uint32_t m0 = 0, m1 = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      m0 = umax(m0, w[i] & 0x7fffu);
+      m1 = umax(m1, (w[i] >> 16) & 0x7fffu);
+    }
+    if (RECIPE == kMx) {  // 32x1 units: one quarter of the tile column
+      const int k0 = mx_exponent<FMT>(bits_to_amax(m0));
+      const int k1 = mx_exponent<FMT>(bits_to_amax(m1));
+      inv0 = exp2_neg(k0);
+      inv1 = exp2_neg(k1);
+      uint8_t *cs = reinterpret_cast<uint8_t *>(a.col_scales) + b * a.cs_bstride;
+      const int64_t ldb = a.ld / 32;
+      cs[(c0 + 2 * fp) * ldb + p0 / 32 + q] = (uint8_t)(k0 + 127);
+      cs[(c0 + 2 * fp + 1) * ldb + p0 / 32 + q] = (uint8_t)(k1 + 127);
+    } else {  // 128x1 units: the whole tile column, reduce the 4 quarters
+      colmax[q][2 * fp] = m0;
+      colmax[q][2 * fp + 1] = m1;
+      __syncthreads();
+      m0 = umax(umax(colmax[0][2 * fp], colmax[1][2 * fp]), umax(colmax[2][2 * fp], colmax[3][2 * fp]));
+      m1 = umax(umax(colmax[0][2 * fp + 1], colmax[1][2 * fp + 1]),
+                umax(colmax[2][2 * fp + 1], colmax[3][2 * fp + 1]));
+      float s0, s1;
+      scale_pair<FMT>(bits_to_amax(m0), s0, inv0);
+      scale_pair<FMT>(bits_to_amax(m1), s1, inv1);
+      if (q == 0) {
+        float *cs = reinterpret_cast<float *>(a.col_scales) + b * a.cs_bstride;
+        const int64_t ldb = a.ld / QT;
+        cs[(c0 + 2 * fp) * ldb + p0 / QT] = s0;
+        cs[(c0 + 2 * fp + 1) * ldb + p0 / QT] = s1;
+      }
+    }
+  }
+
+  // codes of the two columns, 32 rows each -> LDS code tile [feature][pos]
+#pragma unroll
+  for (int i = 0; i < 32; i += 16) {
+    uint32_t d0[4], d1[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = i + 4 * j;
+      d0[j] = cvt4<FMT>(bf16_lo(w[r]) * inv0, bf16_lo(w[r + 1]) * inv0, bf16_lo(w[r + 2]) * inv0,
+                        bf16_lo(w[r + 3]) * inv0);
+      d1[j] = cvt4<FMT>(bf16_hi(w[r]) * inv1, bf16_hi(w[r + 1]) * inv1, bf16_hi(w[r + 2]) * inv1,
+                        bf16_hi(w[r + 3]) * inv1);
+    }
+    *reinterpret_cast<uint4 *>(&ctile[(2 * fp) * CODE_LD + q * 32 + i]) =
+        make_uint4(d0[0], d0[1], d0[2], d0[3]);
+    *reinterpret_cast<uint4 *>(&ctile[(2 * fp + 1) * CODE_LD + q * 32 + i]) =
+        make_uint4(d1[0], d1[1], d1[2], d1[3]);
+  }
+  __syncthreads();
+
+  // coalesced write-out: 128 feature rows x 128 bytes; 8 lanes per row
+  uint8_t *cc = a.col_codes + b * a.col_bstride;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int id = u * QTHREADS + t;
+    const int f = id >> 3, ch = id & 7;
+    const uint4 val = *reinterpret_cast<const uint4 *>(&ctile[f * CODE_LD + ch * 16]);
+    *reinterpret_cast<uint4 *>(cc + (c0 + f) * a.ld + p0 + ch * 16) = val;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// delayed-scaling update: one workgroup per unit
+
+template <int FMT>
+__global__ __launch_bounds__(256) void delayed_update_kernel(float *__restrict__ hist,
+                                                             int32_t *__restrict__ pos,
+                                                             float *__restrict__ amax,
+                                                             float *__restrict__ scale,
+                                                             float *__restrict__ inv, int L) {
+  const int u = blockIdx.x;
+  float *h = hist + (int64_t)u * L;
+  int p = pos[u];
+  p = p < 0 ? 0 : (p >= L ? L - 1 : p);
+  const float am = amax[u];
+  __syncthreads();  // every thread has read pos / amax before they change
+  if (threadIdx.x == 0) h[p] = am;
+  __syncthreads();
+  // max over the ring; NaN / Inf propagate as "non-finite"
+  float m = 0.0f;
+  bool bad = false;
+  for (int i = threadIdx.x; i < L; i += blockDim.x) {
+    const float hv = (i == p) ? am : h[i];
+    bad |= !(hv == hv) || hv == __builtin_inff();
+    m = hv > m ? hv : m;
+  }
+  __shared__ float red[256];
+  __shared__ int sbad[256];
+  red[threadIdx.x] = m;
+  sbad[threadIdx.x] = bad;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) {
+      red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
+      sbad[threadIdx.x] |= sbad[threadIdx.x + s];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const float a = red[0];
+    if (!sbad[0] && a > 0.0f) {
+      scale[u] = __fdiv_rn(a, Fp8<FMT>::fmax);
+      inv[u] = __fdiv_rn(Fp8<FMT>::fmax, a);
+    }
+    pos[u] = (p + 1) % L;
+    amax[u] = 0.0f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// exhaustive cast check: out[i] = code(float(start + i))
+
+template <int FMT>
+__global__ __launch_bounds__(256) void cast_sweep_kernel(uint32_t start, int64_t n,
+                                                         uint8_t *__restrict__ out) {
+  const int64_t i4 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i4 >= n) return;
+  const uint32_t s = start + (uint32_t)i4;
+  const uint32_t c = cvt4<FMT>(__uint_as_float(s), __uint_as_float(s + 1), __uint_as_float(s + 2),
+                               __uint_as_float(s + 3));
+  if (i4 + 4 <= n) {
+    *reinterpret_cast<uint32_t *>(out + i4) = c;
+  } else {
+    for (int j = 0; (int64_t)(i4 + j) < n; ++j) out[i4 + j] = (uint8_t)(c >> (8 * j));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+
+static int tiles_of(int64_t n) { return (int)((n + QT - 1) / QT); }
+
+hipError_t launch_zero(float *p, int n, hipStream_t st) {
+  zero_f32_kernel<<<(n + 255) / 256, 256, 0, st>>>(p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax(const uint16_t *x, int units, int64_t unit_elems, float *amax,
+                       hipStream_t st) {
+  hipError_t e = launch_zero(amax, units, st);
+  if (e != hipSuccess) return e;
+  if (unit_elems == 0) return hipSuccess;
+  int64_t nvec = unit_elems / 8;
+  int64_t blocks = (nvec + 256 * 8 - 1) / (256 * 8);  // ~8 vectors per thread
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  dim3 grid((unsigned)blocks, (unsigned)units);
+  amax_kernel<<<grid, 256, 0, st>>>(x, unit_elems, reinterpret_cast<uint32_t *>(amax));
+  return hipGetLastError();
+}
+
+template <int RECIPE, int FMT>
+static hipError_t tile_dispatch(const TileArgs &a, bool row, bool col, dim3 grid, hipStream_t st) {
+  if (row && col)
+    tile_quant_kernel<RECIPE, FMT, true, true><<<grid, QTHREADS, 0, st>>>(a);
+  else if (row)
+    tile_quant_kernel<RECIPE, FMT, true, false><<<grid, QTHREADS, 0, st>>>(a);
+  else
+    tile_quant_kernel<RECIPE, FMT, false, true><<<grid, QTHREADS, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t tile_by_recipe(int recipe, const TileArgs &a, bool row, bool col, dim3 grid,
+                                 hipStream_t st) {
+  switch (recipe) {
+    case kTensorwise: return tile_dispatch<kTensorwise, FMT>(a, row, col, grid, st);
+    case kDelayed: return tile_dispatch<kDelayed, FMT>(a, row, col, grid, st);
+    case kBlockwise: return tile_dispatch<kBlockwise, FMT>(a, row, col, grid, st);
+    case kMx: return tile_dispatch<kMx, FMT>(a, row, col, grid, st);
+    default: return tile_dispatch<kTile128, FMT>(a, row, col, grid, st);
+  }
+}
+
+hipError_t launch_quantize_act(const QuantActParams &p, hipStream_t st) {
+  hipError_t e;
+  if (p.recipe == kTensorwise) {
+    e = launch_amax(p.x, 1, p.M * p.C, p.amax, st);
+    if (e != hipSuccess) return e;
+  }
+  TileArgs a{};
+  a.x = p.x;
+  a.rows = p.M;
+  a.C = p.C;
+  a.E = p.E;
+  a.ends = p.group_ends;
+  a.row_codes = p.row_codes;
+  a.row_scales = p.row_scales;
+  a.col_codes = p.col_codes;
+  a.col_scales = p.col_scales;
+  a.ld = p.ld;
+  a.padded_out = p.padded_starts;
+  a.amax = p.amax;
+  a.dl_scale = p.dl_scale;
+  a.dl_inv = p.dl_inv;
+  const bool row = p.row_codes != nullptr, col = p.col_codes != nullptr;
+  // at least one tile: an empty tensor still gets its tensor scale written
+  int64_t ytiles = col ? p.ld / QT : tiles_of(p.M);
+  if (ytiles == 0) ytiles = 1;
+  dim3 grid((unsigned)ytiles, (unsigned)(p.C / QT), 1);
+  return p.fmt == kE4M3 ? tile_by_recipe<kE4M3>(p.recipe, a, row, col, grid, st)
+                        : tile_by_recipe<kE5M2>(p.recipe, a, row, col, grid, st);
+}
+
+hipError_t launch_quantize_weight(const QuantWeightParams &p, hipStream_t st) {
+  hipError_t e;
+  if (p.recipe == kTensorwise) {
+    e = launch_amax(p.w, p.E, p.K * p.N, p.amax, st);
+    if (e != hipSuccess) return e;
+  }
+  TileArgs a{};
+  a.x = p.w;
+  a.rows = p.K;
+  a.C = p.N;
+  a.E = 0;
+  a.ends = nullptr;
+  a.row_codes = p.nmajor_codes;
+  a.col_codes = p.kmajor_codes;
+  a.ld = p.K;
+  a.amax = p.amax;
+  a.dl_scale = p.dl_scale;
+  a.dl_inv = p.dl_inv;
+  a.x_bstride = p.K * p.N;
+  a.row_bstride = p.K * p.N;
+  a.col_bstride = p.K * p.N;
+  int recipe = p.recipe;
+  if (recipe == kBlockwise) {
+    recipe = kTile128;
+    a.row_scales = p.nmajor_scales;
+    a.col_scales = p.kmajor_scales;
+    a.rs_bstride = (p.K / QT) * (p.N / QT);
+    a.cs_bstride = a.rs_bstride;
+  } else if (recipe == kMx) {
+    a.row_scales = p.nmajor_scales;  // [E, K, N/32]
+    a.col_scales = p.kmajor_scales;  // [E, N, K/32]
+    a.rs_bstride = p.K * (p.N / 32);
+    a.cs_bstride = p.N * (p.K / 32);
+  } else {
+    a.row_scales = p.nmajor_scales;  // [E]
+    a.col_scales = p.kmajor_scales;
+  }
+  const bool row = p.nmajor_codes != nullptr, col = p.kmajor_codes != nullptr;
+  dim3 grid((unsigned)(p.K / QT), (unsigned)(p.N / QT), (unsigned)p.E);
+  return p.fmt == kE4M3 ? tile_by_recipe<kE4M3>(recipe, a, row, col, grid, st)
+                        : tile_by_recipe<kE5M2>(recipe, a, row, col, grid, st);
+}
+
+hipError_t launch_delayed_update(float *hist, int32_t *pos, float *amax, float *scale, float *inv,
+                                 int units, int L, int fmt, hipStream_t st) {
+  if (units == 0) return hipSuccess;
+  if (fmt == kE4M3)
+    delayed_update_kernel<kE4M3><<<units, 256, 0, st>>>(hist, pos, amax, scale, inv, L);
+  else
+    delayed_update_kernel<kE5M2><<<units, 256, 0, st>>>(hist, pos, amax, scale, inv, L);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_sweep(uint32_t start, int64_t n, int fmt, uint8_t *out, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const int64_t threads = (n + 3) / 4;
+  const int64_t blocks = (threads + 255) / 256;
+  if (fmt == kE4M3)
+    cast_sweep_kernel<kE4M3><<<(unsigned)blocks, 256, 0, st>>>(start, n, out);
+  else
+    cast_sweep_kernel<kE5M2><<<(unsigned)blocks, 256, 0, st>>>(start, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace mxsg

@@ -1,0 +1,127 @@
+"""The C ABI: every symbol include/mxsg.h declares is exported by libmxsg.so,
+and argument errors are reported on the host before any HIP call (so these
+run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mx_scaled_grouped_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxsg.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libmxsg.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxsg_[a-z_]+)\s*\(", text)))
+
+
+def test_header_matches_binding():
+    assert _declared() == sorted(_lib.SIGNATURES)
+
+
+def test_all_symbols_exported():
+    lib = _lib.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    lib = _lib.load()
+    assert lib.mxsg_status_str(0) == b"ok"
+    assert lib.mxsg_status_str(2) == b"bad shape"
+    assert lib.mxsg_status_str(99) == b"unknown status"
+    assert lib.mxsg_version() >= 100
+
+
+def test_padded_capacity():
+    lib = _lib.load()
+    for M, E in [(0, 1), (1, 1), (1024, 4), (16384, 8), (98304, 64), (5, 3)]:
+        cap = lib.mxsg_padded_capacity(M, E)
+        assert cap % 128 == 0
+        # the worst case: every group holds 1 mod 128 tokens
+        assert cap >= M + 127 * E - 127 * 0 - ((M + 127 * E) % 128)
+        assert cap >= ((M + 127 * E) // 128) * 128
+    assert lib.mxsg_padded_capacity(-1, 1) == -1
+
+
+FAKE = 0x1000  # a non-null pointer that is never dereferenced: validation fails first
+
+
+def _qact(**kw):
+    args = dict(x=FAKE, M=16, C=256, recipe=0, fmt=0, E=1, ends=FAKE, rc=FAKE, rs=FAKE, cc=None,
+                cs=None, ld=0, ps=None, amax=FAKE, dls=None, dli=None)
+    args.update(kw)
+    return _lib.status_of("mxsg_quantize_act", *args.values(), None)
+
+
+def test_quantize_act_validation():
+    assert _qact(recipe=7) == _lib.INVALID_ARGUMENT
+    assert _qact(fmt=2) == _lib.INVALID_ARGUMENT
+    assert _qact(C=200) == _lib.BAD_SHAPE                   # feature dim % 128
+    assert _qact(M=-1) == _lib.INVALID_ARGUMENT
+    assert _qact(rc=None) == _lib.INVALID_ARGUMENT          # no output at all
+    assert _qact(amax=None) == _lib.INVALID_ARGUMENT        # tensorwise needs amax
+    assert _qact(recipe=1, dls=None) == _lib.INVALID_ARGUMENT
+    assert _qact(recipe=2, rs=None) == _lib.INVALID_ARGUMENT
+    # column-wise: needs groups, padded starts and a large enough ld
+    assert _qact(cc=FAKE, cs=FAKE, E=0, ps=FAKE, ld=256) == _lib.INVALID_ARGUMENT
+    assert _qact(cc=FAKE, cs=FAKE, ps=None, ld=256) == _lib.INVALID_ARGUMENT
+    assert _qact(cc=FAKE, cs=FAKE, ps=FAKE, ld=100) == _lib.BAD_SHAPE
+    assert _qact(cc=FAKE, cs=FAKE, ps=FAKE, ld=128, M=200) == _lib.BAD_SHAPE
+    assert b"ld" in _lib.load().mxsg_last_error()
+
+
+def _qw(**kw):
+    args = dict(w=FAKE, E=2, K=256, N=256, recipe=0, fmt=0, kc=FAKE, ks=FAKE, nc=FAKE, ns=FAKE,
+                amax=FAKE, dls=None, dli=None)
+    args.update(kw)
+    return _lib.status_of("mxsg_quantize_weight", *args.values(), None)
+
+
+def test_quantize_weight_validation():
+    assert _qw(K=130) == _lib.BAD_SHAPE
+    assert _qw(N=64) == _lib.BAD_SHAPE
+    assert _qw(E=0) == _lib.INVALID_ARGUMENT
+    assert _qw(kc=None, nc=None) == _lib.INVALID_ARGUMENT
+    assert _qw(ks=None) == _lib.INVALID_ARGUMENT
+    assert _qw(recipe=3, amax=None, ns=None) == _lib.INVALID_ARGUMENT
+    assert _qw(recipe=9) == _lib.INVALID_ARGUMENT
+
+
+def _mm(**kw):
+    args = dict(mode=0, recipe=0, fa=0, fb=0, E=4, M=64, K=256, N=256, ends=FAKE, ps=None,
+                a=FAKE, sa=FAKE, lda=256, b=FAKE, sb=FAKE, ldb=256, out=FAKE, acc=0)
+    args.update(kw)
+    return _lib.status_of("mxsg_grouped_mm", *args.values(), None)
+
+
+def test_grouped_mm_validation():
+    assert _mm(mode=3) == _lib.INVALID_ARGUMENT
+    assert _mm(fa=1, fb=1) == _lib.UNSUPPORTED             # e5m2 x e5m2 not built
+    assert _mm(K=200) == _lib.BAD_SHAPE
+    assert _mm(lda=128) == _lib.BAD_SHAPE                  # lda < K
+    assert _mm(ldb=512) == _lib.BAD_SHAPE                  # ldb must equal K
+    assert _mm(out=None) == _lib.INVALID_ARGUMENT
+    assert _mm(acc=1) == _lib.INVALID_ARGUMENT             # accumulate is wgrad-only
+    assert _mm(mode=2, ps=None) == _lib.INVALID_ARGUMENT   # wgrad needs padded starts
+    assert _mm(mode=2, ps=FAKE, lda=128, ldb=128) == _lib.BAD_SHAPE  # ld below capacity
+
+
+def test_delayed_and_sweep_validation():
+    assert _lib.status_of("mxsg_delayed_update", FAKE, FAKE, FAKE, FAKE, FAKE, 2, 0, 0, None) == _lib.INVALID_ARGUMENT
+    assert _lib.status_of("mxsg_delayed_update", None, FAKE, FAKE, FAKE, FAKE, 2, 16, 0, None) == _lib.INVALID_ARGUMENT
+    assert _lib.status_of("mxsg_cast_sweep", 0, 16, 5, FAKE, None) == _lib.INVALID_ARGUMENT
+    assert _lib.status_of("mxsg_cast_sweep", 0, 16, 0, None, None) == _lib.INVALID_ARGUMENT
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(ImportError):
+        _lib.load()

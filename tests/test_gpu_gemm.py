@@ -1,0 +1,218 @@
+"""GPU parity of the grouped GEMM against the float64 oracle.
+
+The GEMM is fed operands made on the CPU (never by the GPU quantizers), so
+its parity does not depend on theirs:
+
+* exact-integer operands (|value| <= 8) with power-of-two scales: every
+  partial sum is exact in fp32, so the GPU output must equal the oracle's
+  rounded result bit for bit - this pins indexing, layouts, group
+  boundaries and scale placement for every mode, recipe and format pair;
+* oracle-quantized random data: relative Frobenius error <= 1e-3 overall
+  and per non-empty group (the tolerance of the problem statement).
+"""
+import numpy as np
+import pytest
+
+from tests.gpu_helpers import (torch, FMT_OBJ, gpu_available, to_dev_u16, to_dev, host, bf16_host_f64,
+                               assert_bits_equal)
+from oracle import quant as OQ
+from oracle import formats as OF
+from oracle import gemm as OG
+from mx_scaled_grouped_amd import workloads as W
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="no GPU")]
+
+FMT_PAIRS = [(0, 0), (1, 0), (0, 1)]
+SIZES = [0, 7, 130, 1, 300, 0, 257]
+
+
+def _api():
+    from mx_scaled_grouped_amd import api
+    return api
+
+
+def _int_codes(rng, shape, fmt):
+    v = rng.integers(-8, 9, size=shape).astype(np.float32)
+    return OF.encode_sat_rne(v, FMT_OBJ[fmt])
+
+
+def _pow2_scales(rng, shape, lo, hi):
+    return np.ldexp(np.float32(1.0), rng.integers(lo, hi + 1, size=shape)).astype(np.float32)
+
+
+def _e8m0(rng, shape, lo, hi):
+    return rng.integers(127 + lo, 127 + hi + 1, size=shape).astype(np.uint8)
+
+
+def _make_scales(rng, recipe, rows, L, per_expert=None, exact=True):
+    """Scales of a code matrix [rows, L] (contiguous along L) for a recipe."""
+    lo, hi = (-2, 2) if exact else (-6, 6)
+    if recipe == "tw":
+        return _pow2_scales(rng, (1,), -3, 3)
+    if recipe == "block":
+        return _pow2_scales(rng, (rows, L // 128), lo, hi)
+    return _e8m0(rng, (rows, L // 32), -1, 1) if exact else _e8m0(rng, (rows, L // 32), -4, 4)
+
+
+class Case:
+    """Raw operands of one grouped GEMM call plus the oracle's result."""
+
+
+def make_case(mode, recipe, fa, fb, sizes, K, N, seed, exact=True):
+    rng = np.random.default_rng(seed)
+    E = len(sizes)
+    ge = W.group_ends_from_sizes(sizes)
+    M = int(ge[-1])
+    c = Case()
+    c.mode, c.recipe, c.fa, c.fb, c.E, c.M, c.K, c.N, c.ge = mode, recipe, fa, fb, E, M, K, N, ge
+    codes = (lambda shape, f: _int_codes(rng, shape, f)) if exact else \
+        (lambda shape, f: OF.encode_sat_rne((rng.standard_normal(shape) * FMT_OBJ[f].fmax / 4).astype(np.float32), FMT_OBJ[f]))
+    if mode in (0, 1):
+        L = K if mode == 0 else N
+        J = N if mode == 0 else K
+        a = codes((M, L), fa)
+        sa = _make_scales(rng, recipe, M, L, exact=exact)
+        b = codes((E, J, L), fb)                 # [E, J, L]: k-major (fwd) / n-major (dgrad)
+        if recipe == "tw":
+            sb = _pow2_scales(rng, (E,), -3, 3)
+        elif recipe == "block":
+            lo, hi = (-2, 2) if exact else (-6, 6)
+            sb = _pow2_scales(rng, (E, K // 128, N // 128), lo, hi)
+        else:
+            sb = _e8m0(rng, (E, J, L // 32), -1, 1) if exact else _e8m0(rng, (E, J, L // 32), -4, 4)
+        c.a, c.sa, c.lda, c.b, c.sb, c.ldb = a, sa, L, b, sb, L
+        A = OG.deq_act_rows(a, sa, recipe, FMT_OBJ[fa])
+        key = "kmajor" if mode == 0 else "nmajor"
+        Wd = OG.deq_weight({key + "_codes": b, key + "_scales": sb}, recipe, FMT_OBJ[fb], "k" if mode == 0 else "n")
+        if mode == 0:
+            c.ref = OG.round_bf16(OG.grouped_fwd(A, Wd, ge))
+        else:
+            c.ref = OG.round_bf16(OG.grouped_dgrad(A, Wd, ge))
+        c.padded = None
+    else:
+        P = OQ.padded_starts(ge)
+        ld = int(_api().padded_capacity(M, E))
+        Rp = int(P[-1])
+        st = OQ.group_starts(ge)
+        mask = np.zeros(Rp, bool)
+        for g in range(E):
+            mask[P[g]:P[g] + sizes[g]] = True
+        a = np.full((K, ld), 0x7F, np.uint8)     # NaN codes past the logical extent
+        b = np.full((N, ld), 0x7F, np.uint8)
+        a[:, :Rp] = np.where(mask[None, :], codes((K, Rp), fa), 0)
+        b[:, :Rp] = np.where(mask[None, :], codes((N, Rp), fb), 0)
+        if recipe == "tw":
+            sa = _pow2_scales(rng, (1,), -3, 3)
+            sb = _pow2_scales(rng, (1,), -3, 3)
+        elif recipe == "block":
+            sa = _make_scales(rng, recipe, K, ld, exact=exact)
+            sb = _make_scales(rng, recipe, N, ld, exact=exact)
+        else:
+            sa = _make_scales(rng, recipe, K, ld, exact=exact)
+            sb = _make_scales(rng, recipe, N, ld, exact=exact)
+        c.a, c.sa, c.lda, c.b, c.sb, c.ldb = a, sa, ld, b, sb, ld
+        c.padded = P.astype(np.int32)
+        sa_l = sa if recipe == "tw" else sa[:, :Rp // (128 if recipe == "block" else 32)]
+        sb_l = sb if recipe == "tw" else sb[:, :Rp // (128 if recipe == "block" else 32)]
+        At = OG.unpad_cols(OG.deq_act_cols(a[:, :Rp], sa_l, recipe, FMT_OBJ[fa]), P, ge)
+        Dt = OG.unpad_cols(OG.deq_act_cols(b[:, :Rp], sb_l, recipe, FMT_OBJ[fb]), P, ge)
+        c.ref = OG.round_f32(OG.grouped_wgrad(At, Dt, ge, E))
+    return c
+
+
+def run_case(c, out=None, accumulate=False):
+    api = _api()
+    return api.grouped_mm(c.mode, c.recipe, c.fa, c.fb, c.E, c.M, c.K, c.N, to_dev(c.ge),
+                          to_dev(c.a), to_dev(c.sa), c.lda, to_dev(c.b), to_dev(c.sb), c.ldb,
+                          padded_starts=None if c.padded is None else to_dev(c.padded), out=out,
+                          accumulate=accumulate)
+
+
+def result_f64(c, y):
+    if c.mode == 2:
+        return host(y).astype(np.float64)
+    return bf16_host_f64(y)
+
+
+@pytest.mark.parametrize("recipe", ["tw", "block", "mx"])
+@pytest.mark.parametrize("mode", [0, 1, 2], ids=["fwd", "dgrad", "wgrad"])
+@pytest.mark.parametrize("fa,fb", FMT_PAIRS, ids=["e4m3xe4m3", "e5m2xe4m3", "e4m3xe5m2"])
+def test_exact_integer(recipe, mode, fa, fb):
+    K, N = 256, 384
+    c = make_case(mode, recipe, fa, fb, SIZES, K, N, seed=7 + mode * 10 + fa + 2 * fb)
+    print(f"gemm exact {recipe} mode={mode} fa={fa} fb={fb} M={c.M}", flush=True)
+    y = run_case(c)
+    got = result_f64(c, y)
+    bad = np.flatnonzero(got.reshape(-1) != c.ref.reshape(-1))
+    assert bad.size == 0, f"{bad.size} mismatches; first {np.unravel_index(bad[0], got.shape)}: " \
+                          f"got {got.reshape(-1)[bad[0]]} want {c.ref.reshape(-1)[bad[0]]}"
+
+
+def _check_tol(c, got, tol=1e-3):
+    ref = c.ref
+    assert OG.rel_fro(got, ref) <= tol, OG.rel_fro(got, ref)
+    st = OQ.group_starts(c.ge)
+    for g in range(c.E):
+        if c.ge[g] > st[g]:
+            if c.mode == 2:
+                e = OG.rel_fro(got[g], ref[g])
+            else:
+                e = OG.rel_fro(got[st[g]:c.ge[g]], ref[st[g]:c.ge[g]])
+            assert e <= tol, (g, e)
+
+
+@pytest.mark.parametrize("recipe", ["tw", "block", "mx"])
+@pytest.mark.parametrize("mode", [0, 1, 2], ids=["fwd", "dgrad", "wgrad"])
+def test_random_within_tolerance(recipe, mode):
+    """Full-range codes and wide scale ranges; multi-tile K (several stages,
+    odd stage counts) and a ragged N tile."""
+    K, N = 640, 640
+    sizes = [3, 0, 520, 129, 700, 1]
+    fa, fb = (1, 0) if mode == 1 else ((0, 1) if mode == 2 else (0, 0))
+    c = make_case(mode, recipe, fa, fb, sizes, K, N, seed=31 + mode, exact=False)
+    print(f"gemm random {recipe} mode={mode} M={c.M}", flush=True)
+    _check_tol(c, result_f64(c, run_case(c)))
+
+
+@pytest.mark.parametrize("recipe", ["tw", "block", "mx"])
+def test_wgrad_accumulate_and_empty_groups(recipe):
+    c = make_case(2, recipe, 0, 0, [5, 0, 140, 0], 256, 256, seed=41)
+    init = np.random.default_rng(3).standard_normal((c.E, c.K, c.N)).astype(np.float32)
+    out = to_dev(init.copy())
+    y = run_case(c, out=out, accumulate=True)
+    got = host(y).astype(np.float64)
+    want = OG.round_f32(c.ref + init.astype(np.float64))
+    # one fp32 rounding of (acc + init) on the GPU vs the oracle's single rounding
+    assert np.max(np.abs(got - want) / (np.abs(want) + 1e-30)) <= 2 ** -23
+    assert np.array_equal(got[1], init[1].astype(np.float64)) and np.array_equal(got[3], init[3].astype(np.float64))
+    # without accumulate the empty groups are written with zeros
+    out2 = to_dev(np.full((c.E, c.K, c.N), np.nan, np.float32))
+    got2 = host(run_case(c, out=out2))
+    assert np.all(got2[1] == 0) and np.all(got2[3] == 0)
+    assert np.array_equal(got2.astype(np.float64), c.ref)
+
+
+def test_poisoned_output_rows_all_written():
+    c = make_case(0, "tw", 0, 0, [0, 17, 0, 300, 2], 256, 256, seed=43)
+    out = torch.full((c.M, c.N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    got = result_f64(c, run_case(c, out=out))
+    assert np.array_equal(got, c.ref)
+
+
+def test_deterministic():
+    c = make_case(2, "block", 0, 1, [100, 0, 333], 256, 384, seed=44, exact=False)
+    y1 = host(run_case(c))
+    y2 = host(run_case(c))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+def test_many_groups_and_single_group():
+    """150 groups (the tile scan runs in passes of 64) and E = 1 (a plain GEMM)."""
+    rng = np.random.default_rng(8)
+    sizes = list(rng.integers(0, 300, size=150))
+    for mode in (0, 2):
+        c = make_case(mode, "tw", 0, 0, sizes, 128, 256, seed=45 + mode)
+        print(f"many groups mode={mode} M={c.M}", flush=True)
+        assert np.array_equal(result_f64(c, run_case(c)), c.ref)
+    c = make_case(0, "mx", 0, 0, [777], 384, 256, seed=47)
+    assert np.array_equal(result_f64(c, run_case(c)), c.ref)
