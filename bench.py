@@ -44,8 +44,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="mixtral-dl", choices=sorted(WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-rows", type=int, default=256)
-    p.add_argument("--cpu-sample-cols", type=int, default=4096)
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB (five times); "
+                        "used to scale the HBM traffic counters")
+    p.add_argument("--cpu-sample-rows", type=int, default=512)
+    p.add_argument("--cpu-sample-cols", type=int, default=28672)
     return p.parse_args()
 
 
@@ -245,6 +248,16 @@ def main():
         sys.exit(2)
     import torch
     from mx_scaled_grouped_amd import api, workloads as W
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+        return
 
     cid = WORKLOADS[args.workload]
     print(f"# generating inputs for {W.SPECS[cid].name}", file=sys.stderr, flush=True)

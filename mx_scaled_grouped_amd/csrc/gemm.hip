@@ -55,10 +55,31 @@ struct GemmArgs {
   int accumulate;
 };
 
+// Workgroup bid runs on XCD bid % 8. Logical tiles are handed to the XCDs in
+// interleaved chunks of XCHUNK consecutive ids: each XCD gets every 8th chunk
+// (balanced even when groups differ wildly in size), and the XCHUNK tiles an
+// XCD runs together are neighbours in the rasterized order (shared L2 data).
+// Ids past the last full round of 8 chunks map to themselves.
+constexpr int XCHUNK = 32;
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  const int round = 8 * XCHUNK;
+  if (bid >= (nblocks / round) * round) return bid;
   const int xcd = bid & 7, local = bid >> 3;
-  const int per = nblocks >> 3, rem = nblocks & 7;
-  return xcd * per + (xcd < rem ? xcd : rem) + local;
+  return (local / XCHUNK) * round + xcd * XCHUNK + (local % XCHUNK);
+}
+
+// Grouped rasterization: runs of GM consecutive i-tiles sweep all j-tiles,
+// so the workgroups an XCD runs at the same time (32, one per CU) cover about
+// GM x 32/GM tiles and share their A and B stage data through that XCD's L2.
+constexpr int GM = 8;
+__device__ __forceinline__ void raster(int lid, int itiles, int jtiles, int &it, int &jt) {
+  const int per = GM * jtiles;
+  const int grp = lid / per;
+  const int first = grp * GM;
+  const int gm = (itiles - first) < GM ? (itiles - first) : GM;
+  const int r = lid - grp * per;
+  it = first + r % gm;
+  jt = r / gm;
 }
 
 // FWD / DGRAD: find the group and first row of i-tile `slot` (tiles of GBM
@@ -169,9 +190,10 @@ __global__ __launch_bounds__(GTHREADS) void grouped_gemm_kernel(GemmArgs a) {
   if (MODE == kWgrad) {
     const int per_g = a.slots * a.jtiles;
     g = lid / per_g;
-    const int rem = lid - g * per_g;
-    i0 = (int64_t)(rem % a.slots) * GBM;
-    j0 = (int64_t)(rem / a.slots) * BN;
+    int it, jt;
+    raster(lid - g * per_g, a.slots, a.jtiles, it, jt);
+    i0 = (int64_t)it * GBM;
+    j0 = (int64_t)jt * BN;
     ilim = a.I;
     int64_t p_lo = a.pstarts[g], p_hi = a.pstarts[g + 1];
     const int64_t cap = a.lda < a.ldb ? a.lda : a.ldb;
@@ -180,8 +202,9 @@ __global__ __launch_bounds__(GTHREADS) void grouped_gemm_kernel(GemmArgs a) {
     l0 = p_lo;
     nsteps = (p_hi - p_lo) / GBK;
   } else {
-    const int slot = lid % a.slots;
-    j0 = (int64_t)(lid / a.slots) * BN;
+    int slot, jt;
+    raster(lid, a.slots, a.jtiles, slot, jt);
+    j0 = (int64_t)jt * BN;
     if (!locate_row_tile(a, slot, g, i0, ilim)) return;
     l0 = 0;
     nsteps = a.L / GBK;
@@ -254,11 +277,11 @@ __global__ __launch_bounds__(GTHREADS) void grouped_gemm_kernel(GemmArgs a) {
   // issue the copies of stage kt into one LDS buffer set
   auto load_stage = [&](int64_t kt, uint8_t *as, uint8_t *bs, float *sa, float *sb, uint32_t *wa,
                         uint32_t *wb) {
-    if (MX) {
+    if (MX) {  // raw words; the per-lane byte shift happens at use, so no wait here
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) wa[mi] = *reinterpret_cast<const uint32_t *>(mxa[mi] + kt * 4) >> (8 * h);
+      for (int mi = 0; mi < MI; ++mi) wa[mi] = *reinterpret_cast<const uint32_t *>(mxa[mi] + kt * 4);
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) wb[ni] = *reinterpret_cast<const uint32_t *>(mxb[ni] + kt * 4) >> (8 * h);
+      for (int ni = 0; ni < NI; ++ni) wb[ni] = *reinterpret_cast<const uint32_t *>(mxb[ni] + kt * 4);
     }
     const uint8_t *ak = abase + kt * GBK;  // uniform base + 32-bit lane offset
     const uint8_t *bk = bbase + kt * GBK;
@@ -289,12 +312,14 @@ __global__ __launch_bounds__(GTHREADS) void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
           for (int ni = 0; ni < NI; ++ni) {
             if (MX) {
+              // lane half h takes block 2s + h of the stage's four: byte 2s of word >> 8h
+              const int sa_w = (int)(wa[mi] >> (8 * h)), sb_w = (int)(wb[ni] >> (8 * h));
               if (s == 0)
                 acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    af[mi], bf[ni], acc[mi][ni], FA, FB, 0, (int)wa[mi], 0, (int)wb[ni]);
+                    af[mi], bf[ni], acc[mi][ni], FA, FB, 0, sa_w, 0, sb_w);
               else
                 acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    af[mi], bf[ni], acc[mi][ni], FA, FB, 2, (int)wa[mi], 2, (int)wb[ni]);
+                    af[mi], bf[ni], acc[mi][ni], FA, FB, 2, sa_w, 2, sb_w);
             } else {
               // unit E8M0 scales (127 = 2^0); the scaled form keeps the
               // accumulators in AGPRs
