@@ -196,6 +196,8 @@ mxsg_status mxsg_delayed_update(float *history, int32_t *pos, float *amax, float
  *  Rows of FWD / DGRAD outputs belong to exactly one group and are all
  *  written. WGRAD: an empty group's dW_g is written with zeros (left
  *  unchanged when accumulating).
+ *  Limits: lda, ldb < 2^23 (BAD_SHAPE); blockwise FWD / DGRAD contraction
+ *  (K resp. N) <= 65536 (UNSUPPORTED).
  */
 mxsg_status mxsg_grouped_mm(int32_t mode, int32_t recipe, int32_t fmt_a, int32_t fmt_b, int32_t E,
                             int64_t M, int64_t K, int64_t N, const int32_t *group_ends,

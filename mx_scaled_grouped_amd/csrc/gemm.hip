@@ -25,13 +25,17 @@
 #include "device_common.hpp"
 #include "launch.hpp"
 
+#include <type_traits>
+
 namespace mxsg {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int GBM = 256;   // tile rows (i)
-constexpr int GBK = 128;   // contraction per stage (bytes of codes)
+constexpr int GBK = 64;    // contraction per stage (bytes of codes)
+constexpr int SBLK = 128;  // blockwise scaling block along the contraction
+constexpr int SB_TAB = 512; // blockwise FWD / DGRAD: contraction blocks per tile (L <= 65536)
 constexpr int GTHREADS = 256;
 constexpr int kUnitScale = 127;  // E8M0 code of 1.0
 
@@ -121,61 +125,65 @@ __device__ bool locate_row_tile(const GemmArgs &a, int slot, int &g_out, int64_t
   return s_found != 0;
 }
 
-__device__ __forceinline__ int swz(int row, int ch) { return row * GBK + ((ch ^ ((row >> 1) & 7)) << 4); }
+// LDS stage tiles hold rows of GBK = 64 code bytes as four 16-byte chunks;
+// chunk c of row r sits at chunk c ^ ((r >> 2) & 3), so the 16 lanes of a
+// fragment read that share a bank sweep (rows r, r+4, r+8, r+12) hit
+// different banks.
+__device__ __forceinline__ int swz(int row, int ch) { return row * GBK + ((ch ^ ((row >> 2) & 3)) << 4); }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
-// lane L of the wave lands at lds + 16 * L.
+// Direct global -> LDS copies (global_load_lds_dwordx4 / _dword): lane L of
+// the wave lands at lds + 16 L (or 4 L); M0 holds the LDS byte address.
+// Issued through inline asm, so the compiler inserts no waits for them: the
+// main loop counts them itself (vmcnt) before each stage's barrier.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
 __device__ __forceinline__ void dma16(const uint8_t *src, uint8_t *lds) {
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src),
-                                   (lds_void_t *)(lds), 16, 0, 0);
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_addr(lds)) : "memory");
 }
-// 4 bytes per lane: lane L lands at lds + 4 * L.
 __device__ __forceinline__ void dma4(const void *src, void *lds) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(lds), 4, 0, 0);
+  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds_addr(lds)) : "memory");
 }
 
-// End of a stage: the stage's MFMAs must not sink below this point (they
-// would then wait for the next stage's copies), then every wave's copies
-// complete, then the workgroup synchronizes.
-__device__ __forceinline__ void wait_vm_then_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-}
-
-// MFMA 32x32x64 f8 operand of k-step s for one lane: the lane's row, and
-// (measured lane layout) bytes 0-15 = k in [16h, 16h+16) of the first
-// 32-block, bytes 16-31 = k in [32+16h, 48+16h) of the second, where h is
-// the lane's half of the wave. The scale operand of lane i + 32b covers
-// row i and 32-block b. In 16-byte LDS chunks of the 128-wide stage:
-// chunks 4s + h and 4s + 2 + h.
-__device__ __forceinline__ v8i frag(const uint8_t *buf, int row, int s, int h) {
-  const uint4 x0 = *reinterpret_cast<const uint4 *>(&buf[swz(row, 4 * s + h)]);
-  const uint4 x1 = *reinterpret_cast<const uint4 *>(&buf[swz(row, 4 * s + 2 + h)]);
+// MFMA 32x32x64 f8 operand for one lane: the lane's row, and (measured lane
+// layout) bytes 0-15 = k in [16h, 16h+16) of the first 32-block, bytes
+// 16-31 = k in [32+16h, 48+16h) of the second, h = the lane's half of the
+// wave; i.e. 16-byte chunks h and 2 + h of the 64-wide stage row. The scale
+// operand of lane i + 32b covers row i and 32-block b.
+__device__ __forceinline__ v8i frag(const uint8_t *buf, int row, int h) {
+  const uint4 x0 = *reinterpret_cast<const uint4 *>(&buf[swz(row, h)]);
+  const uint4 x1 = *reinterpret_cast<const uint4 *>(&buf[swz(row, 2 + h)]);
   return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 template <int MODE, int RECIPE, int FA, int FB, int BN>
 __global__ __launch_bounds__(GTHREADS) void grouped_gemm_kernel(GemmArgs a) {
-  constexpr int WN = BN / 2;       // wave tile width along j
-  constexpr int NI = WN / 32;      // 32-wide sub-tiles along j per wave
-  constexpr int MI = 4;            // 32-high sub-tiles along i per wave (128 rows)
-  constexpr int AQ = GBM / 8 / 4;  // 8-row groups of A per wave per stage (8)
-  constexpr int BQ = BN / 8 / 4;   // 8-row groups of B per wave per stage (8 or 4)
+  constexpr int WN = BN / 2;        // wave tile width along j
+  constexpr int NI = WN / 32;       // 32-wide sub-tiles along j per wave
+  constexpr int MI = 4;             // 32-high sub-tiles along i per wave (128 rows)
+  constexpr int AQ = GBM / 16 / 4;  // 16-row copy groups of A per wave per stage (4)
+  constexpr int BQ = BN / 16 / 4;   // of B (4 or 2)
   constexpr bool BLK = RECIPE == kBlockwise;
   constexpr bool MX = RECIPE == kMx;
+  // vector-memory instructions one wave issues per real stage (the waits count them)
+  constexpr int OPS_BASE = AQ + BQ + (BLK ? 1 : 0) + (MX ? 2 : 0);
 
-  // two stages of A and B tiles as distinct objects, so the compiler can
-  // tell the buffer being filled from the one being read (no wait between
-  // the copies of stage k+1 and the LDS reads of stage k)
-  __shared__ __attribute__((aligned(1024))) uint8_t As0[GBM * GBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t As1[GBM * GBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t Bs0[BN * GBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t Bs1[BN * GBK];
-  __shared__ __attribute__((aligned(16))) float sA0[BLK ? GBM : 4], sA1[BLK ? GBM : 4];
-  __shared__ __attribute__((aligned(16))) float sB0[BLK ? BN : 4], sB1[BLK ? BN : 4];
+  // four stage buffers of A and B as distinct objects: the compiler then
+  // knows the copies into one buffer do not alias the reads of another
+  __shared__ __attribute__((aligned(1024))) uint8_t As0[GBM * GBK], As1[GBM * GBK], As2[GBM * GBK], As3[GBM * GBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t Bs0[BN * GBK], Bs1[BN * GBK], Bs2[BN * GBK], Bs3[BN * GBK];
+  __shared__ __attribute__((aligned(16))) float sA0[BLK ? GBM : 4], sA1[BLK ? GBM : 4], sA2[BLK ? GBM : 4], sA3[BLK ? GBM : 4];
+  __shared__ __attribute__((aligned(16))) float sB0[BLK ? BN : 4], sB1[BLK ? BN : 4], sB2[BLK ? BN : 4], sB3[BLK ? BN : 4];
+  __shared__ float sbtab[BLK ? SB_TAB : 1];  // blockwise weight scales of this tile's j-block, per l-block
+  // MX: per stage buffer, the E8M0 word (4 blocks of 32) holding each tile
+  // row's two blocks of the stage, for A rows and B rows
+  __shared__ uint32_t mA0[MX ? GBM : 1], mA1[MX ? GBM : 1], mA2[MX ? GBM : 1], mA3[MX ? GBM : 1];
+  __shared__ uint32_t mB0[MX ? BN : 1], mB1[MX ? BN : 1], mB2[MX ? BN : 1], mB3[MX ? BN : 1];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -186,7 +194,8 @@ __global__ __launch_bounds__(GTHREADS) void grouped_gemm_kernel(GemmArgs a) {
   // ---- tile coordinates
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   int g = 0;
-  int64_t i0 = 0, ilim = 0, j0 = 0, l0 = 0, nsteps = 0;
+  int64_t i0 = 0, ilim = 0, j0 = 0, l0 = 0;
+  int nsteps = 0;
   if (MODE == kWgrad) {
     const int per_g = a.slots * a.jtiles;
     g = lid / per_g;
@@ -199,16 +208,17 @@ __global__ __launch_bounds__(GTHREADS) void grouped_gemm_kernel(GemmArgs a) {
     const int64_t cap = a.lda < a.ldb ? a.lda : a.ldb;
     p_lo = p_lo < 0 ? 0 : (p_lo > cap ? cap : p_lo);
     p_hi = p_hi < p_lo ? p_lo : (p_hi > cap ? cap : p_hi);
-    l0 = p_lo;
-    nsteps = (p_hi - p_lo) / GBK;
+    l0 = p_lo & ~(int64_t)127;                       // padded starts are 128-aligned
+    nsteps = (int)(((p_hi - l0) / 128) * (128 / GBK));
   } else {
     int slot, jt;
     raster(lid, a.slots, a.jtiles, slot, jt);
     j0 = (int64_t)jt * BN;
     if (!locate_row_tile(a, slot, g, i0, ilim)) return;
     l0 = 0;
-    nsteps = a.L / GBK;
+    nsteps = (int)(a.L / GBK);
   }
+  const int vsteps = (nsteps + 3) & ~3;  // stages rounded up to whole ring turns
 
   // scale-row strides: FWD / DGRAD scales are [rows, L/blk]; WGRAD scales
   // follow the padded column layout, [rows, ld/blk]
@@ -224,43 +234,45 @@ __global__ __launch_bounds__(GTHREADS) void grouped_gemm_kernel(GemmArgs a) {
   uint32_t aoff[AQ], boff[BQ];
 #pragma unroll
   for (int q = 0; q < AQ; ++q) {
-    const int row = (wave * AQ + q) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    const int row = (wave * AQ + q) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 2) & 3);
     aoff[q] = (uint32_t)((row < imax ? row : imax) * (int32_t)a.lda + c * 16);
   }
 #pragma unroll
   for (int q = 0; q < BQ; ++q) {
-    const int row = (wave * BQ + q) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    const int row = (wave * BQ + q) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 2) & 3);
     boff[q] = (uint32_t)((row < jmax ? row : jmax) * (int32_t)a.ldb + c * 16);
   }
 
-  // blockwise scale sources: one fp32 per tile row per stage (wave w copies rows 64w..64w+63)
+  // blockwise: per-row A scales (and per-row B scales for wgrad) copied per
+  // stage, wave w copying rows 64w..64w+63; the weight tile scales of the
+  // whole contraction (forward / dgrad) go to LDS once
   const float *sa_src = nullptr, *sb_src = nullptr;
+  const bool sb_wave = MODE == kWgrad && wave < BN / 64;
   if (BLK) {
     const int r = wave * 64 + lane;
-    sa_src = reinterpret_cast<const float *>(a.a_scales) + (i0 + (r < imax ? r : imax)) * (sa_row / GBK) + l0 / GBK;
-    if (MODE == kWgrad && wave < BN / 64)
-      sb_src = reinterpret_cast<const float *>(a.b_scales) + (j0 + (r < jmax ? r : jmax)) * (sb_row / GBK) + l0 / GBK;
+    sa_src = reinterpret_cast<const float *>(a.a_scales) + (i0 + (r < imax ? r : imax)) * (sa_row / SBLK) + l0 / SBLK;
+    if (sb_wave)
+      sb_src = reinterpret_cast<const float *>(a.b_scales) + (j0 + (r < jmax ? r : jmax)) * (sb_row / SBLK) + l0 / SBLK;
+    if (MODE != kWgrad) {
+      const int64_t jb = j0 / SBLK;
+      for (int lb = t; lb < nsteps / 2 && lb < SB_TAB; lb += GTHREADS)
+        sbtab[lb] = reinterpret_cast<const float *>(a.b_scales)[(int64_t)g * a.bs_gstride + lb * a.sb_l + jb * a.sb_j];
+    }
   }
+  const int ops_wave = OPS_BASE + (sb_wave ? 1 : 0);
 
-  // MX: per-lane E8M0 scale words (4 bytes = the 4 blocks of one stage)
-  const uint8_t *mxa[MI];
-  const uint8_t *mxb[NI];
+  // MX scale words: wave w copies the words of A rows 64w..64w+63 and of B
+  // rows 64w..64w+63 (B has 256 rows here)
+  const uint8_t *mxa = nullptr, *mxb = nullptr;
   if (MX) {
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      const int r = wi * 128 + mi * 32 + l32;
-      mxa[mi] = reinterpret_cast<const uint8_t *>(a.a_scales) + (i0 + (r < imax ? r : imax)) * (sa_row / 32) + l0 / 32;
-    }
-    const uint8_t *sb = reinterpret_cast<const uint8_t *>(a.b_scales) +
-                        (MODE == kWgrad ? 0 : (int64_t)g * a.bs_gstride);
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) {
-      const int r = wj * WN + ni * 32 + l32;
-      mxb[ni] = sb + (j0 + (r < jmax ? r : jmax)) * (sb_row / 32) + l0 / 32;
-    }
+    const int r = wave * 64 + lane;
+    mxa = reinterpret_cast<const uint8_t *>(a.a_scales) + (i0 + (r < imax ? r : imax)) * (sa_row / 32) + l0 / 32;
+    mxb = reinterpret_cast<const uint8_t *>(a.b_scales) + (MODE == kWgrad ? 0 : (int64_t)g * a.bs_gstride) +
+          (j0 + (r < jmax ? r : jmax)) * (sb_row / 32) + l0 / 32;
   }
+  __syncthreads();  // sbtab visible
 
   v16f acc[MI][NI];
 #pragma unroll
@@ -269,155 +281,186 @@ __global__ __launch_bounds__(GTHREADS) void grouped_gemm_kernel(GemmArgs a) {
     for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
+  v16f part[BLK ? MI : 1][BLK ? NI : 1];  // blockwise: partial sum of the current 128-block
 
-  // per-buffer MX scale words (stage in buffer X uses wX), loaded with the
-  // stage's copies so they are ready when the stage is computed
-  uint32_t wa0[MX ? MI : 1], wb0[MX ? NI : 1], wa1[MX ? MI : 1], wb1[MX ? NI : 1];
-
-  // issue the copies of stage kt into one LDS buffer set
-  auto load_stage = [&](int64_t kt, uint8_t *as, uint8_t *bs, float *sa, float *sb, uint32_t *wa,
-                        uint32_t *wb) {
-    if (MX) {  // raw words; the per-lane byte shift happens at use, so no wait here
+  // issue the copies of stage kt (or zero-fill a padding stage past nsteps)
+  auto load_stage = [&](int kt, uint8_t *as, uint8_t *bs, float *sa, float *sb, uint32_t *ma,
+                        uint32_t *mb) {
+    if (kt < nsteps) {
+      if (MX) {  // the 4-byte word holding blocks 2kt, 2kt+1 (4-byte aligned)
+        dma4(mxa + ((kt * 2) & ~3), ma + wave * 64);
+        dma4(mxb + ((kt * 2) & ~3), mb + wave * 64);
+      }
+      const uint8_t *ak = abase + kt * GBK;
+      const uint8_t *bk = bbase + kt * GBK;
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) wa[mi] = *reinterpret_cast<const uint32_t *>(mxa[mi] + kt * 4);
+      for (int q = 0; q < AQ; ++q) dma16(ak + aoff[q], as + (wave * AQ + q) * 1024);
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) wb[ni] = *reinterpret_cast<const uint32_t *>(mxb[ni] + kt * 4);
-    }
-    const uint8_t *ak = abase + kt * GBK;  // uniform base + 32-bit lane offset
-    const uint8_t *bk = bbase + kt * GBK;
-#pragma unroll
-    for (int q = 0; q < AQ; ++q) dma16(ak + aoff[q], as + (wave * AQ + q) * 1024);
-#pragma unroll
-    for (int q = 0; q < BQ; ++q) dma16(bk + boff[q], bs + (wave * BQ + q) * 1024);
-    if (BLK) {
-      dma4(sa_src + kt, sa + wave * 64);
-      if (MODE == kWgrad && wave < BN / 64) dma4(sb_src + kt, sb + wave * 64);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // issue the copies before the stage's MFMAs
-  };
-
-  // MFMAs of one stage from one LDS buffer set
-  auto compute_stage = [&](int64_t kt, const uint8_t *as, const uint8_t *bs, const float *sa_l,
-                           const float *sb_l, const uint32_t *wa, const uint32_t *wb) {
-    if (!BLK) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        v8i af[MI], bf[NI];
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi) af[mi] = frag(as, wi * 128 + mi * 32 + l32, s, h);
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) bf[ni] = frag(bs, wj * WN + ni * 32 + l32, s, h);
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni) {
-            if (MX) {
-              // lane half h takes block 2s + h of the stage's four: byte 2s of word >> 8h
-              const int sa_w = (int)(wa[mi] >> (8 * h)), sb_w = (int)(wb[ni] >> (8 * h));
-              if (s == 0)
-                acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    af[mi], bf[ni], acc[mi][ni], FA, FB, 0, sa_w, 0, sb_w);
-              else
-                acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    af[mi], bf[ni], acc[mi][ni], FA, FB, 2, sa_w, 2, sb_w);
-            } else {
-              // unit E8M0 scales (127 = 2^0); the scaled form keeps the
-              // accumulators in AGPRs
-              acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  af[mi], bf[ni], acc[mi][ni], FA, FB, 0, kUnitScale, 0, kUnitScale);
-            }
-          }
+      for (int q = 0; q < BQ; ++q) dma16(bk + boff[q], bs + (wave * BQ + q) * 1024);
+      if (BLK) {
+        dma4(sa_src + kt / 2, sa + wave * 64);
+        if (sb_wave) dma4(sb_src + kt / 2, sb + wave * 64);
       }
     } else {
-      // blockwise: a stage is one 128-long scaling block; promote its partial
-      v8i af[2][MI], bf[2][NI];
+      const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      for (int u = 0; u < GBM * GBK / 16 / GTHREADS; ++u) *reinterpret_cast<uint4 *>(as + (u * GTHREADS + t) * 16) = z;
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi) af[s][mi] = frag(as, wi * 128 + mi * 32 + l32, s, h);
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) bf[s][ni] = frag(bs, wj * WN + ni * 32 + l32, s, h);
+      for (int u = 0; u < BN * GBK / 16 / GTHREADS; ++u) *reinterpret_cast<uint4 *>(bs + (u * GTHREADS + t) * 16) = z;
+      if (BLK) {
+        sa[t] = 0.0f;
+        if (t < BN) sb[t] = 0.0f;
       }
-      float sbw = 0.0f;  // weight tile scale: one value per wave (FWD / DGRAD)
-      if (MODE != kWgrad) {
-        const int64_t jb = (j0 + wj * WN) / GBK;
-        sbw = reinterpret_cast<const float *>(a.b_scales)[(int64_t)g * a.bs_gstride + kt * a.sb_l + jb * a.sb_j];
-      }
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        float sa[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 v4 = *reinterpret_cast<const float4 *>(&sa_l[wi * 128 + mi * 32 + q * 8 + h * 4]);
-          sa[q * 4 + 0] = v4.x;
-          sa[q * 4 + 1] = v4.y;
-          sa[q * 4 + 2] = v4.z;
-          sa[q * 4 + 3] = v4.w;
-        }
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          v16f p;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) p[v] = 0.0f;
-          p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[0][mi], bf[0][ni], p, FA, FB, 0, 0, 0, 0);
-          p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[1][mi], bf[1][ni], p, FA, FB, 0, 0, 0, 0);
-          const float sbj = (MODE == kWgrad) ? sb_l[wj * WN + ni * 32 + l32] : sbw;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[mi][ni][v] += p[v] * (sa[v] * sbj);
-        }
+      if (MX) {  // unit scales for the zero stage
+        ma[t] = 0x7f7f7f7fu;
+        if (t < BN) mb[t] = 0x7f7f7f7fu;
       }
     }
+    __builtin_amdgcn_sched_barrier(0);  // the copies go out before the MFMAs that follow
   };
 
-  // an empty asm use of every accumulator: keeps a stage's MFMAs issued
-  // before the end-of-stage wait (and the accumulators in AGPRs)
-  // (the AGPR constraint exists only for the device; the host pass of this
-  // file only needs the kernel's launch stub)
+  // wait until this wave's copies of stage kt have landed (the copies of the
+  // two later stages may still be in flight), then synchronize the workgroup
+  auto stage_ready = [&](int kt) {
+    __builtin_amdgcn_sched_barrier(0);
+    const int ahead = nsteps - 1 - kt;  // real stages issued after kt (at most two)
+    if (ahead >= 2) {
+      if (ops_wave == OPS_BASE) wait_vm<2 * OPS_BASE>(); else wait_vm<2 * OPS_BASE + 2>();
+    } else if (ahead == 1) {
+      if (ops_wave == OPS_BASE) wait_vm<OPS_BASE>(); else wait_vm<OPS_BASE + 1>();
+    } else {
+      wait_vm<0>();
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // an empty asm use of every accumulator: keeps the stage's MFMAs issued
+  // before the next wait (and the accumulators in AGPRs)
   auto pin_acc = [&]() {
 #if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
-        if (BLK)
+        if (BLK) {
           asm volatile("" ::"v"(acc[mi][ni]));
-        else
+          asm volatile("" ::"a"(part[mi][ni]));
+        } else {
           asm volatile("" ::"a"(acc[mi][ni]));
+        }
       }
 #endif
   };
 
-  // ---- main loop, double buffered. The loop body is two whole stages (one
-  // per buffer) with no conditional MFMAs, which keeps the accumulators in
-  // AGPRs; an odd stage count computes its first stage before the loop.
-  int64_t kt = 0;
-  if (nsteps & 1) {
-    load_stage(0, As1, Bs1, sA1, sB1, wa1, wb1);
-    wait_vm_then_barrier();
-    if (nsteps > 1) load_stage(1, As0, Bs0, sA0, sB0, wa0, wb0);
-    compute_stage(0, As1, Bs1, sA1, sB1, wa1, wb1);
-    pin_acc();
-    wait_vm_then_barrier();
-    kt = 1;
-  } else if (nsteps > 0) {
-    load_stage(0, As0, Bs0, sA0, sB0, wa0, wb0);
-    wait_vm_then_barrier();
-  }
-  // here stage kt (if any) is resident in buffer 0 and nsteps - kt is even
-  for (; kt < nsteps; kt += 2) {
-    load_stage(kt + 1, As1, Bs1, sA1, sB1, wa1, wb1);
-    compute_stage(kt, As0, Bs0, sA0, sB0, wa0, wb0);
-    pin_acc();
-    wait_vm_then_barrier();
-    if (kt + 2 < nsteps) load_stage(kt + 2, As0, Bs0, sA0, sB0, wa0, wb0);
-    compute_stage(kt + 1, As1, Bs1, sA1, sB1, wa1, wb1);
-    pin_acc();
-    wait_vm_then_barrier();
-  }
+  // MFMAs of stage kt from one buffer set; for blockwise, PH is the stage's
+  // position in its 128-block (0: start the partial, 1: finish and promote)
+  auto compute_stage = [&](const uint8_t *as, const uint8_t *bs, const float *sa_l, const float *sb_l,
+                           const uint32_t *ma, const uint32_t *mb, int kt, auto ph) {
+    constexpr int PH = decltype(ph)::value;
+    v8i af[MI], bf[NI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) af[mi] = frag(as, wi * 128 + mi * 32 + l32, h);
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) bf[ni] = frag(bs, wj * WN + ni * 32 + l32, h);
+    if (!BLK) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          if (MX) {
+            // the word holds blocks 2(kt&~1) .. +3; this stage's are bytes
+            // 2*PH and 2*PH+1; lane half h takes byte 2*PH + h (opsel 2*PH
+            // after a per-lane shift by 8h)
+            const int sa_w = (int)(ma[wi * 128 + mi * 32 + l32] >> (8 * h));
+            const int sb_w = (int)(mb[wj * WN + ni * 32 + l32] >> (8 * h));
+            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                af[mi], bf[ni], acc[mi][ni], FA, FB, 2 * PH, sa_w, 2 * PH, sb_w);
+          } else {
+            // unit E8M0 scales (127 = 2^0); the scaled form keeps the
+            // accumulators in AGPRs
+            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                af[mi], bf[ni], acc[mi][ni], FA, FB, 0, kUnitScale, 0, kUnitScale);
+          }
+        }
+    } else {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          if (PH == 0) {
+            v16f z;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) z[v] = 0.0f;
+            part[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                af[mi], bf[ni], z, FA, FB, 0, kUnitScale, 0, kUnitScale);
+          } else {
+            part[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                af[mi], bf[ni], part[mi][ni], FA, FB, 0, kUnitScale, 0, kUnitScale);
+          }
+        }
+      if (PH == 1) {
+        // promote: acc += partial * sA(row) * sB; sB per column for wgrad,
+        // one value per tile (the 128x128 weight tile) otherwise
+        const float sbw = MODE == kWgrad ? 0.0f : sbtab[(kt >> 1) & (SB_TAB - 1)];
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+          float sa[16];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 v4 = *reinterpret_cast<const float4 *>(&sa_l[wi * 128 + mi * 32 + q * 8 + h * 4]);
+            sa[q * 4 + 0] = v4.x;
+            sa[q * 4 + 1] = v4.y;
+            sa[q * 4 + 2] = v4.z;
+            sa[q * 4 + 3] = v4.w;
+          }
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) {
+            const float sbj = MODE == kWgrad ? sb_l[wj * WN + ni * 32 + l32] : sbw;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[mi][ni][v] += part[mi][ni][v] * (sa[v] * sbj);
+          }
+        }
+      }
+    }
+  };
 
-  // ---- epilogue: each wave stages its 32-row slabs through its own LDS
-  // region (the stage buffers are free now), then writes rows of 8 outputs
-  // with 16-byte stores. The scale multiply happens on the LDS copy.
+  // ---- main loop: a ring of four stage buffers; stage kt lives in buffer
+  // kt % 4 and its copies are issued three stages ahead. The stage count is
+  // rounded up to whole turns of the ring with zero-filled stages, so the
+  // loop body (four stages) has no conditional MFMAs.
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  if (vsteps > 0) {
+    load_stage(0, As0, Bs0, sA0, sB0, mA0, mB0);
+    load_stage(1, As1, Bs1, sA1, sB1, mA1, mB1);
+    load_stage(2, As2, Bs2, sA2, sB2, mA2, mB2);
+  }
+  for (int kt = 0; kt < vsteps; kt += 4) {
+    stage_ready(kt);
+    load_stage(kt + 3, As3, Bs3, sA3, sB3, mA3, mB3);
+    compute_stage(As0, Bs0, sA0, sB0, mA0, mB0, kt, P0{});
+    pin_acc();
+    stage_ready(kt + 1);
+    if (kt + 4 < vsteps) load_stage(kt + 4, As0, Bs0, sA0, sB0, mA0, mB0);
+    compute_stage(As1, Bs1, sA1, sB1, mA1, mB1, kt + 1, P1{});
+    pin_acc();
+    stage_ready(kt + 2);
+    if (kt + 5 < vsteps) load_stage(kt + 5, As1, Bs1, sA1, sB1, mA1, mB1);
+    compute_stage(As2, Bs2, sA2, sB2, mA2, mB2, kt + 2, P0{});
+    pin_acc();
+    stage_ready(kt + 3);
+    if (kt + 6 < vsteps) load_stage(kt + 6, As2, Bs2, sA2, sB2, mA2, mB2);
+    compute_stage(As3, Bs3, sA3, sB3, mA3, mB3, kt + 3, P1{});
+    pin_acc();
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();  // every wave is done with the stage buffers
+
+  // ---- epilogue: each wave stages 16-row half slabs through its own LDS
+  // region, then writes rows of 8 outputs with 16-byte stores. The scale
+  // multiply happens on the LDS copy.
   float scale = 1.0f;
   if (RECIPE == kTensorwise || RECIPE == kDelayed) {
     const float sa = reinterpret_cast<const float *>(a.a_scales)[0];
@@ -425,51 +468,54 @@ __global__ __launch_bounds__(GTHREADS) void grouped_gemm_kernel(GemmArgs a) {
     scale = sa * sb;
   }
   if (MODE == kWgrad && a.accumulate && nsteps == 0) return;  // empty group: dW_g unchanged
-  constexpr int STR = WN + 8;          // LDS row stride in floats (2-way-free halves)
+  constexpr int STR = WN + 8;          // LDS row stride in floats
   constexpr int CPR = WN / 8;          // 8-float chunks per row
-  constexpr int CPL = 32 * CPR / 64;   // chunks per lane per slab
-  float *cb = reinterpret_cast<float *>(wave == 0 ? As0 : wave == 1 ? As1 : wave == 2 ? Bs0 : Bs1);
+  constexpr int CPL = 16 * CPR / 64;   // chunks per lane per half slab
+  float *cb = reinterpret_cast<float *>(wave == 0 ? As0 : wave == 1 ? As1 : wave == 2 ? As2 : As3);
   const int64_t jw = j0 + wj * WN;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
+    for (int hs = 0; hs < 2; ++hs) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        cb[((v >> 2) * 8 + h * 4 + (v & 3)) * STR + ni * 32 + l32] = acc[mi][ni][v];
-    __builtin_amdgcn_wave_barrier();
+      for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-      const int id = k * 64 + lane;
-      const int r = id / CPR, c8 = id % CPR;
-      const int64_t i = i0 + wi * 128 + mi * 32 + r;
-      const int64_t j = jw + c8 * 8;
-      const float4 x0 = *reinterpret_cast<const float4 *>(&cb[r * STR + c8 * 8]);
-      const float4 x1 = *reinterpret_cast<const float4 *>(&cb[r * STR + c8 * 8 + 4]);
-      if (i < ilim && j < a.J) {  // J % 128 == 0: a chunk is all in or all out
-        if (MODE == kWgrad) {
-          float4 y0 = make_float4(x0.x * scale, x0.y * scale, x0.z * scale, x0.w * scale);
-          float4 y1 = make_float4(x1.x * scale, x1.y * scale, x1.z * scale, x1.w * scale);
-          float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.out) +
-                                                   ((int64_t)g * a.I + i) * a.ldo + j);
-          if (a.accumulate) {
-            const float4 o0 = dst[0], o1 = dst[1];
-            y0 = make_float4(y0.x + o0.x, y0.y + o0.y, y0.z + o0.z, y0.w + o0.w);
-            y1 = make_float4(y1.x + o1.x, y1.y + o1.y, y1.z + o1.z, y1.w + o1.w);
+        for (int v = 8 * hs; v < 8 * hs + 8; ++v)
+          cb[(((v >> 2) & 1) * 8 + h * 4 + (v & 3)) * STR + ni * 32 + l32] = acc[mi][ni][v];
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) {
+        const int id = k * 64 + lane;
+        const int r = id / CPR, c8 = id % CPR;
+        const int64_t i = i0 + wi * 128 + mi * 32 + hs * 16 + r;
+        const int64_t j = jw + c8 * 8;
+        const float4 x0 = *reinterpret_cast<const float4 *>(&cb[r * STR + c8 * 8]);
+        const float4 x1 = *reinterpret_cast<const float4 *>(&cb[r * STR + c8 * 8 + 4]);
+        if (i < ilim && j < a.J) {  // J % 128 == 0: a chunk is all in or all out
+          if (MODE == kWgrad) {
+            float4 y0 = make_float4(x0.x * scale, x0.y * scale, x0.z * scale, x0.w * scale);
+            float4 y1 = make_float4(x1.x * scale, x1.y * scale, x1.z * scale, x1.w * scale);
+            float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.out) +
+                                                     ((int64_t)g * a.I + i) * a.ldo + j);
+            if (a.accumulate) {
+              const float4 o0 = dst[0], o1 = dst[1];
+              y0 = make_float4(y0.x + o0.x, y0.y + o0.y, y0.z + o0.z, y0.w + o0.w);
+              y1 = make_float4(y1.x + o1.x, y1.y + o1.y, y1.z + o1.z, y1.w + o1.w);
+            }
+            dst[0] = y0;
+            dst[1] = y1;
+          } else {
+            uint4 o;
+            o.x = f32_to_bf16_bits(x0.x * scale) | (f32_to_bf16_bits(x0.y * scale) << 16);
+            o.y = f32_to_bf16_bits(x0.z * scale) | (f32_to_bf16_bits(x0.w * scale) << 16);
+            o.z = f32_to_bf16_bits(x1.x * scale) | (f32_to_bf16_bits(x1.y * scale) << 16);
+            o.w = f32_to_bf16_bits(x1.z * scale) | (f32_to_bf16_bits(x1.w * scale) << 16);
+            *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.out) + i * a.ldo + j) = o;
           }
-          dst[0] = y0;
-          dst[1] = y1;
-        } else {
-          uint4 o;
-          o.x = f32_to_bf16_bits(x0.x * scale) | (f32_to_bf16_bits(x0.y * scale) << 16);
-          o.y = f32_to_bf16_bits(x0.z * scale) | (f32_to_bf16_bits(x0.w * scale) << 16);
-          o.z = f32_to_bf16_bits(x1.x * scale) | (f32_to_bf16_bits(x1.y * scale) << 16);
-          o.w = f32_to_bf16_bits(x1.z * scale) | (f32_to_bf16_bits(x1.w * scale) << 16);
-          *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.out) + i * a.ldo + j) = o;
         }
       }
+      __builtin_amdgcn_wave_barrier();
     }
-    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -533,8 +579,8 @@ hipError_t launch_grouped_mm(const GemmParams &p, hipStream_t st) {
     a.ldo = p.N;
     a.b_gstride = p.N * p.ldb;
     // blockwise weight scales [E, K/128, N/128]: l-block = k, j-block = n
-    a.bs_gstride = p.recipe == kMx ? p.N * (p.K / 32) : (p.K / GBK) * (p.N / GBK);
-    a.sb_l = p.N / GBK;
+    a.bs_gstride = p.recipe == kMx ? p.N * (p.K / 32) : (p.K / SBLK) * (p.N / SBLK);
+    a.sb_l = p.N / SBLK;
     a.sb_j = 1;
     return launch_recipe<kFwd>(a, p.recipe, p.fmt_a, p.fmt_b, st);
   }
@@ -545,9 +591,9 @@ hipError_t launch_grouped_mm(const GemmParams &p, hipStream_t st) {
     a.ldo = p.K;
     a.b_gstride = p.K * p.ldb;
     // same [E, K/128, N/128] array: l-block = n, j-block = k
-    a.bs_gstride = p.recipe == kMx ? p.K * (p.N / 32) : (p.K / GBK) * (p.N / GBK);
+    a.bs_gstride = p.recipe == kMx ? p.K * (p.N / 32) : (p.K / SBLK) * (p.N / SBLK);
     a.sb_l = 1;
-    a.sb_j = p.N / GBK;
+    a.sb_j = p.N / SBLK;
     return launch_recipe<kDgrad>(a, p.recipe, p.fmt_a, p.fmt_b, st);
   }
   a.I = p.K;

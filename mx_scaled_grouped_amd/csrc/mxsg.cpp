@@ -187,6 +187,9 @@ mxsg_status mxsg_grouped_mm(int32_t mode, int32_t recipe, int32_t fmt_a, int32_t
   REQUIRE(K % 128 == 0 && N % 128 == 0, MXSG_BAD_SHAPE,
           "grouped_mm: K=%lld and N=%lld must be multiples of 128", (long long)K, (long long)N);
   REQUIRE(M <= ((int64_t)1 << 31) - 1 && E <= (1 << 20), MXSG_BAD_SHAPE, "grouped_mm: too large");
+  // the kernel addresses a tile's 256 rows with 32-bit offsets
+  REQUIRE(lda < ((int64_t)1 << 23) && ldb < ((int64_t)1 << 23), MXSG_BAD_SHAPE,
+          "grouped_mm: row strides must be below 2^23");
   REQUIRE(a_codes && b_codes && out && a_scales && b_scales && group_ends, MXSG_INVALID_ARGUMENT,
           "grouped_mm: NULL operand");
   REQUIRE(accumulate == 0 || mode == MXSG_MODE_WGRAD, MXSG_INVALID_ARGUMENT,
@@ -204,6 +207,8 @@ mxsg_status mxsg_grouped_mm(int32_t mode, int32_t recipe, int32_t fmt_a, int32_t
             (long long)L);
     REQUIRE(ldb == L, MXSG_BAD_SHAPE, "grouped_mm: ldb=%lld must equal %lld", (long long)ldb,
             (long long)L);
+    REQUIRE(recipe != MXSG_RECIPE_BLOCKWISE || L <= 65536, MXSG_UNSUPPORTED,
+            "grouped_mm: blockwise contraction %lld > 65536 is not built", (long long)L);
   }
   mxsg::GemmParams p{};
   p.mode = mode;
