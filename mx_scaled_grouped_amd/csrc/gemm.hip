@@ -36,7 +36,9 @@ constexpr int GBM = 256;   // tile rows (i)
 constexpr int GBK = 64;    // contraction per stage (bytes of codes)
 constexpr int SBLK = 128;  // blockwise scaling block along the contraction
 constexpr int SB_TAB = 512; // blockwise FWD / DGRAD: contraction blocks per tile (L <= 65536)
-constexpr int GTHREADS = 256;
+#ifndef MXSG_GEMM_WAVES
+#define MXSG_GEMM_WAVES 4
+#endif
 constexpr int kUnitScale = 127;  // E8M0 code of 1.0
 
 struct GemmArgs {
@@ -160,18 +162,36 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 40]
+__device__ __forceinline__ void wait_vm_n(int n) {
+  switch (n) {
+#define MXSG_VMW(k) case k: wait_vm<k>(); break;
+    MXSG_VMW(1) MXSG_VMW(2) MXSG_VMW(3) MXSG_VMW(4) MXSG_VMW(5) MXSG_VMW(6) MXSG_VMW(7) MXSG_VMW(8)
+    MXSG_VMW(9) MXSG_VMW(10) MXSG_VMW(11) MXSG_VMW(12) MXSG_VMW(13) MXSG_VMW(14) MXSG_VMW(15)
+    MXSG_VMW(16) MXSG_VMW(17) MXSG_VMW(18) MXSG_VMW(19) MXSG_VMW(20) MXSG_VMW(21) MXSG_VMW(22)
+    MXSG_VMW(23) MXSG_VMW(24) MXSG_VMW(25) MXSG_VMW(26) MXSG_VMW(27) MXSG_VMW(28) MXSG_VMW(29)
+    MXSG_VMW(30) MXSG_VMW(31) MXSG_VMW(32) MXSG_VMW(33) MXSG_VMW(34) MXSG_VMW(35) MXSG_VMW(36)
+    MXSG_VMW(37) MXSG_VMW(38) MXSG_VMW(39) MXSG_VMW(40)
+#undef MXSG_VMW
+    default: wait_vm<0>(); break;
+  }
+}
 
-template <int MODE, int RECIPE, int FA, int FB, int BN>
-__global__ __launch_bounds__(GTHREADS) void grouped_gemm_kernel(GemmArgs a) {
-  constexpr int WN = BN / 2;        // wave tile width along j
-  constexpr int NI = WN / 32;       // 32-wide sub-tiles along j per wave
-  constexpr int MI = 4;             // 32-high sub-tiles along i per wave (128 rows)
-  constexpr int AQ = GBM / 16 / 4;  // 16-row copy groups of A per wave per stage (4)
-  constexpr int BQ = BN / 16 / 4;   // of B (4 or 2)
+template <int MODE, int RECIPE, int FA, int FB, int BN, int NW>
+__global__ __launch_bounds__(64 * NW) void grouped_gemm_kernel(GemmArgs a) {
+  constexpr int NT = 64 * NW;        // threads
+  constexpr int WJ = NW / 2;         // waves along j (two along i, 128 rows each)
+  constexpr int WN = BN / WJ;        // wave tile width along j
+  constexpr int NI = WN / 32;        // 32-wide sub-tiles along j per wave
+  constexpr int MI = 4;              // 32-high sub-tiles along i per wave (128 rows)
+  constexpr int AQ = GBM / 16 / NW;  // 16-row copy groups of A per wave per stage
+  constexpr int BQ = BN / 16 / NW;   // of B
   constexpr bool BLK = RECIPE == kBlockwise;
   constexpr bool MX = RECIPE == kMx;
-  // vector-memory instructions one wave issues per real stage (the waits count them)
-  constexpr int OPS_BASE = AQ + BQ + (BLK ? 1 : 0) + (MX ? 2 : 0);
+  // waves copying the per-row scale words: A rows by waves 0..3, B rows by
+  // waves XB..XB+BN/64-1 (the upper half when there are eight waves)
+  constexpr int XB = NW == 8 ? 4 : 0;
+  static_assert(AQ >= 1 && BQ >= 1 && NI >= 1, "tile shape");
 
   // four stage buffers of A and B as distinct objects: the compiler then
   // knows the copies into one buffer do not alias the reads of another
@@ -188,7 +208,7 @@ __global__ __launch_bounds__(GTHREADS) void grouped_gemm_kernel(GemmArgs a) {
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform (SGPR)
-  const int wi = wave >> 1, wj = wave & 1;
+  const int wi = wave / WJ, wj = wave % WJ;
   const int h = lane >> 5, l32 = lane & 31;
 
   // ---- tile coordinates
@@ -249,28 +269,36 @@ __global__ __launch_bounds__(GTHREADS) void grouped_gemm_kernel(GemmArgs a) {
   // stage, wave w copying rows 64w..64w+63; the weight tile scales of the
   // whole contraction (forward / dgrad) go to LDS once
   const float *sa_src = nullptr, *sb_src = nullptr;
-  const bool sb_wave = MODE == kWgrad && wave < BN / 64;
+  const bool a_wave = wave < GBM / 64;                     // copies A-row scales
+  const bool b_wave = wave >= XB && wave < XB + BN / 64;   // copies B-row scales
+  const bool sb_wave = MODE == kWgrad && b_wave;
   if (BLK) {
     const int r = wave * 64 + lane;
-    sa_src = reinterpret_cast<const float *>(a.a_scales) + (i0 + (r < imax ? r : imax)) * (sa_row / SBLK) + l0 / SBLK;
+    const int rb = (wave - XB) * 64 + lane;
+    if (a_wave)
+      sa_src = reinterpret_cast<const float *>(a.a_scales) + (i0 + (r < imax ? r : imax)) * (sa_row / SBLK) + l0 / SBLK;
     if (sb_wave)
-      sb_src = reinterpret_cast<const float *>(a.b_scales) + (j0 + (r < jmax ? r : jmax)) * (sb_row / SBLK) + l0 / SBLK;
+      sb_src = reinterpret_cast<const float *>(a.b_scales) + (j0 + (rb < jmax ? rb : jmax)) * (sb_row / SBLK) + l0 / SBLK;
     if (MODE != kWgrad) {
       const int64_t jb = j0 / SBLK;
-      for (int lb = t; lb < nsteps / 2 && lb < SB_TAB; lb += GTHREADS)
+      for (int lb = t; lb < nsteps / 2 && lb < SB_TAB; lb += NT)
         sbtab[lb] = reinterpret_cast<const float *>(a.b_scales)[(int64_t)g * a.bs_gstride + lb * a.sb_l + jb * a.sb_j];
     }
   }
-  const int ops_wave = OPS_BASE + (sb_wave ? 1 : 0);
+  // vector-memory instructions this wave issues per real stage (the waits count them)
+  const int ops_wave = AQ + BQ + ((BLK || MX) && a_wave ? 1 : 0) + (sb_wave || (MX && b_wave) ? 1 : 0);
 
   // MX scale words: wave w copies the words of A rows 64w..64w+63 and of B
   // rows 64w..64w+63 (B has 256 rows here)
   const uint8_t *mxa = nullptr, *mxb = nullptr;
   if (MX) {
     const int r = wave * 64 + lane;
-    mxa = reinterpret_cast<const uint8_t *>(a.a_scales) + (i0 + (r < imax ? r : imax)) * (sa_row / 32) + l0 / 32;
-    mxb = reinterpret_cast<const uint8_t *>(a.b_scales) + (MODE == kWgrad ? 0 : (int64_t)g * a.bs_gstride) +
-          (j0 + (r < jmax ? r : jmax)) * (sb_row / 32) + l0 / 32;
+    const int rb = (wave - XB) * 64 + lane;
+    if (a_wave)
+      mxa = reinterpret_cast<const uint8_t *>(a.a_scales) + (i0 + (r < imax ? r : imax)) * (sa_row / 32) + l0 / 32;
+    if (b_wave)
+      mxb = reinterpret_cast<const uint8_t *>(a.b_scales) + (MODE == kWgrad ? 0 : (int64_t)g * a.bs_gstride) +
+            (j0 + (rb < jmax ? rb : jmax)) * (sb_row / 32) + l0 / 32;
   }
   __syncthreads();  // sbtab visible
 
@@ -288,8 +316,8 @@ __global__ __launch_bounds__(GTHREADS) void grouped_gemm_kernel(GemmArgs a) {
                         uint32_t *mb) {
     if (kt < nsteps) {
       if (MX) {  // the 4-byte word holding blocks 2kt, 2kt+1 (4-byte aligned)
-        dma4(mxa + ((kt * 2) & ~3), ma + wave * 64);
-        dma4(mxb + ((kt * 2) & ~3), mb + wave * 64);
+        if (a_wave) dma4(mxa + ((kt * 2) & ~3), ma + wave * 64);
+        if (b_wave) dma4(mxb + ((kt * 2) & ~3), mb + (wave - XB) * 64);
       }
       const uint8_t *ak = abase + kt * GBK;
       const uint8_t *bk = bbase + kt * GBK;
@@ -298,21 +326,21 @@ __global__ __launch_bounds__(GTHREADS) void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int q = 0; q < BQ; ++q) dma16(bk + boff[q], bs + (wave * BQ + q) * 1024);
       if (BLK) {
-        dma4(sa_src + kt / 2, sa + wave * 64);
-        if (sb_wave) dma4(sb_src + kt / 2, sb + wave * 64);
+        if (a_wave) dma4(sa_src + kt / 2, sa + wave * 64);
+        if (sb_wave) dma4(sb_src + kt / 2, sb + (wave - XB) * 64);
       }
     } else {
       const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int u = 0; u < GBM * GBK / 16 / GTHREADS; ++u) *reinterpret_cast<uint4 *>(as + (u * GTHREADS + t) * 16) = z;
+      for (int u = 0; u < GBM * GBK / 16 / NT; ++u) *reinterpret_cast<uint4 *>(as + (u * NT + t) * 16) = z;
 #pragma unroll
-      for (int u = 0; u < BN * GBK / 16 / GTHREADS; ++u) *reinterpret_cast<uint4 *>(bs + (u * GTHREADS + t) * 16) = z;
+      for (int u = 0; u < BN * GBK / 16 / NT; ++u) *reinterpret_cast<uint4 *>(bs + (u * NT + t) * 16) = z;
       if (BLK) {
-        sa[t] = 0.0f;
+        if (t < GBM) sa[t] = 0.0f;
         if (t < BN) sb[t] = 0.0f;
       }
       if (MX) {  // unit scales for the zero stage
-        ma[t] = 0x7f7f7f7fu;
+        if (t < GBM) ma[t] = 0x7f7f7f7fu;
         if (t < BN) mb[t] = 0x7f7f7f7fu;
       }
     }
@@ -324,13 +352,7 @@ __global__ __launch_bounds__(GTHREADS) void grouped_gemm_kernel(GemmArgs a) {
   auto stage_ready = [&](int kt) {
     __builtin_amdgcn_sched_barrier(0);
     const int ahead = nsteps - 1 - kt;  // real stages issued after kt (at most two)
-    if (ahead >= 2) {
-      if (ops_wave == OPS_BASE) wait_vm<2 * OPS_BASE>(); else wait_vm<2 * OPS_BASE + 2>();
-    } else if (ahead == 1) {
-      if (ops_wave == OPS_BASE) wait_vm<OPS_BASE>(); else wait_vm<OPS_BASE + 1>();
-    } else {
-      wait_vm<0>();
-    }
+    wait_vm_n(ahead >= 2 ? 2 * ops_wave : (ahead == 1 ? ops_wave : 0));
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -471,7 +493,9 @@ __global__ __launch_bounds__(GTHREADS) void grouped_gemm_kernel(GemmArgs a) {
   constexpr int STR = WN + 8;          // LDS row stride in floats
   constexpr int CPR = WN / 8;          // 8-float chunks per row
   constexpr int CPL = 16 * CPR / 64;   // chunks per lane per half slab
-  float *cb = reinterpret_cast<float *>(wave == 0 ? As0 : wave == 1 ? As1 : wave == 2 ? As2 : As3);
+  uint8_t *creg = wave == 0 ? As0 : wave == 1 ? As1 : wave == 2 ? As2 : wave == 3 ? As3
+                : wave == 4 ? Bs0 : wave == 5 ? Bs1 : wave == 6 ? Bs2 : Bs3;
+  float *cb = reinterpret_cast<float *>(creg);
   const int64_t jw = j0 + wj * WN;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
@@ -524,6 +548,7 @@ __global__ __launch_bounds__(GTHREADS) void grouped_gemm_kernel(GemmArgs a) {
 template <int MODE, int RECIPE, int FA, int FB>
 static hipError_t launch_cfg(const GemmArgs &a0, hipStream_t st) {
   constexpr int BN = RECIPE == kBlockwise ? 128 : 256;
+  constexpr int NW = MXSG_GEMM_WAVES;
   GemmArgs a = a0;
   a.jtiles = (int)((a.J + BN - 1) / BN);
   int64_t nblocks;
@@ -536,7 +561,7 @@ static hipError_t launch_cfg(const GemmArgs &a0, hipStream_t st) {
   }
   if (nblocks == 0) return hipSuccess;
   if (nblocks > 0x7fffffff) return hipErrorInvalidValue;
-  grouped_gemm_kernel<MODE, RECIPE, FA, FB, BN><<<(unsigned)nblocks, GTHREADS, 0, st>>>(a);
+  grouped_gemm_kernel<MODE, RECIPE, FA, FB, BN, NW><<<(unsigned)nblocks, 64 * NW, 0, st>>>(a);
   return hipGetLastError();
 }
 
