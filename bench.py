@@ -28,6 +28,7 @@ sys.path.insert(0, HERE)
 
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+GEMM_SOURCE = os.path.join(HERE, "mx_scaled_grouped_amd", "csrc", "gemm.hip")
 
 WORKLOADS = {
     "mixtral-dl": 3,   # default: Mixtral shapes, delayed hybrid, fwd + dgrad + wgrad
@@ -240,6 +241,28 @@ def cpu_baseline(cid, rows, cols):
                       f"oracle quantization + float64 GEMMs, {dt:.1f} s"}
 
 
+def measured_traffic(workload):
+    """HBM bytes per grouped-GEMM launch from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE, calibrated against a plain copy); None when
+    there is no summary for this workload or the GEMM source has changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(HERE, "profiles", f"grouped_gemm_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if " = " in line:
+            k, v = line.strip().split(" = ", 1)
+            kv[k] = v
+    if "traffic_bytes_per_launch" not in kv:
+        return None
+    src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    if kv.get("gemm_source_sha256") != src:
+        return None
+    return int(float(kv["traffic_bytes_per_launch"]))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -298,6 +321,9 @@ def main():
     quant_gbs = {k: byts[k] / (quant_ms[k] * 1e-3) / 1e9 for k in quant_ms}
     gemm_total_ms = sum(gemm_ms.values())
     quant_total_ms = sum(quant_ms.values())
+    # the dominant kernel is the grouped GEMM: every GEMM call is one launch of
+    # it, so per-launch FLOPs / average launch time = step FLOPs / GEMM time
+    launches = len(gemm_ms)
     achieved = step_flops / (gemm_total_ms * 1e-3) / 1e12
     quant_agg = sum(byts.values()) / (quant_total_ms * 1e-3) / 1e9
 
@@ -324,7 +350,12 @@ def main():
                    "recipe": spec.recipe, "modes": list(spec.modes),
                    "group_sizes": [int(x) for x in routing.group_sizes]},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+                     "traffic": measured_traffic(args.workload),
+                     "kernel": "grouped_gemm_kernel (every GEMM launch of a step)",
+                     "launches_per_step": launches,
+                     "flops_per_launch": step_flops / launches,
+                     "avg_launch_ms": round(gemm_total_ms / launches, 4)},
         "cpu_baseline": cpu,
         "breakdown": {
             "gemm_ms": {k: round(v, 4) for k, v in gemm_ms.items()},

@@ -1,0 +1,294 @@
+"""Full-size parity on the benchmark workloads, in the launch configuration
+the benchmark times: bench.py's own inputs and its `Step` (quantize with
+row- and column-wise outputs, forward, dgrad, wgrad, delayed update).
+
+The oracle cannot run a whole Mixtral-sized step in seconds, so it checks
+sampled outputs: every group's first two and last two rows plus random
+rows in between, and whole 128-wide blocks of the feature dimensions (the
+first, the last and a random one). Quantization of a sample is exactly
+the quantization of the full tensor restricted to it because
+  * tensorwise / delayed scales come from the amax of the FULL tensor,
+    computed by the oracle (tensorwise: current amax; delayed: the
+    oracle's own amax-history state after the previous step), and the
+    sampled rows/columns are cast with that scale;
+  * 1x128 / 1x32 row blocks lie inside one row and 128x1 / 32x1 column
+    blocks inside one column, and the weight's 128x128 tiles inside a
+    sampled 128-block; group boundaries are kept because whole columns are
+    taken for the column-wise layout.
+Codes, scales, padded starts and the delayed state must match bit for bit;
+sampled GEMM outputs within 1e-3 relative Frobenius error of the oracle's
+float64 GEMM of the dequantized sample (overall and per expert)."""
+import numpy as np
+import pytest
+
+from tests.gpu_helpers import torch, gpu_available, assert_bits_equal
+from oracle import quant as OQ
+from oracle import formats as OF
+from oracle import gemm as OG
+from oracle.delayed import DelayedState as ODelayed
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="no GPU")]
+
+FMT = {0: OF.E4M3, 1: OF.E5M2}
+TOL = 1e-3
+WORKLOADS = ["mixtral-tw", "mixtral-dl", "deepseek-block", "llama4-mx"]
+
+_cache = {}
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _np(t):
+    return t.contiguous().cpu().numpy()
+
+
+def _take(t, *idx):
+    """t indexed on the device along (dim, indices) pairs, before the host copy."""
+    for d, ix in idx:
+        t = t.index_select(d, torch.from_numpy(np.asarray(ix, np.int64)).to(t.device))
+    return t
+
+
+def _run(name):
+    """Two benchmark steps (input sets 0 then 1); outputs are step 2's."""
+    if name in _cache:
+        return _cache[name]
+    _cache.clear()
+    import bench
+    from mx_scaled_grouped_amd import api, workloads as W
+    cid = bench.WORKLOADS[name]
+    print(f"[fullsize] {name}: generating inputs", flush=True)
+    spec, routing, ge_t, weights, sets = bench.make_inputs(cid, torch, W)
+    step = bench.Step(torch, api, spec, ge_t, weights, spec.recipe)
+    step.run(sets[0])
+    step.run(sets[1])
+    torch.cuda.synchronize()
+    print(f"[fullsize] {name}: two steps done", flush=True)
+    st = {"spec": spec, "ge": routing.group_ends.astype(np.int64), "step": step,
+          "weights": weights, "sets": sets, "recipe": spec.recipe}
+    if spec.recipe == "dl":
+        st["scales"] = _oracle_delayed(step, spec, weights, sets)
+    _cache[name] = st
+    return st
+
+
+def _oracle_delayed(step, spec, weights, sets):
+    """Replay the delayed-scaling state in the oracle over both steps; check the
+    GPU state after them; return the (s, inv) each unit used in step 2."""
+    ng, E = len(spec.gemms), spec.experts
+    sf = ODelayed(ng + ng * E, OF.E4M3, 1024)
+    sg = ODelayed(ng, OF.E5M2, 1024)
+    w_amax = []
+    for which in spec.gemms:
+        w = _bits(weights[which])
+        w_amax += [OQ.amax_of(OQ.bf16_to_f32(w[e])) for e in range(E)]
+        del w
+    used = None
+    for s in (0, 1):
+        d = sets[s]
+        a_amax = [OQ.amax_of(OQ.bf16_to_f32(_bits(d["a_" + wh]))) for wh in spec.gemms]
+        g_amax = [OQ.amax_of(OQ.bf16_to_f32(_bits(d["dy_" + wh]))) for wh in spec.gemms]
+        if s == 1:
+            used = {"f": (sf.s.copy(), sf.inv.copy()), "g": (sg.s.copy(), sg.inv.copy())}
+        sf.update(np.array(a_amax + w_amax, np.float32))
+        sg.update(np.array(g_amax, np.float32))
+    for gpu, ora, tag in ((step.st_f, sf, "e4m3 state"), (step.st_g, sg, "e5m2 state")):
+        assert_bits_equal(_np(gpu.history), ora.history, tag + " history")
+        assert_bits_equal(_np(gpu.scale), ora.s, tag + " scale")
+        assert_bits_equal(_np(gpu.inv), ora.inv, tag + " inv")
+        assert np.array_equal(_np(gpu.pos).astype(np.int64), ora.pos), tag + " pos"
+    return used
+
+
+def _row_sample(ge, seed, extra=12):
+    rng = np.random.default_rng(seed)
+    st = np.concatenate([[0], ge[:-1]])
+    rows = []
+    for a, b in zip(st, ge):
+        if b <= a:
+            continue
+        pick = {a, b - 1, min(a + 1, b - 1), max(b - 2, a)}
+        pick.update(rng.integers(a, b, size=min(extra, b - a)).tolist())
+        rows += sorted(pick)
+    rows = np.array(rows, np.int64)
+    ge_s = np.searchsorted(rows, ge, side="left").astype(np.int64)
+    return rows, ge_s
+
+
+def _block_sample(D, seed, blk=128):
+    rng = np.random.default_rng(seed)
+    nb = D // blk
+    b = sorted({0, nb - 1, int(rng.integers(0, nb))})
+    return np.concatenate([np.arange(x * blk, (x + 1) * blk) for x in b]), np.array(b)
+
+
+def _act_scale(st, which, kind, x_bits, fmt):
+    """(recipe the oracle runs on the sample, dl_scale) for an activation/gradient."""
+    r = st["recipe"]
+    if r == "tw":
+        return "dl", OQ.fp32_scale_pair(OQ.amax_of(OQ.bf16_to_f32(x_bits)), fmt)
+    if r == "dl":
+        spec = st["spec"]
+        gi = spec.gemms.index(which)
+        s, inv = st["scales"][kind]
+        return "dl", (s[gi], inv[gi])
+    return r, None
+
+
+def _w_scale(st, which, w_bits, fmt):
+    r = st["recipe"]
+    E = w_bits.shape[0]
+    if r == "tw":
+        am = np.array([OQ.amax_of(OQ.bf16_to_f32(w_bits[e])) for e in range(E)], np.float32)
+        return "dl", OQ.fp32_scale_pair(am, fmt)
+    if r == "dl":
+        spec = st["spec"]
+        u0 = len(spec.gemms) + spec.gemms.index(which) * E
+        s, inv = st["scales"]["f"]
+        return "dl", (s[u0:u0 + E], inv[u0:u0 + E])
+    return r, None
+
+
+def _check_scales_rows(gpu_scales, ora_scales, rec, sel, what):
+    g = _np(gpu_scales)
+    if rec == "dl":
+        assert_bits_equal(g.reshape(-1)[:1], np.asarray(ora_scales, np.float32).reshape(-1)[:1], what)
+    else:
+        assert_bits_equal(g[sel], ora_scales, what)
+
+
+def _check_err(got, ref, ge_s, what):
+    e = OG.rel_fro(got, ref)
+    assert e <= TOL, f"{what}: rel err {e:.3e}"
+    st = np.concatenate([[0], ge_s[:-1]])
+    for g, (a, b) in enumerate(zip(st, ge_s)):
+        if b > a:
+            eg = OG.rel_fro(got[a:b], ref[a:b])
+            assert eg <= TOL, f"{what}: group {g} rel err {eg:.3e}"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _release():
+    yield
+    _cache.clear()
+    torch.cuda.empty_cache()
+
+
+def check_forward(name, which):
+    st = _run(name)
+    spec, step, ge = st["spec"], st["step"], st["ge"]
+    K, N = spec.gemm_shape(which)
+    fa = FMT[step.fa]
+    a_bits = _bits(st["sets"][1]["a_" + which])
+    w_bits = _bits(st["weights"][which])
+    rows, ge_s = _row_sample(ge, 11)
+    ncols, nblk = _block_sample(N, 12)
+    rec, dls = _act_scale(st, which, "f", a_bits, fa)
+    ra = OQ.quantize_act(a_bits[rows], rec, fa, dl_scale=dls)
+    qa = step.q["a_" + which]
+    assert_bits_equal(_np(_take(qa.row_codes, (0, rows))), ra["row_codes"], "activation codes")
+    _check_scales_rows(qa.row_scales, ra["row_scales"], rec, rows, "activation scales")
+    wrec, wdl = _w_scale(st, which, w_bits, OF.E4M3)
+    rw = OQ.quantize_weight(np.ascontiguousarray(w_bits[:, :, ncols]), wrec, OF.E4M3, dl_scale=wdl)
+    qw = step.q["w_" + which]
+    assert_bits_equal(_np(_take(qw.kmajor_codes, (1, ncols))), rw["kmajor_codes"], "weight k-major codes")
+    ks = _np(qw.kmajor_scales)
+    if wrec == "dl":
+        assert_bits_equal(ks, rw["kmajor_scales"], "weight scales")
+    elif wrec == "block":
+        assert_bits_equal(ks[:, :, nblk], rw["kmajor_scales"], "weight tile scales")
+    else:
+        assert_bits_equal(ks[:, ncols, :], rw["kmajor_scales"], "weight MX scales (k blocks)")
+    ref = OG.round_bf16(OG.grouped_fwd(OG.deq_act_rows(ra["row_codes"], ra["row_scales"], rec, fa),
+                                       OG.deq_weight(rw, wrec, OF.E4M3, "k"), ge_s))
+    y = step.out["y_" + which]
+    got = OG.bf16_bits_to_f64(_bits(_take(y, (0, rows), (1, ncols))))
+    _check_err(got, ref, ge_s, f"{name} forward {which}")
+
+
+def check_dgrad(name, which):
+    st = _run(name)
+    spec, step, ge = st["spec"], st["step"], st["ge"]
+    K, N = spec.gemm_shape(which)
+    fg = FMT[step.fg]
+    d_bits = _bits(st["sets"][1]["dy_" + which])
+    w_bits = _bits(st["weights"][which])
+    rows, ge_s = _row_sample(ge, 21)
+    kcols, kblk = _block_sample(K, 22)
+    rec, dls = _act_scale(st, which, "g", d_bits, fg)
+    rd = OQ.quantize_act(d_bits[rows], rec, fg, dl_scale=dls)
+    qd = step.q["dy_" + which]
+    assert_bits_equal(_np(_take(qd.row_codes, (0, rows))), rd["row_codes"], "gradient codes")
+    _check_scales_rows(qd.row_scales, rd["row_scales"], rec, rows, "gradient scales")
+    wrec, wdl = _w_scale(st, which, w_bits, OF.E4M3)
+    rw = OQ.quantize_weight(np.ascontiguousarray(w_bits[:, kcols, :]), wrec, OF.E4M3, dl_scale=wdl)
+    qw = step.q["w_" + which]
+    assert_bits_equal(_np(_take(qw.nmajor_codes, (1, kcols))), rw["nmajor_codes"], "weight n-major codes")
+    ns = _np(qw.nmajor_scales)
+    if wrec == "block":
+        assert_bits_equal(ns[:, kblk, :], rw["nmajor_scales"], "weight tile scales")
+    elif wrec == "mx":
+        assert_bits_equal(ns[:, kcols, :], rw["nmajor_scales"], "weight MX scales (n blocks)")
+    ref = OG.round_bf16(OG.grouped_dgrad(OG.deq_act_rows(rd["row_codes"], rd["row_scales"], rec, fg),
+                                         OG.deq_weight(rw, wrec, OF.E4M3, "n"), ge_s))
+    da = step.out["da_" + which]
+    got = OG.bf16_bits_to_f64(_bits(_take(da, (0, rows), (1, kcols))))
+    _check_err(got, ref, ge_s, f"{name} dgrad {which}")
+
+
+def check_wgrad(name, which):
+    st = _run(name)
+    spec, step, ge = st["spec"], st["step"], st["ge"]
+    K, N = spec.gemm_shape(which)
+    E = spec.experts
+    fa, fg = FMT[step.fa], FMT[step.fg]
+    a_bits = _bits(st["sets"][1]["a_" + which])
+    d_bits = _bits(st["sets"][1]["dy_" + which])
+    kcols, _ = _block_sample(K, 31)
+    ncols, _ = _block_sample(N, 32)
+    qa, qd = step.q["a_" + which], step.q["dy_" + which]
+    sides = []
+    for x_bits, cols, fmt, kind, q, tag in ((a_bits, kcols, fa, "f", qa, "activation"),
+                                            (d_bits, ncols, fg, "g", qd, "gradient")):
+        rec, dls = _act_scale(st, which, kind, x_bits, fmt)
+        rc = OQ.quantize_act(np.ascontiguousarray(x_bits[:, cols]), rec, fmt, ge, rowwise=False,
+                             colwise=True, dl_scale=dls)
+        P = rc["padded_starts"]
+        assert np.array_equal(_np(q.padded_starts).astype(np.int64), P), tag + " padded starts"
+        cc = _np(_take(q.col_codes, (0, cols)))
+        assert_bits_equal(cc[:, :P[-1]], rc["col_codes"], tag + " column codes")
+        cs = _np(q.col_scales)
+        if rec == "dl":
+            assert_bits_equal(cs[:1], rc["col_scales"], tag + " column scale")
+        else:
+            blk = 128 if rec == "block" else 32
+            assert_bits_equal(cs[cols][:, :P[-1] // blk], rc["col_scales"], tag + " column scales")
+        deq = OG.unpad_cols(OG.deq_act_cols(rc["col_codes"], rc["col_scales"], rec, fmt), P, ge)
+        sides.append(deq)
+    ref = OG.round_f32(OG.grouped_wgrad(sides[0], sides[1], ge, E))
+    dw = _np(_take(step.out["dw_" + which], (1, kcols), (2, ncols))).astype(np.float64)
+    sizes = np.diff(np.concatenate([[0], ge]))
+    for e in range(E):
+        if sizes[e] == 0:
+            assert not np.any(dw[e]), f"empty expert {e} has a nonzero weight gradient"
+            continue
+        eg = OG.rel_fro(dw[e], ref[e])
+        assert eg <= TOL, f"{name} wgrad {which} expert {e}: rel err {eg:.3e}"
+    assert OG.rel_fro(dw, ref) <= TOL
+
+
+# workload-major order, so each workload's two steps run once
+CASES = [(n, m, w) for n in WORKLOADS for m in ("fwd", "dgrad", "wgrad") for w in ("gu", "dn")]
+
+
+@pytest.mark.parametrize("name,mode,which", CASES)
+def test_sampled(name, mode, which):
+    from mx_scaled_grouped_amd import workloads as W
+    import bench
+    spec = W.SPECS[bench.WORKLOADS[name]]
+    if mode not in spec.modes or which not in spec.gemms:
+        pytest.skip(f"{spec.name} runs no {mode} {which}")
+    print(f"[fullsize] {name} {mode} {which}", flush=True)
+    {"fwd": check_forward, "dgrad": check_dgrad, "wgrad": check_wgrad}[mode](name, which)
