@@ -33,12 +33,9 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int GBM = 256;   // tile rows (i)
-constexpr int GBK = 64;    // contraction per stage (bytes of codes)
-constexpr int SBLK = 128;  // blockwise scaling block along the contraction
+constexpr int GBK = 128;   // contraction per stage (bytes of codes: one 128-byte row piece)
+constexpr int SBLK = 128;  // blockwise scaling block along the contraction (one stage)
 constexpr int SB_TAB = 512; // blockwise FWD / DGRAD: contraction blocks per tile (L <= 65536)
-#ifndef MXSG_GEMM_WAVES
-#define MXSG_GEMM_WAVES 4
-#endif
 constexpr int kUnitScale = 127;  // E8M0 code of 1.0
 
 struct GemmArgs {
@@ -127,16 +124,16 @@ __device__ bool locate_row_tile(const GemmArgs &a, int slot, int &g_out, int64_t
   return s_found != 0;
 }
 
-// LDS stage tiles hold rows of GBK = 64 code bytes as four 16-byte chunks;
-// chunk c of row r sits at chunk c ^ ((r >> 2) & 3), so the 16 lanes of a
-// fragment read that share a bank sweep (rows r, r+4, r+8, r+12) hit
-// different banks.
-__device__ __forceinline__ int swz(int row, int ch) { return row * GBK + ((ch ^ ((row >> 2) & 3)) << 4); }
+// LDS stage tiles hold rows of GBK = 128 code bytes as eight 16-byte chunks;
+// chunk c of row r sits at chunk c ^ ((r >> 1) & 7), so the eight lanes a
+// fragment read serves per LDS cycle (eight consecutive rows, one chunk
+// index) hit eight different 16-byte bank groups.
+__device__ __forceinline__ int swz(int row, int ch) { return row * GBK + ((ch ^ ((row >> 1) & 7)) << 4); }
 
 // Direct global -> LDS copies (global_load_lds_dwordx4 / _dword): lane L of
 // the wave lands at lds + 16 L (or 4 L); M0 holds the LDS byte address.
 // Issued through inline asm, so the compiler inserts no waits for them: the
-// main loop counts them itself (vmcnt) before each stage's barrier.
+// main loop waits for them itself (vmcnt) before each stage's barrier.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
@@ -147,68 +144,47 @@ __device__ __forceinline__ void dma4(const void *src, void *lds) {
   asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds_addr(lds)) : "memory");
 }
 
-// MFMA 32x32x64 f8 operand for one lane: the lane's row, and (measured lane
-// layout) bytes 0-15 = k in [16h, 16h+16) of the first 32-block, bytes
-// 16-31 = k in [32+16h, 48+16h) of the second, h = the lane's half of the
-// wave; i.e. 16-byte chunks h and 2 + h of the 64-wide stage row. The scale
-// operand of lane i + 32b covers row i and 32-block b.
-__device__ __forceinline__ v8i frag(const uint8_t *buf, int row, int h) {
-  const uint4 x0 = *reinterpret_cast<const uint4 *>(&buf[swz(row, h)]);
-  const uint4 x1 = *reinterpret_cast<const uint4 *>(&buf[swz(row, 2 + h)]);
+// MFMA 32x32x64 f8 operand for one lane and 64-deep half s of the stage:
+// the lane's row, and (measured lane layout) bytes 0-15 = k in [16h, 16h+16)
+// of the half's first 32-block, bytes 16-31 = k in [32+16h, 48+16h) of its
+// second, h = the lane's half of the wave; i.e. 16-byte chunks 4s + h and
+// 4s + 2 + h of the 128-byte stage row. The scale operand of lane i + 32b
+// covers row i and 32-block b.
+__device__ __forceinline__ v8i frag(const uint8_t *buf, int row, int c) {
+  const uint4 x0 = *reinterpret_cast<const uint4 *>(&buf[swz(row, c)]);
+  const uint4 x1 = *reinterpret_cast<const uint4 *>(&buf[swz(row, c + 2)]);
   return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 40]
-__device__ __forceinline__ void wait_vm_n(int n) {
-  switch (n) {
-#define MXSG_VMW(k) case k: wait_vm<k>(); break;
-    MXSG_VMW(1) MXSG_VMW(2) MXSG_VMW(3) MXSG_VMW(4) MXSG_VMW(5) MXSG_VMW(6) MXSG_VMW(7) MXSG_VMW(8)
-    MXSG_VMW(9) MXSG_VMW(10) MXSG_VMW(11) MXSG_VMW(12) MXSG_VMW(13) MXSG_VMW(14) MXSG_VMW(15)
-    MXSG_VMW(16) MXSG_VMW(17) MXSG_VMW(18) MXSG_VMW(19) MXSG_VMW(20) MXSG_VMW(21) MXSG_VMW(22)
-    MXSG_VMW(23) MXSG_VMW(24) MXSG_VMW(25) MXSG_VMW(26) MXSG_VMW(27) MXSG_VMW(28) MXSG_VMW(29)
-    MXSG_VMW(30) MXSG_VMW(31) MXSG_VMW(32) MXSG_VMW(33) MXSG_VMW(34) MXSG_VMW(35) MXSG_VMW(36)
-    MXSG_VMW(37) MXSG_VMW(38) MXSG_VMW(39) MXSG_VMW(40)
-#undef MXSG_VMW
-    default: wait_vm<0>(); break;
-  }
-}
-
-template <int MODE, int RECIPE, int FA, int FB, int BN, int NW>
-__global__ __launch_bounds__(64 * NW) void grouped_gemm_kernel(GemmArgs a) {
-  constexpr int NT = 64 * NW;        // threads
-  constexpr int WJ = NW / 2;         // waves along j (two along i, 128 rows each)
-  constexpr int WN = BN / WJ;        // wave tile width along j
+template <int MODE, int RECIPE, int FA, int FB, int BN>
+__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
+  constexpr int NT = 256;            // threads: 4 waves, 2 along i (128 rows each) x 2 along j
+  constexpr int WN = BN / 2;         // wave tile width along j
   constexpr int NI = WN / 32;        // 32-wide sub-tiles along j per wave
   constexpr int MI = 4;              // 32-high sub-tiles along i per wave (128 rows)
-  constexpr int AQ = GBM / 16 / NW;  // 16-row copy groups of A per wave per stage
-  constexpr int BQ = BN / 16 / NW;   // of B
+  constexpr int AQ = GBM / 8 / 4;    // 8-row copy groups (1 KB) of A per wave per stage
+  constexpr int BQ = BN / 8 / 4;     // of B
   constexpr bool BLK = RECIPE == kBlockwise;
   constexpr bool MX = RECIPE == kMx;
-  // waves copying the per-row scale words: A rows by waves 0..3, B rows by
-  // waves XB..XB+BN/64-1 (the upper half when there are eight waves)
-  constexpr int XB = NW == 8 ? 4 : 0;
   static_assert(AQ >= 1 && BQ >= 1 && NI >= 1, "tile shape");
 
-  // four stage buffers of A and B as distinct objects: the compiler then
-  // knows the copies into one buffer do not alias the reads of another
-  __shared__ __attribute__((aligned(1024))) uint8_t As0[GBM * GBK], As1[GBM * GBK], As2[GBM * GBK], As3[GBM * GBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t Bs0[BN * GBK], Bs1[BN * GBK], Bs2[BN * GBK], Bs3[BN * GBK];
-  __shared__ __attribute__((aligned(16))) float sA0[BLK ? GBM : 4], sA1[BLK ? GBM : 4], sA2[BLK ? GBM : 4], sA3[BLK ? GBM : 4];
-  __shared__ __attribute__((aligned(16))) float sB0[BLK ? BN : 4], sB1[BLK ? BN : 4], sB2[BLK ? BN : 4], sB3[BLK ? BN : 4];
+  // two stage buffers of A and B as distinct objects: the compiler then
+  // knows the copies into one buffer do not alias the reads of the other
+  __shared__ __attribute__((aligned(1024))) uint8_t As0[GBM * GBK], As1[GBM * GBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t Bs0[BN * GBK], Bs1[BN * GBK];
+  // blockwise: per-row scales of the stage's 128-block (A rows; B rows for wgrad)
+  __shared__ __attribute__((aligned(16))) float sA0[BLK ? GBM : 4], sA1[BLK ? GBM : 4];
+  __shared__ __attribute__((aligned(16))) float sB0[BLK ? BN : 4], sB1[BLK ? BN : 4];
   __shared__ float sbtab[BLK ? SB_TAB : 1];  // blockwise weight scales of this tile's j-block, per l-block
-  // MX: per stage buffer, the E8M0 word (4 blocks of 32) holding each tile
-  // row's two blocks of the stage, for A rows and B rows
-  __shared__ uint32_t mA0[MX ? GBM : 1], mA1[MX ? GBM : 1], mA2[MX ? GBM : 1], mA3[MX ? GBM : 1];
-  __shared__ uint32_t mB0[MX ? BN : 1], mB1[MX ? BN : 1], mB2[MX ? BN : 1], mB3[MX ? BN : 1];
+  // MX: per stage buffer, each tile row's E8M0 word (the four 32-blocks of
+  // the stage), stored so the four words one lane needs are contiguous
+  __shared__ __attribute__((aligned(16))) uint32_t mA0[MX ? GBM : 4], mA1[MX ? GBM : 4];
+  __shared__ __attribute__((aligned(16))) uint32_t mB0[MX ? BN : 4], mB1[MX ? BN : 4];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform (SGPR)
-  const int wi = wave / WJ, wj = wave % WJ;
+  const int wi = wave >> 1, wj = wave & 1;
   const int h = lane >> 5, l32 = lane & 31;
 
   // ---- tile coordinates
@@ -229,7 +205,7 @@ __global__ __launch_bounds__(64 * NW) void grouped_gemm_kernel(GemmArgs a) {
     p_lo = p_lo < 0 ? 0 : (p_lo > cap ? cap : p_lo);
     p_hi = p_hi < p_lo ? p_lo : (p_hi > cap ? cap : p_hi);
     l0 = p_lo & ~(int64_t)127;                       // padded starts are 128-aligned
-    nsteps = (int)(((p_hi - l0) / 128) * (128 / GBK));
+    nsteps = (int)((p_hi - l0) / GBK);
   } else {
     int slot, jt;
     raster(lid, a.slots, a.jtiles, slot, jt);
@@ -238,7 +214,7 @@ __global__ __launch_bounds__(64 * NW) void grouped_gemm_kernel(GemmArgs a) {
     l0 = 0;
     nsteps = (int)(a.L / GBK);
   }
-  const int vsteps = (nsteps + 3) & ~3;  // stages rounded up to whole ring turns
+  const int vsteps = (nsteps + 1) & ~1;  // stages rounded up to whole turns of the two-buffer ring
 
   // scale-row strides: FWD / DGRAD scales are [rows, L/blk]; WGRAD scales
   // follow the padded column layout, [rows, ld/blk]
@@ -246,7 +222,10 @@ __global__ __launch_bounds__(64 * NW) void grouped_gemm_kernel(GemmArgs a) {
   const int64_t sb_row = MODE == kWgrad ? a.ldb : a.L;
 
   // ---- per-lane byte offsets of the 16-byte chunks this lane copies, relative
-  // to the tile base; rows past the valid range re-read the last valid row
+  // to the tile base; rows past the valid range re-read the last valid row.
+  // Copy group q of a wave is 8 rows x 128 bytes; lane L takes row L / 8 of
+  // it and lands at LDS chunk L % 8, so it reads the global chunk that the
+  // swizzle puts there.
   const uint8_t *abase = a.a + i0 * a.lda + l0;
   const uint8_t *bbase = a.b + (MODE == kWgrad ? 0 : (int64_t)g * a.b_gstride) + j0 * a.ldb + l0;
   const int imax = (int)((ilim - i0) < GBM ? (ilim - i0) : GBM) - 1;
@@ -254,14 +233,14 @@ __global__ __launch_bounds__(64 * NW) void grouped_gemm_kernel(GemmArgs a) {
   uint32_t aoff[AQ], boff[BQ];
 #pragma unroll
   for (int q = 0; q < AQ; ++q) {
-    const int row = (wave * AQ + q) * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ ((row >> 2) & 3);
+    const int row = (wave * AQ + q) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
     aoff[q] = (uint32_t)((row < imax ? row : imax) * (int32_t)a.lda + c * 16);
   }
 #pragma unroll
   for (int q = 0; q < BQ; ++q) {
-    const int row = (wave * BQ + q) * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ ((row >> 2) & 3);
+    const int row = (wave * BQ + q) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
     boff[q] = (uint32_t)((row < jmax ? row : jmax) * (int32_t)a.ldb + c * 16);
   }
 
@@ -269,36 +248,33 @@ __global__ __launch_bounds__(64 * NW) void grouped_gemm_kernel(GemmArgs a) {
   // stage, wave w copying rows 64w..64w+63; the weight tile scales of the
   // whole contraction (forward / dgrad) go to LDS once
   const float *sa_src = nullptr, *sb_src = nullptr;
-  const bool a_wave = wave < GBM / 64;                     // copies A-row scales
-  const bool b_wave = wave >= XB && wave < XB + BN / 64;   // copies B-row scales
-  const bool sb_wave = MODE == kWgrad && b_wave;
+  const bool b_wave = wave < BN / 64;   // copies B-row scale words / scales
   if (BLK) {
     const int r = wave * 64 + lane;
-    const int rb = (wave - XB) * 64 + lane;
-    if (a_wave)
-      sa_src = reinterpret_cast<const float *>(a.a_scales) + (i0 + (r < imax ? r : imax)) * (sa_row / SBLK) + l0 / SBLK;
-    if (sb_wave)
-      sb_src = reinterpret_cast<const float *>(a.b_scales) + (j0 + (rb < jmax ? rb : jmax)) * (sb_row / SBLK) + l0 / SBLK;
+    sa_src = reinterpret_cast<const float *>(a.a_scales) + (i0 + (r < imax ? r : imax)) * (sa_row / SBLK) + l0 / SBLK;
+    if (MODE == kWgrad && b_wave)
+      sb_src = reinterpret_cast<const float *>(a.b_scales) + (j0 + (r < jmax ? r : jmax)) * (sb_row / SBLK) + l0 / SBLK;
     if (MODE != kWgrad) {
       const int64_t jb = j0 / SBLK;
-      for (int lb = t; lb < nsteps / 2 && lb < SB_TAB; lb += NT)
+      for (int lb = t; lb < nsteps && lb < SB_TAB; lb += NT)
         sbtab[lb] = reinterpret_cast<const float *>(a.b_scales)[(int64_t)g * a.bs_gstride + lb * a.sb_l + jb * a.sb_j];
     }
   }
-  // vector-memory instructions this wave issues per real stage (the waits count them)
-  const int ops_wave = AQ + BQ + ((BLK || MX) && a_wave ? 1 : 0) + (sb_wave || (MX && b_wave) ? 1 : 0);
 
-  // MX scale words: wave w copies the words of A rows 64w..64w+63 and of B
-  // rows 64w..64w+63 (B has 256 rows here)
+  // MX scale words: the word of stage kt holds 32-blocks 4kt .. 4kt+3 of a
+  // row. Word slot d of the LDS array holds tile row
+  // 128 (d / 128) + 32 (d % 4) + (d / 4) % 32, so the lane (l32, wave row or
+  // column half w) that needs rows 128w + 32m + l32, m = 0..3, finds them in
+  // slots 4 (32w + l32) .. +3. Lane L of wave w copies slot 64w + L.
+  static_assert(!MX || (MI == 4 && NI == 4 && BN == 256), "MX word layout");
   const uint8_t *mxa = nullptr, *mxb = nullptr;
   if (MX) {
-    const int r = wave * 64 + lane;
-    const int rb = (wave - XB) * 64 + lane;
-    if (a_wave)
-      mxa = reinterpret_cast<const uint8_t *>(a.a_scales) + (i0 + (r < imax ? r : imax)) * (sa_row / 32) + l0 / 32;
+    const int d = wave * 64 + lane;
+    const int r = (d >> 7) * 128 + (d & 3) * 32 + ((d >> 2) & 31);
+    mxa = reinterpret_cast<const uint8_t *>(a.a_scales) + (i0 + (r < imax ? r : imax)) * (sa_row / 32) + l0 / 32;
     if (b_wave)
       mxb = reinterpret_cast<const uint8_t *>(a.b_scales) + (MODE == kWgrad ? 0 : (int64_t)g * a.bs_gstride) +
-            (j0 + (rb < jmax ? rb : jmax)) * (sb_row / 32) + l0 / 32;
+            (j0 + (r < jmax ? r : jmax)) * (sb_row / 32) + l0 / 32;
   }
   __syncthreads();  // sbtab visible
 
@@ -315,9 +291,13 @@ __global__ __launch_bounds__(64 * NW) void grouped_gemm_kernel(GemmArgs a) {
   auto load_stage = [&](int kt, uint8_t *as, uint8_t *bs, float *sa, float *sb, uint32_t *ma,
                         uint32_t *mb) {
     if (kt < nsteps) {
-      if (MX) {  // the 4-byte word holding blocks 2kt, 2kt+1 (4-byte aligned)
-        if (a_wave) dma4(mxa + ((kt * 2) & ~3), ma + wave * 64);
-        if (b_wave) dma4(mxb + ((kt * 2) & ~3), mb + (wave - XB) * 64);
+      if (MX) {
+        dma4(mxa + kt * 4, ma + wave * 64);
+        if (b_wave) dma4(mxb + kt * 4, mb + wave * 64);
+      }
+      if (BLK) {
+        dma4(sa_src + kt, sa + wave * 64);
+        if (MODE == kWgrad && b_wave) dma4(sb_src + kt, sb + wave * 64);
       }
       const uint8_t *ak = abase + kt * GBK;
       const uint8_t *bk = bbase + kt * GBK;
@@ -325,10 +305,6 @@ __global__ __launch_bounds__(64 * NW) void grouped_gemm_kernel(GemmArgs a) {
       for (int q = 0; q < AQ; ++q) dma16(ak + aoff[q], as + (wave * AQ + q) * 1024);
 #pragma unroll
       for (int q = 0; q < BQ; ++q) dma16(bk + boff[q], bs + (wave * BQ + q) * 1024);
-      if (BLK) {
-        if (a_wave) dma4(sa_src + kt / 2, sa + wave * 64);
-        if (sb_wave) dma4(sb_src + kt / 2, sb + (wave - XB) * 64);
-      }
     } else {
       const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
@@ -347,12 +323,12 @@ __global__ __launch_bounds__(64 * NW) void grouped_gemm_kernel(GemmArgs a) {
     __builtin_amdgcn_sched_barrier(0);  // the copies go out before the MFMAs that follow
   };
 
-  // wait until this wave's copies of stage kt have landed (the copies of the
-  // two later stages may still be in flight), then synchronize the workgroup
-  auto stage_ready = [&](int kt) {
+  // wait until this wave's copies of the next stage (the only ones in
+  // flight) have landed, then synchronize the workgroup: after the barrier
+  // every wave's copies are visible and every wave is done with the other buffer
+  auto stage_ready = [&]() {
     __builtin_amdgcn_sched_barrier(0);
-    const int ahead = nsteps - 1 - kt;  // real stages issued after kt (at most two)
-    wait_vm_n(ahead >= 2 ? 2 * ops_wave : (ahead == 1 ? ops_wave : 0));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -376,105 +352,112 @@ __global__ __launch_bounds__(64 * NW) void grouped_gemm_kernel(GemmArgs a) {
 #endif
   };
 
-  // MFMAs of stage kt from one buffer set; for blockwise, PH is the stage's
-  // position in its 128-block (0: start the partial, 1: finish and promote)
+  // the 2 x MI x NI MFMAs of stage kt from one buffer set
   auto compute_stage = [&](const uint8_t *as, const uint8_t *bs, const float *sa_l, const float *sb_l,
-                           const uint32_t *ma, const uint32_t *mb, int kt, auto ph) {
-    constexpr int PH = decltype(ph)::value;
-    v8i af[MI], bf[NI];
+                           const uint32_t *ma, const uint32_t *mb, int kt) {
+    v8i af[2][MI], bf[2][NI];
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) af[mi] = frag(as, wi * 128 + mi * 32 + l32, h);
+    for (int s = 0; s < 2; ++s) {
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni) bf[ni] = frag(bs, wj * WN + ni * 32 + l32, h);
-    if (!BLK) {
+      for (int mi = 0; mi < MI; ++mi) af[s][mi] = frag(as, wi * 128 + mi * 32 + l32, 4 * s + h);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) bf[s][ni] = frag(bs, wj * WN + ni * 32 + l32, 4 * s + h);
+    }
+    int sa_w[MI], sb_w[NI];
+    if (MX) {
+      // lane half h takes byte 2s + h of the row's word: shift by 8h, opsel 2s
+      const uint4 wa = *reinterpret_cast<const uint4 *>(&ma[(wi * 32 + l32) * 4]);
+      const uint4 wb = *reinterpret_cast<const uint4 *>(&mb[(wj * 32 + l32) * 4]);
+      const uint32_t wav[4] = {wa.x, wa.y, wa.z, wa.w}, wbv[4] = {wb.x, wb.y, wb.z, wb.w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        sa_w[m] = (int)(wav[m] >> (8 * h));
+        sb_w[m] = (int)(wbv[m] >> (8 * h));
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
           if (MX) {
-            // the word holds blocks 2(kt&~1) .. +3; this stage's are bytes
-            // 2*PH and 2*PH+1; lane half h takes byte 2*PH + h (opsel 2*PH
-            // after a per-lane shift by 8h)
-            const int sa_w = (int)(ma[wi * 128 + mi * 32 + l32] >> (8 * h));
-            const int sb_w = (int)(mb[wj * WN + ni * 32 + l32] >> (8 * h));
-            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                af[mi], bf[ni], acc[mi][ni], FA, FB, 2 * PH, sa_w, 2 * PH, sb_w);
+            if (s == 0)
+              acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  af[0][mi], bf[0][ni], acc[mi][ni], FA, FB, 0, sa_w[mi], 0, sb_w[ni]);
+            else
+              acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  af[1][mi], bf[1][ni], acc[mi][ni], FA, FB, 2, sa_w[mi], 2, sb_w[ni]);
+          } else if (BLK) {
+            if (s == 0) {
+              v16f z;
+#pragma unroll
+              for (int v = 0; v < 16; ++v) z[v] = 0.0f;
+              part[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  af[0][mi], bf[0][ni], z, FA, FB, 0, kUnitScale, 0, kUnitScale);
+            } else {
+              part[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  af[1][mi], bf[1][ni], part[mi][ni], FA, FB, 0, kUnitScale, 0, kUnitScale);
+            }
           } else {
             // unit E8M0 scales (127 = 2^0); the scaled form keeps the
             // accumulators in AGPRs
             acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                af[mi], bf[ni], acc[mi][ni], FA, FB, 0, kUnitScale, 0, kUnitScale);
+                af[s][mi], bf[s][ni], acc[mi][ni], FA, FB, 0, kUnitScale, 0, kUnitScale);
           }
         }
-    } else {
+    }
+    if (!BLK) {
+      // instruction order: the first half's fragment reads (and MX words),
+      // then the second half's reads one after each of the first half's
+      // MFMAs, then the second half's MFMAs
+      constexpr int RD = 2 * (MI + NI);  // ds_read_b128 per half
+      __builtin_amdgcn_sched_group_barrier(0x100, RD + (MX ? 2 : 0), 0);
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+      for (int i = 0; i < MI * NI; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, MI * NI, 0);
+    }
+    if (BLK) {
+      // promote: acc += partial * sA(row) * sB; sB per column for wgrad,
+      // one value per tile (the 128x128 weight tile) otherwise
+      const float sbw = MODE == kWgrad ? 0.0f : sbtab[kt & (SB_TAB - 1)];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        float sa[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 v4 = *reinterpret_cast<const float4 *>(&sa_l[wi * 128 + mi * 32 + q * 8 + h * 4]);
+          sa[q * 4 + 0] = v4.x;
+          sa[q * 4 + 1] = v4.y;
+          sa[q * 4 + 2] = v4.z;
+          sa[q * 4 + 3] = v4.w;
+        }
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
-          if (PH == 0) {
-            v16f z;
+          const float sbj = MODE == kWgrad ? sb_l[wj * WN + ni * 32 + l32] : sbw;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) z[v] = 0.0f;
-            part[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                af[mi], bf[ni], z, FA, FB, 0, kUnitScale, 0, kUnitScale);
-          } else {
-            part[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                af[mi], bf[ni], part[mi][ni], FA, FB, 0, kUnitScale, 0, kUnitScale);
-          }
-        }
-      if (PH == 1) {
-        // promote: acc += partial * sA(row) * sB; sB per column for wgrad,
-        // one value per tile (the 128x128 weight tile) otherwise
-        const float sbw = MODE == kWgrad ? 0.0f : sbtab[(kt >> 1) & (SB_TAB - 1)];
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi) {
-          float sa[16];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float4 v4 = *reinterpret_cast<const float4 *>(&sa_l[wi * 128 + mi * 32 + q * 8 + h * 4]);
-            sa[q * 4 + 0] = v4.x;
-            sa[q * 4 + 1] = v4.y;
-            sa[q * 4 + 2] = v4.z;
-            sa[q * 4 + 3] = v4.w;
-          }
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni) {
-            const float sbj = MODE == kWgrad ? sb_l[wj * WN + ni * 32 + l32] : sbw;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[mi][ni][v] += part[mi][ni][v] * (sa[v] * sbj);
-          }
+          for (int v = 0; v < 16; ++v) acc[mi][ni][v] += part[mi][ni][v] * (sa[v] * sbj);
         }
       }
     }
   };
 
-  // ---- main loop: a ring of four stage buffers; stage kt lives in buffer
-  // kt % 4 and its copies are issued three stages ahead. The stage count is
+  // ---- main loop: two stage buffers; stage kt lives in buffer kt % 2 and
+  // its copies are issued at the start of stage kt - 1. The stage count is
   // rounded up to whole turns of the ring with zero-filled stages, so the
-  // loop body (four stages) has no conditional MFMAs.
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
-  if (vsteps > 0) {
-    load_stage(0, As0, Bs0, sA0, sB0, mA0, mB0);
-    load_stage(1, As1, Bs1, sA1, sB1, mA1, mB1);
-    load_stage(2, As2, Bs2, sA2, sB2, mA2, mB2);
-  }
-  for (int kt = 0; kt < vsteps; kt += 4) {
-    stage_ready(kt);
-    load_stage(kt + 3, As3, Bs3, sA3, sB3, mA3, mB3);
-    compute_stage(As0, Bs0, sA0, sB0, mA0, mB0, kt, P0{});
+  // loop body (two stages) has no conditional MFMAs.
+  if (vsteps > 0) load_stage(0, As0, Bs0, sA0, sB0, mA0, mB0);
+  for (int kt = 0; kt < vsteps; kt += 2) {
+    stage_ready();
+    load_stage(kt + 1, As1, Bs1, sA1, sB1, mA1, mB1);
+    compute_stage(As0, Bs0, sA0, sB0, mA0, mB0, kt);
     pin_acc();
-    stage_ready(kt + 1);
-    if (kt + 4 < vsteps) load_stage(kt + 4, As0, Bs0, sA0, sB0, mA0, mB0);
-    compute_stage(As1, Bs1, sA1, sB1, mA1, mB1, kt + 1, P1{});
-    pin_acc();
-    stage_ready(kt + 2);
-    if (kt + 5 < vsteps) load_stage(kt + 5, As1, Bs1, sA1, sB1, mA1, mB1);
-    compute_stage(As2, Bs2, sA2, sB2, mA2, mB2, kt + 2, P0{});
-    pin_acc();
-    stage_ready(kt + 3);
-    if (kt + 6 < vsteps) load_stage(kt + 6, As2, Bs2, sA2, sB2, mA2, mB2);
-    compute_stage(As3, Bs3, sA3, sB3, mA3, mB3, kt + 3, P1{});
+    stage_ready();
+    if (kt + 2 < vsteps) load_stage(kt + 2, As0, Bs0, sA0, sB0, mA0, mB0);
+    compute_stage(As1, Bs1, sA1, sB1, mA1, mB1, kt + 1);
     pin_acc();
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -493,8 +476,7 @@ __global__ __launch_bounds__(64 * NW) void grouped_gemm_kernel(GemmArgs a) {
   constexpr int STR = WN + 8;          // LDS row stride in floats
   constexpr int CPR = WN / 8;          // 8-float chunks per row
   constexpr int CPL = 16 * CPR / 64;   // chunks per lane per half slab
-  uint8_t *creg = wave == 0 ? As0 : wave == 1 ? As1 : wave == 2 ? As2 : wave == 3 ? As3
-                : wave == 4 ? Bs0 : wave == 5 ? Bs1 : wave == 6 ? Bs2 : Bs3;
+  uint8_t *creg = wave == 0 ? As0 : wave == 1 ? As1 : wave == 2 ? Bs0 : Bs1;
   float *cb = reinterpret_cast<float *>(creg);
   const int64_t jw = j0 + wj * WN;
 #pragma unroll
@@ -548,7 +530,6 @@ __global__ __launch_bounds__(64 * NW) void grouped_gemm_kernel(GemmArgs a) {
 template <int MODE, int RECIPE, int FA, int FB>
 static hipError_t launch_cfg(const GemmArgs &a0, hipStream_t st) {
   constexpr int BN = RECIPE == kBlockwise ? 128 : 256;
-  constexpr int NW = MXSG_GEMM_WAVES;
   GemmArgs a = a0;
   a.jtiles = (int)((a.J + BN - 1) / BN);
   int64_t nblocks;
@@ -561,7 +542,7 @@ static hipError_t launch_cfg(const GemmArgs &a0, hipStream_t st) {
   }
   if (nblocks == 0) return hipSuccess;
   if (nblocks > 0x7fffffff) return hipErrorInvalidValue;
-  grouped_gemm_kernel<MODE, RECIPE, FA, FB, BN, NW><<<(unsigned)nblocks, 64 * NW, 0, st>>>(a);
+  grouped_gemm_kernel<MODE, RECIPE, FA, FB, BN><<<(unsigned)nblocks, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
