@@ -43,6 +43,17 @@
  *    amax); amax == 0 gives s = inv = 1. fmax = 448 (e4m3), 57344 (e5m2).
  *    MX: E8M0 code k+127 with k the smallest integer such that amax <=
  *    fmax * 2^k (clamped to [-127, 127]; 0 for amax == 0), inv = 2^-k.
+ *  - Code matrices are pair-interleaved: a matrix of R rows of L code bytes
+ *    (L a multiple of 64) stores byte (r, l) at offset
+ *      (r / 2) * 2L + (l / 64) * 128 + (r % 2) * 64 + (l % 64),
+ *    i.e. rows 2p and 2p+1 share 2L bytes as 128-byte lines that each hold
+ *    64 bytes of row 2p followed by the same 64 bytes of row 2p+1. R is
+ *    rounded up to even: a buffer holds 2 * ceil(R / 2) rows; for odd R the
+ *    last row of the last pair is not written and never reaches a result.
+ *    This holds for row-wise token codes [M, C], column-wise codes [C, ld]
+ *    and each expert's weight codes ([N, K] k-major, [K, N] n-major). The
+ *    grouped GEMM reads a 64-byte contraction slice of a run of row pairs
+ *    as whole 128-byte lines.
  *  - Column-wise (transposed) token layout, the wgrad operand: codes
  *    [C, ld] where group g's tokens sit at columns [P_g, P_g + m_g),
  *    P_0 = 0, P_{g+1} = P_g + ceil(m_g / 128) * 128, and columns
@@ -114,8 +125,10 @@ int64_t mxsg_padded_capacity(int64_t M, int32_t E);
  *  recipe MX: row_scales uint8 [M, C/32]; col_scales uint8 [C, ld/32]; a
  *    32-block made only of padding gets code 127.
  *
- *  row_codes uint8 [M, C] (NULL: no row-wise output).
- *  col_codes uint8 [C, ld] (NULL: no column-wise output). When given, E >= 1,
+ *  row_codes uint8 [2 * ceil(M/2), C], pair-interleaved (NULL: no row-wise
+ *    output).
+ *  col_codes uint8 [C, ld], pair-interleaved (NULL: no column-wise output).
+ *    When given, E >= 1,
  *    group_ends and padded_starts (int32 [E+1], receives P_0..P_E) are required.
  *  At least one of row_codes / col_codes must be non-NULL.
  */
@@ -169,10 +182,12 @@ mxsg_status mxsg_delayed_update(float *history, int32_t *pos, float *amax, float
  * accumulation. C[i, j] = sum_l A[i, l] * B[j, l]: both code operands are
  * contiguous along the contraction index l.
  *
- *  FWD:   A = row-wise codes of x  [M, K] (row stride lda >= K),
- *         B = k-major weight codes [E, N, K] (row stride ldb = K),
+ *  Code operands are pair-interleaved (see Layouts) with row length lda
+ *  resp. ldb; A of FWD / DGRAD holds 2 * ceil(M/2) rows.
+ *  FWD:   A = row-wise codes of x  [M, K] (row length lda >= K, a multiple
+ *         of 64), B = k-major weight codes [E, N, K] (ldb = K),
  *         out = Y bf16 [M, N] (row stride N).
- *  DGRAD: A = row-wise codes of dY [M, N] (lda >= N),
+ *  DGRAD: A = row-wise codes of dY [M, N] (lda >= N, a multiple of 64),
  *         B = n-major weight codes [E, K, N] (ldb = N),
  *         out = dA bf16 [M, K] (row stride K).
  *  WGRAD: A = column-wise codes of x  [K, lda], B = column-wise codes of dY

@@ -54,6 +54,31 @@ def padded_capacity(M: int, E: int) -> int:
     return int(_lib.load().mxsg_padded_capacity(M, E))
 
 
+def unpack_codes(t: torch.Tensor, rows: Optional[int] = None) -> torch.Tensor:
+    """Row-major copy [..., rows, L] of pair-interleaved codes [..., Rp, L].
+
+    The library stores every code matrix pair-interleaved: rows 2p and 2p+1
+    share 2L bytes as 128-byte lines, each 64 bytes of row 2p followed by the
+    same 64 bytes of row 2p+1 (mxsg.h, Layouts)."""
+    *lead, rp, L = t.shape
+    if rp % 2 or L % 64:
+        raise ValueError(f"pair-interleaved codes need an even row count and L % 64 == 0, got {tuple(t.shape)}")
+    u = t.reshape(*lead, rp // 2, L // 64, 2, 64).transpose(-3, -2).reshape(*lead, rp, L)
+    return u if rows is None else u[..., :rows, :]
+
+
+def pack_codes(t: torch.Tensor) -> torch.Tensor:
+    """Pair-interleaved copy of row-major codes [..., R, L] (R rounded up to
+    even with a zero row)."""
+    *lead, r, L = t.shape
+    if L % 64:
+        raise ValueError(f"row length {L} is not a multiple of 64")
+    if r % 2:
+        t = torch.cat([t, t.new_zeros(*lead, 1, L)], dim=-2)
+        r += 1
+    return t.reshape(*lead, r // 2, 2, L // 64, 64).transpose(-3, -2).reshape(*lead, r, L).contiguous()
+
+
 def _scale_blocks(recipe: str) -> int:
     return {"block": 128, "mx": 32}.get(recipe, 0)
 
@@ -101,9 +126,9 @@ class QuantAct:
     fmt: int
     M: int
     C: int
-    row_codes: Optional[torch.Tensor] = None     # uint8 [M, C]
+    row_codes: Optional[torch.Tensor] = None     # uint8 [M + M % 2, C], pair-interleaved
     row_scales: Optional[torch.Tensor] = None
-    col_codes: Optional[torch.Tensor] = None     # uint8 [C, ld]
+    col_codes: Optional[torch.Tensor] = None     # uint8 [C, ld], pair-interleaved
     col_scales: Optional[torch.Tensor] = None
     padded_starts: Optional[torch.Tensor] = None  # int32 [E+1]
     amax: Optional[torch.Tensor] = None
@@ -132,7 +157,7 @@ def quantize_act(x: torch.Tensor, recipe: str, fmt, group_ends: Optional[torch.T
         q = QuantAct(recipe, f, M, C)
         sdt = torch.uint8 if recipe == "mx" else torch.float32
         if rowwise:
-            q.row_codes = torch.empty(M, C, dtype=torch.uint8, device=dev)
+            q.row_codes = torch.empty(M + (M & 1), C, dtype=torch.uint8, device=dev)
             q.row_scales = (torch.empty(M, C // blk, dtype=sdt, device=dev) if blk
                             else torch.empty(1, dtype=torch.float32, device=dev))
         if colwise:
@@ -166,9 +191,9 @@ class QuantWeight:
     E: int
     K: int
     N: int
-    kmajor_codes: Optional[torch.Tensor] = None   # uint8 [E, N, K]  (forward operand)
+    kmajor_codes: Optional[torch.Tensor] = None   # uint8 [E, N, K]  (forward operand, pair-interleaved)
     kmajor_scales: Optional[torch.Tensor] = None
-    nmajor_codes: Optional[torch.Tensor] = None   # uint8 [E, K, N]  (dgrad operand)
+    nmajor_codes: Optional[torch.Tensor] = None   # uint8 [E, K, N]  (dgrad operand, pair-interleaved)
     nmajor_scales: Optional[torch.Tensor] = None
     amax: Optional[torch.Tensor] = None
 

@@ -147,4 +147,13 @@ __device__ __forceinline__ void group_bounds(const int32_t *__restrict__ ends, i
   hi = b < a ? a : b;
 }
 
+// Byte offset of code (r, l) in a pair-interleaved code matrix with rows of
+// L bytes (L a multiple of 64): rows 2p and 2p+1 share 2L bytes, as lines of
+// 128 bytes that each hold 64 bytes of row 2p followed by the same 64 bytes
+// of row 2p+1. A GEMM stage of 64 contraction bytes over an even run of rows
+// is then whole 128-byte lines.
+__device__ __forceinline__ int64_t pi_off(int64_t r, int64_t l, int64_t L) {
+  return (r >> 1) * (2 * L) + ((l >> 6) << 7) + ((r & 1) << 6) + (l & 63);
+}
+
 }  // namespace mxsg

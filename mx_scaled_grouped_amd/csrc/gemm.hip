@@ -11,16 +11,20 @@
 //
 // gfx950 design: a 256-thread workgroup (4 waves, 2 x 2) computes a
 // 256 x BN output tile; each wave owns 128 x BN/2 as 4 x (BN/64) MFMA
-// 32x32x64 FP8 sub-tiles (v_mfma_[scale_]f32_32x32x64_f8f6f4). The
-// contraction runs in 128-wide stages: global -> LDS (XOR-swizzled 16-byte
-// chunks so the 32-row fragment reads are bank-conflict free) -> MFMA,
-// with the global -> LDS copies done by global_load_lds_dwordx4 (no
-// staging registers), double buffered one stage ahead.
-// Tiles never straddle expert groups; a workgroup finds its group from the
-// device-resident offsets (no host sync). Workgroup ids are remapped so
+// 32x32x64 FP8 sub-tiles (v_mfma_scale_f32_32x32x64_f8f6f4). The
+// contraction runs in 64-wide stages through a ring of four LDS buffers:
+// global_load_lds_dwordx4 copies (no staging registers) land XOR-swizzled
+// 16-byte chunks (bank-conflict-free fragment reads) three stages ahead of
+// use. The code operands are pair-interleaved, so a stage of 64 bytes over
+// a run of row pairs is whole 128-byte lines. While a stage's MFMAs run,
+// the next stage's fragments are read into a second register set.
+// Tiles never straddle expert groups (row tiles start at a group's first
+// row pair; rows of a neighbouring group in the tile are computed and not
+// stored); a workgroup finds its group from the device-resident offsets
+// (no host sync). Workgroup ids are remapped so
 // each XCD (and its L2) works on a contiguous run of tiles.
 // Scales: tensorwise / delayed in the epilogue (acc * sA * sB); blockwise
-// by promoting each 128-long stage's fp32 partial with sA * sB; MX inside
+// by promoting each 128-long block's fp32 partial with sA * sB; MX inside
 // the MFMA through its per-32-element E8M0 scale operands.
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -33,8 +37,8 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int GBM = 256;   // tile rows (i)
-constexpr int GBK = 128;   // contraction per stage (bytes of codes: one 128-byte row piece)
-constexpr int SBLK = 128;  // blockwise scaling block along the contraction (one stage)
+constexpr int GBK = 64;    // contraction per stage (bytes of codes: one 128-byte line of a row pair)
+constexpr int SBLK = 128;  // blockwise scaling block along the contraction (two stages)
 constexpr int SB_TAB = 512; // blockwise FWD / DGRAD: contraction blocks per tile (L <= 65536)
 constexpr int kUnitScale = 127;  // E8M0 code of 1.0
 
@@ -85,12 +89,15 @@ __device__ __forceinline__ void raster(int lid, int itiles, int jtiles, int &it,
   jt = r / gm;
 }
 
-// FWD / DGRAD: find the group and first row of i-tile `slot` (tiles of GBM
-// rows, each group starting a new tile). Returns false past the last tile.
-__device__ bool locate_row_tile(const GemmArgs &a, int slot, int &g_out, int64_t &i0,
-                                int64_t &ilim) {
+// FWD / DGRAD: find the group and rows of i-tile `slot`. Row tiles lie on
+// the grid of row pairs (the codes are pair-interleaved): group g with rows
+// [lo, hi) covers pairs [lo/2, (hi+1)/2), cut into tiles of GBM/2 pairs. The
+// tile starts at the even row e0; its valid output rows are [ilo, ihi).
+// Returns false past the last tile.
+__device__ bool locate_row_tile(const GemmArgs &a, int slot, int &g_out, int64_t &e0,
+                                int64_t &ilo, int64_t &ihi) {
   __shared__ int s_g, s_found;
-  __shared__ int64_t s_i0, s_ilim;
+  __shared__ int64_t s_e0, s_lo, s_hi;
   if (threadIdx.x == 0) s_found = 0;
   __syncthreads();
   if (threadIdx.x < 64) {
@@ -100,7 +107,8 @@ __device__ bool locate_row_tile(const GemmArgs &a, int slot, int &g_out, int64_t
       const int g = g0 + lane;
       int64_t lo = 0, hi = 0;
       if (g < a.E) group_bounds(a.ends, g, a.M, lo, hi);
-      const int64_t nt = (hi - lo + GBM - 1) / GBM;
+      const int64_t ps = lo >> 1, pe = (hi + 1) >> 1;
+      const int64_t nt = hi > lo ? (pe - ps + GBM / 2 - 1) / (GBM / 2) : 0;
       int64_t incl = nt;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -109,9 +117,11 @@ __device__ bool locate_row_tile(const GemmArgs &a, int slot, int &g_out, int64_t
       }
       const int64_t first = base + incl - nt;
       if (g < a.E && slot >= first && slot < first + nt) {
+        const int64_t t0 = 2 * (ps + (int64_t)(slot - first) * (GBM / 2));
         s_g = g;
-        s_i0 = lo + (int64_t)(slot - first) * GBM;
-        s_ilim = hi;
+        s_e0 = t0;
+        s_lo = lo > t0 ? lo : t0;
+        s_hi = hi < t0 + GBM ? hi : t0 + GBM;
         s_found = 1;
       }
       base += __shfl(incl, 63, 64);
@@ -119,21 +129,22 @@ __device__ bool locate_row_tile(const GemmArgs &a, int slot, int &g_out, int64_t
   }
   __syncthreads();
   g_out = s_g;
-  i0 = s_i0;
-  ilim = s_ilim;
+  e0 = s_e0;
+  ilo = s_lo;
+  ihi = s_hi;
   return s_found != 0;
 }
 
-// LDS stage tiles hold rows of GBK = 128 code bytes as eight 16-byte chunks;
-// chunk c of row r sits at chunk c ^ ((r >> 1) & 7), so the eight lanes a
-// fragment read serves per LDS cycle (eight consecutive rows, one chunk
-// index) hit eight different 16-byte bank groups.
-__device__ __forceinline__ int swz(int row, int ch) { return row * GBK + ((ch ^ ((row >> 1) & 7)) << 4); }
+// LDS stage tiles hold rows of GBK = 64 code bytes as four 16-byte chunks;
+// chunk c of row r sits at chunk c ^ ((r >> 2) & 3), so the lanes of a
+// fragment read that share a bank sweep (rows r, r+4, r+8, r+12) hit
+// different banks.
+__device__ __forceinline__ int swz(int row, int ch) { return row * GBK + ((ch ^ ((row >> 2) & 3)) << 4); }
 
 // Direct global -> LDS copies (global_load_lds_dwordx4 / _dword): lane L of
 // the wave lands at lds + 16 L (or 4 L); M0 holds the LDS byte address.
 // Issued through inline asm, so the compiler inserts no waits for them: the
-// main loop waits for them itself (vmcnt) before each stage's barrier.
+// main loop counts them itself (vmcnt) before each stage's barrier.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
@@ -144,17 +155,40 @@ __device__ __forceinline__ void dma4(const void *src, void *lds) {
   asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds_addr(lds)) : "memory");
 }
 
-// MFMA 32x32x64 f8 operand for one lane and 64-deep half s of the stage:
-// the lane's row, and (measured lane layout) bytes 0-15 = k in [16h, 16h+16)
-// of the half's first 32-block, bytes 16-31 = k in [32+16h, 48+16h) of its
-// second, h = the lane's half of the wave; i.e. 16-byte chunks 4s + h and
-// 4s + 2 + h of the 128-byte stage row. The scale operand of lane i + 32b
-// covers row i and 32-block b.
-__device__ __forceinline__ v8i frag(const uint8_t *buf, int row, int c) {
-  const uint4 x0 = *reinterpret_cast<const uint4 *>(&buf[swz(row, c)]);
-  const uint4 x1 = *reinterpret_cast<const uint4 *>(&buf[swz(row, c + 2)]);
+// MFMA 32x32x64 f8 operand for one lane: the lane's row, and (measured lane
+// layout) bytes 0-15 = k in [16h, 16h+16) of the first 32-block, bytes
+// 16-31 = k in [32+16h, 48+16h) of the second, h = the lane's half of the
+// wave; i.e. 16-byte chunks h and 2 + h of the 64-wide stage row. The scale
+// operand of lane i + 32b covers row i and 32-block b.
+__device__ __forceinline__ v8i frag(const uint8_t *buf, int row, int h) {
+  const uint4 x0 = *reinterpret_cast<const uint4 *>(&buf[swz(row, h)]);
+  const uint4 x1 = *reinterpret_cast<const uint4 *>(&buf[swz(row, 2 + h)]);
   return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
 }
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 24]
+__device__ __forceinline__ void wait_vm_n(int n) {
+  switch (n) {
+#define MXSG_VMW(k) case k: wait_vm<k>(); break;
+    MXSG_VMW(1) MXSG_VMW(2) MXSG_VMW(3) MXSG_VMW(4) MXSG_VMW(5) MXSG_VMW(6) MXSG_VMW(7) MXSG_VMW(8)
+    MXSG_VMW(9) MXSG_VMW(10) MXSG_VMW(11) MXSG_VMW(12) MXSG_VMW(13) MXSG_VMW(14) MXSG_VMW(15)
+    MXSG_VMW(16) MXSG_VMW(17) MXSG_VMW(18) MXSG_VMW(19) MXSG_VMW(20) MXSG_VMW(21) MXSG_VMW(22)
+    MXSG_VMW(23) MXSG_VMW(24)
+#undef MXSG_VMW
+    default: wait_vm<0>(); break;
+  }
+}
+
+// one stage's operands of one lane, in registers
+template <int MI, int NI>
+struct Frags {
+  v8i a[MI], b[NI];
+  int sa[MI], sb[NI];  // MX: the rows' E8M0 words, shifted to this lane's half
+};
 
 template <int MODE, int RECIPE, int FA, int FB, int BN>
 __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
@@ -162,24 +196,28 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
   constexpr int WN = BN / 2;         // wave tile width along j
   constexpr int NI = WN / 32;        // 32-wide sub-tiles along j per wave
   constexpr int MI = 4;              // 32-high sub-tiles along i per wave (128 rows)
-  constexpr int AQ = GBM / 8 / 4;    // 8-row copy groups (1 KB) of A per wave per stage
-  constexpr int BQ = BN / 8 / 4;     // of B
+  constexpr int AQ = GBM / 16 / 4;   // 1 KB copy groups (8 row pairs) of A per wave per stage
+  constexpr int BQ = BN / 16 / 4;    // of B
   constexpr bool BLK = RECIPE == kBlockwise;
   constexpr bool MX = RECIPE == kMx;
+  // the next stage's fragments are read during this stage's MFMAs (two
+  // register sets); blockwise keeps its registers for the partial sums
+  constexpr bool PREF = !BLK;
   static_assert(AQ >= 1 && BQ >= 1 && NI >= 1, "tile shape");
+  static_assert(!MX || (MI == 4 && NI == 4 && BN == 256), "MX word layout");
 
-  // two stage buffers of A and B as distinct objects: the compiler then
-  // knows the copies into one buffer do not alias the reads of the other
-  __shared__ __attribute__((aligned(1024))) uint8_t As0[GBM * GBK], As1[GBM * GBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t Bs0[BN * GBK], Bs1[BN * GBK];
-  // blockwise: per-row scales of the stage's 128-block (A rows; B rows for wgrad)
-  __shared__ __attribute__((aligned(16))) float sA0[BLK ? GBM : 4], sA1[BLK ? GBM : 4];
-  __shared__ __attribute__((aligned(16))) float sB0[BLK ? BN : 4], sB1[BLK ? BN : 4];
+  // four stage buffers of A and B as distinct objects: the compiler then
+  // knows the copies into one buffer do not alias the reads of another
+  __shared__ __attribute__((aligned(1024))) uint8_t As0[GBM * GBK], As1[GBM * GBK], As2[GBM * GBK], As3[GBM * GBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t Bs0[BN * GBK], Bs1[BN * GBK], Bs2[BN * GBK], Bs3[BN * GBK];
+  __shared__ __attribute__((aligned(16))) float sA0[BLK ? GBM : 4], sA1[BLK ? GBM : 4], sA2[BLK ? GBM : 4], sA3[BLK ? GBM : 4];
+  __shared__ __attribute__((aligned(16))) float sB0[BLK ? BN : 4], sB1[BLK ? BN : 4], sB2[BLK ? BN : 4], sB3[BLK ? BN : 4];
   __shared__ float sbtab[BLK ? SB_TAB : 1];  // blockwise weight scales of this tile's j-block, per l-block
-  // MX: per stage buffer, each tile row's E8M0 word (the four 32-blocks of
-  // the stage), stored so the four words one lane needs are contiguous
-  __shared__ __attribute__((aligned(16))) uint32_t mA0[MX ? GBM : 4], mA1[MX ? GBM : 4];
-  __shared__ __attribute__((aligned(16))) uint32_t mB0[MX ? BN : 4], mB1[MX ? BN : 4];
+  // MX: per stage buffer, each tile row's E8M0 word (the 32-blocks 4w..4w+3
+  // holding the stage's two), stored so the four words one lane needs are
+  // contiguous: slot d holds tile row 128 (d / 128) + 32 (d % 4) + (d / 4) % 32
+  __shared__ __attribute__((aligned(16))) uint32_t mA0[MX ? GBM : 4], mA1[MX ? GBM : 4], mA2[MX ? GBM : 4], mA3[MX ? GBM : 4];
+  __shared__ __attribute__((aligned(16))) uint32_t mB0[MX ? BN : 4], mB1[MX ? BN : 4], mB2[MX ? BN : 4], mB3[MX ? BN : 4];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -187,10 +225,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
   const int wi = wave >> 1, wj = wave & 1;
   const int h = lane >> 5, l32 = lane & 31;
 
-  // ---- tile coordinates
+  // ---- tile coordinates: rows [i0, i0 + GBM) of the tile (i0 even), valid
+  // output rows [ilo, ihi); columns [j0, j0 + BN); contraction from l0
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   int g = 0;
-  int64_t i0 = 0, ilim = 0, j0 = 0, l0 = 0;
+  int64_t i0 = 0, ilo = 0, ihi = 0, j0 = 0, l0 = 0;
   int nsteps = 0;
   if (MODE == kWgrad) {
     const int per_g = a.slots * a.jtiles;
@@ -199,50 +238,61 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
     raster(lid - g * per_g, a.slots, a.jtiles, it, jt);
     i0 = (int64_t)it * GBM;
     j0 = (int64_t)jt * BN;
-    ilim = a.I;
+    ilo = i0;
+    ihi = a.I < i0 + GBM ? a.I : i0 + GBM;
     int64_t p_lo = a.pstarts[g], p_hi = a.pstarts[g + 1];
     const int64_t cap = a.lda < a.ldb ? a.lda : a.ldb;
     p_lo = p_lo < 0 ? 0 : (p_lo > cap ? cap : p_lo);
     p_hi = p_hi < p_lo ? p_lo : (p_hi > cap ? cap : p_hi);
     l0 = p_lo & ~(int64_t)127;                       // padded starts are 128-aligned
-    nsteps = (int)((p_hi - l0) / GBK);
+    nsteps = (int)(((p_hi - l0) / 128) * (128 / GBK));
   } else {
     int slot, jt;
     raster(lid, a.slots, a.jtiles, slot, jt);
     j0 = (int64_t)jt * BN;
-    if (!locate_row_tile(a, slot, g, i0, ilim)) return;
+    if (!locate_row_tile(a, slot, g, i0, ilo, ihi)) return;
     l0 = 0;
     nsteps = (int)(a.L / GBK);
   }
-  const int vsteps = (nsteps + 1) & ~1;  // stages rounded up to whole turns of the two-buffer ring
+  const int vsteps = (nsteps + 3) & ~3;  // stages rounded up to whole ring turns
 
   // scale-row strides: FWD / DGRAD scales are [rows, L/blk]; WGRAD scales
   // follow the padded column layout, [rows, ld/blk]
   const int64_t sa_row = MODE == kWgrad ? a.lda : a.L;
   const int64_t sb_row = MODE == kWgrad ? a.ldb : a.L;
 
-  // ---- per-lane byte offsets of the 16-byte chunks this lane copies, relative
-  // to the tile base; rows past the valid range re-read the last valid row.
-  // Copy group q of a wave is 8 rows x 128 bytes; lane L takes row L / 8 of
-  // it and lands at LDS chunk L % 8, so it reads the global chunk that the
-  // swizzle puts there.
-  const uint8_t *abase = a.a + i0 * a.lda + l0;
-  const uint8_t *bbase = a.b + (MODE == kWgrad ? 0 : (int64_t)g * a.b_gstride) + j0 * a.ldb + l0;
-  const int imax = (int)((ilim - i0) < GBM ? (ilim - i0) : GBM) - 1;
-  const int jmax = (int)((a.J - j0) < BN ? (a.J - j0) : BN) - 1;
+  // ---- per-lane byte offsets of the 16-byte chunks this lane copies. Copy
+  // group q of a wave is 8 row pairs (16 rows of the stage tile): lane L
+  // takes tile row 16q' + L / 4 and lands at its LDS chunk L % 4, so it
+  // reads the global chunk that the swizzle puts there. Pairs past the last
+  // valid one re-read the last valid pair.
+  const int64_t lb = l0 / GBK;   // first contraction line of the tile
+  const uint8_t *abase = a.a + (i0 >> 1) * 2 * a.lda + lb * 128;
+  const uint8_t *bbase = a.b + (MODE == kWgrad ? 0 : (int64_t)g * a.b_gstride) + (j0 >> 1) * 2 * a.ldb + lb * 128;
+  const int apmax = (int)(((ihi - 1) >> 1) - (i0 >> 1));   // last valid pair, tile-relative
+  const int64_t jlim = (a.J - j0) < BN ? (a.J - j0) : BN;
+  const int bpmax = (int)((jlim - 1) >> 1);
   uint32_t aoff[AQ], boff[BQ];
 #pragma unroll
   for (int q = 0; q < AQ; ++q) {
-    const int row = (wave * AQ + q) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((row >> 1) & 7);
-    aoff[q] = (uint32_t)((row < imax ? row : imax) * (int32_t)a.lda + c * 16);
+    const int row = (wave * AQ + q) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 2) & 3);
+    const int pr = (row >> 1) < apmax ? (row >> 1) : apmax;
+    aoff[q] = (uint32_t)(pr * 2 * (int32_t)a.lda + (row & 1) * 64 + c * 16);
   }
 #pragma unroll
   for (int q = 0; q < BQ; ++q) {
-    const int row = (wave * BQ + q) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((row >> 1) & 7);
-    boff[q] = (uint32_t)((row < jmax ? row : jmax) * (int32_t)a.ldb + c * 16);
+    const int row = (wave * BQ + q) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 2) & 3);
+    const int pr = (row >> 1) < bpmax ? (row >> 1) : bpmax;
+    boff[q] = (uint32_t)(pr * 2 * (int32_t)a.ldb + (row & 1) * 64 + c * 16);
   }
+  // valid-row clamps for the per-row scale copies
+  auto arow = [&](int r) -> int64_t {
+    const int64_t i = i0 + r;
+    return i < ilo ? ilo : (i >= ihi ? ihi - 1 : i);
+  };
+  auto brow = [&](int r) -> int64_t { return j0 + (r < jlim ? r : jlim - 1); };
 
   // blockwise: per-row A scales (and per-row B scales for wgrad) copied per
   // stage, wave w copying rows 64w..64w+63; the weight tile scales of the
@@ -251,31 +301,29 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
   const bool b_wave = wave < BN / 64;   // copies B-row scale words / scales
   if (BLK) {
     const int r = wave * 64 + lane;
-    sa_src = reinterpret_cast<const float *>(a.a_scales) + (i0 + (r < imax ? r : imax)) * (sa_row / SBLK) + l0 / SBLK;
+    sa_src = reinterpret_cast<const float *>(a.a_scales) + arow(r) * (sa_row / SBLK) + l0 / SBLK;
     if (MODE == kWgrad && b_wave)
-      sb_src = reinterpret_cast<const float *>(a.b_scales) + (j0 + (r < jmax ? r : jmax)) * (sb_row / SBLK) + l0 / SBLK;
+      sb_src = reinterpret_cast<const float *>(a.b_scales) + brow(r) * (sb_row / SBLK) + l0 / SBLK;
     if (MODE != kWgrad) {
       const int64_t jb = j0 / SBLK;
-      for (int lb = t; lb < nsteps && lb < SB_TAB; lb += NT)
-        sbtab[lb] = reinterpret_cast<const float *>(a.b_scales)[(int64_t)g * a.bs_gstride + lb * a.sb_l + jb * a.sb_j];
+      for (int lbk = t; lbk < nsteps / 2 && lbk < SB_TAB; lbk += NT)
+        sbtab[lbk] = reinterpret_cast<const float *>(a.b_scales)[(int64_t)g * a.bs_gstride + lbk * a.sb_l + jb * a.sb_j];
     }
   }
-
-  // MX scale words: the word of stage kt holds 32-blocks 4kt .. 4kt+3 of a
-  // row. Word slot d of the LDS array holds tile row
-  // 128 (d / 128) + 32 (d % 4) + (d / 4) % 32, so the lane (l32, wave row or
-  // column half w) that needs rows 128w + 32m + l32, m = 0..3, finds them in
-  // slots 4 (32w + l32) .. +3. Lane L of wave w copies slot 64w + L.
-  static_assert(!MX || (MI == 4 && NI == 4 && BN == 256), "MX word layout");
+  // MX scale words: lane L of wave w copies word slot d = 64w + L (see the
+  // slot layout above); the word of stage kt holds 32-blocks 4(kt/2) .. +3
   const uint8_t *mxa = nullptr, *mxb = nullptr;
   if (MX) {
     const int d = wave * 64 + lane;
     const int r = (d >> 7) * 128 + (d & 3) * 32 + ((d >> 2) & 31);
-    mxa = reinterpret_cast<const uint8_t *>(a.a_scales) + (i0 + (r < imax ? r : imax)) * (sa_row / 32) + l0 / 32;
+    mxa = reinterpret_cast<const uint8_t *>(a.a_scales) + arow(r) * (sa_row / 32) + l0 / 32;
     if (b_wave)
       mxb = reinterpret_cast<const uint8_t *>(a.b_scales) + (MODE == kWgrad ? 0 : (int64_t)g * a.bs_gstride) +
-            (j0 + (r < jmax ? r : jmax)) * (sb_row / 32) + l0 / 32;
+            brow(r) * (sb_row / 32) + l0 / 32;
   }
+  // vector-memory instructions this wave issues per real stage (the waits count them)
+  const int ops_wave = AQ + BQ + (MX ? 1 + (b_wave ? 1 : 0) : 0) + (BLK ? 1 + (MODE == kWgrad && b_wave ? 1 : 0) : 0);
+  auto ops = [&](int kt) { return kt < nsteps ? ops_wave : 0; };
   __syncthreads();  // sbtab visible
 
   v16f acc[MI][NI];
@@ -292,15 +340,15 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
                         uint32_t *mb) {
     if (kt < nsteps) {
       if (MX) {
-        dma4(mxa + kt * 4, ma + wave * 64);
-        if (b_wave) dma4(mxb + kt * 4, mb + wave * 64);
+        dma4(mxa + (kt >> 1) * 4, ma + wave * 64);
+        if (b_wave) dma4(mxb + (kt >> 1) * 4, mb + wave * 64);
       }
       if (BLK) {
-        dma4(sa_src + kt, sa + wave * 64);
-        if (MODE == kWgrad && b_wave) dma4(sb_src + kt, sb + wave * 64);
+        dma4(sa_src + (kt >> 1), sa + wave * 64);
+        if (MODE == kWgrad && b_wave) dma4(sb_src + (kt >> 1), sb + wave * 64);
       }
-      const uint8_t *ak = abase + kt * GBK;
-      const uint8_t *bk = bbase + kt * GBK;
+      const uint8_t *ak = abase + kt * 128;
+      const uint8_t *bk = bbase + kt * 128;
 #pragma unroll
       for (int q = 0; q < AQ; ++q) dma16(ak + aoff[q], as + (wave * AQ + q) * 1024);
 #pragma unroll
@@ -320,15 +368,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
         if (t < BN) mb[t] = 0x7f7f7f7fu;
       }
     }
-    __builtin_amdgcn_sched_barrier(0);  // the copies go out before the MFMAs that follow
+    __builtin_amdgcn_sched_barrier(0);  // the copies go out before what follows
   };
 
-  // wait until this wave's copies of the next stage (the only ones in
-  // flight) have landed, then synchronize the workgroup: after the barrier
-  // every wave's copies are visible and every wave is done with the other buffer
-  auto stage_ready = [&]() {
+  // wait until at most `pending` of this wave's copies are in flight (copies
+  // complete in issue order), then synchronize the workgroup
+  auto sync_stage = [&](int pending) {
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vm_n(pending);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -352,78 +399,59 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
 #endif
   };
 
-  // the 2 x MI x NI MFMAs of stage kt from one buffer set
-  auto compute_stage = [&](const uint8_t *as, const uint8_t *bs, const float *sa_l, const float *sb_l,
-                           const uint32_t *ma, const uint32_t *mb, int kt) {
-    v8i af[2][MI], bf[2][NI];
+  auto read_frags = [&](Frags<MI, NI> &f, const uint8_t *as, const uint8_t *bs, const uint32_t *ma,
+                        const uint32_t *mb) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int mi = 0; mi < MI; ++mi) f.a[mi] = frag(as, wi * 128 + mi * 32 + l32, h);
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) af[s][mi] = frag(as, wi * 128 + mi * 32 + l32, 4 * s + h);
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) bf[s][ni] = frag(bs, wj * WN + ni * 32 + l32, 4 * s + h);
-    }
-    int sa_w[MI], sb_w[NI];
+    for (int ni = 0; ni < NI; ++ni) f.b[ni] = frag(bs, wj * WN + ni * 32 + l32, h);
     if (MX) {
-      // lane half h takes byte 2s + h of the row's word: shift by 8h, opsel 2s
       const uint4 wa = *reinterpret_cast<const uint4 *>(&ma[(wi * 32 + l32) * 4]);
       const uint4 wb = *reinterpret_cast<const uint4 *>(&mb[(wj * 32 + l32) * 4]);
       const uint32_t wav[4] = {wa.x, wa.y, wa.z, wa.w}, wbv[4] = {wb.x, wb.y, wb.z, wb.w};
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        sa_w[m] = (int)(wav[m] >> (8 * h));
-        sb_w[m] = (int)(wbv[m] >> (8 * h));
+        f.sa[m] = (int)(wav[m] >> (8 * h));
+        f.sb[m] = (int)(wbv[m] >> (8 * h));
       }
     }
+  };
+
+  // the MI x NI MFMAs of stage kt; PH = the stage's position in its
+  // 128-block (MX: which two bytes of the scale word; blockwise: 0 starts
+  // the partial, 1 finishes and promotes it)
+  auto mfma_stage = [&](const Frags<MI, NI> &f, const float *sa_l, const float *sb_l, int kt, auto ph) {
+    constexpr int PH = decltype(ph)::value;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+      for (int ni = 0; ni < NI; ++ni) {
+        if (MX) {
+          // lane half h takes byte 2*PH + h of the row's word (shifted by 8h): opsel 2*PH
+          acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              f.a[mi], f.b[ni], acc[mi][ni], FA, FB, 2 * PH, f.sa[mi], 2 * PH, f.sb[ni]);
+        } else if (BLK) {
+          if (PH == 0) {
+            v16f z;
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          if (MX) {
-            if (s == 0)
-              acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  af[0][mi], bf[0][ni], acc[mi][ni], FA, FB, 0, sa_w[mi], 0, sb_w[ni]);
-            else
-              acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  af[1][mi], bf[1][ni], acc[mi][ni], FA, FB, 2, sa_w[mi], 2, sb_w[ni]);
-          } else if (BLK) {
-            if (s == 0) {
-              v16f z;
-#pragma unroll
-              for (int v = 0; v < 16; ++v) z[v] = 0.0f;
-              part[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  af[0][mi], bf[0][ni], z, FA, FB, 0, kUnitScale, 0, kUnitScale);
-            } else {
-              part[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  af[1][mi], bf[1][ni], part[mi][ni], FA, FB, 0, kUnitScale, 0, kUnitScale);
-            }
+            for (int v = 0; v < 16; ++v) z[v] = 0.0f;
+            part[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                f.a[mi], f.b[ni], z, FA, FB, 0, kUnitScale, 0, kUnitScale);
           } else {
-            // unit E8M0 scales (127 = 2^0); the scaled form keeps the
-            // accumulators in AGPRs
-            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                af[s][mi], bf[s][ni], acc[mi][ni], FA, FB, 0, kUnitScale, 0, kUnitScale);
+            part[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                f.a[mi], f.b[ni], part[mi][ni], FA, FB, 0, kUnitScale, 0, kUnitScale);
           }
+        } else {
+          // unit E8M0 scales (127 = 2^0); the scaled form keeps the
+          // accumulators in AGPRs
+          acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              f.a[mi], f.b[ni], acc[mi][ni], FA, FB, 0, kUnitScale, 0, kUnitScale);
         }
-    }
-    if (!BLK) {
-      // instruction order: the first half's fragment reads (and MX words),
-      // then the second half's reads one after each of the first half's
-      // MFMAs, then the second half's MFMAs
-      constexpr int RD = 2 * (MI + NI);  // ds_read_b128 per half
-      __builtin_amdgcn_sched_group_barrier(0x100, RD + (MX ? 2 : 0), 0);
-#pragma unroll
-      for (int i = 0; i < MI * NI; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, MI * NI, 0);
-    }
-    if (BLK) {
+    if (BLK && PH == 1) {
       // promote: acc += partial * sA(row) * sB; sB per column for wgrad,
       // one value per tile (the 128x128 weight tile) otherwise
-      const float sbw = MODE == kWgrad ? 0.0f : sbtab[kt & (SB_TAB - 1)];
+      const float sbw = MODE == kWgrad ? 0.0f : sbtab[(kt >> 1) & (SB_TAB - 1)];
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         float sa[16];
@@ -445,20 +473,76 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
     }
   };
 
-  // ---- main loop: two stage buffers; stage kt lives in buffer kt % 2 and
-  // its copies are issued at the start of stage kt - 1. The stage count is
+  // instruction order of a prefetching stage: one next-stage fragment read
+  // after each MFMA (then the MX word reads)
+  auto order_pref = [&]() {
+    constexpr int RD = 2 * (MI + NI);
+    static_assert(RD <= MI * NI || !PREF, "read/MFMA interleave");
+#pragma unroll
+    for (int i = 0; i < MI * NI; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if (MX) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  };
+
+  // ---- main loop: a ring of four stage buffers; stage kt lives in buffer
+  // kt % 4 and its copies are issued three stages ahead. The stage count is
   // rounded up to whole turns of the ring with zero-filled stages, so the
-  // loop body (two stages) has no conditional MFMAs.
-  if (vsteps > 0) load_stage(0, As0, Bs0, sA0, sB0, mA0, mB0);
-  for (int kt = 0; kt < vsteps; kt += 2) {
-    stage_ready();
-    load_stage(kt + 1, As1, Bs1, sA1, sB1, mA1, mB1);
-    compute_stage(As0, Bs0, sA0, sB0, mA0, mB0, kt);
-    pin_acc();
-    stage_ready();
-    if (kt + 2 < vsteps) load_stage(kt + 2, As0, Bs0, sA0, sB0, mA0, mB0);
-    compute_stage(As1, Bs1, sA1, sB1, mA1, mB1, kt + 1);
-    pin_acc();
+  // loop body (four stages) has no conditional MFMAs.
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  Frags<MI, NI> F0, F1;
+  if (PREF) {
+    // stage k: wait for stage k+1's copies, barrier, issue stage k+3's
+    // copies, then stage k's MFMAs (fragments read during stage k-1)
+    // interleaved with the reads of stage k+1's fragments
+    auto step = [&](int k, Frags<MI, NI> &fc, Frags<MI, NI> &fn, const uint8_t *an, const uint8_t *bn,
+                    const uint32_t *man, const uint32_t *mbn, uint8_t *al, uint8_t *bl, float *sal,
+                    float *sbl, uint32_t *mal, uint32_t *mbl, auto ph) {
+      sync_stage(ops(k + 2));
+      if (k + 3 < vsteps) load_stage(k + 3, al, bl, sal, sbl, mal, mbl);
+      mfma_stage(fc, nullptr, nullptr, k, ph);
+      read_frags(fn, an, bn, man, mbn);
+      order_pref();
+      pin_acc();
+    };
+    if (vsteps > 0) {
+      load_stage(0, As0, Bs0, sA0, sB0, mA0, mB0);
+      load_stage(1, As1, Bs1, sA1, sB1, mA1, mB1);
+      load_stage(2, As2, Bs2, sA2, sB2, mA2, mB2);
+      sync_stage(ops(1) + ops(2));
+      read_frags(F0, As0, Bs0, mA0, mB0);
+    }
+    for (int kt = 0; kt < vsteps; kt += 4) {
+      step(kt, F0, F1, As1, Bs1, mA1, mB1, As3, Bs3, sA3, sB3, mA3, mB3, P0{});
+      step(kt + 1, F1, F0, As2, Bs2, mA2, mB2, As0, Bs0, sA0, sB0, mA0, mB0, P1{});
+      step(kt + 2, F0, F1, As3, Bs3, mA3, mB3, As1, Bs1, sA1, sB1, mA1, mB1, P0{});
+      step(kt + 3, F1, F0, As0, Bs0, mA0, mB0, As2, Bs2, sA2, sB2, mA2, mB2, P1{});
+    }
+  } else {
+    // stage k: wait for its own copies, barrier, issue stage k+3's copies,
+    // read its fragments and run its MFMAs
+    auto step = [&](int k, const uint8_t *ac, const uint8_t *bc, const float *sac, const float *sbc,
+                    const uint32_t *mac, const uint32_t *mbc, uint8_t *al, uint8_t *bl, float *sal,
+                    float *sbl, uint32_t *mal, uint32_t *mbl, auto ph) {
+      sync_stage(ops(k + 1) + ops(k + 2));
+      if (k + 3 < vsteps) load_stage(k + 3, al, bl, sal, sbl, mal, mbl);
+      read_frags(F0, ac, bc, mac, mbc);
+      mfma_stage(F0, sac, sbc, k, ph);
+      pin_acc();
+    };
+    if (vsteps > 0) {
+      load_stage(0, As0, Bs0, sA0, sB0, mA0, mB0);
+      load_stage(1, As1, Bs1, sA1, sB1, mA1, mB1);
+      load_stage(2, As2, Bs2, sA2, sB2, mA2, mB2);
+    }
+    for (int kt = 0; kt < vsteps; kt += 4) {
+      step(kt, As0, Bs0, sA0, sB0, mA0, mB0, As3, Bs3, sA3, sB3, mA3, mB3, P0{});
+      step(kt + 1, As1, Bs1, sA1, sB1, mA1, mB1, As0, Bs0, sA0, sB0, mA0, mB0, P1{});
+      step(kt + 2, As2, Bs2, sA2, sB2, mA2, mB2, As1, Bs1, sA1, sB1, mA1, mB1, P0{});
+      step(kt + 3, As3, Bs3, sA3, sB3, mA3, mB3, As2, Bs2, sA2, sB2, mA2, mB2, P1{});
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();  // every wave is done with the stage buffers
@@ -476,7 +560,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
   constexpr int STR = WN + 8;          // LDS row stride in floats
   constexpr int CPR = WN / 8;          // 8-float chunks per row
   constexpr int CPL = 16 * CPR / 64;   // chunks per lane per half slab
-  uint8_t *creg = wave == 0 ? As0 : wave == 1 ? As1 : wave == 2 ? Bs0 : Bs1;
+  uint8_t *creg = wave == 0 ? As0 : wave == 1 ? As1 : wave == 2 ? As2 : As3;
   float *cb = reinterpret_cast<float *>(creg);
   const int64_t jw = j0 + wj * WN;
 #pragma unroll
@@ -497,7 +581,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
         const int64_t j = jw + c8 * 8;
         const float4 x0 = *reinterpret_cast<const float4 *>(&cb[r * STR + c8 * 8]);
         const float4 x1 = *reinterpret_cast<const float4 *>(&cb[r * STR + c8 * 8 + 4]);
-        if (i < ilim && j < a.J) {  // J % 128 == 0: a chunk is all in or all out
+        if (i >= ilo && i < ihi && j < a.J) {  // J % 128 == 0: a chunk is all in or all out
           if (MODE == kWgrad) {
             float4 y0 = make_float4(x0.x * scale, x0.y * scale, x0.z * scale, x0.w * scale);
             float4 y1 = make_float4(x1.x * scale, x1.y * scale, x1.z * scale, x1.w * scale);
@@ -537,7 +621,9 @@ static hipError_t launch_cfg(const GemmArgs &a0, hipStream_t st) {
     a.slots = (int)((a.I + GBM - 1) / GBM);
     nblocks = (int64_t)a.E * a.slots * a.jtiles;
   } else {
-    a.slots = (int)((a.M + GBM - 1) / GBM) + a.E;  // upper bound of group-aligned row tiles
+    // upper bound of the row tiles: group g has at most (m_g + 2) / 2 row
+    // pairs, so ceil(((m_g + 2) / 2) / (GBM / 2)) <= (m_g + 2) / GBM + 1 tiles
+    a.slots = (int)((a.M + 2 * (int64_t)a.E + GBM - 1) / GBM) + a.E;
     nblocks = (int64_t)a.slots * a.jtiles;
   }
   if (nblocks == 0) return hipSuccess;

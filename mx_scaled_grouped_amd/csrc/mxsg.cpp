@@ -202,8 +202,8 @@ mxsg_status mxsg_grouped_mm(int32_t mode, int32_t recipe, int32_t fmt_a, int32_t
             (long long)lda, (long long)ldb, (long long)cap);
   } else {
     const int64_t L = mode == MXSG_MODE_FWD ? K : N;
-    REQUIRE(lda >= L && lda % 16 == 0, MXSG_BAD_SHAPE,
-            "grouped_mm: lda=%lld must be >= %lld and a multiple of 16", (long long)lda,
+    REQUIRE(lda >= L && lda % 64 == 0, MXSG_BAD_SHAPE,
+            "grouped_mm: lda=%lld must be >= %lld and a multiple of 64", (long long)lda,
             (long long)L);
     REQUIRE(ldb == L, MXSG_BAD_SHAPE, "grouped_mm: ldb=%lld must equal %lld", (long long)ldb,
             (long long)L);

@@ -18,6 +18,11 @@
 // Column-wise tiles are laid out in padded token space: group g owns padded
 // columns [P_g, P_{g+1}), P_{g+1} = P_g + ceil(m_g/128)*128, so every
 // 128-column tile lies inside one group and a 128x1 unit is one tile column.
+//
+// Every code matrix is written pair-interleaved (pi_off): the grouped GEMM
+// reads 64 contraction bytes of two adjacent rows as one 128-byte line. A
+// wave's stores still cover whole lines (four rows of 128 codes row-wise,
+// eight feature rows of 128 positions column-wise).
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -69,9 +74,9 @@ struct TileArgs {
   int64_t C;              // features
   int32_t E;              // groups (column-wise token layout); 0 = one group of all rows
   const int32_t *ends;    // [E]
-  uint8_t *row_codes;     // [batch][rows, C]
+  uint8_t *row_codes;     // [batch][rows, C], pair-interleaved
   void *row_scales;
-  uint8_t *col_codes;     // [batch][C, ld]
+  uint8_t *col_codes;     // [batch][C, ld], pair-interleaved
   void *col_scales;
   int64_t ld;             // column-wise row stride (bytes)
   int32_t *padded_out;    // [E+1] or null
@@ -247,8 +252,7 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
       }
       if (r < nvalid) {
         const uint2 q = cvt8<FMT>(v[u], inv);
-        *reinterpret_cast<uint2 *>(a.row_codes + b * a.row_bstride + (src0 + r) * a.C + c0 +
-                                   cq * 8) = q;
+        *reinterpret_cast<uint2 *>(a.row_codes + b * a.row_bstride + pi_off(src0 + r, c0 + cq * 8, a.C)) = q;
       }
     }
   }
@@ -332,7 +336,7 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
     const int id = u * QTHREADS + t;
     const int f = id >> 3, ch = id & 7;
     const uint4 val = *reinterpret_cast<const uint4 *>(&ctile[f * CODE_LD + ch * 16]);
-    *reinterpret_cast<uint4 *>(cc + (c0 + f) * a.ld + p0 + ch * 16) = val;
+    *reinterpret_cast<uint4 *>(cc + pi_off(c0 + f, p0 + ch * 16, a.ld)) = val;
   }
 }
 

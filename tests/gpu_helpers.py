@@ -30,6 +30,12 @@ def host(t) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
+def codes_host(t, rows=None) -> np.ndarray:
+    """Row-major host copy of pair-interleaved device codes (the first `rows` rows)."""
+    from mx_scaled_grouped_amd import api
+    return host(api.unpack_codes(t, rows))
+
+
 def bf16_host_f64(t) -> np.ndarray:
     """A device bf16 tensor -> float64 numpy (exact)."""
     b = host(t.view(torch.int16)).view(np.uint16).astype(np.uint32) << np.uint32(16)

@@ -44,6 +44,12 @@ def _np(t):
     return t.contiguous().cpu().numpy()
 
 
+def _unpack(t):
+    """Row-major device copy of pair-interleaved codes."""
+    from mx_scaled_grouped_amd import api
+    return api.unpack_codes(t)
+
+
 def _take(t, *idx):
     """t indexed on the device along (dim, indices) pairs, before the host copy."""
     for d, ix in idx:
@@ -188,12 +194,12 @@ def check_forward(name, which):
     rec, dls = _act_scale(st, which, "f", a_bits, fa)
     ra = OQ.quantize_act(a_bits[rows], rec, fa, dl_scale=dls)
     qa = step.q["a_" + which]
-    assert_bits_equal(_np(_take(qa.row_codes, (0, rows))), ra["row_codes"], "activation codes")
+    assert_bits_equal(_np(_take(_unpack(qa.row_codes), (0, rows))), ra["row_codes"], "activation codes")
     _check_scales_rows(qa.row_scales, ra["row_scales"], rec, rows, "activation scales")
     wrec, wdl = _w_scale(st, which, w_bits, OF.E4M3)
     rw = OQ.quantize_weight(np.ascontiguousarray(w_bits[:, :, ncols]), wrec, OF.E4M3, dl_scale=wdl)
     qw = step.q["w_" + which]
-    assert_bits_equal(_np(_take(qw.kmajor_codes, (1, ncols))), rw["kmajor_codes"], "weight k-major codes")
+    assert_bits_equal(_np(_take(_unpack(qw.kmajor_codes), (1, ncols))), rw["kmajor_codes"], "weight k-major codes")
     ks = _np(qw.kmajor_scales)
     if wrec == "dl":
         assert_bits_equal(ks, rw["kmajor_scales"], "weight scales")
@@ -220,12 +226,12 @@ def check_dgrad(name, which):
     rec, dls = _act_scale(st, which, "g", d_bits, fg)
     rd = OQ.quantize_act(d_bits[rows], rec, fg, dl_scale=dls)
     qd = step.q["dy_" + which]
-    assert_bits_equal(_np(_take(qd.row_codes, (0, rows))), rd["row_codes"], "gradient codes")
+    assert_bits_equal(_np(_take(_unpack(qd.row_codes), (0, rows))), rd["row_codes"], "gradient codes")
     _check_scales_rows(qd.row_scales, rd["row_scales"], rec, rows, "gradient scales")
     wrec, wdl = _w_scale(st, which, w_bits, OF.E4M3)
     rw = OQ.quantize_weight(np.ascontiguousarray(w_bits[:, kcols, :]), wrec, OF.E4M3, dl_scale=wdl)
     qw = step.q["w_" + which]
-    assert_bits_equal(_np(_take(qw.nmajor_codes, (1, kcols))), rw["nmajor_codes"], "weight n-major codes")
+    assert_bits_equal(_np(_take(_unpack(qw.nmajor_codes), (1, kcols))), rw["nmajor_codes"], "weight n-major codes")
     ns = _np(qw.nmajor_scales)
     if wrec == "block":
         assert_bits_equal(ns[:, kblk, :], rw["nmajor_scales"], "weight tile scales")
@@ -257,7 +263,7 @@ def check_wgrad(name, which):
                              colwise=True, dl_scale=dls)
         P = rc["padded_starts"]
         assert np.array_equal(_np(q.padded_starts).astype(np.int64), P), tag + " padded starts"
-        cc = _np(_take(q.col_codes, (0, cols)))
+        cc = _np(_take(_unpack(q.col_codes), (0, cols)))
         assert_bits_equal(cc[:, :P[-1]], rc["col_codes"], tag + " column codes")
         cs = _np(q.col_scales)
         if rec == "dl":

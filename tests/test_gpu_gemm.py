@@ -123,7 +123,8 @@ def make_case(mode, recipe, fa, fb, sizes, K, N, seed, exact=True):
 def run_case(c, out=None, accumulate=False):
     api = _api()
     return api.grouped_mm(c.mode, c.recipe, c.fa, c.fb, c.E, c.M, c.K, c.N, to_dev(c.ge),
-                          to_dev(c.a), to_dev(c.sa), c.lda, to_dev(c.b), to_dev(c.sb), c.ldb,
+                          api.pack_codes(to_dev(c.a)), to_dev(c.sa), c.lda, api.pack_codes(to_dev(c.b)),
+                          to_dev(c.sb), c.ldb,
                           padded_starts=None if c.padded is None else to_dev(c.padded), out=out,
                           accumulate=accumulate)
 

@@ -5,7 +5,7 @@ sizes around the block lengths."""
 import numpy as np
 import pytest
 
-from tests.gpu_helpers import (torch, EDGE_SIZES, FMT_OBJ, gpu_available, to_dev_u16, to_dev, host,
+from tests.gpu_helpers import (torch, EDGE_SIZES, FMT_OBJ, gpu_available, to_dev_u16, to_dev, host, codes_host,
                                assert_bits_equal)
 from oracle import quant as OQ
 from oracle import formats as OF
@@ -68,13 +68,13 @@ RECIPE_FMTS = [("tw", 0), ("tw", 1), ("block", 0), ("block", 1), ("mx", 0), ("mx
 
 def _compare_act(q, ref, recipe, M, C, rowwise, colwise):
     if rowwise:
-        assert_bits_equal(host(q.row_codes), ref["row_codes"], "row codes")
+        assert_bits_equal(codes_host(q.row_codes, M), ref["row_codes"], "row codes")
         assert_bits_equal(host(q.row_scales), ref["row_scales"], "row scales")
     if colwise:
         P = host(q.padded_starts).astype(np.int64)
         assert np.array_equal(P, ref["padded_starts"]), (P, ref["padded_starts"])
         Rp = int(P[-1])
-        assert_bits_equal(host(q.col_codes)[:, :Rp], ref["col_codes"], "col codes")
+        assert_bits_equal(codes_host(q.col_codes)[:, :Rp], ref["col_codes"], "col codes")
         cs = host(q.col_scales)
         if recipe in ("tw", "dl"):
             assert_bits_equal(cs, ref["col_scales"], "col scales")
@@ -173,8 +173,8 @@ def test_weight_layouts(recipe, fmt):
     print(f"quantize_weight {recipe} fmt={fmt}", flush=True)
     ref = OQ.quantize_weight(w, recipe, FMT_OBJ[fmt])
     q = api.quantize_weight(to_dev_u16(w), recipe, fmt)
-    assert_bits_equal(host(q.kmajor_codes), ref["kmajor_codes"], "k-major codes")
-    assert_bits_equal(host(q.nmajor_codes), ref["nmajor_codes"], "n-major codes")
+    assert_bits_equal(codes_host(q.kmajor_codes), ref["kmajor_codes"], "k-major codes")
+    assert_bits_equal(codes_host(q.nmajor_codes), ref["nmajor_codes"], "n-major codes")
     assert_bits_equal(host(q.kmajor_scales), ref["kmajor_scales"], "k-major scales")
     assert_bits_equal(host(q.nmajor_scales), ref["nmajor_scales"], "n-major scales")
     if recipe == "tw":
@@ -212,8 +212,8 @@ def test_delayed_steps_match_oracle():
         rd = OQ.quantize_act(dy, "dl", OF.E5M2, ge, rowwise=True, colwise=True, dl_scale=st_ref[1].scale(0))
         _compare_act(qx, rx, "dl", x.shape[0], 256, True, True)
         _compare_act(qd, rd, "dl", dy.shape[0], 128, True, True)
-        assert_bits_equal(host(qw.kmajor_codes), rw["kmajor_codes"], "dl weight k-major")
-        assert_bits_equal(host(qw.nmajor_codes), rw["nmajor_codes"], "dl weight n-major")
+        assert_bits_equal(codes_host(qw.kmajor_codes), rw["kmajor_codes"], "dl weight k-major")
+        assert_bits_equal(codes_host(qw.nmajor_codes), rw["nmajor_codes"], "dl weight n-major")
         assert_bits_equal(host(qw.kmajor_scales), rw["kmajor_scales"], "dl weight scales")
         assert_bits_equal(host(st_dev[0].amax), np.concatenate([rx["amax"], rw["amax"]]), "recorded amax")
         assert_bits_equal(host(st_dev[1].amax), rd["amax"], "recorded amax dy")
