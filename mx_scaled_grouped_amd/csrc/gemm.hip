@@ -183,6 +183,18 @@ __device__ __forceinline__ void wait_vm_n(int n) {
   }
 }
 
+// scheduling groups: MFMA I, then the LDS reads that spread RD reads evenly
+// over NM MFMAs
+template <int I, int NM, int RD>
+__device__ __forceinline__ void order_groups() {
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int r = (RD * (I + 1)) / NM - (RD * I) / NM;
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+    order_groups<I + 1, NM, RD>();
+  }
+}
+
 // one stage's operands of one lane, in registers
 template <int MI, int NI>
 struct Frags {
@@ -200,9 +212,6 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
   constexpr int BQ = BN / 16 / 4;    // of B
   constexpr bool BLK = RECIPE == kBlockwise;
   constexpr bool MX = RECIPE == kMx;
-  // the next stage's fragments are read during this stage's MFMAs (two
-  // register sets); blockwise keeps its registers for the partial sums
-  constexpr bool PREF = !BLK;
   static_assert(AQ >= 1 && BQ >= 1 && NI >= 1, "tile shape");
   static_assert(!MX || (MI == 4 && NI == 4 && BN == 256), "MX word layout");
 
@@ -372,11 +381,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
   };
 
   // wait until at most `pending` of this wave's copies are in flight (copies
-  // complete in issue order), then synchronize the workgroup
-  auto sync_stage = [&](int pending) {
+  // complete in issue order), then synchronize the workgroup. `lds`: also
+  // wait for this wave's LDS writes (the zero fill of a padding stage that
+  // other waves read after the barrier); outstanding fragment reads need no
+  // wait here, the MFMAs that use them wait for them.
+  auto sync_stage = [&](int pending, bool lds) {
     __builtin_amdgcn_sched_barrier(0);
     wait_vm_n(pending);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (lds) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -417,72 +429,78 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
     }
   };
 
-  // the MI x NI MFMAs of stage kt; PH = the stage's position in its
-  // 128-block (MX: which two bytes of the scale word; blockwise: 0 starts
-  // the partial, 1 finishes and promotes it)
-  auto mfma_stage = [&](const Frags<MI, NI> &f, const float *sa_l, const float *sb_l, int kt, auto ph) {
+  // MFMAs LO..HI-1 (index mi * NI + ni) of stage kt; PH = the stage's
+  // position in its 128-block (MX: which two bytes of the scale word;
+  // blockwise: 0 starts the partial, 1 continues it)
+  auto mfma_range = [&](const Frags<MI, NI> &f, auto ph, auto lo, auto hi) {
     constexpr int PH = decltype(ph)::value;
+    constexpr int LO = decltype(lo)::value, HI = decltype(hi)::value;
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int x = LO; x < HI; ++x) {
+      const int mi = x / NI, ni = x % NI;
+      if (MX) {
+        // lane half h takes byte 2*PH + h of the row's word (shifted by 8h): opsel 2*PH
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            f.a[mi], f.b[ni], acc[mi][ni], FA, FB, 2 * PH, f.sa[mi], 2 * PH, f.sb[ni]);
+      } else if (BLK) {
+        if (PH == 0) {
+          v16f z;
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        if (MX) {
-          // lane half h takes byte 2*PH + h of the row's word (shifted by 8h): opsel 2*PH
-          acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              f.a[mi], f.b[ni], acc[mi][ni], FA, FB, 2 * PH, f.sa[mi], 2 * PH, f.sb[ni]);
-        } else if (BLK) {
-          if (PH == 0) {
-            v16f z;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) z[v] = 0.0f;
-            part[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                f.a[mi], f.b[ni], z, FA, FB, 0, kUnitScale, 0, kUnitScale);
-          } else {
-            part[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                f.a[mi], f.b[ni], part[mi][ni], FA, FB, 0, kUnitScale, 0, kUnitScale);
-          }
+          for (int v = 0; v < 16; ++v) z[v] = 0.0f;
+          part[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              f.a[mi], f.b[ni], z, FA, FB, 0, kUnitScale, 0, kUnitScale);
         } else {
-          // unit E8M0 scales (127 = 2^0); the scaled form keeps the
-          // accumulators in AGPRs
-          acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              f.a[mi], f.b[ni], acc[mi][ni], FA, FB, 0, kUnitScale, 0, kUnitScale);
+          part[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              f.a[mi], f.b[ni], part[mi][ni], FA, FB, 0, kUnitScale, 0, kUnitScale);
         }
-      }
-    if (BLK && PH == 1) {
-      // promote: acc += partial * sA(row) * sB; sB per column for wgrad,
-      // one value per tile (the 128x128 weight tile) otherwise
-      const float sbw = MODE == kWgrad ? 0.0f : sbtab[(kt >> 1) & (SB_TAB - 1)];
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        float sa[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 v4 = *reinterpret_cast<const float4 *>(&sa_l[wi * 128 + mi * 32 + q * 8 + h * 4]);
-          sa[q * 4 + 0] = v4.x;
-          sa[q * 4 + 1] = v4.y;
-          sa[q * 4 + 2] = v4.z;
-          sa[q * 4 + 3] = v4.w;
-        }
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          const float sbj = MODE == kWgrad ? sb_l[wj * WN + ni * 32 + l32] : sbw;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[mi][ni][v] += part[mi][ni][v] * (sa[v] * sbj);
-        }
+      } else {
+        // unit E8M0 scales (127 = 2^0); the scaled form keeps the
+        // accumulators in AGPRs
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            f.a[mi], f.b[ni], acc[mi][ni], FA, FB, 0, kUnitScale, 0, kUnitScale);
       }
     }
   };
 
-  // instruction order of a prefetching stage: one next-stage fragment read
-  // after each MFMA (then the MX word reads)
-  auto order_pref = [&]() {
-    constexpr int RD = 2 * (MI + NI);
-    static_assert(RD <= MI * NI || !PREF, "read/MFMA interleave");
+  // blockwise, after the second stage of a 128-block: acc += partial *
+  // sA(row) * sB; sB per column for wgrad, one value per tile (the 128x128
+  // weight tile) otherwise
+  auto promote = [&](const float *sa_l, const float *sb_l, int kt) {
+    const float sbw = MODE == kWgrad ? 0.0f : sbtab[(kt >> 1) & (SB_TAB - 1)];
 #pragma unroll
-    for (int i = 0; i < MI * NI; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int mi = 0; mi < MI; ++mi) {
+      float sa[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v4 = *reinterpret_cast<const float4 *>(&sa_l[wi * 128 + mi * 32 + q * 8 + h * 4]);
+        sa[q * 4 + 0] = v4.x;
+        sa[q * 4 + 1] = v4.y;
+        sa[q * 4 + 2] = v4.z;
+        sa[q * 4 + 3] = v4.w;
+      }
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const float sbj = MODE == kWgrad ? sb_l[wj * WN + ni * 32 + l32] : sbw;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[mi][ni][v] += part[mi][ni][v] * (sa[v] * sbj);
+      }
     }
+  };
+
+  // MFMAs of a stage issued before its barrier (their operands are already
+  // in registers, so they keep the MFMA pipe busy while the waves sync).
+  // Not for blockwise: there the partials are read back soon after their
+  // MFMAs, and the compiler then placed those reads too close to the MFMAs
+  // (stale values).
+  constexpr int NPRE = BLK ? 0 : 2;
+  using C0 = std::integral_constant<int, 0>;
+  using CPRE = std::integral_constant<int, NPRE>;
+  using CALL = std::integral_constant<int, MI * NI>;
+
+  // instruction order of the rest of a prefetching stage: the next stage's
+  // fragment reads spread evenly over its MFMAs (then the MX word reads)
+  auto order_pref = [&]() {
+    order_groups<0, MI * NI - NPRE, 2 * (MI + NI)>();
     if (MX) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
   };
 
@@ -493,55 +511,44 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   Frags<MI, NI> F0, F1;
-  if (PREF) {
+  {
     // stage k: wait for stage k+1's copies, barrier, issue stage k+3's
     // copies, then stage k's MFMAs (fragments read during stage k-1)
     // interleaved with the reads of stage k+1's fragments
-    auto step = [&](int k, Frags<MI, NI> &fc, Frags<MI, NI> &fn, const uint8_t *an, const uint8_t *bn,
-                    const uint32_t *man, const uint32_t *mbn, uint8_t *al, uint8_t *bl, float *sal,
-                    float *sbl, uint32_t *mal, uint32_t *mbl, auto ph) {
-      sync_stage(ops(k + 2));
+    auto step = [&](int k, Frags<MI, NI> &fc, Frags<MI, NI> &fn, const float *sac, const float *sbc,
+                    const uint8_t *an, const uint8_t *bn, const uint32_t *man, const uint32_t *mbn,
+                    uint8_t *al, uint8_t *bl, float *sal, float *sbl, uint32_t *mal, uint32_t *mbl,
+                    auto ph) {
+      mfma_range(fc, ph, C0{}, CPRE{});
+      sync_stage(ops(k + 2), k + 1 >= nsteps);
       if (k + 3 < vsteps) load_stage(k + 3, al, bl, sal, sbl, mal, mbl);
-      mfma_stage(fc, nullptr, nullptr, k, ph);
+      mfma_range(fc, ph, CPRE{}, CALL{});
       read_frags(fn, an, bn, man, mbn);
       order_pref();
+      if (BLK && decltype(ph)::value == 1) {
+        // a v_mfma_scale 32x32x64 result read back by the VALU needs more
+        // independent cycles than the compiler left in one schedule: pad
+        // explicitly (>= 40 wait states) between the last MFMA of the block
+        // and the reads of its partials
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        promote(sac, sbc, k);
+      }
       pin_acc();
     };
     if (vsteps > 0) {
       load_stage(0, As0, Bs0, sA0, sB0, mA0, mB0);
       load_stage(1, As1, Bs1, sA1, sB1, mA1, mB1);
       load_stage(2, As2, Bs2, sA2, sB2, mA2, mB2);
-      sync_stage(ops(1) + ops(2));
+      sync_stage(ops(1) + ops(2), true);
       read_frags(F0, As0, Bs0, mA0, mB0);
     }
     for (int kt = 0; kt < vsteps; kt += 4) {
-      step(kt, F0, F1, As1, Bs1, mA1, mB1, As3, Bs3, sA3, sB3, mA3, mB3, P0{});
-      step(kt + 1, F1, F0, As2, Bs2, mA2, mB2, As0, Bs0, sA0, sB0, mA0, mB0, P1{});
-      step(kt + 2, F0, F1, As3, Bs3, mA3, mB3, As1, Bs1, sA1, sB1, mA1, mB1, P0{});
-      step(kt + 3, F1, F0, As0, Bs0, mA0, mB0, As2, Bs2, sA2, sB2, mA2, mB2, P1{});
-    }
-  } else {
-    // stage k: wait for its own copies, barrier, issue stage k+3's copies,
-    // read its fragments and run its MFMAs
-    auto step = [&](int k, const uint8_t *ac, const uint8_t *bc, const float *sac, const float *sbc,
-                    const uint32_t *mac, const uint32_t *mbc, uint8_t *al, uint8_t *bl, float *sal,
-                    float *sbl, uint32_t *mal, uint32_t *mbl, auto ph) {
-      sync_stage(ops(k + 1) + ops(k + 2));
-      if (k + 3 < vsteps) load_stage(k + 3, al, bl, sal, sbl, mal, mbl);
-      read_frags(F0, ac, bc, mac, mbc);
-      mfma_stage(F0, sac, sbc, k, ph);
-      pin_acc();
-    };
-    if (vsteps > 0) {
-      load_stage(0, As0, Bs0, sA0, sB0, mA0, mB0);
-      load_stage(1, As1, Bs1, sA1, sB1, mA1, mB1);
-      load_stage(2, As2, Bs2, sA2, sB2, mA2, mB2);
-    }
-    for (int kt = 0; kt < vsteps; kt += 4) {
-      step(kt, As0, Bs0, sA0, sB0, mA0, mB0, As3, Bs3, sA3, sB3, mA3, mB3, P0{});
-      step(kt + 1, As1, Bs1, sA1, sB1, mA1, mB1, As0, Bs0, sA0, sB0, mA0, mB0, P1{});
-      step(kt + 2, As2, Bs2, sA2, sB2, mA2, mB2, As1, Bs1, sA1, sB1, mA1, mB1, P0{});
-      step(kt + 3, As3, Bs3, sA3, sB3, mA3, mB3, As2, Bs2, sA2, sB2, mA2, mB2, P1{});
+      step(kt, F0, F1, sA0, sB0, As1, Bs1, mA1, mB1, As3, Bs3, sA3, sB3, mA3, mB3, P0{});
+      step(kt + 1, F1, F0, sA1, sB1, As2, Bs2, mA2, mB2, As0, Bs0, sA0, sB0, mA0, mB0, P1{});
+      step(kt + 2, F0, F1, sA2, sB2, As3, Bs3, mA3, mB3, As1, Bs1, sA1, sB1, mA1, mB1, P0{});
+      step(kt + 3, F1, F0, sA3, sB3, As0, Bs0, mA0, mB0, As2, Bs2, sA2, sB2, mA2, mB2, P1{});
     }
   }
   __builtin_amdgcn_sched_barrier(0);
