@@ -147,6 +147,14 @@ __device__ __forceinline__ void group_bounds(const int32_t *__restrict__ ends, i
   hi = b < a ? a : b;
 }
 
+// Max-reduce a non-negative fp32 bit pattern into *p (bit order = value
+// order for non-negative floats). The atomic is skipped when the stored value
+// is already at least as large, so a tensor's tiles mostly stop contending for
+// one word once its maximum is in; a stale read only costs an extra atomic.
+__device__ __forceinline__ void atomic_max_bits(uint32_t *p, uint32_t v) {
+  if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < v) atomicMax(p, v);
+}
+
 // Byte offset of code (r, l) in a pair-interleaved code matrix with rows of
 // L bytes (L a multiple of 64): rows 2p and 2p+1 share 2L bytes, as lines of
 // 128 bytes that each hold 64 bytes of row 2p followed by the same 64 bytes

@@ -97,6 +97,13 @@ mxsg_status mxsg_quantize_act(const void *x, int64_t M, int64_t C, int32_t recip
     REQUIRE(amax, MXSG_INVALID_ARGUMENT, "quantize_act: amax is NULL");
   if (recipe == MXSG_RECIPE_DELAYED)
     REQUIRE(dl_scale && dl_inv, MXSG_INVALID_ARGUMENT, "quantize_act: dl_scale/dl_inv NULL");
+  {
+    // one workgroup per 128 x 128 tile (row tiles, or padded-column tiles)
+    const int64_t rt = col_codes ? ld / 128 : (M + 127) / 128;
+    REQUIRE((rt > 0 ? rt : 1) * (C / 128) <= INT32_MAX, MXSG_BAD_SHAPE,
+            "quantize_act: %lld x %lld tiles exceed the launch limit", (long long)rt,
+            (long long)(C / 128));
+  }
 
   mxsg::QuantActParams p{};
   p.x = static_cast<const uint16_t *>(x);
@@ -129,7 +136,8 @@ mxsg_status mxsg_quantize_weight(const void *w, int32_t E, int64_t K, int64_t N,
           E, (long long)K, (long long)N);
   REQUIRE(K % 128 == 0 && N % 128 == 0, MXSG_BAD_SHAPE,
           "quantize_weight: K=%lld and N=%lld must be multiples of 128", (long long)K, (long long)N);
-  REQUIRE(E <= 65535 && K / 128 <= 65535, MXSG_BAD_SHAPE, "quantize_weight: too large");
+  REQUIRE(E <= 65535 && (K / 128) * (N / 128) <= INT32_MAX, MXSG_BAD_SHAPE,
+          "quantize_weight: too large");
   REQUIRE(w, MXSG_INVALID_ARGUMENT, "quantize_weight: w is NULL");
   REQUIRE(kmajor_codes || nmajor_codes, MXSG_INVALID_ARGUMENT, "quantize_weight: no output");
   if (kmajor_codes) REQUIRE(kmajor_scales, MXSG_INVALID_ARGUMENT, "quantize_weight: kmajor_scales NULL");

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint16_t *__restrict__ 
   __syncthreads();
   if (threadIdx.x == 0) {
     m = umax(umax(red[0], red[1]), umax(red[2], red[3]));
-    if (m) atomicMax(amax_bits + u, m << 16);
+    if (m) atomic_max_bits(amax_bits + u, m << 16);
   }
 }
 
@@ -119,7 +119,7 @@ __device__ bool locate_padded_tile(const TileArgs &a, int64_t p0, int64_t &src0,
         s_nvalid = (int)(nv > QT ? QT : nv);
         s_found = 1;
       }
-      if (a.padded_out && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && g < a.E) {
+      if (a.padded_out && blockIdx.x == 0 && blockIdx.z == 0 && g < a.E) {
         a.padded_out[g + 1] = (int32_t)(start + padm);
         if (g == 0) a.padded_out[0] = 0;
       }
@@ -135,7 +135,10 @@ __device__ bool locate_padded_tile(const TileArgs &a, int64_t p0, int64_t &src0,
 template <int RECIPE, int FMT, bool ROW, bool COL>
 __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[QT * QT];       // bf16, row stride 256 B
-  __shared__ __attribute__((aligned(16))) uint8_t ctile[QT * CODE_LD];  // codes [feature][pos]
+  // codes [feature][pos] of the column-wise output, in the same LDS as the
+  // bf16 tile (written once every thread has read its columns)
+  uint8_t *const ctile = reinterpret_cast<uint8_t *>(tile);
+  static_assert(QT * CODE_LD <= QT * QT * 2, "code tile fits in the bf16 tile");
   __shared__ uint32_t colmax[4][QT];
   __shared__ uint32_t red[4];
   __shared__ int32_t scan[72];
@@ -143,12 +146,17 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int64_t b = blockIdx.z;
-  const int64_t c0 = (int64_t)blockIdx.y * QT;  // feature tile (grid.x walks the row tiles)
+  // grid.x = row tiles x feature tiles, feature tiles fastest: consecutive
+  // workgroups read the 256-byte pieces of the same 128 rows (contiguous memory)
+  const int nft = (int)(a.C / QT);
+  const int ftile = (int)(blockIdx.x % (unsigned)nft);
+  const int64_t rtile = blockIdx.x / (unsigned)nft;
+  const int64_t c0 = (int64_t)ftile * QT;
   const uint16_t *x = a.x + b * a.x_bstride;
 
   // the tensor scale (tensorwise / delayed) is written first, so that it is
   // there even when no tile holds a row (an empty tensor or empty groups)
-  if ((RECIPE == kTensorwise || RECIPE == kDelayed) && blockIdx.x == 0 && blockIdx.y == 0 &&
+  if ((RECIPE == kTensorwise || RECIPE == kDelayed) && blockIdx.x == 0 &&
       t == 0) {
     float s0 = 1.0f, i0 = 1.0f;
     if (RECIPE == kTensorwise)
@@ -163,7 +171,7 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
   int64_t src0 = 0, p0 = 0;
   int nvalid = 0;
   if (COL) {
-    p0 = (int64_t)blockIdx.x * QT;
+    p0 = rtile * QT;
     if (a.E > 0) {
       if (!locate_padded_tile(a, p0, src0, nvalid, scan)) return;
     } else {  // weights: one group of all rows, rows % 128 == 0
@@ -171,7 +179,7 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
       nvalid = 128;
     }
   } else {
-    src0 = (int64_t)blockIdx.x * QT;
+    src0 = rtile * QT;
     int64_t nv = a.rows - src0;
     nvalid = (int)(nv > QT ? QT : nv);
   }
@@ -213,12 +221,12 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
     __syncthreads();
     const uint32_t m = umax(umax(red[0], red[1]), umax(red[2], red[3]));
     if (RECIPE == kDelayed) {
-      if (t == 0 && m) atomicMax(reinterpret_cast<uint32_t *>(a.amax + b), m << 16);
+      if (t == 0 && m) atomic_max_bits(reinterpret_cast<uint32_t *>(a.amax + b), m << 16);
     } else {
       scale_pair<FMT>(bits_to_amax(m), t_s, t_inv);
       if (t == 0) {
         // 128x128 tile scale: [K/128, N/128] per expert, shared by both layouts
-        const int64_t idx = b * a.rs_bstride + (int64_t)blockIdx.x * (a.C / QT) + blockIdx.y;
+        const int64_t idx = b * a.rs_bstride + rtile * (a.C / QT) + ftile;
         if (a.row_scales) reinterpret_cast<float *>(a.row_scales)[idx] = t_s;
         if (a.col_scales) reinterpret_cast<float *>(a.col_scales)[idx] = t_s;
       }
@@ -239,7 +247,7 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
         scale_pair<FMT>(bits_to_amax(m), s, inv);
         if (cq == 0 && r < nvalid)
           reinterpret_cast<float *>(a.row_scales)[b * a.rs_bstride + (src0 + r) * (a.C / QT) +
-                                                  blockIdx.y] = s;
+                                                  ftile] = s;
       } else if (RECIPE == kMx) {  // 1x32: the 4 lanes holding 32 features
         uint32_t m = absmax_bits8(v[u], 0);
         m = umax(m, (uint32_t)__shfl_xor((int)m, 1, 64));
@@ -309,6 +317,10 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
       }
     }
   }
+
+  // the code tile overwrites the bf16 tile: every thread must have read its
+  // columns first (blockwise already synchronized after its column maxima)
+  if (RECIPE != kBlockwise) __syncthreads();
 
   // codes of the two columns, 32 rows each -> LDS code tile [feature][pos]
 #pragma unroll
@@ -478,7 +490,9 @@ hipError_t launch_quantize_act(const QuantActParams &p, hipStream_t st) {
   // at least one tile: an empty tensor still gets its tensor scale written
   int64_t ytiles = col ? p.ld / QT : tiles_of(p.M);
   if (ytiles == 0) ytiles = 1;
-  dim3 grid((unsigned)ytiles, (unsigned)(p.C / QT), 1);
+  const int64_t tiles = ytiles * (p.C / QT);
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  dim3 grid((unsigned)tiles, 1, 1);
   return p.fmt == kE4M3 ? tile_by_recipe<kE4M3>(p.recipe, a, row, col, grid, st)
                         : tile_by_recipe<kE5M2>(p.recipe, a, row, col, grid, st);
 }
@@ -521,7 +535,9 @@ hipError_t launch_quantize_weight(const QuantWeightParams &p, hipStream_t st) {
     a.col_scales = p.kmajor_scales;
   }
   const bool row = p.nmajor_codes != nullptr, col = p.kmajor_codes != nullptr;
-  dim3 grid((unsigned)(p.K / QT), (unsigned)(p.N / QT), (unsigned)p.E);
+  const int64_t tiles = (p.K / QT) * (p.N / QT);
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  dim3 grid((unsigned)tiles, 1, (unsigned)p.E);
   return p.fmt == kE4M3 ? tile_by_recipe<kE4M3>(recipe, a, row, col, grid, st)
                         : tile_by_recipe<kE5M2>(recipe, a, row, col, grid, st);
 }
