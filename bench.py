@@ -48,7 +48,7 @@ def parse():
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (five times); "
                         "used to scale the HBM traffic counters")
-    p.add_argument("--cpu-sample-rows", type=int, default=512)
+    p.add_argument("--cpu-sample-rows", type=int, default=1024)
     p.add_argument("--cpu-sample-cols", type=int, default=28672)
     return p.parse_args()
 
