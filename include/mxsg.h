@@ -108,6 +108,36 @@ int32_t mxsg_version(void);
 int64_t mxsg_padded_capacity(int64_t M, int32_t E);
 
 /*
+ * Byte sizes of the buffers mxsg_quantize_act writes for tokens x [M, C]
+ * under `recipe`, with the column-wise output laid out for E groups
+ * (ld = mxsg_padded_capacity(M, E)); E = 0 asks for the row-wise sizes only.
+ * Pure host function: applies the same shape rules as mxsg_quantize_act
+ * (C a multiple of 128, M < 2^31) and returns their status.
+ *   bytes[0] row_codes      (M + (M & 1)) * C
+ *   bytes[1] row_scales     BLOCKWISE 4 * M * C/128, MX M * C/32, else 4
+ *   bytes[2] col_codes      C * ld                   (0 when E = 0)
+ *   bytes[3] col_scales     BLOCKWISE 4 * C * ld/128, MX C * ld/32, else 4
+ *   bytes[4] padded_starts  4 * (E + 1)              (0 when E = 0)
+ * Units and shape rule: the Transformer Engine "FP8BlockQuantizer not
+ * work" issue, design note (1x128 units; the blocked dimension divides by
+ * the block). The padded token layout of the column-wise output is that
+ * note's zero fill of partial blocks.
+ */
+mxsg_status mxsg_quantize_act_sizes(int64_t M, int64_t C, int32_t recipe, int32_t E,
+                                    int64_t bytes[5]);
+
+/*
+ * Byte sizes of the buffers mxsg_quantize_weight writes for w [E, K, N]:
+ *   bytes[0] kmajor_codes, bytes[2] nmajor_codes   E * K * N each
+ *   bytes[1] kmajor_scales, bytes[3] nmajor_scales BLOCKWISE 4 * E * K/128 * N/128,
+ *                                                  MX E * K * N / 32, else 4 * E
+ * Pure host function with the shape rules of mxsg_quantize_weight (K, N
+ * multiples of 128; 128x128 weight blocks of the same issue's design note).
+ */
+mxsg_status mxsg_quantize_weight_sizes(int32_t E, int64_t K, int64_t N, int32_t recipe,
+                                       int64_t bytes[4]);
+
+/*
  * Quantize a token-major tensor x [M, C] (routed-row activations or output
  * gradients), producing the row-wise operand (forward / dgrad) and/or the
  * column-wise operand (wgrad).
@@ -220,6 +250,19 @@ mxsg_status mxsg_grouped_mm(int32_t mode, int32_t recipe, int32_t fmt_a, int32_t
                             const void *a_scales, int64_t lda, const void *b_codes,
                             const void *b_scales, int64_t ldb, void *out, int32_t accumulate,
                             mxsg_stream_t stream);
+
+/*
+ * Validation of a mxsg_grouped_mm call without its pointers: the mode,
+ * recipe, formats, E, M, K, N, lda, ldb and accumulate rules documented
+ * above, returning the status (and mxsg_last_error text) mxsg_grouped_mm
+ * would return for them. Pure host function; launches nothing. The
+ * accumulate flag is the wgrad accumulation into an fp32 main gradient
+ * (Megatron-LM single grouped weight PR, gradient-accumulation-fusion
+ * coverage table).
+ */
+mxsg_status mxsg_grouped_mm_check(int32_t mode, int32_t recipe, int32_t fmt_a, int32_t fmt_b,
+                                  int32_t E, int64_t M, int64_t K, int64_t N, int64_t lda,
+                                  int64_t ldb, int32_t accumulate);
 
 /*
  * The device FP8 cast used by every quantizer (saturating round to nearest

@@ -11,8 +11,9 @@ products over per-expert token groups.
 """
 from __future__ import annotations
 
+import ctypes
 import dataclasses
-from typing import Optional
+from typing import List, Optional
 
 import torch
 
@@ -81,6 +82,29 @@ def pack_codes(t: torch.Tensor) -> torch.Tensor:
 
 def _scale_blocks(recipe: str) -> int:
     return {"block": 128, "mx": 32}.get(recipe, 0)
+
+
+def quantize_act_sizes(M: int, C: int, recipe: str, E: int = 0) -> List[int]:
+    """Byte sizes [row_codes, row_scales, col_codes, col_scales,
+    padded_starts] of mxsg_quantize_act's outputs (E = 0: row-wise only)."""
+    out = (ctypes.c_int64 * 5)()
+    _lib.call("mxsg_quantize_act_sizes", M, C, RECIPES[recipe], E, ctypes.addressof(out))
+    return list(out)
+
+
+def quantize_weight_sizes(E: int, K: int, N: int, recipe: str) -> List[int]:
+    """Byte sizes [kmajor_codes, kmajor_scales, nmajor_codes, nmajor_scales]
+    of mxsg_quantize_weight's outputs."""
+    out = (ctypes.c_int64 * 4)()
+    _lib.call("mxsg_quantize_weight_sizes", E, K, N, RECIPES[recipe], ctypes.addressof(out))
+    return list(out)
+
+
+def _buffer(nbytes: int, dtype: torch.dtype, cols: int, dev) -> torch.Tensor:
+    """A [nbytes / itemsize / cols, cols] tensor (cols = 0: a flat one)."""
+    n = nbytes // torch.empty(0, dtype=dtype).element_size()
+    t = torch.empty(n, dtype=dtype, device=dev)
+    return t.view(-1, cols) if cols else t
 
 
 @dataclasses.dataclass
@@ -154,20 +178,19 @@ def quantize_act(x: torch.Tensor, recipe: str, fmt, group_ends: Optional[torch.T
     E = int(group_ends.numel()) if group_ends is not None else 0
     q = out
     if q is None:
+        if colwise and group_ends is None:
+            raise ValueError("column-wise output needs group_ends")
         q = QuantAct(recipe, f, M, C)
         sdt = torch.uint8 if recipe == "mx" else torch.float32
+        nb = quantize_act_sizes(M, C, recipe, E if colwise else 0)
         if rowwise:
-            q.row_codes = torch.empty(M + (M & 1), C, dtype=torch.uint8, device=dev)
-            q.row_scales = (torch.empty(M, C // blk, dtype=sdt, device=dev) if blk
-                            else torch.empty(1, dtype=torch.float32, device=dev))
+            q.row_codes = _buffer(nb[0], torch.uint8, C, dev)
+            q.row_scales = _buffer(nb[1], sdt, C // blk if blk else 0, dev)
         if colwise:
-            if group_ends is None:
-                raise ValueError("column-wise output needs group_ends")
             q.ld = padded_capacity(M, E)
-            q.col_codes = torch.empty(C, q.ld, dtype=torch.uint8, device=dev)
-            q.col_scales = (torch.empty(C, q.ld // blk, dtype=sdt, device=dev) if blk
-                            else torch.empty(1, dtype=torch.float32, device=dev))
-            q.padded_starts = torch.empty(E + 1, dtype=torch.int32, device=dev)
+            q.col_codes = _buffer(nb[2], torch.uint8, q.ld, dev)
+            q.col_scales = _buffer(nb[3], sdt, q.ld // blk if blk else 0, dev)
+            q.padded_starts = _buffer(nb[4], torch.int32, 0, dev)
         if recipe == "tw":
             q.amax = torch.empty(1, dtype=torch.float32, device=dev)
     amax = q.amax
@@ -210,18 +233,19 @@ def quantize_weight(w: torch.Tensor, recipe: str, fmt, kmajor: bool = True, nmaj
     q = out
     if q is None:
         q = QuantWeight(recipe, f, E, K, N)
+        nb = quantize_weight_sizes(E, K, N, recipe)
         if recipe in ("tw", "dl"):
-            ks = ns = torch.empty(E, dtype=torch.float32, device=dev)
+            ks = ns = _buffer(nb[1], torch.float32, 0, dev)
         elif recipe == "block":
-            ks = ns = torch.empty(E, K // 128, N // 128, dtype=torch.float32, device=dev)
+            ks = ns = _buffer(nb[1], torch.float32, N // 128, dev).view(E, K // 128, N // 128)
         else:
-            ks = torch.empty(E, N, K // 32, dtype=torch.uint8, device=dev)
-            ns = torch.empty(E, K, N // 32, dtype=torch.uint8, device=dev)
+            ks = _buffer(nb[1], torch.uint8, K // 32, dev).view(E, N, K // 32)
+            ns = _buffer(nb[3], torch.uint8, N // 32, dev).view(E, K, N // 32)
         if kmajor:
-            q.kmajor_codes = torch.empty(E, N, K, dtype=torch.uint8, device=dev)
+            q.kmajor_codes = _buffer(nb[0], torch.uint8, K, dev).view(E, N, K)
             q.kmajor_scales = ks
         if nmajor:
-            q.nmajor_codes = torch.empty(E, K, N, dtype=torch.uint8, device=dev)
+            q.nmajor_codes = _buffer(nb[2], torch.uint8, N, dev).view(E, K, N)
             q.nmajor_scales = ns
         if recipe == "tw":
             q.amax = torch.empty(E, dtype=torch.float32, device=dev)

@@ -42,6 +42,29 @@ bool fmt_ok(int32_t f) { return f == MXSG_FMT_E4M3 || f == MXSG_FMT_E5M2; }
     if (!(cond)) return fail(code, __VA_ARGS__); \
   } while (0)
 
+// Shape rules shared by the size queries and the launching entry points;
+// fn names the caller in the error message.
+mxsg_status act_shape(const char *fn, int64_t M, int64_t C, int32_t recipe) {
+  REQUIRE(recipe_ok(recipe), MXSG_INVALID_ARGUMENT, "%s: unknown recipe %d", fn, recipe);
+  REQUIRE(M >= 0 && C > 0, MXSG_INVALID_ARGUMENT, "%s: M=%lld C=%lld", fn, (long long)M,
+          (long long)C);
+  REQUIRE(C % 128 == 0, MXSG_BAD_SHAPE, "%s: C=%lld is not a multiple of 128", fn, (long long)C);
+  REQUIRE(M <= ((int64_t)1 << 31) - 1 && C <= ((int64_t)1 << 31) - 1, MXSG_BAD_SHAPE,
+          "%s: M or C too large", fn);
+  return MXSG_OK;
+}
+
+mxsg_status weight_shape(const char *fn, int32_t E, int64_t K, int64_t N, int32_t recipe) {
+  REQUIRE(recipe_ok(recipe), MXSG_INVALID_ARGUMENT, "%s: unknown recipe %d", fn, recipe);
+  REQUIRE(E >= 1 && K > 0 && N > 0, MXSG_INVALID_ARGUMENT, "%s: E=%d K=%lld N=%lld", fn, E,
+          (long long)K, (long long)N);
+  REQUIRE(K % 128 == 0 && N % 128 == 0, MXSG_BAD_SHAPE,
+          "%s: K=%lld and N=%lld must be multiples of 128", fn, (long long)K, (long long)N);
+  // one workgroup per 128 x 128 tile of one expert, experts on grid.z
+  REQUIRE(E <= 65535 && (K / 128) * (N / 128) <= INT32_MAX, MXSG_BAD_SHAPE, "%s: too large", fn);
+  return MXSG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -66,25 +89,64 @@ int64_t mxsg_padded_capacity(int64_t M, int32_t E) {
   return ((M + 127 * (int64_t)E + 127) / 128) * 128;
 }
 
+mxsg_status mxsg_quantize_act_sizes(int64_t M, int64_t C, int32_t recipe, int32_t E,
+                                    int64_t bytes[5]) {
+  REQUIRE(bytes, MXSG_INVALID_ARGUMENT, "quantize_act_sizes: bytes is NULL");
+  mxsg_status st = act_shape("quantize_act_sizes", M, C, recipe);
+  if (st != MXSG_OK) return st;
+  REQUIRE(E >= 0 && E <= (1 << 20), MXSG_INVALID_ARGUMENT, "quantize_act_sizes: E=%d", E);
+  // scale bytes of n elements along a row: fp32 per 128, E8M0 per 32, or one fp32
+  auto scale_bytes = [recipe](int64_t rows, int64_t n) -> int64_t {
+    if (recipe == MXSG_RECIPE_BLOCKWISE) return rows * (n / 128) * 4;
+    if (recipe == MXSG_RECIPE_MX) return rows * (n / 32);
+    return 4;
+  };
+  bytes[0] = (M + (M & 1)) * C;
+  bytes[1] = scale_bytes(M, C);
+  if (E >= 1) {
+    const int64_t ld = mxsg_padded_capacity(M, E);
+    bytes[2] = C * ld;
+    bytes[3] = scale_bytes(C, ld);
+    bytes[4] = ((int64_t)E + 1) * 4;
+  } else {
+    bytes[2] = bytes[3] = bytes[4] = 0;
+  }
+  g_err[0] = 0;
+  return MXSG_OK;
+}
+
+mxsg_status mxsg_quantize_weight_sizes(int32_t E, int64_t K, int64_t N, int32_t recipe,
+                                       int64_t bytes[4]) {
+  REQUIRE(bytes, MXSG_INVALID_ARGUMENT, "quantize_weight_sizes: bytes is NULL");
+  mxsg_status st = weight_shape("quantize_weight_sizes", E, K, N, recipe);
+  if (st != MXSG_OK) return st;
+  const int64_t codes = (int64_t)E * K * N;
+  bytes[0] = bytes[2] = codes;
+  switch (recipe) {
+    case MXSG_RECIPE_BLOCKWISE: bytes[1] = bytes[3] = (int64_t)E * (K / 128) * (N / 128) * 4; break;
+    case MXSG_RECIPE_MX: bytes[1] = bytes[3] = codes / 32; break;
+    default: bytes[1] = bytes[3] = (int64_t)E * 4; break;
+  }
+  g_err[0] = 0;
+  return MXSG_OK;
+}
+
 mxsg_status mxsg_quantize_act(const void *x, int64_t M, int64_t C, int32_t recipe, int32_t fmt,
                               int32_t E, const int32_t *group_ends, void *row_codes,
                               void *row_scales, void *col_codes, void *col_scales, int64_t ld,
                               int32_t *padded_starts, float *amax, const float *dl_scale,
                               const float *dl_inv, mxsg_stream_t stream) {
-  REQUIRE(recipe_ok(recipe), MXSG_INVALID_ARGUMENT, "quantize_act: unknown recipe %d", recipe);
+  mxsg_status st = act_shape("quantize_act", M, C, recipe);
+  if (st != MXSG_OK) return st;
   REQUIRE(fmt_ok(fmt), MXSG_INVALID_ARGUMENT, "quantize_act: unknown format %d", fmt);
-  REQUIRE(M >= 0 && C > 0, MXSG_INVALID_ARGUMENT, "quantize_act: M=%lld C=%lld", (long long)M,
-          (long long)C);
-  REQUIRE(C % 128 == 0, MXSG_BAD_SHAPE, "quantize_act: C=%lld is not a multiple of 128",
-          (long long)C);
-  REQUIRE(M <= ((int64_t)1 << 31) - 1, MXSG_BAD_SHAPE, "quantize_act: M too large");
   REQUIRE(row_codes || col_codes, MXSG_INVALID_ARGUMENT, "quantize_act: no output requested");
   REQUIRE(M == 0 || x, MXSG_INVALID_ARGUMENT, "quantize_act: x is NULL");
   const bool scaled_unit = recipe == MXSG_RECIPE_BLOCKWISE || recipe == MXSG_RECIPE_MX;
   if (row_codes && scaled_unit)
     REQUIRE(row_scales, MXSG_INVALID_ARGUMENT, "quantize_act: row_scales is NULL");
   if (col_codes) {
-    REQUIRE(E >= 1, MXSG_INVALID_ARGUMENT, "quantize_act: column-wise output needs E >= 1");
+    REQUIRE(E >= 1 && E <= (1 << 20), MXSG_INVALID_ARGUMENT,
+            "quantize_act: column-wise output needs 1 <= E <= 2^20, got %d", E);
     REQUIRE(group_ends && padded_starts, MXSG_INVALID_ARGUMENT,
             "quantize_act: column-wise output needs group_ends and padded_starts");
     REQUIRE(ld % 128 == 0 && ld >= mxsg_padded_capacity(M, E), MXSG_BAD_SHAPE,
@@ -130,14 +192,9 @@ mxsg_status mxsg_quantize_weight(const void *w, int32_t E, int64_t K, int64_t N,
                                  void *nmajor_codes, void *nmajor_scales, float *amax,
                                  const float *dl_scale, const float *dl_inv,
                                  mxsg_stream_t stream) {
-  REQUIRE(recipe_ok(recipe), MXSG_INVALID_ARGUMENT, "quantize_weight: unknown recipe %d", recipe);
+  mxsg_status st = weight_shape("quantize_weight", E, K, N, recipe);
+  if (st != MXSG_OK) return st;
   REQUIRE(fmt_ok(fmt), MXSG_INVALID_ARGUMENT, "quantize_weight: unknown format %d", fmt);
-  REQUIRE(E >= 1 && K > 0 && N > 0, MXSG_INVALID_ARGUMENT, "quantize_weight: E=%d K=%lld N=%lld",
-          E, (long long)K, (long long)N);
-  REQUIRE(K % 128 == 0 && N % 128 == 0, MXSG_BAD_SHAPE,
-          "quantize_weight: K=%lld and N=%lld must be multiples of 128", (long long)K, (long long)N);
-  REQUIRE(E <= 65535 && (K / 128) * (N / 128) <= INT32_MAX, MXSG_BAD_SHAPE,
-          "quantize_weight: too large");
   REQUIRE(w, MXSG_INVALID_ARGUMENT, "quantize_weight: w is NULL");
   REQUIRE(kmajor_codes || nmajor_codes, MXSG_INVALID_ARGUMENT, "quantize_weight: no output");
   if (kmajor_codes) REQUIRE(kmajor_scales, MXSG_INVALID_ARGUMENT, "quantize_weight: kmajor_scales NULL");
@@ -178,12 +235,9 @@ mxsg_status mxsg_delayed_update(float *history, int32_t *pos, float *amax, float
                   "delayed_update");
 }
 
-mxsg_status mxsg_grouped_mm(int32_t mode, int32_t recipe, int32_t fmt_a, int32_t fmt_b, int32_t E,
-                            int64_t M, int64_t K, int64_t N, const int32_t *group_ends,
-                            const int32_t *padded_starts, const void *a_codes,
-                            const void *a_scales, int64_t lda, const void *b_codes,
-                            const void *b_scales, int64_t ldb, void *out, int32_t accumulate,
-                            mxsg_stream_t stream) {
+mxsg_status mxsg_grouped_mm_check(int32_t mode, int32_t recipe, int32_t fmt_a, int32_t fmt_b,
+                                  int32_t E, int64_t M, int64_t K, int64_t N, int64_t lda,
+                                  int64_t ldb, int32_t accumulate) {
   REQUIRE(mode >= MXSG_MODE_FWD && mode <= MXSG_MODE_WGRAD, MXSG_INVALID_ARGUMENT,
           "grouped_mm: unknown mode %d", mode);
   REQUIRE(recipe_ok(recipe), MXSG_INVALID_ARGUMENT, "grouped_mm: unknown recipe %d", recipe);
@@ -198,12 +252,9 @@ mxsg_status mxsg_grouped_mm(int32_t mode, int32_t recipe, int32_t fmt_a, int32_t
   // the kernel addresses a tile's 256 rows with 32-bit offsets
   REQUIRE(lda < ((int64_t)1 << 23) && ldb < ((int64_t)1 << 23), MXSG_BAD_SHAPE,
           "grouped_mm: row strides must be below 2^23");
-  REQUIRE(a_codes && b_codes && out && a_scales && b_scales && group_ends, MXSG_INVALID_ARGUMENT,
-          "grouped_mm: NULL operand");
   REQUIRE(accumulate == 0 || mode == MXSG_MODE_WGRAD, MXSG_INVALID_ARGUMENT,
           "grouped_mm: accumulate is only defined for WGRAD");
   if (mode == MXSG_MODE_WGRAD) {
-    REQUIRE(padded_starts, MXSG_INVALID_ARGUMENT, "grouped_mm: WGRAD needs padded_starts");
     const int64_t cap = mxsg_padded_capacity(M, E);
     REQUIRE(lda % 128 == 0 && ldb % 128 == 0 && lda >= cap && ldb >= cap, MXSG_BAD_SHAPE,
             "grouped_mm: WGRAD lda=%lld ldb=%lld must be multiples of 128 and >= %lld",
@@ -218,6 +269,22 @@ mxsg_status mxsg_grouped_mm(int32_t mode, int32_t recipe, int32_t fmt_a, int32_t
     REQUIRE(recipe != MXSG_RECIPE_BLOCKWISE || L <= 65536, MXSG_UNSUPPORTED,
             "grouped_mm: blockwise contraction %lld > 65536 is not built", (long long)L);
   }
+  g_err[0] = 0;
+  return MXSG_OK;
+}
+
+mxsg_status mxsg_grouped_mm(int32_t mode, int32_t recipe, int32_t fmt_a, int32_t fmt_b, int32_t E,
+                            int64_t M, int64_t K, int64_t N, const int32_t *group_ends,
+                            const int32_t *padded_starts, const void *a_codes,
+                            const void *a_scales, int64_t lda, const void *b_codes,
+                            const void *b_scales, int64_t ldb, void *out, int32_t accumulate,
+                            mxsg_stream_t stream) {
+  mxsg_status st = mxsg_grouped_mm_check(mode, recipe, fmt_a, fmt_b, E, M, K, N, lda, ldb, accumulate);
+  if (st != MXSG_OK) return st;
+  REQUIRE(a_codes && b_codes && out && a_scales && b_scales && group_ends, MXSG_INVALID_ARGUMENT,
+          "grouped_mm: NULL operand");
+  REQUIRE(mode != MXSG_MODE_WGRAD || padded_starts, MXSG_INVALID_ARGUMENT,
+          "grouped_mm: WGRAD needs padded_starts");
   mxsg::GemmParams p{};
   p.mode = mode;
   p.recipe = recipe;

@@ -109,8 +109,99 @@ def test_grouped_mm_validation():
     assert _mm(ldb=512) == _lib.BAD_SHAPE                  # ldb must equal K
     assert _mm(out=None) == _lib.INVALID_ARGUMENT
     assert _mm(acc=1) == _lib.INVALID_ARGUMENT             # accumulate is wgrad-only
-    assert _mm(mode=2, ps=None) == _lib.INVALID_ARGUMENT   # wgrad needs padded starts
+    assert _mm(mode=2, ps=None, lda=640, ldb=640) == _lib.INVALID_ARGUMENT  # needs padded starts
     assert _mm(mode=2, ps=FAKE, lda=128, ldb=128) == _lib.BAD_SHAPE  # ld below capacity
+
+
+def _act_sizes(M, C, recipe, E):
+    out = (ctypes.c_int64 * 5)()
+    st = _lib.status_of("mxsg_quantize_act_sizes", M, C, recipe, E, ctypes.addressof(out))
+    return st, list(out)
+
+
+def _w_sizes(E, K, N, recipe):
+    out = (ctypes.c_int64 * 4)()
+    st = _lib.status_of("mxsg_quantize_weight_sizes", E, K, N, recipe, ctypes.addressof(out))
+    return st, list(out)
+
+
+@pytest.mark.parametrize("M,C,E", [(0, 128, 1), (1, 128, 1), (7, 256, 3), (1000, 384, 8),
+                                   (65536, 4096, 64), (5, 128, 0)])
+def test_quantize_act_sizes(M, C, E):
+    lib = _lib.load()
+    ld = lib.mxsg_padded_capacity(M, E) if E else 0
+    rows = M + (M % 2)                                  # rows are stored in pairs
+    for recipe, row_s, col_s in [(0, 4, 4), (1, 4, 4),
+                                 (2, 4 * M * (C // 128), 4 * C * (ld // 128)),
+                                 (3, M * (C // 32), C * (ld // 32))]:
+        st, b = _act_sizes(M, C, recipe, E)
+        assert st == _lib.OK
+        assert b[0] == rows * C and b[1] == row_s
+        if E:
+            assert b[2:] == [C * ld, col_s, 4 * (E + 1)]
+        else:
+            assert b[2:] == [0, 0, 0]
+
+
+def test_quantize_act_sizes_validation():
+    assert _act_sizes(16, 200, 0, 1)[0] == _lib.BAD_SHAPE
+    assert _act_sizes(-1, 128, 0, 1)[0] == _lib.INVALID_ARGUMENT
+    assert _act_sizes(16, 128, 4, 1)[0] == _lib.INVALID_ARGUMENT
+    assert _act_sizes(16, 128, 0, -1)[0] == _lib.INVALID_ARGUMENT
+    assert _act_sizes(1 << 31, 128, 0, 1)[0] == _lib.BAD_SHAPE
+    assert _lib.status_of("mxsg_quantize_act_sizes", 16, 128, 0, 1, None) == _lib.INVALID_ARGUMENT
+    # the same shape rule answers the launching call the same way
+    assert _qact(C=200) == _act_sizes(16, 200, 0, 1)[0]
+
+
+@pytest.mark.parametrize("E,K,N", [(1, 128, 128), (8, 4096, 14336), (3, 256, 640)])
+def test_quantize_weight_sizes(E, K, N):
+    for recipe, sc in [(0, 4 * E), (1, 4 * E), (2, 4 * E * (K // 128) * (N // 128)),
+                       (3, E * K * N // 32)]:
+        st, b = _w_sizes(E, K, N, recipe)
+        assert st == _lib.OK
+        assert b == [E * K * N, sc, E * K * N, sc]
+
+
+def test_quantize_weight_sizes_validation():
+    assert _w_sizes(2, 130, 256, 0)[0] == _lib.BAD_SHAPE
+    assert _w_sizes(0, 128, 128, 0)[0] == _lib.INVALID_ARGUMENT
+    assert _w_sizes(1 << 16, 128, 128, 0)[0] == _lib.BAD_SHAPE
+    assert _w_sizes(2, 128, 128, 5)[0] == _lib.INVALID_ARGUMENT
+    assert _qw(K=130) == _w_sizes(2, 130, 256, 0)[0]
+
+
+def _mm_check(**kw):
+    args = dict(mode=0, recipe=0, fa=0, fb=0, E=4, M=64, K=256, N=256, lda=256, ldb=256, acc=0)
+    args.update(kw)
+    return _lib.status_of("mxsg_grouped_mm_check", *args.values())
+
+
+def test_grouped_mm_check_agrees_with_launcher():
+    """Over a grid of shape arguments (pointers all valid), the host-only
+    check and the launching call return the same status; every case here
+    fails validation or would launch, so only failing ones go to the
+    launcher."""
+    lib = _lib.load()
+    seen = set()
+    for mode in (0, 1, 2, 3):
+        for recipe in (0, 2, 3, 5):
+            for fa, fb in ((0, 0), (1, 0), (1, 1)):
+                for K, N in ((256, 256), (200, 256), (256, 384)):
+                    for lda, ldb in ((256, 256), (128, 256), (384, 384), (1024, 1024)):
+                        for acc in (0, 1):
+                            kw = dict(mode=mode, recipe=recipe, fa=fa, fb=fb, K=K, N=N, lda=lda,
+                                      ldb=ldb, acc=acc)
+                            st = _mm_check(**kw)
+                            seen.add(st)
+                            if st != _lib.OK:
+                                msg = lib.mxsg_last_error()
+                                assert _mm(ps=FAKE, **kw) == st, kw
+                                assert lib.mxsg_last_error() == msg
+    assert seen == {_lib.OK, _lib.INVALID_ARGUMENT, _lib.BAD_SHAPE, _lib.UNSUPPORTED}
+    assert _mm_check(mode=2, lda=128, ldb=128) == _lib.BAD_SHAPE
+    assert _mm_check(mode=2, lda=1024, ldb=1024) == _lib.OK
+    assert _mm_check(mode=1, recipe=2, N=65536 + 128, lda=65536 + 128, ldb=65536 + 128) == _lib.UNSUPPORTED
 
 
 def test_delayed_and_sweep_validation():
