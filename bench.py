@@ -2,9 +2,10 @@
 """Benchmark of the quantized MoE expert grouped GEMM on one MI355X.
 
 One step = the whole hot path over one batch of synthetic routed rows:
-quantize activations, expert weights and output gradients, then the
-grouped GEMMs (forward, dgrad, wgrad for both expert GEMMs) and, for
-delayed scaling, the amax-history update.
+quantize activations (the gate/up input gathered from the token tensor
+through the routing index inside the quantization kernel), expert weights
+and output gradients, then the grouped GEMMs (forward, dgrad, wgrad for
+both expert GEMMs) and, for delayed scaling, the amax-history update.
 
 Default workload: Mixtral-8x7B-shaped experts (8 experts, hidden 4096,
 ffn 14336, 8192 tokens top-2 = 16384 routed rows) with delayed scaling
@@ -89,8 +90,10 @@ def make_inputs(cid, torch, W, sets=2):
     for s in range(sets):
         drift = 1.01 ** s if cid == 3 else 1.0
         x = outliers(normal((spec.tokens, gu_k), drift))
-        d = {"a_gu": x.index_select(0, row_token).contiguous()}
-        del x
+        # x_gu: the token tensor the step quantizes through the routing index
+        # (gather fused into the quantization); a_gu: the same routed rows as
+        # an explicit copy, for checks against the oracle
+        d = {"x_gu": x, "a_gu": x.index_select(0, row_token).contiguous()}
         if "dn" in spec.gemms:
             d["a_dn"] = outliers(normal((R, dn_k), drift))
         if "dgrad" in spec.modes:
@@ -102,14 +105,20 @@ def make_inputs(cid, torch, W, sets=2):
     return spec, r, ge, weights, sets_out
 
 
+def routing_index(r, torch):
+    """int32 routed-row -> token index on the GPU (the gather of the gate/up input)."""
+    return torch.from_numpy(r.row_token.astype("int32")).to("cuda")
+
+
 # ---------------------------------------------------------------------------
 
 class Step:
     """One pass of the hot path; every call's duration is recorded with HIP
     events on the stream the kernels run on (torch's current stream)."""
 
-    def __init__(self, torch, api, spec, ge, weights, recipe):
+    def __init__(self, torch, api, spec, ge, weights, recipe, row_index=None):
         self.torch, self.api, self.spec, self.ge, self.weights = torch, api, spec, ge, weights
+        self.row_index = row_index   # routed row -> token; None: a_gu is already gathered
         self.recipe = recipe
         self.fa, self.fg = 0, (1 if recipe == "dl" else 0)     # hybrid: e5m2 gradients
         self.E = spec.experts
@@ -146,6 +155,10 @@ class Step:
             kw = {}
             if r == "dl":
                 kw = dict(state=self.st_f, unit=gi)
+            if which == "gu" and self.row_index is not None:
+                # the routed rows are gathered from the tokens inside the kernel
+                a = data["x_gu"]
+                kw["row_index"] = self.row_index
             qa = self._t(f"quant_a_{which}", lambda: api.quantize_act(
                 a, r, self.fa, self.ge, rowwise=True, colwise=bwd, out=self.q.get("a_" + which), **kw))
             self.q["a_" + which] = qa
@@ -190,6 +203,36 @@ class Step:
                 flops[f"gemm_wgrad_{which}"] = f
                 byts[f"quant_dy_{which}"] = R * N * (read + 2 * per_layout)
         return flops, byts
+
+
+def attainable_ms(spec, group_sizes, modes):
+    """Roofline time of each GEMM call: sum over groups of max(FLOPs / MFMA
+    peak, bytes / HBM peak), with a group's algorithmic bytes = its FP8
+    operand codes read once plus its output written once (bf16 for forward
+    and dgrad, fp32 dW for wgrad; an empty group still writes its zero dW)."""
+    out = {}
+    for which in spec.gemms:
+        K, N = spec.gemm_shape(which)
+        for mode in modes:
+            t = 0.0
+            for m in group_sizes:
+                m = int(m)
+                f = 2.0 * m * K * N
+                if mode == "fwd":
+                    b = (m * K + K * N + 2 * m * N) if m else 0
+                elif mode == "dgrad":
+                    b = (m * N + K * N + 2 * m * K) if m else 0
+                else:
+                    b = m * K + m * N + 4 * K * N
+                t = t + max(f / (PEAK_FP8_TFLOPS * 1e12), b / (PEAK_HBM_GBS * 1e9))
+            out[f"gemm_{mode}_{which}"] = t * 1e3
+    return out
+
+
+def percentiles(v):
+    """p10, median, p90 of a list of per-call times (ms)."""
+    import numpy as np
+    return [round(float(x), 4) for x in np.percentile(np.asarray(v, dtype=np.float64), [10, 50, 90])]
 
 
 def cpu_baseline(cid, rows, cols):
@@ -286,7 +329,7 @@ def main():
     print(f"# generating inputs for {W.SPECS[cid].name}", file=sys.stderr, flush=True)
     spec, routing, ge, weights, sets = make_inputs(cid, torch, W)
     R = routing.rows
-    step = Step(torch, api, spec, ge, weights, spec.recipe)
+    step = Step(torch, api, spec, ge, weights, spec.recipe, row_index=routing_index(routing, torch))
     torch.cuda.synchronize()
     print("# warmup", file=sys.stderr, flush=True)
     for i in range(args.warmup):
@@ -326,6 +369,33 @@ def main():
     launches = len(gemm_ms)
     achieved = step_flops / (gemm_total_ms * 1e-3) / 1e12
     quant_agg = sum(byts.values()) / (quant_total_ms * 1e-3) / 1e9
+    att = attainable_ms(spec, routing.group_sizes, spec.modes)
+    att_frac = {k: att[k] / gemm_ms[k] for k in gemm_ms}
+    att_total = sum(att[k] for k in gemm_ms) / gemm_total_ms
+
+    # reference copy rates on the same GPU, 1 GiB device to device: the
+    # library's streaming copy (16-byte streaming loads and stores, the
+    # practical HBM ceiling the quantization passes are compared with next to
+    # the 8 TB/s datasheet figure) and torch's own copy
+    n_copy = 1 << 30
+    src = torch.ones(n_copy, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+
+    def copy_rate(fn):
+        fn()
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        c0.record()
+        for _ in range(5):
+            fn()
+        c1.record()
+        torch.cuda.synchronize()
+        return 2 * n_copy * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+
+    copy_gbs = copy_rate(lambda: api.stream_copy(src, dst))
+    torch_copy_gbs = copy_rate(lambda: dst.copy_(src))
+    del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -364,6 +434,13 @@ def main():
             "quant_gbs": {k: round(v, 1) for k, v in quant_gbs.items()},
             "quant_gbs_total": round(quant_agg, 1),
             "quant_hbm_frac": round(quant_agg / PEAK_HBM_GBS, 4),
+            "copy_1gib_gbs": round(copy_gbs, 1),
+            "torch_copy_1gib_gbs": round(torch_copy_gbs, 1),
+            "quant_copy_frac": round(quant_agg / copy_gbs, 4),
+            "gemm_attainable_ms": {k: round(att[k], 4) for k in gemm_ms},
+            "gemm_attainable_frac": {k: round(v, 4) for k, v in att_frac.items()},
+            "gemm_attainable_frac_total": round(att_total, 4),
+            "call_ms_p10_p50_p90": {k: percentiles(v) for k, v in per.items()},
             "gemm_ms_total": round(gemm_total_ms, 4),
             "quant_ms_total": round(quant_total_ms, 4),
             "wall_s": round(wall, 3),

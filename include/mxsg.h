@@ -169,6 +169,28 @@ mxsg_status mxsg_quantize_act(const void *x, int64_t M, int64_t C, int32_t recip
                               const float *dl_inv, mxsg_stream_t stream);
 
 /*
+ * mxsg_quantize_act on routed rows gathered from a token tensor: x is
+ * [T, C] (one row per token) and routed row i, i < M, is x row
+ * row_index[i] (int32 [M], device). This is the MoE dispatch permutation
+ * that puts each token's copies in expert order in front of the grouped
+ * GEMM (the torchao float8 MoE training PR overrides grouped_mm for the
+ * routed experts, Limitations; its offsets imply rows contiguous per
+ * expert), fused with the quantization so the permuted bf16 copy is never
+ * written. Results equal mxsg_quantize_act on the tensor x[row_index];
+ * tensorwise amax is taken over the routed rows only. Indices outside
+ * [0, T) are clamped on the device (wrong rows, never out-of-bounds
+ * reads); a token may appear any number of times or not at all. Every
+ * other argument, output and rule is that of mxsg_quantize_act with
+ * M = routed rows; mxsg_quantize_act_sizes gives the output sizes.
+ */
+mxsg_status mxsg_quantize_act_gather(const void *x, int64_t T, const int32_t *row_index, int64_t M,
+                                     int64_t C, int32_t recipe, int32_t fmt, int32_t E,
+                                     const int32_t *group_ends, void *row_codes, void *row_scales,
+                                     void *col_codes, void *col_scales, int64_t ld,
+                                     int32_t *padded_starts, float *amax, const float *dl_scale,
+                                     const float *dl_inv, mxsg_stream_t stream);
+
+/*
  * Quantize expert weights w [E, K, N] (the single contiguous grouped weight
  * of the Megatron-LM PR), into the forward operand (k-major codes
  * [E, N, K], contiguous along K) and/or the dgrad operand (n-major codes
@@ -273,6 +295,14 @@ mxsg_status mxsg_grouped_mm_check(int32_t mode, int32_t recipe, int32_t fmt_a, i
  */
 mxsg_status mxsg_cast_sweep(uint32_t start_bits, int64_t n, int32_t fmt, void *out,
                             mxsg_stream_t stream);
+
+/*
+ * Device-to-device copy of `bytes` (a multiple of 16; both pointers 16-byte
+ * aligned) with one 16-byte streaming load and store per thread. Not a step
+ * of the method: it is the HBM reference rate the quantization passes are
+ * measured against, next to the datasheet bandwidth.
+ */
+mxsg_status mxsg_stream_copy(const void *src, void *dst, int64_t bytes, mxsg_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -162,16 +162,26 @@ class QuantAct:
 def quantize_act(x: torch.Tensor, recipe: str, fmt, group_ends: Optional[torch.Tensor] = None,
                  rowwise: bool = True, colwise: bool = False,
                  state: Optional[DelayedState] = None, unit: int = 0,
-                 out: Optional[QuantAct] = None) -> QuantAct:
+                 out: Optional[QuantAct] = None,
+                 row_index: Optional[torch.Tensor] = None) -> QuantAct:
     """Quantize a token-major bf16 tensor [M, C] (mxsg_quantize_act).
 
     recipe "dl" takes its scale from ``state`` unit ``unit`` and records
     the amax there. Column-wise output needs ``group_ends`` (int32 [E]).
     ``out`` reuses previously allocated outputs of the same shape.
+    With ``row_index`` (int32 [M]) the operand is the routed rows
+    x[row_index] of a token tensor x [T, C], gathered inside the kernel
+    (mxsg_quantize_act_gather).
     """
     x = _bits16(x)
-    _check_dev(x, group_ends)
-    M, C = x.shape
+    _check_dev(x, group_ends, row_index)
+    T, C = x.shape
+    if row_index is not None:
+        if row_index.dtype != torch.int32 or row_index.dim() != 1:
+            raise TypeError("row_index must be a 1-D int32 tensor")
+        M = int(row_index.numel())
+    else:
+        M = T
     f = FMT[fmt]
     dev = x.device
     blk = _scale_blocks(recipe)
@@ -201,9 +211,14 @@ def quantize_act(x: torch.Tensor, recipe: str, fmt, group_ends: Optional[torch.T
         amax = state.amax[unit:unit + 1]
         dls = state.scale[unit:unit + 1]
         dli = state.inv[unit:unit + 1]
-    _lib.call("mxsg_quantize_act", _ptr(x), M, C, RECIPES[recipe], f, E, _ptr(group_ends),
-              _ptr(q.row_codes), _ptr(q.row_scales), _ptr(q.col_codes), _ptr(q.col_scales),
-              q.ld, _ptr(q.padded_starts), _ptr(amax), _ptr(dls), _ptr(dli), _stream())
+    outs = (E, _ptr(group_ends), _ptr(q.row_codes), _ptr(q.row_scales), _ptr(q.col_codes),
+            _ptr(q.col_scales), q.ld, _ptr(q.padded_starts), _ptr(amax), _ptr(dls), _ptr(dli),
+            _stream())
+    if row_index is None:
+        _lib.call("mxsg_quantize_act", _ptr(x), M, C, RECIPES[recipe], f, *outs)
+    else:
+        _lib.call("mxsg_quantize_act_gather", _ptr(x), T, _ptr(row_index), M, C, RECIPES[recipe],
+                  f, *outs)
     return q
 
 
@@ -315,3 +330,13 @@ def cast_sweep(start_bits: int, n: int, fmt, out: Optional[torch.Tensor] = None)
         out = torch.empty(n, dtype=torch.uint8, device="cuda")
     _lib.call("mxsg_cast_sweep", start_bits & 0xFFFFFFFF, n, FMT[fmt], _ptr(out), _stream())
     return out
+
+
+def stream_copy(src: torch.Tensor, dst: torch.Tensor) -> None:
+    """Device copy of src's bytes into dst (mxsg_stream_copy): the HBM
+    reference rate for the quantization passes."""
+    _check_dev(src, dst)
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst is smaller than src")
+    _lib.call("mxsg_stream_copy", _ptr(src), _ptr(dst), n, _stream())

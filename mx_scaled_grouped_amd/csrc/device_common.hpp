@@ -160,6 +160,24 @@ __device__ __forceinline__ void atomic_max_bits(uint32_t *p, uint32_t v) {
 // 128 bytes that each hold 64 bytes of row 2p followed by the same 64 bytes
 // of row 2p+1. A GEMM stage of 64 contraction bytes over an even run of rows
 // is then whole 128-byte lines.
+// Streaming (nontemporal) 16- and 8-byte global accesses: data read or
+// written exactly once by a pass that moves far more bytes than the caches
+// hold bypasses them instead of evicting what other passes reuse.
+typedef unsigned int nt_v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int nt_v2u __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 load16_stream(const void *p) {
+  const nt_v4u v = __builtin_nontemporal_load(reinterpret_cast<const nt_v4u *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store16_stream(void *p, uint4 v) {
+  const nt_v4u w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<nt_v4u *>(p));
+}
+__device__ __forceinline__ void store8_stream(void *p, uint2 v) {
+  const nt_v2u w = {v.x, v.y};
+  __builtin_nontemporal_store(w, reinterpret_cast<nt_v2u *>(p));
+}
+
 __device__ __forceinline__ int64_t pi_off(int64_t r, int64_t l, int64_t L) {
   return (r >> 1) * (2 * L) + ((l >> 6) << 7) + ((r & 1) << 6) + (l & 63);
 }

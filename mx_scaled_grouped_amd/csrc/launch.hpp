@@ -20,6 +20,8 @@ struct QuantActParams {
   int32_t *padded_starts;
   float *amax;
   const float *dl_scale, *dl_inv;
+  const int32_t *row_index;  // optional: routed row i is x row row_index[i]
+  int64_t src_rows;          // rows of x when row_index is given
 };
 
 struct QuantWeightParams {
@@ -57,6 +59,7 @@ hipError_t launch_quantize_weight(const QuantWeightParams &p, hipStream_t st);
 hipError_t launch_delayed_update(float *hist, int32_t *pos, float *amax, float *scale, float *inv,
                                  int units, int L, int fmt, hipStream_t st);
 hipError_t launch_cast_sweep(uint32_t start, int64_t n, int fmt, uint8_t *out, hipStream_t st);
+hipError_t launch_stream_copy(const void *src, void *dst, int64_t bytes, hipStream_t st);
 hipError_t launch_grouped_mm(const GemmParams &p, hipStream_t st);
 
 }  // namespace mxsg

@@ -67,6 +67,71 @@ mxsg_status weight_shape(const char *fn, int32_t E, int64_t K, int64_t N, int32_
 
 }  // namespace
 
+static mxsg_status quantize_act_impl(const char *fn, const void *x, int64_t T,
+                                     const int32_t *row_index, int64_t M, int64_t C,
+                                     int32_t recipe, int32_t fmt, int32_t E,
+                                     const int32_t *group_ends, void *row_codes, void *row_scales,
+                                     void *col_codes, void *col_scales, int64_t ld,
+                                     int32_t *padded_starts, float *amax, const float *dl_scale,
+                                     const float *dl_inv, mxsg_stream_t stream) {
+  mxsg_status st = act_shape(fn, M, C, recipe);
+  if (st != MXSG_OK) return st;
+  REQUIRE(fmt_ok(fmt), MXSG_INVALID_ARGUMENT, "%s: unknown format %d", fn, fmt);
+  REQUIRE(row_codes || col_codes, MXSG_INVALID_ARGUMENT, "%s: no output requested", fn);
+  REQUIRE(M == 0 || x, MXSG_INVALID_ARGUMENT, "%s: x is NULL", fn);
+  if (row_index || T != M) {  // gathered rows: an index per routed row into x [T, C]
+    REQUIRE(M == 0 || row_index, MXSG_INVALID_ARGUMENT, "%s: row_index is NULL", fn);
+    REQUIRE(T >= 0 && T <= ((int64_t)1 << 31) - 1 && (M == 0 || T > 0), MXSG_BAD_SHAPE,
+            "%s: x has %lld rows for %lld routed rows", fn, (long long)T, (long long)M);
+  }
+  const bool scaled_unit = recipe == MXSG_RECIPE_BLOCKWISE || recipe == MXSG_RECIPE_MX;
+  if (row_codes && scaled_unit)
+    REQUIRE(row_scales, MXSG_INVALID_ARGUMENT, "%s: row_scales is NULL", fn);
+  if (col_codes) {
+    REQUIRE(E >= 1 && E <= (1 << 20), MXSG_INVALID_ARGUMENT,
+            "%s: column-wise output needs 1 <= E <= 2^20, got %d", fn, E);
+    REQUIRE(group_ends && padded_starts, MXSG_INVALID_ARGUMENT,
+            "%s: column-wise output needs group_ends and padded_starts", fn);
+    REQUIRE(ld % 128 == 0 && ld >= mxsg_padded_capacity(M, E), MXSG_BAD_SHAPE,
+            "%s: ld=%lld must be a multiple of 128 and >= %lld", fn, (long long)ld,
+            (long long)mxsg_padded_capacity(M, E));
+    if (scaled_unit)
+      REQUIRE(col_scales, MXSG_INVALID_ARGUMENT, "%s: col_scales is NULL", fn);
+  }
+  if (recipe == MXSG_RECIPE_TENSORWISE || recipe == MXSG_RECIPE_DELAYED)
+    REQUIRE(amax, MXSG_INVALID_ARGUMENT, "%s: amax is NULL", fn);
+  if (recipe == MXSG_RECIPE_DELAYED)
+    REQUIRE(dl_scale && dl_inv, MXSG_INVALID_ARGUMENT, "%s: dl_scale/dl_inv NULL", fn);
+  {
+    // one workgroup per 128 x 128 tile (row tiles, or padded-column tiles)
+    const int64_t rt = col_codes ? ld / 128 : (M + 127) / 128;
+    REQUIRE((rt > 0 ? rt : 1) * (C / 128) <= INT32_MAX, MXSG_BAD_SHAPE,
+            "%s: %lld x %lld tiles exceed the launch limit", fn, (long long)rt,
+            (long long)(C / 128));
+  }
+
+  mxsg::QuantActParams p{};
+  p.x = static_cast<const uint16_t *>(x);
+  p.M = M;
+  p.C = C;
+  p.recipe = recipe;
+  p.fmt = fmt;
+  p.E = col_codes ? E : 0;
+  p.group_ends = group_ends;
+  p.row_codes = static_cast<uint8_t *>(row_codes);
+  p.row_scales = row_scales;
+  p.col_codes = static_cast<uint8_t *>(col_codes);
+  p.col_scales = col_scales;
+  p.ld = ld;
+  p.padded_starts = padded_starts;
+  p.amax = amax;
+  p.dl_scale = dl_scale;
+  p.dl_inv = dl_inv;
+  p.row_index = row_index;
+  p.src_rows = T;
+  return from_hip(mxsg::launch_quantize_act(p, static_cast<hipStream_t>(stream)), fn);
+}
+
 extern "C" {
 
 const char *mxsg_status_str(mxsg_status s) {
@@ -136,55 +201,21 @@ mxsg_status mxsg_quantize_act(const void *x, int64_t M, int64_t C, int32_t recip
                               void *row_scales, void *col_codes, void *col_scales, int64_t ld,
                               int32_t *padded_starts, float *amax, const float *dl_scale,
                               const float *dl_inv, mxsg_stream_t stream) {
-  mxsg_status st = act_shape("quantize_act", M, C, recipe);
-  if (st != MXSG_OK) return st;
-  REQUIRE(fmt_ok(fmt), MXSG_INVALID_ARGUMENT, "quantize_act: unknown format %d", fmt);
-  REQUIRE(row_codes || col_codes, MXSG_INVALID_ARGUMENT, "quantize_act: no output requested");
-  REQUIRE(M == 0 || x, MXSG_INVALID_ARGUMENT, "quantize_act: x is NULL");
-  const bool scaled_unit = recipe == MXSG_RECIPE_BLOCKWISE || recipe == MXSG_RECIPE_MX;
-  if (row_codes && scaled_unit)
-    REQUIRE(row_scales, MXSG_INVALID_ARGUMENT, "quantize_act: row_scales is NULL");
-  if (col_codes) {
-    REQUIRE(E >= 1 && E <= (1 << 20), MXSG_INVALID_ARGUMENT,
-            "quantize_act: column-wise output needs 1 <= E <= 2^20, got %d", E);
-    REQUIRE(group_ends && padded_starts, MXSG_INVALID_ARGUMENT,
-            "quantize_act: column-wise output needs group_ends and padded_starts");
-    REQUIRE(ld % 128 == 0 && ld >= mxsg_padded_capacity(M, E), MXSG_BAD_SHAPE,
-            "quantize_act: ld=%lld must be a multiple of 128 and >= %lld", (long long)ld,
-            (long long)mxsg_padded_capacity(M, E));
-    if (scaled_unit)
-      REQUIRE(col_scales, MXSG_INVALID_ARGUMENT, "quantize_act: col_scales is NULL");
-  }
-  if (recipe == MXSG_RECIPE_TENSORWISE || recipe == MXSG_RECIPE_DELAYED)
-    REQUIRE(amax, MXSG_INVALID_ARGUMENT, "quantize_act: amax is NULL");
-  if (recipe == MXSG_RECIPE_DELAYED)
-    REQUIRE(dl_scale && dl_inv, MXSG_INVALID_ARGUMENT, "quantize_act: dl_scale/dl_inv NULL");
-  {
-    // one workgroup per 128 x 128 tile (row tiles, or padded-column tiles)
-    const int64_t rt = col_codes ? ld / 128 : (M + 127) / 128;
-    REQUIRE((rt > 0 ? rt : 1) * (C / 128) <= INT32_MAX, MXSG_BAD_SHAPE,
-            "quantize_act: %lld x %lld tiles exceed the launch limit", (long long)rt,
-            (long long)(C / 128));
-  }
+  return quantize_act_impl("quantize_act", x, M, nullptr, M, C, recipe, fmt, E, group_ends,
+                           row_codes, row_scales, col_codes, col_scales, ld, padded_starts, amax,
+                           dl_scale, dl_inv, stream);
+}
 
-  mxsg::QuantActParams p{};
-  p.x = static_cast<const uint16_t *>(x);
-  p.M = M;
-  p.C = C;
-  p.recipe = recipe;
-  p.fmt = fmt;
-  p.E = col_codes ? E : 0;
-  p.group_ends = group_ends;
-  p.row_codes = static_cast<uint8_t *>(row_codes);
-  p.row_scales = row_scales;
-  p.col_codes = static_cast<uint8_t *>(col_codes);
-  p.col_scales = col_scales;
-  p.ld = ld;
-  p.padded_starts = padded_starts;
-  p.amax = amax;
-  p.dl_scale = dl_scale;
-  p.dl_inv = dl_inv;
-  return from_hip(mxsg::launch_quantize_act(p, static_cast<hipStream_t>(stream)), "quantize_act");
+mxsg_status mxsg_quantize_act_gather(const void *x, int64_t T, const int32_t *row_index, int64_t M,
+                                     int64_t C, int32_t recipe, int32_t fmt, int32_t E,
+                                     const int32_t *group_ends, void *row_codes, void *row_scales,
+                                     void *col_codes, void *col_scales, int64_t ld,
+                                     int32_t *padded_starts, float *amax, const float *dl_scale,
+                                     const float *dl_inv, mxsg_stream_t stream) {
+  REQUIRE(M == 0 || row_index, MXSG_INVALID_ARGUMENT, "quantize_act_gather: row_index is NULL");
+  return quantize_act_impl("quantize_act_gather", x, T, row_index, M, C, recipe, fmt, E,
+                           group_ends, row_codes, row_scales, col_codes, col_scales, ld,
+                           padded_starts, amax, dl_scale, dl_inv, stream);
 }
 
 mxsg_status mxsg_quantize_weight(const void *w, int32_t E, int64_t K, int64_t N, int32_t recipe,
@@ -316,6 +347,16 @@ mxsg_status mxsg_cast_sweep(uint32_t start_bits, int64_t n, int32_t fmt, void *o
   return from_hip(mxsg::launch_cast_sweep(start_bits, n, fmt, static_cast<uint8_t *>(out),
                                           static_cast<hipStream_t>(stream)),
                   "cast_sweep");
+}
+
+mxsg_status mxsg_stream_copy(const void *src, void *dst, int64_t bytes, mxsg_stream_t stream) {
+  REQUIRE(bytes >= 0 && bytes % 16 == 0 && bytes / 16 / 256 < INT32_MAX, MXSG_INVALID_ARGUMENT,
+          "stream_copy: bytes=%lld must be a non-negative multiple of 16", (long long)bytes);
+  REQUIRE(bytes == 0 || (src && dst), MXSG_INVALID_ARGUMENT, "stream_copy: NULL pointer");
+  REQUIRE(((uintptr_t)src | (uintptr_t)dst) % 16 == 0, MXSG_INVALID_ARGUMENT,
+          "stream_copy: pointers must be 16-byte aligned");
+  return from_hip(mxsg::launch_stream_copy(src, dst, bytes, static_cast<hipStream_t>(stream)),
+                  "stream_copy");
 }
 
 }  // extern "C"

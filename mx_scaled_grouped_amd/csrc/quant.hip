@@ -4,7 +4,9 @@
 // 128x128) and MX (32-element, E8M0) recipes.
 //
 // Design (gfx950): HBM-bound, so each element is read once per pass with
-// 16-byte vector loads and each code written once with coalesced stores.
+// 16-byte vector loads and each code written once with coalesced streaming
+// (nontemporal) stores; inputs larger than the last-level cache are read
+// with streaming loads too.
 // A 256-thread workgroup owns a 128 x 128 tile of the input (128 rows of
 // 128 features). Row-wise units (1x128, 1x32) are reduced across the 16 (or
 // 4) lanes that hold one row; the tile is staged in LDS and re-read by
@@ -65,6 +67,39 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint16_t *__restrict__ 
   }
 }
 
+// Source row of routed row i: row_index[i] clamped into [0, src_rows), or i
+// itself without an index. A malformed index gives wrong rows, never an
+// out-of-bounds read.
+__device__ __forceinline__ int64_t source_row(const int32_t *row_index, int64_t src_rows, int64_t i) {
+  if (!row_index) return i;
+  const int64_t t = row_index[i];
+  return t < 0 ? 0 : (t >= src_rows ? src_rows - 1 : t);
+}
+
+// amax over the routed rows x[row_index[i]], i < M, of a [src_rows, C]
+// tensor (tensorwise dynamic scaling of a gathered operand): a workgroup
+// takes whole rows, its threads the row's 16-byte chunks.
+__global__ __launch_bounds__(256) void amax_rows_kernel(const uint16_t *__restrict__ x, int64_t C,
+                                                        const int32_t *__restrict__ row_index,
+                                                        int64_t M, int64_t src_rows,
+                                                        uint32_t *__restrict__ amax_bits) {
+  uint32_t m = 0;
+  const int64_t nvec = C / 8;
+  for (int64_t i = blockIdx.x; i < M; i += gridDim.x) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(x + source_row(row_index, src_rows, i) * C);
+    for (int64_t c = threadIdx.x; c < nvec; c += blockDim.x) m = absmax_bits8(p[c], m);
+  }
+  m = wave_max_u32(m);
+  __shared__ uint32_t red[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = umax(umax(red[0], red[1]), umax(red[2], red[3]));
+    if (m) atomic_max_bits(amax_bits, m << 16);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // the 128x128 tile quantizer
 
@@ -85,6 +120,9 @@ struct TileArgs {
   const float *dl_inv;    // [batch]
   int64_t x_bstride, row_bstride, col_bstride;       // per batch element (elements / bytes)
   int64_t rs_bstride, cs_bstride;                    // scale strides per batch element
+  int32_t stream_x;       // read x with streaming loads (x far larger than the caches)
+  const int32_t *row_index;  // optional gather: routed row i is x row row_index[i]
+  int64_t src_rows;          // rows of x when row_index is given
 };
 
 // Padded start of the tile and its source rows. Returns false if the tile is
@@ -192,7 +230,8 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
   for (int u = 0; u < 8; ++u) {
     const int r = u * 16 + rq;
     if (r < nvalid) {
-      v[u] = *reinterpret_cast<const uint4 *>(x + (src0 + r) * a.C + c0 + cq * 8);
+      const uint16_t *src = x + source_row(a.row_index, a.src_rows, src0 + r) * a.C + c0 + cq * 8;
+      v[u] = a.stream_x ? load16_stream(src) : *reinterpret_cast<const uint4 *>(src);
     } else {
       v[u] = make_uint4(0, 0, 0, 0);
     }
@@ -260,7 +299,7 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
       }
       if (r < nvalid) {
         const uint2 q = cvt8<FMT>(v[u], inv);
-        *reinterpret_cast<uint2 *>(a.row_codes + b * a.row_bstride + pi_off(src0 + r, c0 + cq * 8, a.C)) = q;
+        store8_stream(a.row_codes + b * a.row_bstride + pi_off(src0 + r, c0 + cq * 8, a.C), q);
       }
     }
   }
@@ -348,7 +387,7 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
     const int id = u * QTHREADS + t;
     const int f = id >> 3, ch = id & 7;
     const uint4 val = *reinterpret_cast<const uint4 *>(&ctile[f * CODE_LD + ch * 16]);
-    *reinterpret_cast<uint4 *>(cc + pi_off(c0 + f, p0 + ch * 16, a.ld)) = val;
+    store16_stream(cc + pi_off(c0 + f, p0 + ch * 16, a.ld), val);
   }
 }
 
@@ -419,9 +458,22 @@ __global__ __launch_bounds__(256) void cast_sweep_kernel(uint32_t start, int64_t
 }
 
 // ---------------------------------------------------------------------------
+// streaming device copy (the HBM reference rate): one 16-byte chunk per thread
+
+__global__ __launch_bounds__(256) void stream_copy_kernel(const uint8_t *__restrict__ src,
+                                                          uint8_t *__restrict__ dst, int64_t n16) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n16) store16_stream(dst + 16 * i, load16_stream(src + 16 * i));
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 
 static int tiles_of(int64_t n) { return (int)((n + QT - 1) / QT); }
+
+// inputs above this size cannot stay in the last-level cache (256 MiB) for a
+// later pass anyway, so the tile pass streams them past it
+constexpr int64_t kStreamBytes = (int64_t)256 << 20;
 
 hipError_t launch_zero(float *p, int n, hipStream_t st) {
   zero_f32_kernel<<<(n + 255) / 256, 256, 0, st>>>(p, n);
@@ -468,7 +520,18 @@ static hipError_t tile_by_recipe(int recipe, const TileArgs &a, bool row, bool c
 hipError_t launch_quantize_act(const QuantActParams &p, hipStream_t st) {
   hipError_t e;
   if (p.recipe == kTensorwise) {
-    e = launch_amax(p.x, 1, p.M * p.C, p.amax, st);
+    if (p.row_index) {
+      e = launch_zero(p.amax, 1, st);
+      if (e != hipSuccess) return e;
+      if (p.M > 0) {
+        const unsigned blocks = (unsigned)(p.M < 8192 ? p.M : 8192);
+        amax_rows_kernel<<<blocks, 256, 0, st>>>(p.x, p.C, p.row_index, p.M, p.src_rows,
+                                                 reinterpret_cast<uint32_t *>(p.amax));
+        e = hipGetLastError();
+      }
+    } else {
+      e = launch_amax(p.x, 1, p.M * p.C, p.amax, st);
+    }
     if (e != hipSuccess) return e;
   }
   TileArgs a{};
@@ -486,6 +549,11 @@ hipError_t launch_quantize_act(const QuantActParams &p, hipStream_t st) {
   a.amax = p.amax;
   a.dl_scale = p.dl_scale;
   a.dl_inv = p.dl_inv;
+  // a gathered operand re-reads token rows (one read per routed copy): those
+  // reads can hit the last-level cache whenever the token tensor fits in it
+  a.stream_x = (p.row_index ? p.src_rows : p.M) * p.C * 2 > kStreamBytes;
+  a.row_index = p.row_index;
+  a.src_rows = p.src_rows;
   const bool row = p.row_codes != nullptr, col = p.col_codes != nullptr;
   // at least one tile: an empty tensor still gets its tensor scale written
   int64_t ytiles = col ? p.ld / QT : tiles_of(p.M);
@@ -516,6 +584,7 @@ hipError_t launch_quantize_weight(const QuantWeightParams &p, hipStream_t st) {
   a.dl_scale = p.dl_scale;
   a.dl_inv = p.dl_inv;
   a.x_bstride = p.K * p.N;
+  a.stream_x = (int64_t)p.E * p.K * p.N * 2 > kStreamBytes;
   a.row_bstride = p.K * p.N;
   a.col_bstride = p.K * p.N;
   int recipe = p.recipe;
@@ -549,6 +618,14 @@ hipError_t launch_delayed_update(float *hist, int32_t *pos, float *amax, float *
     delayed_update_kernel<kE4M3><<<units, 256, 0, st>>>(hist, pos, amax, scale, inv, L);
   else
     delayed_update_kernel<kE5M2><<<units, 256, 0, st>>>(hist, pos, amax, scale, inv, L);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_copy(const void *src, void *dst, int64_t bytes, hipStream_t st) {
+  const int64_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  stream_copy_kernel<<<(unsigned)((n16 + 255) / 256), 256, 0, st>>>(
+      static_cast<const uint8_t *>(src), static_cast<uint8_t *>(dst), n16);
   return hipGetLastError();
 }
 

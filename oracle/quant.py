@@ -230,6 +230,31 @@ def quantize_act(x_bf16, recipe: str, fmt: Fp8Format, group_ends=None,
     return out
 
 
+def gather_rows(x_bf16, row_index) -> np.ndarray:
+    """Routed rows A [M, C] of a token tensor x [T, C]: A[i] = x[row_index[i]].
+
+    The grouped matmul is overridden for the routed experts only (torchao
+    float8 MoE training PR, Limitations), whose operand holds each token's
+    copies in expert order (the group offsets make every expert's rows one
+    contiguous run). The permutation that builds it is a plain row gather;
+    indices must lie in [0, T)."""
+    x_bf16 = np.asarray(x_bf16, dtype=np.uint16)
+    idx = np.asarray(row_index, dtype=np.int64)
+    if idx.ndim != 1 or (idx.size and (idx.min() < 0 or idx.max() >= x_bf16.shape[0])):
+        raise ValueError("row_index must be 1-D with entries in [0, T)")
+    return x_bf16[idx]
+
+
+def quantize_act_gather(x_bf16, row_index, recipe: str, fmt: Fp8Format, group_ends=None,
+                        rowwise: bool = True, colwise: bool = False,
+                        dl_scale: Optional[tuple] = None) -> dict:
+    """``quantize_act`` of the routed rows ``gather_rows(x, row_index)``: the
+    gather happens first, so every unit (including the tensorwise amax)
+    covers the routed rows only."""
+    return quantize_act(gather_rows(x_bf16, row_index), recipe, fmt, group_ends,
+                        rowwise=rowwise, colwise=colwise, dl_scale=dl_scale)
+
+
 def _block_codes(xb, am, recipe, fmt):
     """Codes and scales of blocks along the last axis; xb [..., nb, blk], am [..., nb]."""
     if recipe == "block":

@@ -77,6 +77,23 @@ def test_quantize_act_validation():
     assert b"ld" in _lib.load().mxsg_last_error()
 
 
+def _qag(**kw):
+    args = dict(x=FAKE, T=100, idx=FAKE, M=16, C=256, recipe=0, fmt=0, E=1, ends=FAKE, rc=FAKE,
+                rs=FAKE, cc=None, cs=None, ld=0, ps=None, amax=FAKE, dls=None, dli=None)
+    args.update(kw)
+    return _lib.status_of("mxsg_quantize_act_gather", *args.values(), None)
+
+
+def test_quantize_act_gather_validation():
+    assert _qag(idx=None) == _lib.INVALID_ARGUMENT          # routed rows need an index
+    assert _qag(T=0) == _lib.BAD_SHAPE                      # nothing to gather from
+    assert _qag(T=-3) == _lib.BAD_SHAPE
+    assert _qag(C=200) == _lib.BAD_SHAPE
+    assert _qag(recipe=7) == _lib.INVALID_ARGUMENT
+    assert _qag(cc=FAKE, cs=FAKE, ps=FAKE, ld=100) == _lib.BAD_SHAPE
+    assert b"quantize_act_gather" in _lib.load().mxsg_last_error()
+
+
 def _qw(**kw):
     args = dict(w=FAKE, E=2, K=256, N=256, recipe=0, fmt=0, kc=FAKE, ks=FAKE, nc=FAKE, ns=FAKE,
                 amax=FAKE, dls=None, dli=None)
@@ -209,6 +226,9 @@ def test_delayed_and_sweep_validation():
     assert _lib.status_of("mxsg_delayed_update", None, FAKE, FAKE, FAKE, FAKE, 2, 16, 0, None) == _lib.INVALID_ARGUMENT
     assert _lib.status_of("mxsg_cast_sweep", 0, 16, 5, FAKE, None) == _lib.INVALID_ARGUMENT
     assert _lib.status_of("mxsg_cast_sweep", 0, 16, 0, None, None) == _lib.INVALID_ARGUMENT
+    assert _lib.status_of("mxsg_stream_copy", FAKE, FAKE, 24, None) == _lib.INVALID_ARGUMENT
+    assert _lib.status_of("mxsg_stream_copy", None, FAKE, 32, None) == _lib.INVALID_ARGUMENT
+    assert _lib.status_of("mxsg_stream_copy", FAKE + 8, FAKE, 32, None) == _lib.INVALID_ARGUMENT
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

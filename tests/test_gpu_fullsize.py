@@ -67,7 +67,8 @@ def _run(name):
     cid = bench.WORKLOADS[name]
     print(f"[fullsize] {name}: generating inputs", flush=True)
     spec, routing, ge_t, weights, sets = bench.make_inputs(cid, torch, W)
-    step = bench.Step(torch, api, spec, ge_t, weights, spec.recipe)
+    step = bench.Step(torch, api, spec, ge_t, weights, spec.recipe,
+                      row_index=bench.routing_index(routing, torch))
     step.run(sets[0])
     step.run(sets[1])
     torch.cuda.synchronize()

@@ -60,6 +60,20 @@ def test_cast_exhaustive(fmt):
             s += n
 
 
+def test_stream_copy():
+    """The reference copy moves every byte, including a size that ends
+    inside the last workgroup."""
+    import torch
+    api = _api()
+    for n in (16, 4096 + 48, 3 * (1 << 20) + 16 * 7):
+        src = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")
+        dst = torch.zeros(n + 64, dtype=torch.uint8, device="cuda")
+        api.stream_copy(src, dst)
+        torch.cuda.synchronize()
+        assert torch.equal(dst[:n], src), n
+        assert int(dst[n:].count_nonzero()) == 0, n
+
+
 # ---------------------------------------------------------------------------
 # token tensors
 
@@ -113,6 +127,95 @@ def test_act_poisoned_outputs(recipe, fmt):
         t.view(torch.uint8).fill_(0xFF)
     api.quantize_act(to_dev_u16(x), recipe, fmt, to_dev(ge), rowwise=True, colwise=True, out=q)
     _compare_act(q, ref, recipe, M, C, True, True)
+
+
+def _routing_index(seed, T, M, drop):
+    """A routed-row index: random tokens with repeats, out of order, never
+    `drop`; the first entries hit both ends of x."""
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, T - 1, size=M)
+    idx[idx >= drop] += 1
+    idx[:2] = [T - 1, 0][:M]
+    return idx.astype(np.int32)
+
+
+@pytest.mark.parametrize("recipe,fmt", RECIPE_FMTS)
+def test_act_gather(recipe, fmt):
+    """Rows gathered inside the kernel (the dispatch permutation fused with
+    quantization) are bit-exact against the oracle's gather-then-quantize,
+    with a dropped token holding the largest value (tensorwise amax covers
+    the routed rows only), on ragged groups including empty ones; and equal
+    to the plain call on the explicitly gathered tensor."""
+    api = _api()
+    T, C = 300, 256
+    x = W.normal_bf16(106, 0, (T, C))
+    x[17, 3] = 0x4480                      # 1024.0 in a token nobody routes
+    sizes = [0, 129, 1, 0, 260, 33]
+    M = sum(sizes)
+    idx = _routing_index(106, T, M, 17)
+    ge = W.group_ends_from_sizes(sizes)
+    print(f"quantize_act_gather {recipe} fmt={fmt} T={T} M={M}", flush=True)
+    ref = OQ.quantize_act_gather(x, idx, recipe, FMT_OBJ[fmt], ge, rowwise=True, colwise=True)
+    q = api.quantize_act(to_dev_u16(x), recipe, fmt, to_dev(ge), rowwise=True, colwise=True,
+                         row_index=to_dev(idx))
+    _compare_act(q, ref, recipe, M, C, True, True)
+    p = api.quantize_act(to_dev_u16(x[idx.astype(np.int64)]), recipe, fmt, to_dev(ge), rowwise=True,
+                         colwise=True)
+    # defined parts only: the pad row of odd M and the columns past P_E are
+    # not written
+    Rp = int(ref["padded_starts"][-1])
+    blk = {"block": 128, "mx": 32}.get(recipe)
+    assert torch.equal(q.padded_starts, p.padded_starts)
+    assert_bits_equal(codes_host(q.row_codes, M), codes_host(p.row_codes, M), "gathered row codes")
+    assert torch.equal(q.row_scales, p.row_scales)
+    assert_bits_equal(codes_host(q.col_codes)[:, :Rp], codes_host(p.col_codes)[:, :Rp],
+                      "gathered column codes")
+    if blk:
+        assert torch.equal(q.col_scales[:, :Rp // blk], p.col_scales[:, :Rp // blk])
+    else:
+        assert torch.equal(q.col_scales, p.col_scales)
+
+
+@pytest.mark.parametrize("fmt", [0, 1], ids=["e4m3", "e5m2"])
+def test_act_gather_delayed(fmt):
+    """Delayed scaling on gathered rows: codes from the state's scale, and the
+    amax recorded in the state is that of the routed rows."""
+    api = _api()
+    T, C = 200, 384
+    x = W.normal_bf16(107, 0, (T, C), std=3.0)
+    x[5, 0] = 0x4600                       # 8192.0, dropped
+    sizes = [64, 0, 77, 50]
+    M = sum(sizes)
+    idx = _routing_index(107, T, M, 5)
+    ge = W.group_ends_from_sizes(sizes)
+    st = api.DelayedState.create(1, fmt, 16)
+    st.scale.fill_(0.125)
+    st.inv.fill_(8.0)
+    q = api.quantize_act(to_dev_u16(x), "dl", fmt, to_dev(ge), rowwise=True, colwise=True,
+                         state=st, unit=0, row_index=to_dev(idx))
+    ref = OQ.quantize_act_gather(x, idx, "dl", FMT_OBJ[fmt], ge, rowwise=True, colwise=True,
+                                 dl_scale=(np.float32(0.125), np.float32(8.0)))
+    _compare_act(q, ref, "dl", M, C, True, True)
+    assert_bits_equal(host(st.amax), ref["amax"], "delayed amax")
+
+
+def test_act_gather_empty_and_clamped():
+    """M = 0 writes only the scales; indices outside [0, T) read a clamped
+    row instead of faulting (the documented guard, not a supported use)."""
+    api = _api()
+    T, C = 40, 128
+    x = W.normal_bf16(108, 0, (T, C))
+    ge = W.group_ends_from_sizes([0, 0])
+    q = api.quantize_act(to_dev_u16(x), "tw", 0, to_dev(ge), rowwise=True, colwise=True,
+                         row_index=to_dev(np.zeros(0, np.int32)))
+    assert host(q.padded_starts).tolist() == [0, 0, 0]
+    assert host(q.amax).tolist() == [0.0] and host(q.row_scales).tolist() == [1.0]
+    idx = np.array([-5, 3, T + 7, T - 1], np.int32)
+    ge = W.group_ends_from_sizes([4])
+    q = api.quantize_act(to_dev_u16(x), "mx", 0, to_dev(ge), rowwise=True, colwise=False,
+                         row_index=to_dev(idx))
+    ref = OQ.quantize_act_gather(x, np.clip(idx, 0, T - 1), "mx", OF.E4M3, ge)
+    _compare_act(q, ref, "mx", 4, C, True, False)
 
 
 def test_act_empty_and_single_row():

@@ -209,6 +209,58 @@ def test_shape_rules():
         Q.quantize_weight(W.normal_bf16(15, 3, (1, 200, 128)), "tw", F.E4M3)
 
 
+@pytest.mark.parametrize("recipe", ["dl", "block", "mx"])
+def test_gather_row_equivariance(recipe):
+    """Row-wise units never mix rows, so quantizing gathered rows equals
+    gathering the rows of the quantized tensor (codes and per-row scales),
+    for a permutation with repeats and tokens left out."""
+    x = W.normal_bf16(16, 0, (40, 256))
+    rng = np.random.default_rng(5)
+    idx = rng.integers(0, 40, size=57)
+    idx[:3] = [39, 0, 39]
+    dl = (np.float32(0.01), np.float32(100.0))
+    full = Q.quantize_act(x, recipe, F.E4M3, dl_scale=dl)
+    g = Q.quantize_act_gather(x, idx, recipe, F.E4M3, dl_scale=dl)
+    assert np.array_equal(g["row_codes"], full["row_codes"][idx])
+    if recipe != "dl":
+        assert np.array_equal(g["row_scales"], full["row_scales"][idx])
+
+
+def test_gather_tensorwise_amax_over_routed_rows():
+    """The tensorwise scale of a gathered operand comes from the routed rows:
+    a token that no expert receives does not raise it."""
+    x = W.normal_bf16(16, 1, (8, 128))
+    big = np.float32(1000.0).view(np.uint32) >> 16
+    x[5, 7] = big                       # the largest element sits in token 5
+    idx = np.array([0, 1, 2, 3, 4, 6, 7, 0], np.int64)    # token 5 is dropped
+    g = Q.quantize_act_gather(x, idx, "tw", F.E4M3)
+    xf = Q.bf16_to_f32(x)
+    want = np.max(np.abs(xf[[0, 1, 2, 3, 4, 6, 7]]))
+    assert g["amax"][0] == want and want < 1000.0
+    assert Q.quantize_act(x, "tw", F.E4M3)["amax"][0] == np.float32(1000.0)
+    with pytest.raises(ValueError):
+        Q.gather_rows(x, [0, 8])
+
+
+def test_gather_columnwise_follows_groups():
+    """Column-wise output of gathered rows: group g's tokens in routed order
+    at padded columns [P_g, P_g + m_g); an identity index reproduces the
+    plain call."""
+    x = W.normal_bf16(16, 2, (30, 128))
+    ge = W.group_ends_from_sizes([7, 0, 23])
+    ident = np.arange(30)
+    a = Q.quantize_act_gather(x, ident, "mx", F.E4M3, ge, colwise=True)
+    b = Q.quantize_act(x, "mx", F.E4M3, ge, colwise=True)
+    for k in ("row_codes", "row_scales", "col_codes", "col_scales", "padded_starts"):
+        assert np.array_equal(a[k], b[k]), k
+    rev = ident[::-1].copy()
+    c = Q.quantize_act_gather(x, rev, "block", F.E4M3, ge, colwise=True)
+    # group 0 = routed rows 0..6 = tokens 29..23, in that order
+    d = Q.quantize_act(x[23:30][::-1].copy(), "block", F.E4M3, W.group_ends_from_sizes([7]), colwise=True)
+    assert np.array_equal(c["col_codes"][:, :7], d["col_codes"][:, :7])
+    assert np.array_equal(c["col_scales"][:, 0], d["col_scales"][:, 0])
+
+
 def test_weight_layouts_agree():
     """k-major codes are the transposed n-major codes for tw and 128x128 tiles;
     128x128 units: a tile's max element lands on fmax."""
