@@ -35,7 +35,7 @@ def _parse(v: str) -> float:
     return sign * val
 
 
-@pytest.mark.parametrize("name", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("name", ["e4m3", "e5m2", "e2m1"])
 def test_spec_points(name):
     g = json.load(open(GOLDEN))
     fmt = F.FORMATS[name]
@@ -48,8 +48,8 @@ def test_spec_points(name):
             assert math.isnan(got), (name, code)
         else:
             assert got == want and math.copysign(1, got) == math.copysign(1, want), (name, code, got, want)
-    assert fmt.fmax == {"e4m3": 448.0, "e5m2": 57344.0}[name]
-    assert fmt.fmax == 1.75 * 2.0 ** fmt.emax
+    assert fmt.fmax == {"e4m3": 448.0, "e5m2": 57344.0, "e2m1": 6.0}[name]
+    assert fmt.fmax == {"e4m3": 1.75, "e5m2": 1.75, "e2m1": 1.5}[name] * 2.0 ** fmt.emax
 
 
 def test_e8m0_points():
@@ -60,17 +60,17 @@ def test_e8m0_points():
         assert (math.isnan(want) and math.isnan(got)) or got == want
 
 
-@pytest.mark.parametrize("name", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("name", ["e4m3", "e5m2", "e2m1"])
 def test_roundtrip_all_codes(name):
     """decode -> encode is the identity on every finite code, including +-0."""
     fmt = F.FORMATS[name]
     t = F.decode_table(fmt)
-    codes = np.arange(256)
+    codes = np.arange(1 << fmt.bits)
     finite = np.isfinite(t)
-    assert finite.sum() == {"e4m3": 254, "e5m2": 248}[name]
+    assert finite.sum() == {"e4m3": 254, "e5m2": 248, "e2m1": 16}[name]
     vals = t[finite].astype(np.float32)
     # -0.0 keeps its sign through float32
-    vals[codes[finite] == 0x80] = np.float32(-0.0)
+    vals[codes[finite] == fmt.sign_bit] = np.float32(-0.0)
     back = F.encode_sat_rne(vals, fmt)
     assert np.array_equal(back, codes[finite].astype(np.uint8))
     if fmt.ieee_specials:
@@ -81,10 +81,11 @@ def test_roundtrip_all_codes(name):
 
 
 def _brute_force_encode(v: np.ndarray, fmt) -> np.ndarray:
-    """Nearest finite code by exhaustive distance to all 256 codes; ties to the
+    """Nearest finite code by exhaustive distance to every code; ties to the
     even code; saturating; sign from the sign bit (independent of the oracle)."""
-    vals = np.array([F.decode_value(fmt, c) for c in range(256)])
-    cand = np.array([c for c in range(128) if np.isfinite(vals[c])])      # non-negative codes
+    vals = np.array([F.decode_value(fmt, c) for c in range(1 << fmt.bits)])
+    half = 1 << (fmt.bits - 1)
+    cand = np.array([c for c in range(half) if np.isfinite(vals[c])])     # non-negative codes
     a = np.abs(v.astype(np.float64))
     a = np.minimum(a, vals[fmt.max_code])                                  # saturate
     d = np.abs(a[:, None] - vals[cand][None, :])
@@ -93,10 +94,10 @@ def _brute_force_encode(v: np.ndarray, fmt) -> np.ndarray:
     # among the nearest, prefer even codes, then the smaller one
     score = np.where(tie_ok, (cand[None, :] & 1) * 1000 + cand[None, :], 10 ** 9)
     code = cand[np.argmin(score, axis=1)]
-    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+    return (code | np.where(np.signbit(v), half, 0)).astype(np.uint8)
 
 
-@pytest.mark.parametrize("name", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("name", ["e4m3", "e5m2", "e2m1"])
 def test_encoder_all_bf16_inputs(name):
     """Every bf16 bit pattern (as an fp32 value) encodes like the brute force."""
     fmt = F.FORMATS[name]
@@ -107,7 +108,7 @@ def test_encoder_all_bf16_inputs(name):
         assert np.array_equal(F.encode_sat_rne(chunk, fmt), _brute_force_encode(chunk, fmt))
 
 
-@pytest.mark.parametrize("name", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("name", ["e4m3", "e5m2", "e2m1"])
 def test_encoder_midpoints_and_neighbours(name):
     """Every midpoint between adjacent codes goes to the even code; one fp32
     ulp either side goes to the nearer code; (max, inf) saturates."""
@@ -125,13 +126,13 @@ def test_encoder_midpoints_and_neighbours(name):
     above = np.nextafter(mids, np.float32(np.inf))
     assert np.array_equal(F.encode_sat_rne(below, fmt), lo.astype(np.uint8))
     assert np.array_equal(F.encode_sat_rne(above, fmt), hi.astype(np.uint8))
-    assert np.array_equal(F.encode_sat_rne(-mids, fmt), (want | 0x80).astype(np.uint8))
+    assert np.array_equal(F.encode_sat_rne(-mids, fmt), (want | fmt.sign_bit).astype(np.uint8))
     big = np.float32([fmt.fmax * 1.0001, fmt.fmax * 2, 3.0e38, np.float32(fmt.fmax) + np.float32(8)])
     assert np.all(F.encode_sat_rne(big, fmt) == fmt.max_code)
-    assert np.all(F.encode_sat_rne(-big, fmt) == fmt.max_code | 0x80)
+    assert np.all(F.encode_sat_rne(-big, fmt) == fmt.max_code | fmt.sign_bit)
 
 
-@pytest.mark.parametrize("name", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("name", ["e4m3", "e5m2", "e2m1"])
 def test_encoder_random_fp32(name):
     """Random fp32 bit patterns over the finite range vs the brute force."""
     fmt = F.FORMATS[name]
@@ -147,8 +148,21 @@ def test_encoder_random_fp32(name):
 
 
 def test_signed_zero_and_underflow():
-    for fmt in (F.E4M3, F.E5M2):
+    for fmt in (F.E4M3, F.E5M2, F.E2M1):
         tiny = np.float32([0.0, -0.0, 1e-30, -1e-30, 1e-45, -1e-45])
-        assert F.encode_sat_rne(tiny, fmt).tolist() == [0, 0x80, 0, 0x80, 0, 0x80]
+        sb = fmt.sign_bit
+        assert F.encode_sat_rne(tiny, fmt).tolist() == [0, sb, 0, sb, 0, sb]
+
+
+def test_nibble_packing():
+    """Element 2i in the low nibble, 2i+1 in the high nibble; round trip."""
+    c = np.array([[0x1, 0xF, 0x0, 0x8, 0x7, 0x2]], np.uint8)
+    p = F.pack_nibbles(c)
+    assert p.tolist() == [[0xF1, 0x80, 0x27]]
+    assert np.array_equal(F.unpack_nibbles(p), c)
+    r = np.random.default_rng(3).integers(0, 16, size=(5, 64)).astype(np.uint8)
+    assert np.array_equal(F.unpack_nibbles(F.pack_nibbles(r)), r)
+    with pytest.raises(ValueError):
+        F.pack_nibbles(np.array([1, 2, 3], np.uint8))
     with pytest.raises(ValueError):
         F.encode_sat_rne(np.float32([np.nan]), F.E4M3)

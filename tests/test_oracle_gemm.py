@@ -38,14 +38,14 @@ def _unit_scale_w(q, recipe, e, k, n, layout):
     return 2.0 ** (int(q["nmajor_scales"][e][k][n // 32]) - 127)
 
 
-@pytest.mark.parametrize("recipe", ["tw", "block", "mx"])
-def test_brute_force_tiny(recipe):
+@pytest.mark.parametrize("recipe,fa,fg", [("tw", F.E4M3, F.E5M2), ("block", F.E4M3, F.E4M3),
+                                          ("mx", F.E4M3, F.E4M3), ("mx", F.E2M1, F.E2M1)],
+                         ids=["tw", "block", "mx", "mxfp4"])
+def test_brute_force_tiny(recipe, fa, fg):
     """Forward, dgrad and wgrad of E=3, m = {0, 5, 13}, K=N=128 by triple loops."""
     sizes = [0, 5, 13]
     K, N = 128, 128
     a, w, dy, ge = W.small_case(21, sizes, K, N, outlier=True)
-    fa = F.E4M3
-    fg = F.E5M2 if recipe == "tw" else F.E4M3
     qa = Q.quantize_act(a, recipe, fa, ge, rowwise=True, colwise=True)
     qd = Q.quantize_act(dy, recipe, fg, ge, rowwise=True, colwise=True)
     qw = Q.quantize_weight(w, recipe, fa)

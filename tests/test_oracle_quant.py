@@ -19,6 +19,7 @@ from oracle.delayed import DelayedState
 from mx_scaled_grouped_amd import workloads as W
 
 FMTS = [F.E4M3, F.E5M2]
+MX_FMTS = [F.E4M3, F.E5M2, F.E2M1]   # MX also carries the 4-bit e2m1 element (MXFP4)
 
 
 def _f32_round_fraction(fr: Fraction) -> float:
@@ -63,16 +64,18 @@ def test_amax_element_encodes_to_max(fmt, recipe):
 
 
 def _mx_k_closed_form(a: float, fmt) -> int:
-    """k = E - emax + [f > 1.75] with a = f * 2^E, 1 <= f < 2 (the algebra of
-    amax <= 1.75 * 2^(emax + k)), clamped to [-127, 127]."""
+    """k = E - emax + [f > F] with a = f * 2^E, 1 <= f < 2 and fmax = F * 2^emax
+    (F = 1.75 for e4m3 / e5m2, 1.5 for e2m1): the algebra of
+    amax <= F * 2^(emax + k), clamped to [-127, 127]."""
     if a == 0:
         return 0
     m, e = math.frexp(a)          # a = m 2^e, 0.5 <= m < 1
     f, E = 2 * m, e - 1
-    return max(-127, min(127, E - fmt.emax + (1 if f > 1.75 else 0)))
+    F_sig = {"e4m3": 1.75, "e5m2": 1.75, "e2m1": 1.5}[fmt.name]
+    return max(-127, min(127, E - fmt.emax + (1 if f > F_sig else 0)))
 
 
-@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: f.name)
+@pytest.mark.parametrize("fmt", MX_FMTS, ids=lambda f: f.name)
 def test_mx_exponent_edges(fmt):
     pts = [0.0]
     for j in range(-30, 30, 3):
@@ -94,7 +97,7 @@ def test_mx_exponent_edges(fmt):
 
 def test_mx_block_never_saturates():
     x = W.normal_bf16(12, 0, (64, 256), std=10.0)
-    for fmt in FMTS:
+    for fmt in MX_FMTS:
         q = Q.quantize_act(x, "mx", fmt)
         xf = Q.bf16_to_f32(x).reshape(64, 8, 32)
         inv = Q.mx_inv_from_codes(q["row_scales"])
