@@ -43,6 +43,11 @@
  *    amax); amax == 0 gives s = inv = 1. fmax = 448 (e4m3), 57344 (e5m2).
  *    MX: E8M0 code k+127 with k the smallest integer such that amax <=
  *    fmax * 2^k (clamped to [-127, 127]; 0 for amax == 0), inv = 2^-k.
+ *  - 4-bit e2m1 codes (MXFP4) sit two per byte along a row: element 2i in
+ *    the low nibble of byte i, element 2i + 1 in the high nibble; a row of
+ *    L elements is L/2 code bytes. Sign in bit 3; magnitudes 0, 0.5, 1,
+ *    1.5, 2, 3, 4, 6 (OCP MX v1.0 element formats); the MX exponent uses
+ *    fmax = 6, and MX is the only recipe with e2m1 elements.
  *  - Code matrices are pair-interleaved: a matrix of R rows of L code bytes
  *    (L a multiple of 64) stores byte (r, l) at offset
  *      (r / 2) * 2L + (l / 64) * 128 + (r % 2) * 64 + (l % 64),
@@ -87,6 +92,7 @@ typedef int32_t mxsg_status;
 /* element formats */
 #define MXSG_FMT_E4M3 0
 #define MXSG_FMT_E5M2 1
+#define MXSG_FMT_E2M1 2 /* OCP MX 4-bit element (MXFP4); MX recipe only, two codes per byte */
 
 /* grouped GEMM modes */
 #define MXSG_MODE_FWD 0   /* Y[M,N]    = A[M,K]  x W_g[K,N]   (bf16 out) */
@@ -109,13 +115,15 @@ int64_t mxsg_padded_capacity(int64_t M, int32_t E);
 
 /*
  * Byte sizes of the buffers mxsg_quantize_act writes for tokens x [M, C]
- * under `recipe`, with the column-wise output laid out for E groups
- * (ld = mxsg_padded_capacity(M, E)); E = 0 asks for the row-wise sizes only.
- * Pure host function: applies the same shape rules as mxsg_quantize_act
- * (C a multiple of 128, M < 2^31) and returns their status.
- *   bytes[0] row_codes      (M + (M & 1)) * C
+ * under `recipe` and element format `fmt`, with the column-wise output laid
+ * out for E groups (ld = mxsg_padded_capacity(M, E)); E = 0 asks for the
+ * row-wise sizes only. Pure host function: applies the same shape and
+ * recipe/format rules as mxsg_quantize_act (C a multiple of 128, M < 2^31,
+ * e2m1 only with MX) and returns their status. With b = 1 code byte per
+ * element (e4m3, e5m2) or 1/2 (e2m1):
+ *   bytes[0] row_codes      (M + (M & 1)) * C * b
  *   bytes[1] row_scales     BLOCKWISE 4 * M * C/128, MX M * C/32, else 4
- *   bytes[2] col_codes      C * ld                   (0 when E = 0)
+ *   bytes[2] col_codes      C * ld * b               (0 when E = 0)
  *   bytes[3] col_scales     BLOCKWISE 4 * C * ld/128, MX C * ld/32, else 4
  *   bytes[4] padded_starts  4 * (E + 1)              (0 when E = 0)
  * Units and shape rule: the Transformer Engine "FP8BlockQuantizer not
@@ -123,19 +131,20 @@ int64_t mxsg_padded_capacity(int64_t M, int32_t E);
  * the block). The padded token layout of the column-wise output is that
  * note's zero fill of partial blocks.
  */
-mxsg_status mxsg_quantize_act_sizes(int64_t M, int64_t C, int32_t recipe, int32_t E,
+mxsg_status mxsg_quantize_act_sizes(int64_t M, int64_t C, int32_t recipe, int32_t fmt, int32_t E,
                                     int64_t bytes[5]);
 
 /*
- * Byte sizes of the buffers mxsg_quantize_weight writes for w [E, K, N]:
- *   bytes[0] kmajor_codes, bytes[2] nmajor_codes   E * K * N each
+ * Byte sizes of the buffers mxsg_quantize_weight writes for w [E, K, N]
+ * (b as above):
+ *   bytes[0] kmajor_codes, bytes[2] nmajor_codes   E * K * N * b each
  *   bytes[1] kmajor_scales, bytes[3] nmajor_scales BLOCKWISE 4 * E * K/128 * N/128,
  *                                                  MX E * K * N / 32, else 4 * E
  * Pure host function with the shape rules of mxsg_quantize_weight (K, N
  * multiples of 128; 128x128 weight blocks of the same issue's design note).
  */
 mxsg_status mxsg_quantize_weight_sizes(int32_t E, int64_t K, int64_t N, int32_t recipe,
-                                       int64_t bytes[4]);
+                                       int32_t fmt, int64_t bytes[4]);
 
 /*
  * Quantize a token-major tensor x [M, C] (routed-row activations or output
@@ -153,11 +162,12 @@ mxsg_status mxsg_quantize_weight_sizes(int32_t E, int64_t K, int64_t N, int32_t 
  *    col_scales fp32 [C, ld/128] (128x1 units along the padded tokens,
  *    restarting at each group). amax, dl_* unused.
  *  recipe MX: row_scales uint8 [M, C/32]; col_scales uint8 [C, ld/32]; a
- *    32-block made only of padding gets code 127.
+ *    32-block made only of padding gets code 127. fmt e2m1 (MXFP4): the
+ *    same scales; code rows hold C/2 resp. ld/2 bytes.
  *
- *  row_codes uint8 [2 * ceil(M/2), C], pair-interleaved (NULL: no row-wise
+ *  row_codes uint8 [2 * ceil(M/2), C] (C/2 for e2m1), pair-interleaved (NULL: no row-wise
  *    output).
- *  col_codes uint8 [C, ld], pair-interleaved (NULL: no column-wise output).
+ *  col_codes uint8 [C, ld] (ld/2 for e2m1), pair-interleaved (NULL: no column-wise output).
  *    When given, E >= 1,
  *    group_ends and padded_starts (int32 [E+1], receives P_0..P_E) are required.
  *  At least one of row_codes / col_codes must be non-NULL.
@@ -204,7 +214,7 @@ mxsg_status mxsg_quantize_act_gather(const void *x, int64_t T, const int32_t *ro
  *    scales fp32 [E, K/128, N/128] (same array content for both layouts).
  *  MX: two code sets. k-major: blocks of 32 along K, kmajor_scales uint8
  *    [E, N, K/32]; n-major: blocks of 32 along N, nmajor_scales uint8
- *    [E, K, N/32].
+ *    [E, K, N/32]. fmt e2m1: code rows of K/2 resp. N/2 bytes, same scales.
  *  Scale pointers belonging to a non-NULL code pointer are required.
  */
 mxsg_status mxsg_quantize_weight(const void *w, int32_t E, int64_t K, int64_t N, int32_t recipe,
@@ -258,7 +268,15 @@ mxsg_status mxsg_delayed_update(float *history, int32_t *pos, float *amax, float
  *     FWD a [M, K/32], b [E, N, K/32]; DGRAD a [M, N/32], b [E, K, N/32];
  *     WGRAD a [K, lda/32], b [N, ldb/32]; applied inside the MFMA.
  *  fmt_a / fmt_b: element formats of A and B (e4m3 x e4m3, e5m2 x e4m3 and
- *  e4m3 x e5m2 are supported; hybrid training uses e5m2 gradients).
+ *  e4m3 x e5m2 are supported; hybrid training uses e5m2 gradients; e2m1 x
+ *  e2m1 with the MX recipe is MXFP4).
+ *  4-bit operands (e2m1): rows hold two codes per byte, so every row length
+ *  above is in code bytes: FWD lda >= K/2 and ldb = K/2, DGRAD lda >= N/2
+ *  and ldb = N/2, WGRAD lda, ldb = column-wise code bytes per row (ld/2 of
+ *  the quantize call, >= mxsg_padded_capacity(M, E) / 2, a multiple of 64);
+ *  scale shapes count contraction elements as for 8-bit codes. The MFMA
+ *  consumes 64 contraction elements (32 bytes) per instruction, so each
+ *  64-byte stage of a row is two MFMAs at the 4-bit rate.
  *
  *  Rows of FWD / DGRAD outputs belong to exactly one group and are all
  *  written. WGRAD: an empty group's dW_g is written with zeros (left
@@ -287,11 +305,12 @@ mxsg_status mxsg_grouped_mm_check(int32_t mode, int32_t recipe, int32_t fmt_a, i
                                   int64_t ldb, int32_t accumulate);
 
 /*
- * The device FP8 cast used by every quantizer (saturating round to nearest
+ * The device cast used by every quantizer (saturating round to nearest
  * even), applied to the n consecutive fp32 bit patterns start_bits,
  * start_bits + 1, ... (wrapping modulo 2^32): out[i] = code(float(start_bits
- * + i)). out uint8 [n]. NaN patterns give an unspecified code. Lets a
- * caller check the cast exhaustively over all 2^32 inputs.
+ * + i)). out uint8 [n] (e2m1: one 4-bit code per byte). NaN patterns give an
+ * unspecified code. Lets a caller check the cast exhaustively over all 2^32
+ * inputs.
  */
 mxsg_status mxsg_cast_sweep(uint32_t start_bits, int64_t n, int32_t fmt, void *out,
                             mxsg_stream_t stream);

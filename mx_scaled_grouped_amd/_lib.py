@@ -25,8 +25,8 @@ SIGNATURES = {
     "mxsg_last_error": (ctypes.c_char_p, []),
     "mxsg_version": (_i32, []),
     "mxsg_padded_capacity": (_i64, [_i64, _i32]),
-    "mxsg_quantize_act_sizes": (_i32, [_i64, _i64, _i32, _i32, _c_p]),
-    "mxsg_quantize_weight_sizes": (_i32, [_i32, _i64, _i64, _i32, _c_p]),
+    "mxsg_quantize_act_sizes": (_i32, [_i64, _i64, _i32, _i32, _i32, _c_p]),
+    "mxsg_quantize_weight_sizes": (_i32, [_i32, _i64, _i64, _i32, _i32, _c_p]),
     "mxsg_grouped_mm_check": (_i32, [_i32, _i32, _i32, _i32, _i32, _i64, _i64, _i64, _i64, _i64,
                                      _i32]),
     "mxsg_quantize_act": (_i32, [_c_p, _i64, _i64, _i32, _i32, _i32, _c_p, _c_p, _c_p, _c_p, _c_p,

@@ -19,8 +19,13 @@ import torch
 
 from . import _lib
 
-E4M3, E5M2 = 0, 1
-FMT = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
+E4M3, E5M2, E2M1 = 0, 1, 2
+FMT = {"e4m3": E4M3, "e5m2": E5M2, "e2m1": E2M1, E4M3: E4M3, E5M2: E5M2, E2M1: E2M1}
+
+
+def elems_per_byte(fmt) -> int:
+    """Elements per code byte: 2 for 4-bit e2m1 (MXFP4), else 1."""
+    return 2 if FMT[fmt] == E2M1 else 1
 RECIPES = {"tw": 0, "dl": 1, "block": 2, "mx": 3}
 MODE_FWD, MODE_DGRAD, MODE_WGRAD = 0, 1, 2
 
@@ -84,19 +89,19 @@ def _scale_blocks(recipe: str) -> int:
     return {"block": 128, "mx": 32}.get(recipe, 0)
 
 
-def quantize_act_sizes(M: int, C: int, recipe: str, E: int = 0) -> List[int]:
+def quantize_act_sizes(M: int, C: int, recipe: str, fmt=E4M3, E: int = 0) -> List[int]:
     """Byte sizes [row_codes, row_scales, col_codes, col_scales,
     padded_starts] of mxsg_quantize_act's outputs (E = 0: row-wise only)."""
     out = (ctypes.c_int64 * 5)()
-    _lib.call("mxsg_quantize_act_sizes", M, C, RECIPES[recipe], E, ctypes.addressof(out))
+    _lib.call("mxsg_quantize_act_sizes", M, C, RECIPES[recipe], FMT[fmt], E, ctypes.addressof(out))
     return list(out)
 
 
-def quantize_weight_sizes(E: int, K: int, N: int, recipe: str) -> List[int]:
+def quantize_weight_sizes(E: int, K: int, N: int, recipe: str, fmt=E4M3) -> List[int]:
     """Byte sizes [kmajor_codes, kmajor_scales, nmajor_codes, nmajor_scales]
     of mxsg_quantize_weight's outputs."""
     out = (ctypes.c_int64 * 4)()
-    _lib.call("mxsg_quantize_weight_sizes", E, K, N, RECIPES[recipe], ctypes.addressof(out))
+    _lib.call("mxsg_quantize_weight_sizes", E, K, N, RECIPES[recipe], FMT[fmt], ctypes.addressof(out))
     return list(out)
 
 
@@ -150,9 +155,9 @@ class QuantAct:
     fmt: int
     M: int
     C: int
-    row_codes: Optional[torch.Tensor] = None     # uint8 [M + M % 2, C], pair-interleaved
+    row_codes: Optional[torch.Tensor] = None     # uint8 [M + M % 2, C] (C/2 for e2m1), pair-interleaved
     row_scales: Optional[torch.Tensor] = None
-    col_codes: Optional[torch.Tensor] = None     # uint8 [C, ld], pair-interleaved
+    col_codes: Optional[torch.Tensor] = None     # uint8 [C, ld] (ld/2 for e2m1), pair-interleaved
     col_scales: Optional[torch.Tensor] = None
     padded_starts: Optional[torch.Tensor] = None  # int32 [E+1]
     amax: Optional[torch.Tensor] = None
@@ -192,13 +197,14 @@ def quantize_act(x: torch.Tensor, recipe: str, fmt, group_ends: Optional[torch.T
             raise ValueError("column-wise output needs group_ends")
         q = QuantAct(recipe, f, M, C)
         sdt = torch.uint8 if recipe == "mx" else torch.float32
-        nb = quantize_act_sizes(M, C, recipe, E if colwise else 0)
+        nb = quantize_act_sizes(M, C, recipe, f, E if colwise else 0)
+        epb = elems_per_byte(f)
         if rowwise:
-            q.row_codes = _buffer(nb[0], torch.uint8, C, dev)
+            q.row_codes = _buffer(nb[0], torch.uint8, C // epb, dev)
             q.row_scales = _buffer(nb[1], sdt, C // blk if blk else 0, dev)
         if colwise:
             q.ld = padded_capacity(M, E)
-            q.col_codes = _buffer(nb[2], torch.uint8, q.ld, dev)
+            q.col_codes = _buffer(nb[2], torch.uint8, q.ld // epb, dev)
             q.col_scales = _buffer(nb[3], sdt, q.ld // blk if blk else 0, dev)
             q.padded_starts = _buffer(nb[4], torch.int32, 0, dev)
         if recipe == "tw":
@@ -229,9 +235,9 @@ class QuantWeight:
     E: int
     K: int
     N: int
-    kmajor_codes: Optional[torch.Tensor] = None   # uint8 [E, N, K]  (forward operand, pair-interleaved)
+    kmajor_codes: Optional[torch.Tensor] = None   # uint8 [E, N, K] (K/2 for e2m1; forward operand, pair-interleaved)
     kmajor_scales: Optional[torch.Tensor] = None
-    nmajor_codes: Optional[torch.Tensor] = None   # uint8 [E, K, N]  (dgrad operand, pair-interleaved)
+    nmajor_codes: Optional[torch.Tensor] = None   # uint8 [E, K, N] (N/2 for e2m1; dgrad operand, pair-interleaved)
     nmajor_scales: Optional[torch.Tensor] = None
     amax: Optional[torch.Tensor] = None
 
@@ -248,7 +254,8 @@ def quantize_weight(w: torch.Tensor, recipe: str, fmt, kmajor: bool = True, nmaj
     q = out
     if q is None:
         q = QuantWeight(recipe, f, E, K, N)
-        nb = quantize_weight_sizes(E, K, N, recipe)
+        nb = quantize_weight_sizes(E, K, N, recipe, f)
+        epb = elems_per_byte(f)
         if recipe in ("tw", "dl"):
             ks = ns = _buffer(nb[1], torch.float32, 0, dev)
         elif recipe == "block":
@@ -257,10 +264,10 @@ def quantize_weight(w: torch.Tensor, recipe: str, fmt, kmajor: bool = True, nmaj
             ks = _buffer(nb[1], torch.uint8, K // 32, dev).view(E, N, K // 32)
             ns = _buffer(nb[3], torch.uint8, N // 32, dev).view(E, K, N // 32)
         if kmajor:
-            q.kmajor_codes = _buffer(nb[0], torch.uint8, K, dev).view(E, N, K)
+            q.kmajor_codes = _buffer(nb[0], torch.uint8, K // epb, dev).view(E, N, K // epb)
             q.kmajor_scales = ks
         if nmajor:
-            q.nmajor_codes = _buffer(nb[2], torch.uint8, N, dev).view(E, K, N)
+            q.nmajor_codes = _buffer(nb[2], torch.uint8, N // epb, dev).view(E, K, N // epb)
             q.nmajor_scales = ns
         if recipe == "tw":
             q.amax = torch.empty(E, dtype=torch.float32, device=dev)
@@ -302,26 +309,29 @@ def grouped_mm(mode: int, recipe: str, fmt_a, fmt_b, E: int, M: int, K: int, N: 
 def grouped_mm_fwd(qa: QuantAct, qw: QuantWeight, group_ends: torch.Tensor,
                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Y [M, N] (bf16) = A_g @ W_g per group, from row-wise A and k-major W."""
+    epb = elems_per_byte(qa.fmt)
     return grouped_mm(MODE_FWD, qa.recipe, qa.fmt, qw.fmt, qw.E, qa.M, qw.K, qw.N, group_ends,
-                      qa.row_codes, qa.row_scales, qa.C, qw.kmajor_codes, qw.kmajor_scales, qw.K,
-                      out=out)
+                      qa.row_codes, qa.row_scales, qa.C // epb, qw.kmajor_codes, qw.kmajor_scales,
+                      qw.K // epb, out=out)
 
 
 def grouped_mm_dgrad(qdy: QuantAct, qw: QuantWeight, group_ends: torch.Tensor,
                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """dA [M, K] (bf16) = dY_g @ W_g^T per group, from row-wise dY and n-major W."""
+    epb = elems_per_byte(qdy.fmt)
     return grouped_mm(MODE_DGRAD, qdy.recipe, qdy.fmt, qw.fmt, qw.E, qdy.M, qw.K, qw.N, group_ends,
-                      qdy.row_codes, qdy.row_scales, qdy.C, qw.nmajor_codes, qw.nmajor_scales,
-                      qw.N, out=out)
+                      qdy.row_codes, qdy.row_scales, qdy.C // epb, qw.nmajor_codes, qw.nmajor_scales,
+                      qw.N // epb, out=out)
 
 
 def grouped_mm_wgrad(qa: QuantAct, qdy: QuantAct, group_ends: torch.Tensor,
                      out: Optional[torch.Tensor] = None, accumulate: bool = False) -> torch.Tensor:
     """dW [E, K, N] (fp32) = A_g^T @ dY_g per group, from the column-wise operands."""
     E = int(group_ends.numel())
+    epb = elems_per_byte(qa.fmt)
     return grouped_mm(MODE_WGRAD, qa.recipe, qa.fmt, qdy.fmt, E, qa.M, qa.C, qdy.C, group_ends,
-                      qa.col_codes, qa.col_scales, qa.ld, qdy.col_codes, qdy.col_scales, qdy.ld,
-                      padded_starts=qa.padded_starts, out=out, accumulate=accumulate)
+                      qa.col_codes, qa.col_scales, qa.ld // epb, qdy.col_codes, qdy.col_scales,
+                      qdy.ld // epb, padded_starts=qa.padded_starts, out=out, accumulate=accumulate)
 
 
 def cast_sweep(start_bits: int, n: int, fmt, out: Optional[torch.Tensor] = None) -> torch.Tensor:

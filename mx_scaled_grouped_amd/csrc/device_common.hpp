@@ -15,17 +15,27 @@
 namespace mxsg {
 
 enum Recipe : int { kTensorwise = 0, kDelayed = 1, kBlockwise = 2, kMx = 3, kTile128 = 4 };
-enum Format : int { kE4M3 = 0, kE5M2 = 1 };
+enum Format : int { kE4M3 = 0, kE5M2 = 1, kE2M1 = 2 };
 enum Mode : int { kFwd = 0, kDgrad = 1, kWgrad = 2 };
 
+// fmax = F * 2^emax; sig_man = the fp32 mantissa field of F (the MX
+// exponent rounds up when amax's significand exceeds F)
 template <int FMT> struct Fp8;
 template <> struct Fp8<kE4M3> {
   static constexpr float fmax = 448.0f;
   static constexpr int emax = 8;  // 448 = 1.75 * 2^8
+  static constexpr uint32_t sig_man = 0x600000u;
 };
 template <> struct Fp8<kE5M2> {
   static constexpr float fmax = 57344.0f;
   static constexpr int emax = 15;  // 57344 = 1.75 * 2^15
+  static constexpr uint32_t sig_man = 0x600000u;
+};
+// OCP MX e2m1 (MXFP4 element): magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6
+template <> struct Fp8<kE2M1> {
+  static constexpr float fmax = 6.0f;
+  static constexpr int emax = 2;  // 6 = 1.5 * 2^2
+  static constexpr uint32_t sig_man = 0x400000u;
 };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -77,6 +87,33 @@ __device__ __forceinline__ uint2 cvt8(uint4 v, float inv) {
   return r;
 }
 
+// e2m1 code (4 bits, sign in bit 3) of a float: saturating round to nearest
+// even. The magnitude code is the number of decision points below |v|: the
+// midpoints between neighbouring values, a tie going to the even code (the
+// one whose mantissa bit is 0), so the comparison is strict (>) at ties that
+// round down and non-strict (>=) at ties that round up; above 5 every value
+// saturates to 6 (code 7). The sign comes from the sign bit (-0 -> 0x8).
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = __builtin_fabsf(v);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// 8 bf16 (one 16-byte vector) times inv -> 8 e2m1 codes, element i in
+// nibble i (element 2j in the low nibble of byte j)
+__device__ __forceinline__ uint32_t cvt8_e2m1(uint4 v, float inv) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r |= e2m1_code(bf16_lo(w[i]) * inv) << (8 * i);
+    r |= e2m1_code(bf16_hi(w[i]) * inv) << (8 * i + 4);
+  }
+  return r;
+}
+
 // fp32 scale pair of a unit: s = amax / fmax, inv = fmax / amax (IEEE
 // correctly rounded divisions); amax == 0 gives (1, 1).
 template <int FMT>
@@ -92,7 +129,8 @@ __device__ __forceinline__ void scale_pair(float amax, float &s, float &inv) {
 
 // MX shared exponent: the smallest k with amax <= fmax * 2^k, clamped to
 // [-127, 127], from the bits of amax = f * 2^E (1 <= f < 2):
-// k = E - emax + (f > 1.75), because fmax = 1.75 * 2^emax.
+// k = E - emax + (f > F), because fmax = F * 2^emax (F = 1.75 for e4m3 and
+// e5m2, 1.5 for e2m1).
 template <int FMT>
 __device__ __forceinline__ int mx_exponent(float amax) {
   uint32_t u = __float_as_uint(amax) & 0x7fffffffu;
@@ -107,7 +145,7 @@ __device__ __forceinline__ int mx_exponent(float amax) {
   } else {
     E = eb - 127;
   }
-  int k = E - Fp8<FMT>::emax + (man > 0x600000u ? 1 : 0);
+  int k = E - Fp8<FMT>::emax + (man > Fp8<FMT>::sig_man ? 1 : 0);
   return k < -127 ? -127 : (k > 127 ? 127 : k);
 }
 

@@ -52,7 +52,7 @@ struct GemmArgs {
   const int32_t *pstarts;
   int64_t lda, ldb, ldo;
   int64_t M;             // token rows (group ends live in [0, M])
-  int64_t I, J, L;       // extents of i and j; L = contraction for FWD / DGRAD
+  int64_t I, J, L;       // extents of i and j; L = code bytes of a contraction row (FWD / DGRAD)
   int64_t b_gstride;     // bytes of B per expert (FWD / DGRAD)
   int64_t bs_gstride;    // B scale entries per expert (FWD / DGRAD)
   int64_t sb_l, sb_j;    // blockwise weight scale strides along l-block and j-block
@@ -195,12 +195,19 @@ __device__ __forceinline__ void order_groups() {
   }
 }
 
+// the upper 16 bytes of a fragment in the operand's low registers (a 4-bit
+// MFMA reads only the first four)
+__device__ __forceinline__ v8i upper4(v8i x) { return __builtin_shufflevector(x, x, 4, 5, 6, 7, 4, 5, 6, 7); }
+
 // one stage's operands of one lane, in registers
 template <int MI, int NI>
 struct Frags {
   v8i a[MI], b[NI];
   int sa[MI], sb[NI];  // MX: the rows' E8M0 words, shifted to this lane's half
 };
+
+// MFMA operand format code (cbsz / blgp) of an element format
+__host__ __device__ constexpr int mfma_fmt(int f) { return f == kE2M1 ? 4 : f; }
 
 template <int MODE, int RECIPE, int FA, int FB, int BN>
 __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
@@ -212,6 +219,13 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
   constexpr int BQ = BN / 16 / 4;    // of B
   constexpr bool BLK = RECIPE == kBlockwise;
   constexpr bool MX = RECIPE == kMx;
+  // MXFP4: two e2m1 codes per byte, so a 64-byte stage is 128 contraction
+  // elements (four 32-blocks, one E8M0 word per row) and each tile takes two
+  // MFMAs per stage, on the first and second 32 bytes of the stage
+  constexpr bool FP4 = FA == kE2M1;
+  constexpr int EPB = FP4 ? 2 : 1;  // contraction elements per code byte
+  constexpr int MPT = FP4 ? 2 : 1;  // MFMAs per tile and stage
+  static_assert(!FP4 || (MX && FB == kE2M1), "4-bit operands: MX, both sides");
   static_assert(AQ >= 1 && BQ >= 1 && NI >= 1, "tile shape");
   static_assert(!MX || (MI == 4 && NI == 4 && BN == 256), "MX word layout");
 
@@ -250,11 +264,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
     ilo = i0;
     ihi = a.I < i0 + GBM ? a.I : i0 + GBM;
     int64_t p_lo = a.pstarts[g], p_hi = a.pstarts[g + 1];
-    const int64_t cap = a.lda < a.ldb ? a.lda : a.ldb;
+    const int64_t cap = (a.lda < a.ldb ? a.lda : a.ldb) * EPB;   // token positions
     p_lo = p_lo < 0 ? 0 : (p_lo > cap ? cap : p_lo);
     p_hi = p_hi < p_lo ? p_lo : (p_hi > cap ? cap : p_hi);
     l0 = p_lo & ~(int64_t)127;                       // padded starts are 128-aligned
-    nsteps = (int)(((p_hi - l0) / 128) * (128 / GBK));
+    nsteps = (int)(((p_hi - l0) / 128) * (128 / (GBK * EPB)));
   } else {
     int slot, jt;
     raster(lid, a.slots, a.jtiles, slot, jt);
@@ -265,17 +279,17 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
   }
   const int vsteps = (nsteps + 3) & ~3;  // stages rounded up to whole ring turns
 
-  // scale-row strides: FWD / DGRAD scales are [rows, L/blk]; WGRAD scales
-  // follow the padded column layout, [rows, ld/blk]
-  const int64_t sa_row = MODE == kWgrad ? a.lda : a.L;
-  const int64_t sb_row = MODE == kWgrad ? a.ldb : a.L;
+  // scale-row strides (contraction elements per row): FWD / DGRAD scales are
+  // [rows, L/blk]; WGRAD scales follow the padded column layout, [rows, ld/blk]
+  const int64_t sa_row = (MODE == kWgrad ? a.lda : a.L) * EPB;
+  const int64_t sb_row = (MODE == kWgrad ? a.ldb : a.L) * EPB;
 
   // ---- per-lane byte offsets of the 16-byte chunks this lane copies. Copy
   // group q of a wave is 8 row pairs (16 rows of the stage tile): lane L
   // takes tile row 16q' + L / 4 and lands at its LDS chunk L % 4, so it
   // reads the global chunk that the swizzle puts there. Pairs past the last
   // valid one re-read the last valid pair.
-  const int64_t lb = l0 / GBK;   // first contraction line of the tile
+  const int64_t lb = l0 / (GBK * EPB);   // first contraction line of the tile
   const uint8_t *abase = a.a + (i0 >> 1) * 2 * a.lda + lb * 128;
   const uint8_t *bbase = a.b + (MODE == kWgrad ? 0 : (int64_t)g * a.b_gstride) + (j0 >> 1) * 2 * a.ldb + lb * 128;
   const int apmax = (int)(((ihi - 1) >> 1) - (i0 >> 1));   // last valid pair, tile-relative
@@ -348,9 +362,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
   auto load_stage = [&](int kt, uint8_t *as, uint8_t *bs, float *sa, float *sb, uint32_t *ma,
                         uint32_t *mb) {
     if (kt < nsteps) {
-      if (MX) {
-        dma4(mxa + (kt >> 1) * 4, ma + wave * 64);
-        if (b_wave) dma4(mxb + (kt >> 1) * 4, mb + wave * 64);
+      if (MX) {  // the E8M0 word holding this stage's 32-blocks
+        const int wofs = ((kt * EPB) >> 1) * 4;
+        dma4(mxa + wofs, ma + wave * 64);
+        if (b_wave) dma4(mxb + wofs, mb + wave * 64);
       }
       if (BLK) {
         dma4(sa_src + (kt >> 1), sa + wave * 64);
@@ -438,7 +453,16 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int x = LO; x < HI; ++x) {
       const int mi = x / NI, ni = x % NI;
-      if (MX) {
+      if (MX && FP4) {
+        // stage blocks 2m + h of MFMA m = byte 2m + h of the word (shifted
+        // by 8h): opsel 2m; its operands are the 16 bytes at 32m + 16h
+        // (measured lane layout: lane half h holds the MFMA's 32-block h)
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            f.a[mi], f.b[ni], acc[mi][ni], mfma_fmt(FA), mfma_fmt(FB), 0, f.sa[mi], 0, f.sb[ni]);
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            upper4(f.a[mi]), upper4(f.b[ni]), acc[mi][ni], mfma_fmt(FA), mfma_fmt(FB), 2, f.sa[mi], 2,
+            f.sb[ni]);
+      } else if (MX) {
         // lane half h takes byte 2*PH + h of the row's word (shifted by 8h): opsel 2*PH
         acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             f.a[mi], f.b[ni], acc[mi][ni], FA, FB, 2 * PH, f.sa[mi], 2 * PH, f.sb[ni]);
@@ -500,7 +524,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
   // instruction order of the rest of a prefetching stage: the next stage's
   // fragment reads spread evenly over its MFMAs (then the MX word reads)
   auto order_pref = [&]() {
-    order_groups<0, MI * NI - NPRE, 2 * (MI + NI)>();
+    order_groups<0, MPT * (MI * NI - NPRE), 2 * (MI + NI)>();
     if (MX) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
   };
 
@@ -641,6 +665,8 @@ static hipError_t launch_cfg(const GemmArgs &a0, hipStream_t st) {
 
 template <int MODE, int RECIPE>
 static hipError_t launch_fmt(const GemmArgs &a, int fa, int fb, hipStream_t st) {
+  if constexpr (RECIPE == kMx)
+    if (fa == kE2M1 && fb == kE2M1) return launch_cfg<MODE, RECIPE, kE2M1, kE2M1>(a, st);
   if (fa == kE4M3 && fb == kE4M3) return launch_cfg<MODE, RECIPE, kE4M3, kE4M3>(a, st);
   if (fa == kE5M2 && fb == kE4M3) return launch_cfg<MODE, RECIPE, kE5M2, kE4M3>(a, st);
   if (fa == kE4M3 && fb == kE5M2) return launch_cfg<MODE, RECIPE, kE4M3, kE5M2>(a, st);
@@ -658,6 +684,7 @@ static hipError_t launch_recipe(const GemmArgs &a, int recipe, int fa, int fb, h
 }
 
 hipError_t launch_grouped_mm(const GemmParams &p, hipStream_t st) {
+  const int64_t epb = p.fmt_a == kE2M1 ? 2 : 1;  // contraction elements per code byte
   GemmArgs a{};
   a.a = p.a;
   a.b = p.b;
@@ -674,7 +701,7 @@ hipError_t launch_grouped_mm(const GemmParams &p, hipStream_t st) {
   if (p.mode == kFwd) {
     a.I = p.M;
     a.J = p.N;
-    a.L = p.K;
+    a.L = p.K / epb;  // code bytes per row
     a.ldo = p.N;
     a.b_gstride = p.N * p.ldb;
     // blockwise weight scales [E, K/128, N/128]: l-block = k, j-block = n
@@ -686,7 +713,7 @@ hipError_t launch_grouped_mm(const GemmParams &p, hipStream_t st) {
   if (p.mode == kDgrad) {
     a.I = p.M;
     a.J = p.K;
-    a.L = p.N;
+    a.L = p.N / epb;
     a.ldo = p.K;
     a.b_gstride = p.K * p.ldb;
     // same [E, K/128, N/128] array: l-block = n, j-block = k

@@ -35,7 +35,10 @@ mxsg_status from_hip(hipError_t e, const char *what) {
 }
 
 bool recipe_ok(int32_t r) { return r >= MXSG_RECIPE_TENSORWISE && r <= MXSG_RECIPE_MX; }
-bool fmt_ok(int32_t f) { return f == MXSG_FMT_E4M3 || f == MXSG_FMT_E5M2; }
+bool fmt_ok(int32_t f) { return f == MXSG_FMT_E4M3 || f == MXSG_FMT_E5M2 || f == MXSG_FMT_E2M1; }
+bool fp8_fmt(int32_t f) { return f == MXSG_FMT_E4M3 || f == MXSG_FMT_E5M2; }
+// contraction / feature elements per code byte
+int64_t elems_per_byte(int32_t f) { return f == MXSG_FMT_E2M1 ? 2 : 1; }
 
 #define REQUIRE(cond, code, ...) \
   do {                           \
@@ -44,8 +47,11 @@ bool fmt_ok(int32_t f) { return f == MXSG_FMT_E4M3 || f == MXSG_FMT_E5M2; }
 
 // Shape rules shared by the size queries and the launching entry points;
 // fn names the caller in the error message.
-mxsg_status act_shape(const char *fn, int64_t M, int64_t C, int32_t recipe) {
+mxsg_status act_shape(const char *fn, int64_t M, int64_t C, int32_t recipe, int32_t fmt) {
   REQUIRE(recipe_ok(recipe), MXSG_INVALID_ARGUMENT, "%s: unknown recipe %d", fn, recipe);
+  REQUIRE(fmt_ok(fmt), MXSG_INVALID_ARGUMENT, "%s: unknown format %d", fn, fmt);
+  REQUIRE(fmt != MXSG_FMT_E2M1 || recipe == MXSG_RECIPE_MX, MXSG_UNSUPPORTED,
+          "%s: e2m1 codes need the MX recipe", fn);
   REQUIRE(M >= 0 && C > 0, MXSG_INVALID_ARGUMENT, "%s: M=%lld C=%lld", fn, (long long)M,
           (long long)C);
   REQUIRE(C % 128 == 0, MXSG_BAD_SHAPE, "%s: C=%lld is not a multiple of 128", fn, (long long)C);
@@ -54,8 +60,12 @@ mxsg_status act_shape(const char *fn, int64_t M, int64_t C, int32_t recipe) {
   return MXSG_OK;
 }
 
-mxsg_status weight_shape(const char *fn, int32_t E, int64_t K, int64_t N, int32_t recipe) {
+mxsg_status weight_shape(const char *fn, int32_t E, int64_t K, int64_t N, int32_t recipe,
+                         int32_t fmt) {
   REQUIRE(recipe_ok(recipe), MXSG_INVALID_ARGUMENT, "%s: unknown recipe %d", fn, recipe);
+  REQUIRE(fmt_ok(fmt), MXSG_INVALID_ARGUMENT, "%s: unknown format %d", fn, fmt);
+  REQUIRE(fmt != MXSG_FMT_E2M1 || recipe == MXSG_RECIPE_MX, MXSG_UNSUPPORTED,
+          "%s: e2m1 codes need the MX recipe", fn);
   REQUIRE(E >= 1 && K > 0 && N > 0, MXSG_INVALID_ARGUMENT, "%s: E=%d K=%lld N=%lld", fn, E,
           (long long)K, (long long)N);
   REQUIRE(K % 128 == 0 && N % 128 == 0, MXSG_BAD_SHAPE,
@@ -74,9 +84,8 @@ static mxsg_status quantize_act_impl(const char *fn, const void *x, int64_t T,
                                      void *col_codes, void *col_scales, int64_t ld,
                                      int32_t *padded_starts, float *amax, const float *dl_scale,
                                      const float *dl_inv, mxsg_stream_t stream) {
-  mxsg_status st = act_shape(fn, M, C, recipe);
+  mxsg_status st = act_shape(fn, M, C, recipe, fmt);
   if (st != MXSG_OK) return st;
-  REQUIRE(fmt_ok(fmt), MXSG_INVALID_ARGUMENT, "%s: unknown format %d", fn, fmt);
   REQUIRE(row_codes || col_codes, MXSG_INVALID_ARGUMENT, "%s: no output requested", fn);
   REQUIRE(M == 0 || x, MXSG_INVALID_ARGUMENT, "%s: x is NULL", fn);
   if (row_index || T != M) {  // gathered rows: an index per routed row into x [T, C]
@@ -154,10 +163,10 @@ int64_t mxsg_padded_capacity(int64_t M, int32_t E) {
   return ((M + 127 * (int64_t)E + 127) / 128) * 128;
 }
 
-mxsg_status mxsg_quantize_act_sizes(int64_t M, int64_t C, int32_t recipe, int32_t E,
+mxsg_status mxsg_quantize_act_sizes(int64_t M, int64_t C, int32_t recipe, int32_t fmt, int32_t E,
                                     int64_t bytes[5]) {
   REQUIRE(bytes, MXSG_INVALID_ARGUMENT, "quantize_act_sizes: bytes is NULL");
-  mxsg_status st = act_shape("quantize_act_sizes", M, C, recipe);
+  mxsg_status st = act_shape("quantize_act_sizes", M, C, recipe, fmt);
   if (st != MXSG_OK) return st;
   REQUIRE(E >= 0 && E <= (1 << 20), MXSG_INVALID_ARGUMENT, "quantize_act_sizes: E=%d", E);
   // scale bytes of n elements along a row: fp32 per 128, E8M0 per 32, or one fp32
@@ -166,11 +175,12 @@ mxsg_status mxsg_quantize_act_sizes(int64_t M, int64_t C, int32_t recipe, int32_
     if (recipe == MXSG_RECIPE_MX) return rows * (n / 32);
     return 4;
   };
-  bytes[0] = (M + (M & 1)) * C;
+  const int64_t epb = elems_per_byte(fmt);
+  bytes[0] = (M + (M & 1)) * (C / epb);
   bytes[1] = scale_bytes(M, C);
   if (E >= 1) {
     const int64_t ld = mxsg_padded_capacity(M, E);
-    bytes[2] = C * ld;
+    bytes[2] = C * (ld / epb);
     bytes[3] = scale_bytes(C, ld);
     bytes[4] = ((int64_t)E + 1) * 4;
   } else {
@@ -181,15 +191,15 @@ mxsg_status mxsg_quantize_act_sizes(int64_t M, int64_t C, int32_t recipe, int32_
 }
 
 mxsg_status mxsg_quantize_weight_sizes(int32_t E, int64_t K, int64_t N, int32_t recipe,
-                                       int64_t bytes[4]) {
+                                       int32_t fmt, int64_t bytes[4]) {
   REQUIRE(bytes, MXSG_INVALID_ARGUMENT, "quantize_weight_sizes: bytes is NULL");
-  mxsg_status st = weight_shape("quantize_weight_sizes", E, K, N, recipe);
+  mxsg_status st = weight_shape("quantize_weight_sizes", E, K, N, recipe, fmt);
   if (st != MXSG_OK) return st;
-  const int64_t codes = (int64_t)E * K * N;
-  bytes[0] = bytes[2] = codes;
+  const int64_t elems = (int64_t)E * K * N;
+  bytes[0] = bytes[2] = elems / elems_per_byte(fmt);
   switch (recipe) {
     case MXSG_RECIPE_BLOCKWISE: bytes[1] = bytes[3] = (int64_t)E * (K / 128) * (N / 128) * 4; break;
-    case MXSG_RECIPE_MX: bytes[1] = bytes[3] = codes / 32; break;
+    case MXSG_RECIPE_MX: bytes[1] = bytes[3] = elems / 32; break;
     default: bytes[1] = bytes[3] = (int64_t)E * 4; break;
   }
   g_err[0] = 0;
@@ -223,9 +233,8 @@ mxsg_status mxsg_quantize_weight(const void *w, int32_t E, int64_t K, int64_t N,
                                  void *nmajor_codes, void *nmajor_scales, float *amax,
                                  const float *dl_scale, const float *dl_inv,
                                  mxsg_stream_t stream) {
-  mxsg_status st = weight_shape("quantize_weight", E, K, N, recipe);
+  mxsg_status st = weight_shape("quantize_weight", E, K, N, recipe, fmt);
   if (st != MXSG_OK) return st;
-  REQUIRE(fmt_ok(fmt), MXSG_INVALID_ARGUMENT, "quantize_weight: unknown format %d", fmt);
   REQUIRE(w, MXSG_INVALID_ARGUMENT, "quantize_weight: w is NULL");
   REQUIRE(kmajor_codes || nmajor_codes, MXSG_INVALID_ARGUMENT, "quantize_weight: no output");
   if (kmajor_codes) REQUIRE(kmajor_scales, MXSG_INVALID_ARGUMENT, "quantize_weight: kmajor_scales NULL");
@@ -256,7 +265,7 @@ mxsg_status mxsg_quantize_weight(const void *w, int32_t E, int64_t K, int64_t N,
 mxsg_status mxsg_delayed_update(float *history, int32_t *pos, float *amax, float *scale,
                                 float *inv, int32_t units, int32_t L, int32_t fmt,
                                 mxsg_stream_t stream) {
-  REQUIRE(fmt_ok(fmt), MXSG_INVALID_ARGUMENT, "delayed_update: unknown format %d", fmt);
+  REQUIRE(fp8_fmt(fmt), MXSG_INVALID_ARGUMENT, "delayed_update: unknown FP8 format %d", fmt);
   REQUIRE(units >= 0 && L >= 1, MXSG_INVALID_ARGUMENT, "delayed_update: units=%d L=%d", units, L);
   if (units > 0)
     REQUIRE(history && pos && amax && scale && inv, MXSG_INVALID_ARGUMENT,
@@ -275,6 +284,11 @@ mxsg_status mxsg_grouped_mm_check(int32_t mode, int32_t recipe, int32_t fmt_a, i
   REQUIRE(fmt_ok(fmt_a) && fmt_ok(fmt_b), MXSG_INVALID_ARGUMENT, "grouped_mm: unknown format");
   REQUIRE(!(fmt_a == MXSG_FMT_E5M2 && fmt_b == MXSG_FMT_E5M2), MXSG_UNSUPPORTED,
           "grouped_mm: e5m2 x e5m2 is not built");
+  REQUIRE((fmt_a == MXSG_FMT_E2M1) == (fmt_b == MXSG_FMT_E2M1), MXSG_UNSUPPORTED,
+          "grouped_mm: 4-bit operands are built only against 4-bit operands");
+  REQUIRE(fmt_a != MXSG_FMT_E2M1 || recipe == MXSG_RECIPE_MX, MXSG_UNSUPPORTED,
+          "grouped_mm: e2m1 operands need the MX recipe");
+  const int64_t epb = elems_per_byte(fmt_a);
   REQUIRE(E >= 1 && M >= 0 && K > 0 && N > 0, MXSG_INVALID_ARGUMENT,
           "grouped_mm: E=%d M=%lld K=%lld N=%lld", E, (long long)M, (long long)K, (long long)N);
   REQUIRE(K % 128 == 0 && N % 128 == 0, MXSG_BAD_SHAPE,
@@ -286,12 +300,13 @@ mxsg_status mxsg_grouped_mm_check(int32_t mode, int32_t recipe, int32_t fmt_a, i
   REQUIRE(accumulate == 0 || mode == MXSG_MODE_WGRAD, MXSG_INVALID_ARGUMENT,
           "grouped_mm: accumulate is only defined for WGRAD");
   if (mode == MXSG_MODE_WGRAD) {
-    const int64_t cap = mxsg_padded_capacity(M, E);
-    REQUIRE(lda % 128 == 0 && ldb % 128 == 0 && lda >= cap && ldb >= cap, MXSG_BAD_SHAPE,
-            "grouped_mm: WGRAD lda=%lld ldb=%lld must be multiples of 128 and >= %lld",
-            (long long)lda, (long long)ldb, (long long)cap);
+    const int64_t cap = mxsg_padded_capacity(M, E) / epb;   // code bytes
+    const int64_t q = 128 / epb;
+    REQUIRE(lda % q == 0 && ldb % q == 0 && lda >= cap && ldb >= cap, MXSG_BAD_SHAPE,
+            "grouped_mm: WGRAD lda=%lld ldb=%lld (code bytes) must be multiples of %lld and >= %lld",
+            (long long)lda, (long long)ldb, (long long)q, (long long)cap);
   } else {
-    const int64_t L = mode == MXSG_MODE_FWD ? K : N;
+    const int64_t L = (mode == MXSG_MODE_FWD ? K : N) / epb;   // code bytes
     REQUIRE(lda >= L && lda % 64 == 0, MXSG_BAD_SHAPE,
             "grouped_mm: lda=%lld must be >= %lld and a multiple of 64", (long long)lda,
             (long long)L);
@@ -340,7 +355,7 @@ mxsg_status mxsg_grouped_mm(int32_t mode, int32_t recipe, int32_t fmt_a, int32_t
 
 mxsg_status mxsg_cast_sweep(uint32_t start_bits, int64_t n, int32_t fmt, void *out,
                             mxsg_stream_t stream) {
-  REQUIRE(fmt_ok(fmt), MXSG_INVALID_ARGUMENT, "cast_sweep: unknown format %d", fmt);
+  REQUIRE(fmt_ok(fmt), MXSG_INVALID_ARGUMENT, "cast_sweep: unknown format %d", fmt);  // e2m1: one code per byte
   REQUIRE(n >= 0 && n <= ((int64_t)1 << 32), MXSG_INVALID_ARGUMENT, "cast_sweep: n=%lld",
           (long long)n);
   REQUIRE(n == 0 || out, MXSG_INVALID_ARGUMENT, "cast_sweep: out is NULL");

@@ -33,6 +33,7 @@ namespace mxsg {
 constexpr int QT = 128;       // tile rows (tokens or K) and columns (features)
 constexpr int QTHREADS = 256;
 constexpr int CODE_LD = 144;  // LDS row stride (bytes) of the transposed code tile
+constexpr int CODE_LD4 = 80;  // the same for 4-bit codes (64 bytes of codes per feature row)
 
 // ---------------------------------------------------------------------------
 // small kernels
@@ -172,6 +173,9 @@ __device__ bool locate_padded_tile(const TileArgs &a, int64_t p0, int64_t &src0,
 
 template <int RECIPE, int FMT, bool ROW, bool COL>
 __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
+  // 4-bit codes (MXFP4) exist for the MX recipe only; two codes per byte
+  static_assert(FMT != kE2M1 || RECIPE == kMx, "e2m1 codes are MX-scaled");
+  constexpr bool FP4 = FMT == kE2M1;
   __shared__ __attribute__((aligned(16))) uint16_t tile[QT * QT];       // bf16, row stride 256 B
   // codes [feature][pos] of the column-wise output, in the same LDS as the
   // bf16 tile (written once every thread has read its columns)
@@ -298,8 +302,14 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
                                                     (c0 / 32) + (cq >> 2)] = (uint8_t)(k + 127);
       }
       if (r < nvalid) {
-        const uint2 q = cvt8<FMT>(v[u], inv);
-        store8_stream(a.row_codes + b * a.row_bstride + pi_off(src0 + r, c0 + cq * 8, a.C), q);
+        if constexpr (FP4) {
+          const uint32_t q = cvt8_e2m1(v[u], inv);
+          *reinterpret_cast<uint32_t *>(a.row_codes + b * a.row_bstride +
+                                        pi_off(src0 + r, (c0 + cq * 8) / 2, a.C / 2)) = q;
+        } else {
+          const uint2 q = cvt8<FMT>(v[u], inv);
+          store8_stream(a.row_codes + b * a.row_bstride + pi_off(src0 + r, c0 + cq * 8, a.C), q);
+        }
       }
     }
   }
@@ -362,32 +372,60 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
   if (RECIPE != kBlockwise) __syncthreads();
 
   // codes of the two columns, 32 rows each -> LDS code tile [feature][pos]
-#pragma unroll
-  for (int i = 0; i < 32; i += 16) {
+  uint8_t *cc = a.col_codes + b * a.col_bstride;
+  if constexpr (FP4) {
+    // 32 codes of a column = 16 bytes: nibble i of dword j is row 8j + i
     uint32_t d0[4], d1[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int r = i + 4 * j;
-      d0[j] = cvt4<FMT>(bf16_lo(w[r]) * inv0, bf16_lo(w[r + 1]) * inv0, bf16_lo(w[r + 2]) * inv0,
-                        bf16_lo(w[r + 3]) * inv0);
-      d1[j] = cvt4<FMT>(bf16_hi(w[r]) * inv1, bf16_hi(w[r + 1]) * inv1, bf16_hi(w[r + 2]) * inv1,
-                        bf16_hi(w[r + 3]) * inv1);
-    }
-    *reinterpret_cast<uint4 *>(&ctile[(2 * fp) * CODE_LD + q * 32 + i]) =
-        make_uint4(d0[0], d0[1], d0[2], d0[3]);
-    *reinterpret_cast<uint4 *>(&ctile[(2 * fp + 1) * CODE_LD + q * 32 + i]) =
-        make_uint4(d1[0], d1[1], d1[2], d1[3]);
-  }
-  __syncthreads();
-
-  // coalesced write-out: 128 feature rows x 128 bytes; 8 lanes per row
-  uint8_t *cc = a.col_codes + b * a.col_bstride;
+      d0[j] = 0;
+      d1[j] = 0;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int id = u * QTHREADS + t;
-    const int f = id >> 3, ch = id & 7;
-    const uint4 val = *reinterpret_cast<const uint4 *>(&ctile[f * CODE_LD + ch * 16]);
-    store16_stream(cc + pi_off(c0 + f, p0 + ch * 16, a.ld), val);
+      for (int i = 0; i < 8; ++i) {
+        d0[j] |= e2m1_code(bf16_lo(w[8 * j + i]) * inv0) << (4 * i);
+        d1[j] |= e2m1_code(bf16_hi(w[8 * j + i]) * inv1) << (4 * i);
+      }
+    }
+    *reinterpret_cast<uint4 *>(&ctile[(2 * fp) * CODE_LD4 + q * 16]) = make_uint4(d0[0], d0[1], d0[2], d0[3]);
+    *reinterpret_cast<uint4 *>(&ctile[(2 * fp + 1) * CODE_LD4 + q * 16]) =
+        make_uint4(d1[0], d1[1], d1[2], d1[3]);
+    __syncthreads();
+    // 128 feature rows x 64 bytes; 4 lanes per row
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int id = u * QTHREADS + t;
+      const int f = id >> 2, ch = id & 3;
+      const uint4 val = *reinterpret_cast<const uint4 *>(&ctile[f * CODE_LD4 + ch * 16]);
+      store16_stream(cc + pi_off(c0 + f, p0 / 2 + ch * 16, a.ld / 2), val);
+    }
+    return;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; i += 16) {
+      uint32_t d0[4], d1[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = i + 4 * j;
+        d0[j] = cvt4<FMT>(bf16_lo(w[r]) * inv0, bf16_lo(w[r + 1]) * inv0, bf16_lo(w[r + 2]) * inv0,
+                          bf16_lo(w[r + 3]) * inv0);
+        d1[j] = cvt4<FMT>(bf16_hi(w[r]) * inv1, bf16_hi(w[r + 1]) * inv1, bf16_hi(w[r + 2]) * inv1,
+                          bf16_hi(w[r + 3]) * inv1);
+      }
+      *reinterpret_cast<uint4 *>(&ctile[(2 * fp) * CODE_LD + q * 32 + i]) =
+          make_uint4(d0[0], d0[1], d0[2], d0[3]);
+      *reinterpret_cast<uint4 *>(&ctile[(2 * fp + 1) * CODE_LD + q * 32 + i]) =
+          make_uint4(d1[0], d1[1], d1[2], d1[3]);
+    }
+    __syncthreads();
+
+    // coalesced write-out: 128 feature rows x 128 bytes; 8 lanes per row
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int id = u * QTHREADS + t;
+      const int f = id >> 3, ch = id & 7;
+      const uint4 val = *reinterpret_cast<const uint4 *>(&ctile[f * CODE_LD + ch * 16]);
+      store16_stream(cc + pi_off(c0 + f, p0 + ch * 16, a.ld), val);
+    }
   }
 }
 
@@ -448,8 +486,14 @@ __global__ __launch_bounds__(256) void cast_sweep_kernel(uint32_t start, int64_t
   const int64_t i4 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (i4 >= n) return;
   const uint32_t s = start + (uint32_t)i4;
-  const uint32_t c = cvt4<FMT>(__uint_as_float(s), __uint_as_float(s + 1), __uint_as_float(s + 2),
-                               __uint_as_float(s + 3));
+  uint32_t c;
+  if constexpr (FMT == kE2M1) {  // one 4-bit code per output byte
+    c = e2m1_code(__uint_as_float(s)) | (e2m1_code(__uint_as_float(s + 1)) << 8) |
+        (e2m1_code(__uint_as_float(s + 2)) << 16) | (e2m1_code(__uint_as_float(s + 3)) << 24);
+  } else {
+    c = cvt4<FMT>(__uint_as_float(s), __uint_as_float(s + 1), __uint_as_float(s + 2),
+                  __uint_as_float(s + 3));
+  }
   if (i4 + 4 <= n) {
     *reinterpret_cast<uint32_t *>(out + i4) = c;
   } else {
@@ -561,6 +605,7 @@ hipError_t launch_quantize_act(const QuantActParams &p, hipStream_t st) {
   const int64_t tiles = ytiles * (p.C / QT);
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
   dim3 grid((unsigned)tiles, 1, 1);
+  if (p.fmt == kE2M1) return tile_dispatch<kMx, kE2M1>(a, row, col, grid, st);
   return p.fmt == kE4M3 ? tile_by_recipe<kE4M3>(p.recipe, a, row, col, grid, st)
                         : tile_by_recipe<kE5M2>(p.recipe, a, row, col, grid, st);
 }
@@ -585,8 +630,9 @@ hipError_t launch_quantize_weight(const QuantWeightParams &p, hipStream_t st) {
   a.dl_inv = p.dl_inv;
   a.x_bstride = p.K * p.N;
   a.stream_x = (int64_t)p.E * p.K * p.N * 2 > kStreamBytes;
-  a.row_bstride = p.K * p.N;
-  a.col_bstride = p.K * p.N;
+  const int64_t code_bytes = p.fmt == kE2M1 ? p.K * p.N / 2 : p.K * p.N;  // per expert
+  a.row_bstride = code_bytes;
+  a.col_bstride = code_bytes;
   int recipe = p.recipe;
   if (recipe == kBlockwise) {
     recipe = kTile128;
@@ -607,6 +653,7 @@ hipError_t launch_quantize_weight(const QuantWeightParams &p, hipStream_t st) {
   const int64_t tiles = (p.K / QT) * (p.N / QT);
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
   dim3 grid((unsigned)tiles, 1, (unsigned)p.E);
+  if (p.fmt == kE2M1) return tile_dispatch<kMx, kE2M1>(a, row, col, grid, st);
   return p.fmt == kE4M3 ? tile_by_recipe<kE4M3>(recipe, a, row, col, grid, st)
                         : tile_by_recipe<kE5M2>(recipe, a, row, col, grid, st);
 }
@@ -635,8 +682,10 @@ hipError_t launch_cast_sweep(uint32_t start, int64_t n, int fmt, uint8_t *out, h
   const int64_t blocks = (threads + 255) / 256;
   if (fmt == kE4M3)
     cast_sweep_kernel<kE4M3><<<(unsigned)blocks, 256, 0, st>>>(start, n, out);
-  else
+  else if (fmt == kE5M2)
     cast_sweep_kernel<kE5M2><<<(unsigned)blocks, 256, 0, st>>>(start, n, out);
+  else
+    cast_sweep_kernel<kE2M1><<<(unsigned)blocks, 256, 0, st>>>(start, n, out);
   return hipGetLastError();
 }
 

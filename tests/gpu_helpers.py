@@ -6,7 +6,7 @@ torch = pytest.importorskip("torch")
 
 from oracle import formats as OF  # noqa: E402
 
-FMT_OBJ = {0: OF.E4M3, 1: OF.E5M2}
+FMT_OBJ = {0: OF.E4M3, 1: OF.E5M2, 2: OF.E2M1}
 
 # group-size mixes covering empty, 1, block-1, block, block+1 and large groups
 EDGE_SIZES = [0, 1, 31, 32, 33, 127, 128, 129, 255, 256, 257, 0, 5]
@@ -34,6 +34,13 @@ def codes_host(t, rows=None) -> np.ndarray:
     """Row-major host copy of pair-interleaved device codes (the first `rows` rows)."""
     from mx_scaled_grouped_amd import api
     return host(api.unpack_codes(t, rows))
+
+
+def codes_of(t, fmt, rows=None) -> np.ndarray:
+    """Row-major codes, one per uint8, of pair-interleaved device codes; 4-bit
+    e2m1 codes (fmt 2) are split out of their bytes."""
+    c = codes_host(t, rows)
+    return OF.unpack_nibbles(c) if fmt == 2 else c
 
 
 def bf16_host_f64(t) -> np.ndarray:

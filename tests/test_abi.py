@@ -62,7 +62,8 @@ def _qact(**kw):
 
 def test_quantize_act_validation():
     assert _qact(recipe=7) == _lib.INVALID_ARGUMENT
-    assert _qact(fmt=2) == _lib.INVALID_ARGUMENT
+    assert _qact(fmt=5) == _lib.INVALID_ARGUMENT
+    assert _qact(fmt=2) == _lib.UNSUPPORTED                 # e2m1 only with MX
     assert _qact(C=200) == _lib.BAD_SHAPE                   # feature dim % 128
     assert _qact(M=-1) == _lib.INVALID_ARGUMENT
     assert _qact(rc=None) == _lib.INVALID_ARGUMENT          # no output at all
@@ -130,15 +131,15 @@ def test_grouped_mm_validation():
     assert _mm(mode=2, ps=FAKE, lda=128, ldb=128) == _lib.BAD_SHAPE  # ld below capacity
 
 
-def _act_sizes(M, C, recipe, E):
+def _act_sizes(M, C, recipe, E, fmt=0):
     out = (ctypes.c_int64 * 5)()
-    st = _lib.status_of("mxsg_quantize_act_sizes", M, C, recipe, E, ctypes.addressof(out))
+    st = _lib.status_of("mxsg_quantize_act_sizes", M, C, recipe, fmt, E, ctypes.addressof(out))
     return st, list(out)
 
 
-def _w_sizes(E, K, N, recipe):
+def _w_sizes(E, K, N, recipe, fmt=0):
     out = (ctypes.c_int64 * 4)()
-    st = _lib.status_of("mxsg_quantize_weight_sizes", E, K, N, recipe, ctypes.addressof(out))
+    st = _lib.status_of("mxsg_quantize_weight_sizes", E, K, N, recipe, fmt, ctypes.addressof(out))
     return st, list(out)
 
 
@@ -166,7 +167,14 @@ def test_quantize_act_sizes_validation():
     assert _act_sizes(16, 128, 4, 1)[0] == _lib.INVALID_ARGUMENT
     assert _act_sizes(16, 128, 0, -1)[0] == _lib.INVALID_ARGUMENT
     assert _act_sizes(1 << 31, 128, 0, 1)[0] == _lib.BAD_SHAPE
-    assert _lib.status_of("mxsg_quantize_act_sizes", 16, 128, 0, 1, None) == _lib.INVALID_ARGUMENT
+    assert _lib.status_of("mxsg_quantize_act_sizes", 16, 128, 0, 0, 1, None) == _lib.INVALID_ARGUMENT
+    # 4-bit codes: MX only, half the code bytes, same scales
+    assert _act_sizes(16, 128, 0, 1, fmt=2)[0] == _lib.UNSUPPORTED
+    assert _act_sizes(16, 128, 3, 1, fmt=5)[0] == _lib.INVALID_ARGUMENT
+    st, b4 = _act_sizes(7, 256, 3, 3, fmt=2)
+    st8, b8 = _act_sizes(7, 256, 3, 3, fmt=0)
+    assert st == st8 == _lib.OK
+    assert [b4[0], b4[2]] == [b8[0] // 2, b8[2] // 2] and [b4[1], b4[3], b4[4]] == [b8[1], b8[3], b8[4]]
     # the same shape rule answers the launching call the same way
     assert _qact(C=200) == _act_sizes(16, 200, 0, 1)[0]
 
@@ -186,6 +194,8 @@ def test_quantize_weight_sizes_validation():
     assert _w_sizes(1 << 16, 128, 128, 0)[0] == _lib.BAD_SHAPE
     assert _w_sizes(2, 128, 128, 5)[0] == _lib.INVALID_ARGUMENT
     assert _qw(K=130) == _w_sizes(2, 130, 256, 0)[0]
+    assert _w_sizes(2, 256, 256, 2, fmt=2)[0] == _lib.UNSUPPORTED
+    assert _w_sizes(2, 256, 384, 3, fmt=2)[1] == [2 * 256 * 384 // 2, 2 * 256 * 384 // 32] * 2
 
 
 def _mm_check(**kw):
@@ -219,11 +229,19 @@ def test_grouped_mm_check_agrees_with_launcher():
     assert _mm_check(mode=2, lda=128, ldb=128) == _lib.BAD_SHAPE
     assert _mm_check(mode=2, lda=1024, ldb=1024) == _lib.OK
     assert _mm_check(mode=1, recipe=2, N=65536 + 128, lda=65536 + 128, ldb=65536 + 128) == _lib.UNSUPPORTED
+    # 4-bit operands: MX, both sides, row lengths in code bytes
+    assert _mm_check(recipe=3, fa=2, fb=2, lda=128, ldb=128) == _lib.OK
+    assert _mm_check(recipe=3, fa=2, fb=2, lda=256, ldb=256) == _lib.BAD_SHAPE   # ldb must be K/2
+    assert _mm_check(recipe=3, fa=2, fb=0, lda=128, ldb=128) == _lib.UNSUPPORTED
+    assert _mm_check(recipe=0, fa=2, fb=2, lda=128, ldb=128) == _lib.UNSUPPORTED
+    assert _mm_check(mode=2, recipe=3, fa=2, fb=2, lda=320, ldb=320) == _lib.OK   # capacity 640 / 2
+    assert _mm_check(mode=2, recipe=3, fa=2, fb=2, lda=288, ldb=320) == _lib.BAD_SHAPE
 
 
 def test_delayed_and_sweep_validation():
     assert _lib.status_of("mxsg_delayed_update", FAKE, FAKE, FAKE, FAKE, FAKE, 2, 0, 0, None) == _lib.INVALID_ARGUMENT
     assert _lib.status_of("mxsg_delayed_update", None, FAKE, FAKE, FAKE, FAKE, 2, 16, 0, None) == _lib.INVALID_ARGUMENT
+    assert _lib.status_of("mxsg_delayed_update", FAKE, FAKE, FAKE, FAKE, FAKE, 2, 16, 2, None) == _lib.INVALID_ARGUMENT
     assert _lib.status_of("mxsg_cast_sweep", 0, 16, 5, FAKE, None) == _lib.INVALID_ARGUMENT
     assert _lib.status_of("mxsg_cast_sweep", 0, 16, 0, None, None) == _lib.INVALID_ARGUMENT
     assert _lib.status_of("mxsg_stream_copy", FAKE, FAKE, 24, None) == _lib.INVALID_ARGUMENT

@@ -31,8 +31,14 @@ def _api():
     return api
 
 
+E2M1_INTS = np.array([0, 1, 2, 3, 4, 6, -1, -2, -3, -4, -6], np.float32)
+
+
 def _int_codes(rng, shape, fmt):
-    v = rng.integers(-8, 9, size=shape).astype(np.float32)
+    if fmt == 2:    # e2m1 holds the integers 0, +-1, +-2, +-3, +-4, +-6
+        v = rng.choice(E2M1_INTS, size=shape)
+    else:
+        v = rng.integers(-8, 9, size=shape).astype(np.float32)
     return OF.encode_sat_rne(v, FMT_OBJ[fmt])
 
 
@@ -97,8 +103,10 @@ def make_case(mode, recipe, fa, fb, sizes, K, N, seed, exact=True):
         mask = np.zeros(Rp, bool)
         for g in range(E):
             mask[P[g]:P[g] + sizes[g]] = True
-        a = np.full((K, ld), 0x7F, np.uint8)     # NaN codes past the logical extent
-        b = np.full((N, ld), 0x7F, np.uint8)
+        # NaN codes past the logical extent (e2m1 has none: its largest value)
+        fill = 0x7 if fa == 2 else 0x7F
+        a = np.full((K, ld), fill, np.uint8)
+        b = np.full((N, ld), fill, np.uint8)
         a[:, :Rp] = np.where(mask[None, :], codes((K, Rp), fa), 0)
         b[:, :Rp] = np.where(mask[None, :], codes((N, Rp), fb), 0)
         if recipe == "tw":
@@ -122,9 +130,12 @@ def make_case(mode, recipe, fa, fb, sizes, K, N, seed, exact=True):
 
 def run_case(c, out=None, accumulate=False):
     api = _api()
+    a, b, lda, ldb = c.a, c.b, c.lda, c.ldb
+    if c.fa == 2:   # two e2m1 codes per byte; row lengths in code bytes
+        a, b, lda, ldb = OF.pack_nibbles(a), OF.pack_nibbles(b), lda // 2, ldb // 2
     return api.grouped_mm(c.mode, c.recipe, c.fa, c.fb, c.E, c.M, c.K, c.N, to_dev(c.ge),
-                          api.pack_codes(to_dev(c.a)), to_dev(c.sa), c.lda, api.pack_codes(to_dev(c.b)),
-                          to_dev(c.sb), c.ldb,
+                          api.pack_codes(to_dev(a)), to_dev(c.sa), lda, api.pack_codes(to_dev(b)),
+                          to_dev(c.sb), ldb,
                           padded_starts=None if c.padded is None else to_dev(c.padded), out=out,
                           accumulate=accumulate)
 
@@ -172,6 +183,29 @@ def test_random_within_tolerance(recipe, mode):
     fa, fb = (1, 0) if mode == 1 else ((0, 1) if mode == 2 else (0, 0))
     c = make_case(mode, recipe, fa, fb, sizes, K, N, seed=31 + mode, exact=False)
     print(f"gemm random {recipe} mode={mode} M={c.M}", flush=True)
+    _check_tol(c, result_f64(c, run_case(c)))
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2], ids=["fwd", "dgrad", "wgrad"])
+def test_mxfp4_exact_integer(mode):
+    """MXFP4 (e2m1 x e2m1, two codes per byte, E8M0 scales per 32): exact
+    integer operands, bit-exact against the oracle; K and N give odd stage
+    counts and a ragged N tile."""
+    K, N = 384, 640
+    c = make_case(mode, "mx", 2, 2, SIZES, K, N, seed=60 + mode)
+    print(f"gemm mxfp4 exact mode={mode} M={c.M}", flush=True)
+    got = result_f64(c, run_case(c))
+    bad = np.flatnonzero(got.reshape(-1) != c.ref.reshape(-1))
+    assert bad.size == 0, f"{bad.size} mismatches; first {np.unravel_index(bad[0], got.shape)}: " \
+                          f"got {got.reshape(-1)[bad[0]]} want {c.ref.reshape(-1)[bad[0]]}"
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2], ids=["fwd", "dgrad", "wgrad"])
+def test_mxfp4_random_within_tolerance(mode):
+    K, N = 640, 512
+    sizes = [3, 0, 520, 129, 700, 1]
+    c = make_case(mode, "mx", 2, 2, sizes, K, N, seed=70 + mode, exact=False)
+    print(f"gemm mxfp4 random mode={mode} M={c.M}", flush=True)
     _check_tol(c, result_f64(c, run_case(c)))
 
 

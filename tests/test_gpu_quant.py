@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 from tests.gpu_helpers import (torch, EDGE_SIZES, FMT_OBJ, gpu_available, to_dev_u16, to_dev, host, codes_host,
-                               assert_bits_equal)
+                               codes_of, assert_bits_equal)
 from oracle import quant as OQ
 from oracle import formats as OF
 from oracle.delayed import DelayedState as OracleDelayed
@@ -42,7 +42,7 @@ def _segments_check(codes_dev, start: int, fmt, label: str):
     return int(change.numel())
 
 
-@pytest.mark.parametrize("fmt", [0, 1], ids=["e4m3", "e5m2"])
+@pytest.mark.parametrize("fmt", [0, 1, 2], ids=["e4m3", "e5m2", "e2m1"])
 def test_cast_exhaustive(fmt):
     """Every non-NaN fp32 input, both signs: the saturating RNE cast used by
     all quantizers equals the oracle's table-search encoder."""
@@ -77,18 +77,18 @@ def test_stream_copy():
 # ---------------------------------------------------------------------------
 # token tensors
 
-RECIPE_FMTS = [("tw", 0), ("tw", 1), ("block", 0), ("block", 1), ("mx", 0), ("mx", 1)]
+RECIPE_FMTS = [("tw", 0), ("tw", 1), ("block", 0), ("block", 1), ("mx", 0), ("mx", 1), ("mx", 2)]
 
 
 def _compare_act(q, ref, recipe, M, C, rowwise, colwise):
     if rowwise:
-        assert_bits_equal(codes_host(q.row_codes, M), ref["row_codes"], "row codes")
+        assert_bits_equal(codes_of(q.row_codes, q.fmt, M), ref["row_codes"], "row codes")
         assert_bits_equal(host(q.row_scales), ref["row_scales"], "row scales")
     if colwise:
         P = host(q.padded_starts).astype(np.int64)
         assert np.array_equal(P, ref["padded_starts"]), (P, ref["padded_starts"])
         Rp = int(P[-1])
-        assert_bits_equal(codes_host(q.col_codes)[:, :Rp], ref["col_codes"], "col codes")
+        assert_bits_equal(codes_of(q.col_codes, q.fmt)[:, :Rp], ref["col_codes"], "col codes")
         cs = host(q.col_scales)
         if recipe in ("tw", "dl"):
             assert_bits_equal(cs, ref["col_scales"], "col scales")
@@ -166,9 +166,9 @@ def test_act_gather(recipe, fmt):
     Rp = int(ref["padded_starts"][-1])
     blk = {"block": 128, "mx": 32}.get(recipe)
     assert torch.equal(q.padded_starts, p.padded_starts)
-    assert_bits_equal(codes_host(q.row_codes, M), codes_host(p.row_codes, M), "gathered row codes")
+    assert_bits_equal(codes_of(q.row_codes, fmt, M), codes_of(p.row_codes, fmt, M), "gathered row codes")
     assert torch.equal(q.row_scales, p.row_scales)
-    assert_bits_equal(codes_host(q.col_codes)[:, :Rp], codes_host(p.col_codes)[:, :Rp],
+    assert_bits_equal(codes_of(q.col_codes, fmt)[:, :Rp], codes_of(p.col_codes, fmt)[:, :Rp],
                       "gathered column codes")
     if blk:
         assert torch.equal(q.col_scales[:, :Rp // blk], p.col_scales[:, :Rp // blk])
@@ -258,7 +258,7 @@ def test_act_special_values():
     x[4, 7] = 0x4780                       # 65536
     ge = W.group_ends_from_sizes([50, 46])
     for recipe in ("tw", "block", "mx"):
-        for fmt in (0, 1):
+        for fmt in ((0, 1, 2) if recipe == "mx" else (0, 1)):
             print(f"special values {recipe} fmt={fmt}", flush=True)
             ref = OQ.quantize_act(x, recipe, FMT_OBJ[fmt], ge, rowwise=True, colwise=True)
             q = api.quantize_act(to_dev_u16(x), recipe, fmt, to_dev(ge), rowwise=True, colwise=True)
@@ -268,7 +268,7 @@ def test_act_special_values():
 # ---------------------------------------------------------------------------
 # weights
 
-@pytest.mark.parametrize("recipe,fmt", [("tw", 0), ("tw", 1), ("block", 0), ("block", 1), ("mx", 0), ("mx", 1)])
+@pytest.mark.parametrize("recipe,fmt", RECIPE_FMTS)
 def test_weight_layouts(recipe, fmt):
     api = _api()
     w = W.normal_bf16(106, 0, (3, 256, 384), std=0.02)
@@ -276,8 +276,8 @@ def test_weight_layouts(recipe, fmt):
     print(f"quantize_weight {recipe} fmt={fmt}", flush=True)
     ref = OQ.quantize_weight(w, recipe, FMT_OBJ[fmt])
     q = api.quantize_weight(to_dev_u16(w), recipe, fmt)
-    assert_bits_equal(codes_host(q.kmajor_codes), ref["kmajor_codes"], "k-major codes")
-    assert_bits_equal(codes_host(q.nmajor_codes), ref["nmajor_codes"], "n-major codes")
+    assert_bits_equal(codes_of(q.kmajor_codes, fmt), ref["kmajor_codes"], "k-major codes")
+    assert_bits_equal(codes_of(q.nmajor_codes, fmt), ref["nmajor_codes"], "n-major codes")
     assert_bits_equal(host(q.kmajor_scales), ref["kmajor_scales"], "k-major scales")
     assert_bits_equal(host(q.nmajor_scales), ref["nmajor_scales"], "n-major scales")
     if recipe == "tw":
