@@ -28,6 +28,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
+PEAK_FP4_TFLOPS = 10100.0      # MI355X dense FP4 / FP6 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 GEMM_SOURCE = os.path.join(HERE, "mx_scaled_grouped_amd", "csrc", "gemm.hip")
 
@@ -36,6 +37,7 @@ WORKLOADS = {
     "mixtral-tw": 2,   # Mixtral shapes, tensorwise e4m3, forward only
     "deepseek-block": 4,
     "llama4-mx": 5,
+    "llama4-mxfp4": 6,
 }
 
 
@@ -74,7 +76,7 @@ def make_inputs(cid, torch, W, sets=2):
         return t.to(torch.bfloat16)
 
     def outliers(t):
-        if cid != 5:
+        if cid not in (5, 6):
             return t
         flat = t.view(-1)
         idx = torch.randint(0, flat.numel(), (max(1, flat.numel() // 1000),), generator=g, device=dev)
@@ -119,8 +121,14 @@ class Step:
     def __init__(self, torch, api, spec, ge, weights, recipe, row_index=None):
         self.torch, self.api, self.spec, self.ge, self.weights = torch, api, spec, ge, weights
         self.row_index = row_index   # routed row -> token; None: a_gu is already gathered
-        self.recipe = recipe
-        self.fa, self.fg = 0, (1 if recipe == "dl" else 0)     # hybrid: e5m2 gradients
+        # "mxfp4" is the MX recipe with e2m1 elements for every operand
+        self.recipe = "mx" if recipe == "mxfp4" else recipe
+        if recipe == "mxfp4":
+            self.fa = self.fw = self.fg = 2
+        else:
+            self.fa, self.fw = 0, 0
+            self.fg = 1 if recipe == "dl" else 0     # hybrid: e5m2 gradients
+        self.fp4 = recipe == "mxfp4"
         self.E = spec.experts
         self.bwd = "dgrad" in spec.modes
         self.q = {}        # reused quantized outputs
@@ -166,7 +174,7 @@ class Step:
             if r == "dl":
                 kw = dict(state=self.st_f, unit=len(spec.gemms) + gi * self.E)
             qw = self._t(f"quant_w_{which}", lambda: api.quantize_weight(
-                w, r, 0, kmajor=True, nmajor=bwd, out=self.q.get("w_" + which), **kw))
+                w, r, self.fw, kmajor=True, nmajor=bwd, out=self.q.get("w_" + which), **kw))
             self.q["w_" + which] = qw
             self.out["y_" + which] = self._t(f"gemm_fwd_{which}", lambda: api.grouped_mm_fwd(
                 qa, qw, self.ge, out=self.out.get("y_" + which)))
@@ -188,7 +196,8 @@ class Step:
         """Algorithmic GEMM FLOPs and quantization bytes per call name."""
         spec, r = self.spec, self.recipe
         flops, byts = {}, {}
-        per_layout = {"tw": 1.0, "dl": 1.0, "block": 1.0 + 4 / 128, "mx": 1.0 + 1 / 32}[r]
+        code = 0.5 if self.fp4 else 1.0      # bytes per element of one code layout
+        per_layout = {"tw": code, "dl": code, "block": code + 4 / 128, "mx": code + 1 / 32}[r]
         read = {"tw": 4.0, "dl": 2.0, "block": 2.0, "mx": 2.0}[r]   # tw reads twice (amax pass)
         w_layout = {"block": 1.0 + 4 / 16384}.get(r, per_layout)
         for which in spec.gemms:
@@ -205,11 +214,13 @@ class Step:
         return flops, byts
 
 
-def attainable_ms(spec, group_sizes, modes):
+def attainable_ms(spec, group_sizes, modes, peak_tflops=PEAK_FP8_TFLOPS, code_bytes=1.0):
     """Roofline time of each GEMM call: sum over groups of max(FLOPs / MFMA
-    peak, bytes / HBM peak), with a group's algorithmic bytes = its FP8
-    operand codes read once plus its output written once (bf16 for forward
-    and dgrad, fp32 dW for wgrad; an empty group still writes its zero dW)."""
+    peak, bytes / HBM peak), with a group's algorithmic bytes = its operand
+    codes (code_bytes per element) read once plus its output written once
+    (bf16 for forward and dgrad, fp32 dW for wgrad; an empty group still
+    writes its zero dW)."""
+    cb = code_bytes
     out = {}
     for which in spec.gemms:
         K, N = spec.gemm_shape(which)
@@ -219,12 +230,12 @@ def attainable_ms(spec, group_sizes, modes):
                 m = int(m)
                 f = 2.0 * m * K * N
                 if mode == "fwd":
-                    b = (m * K + K * N + 2 * m * N) if m else 0
+                    b = (cb * (m * K + K * N) + 2 * m * N) if m else 0
                 elif mode == "dgrad":
-                    b = (m * N + K * N + 2 * m * K) if m else 0
+                    b = (cb * (m * N + K * N) + 2 * m * K) if m else 0
                 else:
-                    b = m * K + m * N + 4 * K * N
-                t = t + max(f / (PEAK_FP8_TFLOPS * 1e12), b / (PEAK_HBM_GBS * 1e9))
+                    b = cb * (m * K + m * N) + 4 * K * N
+                t = t + max(f / (peak_tflops * 1e12), b / (PEAK_HBM_GBS * 1e9))
             out[f"gemm_{mode}_{which}"] = t * 1e3
     return out
 
@@ -254,26 +265,27 @@ def cpu_baseline(cid, rows, cols):
     K, N = spec.gemm_shape("gu")
     N = min(N, cols)
     m = min(rows, int(r.group_sizes[0]))
-    rec = {"tw": "tw", "dl": "dl", "block": "block", "mx": "mx"}[spec.recipe]
+    rec = {"tw": "tw", "dl": "dl", "block": "block", "mx": "mx", "mxfp4": "mx"}[spec.recipe]
+    fq = OF.E2M1 if spec.recipe == "mxfp4" else OF.E4M3     # activations and weights
     a = W.normal_bf16(cid, W.T_X, (m, K))
     w = W.normal_bf16(cid, W.T_W1, (1, K, N), std=0.02, chunk_rows=256)
     ge = np.array([m], np.int32)
     bwd = "dgrad" in spec.modes
-    fg = OF.E5M2 if rec == "dl" else OF.E4M3
+    fg = OF.E5M2 if rec == "dl" else fq
     dl = (np.float32(1.0), np.float32(1.0))
     t0 = time.perf_counter()
-    qa = OQ.quantize_act(a, rec, OF.E4M3, ge, rowwise=True, colwise=bwd, dl_scale=dl)
-    qw = OQ.quantize_weight(w, rec, OF.E4M3, dl_scale=(np.ones(1, np.float32), np.ones(1, np.float32)))
-    A = OG.deq_act_rows(qa["row_codes"], qa["row_scales"], rec, OF.E4M3)
-    Y = OG.round_bf16(OG.grouped_fwd(A, OG.deq_weight(qw, rec, OF.E4M3, "k"), ge))
+    qa = OQ.quantize_act(a, rec, fq, ge, rowwise=True, colwise=bwd, dl_scale=dl)
+    qw = OQ.quantize_weight(w, rec, fq, dl_scale=(np.ones(1, np.float32), np.ones(1, np.float32)))
+    A = OG.deq_act_rows(qa["row_codes"], qa["row_scales"], rec, fq)
+    Y = OG.round_bf16(OG.grouped_fwd(A, OG.deq_weight(qw, rec, fq, "k"), ge))
     flops = 2.0 * m * K * N
     if bwd:
         dy = W.normal_bf16(cid, W.T_DY1, (m, N), std=2.0 ** -10)
         qd = OQ.quantize_act(dy, rec, fg, ge, rowwise=True, colwise=True, dl_scale=dl)
         D = OG.deq_act_rows(qd["row_codes"], qd["row_scales"], rec, fg)
-        dA = OG.round_bf16(OG.grouped_dgrad(D, OG.deq_weight(qw, rec, OF.E4M3, "n"), ge))
+        dA = OG.round_bf16(OG.grouped_dgrad(D, OG.deq_weight(qw, rec, fq, "n"), ge))
         P = qa["padded_starts"]
-        At = OG.unpad_cols(OG.deq_act_cols(qa["col_codes"], qa["col_scales"], rec, OF.E4M3), P, ge)
+        At = OG.unpad_cols(OG.deq_act_cols(qa["col_codes"], qa["col_scales"], rec, fq), P, ge)
         Dt = OG.unpad_cols(OG.deq_act_cols(qd["col_codes"], qd["col_scales"], rec, fg), P, ge)
         dW = OG.round_f32(OG.grouped_wgrad(At, Dt, ge, 1))
         flops *= 3
@@ -369,7 +381,8 @@ def main():
     launches = len(gemm_ms)
     achieved = step_flops / (gemm_total_ms * 1e-3) / 1e12
     quant_agg = sum(byts.values()) / (quant_total_ms * 1e-3) / 1e9
-    att = attainable_ms(spec, routing.group_sizes, spec.modes)
+    peak = PEAK_FP4_TFLOPS if step.fp4 else PEAK_FP8_TFLOPS
+    att = attainable_ms(spec, routing.group_sizes, spec.modes, peak, 0.5 if step.fp4 else 1.0)
     att_frac = {k: att[k] / gemm_ms[k] for k in gemm_ms}
     att_total = sum(att[k] for k in gemm_ms) / gemm_total_ms
 
@@ -413,14 +426,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8(e4m3/e5m2) codes, fp32 accumulate, bf16/fp32 out",
+        "dtype": ("fp4(e2m1) codes with E8M0 block scales" if step.fp4 else "fp8(e4m3/e5m2) codes")
+                 + ", fp32 accumulate, bf16/fp32 out",
         "data": "synthetic (seeded torch generator on the GPU; routing seeded numpy)",
         "config": {"workload": spec.name, "experts": spec.experts, "tokens": spec.tokens,
                    "topk": spec.topk, "routed_rows": R, "hidden": spec.hidden, "ffn": spec.ffn,
                    "recipe": spec.recipe, "modes": list(spec.modes),
                    "group_sizes": [int(x) for x in routing.group_sizes]},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(args.workload),
                      "kernel": "grouped_gemm_kernel (every GEMM launch of a step)",
                      "launches_per_step": launches,

@@ -87,30 +87,25 @@ __device__ __forceinline__ uint2 cvt8(uint4 v, float inv) {
   return r;
 }
 
-// e2m1 code (4 bits, sign in bit 3) of a float: saturating round to nearest
-// even. The magnitude code is the number of decision points below |v|: the
-// midpoints between neighbouring values, a tie going to the even code (the
-// one whose mantissa bit is 0), so the comparison is strict (>) at ties that
-// round down and non-strict (>=) at ties that round up; above 5 every value
-// saturates to 6 (code 7). The sign comes from the sign bit (-0 -> 0x8).
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-  const float a = __builtin_fabsf(v);
-  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                     (uint32_t)(a > 5.0f);
-  return c | ((__float_as_uint(v) >> 28) & 8u);
+// Two floats -> two e2m1 codes (4 bits each, sign in bit 3; `a` in the low
+// nibble) written into byte SEL of `old`: saturating round to nearest even,
+// by v_cvt_scalef32_pk_fp4_f32 with scale 1.0 (the multiplier is applied
+// before, in fp32). Measured on the device against a comparison-based
+// encoder over all 2^32 non-NaN fp32 inputs: identical, including the ties
+// to the even code, the saturation to 6 and the sign of zero results.
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_pk(uint32_t old, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
 }
 
 // 8 bf16 (one 16-byte vector) times inv -> 8 e2m1 codes, element i in
 // nibble i (element 2j in the low nibble of byte j)
 __device__ __forceinline__ uint32_t cvt8_e2m1(uint4 v, float inv) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   uint32_t r = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r |= e2m1_code(bf16_lo(w[i]) * inv) << (8 * i);
-    r |= e2m1_code(bf16_hi(w[i]) * inv) << (8 * i + 4);
-  }
+  r = e2m1_pk<0>(r, bf16_lo(v.x) * inv, bf16_hi(v.x) * inv);
+  r = e2m1_pk<1>(r, bf16_lo(v.y) * inv, bf16_hi(v.y) * inv);
+  r = e2m1_pk<2>(r, bf16_lo(v.z) * inv, bf16_hi(v.z) * inv);
+  r = e2m1_pk<3>(r, bf16_lo(v.w) * inv, bf16_hi(v.w) * inv);
   return r;
 }
 

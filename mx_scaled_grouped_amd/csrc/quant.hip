@@ -378,13 +378,18 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
     uint32_t d0[4], d1[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      d0[j] = 0;
-      d1[j] = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        d0[j] |= e2m1_code(bf16_lo(w[8 * j + i]) * inv0) << (4 * i);
-        d1[j] |= e2m1_code(bf16_hi(w[8 * j + i]) * inv1) << (4 * i);
-      }
+      const uint32_t *wj = &w[8 * j];
+      uint32_t x = 0, y = 0;
+      x = e2m1_pk<0>(x, bf16_lo(wj[0]) * inv0, bf16_lo(wj[1]) * inv0);
+      x = e2m1_pk<1>(x, bf16_lo(wj[2]) * inv0, bf16_lo(wj[3]) * inv0);
+      x = e2m1_pk<2>(x, bf16_lo(wj[4]) * inv0, bf16_lo(wj[5]) * inv0);
+      x = e2m1_pk<3>(x, bf16_lo(wj[6]) * inv0, bf16_lo(wj[7]) * inv0);
+      y = e2m1_pk<0>(y, bf16_hi(wj[0]) * inv1, bf16_hi(wj[1]) * inv1);
+      y = e2m1_pk<1>(y, bf16_hi(wj[2]) * inv1, bf16_hi(wj[3]) * inv1);
+      y = e2m1_pk<2>(y, bf16_hi(wj[4]) * inv1, bf16_hi(wj[5]) * inv1);
+      y = e2m1_pk<3>(y, bf16_hi(wj[6]) * inv1, bf16_hi(wj[7]) * inv1);
+      d0[j] = x;
+      d1[j] = y;
     }
     *reinterpret_cast<uint4 *>(&ctile[(2 * fp) * CODE_LD4 + q * 16]) = make_uint4(d0[0], d0[1], d0[2], d0[3]);
     *reinterpret_cast<uint4 *>(&ctile[(2 * fp + 1) * CODE_LD4 + q * 16]) =
@@ -488,8 +493,9 @@ __global__ __launch_bounds__(256) void cast_sweep_kernel(uint32_t start, int64_t
   const uint32_t s = start + (uint32_t)i4;
   uint32_t c;
   if constexpr (FMT == kE2M1) {  // one 4-bit code per output byte
-    c = e2m1_code(__uint_as_float(s)) | (e2m1_code(__uint_as_float(s + 1)) << 8) |
-        (e2m1_code(__uint_as_float(s + 2)) << 16) | (e2m1_code(__uint_as_float(s + 3)) << 24);
+    const uint32_t p = e2m1_pk<1>(e2m1_pk<0>(0u, __uint_as_float(s), __uint_as_float(s + 1)),
+                                  __uint_as_float(s + 2), __uint_as_float(s + 3));
+    c = (p & 0xfu) | ((p & 0xf0u) << 4) | ((p & 0xf00u) << 8) | ((p & 0xf000u) << 12);
   } else {
     c = cvt4<FMT>(__uint_as_float(s), __uint_as_float(s + 1), __uint_as_float(s + 2),
                   __uint_as_float(s + 3));

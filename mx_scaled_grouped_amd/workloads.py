@@ -130,7 +130,7 @@ class WorkloadSpec:
     topk: int
     hidden: int            # K of the gate/up GEMM
     ffn: int               # per-expert FFN width
-    recipe: str            # "tw", "dl", "block", "mx"
+    recipe: str            # "tw", "dl", "block", "mx", "mxfp4" (MX with e2m1 elements)
     modes: tuple           # subset of ("fwd", "dgrad", "wgrad")
     gemms: tuple           # ("gu",) or ("gu", "dn")
     steps: int = 1
@@ -156,6 +156,9 @@ SPECS: Dict[int, WorkloadSpec] = {
                     ("fwd", "dgrad", "wgrad"), ("gu", "dn")),
     5: WorkloadSpec(5, "llama4-scout-experts-mxfp8", 16, 16384, 1, 5120, 8192, "mx",
                     ("fwd", "dgrad", "wgrad"), ("gu", "dn")),
+    # the MXFP4 variant of the same shapes: e2m1 elements for every operand
+    6: WorkloadSpec(6, "llama4-scout-experts-mxfp4", 16, 16384, 1, 5120, 8192, "mxfp4",
+                    ("fwd", "dgrad", "wgrad"), ("gu", "dn")),
 }
 
 C4_MASKED = (0, 21, 42, 63)
@@ -169,8 +172,8 @@ def routing_for(cid: int) -> Routing:
         return route_topk(2, s.tokens, s.experts, s.topk)   # C3 reuses C2's routing
     if cid == 4:
         return route_topk(cid, s.tokens, s.experts, s.topk, masked=C4_MASKED)
-    if cid == 5:
-        return route_zipf(cid, s.tokens, s.experts, 1.1)
+    if cid in (5, 6):
+        return route_zipf(5, s.tokens, s.experts, 1.1)   # C6 reuses C5's routing
     raise KeyError(cid)
 
 
@@ -186,11 +189,11 @@ def activation_bf16(cid: int, which: str, routing: Routing, step: int = 0) -> np
     std = 1.01 ** step if cid == 3 else 1.0
     if which == "gu":
         x = normal_bf16(cid, tid, (s.tokens, K), std=std, step=step)
-        if cid == 5:
+        if cid in (5, 6):
             x = _outliers(cid, tid, x)
         return x[routing.row_token]
     a = normal_bf16(cid, tid, (routing.rows, K), std=std, step=step)
-    if cid == 5:
+    if cid in (5, 6):
         a = _outliers(cid, tid, a)
     return a
 

@@ -29,7 +29,14 @@ from oracle.delayed import DelayedState as ODelayed
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="no GPU")]
 
-FMT = {0: OF.E4M3, 1: OF.E5M2}
+FMT = {0: OF.E4M3, 1: OF.E5M2, 2: OF.E2M1}
+
+
+def _codes(t, fmt):
+    """Host codes (one per uint8) of a selection of unpacked device code rows;
+    e2m1 rows hold two codes per byte."""
+    c = _np(t)
+    return OF.unpack_nibbles(c) if fmt is OF.E2M1 else c
 TOL = 1e-3
 WORKLOADS = ["mixtral-tw", "mixtral-dl", "deepseek-block", "llama4-mx"]
 
@@ -74,7 +81,7 @@ def _run(name):
     torch.cuda.synchronize()
     print(f"[fullsize] {name}: two steps done", flush=True)
     st = {"spec": spec, "ge": routing.group_ends.astype(np.int64), "step": step,
-          "weights": weights, "sets": sets, "recipe": spec.recipe}
+          "weights": weights, "sets": sets, "recipe": step.recipe}
     if spec.recipe == "dl":
         st["scales"] = _oracle_delayed(step, spec, weights, sets)
     _cache[name] = st
@@ -195,12 +202,14 @@ def check_forward(name, which):
     rec, dls = _act_scale(st, which, "f", a_bits, fa)
     ra = OQ.quantize_act(a_bits[rows], rec, fa, dl_scale=dls)
     qa = step.q["a_" + which]
-    assert_bits_equal(_np(_take(_unpack(qa.row_codes), (0, rows))), ra["row_codes"], "activation codes")
+    assert_bits_equal(_codes(_take(_unpack(qa.row_codes), (0, rows)), fa), ra["row_codes"], "activation codes")
     _check_scales_rows(qa.row_scales, ra["row_scales"], rec, rows, "activation scales")
-    wrec, wdl = _w_scale(st, which, w_bits, OF.E4M3)
-    rw = OQ.quantize_weight(np.ascontiguousarray(w_bits[:, :, ncols]), wrec, OF.E4M3, dl_scale=wdl)
+    fw = FMT[step.fw]
+    wrec, wdl = _w_scale(st, which, w_bits, fw)
+    rw = OQ.quantize_weight(np.ascontiguousarray(w_bits[:, :, ncols]), wrec, fw, dl_scale=wdl)
     qw = step.q["w_" + which]
-    assert_bits_equal(_np(_take(_unpack(qw.kmajor_codes), (1, ncols))), rw["kmajor_codes"], "weight k-major codes")
+    assert_bits_equal(_codes(_take(_unpack(qw.kmajor_codes), (1, ncols)), fw), rw["kmajor_codes"],
+                      "weight k-major codes")
     ks = _np(qw.kmajor_scales)
     if wrec == "dl":
         assert_bits_equal(ks, rw["kmajor_scales"], "weight scales")
@@ -209,7 +218,7 @@ def check_forward(name, which):
     else:
         assert_bits_equal(ks[:, ncols, :], rw["kmajor_scales"], "weight MX scales (k blocks)")
     ref = OG.round_bf16(OG.grouped_fwd(OG.deq_act_rows(ra["row_codes"], ra["row_scales"], rec, fa),
-                                       OG.deq_weight(rw, wrec, OF.E4M3, "k"), ge_s))
+                                       OG.deq_weight(rw, wrec, fw, "k"), ge_s))
     y = step.out["y_" + which]
     got = OG.bf16_bits_to_f64(_bits(_take(y, (0, rows), (1, ncols))))
     _check_err(got, ref, ge_s, f"{name} forward {which}")
@@ -227,19 +236,21 @@ def check_dgrad(name, which):
     rec, dls = _act_scale(st, which, "g", d_bits, fg)
     rd = OQ.quantize_act(d_bits[rows], rec, fg, dl_scale=dls)
     qd = step.q["dy_" + which]
-    assert_bits_equal(_np(_take(_unpack(qd.row_codes), (0, rows))), rd["row_codes"], "gradient codes")
+    assert_bits_equal(_codes(_take(_unpack(qd.row_codes), (0, rows)), fg), rd["row_codes"], "gradient codes")
     _check_scales_rows(qd.row_scales, rd["row_scales"], rec, rows, "gradient scales")
-    wrec, wdl = _w_scale(st, which, w_bits, OF.E4M3)
-    rw = OQ.quantize_weight(np.ascontiguousarray(w_bits[:, kcols, :]), wrec, OF.E4M3, dl_scale=wdl)
+    fw = FMT[step.fw]
+    wrec, wdl = _w_scale(st, which, w_bits, fw)
+    rw = OQ.quantize_weight(np.ascontiguousarray(w_bits[:, kcols, :]), wrec, fw, dl_scale=wdl)
     qw = step.q["w_" + which]
-    assert_bits_equal(_np(_take(_unpack(qw.nmajor_codes), (1, kcols))), rw["nmajor_codes"], "weight n-major codes")
+    assert_bits_equal(_codes(_take(_unpack(qw.nmajor_codes), (1, kcols)), fw), rw["nmajor_codes"],
+                      "weight n-major codes")
     ns = _np(qw.nmajor_scales)
     if wrec == "block":
         assert_bits_equal(ns[:, kblk, :], rw["nmajor_scales"], "weight tile scales")
     elif wrec == "mx":
         assert_bits_equal(ns[:, kcols, :], rw["nmajor_scales"], "weight MX scales (n blocks)")
     ref = OG.round_bf16(OG.grouped_dgrad(OG.deq_act_rows(rd["row_codes"], rd["row_scales"], rec, fg),
-                                         OG.deq_weight(rw, wrec, OF.E4M3, "n"), ge_s))
+                                         OG.deq_weight(rw, wrec, fw, "n"), ge_s))
     da = step.out["da_" + which]
     got = OG.bf16_bits_to_f64(_bits(_take(da, (0, rows), (1, kcols))))
     _check_err(got, ref, ge_s, f"{name} dgrad {which}")
@@ -264,7 +275,7 @@ def check_wgrad(name, which):
                              colwise=True, dl_scale=dls)
         P = rc["padded_starts"]
         assert np.array_equal(_np(q.padded_starts).astype(np.int64), P), tag + " padded starts"
-        cc = _np(_take(_unpack(q.col_codes), (0, cols)))
+        cc = _codes(_take(_unpack(q.col_codes), (0, cols)), fmt)
         assert_bits_equal(cc[:, :P[-1]], rc["col_codes"], tag + " column codes")
         cs = _np(q.col_scales)
         if rec == "dl":
