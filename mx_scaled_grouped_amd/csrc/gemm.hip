@@ -16,8 +16,13 @@
 // global_load_lds_dwordx4 copies (no staging registers) land XOR-swizzled
 // 16-byte chunks (bank-conflict-free fragment reads) three stages ahead of
 // use. The code operands are pair-interleaved, so a stage of 64 bytes over
-// a run of row pairs is whole 128-byte lines. While a stage's MFMAs run,
-// the next stage's fragments are read into a second register set.
+// a run of row pairs is whole 128-byte lines. A stage is one barrier: its
+// first two MFMAs are issued before it, and after it every MFMA slot also
+// issues one copy of the stage three ahead and part of the next stage's
+// fragment reads (into a second register set), so the matrix pipe is not
+// left idle while copies go out. Every stage issues the same number of
+// copies (the padding stages of the last ring turn copy from a static zero
+// source), so each wait count is a constant and the loop has no branch.
 // Tiles never straddle expert groups (row tiles start at a group's first
 // row pair; rows of a neighbouring group in the tile are computed and not
 // stored); a workgroup finds its group from the device-resident offsets
@@ -135,6 +140,18 @@ __device__ bool locate_row_tile(const GemmArgs &a, int slot, int &g_out, int64_t
   return s_found != 0;
 }
 
+// Read-only copy sources for the stages past a tile's contraction (the ring
+// runs in whole turns of four stages): zero codes and zero blockwise scales,
+// and E8M0 words of four unit scales. Reading them keeps every stage's copy
+// count the same, so no wait depends on the stage.
+#define MXSG_U7F4 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu
+#define MXSG_U7F16 MXSG_U7F4, MXSG_U7F4, MXSG_U7F4, MXSG_U7F4
+__device__ __attribute__((aligned(1024))) const uint32_t kZeroSrc[256] = {};
+__device__ __attribute__((aligned(256))) const uint32_t kUnitScaleSrc[64] = {MXSG_U7F16, MXSG_U7F16, MXSG_U7F16,
+                                                                           MXSG_U7F16};
+#undef MXSG_U7F16
+#undef MXSG_U7F4
+
 // LDS stage tiles hold rows of GBK = 64 code bytes as four 16-byte chunks;
 // chunk c of row r sits at chunk c ^ ((r >> 2) & 3), so the lanes of a
 // fragment read that share a bank sweep (rows r, r+4, r+8, r+12) hit
@@ -149,10 +166,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 __device__ __forceinline__ void dma16(const uint8_t *src, uint8_t *lds) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_addr(lds)) : "memory");
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_addr(lds)));
 }
 __device__ __forceinline__ void dma4(const void *src, void *lds) {
-  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds_addr(lds)) : "memory");
+  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds_addr(lds)));
 }
 
 // MFMA 32x32x64 f8 operand for one lane: the lane's row, and (measured lane
@@ -169,30 +186,6 @@ __device__ __forceinline__ v8i frag(const uint8_t *buf, int row, int h) {
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 24]
-__device__ __forceinline__ void wait_vm_n(int n) {
-  switch (n) {
-#define MXSG_VMW(k) case k: wait_vm<k>(); break;
-    MXSG_VMW(1) MXSG_VMW(2) MXSG_VMW(3) MXSG_VMW(4) MXSG_VMW(5) MXSG_VMW(6) MXSG_VMW(7) MXSG_VMW(8)
-    MXSG_VMW(9) MXSG_VMW(10) MXSG_VMW(11) MXSG_VMW(12) MXSG_VMW(13) MXSG_VMW(14) MXSG_VMW(15)
-    MXSG_VMW(16) MXSG_VMW(17) MXSG_VMW(18) MXSG_VMW(19) MXSG_VMW(20) MXSG_VMW(21) MXSG_VMW(22)
-    MXSG_VMW(23) MXSG_VMW(24)
-#undef MXSG_VMW
-    default: wait_vm<0>(); break;
-  }
-}
-
-// scheduling groups: MFMA I, then the LDS reads that spread RD reads evenly
-// over NM MFMAs
-template <int I, int NM, int RD>
-__device__ __forceinline__ void order_groups() {
-  if constexpr (I < NM) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    constexpr int r = (RD * (I + 1)) / NM - (RD * I) / NM;
-    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
-    order_groups<I + 1, NM, RD>();
-  }
 }
 
 // the upper 16 bytes of a fragment in the operand's low registers (a 4-bit
@@ -235,7 +228,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t Bs0[BN * GBK], Bs1[BN * GBK], Bs2[BN * GBK], Bs3[BN * GBK];
   __shared__ __attribute__((aligned(16))) float sA0[BLK ? GBM : 4], sA1[BLK ? GBM : 4], sA2[BLK ? GBM : 4], sA3[BLK ? GBM : 4];
   __shared__ __attribute__((aligned(16))) float sB0[BLK ? BN : 4], sB1[BLK ? BN : 4], sB2[BLK ? BN : 4], sB3[BLK ? BN : 4];
-  __shared__ float sbtab[BLK ? SB_TAB : 1];  // blockwise weight scales of this tile's j-block, per l-block
+  __shared__ float sbtab[BLK ? SB_TAB : 1];
+  __shared__ __attribute__((aligned(256))) uint32_t dmy[64];  // target of filler copies  // blockwise weight scales of this tile's j-block, per l-block
   // MX: per stage buffer, each tile row's E8M0 word (the 32-blocks 4w..4w+3
   // holding the stage's two), stored so the four words one lane needs are
   // contiguous: slot d holds tile row 128 (d / 128) + 32 (d % 4) + (d / 4) % 32
@@ -344,9 +338,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
       mxb = reinterpret_cast<const uint8_t *>(a.b_scales) + (MODE == kWgrad ? 0 : (int64_t)g * a.bs_gstride) +
             brow(r) * (sb_row / 32) + l0 / 32;
   }
-  // vector-memory instructions this wave issues per real stage (the waits count them)
-  const int ops_wave = AQ + BQ + (MX ? 1 + (b_wave ? 1 : 0) : 0) + (BLK ? 1 + (MODE == kWgrad && b_wave ? 1 : 0) : 0);
-  auto ops = [&](int kt) { return kt < nsteps ? ops_wave : 0; };
+  // vector-memory instructions every wave issues per stage (the waits count
+  // them): scale words first (a filler copy into dmy where the wave has no
+  // B-side scale row), then the A and B code chunks
+  constexpr int NSC = MX ? 2 : (BLK ? (MODE == kWgrad ? 2 : 1) : 0);
+  constexpr int OPS = NSC + AQ + BQ;
+  const uint8_t *zsrc = reinterpret_cast<const uint8_t *>(kZeroSrc) + lane * 16;
+  const uint32_t *usrc = kUnitScaleSrc + lane;
+  const float *zsrc4 = reinterpret_cast<const float *>(kZeroSrc) + lane;
   __syncthreads();  // sbtab visible
 
   v16f acc[MI][NI];
@@ -358,55 +357,48 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
   v16f part[BLK ? MI : 1][BLK ? NI : 1];  // blockwise: partial sum of the current 128-block
 
-  // issue the copies of stage kt (or zero-fill a padding stage past nsteps)
+  // copy C (0 <= C < OPS) of stage kt into the stage buffers; a stage past
+  // the contraction copies zeros (unit E8M0 scales), so the MFMAs of the
+  // padding stages of the last ring turn add nothing. No branches.
+  auto copy = [&](auto c, int kt, uint8_t *as, uint8_t *bs, float *sa, float *sb, uint32_t *ma,
+                  uint32_t *mb) {
+    constexpr int C = decltype(c)::value;
+    const bool real = kt < nsteps;
+    if constexpr (C < NSC) {
+      if constexpr (MX) {  // the E8M0 word holding this stage's 32-blocks
+        const int wofs = ((kt * EPB) >> 1) * 4;
+        if constexpr (C == 0) dma4(real ? (const void *)(mxa + wofs) : (const void *)usrc, ma + wave * 64);
+        else dma4(real && b_wave ? (const void *)(mxb + wofs) : (const void *)usrc, b_wave ? mb + wave * 64 : dmy);
+      } else {
+        if constexpr (C == 0) dma4(real ? sa_src + (kt >> 1) : zsrc4, sa + wave * 64);
+        else dma4(real && b_wave ? sb_src + (kt >> 1) : zsrc4, b_wave ? sb + wave * 64 : (float *)dmy);
+      }
+    } else if constexpr (C < NSC + AQ) {
+      constexpr int q = C - NSC;
+      dma16(real ? abase + kt * 128 + aoff[q] : zsrc, as + (wave * AQ + q) * 1024);
+    } else {
+      constexpr int q = C - NSC - AQ;
+      dma16(real ? bbase + kt * 128 + boff[q] : zsrc, bs + (wave * BQ + q) * 1024);
+    }
+  };
   auto load_stage = [&](int kt, uint8_t *as, uint8_t *bs, float *sa, float *sb, uint32_t *ma,
                         uint32_t *mb) {
-    if (kt < nsteps) {
-      if (MX) {  // the E8M0 word holding this stage's 32-blocks
-        const int wofs = ((kt * EPB) >> 1) * 4;
-        dma4(mxa + wofs, ma + wave * 64);
-        if (b_wave) dma4(mxb + wofs, mb + wave * 64);
-      }
-      if (BLK) {
-        dma4(sa_src + (kt >> 1), sa + wave * 64);
-        if (MODE == kWgrad && b_wave) dma4(sb_src + (kt >> 1), sb + wave * 64);
-      }
-      const uint8_t *ak = abase + kt * 128;
-      const uint8_t *bk = bbase + kt * 128;
-#pragma unroll
-      for (int q = 0; q < AQ; ++q) dma16(ak + aoff[q], as + (wave * AQ + q) * 1024);
-#pragma unroll
-      for (int q = 0; q < BQ; ++q) dma16(bk + boff[q], bs + (wave * BQ + q) * 1024);
-    } else {
-      const uint4 z = make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int u = 0; u < GBM * GBK / 16 / NT; ++u) *reinterpret_cast<uint4 *>(as + (u * NT + t) * 16) = z;
-#pragma unroll
-      for (int u = 0; u < BN * GBK / 16 / NT; ++u) *reinterpret_cast<uint4 *>(bs + (u * NT + t) * 16) = z;
-      if (BLK) {
-        if (t < GBM) sa[t] = 0.0f;
-        if (t < BN) sb[t] = 0.0f;
-      }
-      if (MX) {  // unit scales for the zero stage
-        if (t < GBM) ma[t] = 0x7f7f7f7fu;
-        if (t < BN) mb[t] = 0x7f7f7f7fu;
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);  // the copies go out before what follows
+    [&]<int... Cs>(std::integer_sequence<int, Cs...>) {
+      (copy(std::integral_constant<int, Cs>{}, kt, as, bs, sa, sb, ma, mb), ...);
+    }(std::make_integer_sequence<int, OPS>{});
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  // wait until at most `pending` of this wave's copies are in flight (copies
-  // complete in issue order), then synchronize the workgroup. `lds`: also
-  // wait for this wave's LDS writes (the zero fill of a padding stage that
-  // other waves read after the barrier); outstanding fragment reads need no
-  // wait here, the MFMAs that use them wait for them.
-  auto sync_stage = [&](int pending, bool lds) {
+  // wait until at most PEND stages of this wave's copies are in flight
+  // (copies complete in issue order), then synchronize the workgroup
+  auto sync_stage = [&](auto pend) {
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm_n(pending);
-    if (lds) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    wait_vm<decltype(pend)::value * OPS>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
+  using W1 = std::integral_constant<int, 1>;
+  using W2 = std::integral_constant<int, 2>;
 
   // an empty asm use of every accumulator: keeps the stage's MFMAs issued
   // before the next wait (and the accumulators in AGPRs)
@@ -426,6 +418,27 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
 #endif
   };
 
+  // fragment unit U of a stage: A sub-tiles 0..MI-1, B sub-tiles MI..MI+NI-1,
+  // then (MX) the scale words
+  auto read_unit = [&](auto u, Frags<MI, NI> &f, const uint8_t *as, const uint8_t *bs, const uint32_t *ma,
+                       const uint32_t *mb) {
+    constexpr int U = decltype(u)::value;
+    if constexpr (U < MI) {
+      f.a[U] = frag(as, wi * 128 + U * 32 + l32, h);
+    } else if constexpr (U < MI + NI) {
+      f.b[U - MI] = frag(bs, wj * WN + (U - MI) * 32 + l32, h);
+    } else if constexpr (MX) {
+      const uint4 wa = *reinterpret_cast<const uint4 *>(&ma[(wi * 32 + l32) * 4]);
+      const uint4 wb = *reinterpret_cast<const uint4 *>(&mb[(wj * 32 + l32) * 4]);
+      const uint32_t wav[4] = {wa.x, wa.y, wa.z, wa.w}, wbv[4] = {wb.x, wb.y, wb.z, wb.w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        f.sa[m] = (int)(wav[m] >> (8 * h));
+        f.sb[m] = (int)(wbv[m] >> (8 * h));
+      }
+    }
+  };
+  constexpr int NUNIT = MI + NI + (MX ? 1 : 0);
   auto read_frags = [&](Frags<MI, NI> &f, const uint8_t *as, const uint8_t *bs, const uint32_t *ma,
                         const uint32_t *mb) {
 #pragma unroll
@@ -519,14 +532,6 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
   constexpr int NPRE = BLK ? 0 : 2;
   using C0 = std::integral_constant<int, 0>;
   using CPRE = std::integral_constant<int, NPRE>;
-  using CALL = std::integral_constant<int, MI * NI>;
-
-  // instruction order of the rest of a prefetching stage: the next stage's
-  // fragment reads spread evenly over its MFMAs (then the MX word reads)
-  auto order_pref = [&]() {
-    order_groups<0, MPT * (MI * NI - NPRE), 2 * (MI + NI)>();
-    if (MX) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-  };
 
   // ---- main loop: a ring of four stage buffers; stage kt lives in buffer
   // kt % 4 and its copies are issued three stages ahead. The stage count is
@@ -539,16 +544,32 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
     // stage k: wait for stage k+1's copies, barrier, issue stage k+3's
     // copies, then stage k's MFMAs (fragments read during stage k-1)
     // interleaved with the reads of stage k+1's fragments
+    // stage k: its first NPRE MFMAs (fragments read during stage k-1), wait
+    // for stage k+1's copies, barrier, then slot by slot: one MFMA, one copy
+    // of stage k+3, and the fragment reads of stage k+1 spread over the slots
     auto step = [&](int k, Frags<MI, NI> &fc, Frags<MI, NI> &fn, const float *sac, const float *sbc,
                     const uint8_t *an, const uint8_t *bn, const uint32_t *man, const uint32_t *mbn,
                     uint8_t *al, uint8_t *bl, float *sal, float *sbl, uint32_t *mal, uint32_t *mbl,
                     auto ph) {
       mfma_range(fc, ph, C0{}, CPRE{});
-      sync_stage(ops(k + 2), k + 1 >= nsteps);
-      if (k + 3 < vsteps) load_stage(k + 3, al, bl, sal, sbl, mal, mbl);
-      mfma_range(fc, ph, CPRE{}, CALL{});
-      read_frags(fn, an, bn, man, mbn);
-      order_pref();
+      sync_stage(W1{});
+      constexpr int NS = MI * NI - NPRE;   // slots
+      [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
+        ([&] {
+          constexpr int S = Ss;
+          mfma_range(fc, ph, std::integral_constant<int, NPRE + S>{}, std::integral_constant<int, NPRE + S + 1>{});
+          if constexpr (S < OPS) copy(std::integral_constant<int, S>{}, k + 3, al, bl, sal, sbl, mal, mbl);
+          constexpr int u0 = (NUNIT * S) / NS, u1 = (NUNIT * (S + 1)) / NS;
+          if constexpr (u1 > u0) read_unit(std::integral_constant<int, u0>{}, fn, an, bn, man, mbn);
+          if constexpr (u1 > u0 + 1) read_unit(std::integral_constant<int, u0 + 1>{}, fn, an, bn, man, mbn);
+          __builtin_amdgcn_sched_barrier(0);
+        }(), ...);
+      }(std::make_integer_sequence<int, NS>{});
+      if constexpr (OPS > NS) {
+        [&]<int... Cs>(std::integer_sequence<int, Cs...>) {
+          (copy(std::integral_constant<int, NS + Cs>{}, k + 3, al, bl, sal, sbl, mal, mbl), ...);
+        }(std::make_integer_sequence<int, OPS - NS>{});
+      }
       if (BLK && decltype(ph)::value == 1) {
         // a v_mfma_scale 32x32x64 result read back by the VALU needs more
         // independent cycles than the compiler left in one schedule: pad
@@ -565,7 +586,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
       load_stage(0, As0, Bs0, sA0, sB0, mA0, mB0);
       load_stage(1, As1, Bs1, sA1, sB1, mA1, mB1);
       load_stage(2, As2, Bs2, sA2, sB2, mA2, mB2);
-      sync_stage(ops(1) + ops(2), true);
+      sync_stage(W2{});
       read_frags(F0, As0, Bs0, mA0, mB0);
     }
     for (int kt = 0; kt < vsteps; kt += 4) {
@@ -576,6 +597,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
     }
   }
   __builtin_amdgcn_sched_barrier(0);
+  wait_vm<0>();     // the copies of the stages past the contraction have landed
   __syncthreads();  // every wave is done with the stage buffers
 
   // ---- epilogue: each wave stages 16-row half slabs through its own LDS
