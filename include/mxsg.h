@@ -65,6 +65,15 @@
  *    [P_g + m_g, P_{g+1}) hold code 0x00 (zero fill of partial blocks).
  *    ld must be a multiple of 128 and >= mxsg_padded_capacity(M, E).
  *    Columns >= P_E are not written.
+ *  - MX (E8M0) scale matrices are word-major: a matrix of R rows of B
+ *    blocks (B = 4 * words, one 32-element block per byte) stores the
+ *    scale of (row r, block b) at byte offset
+ *      ((b / 4) * R + r) * 4 + (b % 4),
+ *    i.e. word w (the four blocks of contraction elements [128w, 128w+128))
+ *    of every row, rows consecutive, then word w + 1. The shapes below are
+ *    logical [R, B]; each expert's matrix of a weight is its own [R, B]
+ *    in this order. The grouped GEMM reads one word for a run of rows as
+ *    contiguous memory.
  */
 #ifndef MXSG_H
 #define MXSG_H
@@ -122,9 +131,9 @@ int64_t mxsg_padded_capacity(int64_t M, int32_t E);
  * e2m1 only with MX) and returns their status. With b = 1 code byte per
  * element (e4m3, e5m2) or 1/2 (e2m1):
  *   bytes[0] row_codes      (M + (M & 1)) * C * b
- *   bytes[1] row_scales     BLOCKWISE 4 * M * C/128, MX M * C/32, else 4
+ *   bytes[1] row_scales     BLOCKWISE 4 * M * C/128, MX M * C/32 (word-major), else 4
  *   bytes[2] col_codes      C * ld * b               (0 when E = 0)
- *   bytes[3] col_scales     BLOCKWISE 4 * C * ld/128, MX C * ld/32, else 4
+ *   bytes[3] col_scales     BLOCKWISE 4 * C * ld/128, MX C * ld/32 (word-major), else 4
  *   bytes[4] padded_starts  4 * (E + 1)              (0 when E = 0)
  * Units and shape rule: the Transformer Engine "FP8BlockQuantizer not
  * work" issue, design note (1x128 units; the blocked dimension divides by
@@ -161,7 +170,8 @@ mxsg_status mxsg_quantize_weight_sizes(int32_t E, int64_t K, int64_t N, int32_t 
  *  recipe BLOCKWISE: row_scales fp32 [M, C/128] (1x128 units along C);
  *    col_scales fp32 [C, ld/128] (128x1 units along the padded tokens,
  *    restarting at each group). amax, dl_* unused.
- *  recipe MX: row_scales uint8 [M, C/32]; col_scales uint8 [C, ld/32]; a
+ *  recipe MX: row_scales uint8 [M, C/32]; col_scales uint8 [C, ld/32]
+ *    (both word-major, R = M resp. C); a
  *    32-block made only of padding gets code 127. fmt e2m1 (MXFP4): the
  *    same scales; code rows hold C/2 resp. ld/2 bytes.
  *
@@ -214,7 +224,8 @@ mxsg_status mxsg_quantize_act_gather(const void *x, int64_t T, const int32_t *ro
  *    scales fp32 [E, K/128, N/128] (same array content for both layouts).
  *  MX: two code sets. k-major: blocks of 32 along K, kmajor_scales uint8
  *    [E, N, K/32]; n-major: blocks of 32 along N, nmajor_scales uint8
- *    [E, K, N/32]. fmt e2m1: code rows of K/2 resp. N/2 bytes, same scales.
+ *    [E, K, N/32] (each expert's matrix word-major, R = N resp. K). fmt
+ *    e2m1: code rows of K/2 resp. N/2 bytes, same scales.
  *  Scale pointers belonging to a non-NULL code pointer are required.
  */
 mxsg_status mxsg_quantize_weight(const void *w, int32_t E, int64_t K, int64_t N, int32_t recipe,
@@ -266,7 +277,9 @@ mxsg_status mxsg_delayed_update(float *history, int32_t *pos, float *amax, float
  *     are scaled by sA * sB and accumulated in fp32.
  *   MX: uint8 E8M0 scales with one byte per 32 contraction elements:
  *     FWD a [M, K/32], b [E, N, K/32]; DGRAD a [M, N/32], b [E, K, N/32];
- *     WGRAD a [K, lda/32], b [N, ldb/32]; applied inside the MFMA.
+ *     WGRAD a [K, lda/32], b [N, ldb/32], all word-major (the layout
+ *     mxsg_quantize_act / mxsg_quantize_weight write); applied inside the
+ *     MFMA.
  *  fmt_a / fmt_b: element formats of A and B (e4m3 x e4m3, e5m2 x e4m3 and
  *  e4m3 x e5m2 are supported; hybrid training uses e5m2 gradients; e2m1 x
  *  e2m1 with the MX recipe is MXFP4).

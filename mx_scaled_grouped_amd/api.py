@@ -85,6 +85,26 @@ def pack_codes(t: torch.Tensor) -> torch.Tensor:
     return t.reshape(*lead, r // 2, 2, L // 64, 64).transpose(-3, -2).reshape(*lead, r, L).contiguous()
 
 
+def unpack_mx_scales(t: torch.Tensor) -> torch.Tensor:
+    """Row-major copy [..., R, 4W] of word-major E8M0 scales [..., W, R, 4].
+
+    The library stores MX scale matrices word-major: word w (the four
+    32-blocks of contraction elements [128w, 128w + 128)) of every row,
+    rows consecutive, then word w + 1 (mxsg.h, Layouts)."""
+    *lead, w, r, four = t.shape
+    if four != 4:
+        raise ValueError(f"word-major scales need a last dimension of 4, got {tuple(t.shape)}")
+    return t.transpose(-3, -2).reshape(*lead, r, 4 * w)
+
+
+def pack_mx_scales(t: torch.Tensor) -> torch.Tensor:
+    """Word-major copy [..., B/4, R, 4] of row-major E8M0 scales [..., R, B]."""
+    *lead, r, b = t.shape
+    if b % 4:
+        raise ValueError(f"block count {b} is not a multiple of 4")
+    return t.reshape(*lead, r, b // 4, 4).transpose(-3, -2).contiguous()
+
+
 def _scale_blocks(recipe: str) -> int:
     return {"block": 128, "mx": 32}.get(recipe, 0)
 
@@ -202,10 +222,14 @@ def quantize_act(x: torch.Tensor, recipe: str, fmt, group_ends: Optional[torch.T
         if rowwise:
             q.row_codes = _buffer(nb[0], torch.uint8, C // epb, dev)
             q.row_scales = _buffer(nb[1], sdt, C // blk if blk else 0, dev)
+            if recipe == "mx":  # word-major [C/128, M, 4]
+                q.row_scales = q.row_scales.view(C // 128, M, 4)
         if colwise:
             q.ld = padded_capacity(M, E)
             q.col_codes = _buffer(nb[2], torch.uint8, q.ld // epb, dev)
             q.col_scales = _buffer(nb[3], sdt, q.ld // blk if blk else 0, dev)
+            if recipe == "mx":  # word-major [ld/128, C, 4]
+                q.col_scales = q.col_scales.view(q.ld // 128, C, 4)
             q.padded_starts = _buffer(nb[4], torch.int32, 0, dev)
         if recipe == "tw":
             q.amax = torch.empty(1, dtype=torch.float32, device=dev)
@@ -260,9 +284,9 @@ def quantize_weight(w: torch.Tensor, recipe: str, fmt, kmajor: bool = True, nmaj
             ks = ns = _buffer(nb[1], torch.float32, 0, dev)
         elif recipe == "block":
             ks = ns = _buffer(nb[1], torch.float32, N // 128, dev).view(E, K // 128, N // 128)
-        else:
-            ks = _buffer(nb[1], torch.uint8, K // 32, dev).view(E, N, K // 32)
-            ns = _buffer(nb[3], torch.uint8, N // 32, dev).view(E, K, N // 32)
+        else:  # word-major per expert: [E, K/128, N, 4] and [E, N/128, K, 4]
+            ks = _buffer(nb[1], torch.uint8, 0, dev).view(E, K // 128, N, 4)
+            ns = _buffer(nb[3], torch.uint8, 0, dev).view(E, N // 128, K, 4)
         if kmajor:
             q.kmajor_codes = _buffer(nb[0], torch.uint8, K // epb, dev).view(E, N, K // epb)
             q.kmajor_scales = ks

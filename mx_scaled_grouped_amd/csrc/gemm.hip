@@ -322,21 +322,32 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
     if (MODE == kWgrad && b_wave)
       sb_src = reinterpret_cast<const float *>(a.b_scales) + brow(r) * (sb_row / SBLK) + l0 / SBLK;
     if (MODE != kWgrad) {
+      // zeros for the padding blocks of the last ring turn: their partials
+      // are zero, and a zero table entry keeps uninitialized LDS (possibly
+      // an Inf or NaN pattern) out of the product
       const int64_t jb = j0 / SBLK;
-      for (int lbk = t; lbk < nsteps / 2 && lbk < SB_TAB; lbk += NT)
-        sbtab[lbk] = reinterpret_cast<const float *>(a.b_scales)[(int64_t)g * a.bs_gstride + lbk * a.sb_l + jb * a.sb_j];
+      for (int lbk = t; lbk < vsteps / 2 && lbk < SB_TAB; lbk += NT)
+        sbtab[lbk] = lbk < nsteps / 2 ? reinterpret_cast<const float *>(
+                                            a.b_scales)[(int64_t)g * a.bs_gstride + lbk * a.sb_l + jb * a.sb_j]
+                                      : 0.0f;
     }
   }
   // MX scale words: lane L of wave w copies word slot d = 64w + L (see the
-  // slot layout above); the word of stage kt holds 32-blocks 4(kt/2) .. +3
+  // slot layout above). The scale matrices are word-major (word w of all
+  // rows, then word w + 1), so the words of one stage for a run of rows are
+  // contiguous: a wave's copy reads four 64-byte runs. The word of stage kt
+  // holds the 32-blocks 4w .. 4w+3 with w = l0/128 + (kt * EPB) / 2.
   const uint8_t *mxa = nullptr, *mxb = nullptr;
+  int64_t mxa_word = 0, mxb_word = 0;  // bytes from one word of a matrix to the next
   if (MX) {
     const int d = wave * 64 + lane;
     const int r = (d >> 7) * 128 + (d & 3) * 32 + ((d >> 2) & 31);
-    mxa = reinterpret_cast<const uint8_t *>(a.a_scales) + arow(r) * (sa_row / 32) + l0 / 32;
+    mxa_word = (MODE == kWgrad ? a.I : a.M) * 4;
+    mxb_word = a.J * 4;
+    mxa = reinterpret_cast<const uint8_t *>(a.a_scales) + (l0 / 128) * mxa_word + arow(r) * 4;
     if (b_wave)
       mxb = reinterpret_cast<const uint8_t *>(a.b_scales) + (MODE == kWgrad ? 0 : (int64_t)g * a.bs_gstride) +
-            brow(r) * (sb_row / 32) + l0 / 32;
+            (l0 / 128) * mxb_word + brow(r) * 4;
   }
   // vector-memory instructions every wave issues per stage (the waits count
   // them): scale words first (a filler copy into dmy where the wave has no
@@ -366,9 +377,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
     const bool real = kt < nsteps;
     if constexpr (C < NSC) {
       if constexpr (MX) {  // the E8M0 word holding this stage's 32-blocks
-        const int wofs = ((kt * EPB) >> 1) * 4;
-        if constexpr (C == 0) dma4(real ? (const void *)(mxa + wofs) : (const void *)usrc, ma + wave * 64);
-        else dma4(real && b_wave ? (const void *)(mxb + wofs) : (const void *)usrc, b_wave ? mb + wave * 64 : dmy);
+        const int64_t w = (kt * EPB) >> 1;
+        if constexpr (C == 0)
+          dma4(real ? (const void *)(mxa + w * mxa_word) : (const void *)usrc, ma + wave * 64);
+        else
+          dma4(real && b_wave ? (const void *)(mxb + w * mxb_word) : (const void *)usrc,
+               b_wave ? mb + wave * 64 : dmy);
       } else {
         if constexpr (C == 0) dma4(real ? sa_src + (kt >> 1) : zsrc4, sa + wave * 64);
         else dma4(real && b_wave ? sb_src + (kt >> 1) : zsrc4, b_wave ? sb + wave * 64 : (float *)dmy);

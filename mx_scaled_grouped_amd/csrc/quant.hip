@@ -297,9 +297,10 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
         m = umax(m, (uint32_t)__shfl_xor((int)m, 2, 64));
         const int k = mx_exponent<FMT>(bits_to_amax(m));
         inv = exp2_neg(k);
+        // word-major E8M0 layout: word c0/128 of every row, then the next word
         if ((cq & 3) == 0 && r < nvalid)
-          reinterpret_cast<uint8_t *>(a.row_scales)[b * a.rs_bstride + (src0 + r) * (a.C / 32) +
-                                                    (c0 / 32) + (cq >> 2)] = (uint8_t)(k + 127);
+          reinterpret_cast<uint8_t *>(a.row_scales)[b * a.rs_bstride + ((c0 / QT) * a.rows + src0 + r) * 4 +
+                                                    (cq >> 2)] = (uint8_t)(k + 127);
       }
       if (r < nvalid) {
         if constexpr (FP4) {
@@ -345,9 +346,10 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
       inv0 = exp2_neg(k0);
       inv1 = exp2_neg(k1);
       uint8_t *cs = reinterpret_cast<uint8_t *>(a.col_scales) + b * a.cs_bstride;
-      const int64_t ldb = a.ld / 32;
-      cs[(c0 + 2 * fp) * ldb + p0 / 32 + q] = (uint8_t)(k0 + 127);
-      cs[(c0 + 2 * fp + 1) * ldb + p0 / 32 + q] = (uint8_t)(k1 + 127);
+      // word-major [C, ld/32]: word p0/128 of feature row c, byte q
+      const int64_t wrow = (p0 / QT) * a.C + c0 + 2 * fp;
+      cs[wrow * 4 + q] = (uint8_t)(k0 + 127);
+      cs[(wrow + 1) * 4 + q] = (uint8_t)(k1 + 127);
     } else {  // 128x1 units: the whole tile column, reduce the 4 quarters
       colmax[q][2 * fp] = m0;
       colmax[q][2 * fp + 1] = m1;

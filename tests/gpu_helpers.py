@@ -30,6 +30,25 @@ def host(t) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
+def scales_host(t, recipe) -> np.ndarray:
+    """Host copy of device scales in their logical [..., rows, blocks]
+    layout: MX (E8M0) scales are stored word-major and unpacked here."""
+    if recipe == "mx":
+        from mx_scaled_grouped_amd import api
+        return host(api.unpack_mx_scales(t))
+    return host(t)
+
+
+def scales_dev(a: np.ndarray, recipe):
+    """Device copy of host scales [..., rows, blocks] in the library's
+    layout (word-major for MX)."""
+    t = to_dev(a)
+    if recipe == "mx":
+        from mx_scaled_grouped_amd import api
+        return api.pack_mx_scales(t)
+    return t
+
+
 def codes_host(t, rows=None) -> np.ndarray:
     """Row-major host copy of pair-interleaved device codes (the first `rows` rows)."""
     from mx_scaled_grouped_amd import api

@@ -165,8 +165,16 @@ def _w_scale(st, which, w_bits, fmt):
     return r, None
 
 
+def _sc(t, rec):
+    """Host scales in their logical layout (MX scales are stored word-major)."""
+    if rec == "mx":
+        from mx_scaled_grouped_amd import api
+        return _np(api.unpack_mx_scales(t))
+    return _np(t)
+
+
 def _check_scales_rows(gpu_scales, ora_scales, rec, sel, what):
-    g = _np(gpu_scales)
+    g = _sc(gpu_scales, rec)
     if rec == "dl":
         assert_bits_equal(g.reshape(-1)[:1], np.asarray(ora_scales, np.float32).reshape(-1)[:1], what)
     else:
@@ -210,7 +218,7 @@ def check_forward(name, which):
     qw = step.q["w_" + which]
     assert_bits_equal(_codes(_take(_unpack(qw.kmajor_codes), (1, ncols)), fw), rw["kmajor_codes"],
                       "weight k-major codes")
-    ks = _np(qw.kmajor_scales)
+    ks = _sc(qw.kmajor_scales, wrec)
     if wrec == "dl":
         assert_bits_equal(ks, rw["kmajor_scales"], "weight scales")
     elif wrec == "block":
@@ -244,7 +252,7 @@ def check_dgrad(name, which):
     qw = step.q["w_" + which]
     assert_bits_equal(_codes(_take(_unpack(qw.nmajor_codes), (1, kcols)), fw), rw["nmajor_codes"],
                       "weight n-major codes")
-    ns = _np(qw.nmajor_scales)
+    ns = _sc(qw.nmajor_scales, wrec)
     if wrec == "block":
         assert_bits_equal(ns[:, kblk, :], rw["nmajor_scales"], "weight tile scales")
     elif wrec == "mx":
@@ -277,7 +285,7 @@ def check_wgrad(name, which):
         assert np.array_equal(_np(q.padded_starts).astype(np.int64), P), tag + " padded starts"
         cc = _codes(_take(_unpack(q.col_codes), (0, cols)), fmt)
         assert_bits_equal(cc[:, :P[-1]], rc["col_codes"], tag + " column codes")
-        cs = _np(q.col_scales)
+        cs = _sc(q.col_scales, rec)
         if rec == "dl":
             assert_bits_equal(cs[:1], rc["col_scales"], tag + " column scale")
         else:

@@ -13,7 +13,7 @@ its parity does not depend on theirs:
 import numpy as np
 import pytest
 
-from tests.gpu_helpers import (torch, FMT_OBJ, gpu_available, to_dev_u16, to_dev, host, bf16_host_f64,
+from tests.gpu_helpers import (torch, FMT_OBJ, gpu_available, to_dev_u16, to_dev, host, bf16_host_f64, scales_dev,
                                assert_bits_equal)
 from oracle import quant as OQ
 from oracle import formats as OF
@@ -134,8 +134,8 @@ def run_case(c, out=None, accumulate=False):
     if c.fa == 2:   # two e2m1 codes per byte; row lengths in code bytes
         a, b, lda, ldb = OF.pack_nibbles(a), OF.pack_nibbles(b), lda // 2, ldb // 2
     return api.grouped_mm(c.mode, c.recipe, c.fa, c.fb, c.E, c.M, c.K, c.N, to_dev(c.ge),
-                          api.pack_codes(to_dev(a)), to_dev(c.sa), lda, api.pack_codes(to_dev(b)),
-                          to_dev(c.sb), ldb,
+                          api.pack_codes(to_dev(a)), scales_dev(c.sa, c.recipe), lda,
+                          api.pack_codes(to_dev(b)), scales_dev(c.sb, c.recipe), ldb,
                           padded_starts=None if c.padded is None else to_dev(c.padded), out=out,
                           accumulate=accumulate)
 

@@ -5,7 +5,7 @@ sizes around the block lengths."""
 import numpy as np
 import pytest
 
-from tests.gpu_helpers import (torch, EDGE_SIZES, FMT_OBJ, gpu_available, to_dev_u16, to_dev, host, codes_host,
+from tests.gpu_helpers import (torch, EDGE_SIZES, FMT_OBJ, gpu_available, to_dev_u16, to_dev, host, codes_host, scales_host,
                                codes_of, assert_bits_equal)
 from oracle import quant as OQ
 from oracle import formats as OF
@@ -83,13 +83,13 @@ RECIPE_FMTS = [("tw", 0), ("tw", 1), ("block", 0), ("block", 1), ("mx", 0), ("mx
 def _compare_act(q, ref, recipe, M, C, rowwise, colwise):
     if rowwise:
         assert_bits_equal(codes_of(q.row_codes, q.fmt, M), ref["row_codes"], "row codes")
-        assert_bits_equal(host(q.row_scales), ref["row_scales"], "row scales")
+        assert_bits_equal(scales_host(q.row_scales, recipe), ref["row_scales"], "row scales")
     if colwise:
         P = host(q.padded_starts).astype(np.int64)
         assert np.array_equal(P, ref["padded_starts"]), (P, ref["padded_starts"])
         Rp = int(P[-1])
         assert_bits_equal(codes_of(q.col_codes, q.fmt)[:, :Rp], ref["col_codes"], "col codes")
-        cs = host(q.col_scales)
+        cs = scales_host(q.col_scales, recipe)
         if recipe in ("tw", "dl"):
             assert_bits_equal(cs, ref["col_scales"], "col scales")
         else:
@@ -171,7 +171,8 @@ def test_act_gather(recipe, fmt):
     assert_bits_equal(codes_of(q.col_codes, fmt)[:, :Rp], codes_of(p.col_codes, fmt)[:, :Rp],
                       "gathered column codes")
     if blk:
-        assert torch.equal(q.col_scales[:, :Rp // blk], p.col_scales[:, :Rp // blk])
+        assert_bits_equal(scales_host(q.col_scales, recipe)[:, :Rp // blk],
+                          scales_host(p.col_scales, recipe)[:, :Rp // blk], "gathered column scales")
     else:
         assert torch.equal(q.col_scales, p.col_scales)
 
@@ -278,8 +279,8 @@ def test_weight_layouts(recipe, fmt):
     q = api.quantize_weight(to_dev_u16(w), recipe, fmt)
     assert_bits_equal(codes_of(q.kmajor_codes, fmt), ref["kmajor_codes"], "k-major codes")
     assert_bits_equal(codes_of(q.nmajor_codes, fmt), ref["nmajor_codes"], "n-major codes")
-    assert_bits_equal(host(q.kmajor_scales), ref["kmajor_scales"], "k-major scales")
-    assert_bits_equal(host(q.nmajor_scales), ref["nmajor_scales"], "n-major scales")
+    assert_bits_equal(scales_host(q.kmajor_scales, recipe), ref["kmajor_scales"], "k-major scales")
+    assert_bits_equal(scales_host(q.nmajor_scales, recipe), ref["nmajor_scales"], "n-major scales")
     if recipe == "tw":
         assert_bits_equal(host(q.amax), ref["amax"], "amax")
 
