@@ -42,3 +42,40 @@ def test_shape_errors():
         api.unpack_codes(torch.zeros(3, 64, dtype=torch.uint8))
     with pytest.raises(ValueError):
         api.pack_codes(torch.zeros(2, 96, dtype=torch.uint8))
+
+
+# ---------------------------------------------------------------------------
+# word-major MX (E8M0) scales
+
+def _mx_offset(r, b, R):
+    # word b//4 of every row, rows consecutive; byte b%4 of the row's word
+    return ((b // 4) * R + r) * 4 + (b % 4)
+
+
+@pytest.mark.parametrize("R,B", [(1, 4), (5, 8), (130, 12), (64, 128)])
+def test_mx_pack_matches_offset_formula(R, B):
+    rng = np.random.default_rng(R * 7 + B)
+    x = rng.integers(0, 256, size=(R, B), dtype=np.uint8)
+    p = api.pack_mx_scales(torch.from_numpy(x))
+    assert tuple(p.shape) == (B // 4, R, 4)
+    flat = p.numpy().reshape(-1)
+    rr, bb = np.meshgrid(np.arange(R), np.arange(B), indexing="ij")
+    assert np.array_equal(flat[_mx_offset(rr, bb, R)], x)
+
+
+def test_mx_unpack_inverts_pack_with_expert_dim():
+    rng = np.random.default_rng(11)
+    x = torch.from_numpy(rng.integers(0, 256, size=(3, 9, 16), dtype=np.uint8))
+    p = api.pack_mx_scales(x)
+    assert tuple(p.shape) == (3, 4, 9, 4)
+    assert torch.equal(api.unpack_mx_scales(p), x)
+    # unpack is a permutation: pack(unpack(y)) == y
+    y = torch.from_numpy(rng.integers(0, 256, size=(2, 6, 4), dtype=np.uint8))
+    assert torch.equal(api.pack_mx_scales(api.unpack_mx_scales(y)), y)
+
+
+def test_mx_shape_errors():
+    with pytest.raises(ValueError):
+        api.pack_mx_scales(torch.zeros(3, 6, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        api.unpack_mx_scales(torch.zeros(2, 3, 2, dtype=torch.uint8))
