@@ -23,6 +23,7 @@
 // left idle while copies go out. Every stage issues the same number of
 // copies (the padding stages of the last ring turn copy from a static zero
 // source), so each wait count is a constant and the loop has no branch.
+// The grid is persistent (one workgroup per CU looping over tiles).
 // Tiles never straddle expert groups (row tiles start at a group's first
 // row pair; rows of a neighbouring group in the tile are computed and not
 // stored); a workgroup finds its group from the device-resident offsets
@@ -64,6 +65,7 @@ struct GemmArgs {
   int E;
   int slots;             // FWD / DGRAD: i-tile slots launched; WGRAD: i-tiles
   int jtiles;
+  int nblocks;           // tiles (slots x jtiles, or E x slots x jtiles)
   int accumulate;
 };
 
@@ -244,7 +246,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
 
   // ---- tile coordinates: rows [i0, i0 + GBM) of the tile (i0 even), valid
   // output rows [ilo, ihi); columns [j0, j0 + BN); contraction from l0
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  // persistent: the grid is one workgroup per CU (a multiple of 8, so tile
+  // vb runs on XCD vb % 8 as it would in a one-tile-per-workgroup grid), each
+  // walking the tiles vb = blockIdx.x, + gridDim.x, ...; the next tile's
+  // copies then start as soon as this tile's stores are issued
+  for (int vb = blockIdx.x; vb < a.nblocks; vb += gridDim.x) {
+  const int lid = xcd_remap(vb, a.nblocks);
   int g = 0;
   int64_t i0 = 0, ilo = 0, ihi = 0, j0 = 0, l0 = 0;
   int nsteps = 0;
@@ -267,7 +274,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
     int slot, jt;
     raster(lid, a.slots, a.jtiles, slot, jt);
     j0 = (int64_t)jt * BN;
-    if (!locate_row_tile(a, slot, g, i0, ilo, ihi)) return;
+    if (!locate_row_tile(a, slot, g, i0, ilo, ihi)) continue;
     l0 = 0;
     nsteps = (int)(a.L / GBK);
   }
@@ -611,6 +618,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
     }
   }
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (!BLK) {
+    // the epilogue's first LDS writes take the last MFMA's accumulators
+    // straight from AGPRs: keep >= 40 wait states between them (blockwise
+    // pads every ring turn)
+    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" ::: "memory");
+  }
   wait_vm<0>();     // the copies of the stages past the contraction have landed
   __syncthreads();  // every wave is done with the stage buffers
 
@@ -623,7 +636,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
     const float sb = reinterpret_cast<const float *>(a.b_scales)[MODE == kWgrad ? 0 : g];
     scale = sa * sb;
   }
-  if (MODE == kWgrad && a.accumulate && nsteps == 0) return;  // empty group: dW_g unchanged
+  if (MODE == kWgrad && a.accumulate && nsteps == 0) continue;  // empty group: dW_g unchanged
   constexpr int STR = WN + 8;          // LDS row stride in floats
   constexpr int CPR = WN / 8;          // 8-float chunks per row
   constexpr int CPL = 16 * CPR / 64;   // chunks per lane per half slab
@@ -674,6 +687,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
       __builtin_amdgcn_wave_barrier();
     }
   }
+  __syncthreads();  // the staging buffers are free before the next tile's copies land
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -695,7 +710,17 @@ static hipError_t launch_cfg(const GemmArgs &a0, hipStream_t st) {
   }
   if (nblocks == 0) return hipSuccess;
   if (nblocks > 0x7fffffff) return hipErrorInvalidValue;
-  grouped_gemm_kernel<MODE, RECIPE, FA, FB, BN><<<(unsigned)nblocks, 256, 0, st>>>(a);
+  a.nblocks = (int)nblocks;
+  // one workgroup per CU (the LDS ring allows one), rounded down to whole
+  // rounds of the 8 XCDs; each loops over its share of the tiles
+  int64_t grid = nblocks;
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ncu >= 8) {
+    const int64_t persistent = (int64_t)(ncu / 8) * 8;
+    grid = nblocks < persistent ? nblocks : persistent;
+  }
+  grouped_gemm_kernel<MODE, RECIPE, FA, FB, BN><<<(unsigned)grid, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
