@@ -38,7 +38,7 @@ def _codes(t, fmt):
     c = _np(t)
     return OF.unpack_nibbles(c) if fmt is OF.E2M1 else c
 TOL = 1e-3
-WORKLOADS = ["mixtral-tw", "mixtral-dl", "deepseek-block", "llama4-mx"]
+WORKLOADS = ["mixtral-tw", "mixtral-dl", "deepseek-block", "llama4-mx", "llama4-mxfp4"]
 
 _cache = {}
 
