@@ -92,6 +92,20 @@ typedef int32_t mxsg_status;
 #define MXSG_UNSUPPORTED 3      /* a recipe / format / mode combination not built */
 #define MXSG_HIP_ERROR 4        /* a HIP launch failed */
 
+/*
+ * Device status word bits. The quantize and grouped-GEMM calls take an
+ * optional `status_word` (device int32, NULL = no checks); the kernels OR
+ * these bits into it when they meet a violation that only the device can
+ * see. The library never clears the word (the caller zeroes it and reads it
+ * whenever it likes, e.g. once per step). A violation never causes an
+ * out-of-bounds access: offsets are clamped, non-finite inputs give
+ * non-finite scales.
+ */
+#define MXSG_STATUS_ENDS_DECREASING 1 /* group_ends[g] < group_ends[g-1] for some g (group_ends[-1] = 0) */
+#define MXSG_STATUS_ENDS_RANGE 2      /* some group end outside [0, M] */
+#define MXSG_STATUS_ENDS_TOTAL 4      /* group_ends[E-1] != M (rows not covered exactly) */
+#define MXSG_STATUS_NONFINITE 8       /* an amax reduction met a NaN or Inf input element */
+
 /* recipes */
 #define MXSG_RECIPE_TENSORWISE 0 /* one unit per 2-D tensor (per expert for weights), dynamic amax */
 #define MXSG_RECIPE_DELAYED 1    /* as tensorwise, scale taken from a delayed-scaling state */
@@ -181,12 +195,15 @@ mxsg_status mxsg_quantize_weight_sizes(int32_t E, int64_t K, int64_t N, int32_t 
  *    When given, E >= 1,
  *    group_ends and padded_starts (int32 [E+1], receives P_0..P_E) are required.
  *  At least one of row_codes / col_codes must be non-NULL.
+ *  status_word (optional, see the status bits): group_ends are checked when
+ *    given (E >= 1); every input element passes an amax reduction, which
+ *    flags NaN / Inf inputs (out of contract: their codes are undefined).
  */
 mxsg_status mxsg_quantize_act(const void *x, int64_t M, int64_t C, int32_t recipe, int32_t fmt,
                               int32_t E, const int32_t *group_ends, void *row_codes,
                               void *row_scales, void *col_codes, void *col_scales, int64_t ld,
                               int32_t *padded_starts, float *amax, const float *dl_scale,
-                              const float *dl_inv, mxsg_stream_t stream);
+                              const float *dl_inv, int32_t *status_word, mxsg_stream_t stream);
 
 /*
  * mxsg_quantize_act on routed rows gathered from a token tensor: x is
@@ -208,7 +225,7 @@ mxsg_status mxsg_quantize_act_gather(const void *x, int64_t T, const int32_t *ro
                                      const int32_t *group_ends, void *row_codes, void *row_scales,
                                      void *col_codes, void *col_scales, int64_t ld,
                                      int32_t *padded_starts, float *amax, const float *dl_scale,
-                                     const float *dl_inv, mxsg_stream_t stream);
+                                     const float *dl_inv, int32_t *status_word, mxsg_stream_t stream);
 
 /*
  * Quantize expert weights w [E, K, N] (the single contiguous grouped weight
@@ -227,11 +244,12 @@ mxsg_status mxsg_quantize_act_gather(const void *x, int64_t T, const int32_t *ro
  *    [E, K, N/32] (each expert's matrix word-major, R = N resp. K). fmt
  *    e2m1: code rows of K/2 resp. N/2 bytes, same scales.
  *  Scale pointers belonging to a non-NULL code pointer are required.
+ *  status_word (optional): NaN / Inf weights set MXSG_STATUS_NONFINITE.
  */
 mxsg_status mxsg_quantize_weight(const void *w, int32_t E, int64_t K, int64_t N, int32_t recipe,
                                  int32_t fmt, void *kmajor_codes, void *kmajor_scales,
                                  void *nmajor_codes, void *nmajor_scales, float *amax,
-                                 const float *dl_scale, const float *dl_inv,
+                                 const float *dl_scale, const float *dl_inv, int32_t *status_word,
                                  mxsg_stream_t stream);
 
 /*
@@ -296,13 +314,14 @@ mxsg_status mxsg_delayed_update(float *history, int32_t *pos, float *amax, float
  *  unchanged when accumulating).
  *  Limits: lda, ldb < 2^23 (BAD_SHAPE); blockwise FWD / DGRAD contraction
  *  (K resp. N) <= 65536 (UNSUPPORTED).
+ *  status_word (optional): group_ends are checked (status bits ENDS_*).
  */
 mxsg_status mxsg_grouped_mm(int32_t mode, int32_t recipe, int32_t fmt_a, int32_t fmt_b, int32_t E,
                             int64_t M, int64_t K, int64_t N, const int32_t *group_ends,
                             const int32_t *padded_starts, const void *a_codes,
                             const void *a_scales, int64_t lda, const void *b_codes,
                             const void *b_scales, int64_t ldb, void *out, int32_t accumulate,
-                            mxsg_stream_t stream);
+                            int32_t *status_word, mxsg_stream_t stream);
 
 /*
  * Validation of a mxsg_grouped_mm call without its pointers: the mode,

@@ -30,14 +30,14 @@ SIGNATURES = {
     "mxsg_grouped_mm_check": (_i32, [_i32, _i32, _i32, _i32, _i32, _i64, _i64, _i64, _i64, _i64,
                                      _i32]),
     "mxsg_quantize_act": (_i32, [_c_p, _i64, _i64, _i32, _i32, _i32, _c_p, _c_p, _c_p, _c_p, _c_p,
-                                 _i64, _c_p, _c_p, _c_p, _c_p, _c_p]),
+                                 _i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "mxsg_quantize_act_gather": (_i32, [_c_p, _i64, _c_p, _i64, _i64, _i32, _i32, _i32, _c_p, _c_p,
-                                        _c_p, _c_p, _c_p, _i64, _c_p, _c_p, _c_p, _c_p, _c_p]),
+                                        _c_p, _c_p, _c_p, _i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "mxsg_quantize_weight": (_i32, [_c_p, _i32, _i64, _i64, _i32, _i32, _c_p, _c_p, _c_p, _c_p,
-                                    _c_p, _c_p, _c_p, _c_p]),
+                                    _c_p, _c_p, _c_p, _c_p, _c_p]),
     "mxsg_delayed_update": (_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _i32, _i32, _i32, _c_p]),
     "mxsg_grouped_mm": (_i32, [_i32, _i32, _i32, _i32, _i32, _i64, _i64, _i64, _c_p, _c_p, _c_p,
-                               _c_p, _i64, _c_p, _c_p, _i64, _c_p, _i32, _c_p]),
+                               _c_p, _i64, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p]),
     "mxsg_cast_sweep": (_i32, [_u32, _i64, _i32, _c_p, _c_p]),
     "mxsg_stream_copy": (_i32, [_c_p, _c_p, _i64, _c_p]),
 }

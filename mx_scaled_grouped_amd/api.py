@@ -105,6 +105,16 @@ def pack_mx_scales(t: torch.Tensor) -> torch.Tensor:
     return t.reshape(*lead, r, b // 4, 4).transpose(-3, -2).contiguous()
 
 
+# status word bits (mxsg.h)
+STATUS_ENDS_DECREASING, STATUS_ENDS_RANGE, STATUS_ENDS_TOTAL, STATUS_NONFINITE = 1, 2, 4, 8
+
+
+def _status_word(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if t is not None and (t.dtype != torch.int32 or t.numel() < 1):
+        raise TypeError("status must be an int32 device tensor with at least one element")
+    return t
+
+
 def _scale_blocks(recipe: str) -> int:
     return {"block": 128, "mx": 32}.get(recipe, 0)
 
@@ -188,7 +198,8 @@ def quantize_act(x: torch.Tensor, recipe: str, fmt, group_ends: Optional[torch.T
                  rowwise: bool = True, colwise: bool = False,
                  state: Optional[DelayedState] = None, unit: int = 0,
                  out: Optional[QuantAct] = None,
-                 row_index: Optional[torch.Tensor] = None) -> QuantAct:
+                 row_index: Optional[torch.Tensor] = None,
+                 status: Optional[torch.Tensor] = None) -> QuantAct:
     """Quantize a token-major bf16 tensor [M, C] (mxsg_quantize_act).
 
     recipe "dl" takes its scale from ``state`` unit ``unit`` and records
@@ -196,10 +207,11 @@ def quantize_act(x: torch.Tensor, recipe: str, fmt, group_ends: Optional[torch.T
     ``out`` reuses previously allocated outputs of the same shape.
     With ``row_index`` (int32 [M]) the operand is the routed rows
     x[row_index] of a token tensor x [T, C], gathered inside the kernel
-    (mxsg_quantize_act_gather).
+    (mxsg_quantize_act_gather). ``status`` (int32 [1], device) receives the
+    MXSG_STATUS_* bits of malformed group ends and non-finite inputs.
     """
     x = _bits16(x)
-    _check_dev(x, group_ends, row_index)
+    _check_dev(x, group_ends, row_index, status)
     T, C = x.shape
     if row_index is not None:
         if row_index.dtype != torch.int32 or row_index.dim() != 1:
@@ -243,7 +255,7 @@ def quantize_act(x: torch.Tensor, recipe: str, fmt, group_ends: Optional[torch.T
         dli = state.inv[unit:unit + 1]
     outs = (E, _ptr(group_ends), _ptr(q.row_codes), _ptr(q.row_scales), _ptr(q.col_codes),
             _ptr(q.col_scales), q.ld, _ptr(q.padded_starts), _ptr(amax), _ptr(dls), _ptr(dli),
-            _stream())
+            _ptr(_status_word(status)), _stream())
     if row_index is None:
         _lib.call("mxsg_quantize_act", _ptr(x), M, C, RECIPES[recipe], f, *outs)
     else:
@@ -268,10 +280,12 @@ class QuantWeight:
 
 def quantize_weight(w: torch.Tensor, recipe: str, fmt, kmajor: bool = True, nmajor: bool = True,
                     state: Optional[DelayedState] = None, unit: int = 0,
-                    out: Optional[QuantWeight] = None) -> QuantWeight:
-    """Quantize expert weights [E, K, N] (mxsg_quantize_weight)."""
+                    out: Optional[QuantWeight] = None,
+                    status: Optional[torch.Tensor] = None) -> QuantWeight:
+    """Quantize expert weights [E, K, N] (mxsg_quantize_weight); ``status``
+    (int32 [1], device) receives MXSG_STATUS_NONFINITE for NaN / Inf weights."""
     w = _bits16(w)
-    _check_dev(w)
+    _check_dev(w, status)
     E, K, N = w.shape
     f = FMT[fmt]
     dev = w.device
@@ -305,7 +319,8 @@ def quantize_weight(w: torch.Tensor, recipe: str, fmt, kmajor: bool = True, nmaj
         dli = state.inv[unit:unit + E]
     _lib.call("mxsg_quantize_weight", _ptr(w), E, K, N, RECIPES[recipe], f,
               _ptr(q.kmajor_codes), _ptr(q.kmajor_scales), _ptr(q.nmajor_codes),
-              _ptr(q.nmajor_scales), _ptr(amax), _ptr(dls), _ptr(dli), _stream())
+              _ptr(q.nmajor_scales), _ptr(amax), _ptr(dls), _ptr(dli), _ptr(_status_word(status)),
+              _stream())
     return q
 
 
@@ -313,9 +328,10 @@ def grouped_mm(mode: int, recipe: str, fmt_a, fmt_b, E: int, M: int, K: int, N: 
                group_ends: torch.Tensor, a: torch.Tensor, a_scales: torch.Tensor, lda: int,
                b: torch.Tensor, b_scales: torch.Tensor, ldb: int,
                padded_starts: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-               accumulate: bool = False) -> torch.Tensor:
-    """Raw grouped GEMM call (mxsg_grouped_mm); see the helpers below."""
-    _check_dev(group_ends, a, a_scales, b, b_scales, padded_starts, out)
+               accumulate: bool = False, status: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Raw grouped GEMM call (mxsg_grouped_mm); see the helpers below.
+    ``status`` (int32 [1], device) receives the MXSG_STATUS_ENDS_* bits."""
+    _check_dev(group_ends, a, a_scales, b, b_scales, padded_starts, out, status)
     dev = a.device
     if out is None:
         if mode == MODE_FWD:
@@ -326,36 +342,39 @@ def grouped_mm(mode: int, recipe: str, fmt_a, fmt_b, E: int, M: int, K: int, N: 
             out = torch.empty(E, K, N, dtype=torch.float32, device=dev)
     _lib.call("mxsg_grouped_mm", mode, RECIPES[recipe], FMT[fmt_a], FMT[fmt_b], E, M, K, N,
               _ptr(group_ends), _ptr(padded_starts), _ptr(a), _ptr(a_scales), lda, _ptr(b),
-              _ptr(b_scales), ldb, _ptr(out), int(bool(accumulate)), _stream())
+              _ptr(b_scales), ldb, _ptr(out), int(bool(accumulate)), _ptr(_status_word(status)),
+              _stream())
     return out
 
 
 def grouped_mm_fwd(qa: QuantAct, qw: QuantWeight, group_ends: torch.Tensor,
-                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                   out: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Y [M, N] (bf16) = A_g @ W_g per group, from row-wise A and k-major W."""
     epb = elems_per_byte(qa.fmt)
     return grouped_mm(MODE_FWD, qa.recipe, qa.fmt, qw.fmt, qw.E, qa.M, qw.K, qw.N, group_ends,
                       qa.row_codes, qa.row_scales, qa.C // epb, qw.kmajor_codes, qw.kmajor_scales,
-                      qw.K // epb, out=out)
+                      qw.K // epb, out=out, status=status)
 
 
 def grouped_mm_dgrad(qdy: QuantAct, qw: QuantWeight, group_ends: torch.Tensor,
-                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                     out: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None) -> torch.Tensor:
     """dA [M, K] (bf16) = dY_g @ W_g^T per group, from row-wise dY and n-major W."""
     epb = elems_per_byte(qdy.fmt)
     return grouped_mm(MODE_DGRAD, qdy.recipe, qdy.fmt, qw.fmt, qw.E, qdy.M, qw.K, qw.N, group_ends,
                       qdy.row_codes, qdy.row_scales, qdy.C // epb, qw.nmajor_codes, qw.nmajor_scales,
-                      qw.N // epb, out=out)
+                      qw.N // epb, out=out, status=status)
 
 
 def grouped_mm_wgrad(qa: QuantAct, qdy: QuantAct, group_ends: torch.Tensor,
-                     out: Optional[torch.Tensor] = None, accumulate: bool = False) -> torch.Tensor:
+                     out: Optional[torch.Tensor] = None, accumulate: bool = False,
+                     status: Optional[torch.Tensor] = None) -> torch.Tensor:
     """dW [E, K, N] (fp32) = A_g^T @ dY_g per group, from the column-wise operands."""
     E = int(group_ends.numel())
     epb = elems_per_byte(qa.fmt)
     return grouped_mm(MODE_WGRAD, qa.recipe, qa.fmt, qdy.fmt, E, qa.M, qa.C, qdy.C, group_ends,
                       qa.col_codes, qa.col_scales, qa.ld // epb, qdy.col_codes, qdy.col_scales,
-                      qdy.ld // epb, padded_starts=qa.padded_starts, out=out, accumulate=accumulate)
+                      qdy.ld // epb, padded_starts=qa.padded_starts, out=out, accumulate=accumulate,
+                      status=status)
 
 
 def cast_sweep(start_bits: int, n: int, fmt, out: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -22,6 +22,7 @@ struct QuantActParams {
   const float *dl_scale, *dl_inv;
   const int32_t *row_index;  // optional: routed row i is x row row_index[i]
   int64_t src_rows;          // rows of x when row_index is given
+  int32_t *status;           // optional device status word (MXSG_STATUS_* bits)
 };
 
 struct QuantWeightParams {
@@ -35,6 +36,7 @@ struct QuantWeightParams {
   void *nmajor_scales;
   float *amax;
   const float *dl_scale, *dl_inv;
+  int32_t *status;           // optional device status word
 };
 
 struct GemmParams {
@@ -61,5 +63,7 @@ hipError_t launch_delayed_update(float *hist, int32_t *pos, float *amax, float *
 hipError_t launch_cast_sweep(uint32_t start, int64_t n, int fmt, uint8_t *out, hipStream_t st);
 hipError_t launch_stream_copy(const void *src, void *dst, int64_t bytes, hipStream_t st);
 hipError_t launch_grouped_mm(const GemmParams &p, hipStream_t st);
+// ORs MXSG_STATUS_ENDS_* bits into *status for malformed group ends
+hipError_t launch_check_ends(const int32_t *ends, int E, int64_t M, int32_t *status, hipStream_t st);
 
 }  // namespace mxsg

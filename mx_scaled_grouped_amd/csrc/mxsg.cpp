@@ -83,7 +83,8 @@ static mxsg_status quantize_act_impl(const char *fn, const void *x, int64_t T,
                                      const int32_t *group_ends, void *row_codes, void *row_scales,
                                      void *col_codes, void *col_scales, int64_t ld,
                                      int32_t *padded_starts, float *amax, const float *dl_scale,
-                                     const float *dl_inv, mxsg_stream_t stream) {
+                                     const float *dl_inv, int32_t *status_word,
+                                     mxsg_stream_t stream) {
   mxsg_status st = act_shape(fn, M, C, recipe, fmt);
   if (st != MXSG_OK) return st;
   REQUIRE(row_codes || col_codes, MXSG_INVALID_ARGUMENT, "%s: no output requested", fn);
@@ -138,6 +139,11 @@ static mxsg_status quantize_act_impl(const char *fn, const void *x, int64_t T,
   p.dl_inv = dl_inv;
   p.row_index = row_index;
   p.src_rows = T;
+  p.status = status_word;
+  if (status_word && group_ends && E >= 1) {
+    const hipError_t e = mxsg::launch_check_ends(group_ends, E, M, status_word, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return from_hip(e, fn);
+  }
   return from_hip(mxsg::launch_quantize_act(p, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -210,10 +216,10 @@ mxsg_status mxsg_quantize_act(const void *x, int64_t M, int64_t C, int32_t recip
                               int32_t E, const int32_t *group_ends, void *row_codes,
                               void *row_scales, void *col_codes, void *col_scales, int64_t ld,
                               int32_t *padded_starts, float *amax, const float *dl_scale,
-                              const float *dl_inv, mxsg_stream_t stream) {
+                              const float *dl_inv, int32_t *status_word, mxsg_stream_t stream) {
   return quantize_act_impl("quantize_act", x, M, nullptr, M, C, recipe, fmt, E, group_ends,
                            row_codes, row_scales, col_codes, col_scales, ld, padded_starts, amax,
-                           dl_scale, dl_inv, stream);
+                           dl_scale, dl_inv, status_word, stream);
 }
 
 mxsg_status mxsg_quantize_act_gather(const void *x, int64_t T, const int32_t *row_index, int64_t M,
@@ -221,17 +227,17 @@ mxsg_status mxsg_quantize_act_gather(const void *x, int64_t T, const int32_t *ro
                                      const int32_t *group_ends, void *row_codes, void *row_scales,
                                      void *col_codes, void *col_scales, int64_t ld,
                                      int32_t *padded_starts, float *amax, const float *dl_scale,
-                                     const float *dl_inv, mxsg_stream_t stream) {
+                                     const float *dl_inv, int32_t *status_word, mxsg_stream_t stream) {
   REQUIRE(M == 0 || row_index, MXSG_INVALID_ARGUMENT, "quantize_act_gather: row_index is NULL");
   return quantize_act_impl("quantize_act_gather", x, T, row_index, M, C, recipe, fmt, E,
                            group_ends, row_codes, row_scales, col_codes, col_scales, ld,
-                           padded_starts, amax, dl_scale, dl_inv, stream);
+                           padded_starts, amax, dl_scale, dl_inv, status_word, stream);
 }
 
 mxsg_status mxsg_quantize_weight(const void *w, int32_t E, int64_t K, int64_t N, int32_t recipe,
                                  int32_t fmt, void *kmajor_codes, void *kmajor_scales,
                                  void *nmajor_codes, void *nmajor_scales, float *amax,
-                                 const float *dl_scale, const float *dl_inv,
+                                 const float *dl_scale, const float *dl_inv, int32_t *status_word,
                                  mxsg_stream_t stream) {
   mxsg_status st = weight_shape("quantize_weight", E, K, N, recipe, fmt);
   if (st != MXSG_OK) return st;
@@ -258,6 +264,7 @@ mxsg_status mxsg_quantize_weight(const void *w, int32_t E, int64_t K, int64_t N,
   p.amax = amax;
   p.dl_scale = dl_scale;
   p.dl_inv = dl_inv;
+  p.status = status_word;
   return from_hip(mxsg::launch_quantize_weight(p, static_cast<hipStream_t>(stream)),
                   "quantize_weight");
 }
@@ -324,7 +331,7 @@ mxsg_status mxsg_grouped_mm(int32_t mode, int32_t recipe, int32_t fmt_a, int32_t
                             const int32_t *padded_starts, const void *a_codes,
                             const void *a_scales, int64_t lda, const void *b_codes,
                             const void *b_scales, int64_t ldb, void *out, int32_t accumulate,
-                            mxsg_stream_t stream) {
+                            int32_t *status_word, mxsg_stream_t stream) {
   mxsg_status st = mxsg_grouped_mm_check(mode, recipe, fmt_a, fmt_b, E, M, K, N, lda, ldb, accumulate);
   if (st != MXSG_OK) return st;
   REQUIRE(a_codes && b_codes && out && a_scales && b_scales && group_ends, MXSG_INVALID_ARGUMENT,
@@ -350,6 +357,10 @@ mxsg_status mxsg_grouped_mm(int32_t mode, int32_t recipe, int32_t fmt_a, int32_t
   p.ldb = ldb;
   p.out = out;
   p.accumulate = accumulate;
+  if (status_word) {
+    const hipError_t e = mxsg::launch_check_ends(group_ends, E, M, status_word, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return from_hip(e, "grouped_mm");
+  }
   return from_hip(mxsg::launch_grouped_mm(p, static_cast<hipStream_t>(stream)), "grouped_mm");
 }
 

@@ -27,6 +27,7 @@
 // eight feature rows of 128 positions column-wise).
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "mxsg.h"
 
 namespace mxsg {
 
@@ -38,6 +39,25 @@ constexpr int CODE_LD4 = 80;  // the same for 4-bit codes (64 bytes of codes per
 // ---------------------------------------------------------------------------
 // small kernels
 
+// status word: an amax reduction's maximum bf16 magnitude bits with an
+// all-ones exponent mean an Inf or NaN input (only then an atomic)
+__device__ __forceinline__ void flag_nonfinite(int32_t *status, uint32_t absbits) {
+  if (status && absbits >= 0x7F80u) atomicOr(status, MXSG_STATUS_NONFINITE);
+}
+
+// status word: malformed group ends (one workgroup)
+__global__ __launch_bounds__(256) void check_ends_kernel(const int32_t *__restrict__ ends, int E, int64_t M,
+                                                         int32_t *__restrict__ status) {
+  int bits = 0;
+  for (int g = threadIdx.x; g < E; g += blockDim.x) {
+    const int64_t e = ends[g], prev = g ? ends[g - 1] : 0;
+    if (e < prev) bits |= MXSG_STATUS_ENDS_DECREASING;
+    if (e < 0 || e > M) bits |= MXSG_STATUS_ENDS_RANGE;
+    if (g == E - 1 && e != M) bits |= MXSG_STATUS_ENDS_TOTAL;
+  }
+  if (bits) atomicOr(status, bits);
+}
+
 __global__ void zero_f32_kernel(float *__restrict__ p, int n) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0.0f;
@@ -48,7 +68,8 @@ __global__ void zero_f32_kernel(float *__restrict__ p, int n) {
 // slot must start at 0).
 __global__ __launch_bounds__(256) void amax_kernel(const uint16_t *__restrict__ x,
                                                    int64_t unit_elems,
-                                                   uint32_t *__restrict__ amax_bits) {
+                                                   uint32_t *__restrict__ amax_bits,
+                                                   int32_t *__restrict__ status) {
   const int u = blockIdx.y;
   const uint4 *p = reinterpret_cast<const uint4 *>(x + (int64_t)u * unit_elems);
   const int64_t nvec = unit_elems / 8;
@@ -65,6 +86,7 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint16_t *__restrict__ 
   if (threadIdx.x == 0) {
     m = umax(umax(red[0], red[1]), umax(red[2], red[3]));
     if (m) atomic_max_bits(amax_bits + u, m << 16);
+    flag_nonfinite(status, m);
   }
 }
 
@@ -83,7 +105,8 @@ __device__ __forceinline__ int64_t source_row(const int32_t *row_index, int64_t 
 __global__ __launch_bounds__(256) void amax_rows_kernel(const uint16_t *__restrict__ x, int64_t C,
                                                         const int32_t *__restrict__ row_index,
                                                         int64_t M, int64_t src_rows,
-                                                        uint32_t *__restrict__ amax_bits) {
+                                                        uint32_t *__restrict__ amax_bits,
+                                                        int32_t *__restrict__ status) {
   uint32_t m = 0;
   const int64_t nvec = C / 8;
   for (int64_t i = blockIdx.x; i < M; i += gridDim.x) {
@@ -98,6 +121,7 @@ __global__ __launch_bounds__(256) void amax_rows_kernel(const uint16_t *__restri
   if (threadIdx.x == 0) {
     m = umax(umax(red[0], red[1]), umax(red[2], red[3]));
     if (m) atomic_max_bits(amax_bits, m << 16);
+    flag_nonfinite(status, m);
   }
 }
 
@@ -124,6 +148,7 @@ struct TileArgs {
   int32_t stream_x;       // read x with streaming loads (x far larger than the caches)
   const int32_t *row_index;  // optional gather: routed row i is x row row_index[i]
   int64_t src_rows;          // rows of x when row_index is given
+  int32_t *status;           // optional status word (non-finite inputs)
 };
 
 // Padded start of the tile and its source rows. Returns false if the tile is
@@ -263,6 +288,7 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
   if (RECIPE == kDelayed || RECIPE == kTile128) {
     __syncthreads();
     const uint32_t m = umax(umax(red[0], red[1]), umax(red[2], red[3]));
+    if (t == 0) flag_nonfinite(a.status, m);
     if (RECIPE == kDelayed) {
       if (t == 0 && m) atomic_max_bits(reinterpret_cast<uint32_t *>(a.amax + b), m << 16);
     } else {
@@ -286,6 +312,7 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
         uint32_t m = absmax_bits8(v[u], 0);
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) m = umax(m, (uint32_t)__shfl_xor((int)m, o, 64));
+        if (cq == 0) flag_nonfinite(a.status, m);
         float s;
         scale_pair<FMT>(bits_to_amax(m), s, inv);
         if (cq == 0 && r < nvalid)
@@ -295,6 +322,7 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
         uint32_t m = absmax_bits8(v[u], 0);
         m = umax(m, (uint32_t)__shfl_xor((int)m, 1, 64));
         m = umax(m, (uint32_t)__shfl_xor((int)m, 2, 64));
+        if ((cq & 3) == 0) flag_nonfinite(a.status, m);
         const int k = mx_exponent<FMT>(bits_to_amax(m));
         inv = exp2_neg(k);
         // word-major E8M0 layout: word c0/128 of every row, then the next word
@@ -340,6 +368,7 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
       m0 = umax(m0, w[i] & 0x7fffu);
       m1 = umax(m1, (w[i] >> 16) & 0x7fffu);
     }
+    flag_nonfinite(a.status, umax(m0, m1));
     if (RECIPE == kMx) {  // 32x1 units: one quarter of the tile column
       const int k0 = mx_exponent<FMT>(bits_to_amax(m0));
       const int k1 = mx_exponent<FMT>(bits_to_amax(m1));
@@ -532,8 +561,14 @@ hipError_t launch_zero(float *p, int n, hipStream_t st) {
   return hipGetLastError();
 }
 
+hipError_t launch_check_ends(const int32_t *ends, int E, int64_t M, int32_t *status, hipStream_t st) {
+  if (E <= 0 || !status) return hipSuccess;
+  check_ends_kernel<<<1, 256, 0, st>>>(ends, E, M, status);
+  return hipGetLastError();
+}
+
 hipError_t launch_amax(const uint16_t *x, int units, int64_t unit_elems, float *amax,
-                       hipStream_t st) {
+                       int32_t *status, hipStream_t st) {
   hipError_t e = launch_zero(amax, units, st);
   if (e != hipSuccess) return e;
   if (unit_elems == 0) return hipSuccess;
@@ -542,7 +577,7 @@ hipError_t launch_amax(const uint16_t *x, int units, int64_t unit_elems, float *
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
   dim3 grid((unsigned)blocks, (unsigned)units);
-  amax_kernel<<<grid, 256, 0, st>>>(x, unit_elems, reinterpret_cast<uint32_t *>(amax));
+  amax_kernel<<<grid, 256, 0, st>>>(x, unit_elems, reinterpret_cast<uint32_t *>(amax), status);
   return hipGetLastError();
 }
 
@@ -578,11 +613,11 @@ hipError_t launch_quantize_act(const QuantActParams &p, hipStream_t st) {
       if (p.M > 0) {
         const unsigned blocks = (unsigned)(p.M < 8192 ? p.M : 8192);
         amax_rows_kernel<<<blocks, 256, 0, st>>>(p.x, p.C, p.row_index, p.M, p.src_rows,
-                                                 reinterpret_cast<uint32_t *>(p.amax));
+                                                 reinterpret_cast<uint32_t *>(p.amax), p.status);
         e = hipGetLastError();
       }
     } else {
-      e = launch_amax(p.x, 1, p.M * p.C, p.amax, st);
+      e = launch_amax(p.x, 1, p.M * p.C, p.amax, p.status, st);
     }
     if (e != hipSuccess) return e;
   }
@@ -606,6 +641,7 @@ hipError_t launch_quantize_act(const QuantActParams &p, hipStream_t st) {
   a.stream_x = (p.row_index ? p.src_rows : p.M) * p.C * 2 > kStreamBytes;
   a.row_index = p.row_index;
   a.src_rows = p.src_rows;
+  a.status = p.status;
   const bool row = p.row_codes != nullptr, col = p.col_codes != nullptr;
   // at least one tile: an empty tensor still gets its tensor scale written
   int64_t ytiles = col ? p.ld / QT : tiles_of(p.M);
@@ -621,7 +657,7 @@ hipError_t launch_quantize_act(const QuantActParams &p, hipStream_t st) {
 hipError_t launch_quantize_weight(const QuantWeightParams &p, hipStream_t st) {
   hipError_t e;
   if (p.recipe == kTensorwise) {
-    e = launch_amax(p.w, p.E, p.K * p.N, p.amax, st);
+    e = launch_amax(p.w, p.E, p.K * p.N, p.amax, p.status, st);
     if (e != hipSuccess) return e;
   }
   TileArgs a{};
@@ -638,6 +674,7 @@ hipError_t launch_quantize_weight(const QuantWeightParams &p, hipStream_t st) {
   a.dl_inv = p.dl_inv;
   a.x_bstride = p.K * p.N;
   a.stream_x = (int64_t)p.E * p.K * p.N * 2 > kStreamBytes;
+  a.status = p.status;
   const int64_t code_bytes = p.fmt == kE2M1 ? p.K * p.N / 2 : p.K * p.N;  // per expert
   a.row_bstride = code_bytes;
   a.col_bstride = code_bytes;

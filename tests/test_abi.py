@@ -25,6 +25,30 @@ def test_header_matches_binding():
     assert _declared() == sorted(_lib.SIGNATURES)
 
 
+def _declared_arity():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for name, params in re.findall(r"\b(mxsg_[a-z_]+)\s*\(([^)]*)\)\s*;", text):
+        params = params.strip()
+        out[name] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_header_arity_matches_binding():
+    arity = _declared_arity()
+    for name, (_, argtypes) in _lib.SIGNATURES.items():
+        assert arity[name] == len(argtypes), (name, arity[name], len(argtypes))
+
+
+def test_status_bits_match_header():
+    from mx_scaled_grouped_amd import api
+    text = open(HEADER).read()
+    bits = {k: int(v) for k, v in re.findall(r"#define MXSG_STATUS_(\w+) (\d+)", text)}
+    assert bits == {"ENDS_DECREASING": api.STATUS_ENDS_DECREASING, "ENDS_RANGE": api.STATUS_ENDS_RANGE,
+                    "ENDS_TOTAL": api.STATUS_ENDS_TOTAL, "NONFINITE": api.STATUS_NONFINITE}
+    assert len(set(bits.values())) == 4 and all(v & (v - 1) == 0 for v in bits.values())
+
+
 def test_all_symbols_exported():
     lib = _lib.load()
     for name in _declared():
@@ -57,7 +81,7 @@ def _qact(**kw):
     args = dict(x=FAKE, M=16, C=256, recipe=0, fmt=0, E=1, ends=FAKE, rc=FAKE, rs=FAKE, cc=None,
                 cs=None, ld=0, ps=None, amax=FAKE, dls=None, dli=None)
     args.update(kw)
-    return _lib.status_of("mxsg_quantize_act", *args.values(), None)
+    return _lib.status_of("mxsg_quantize_act", *args.values(), None, None)
 
 
 def test_quantize_act_validation():
@@ -82,7 +106,7 @@ def _qag(**kw):
     args = dict(x=FAKE, T=100, idx=FAKE, M=16, C=256, recipe=0, fmt=0, E=1, ends=FAKE, rc=FAKE,
                 rs=FAKE, cc=None, cs=None, ld=0, ps=None, amax=FAKE, dls=None, dli=None)
     args.update(kw)
-    return _lib.status_of("mxsg_quantize_act_gather", *args.values(), None)
+    return _lib.status_of("mxsg_quantize_act_gather", *args.values(), None, None)
 
 
 def test_quantize_act_gather_validation():
@@ -99,7 +123,7 @@ def _qw(**kw):
     args = dict(w=FAKE, E=2, K=256, N=256, recipe=0, fmt=0, kc=FAKE, ks=FAKE, nc=FAKE, ns=FAKE,
                 amax=FAKE, dls=None, dli=None)
     args.update(kw)
-    return _lib.status_of("mxsg_quantize_weight", *args.values(), None)
+    return _lib.status_of("mxsg_quantize_weight", *args.values(), None, None)
 
 
 def test_quantize_weight_validation():
@@ -116,7 +140,7 @@ def _mm(**kw):
     args = dict(mode=0, recipe=0, fa=0, fb=0, E=4, M=64, K=256, N=256, ends=FAKE, ps=None,
                 a=FAKE, sa=FAKE, lda=256, b=FAKE, sb=FAKE, ldb=256, out=FAKE, acc=0)
     args.update(kw)
-    return _lib.status_of("mxsg_grouped_mm", *args.values(), None)
+    return _lib.status_of("mxsg_grouped_mm", *args.values(), None, None)
 
 
 def test_grouped_mm_validation():
