@@ -251,3 +251,20 @@ def test_many_groups_and_single_group():
         assert np.array_equal(result_f64(c, run_case(c)), c.ref)
     c = make_case(0, "mx", 0, 0, [777], 384, 256, seed=47)
     assert np.array_equal(result_f64(c, run_case(c)), c.ref)
+
+
+@pytest.mark.parametrize("recipe,fmt", [("tw", 0), ("block", 0), ("mx", 0), ("mx", 2)],
+                         ids=["tw", "block", "mx", "mxfp4"])
+@pytest.mark.parametrize("mode", [0, 1, 2], ids=["fwd", "dgrad", "wgrad"])
+def test_minimum_feature_sizes(recipe, fmt, mode):
+    """K = N = 128, the smallest feature size: a contraction of one 128-block
+    (two of the four stages of the only ring turn are padding; for blockwise
+    the padding block's weight-scale entry is read), one column tile, and
+    exact integer operands so the result is bit-exact."""
+    K, N = 128, 128
+    c = make_case(mode, recipe, fmt, fmt, [5, 0, 130, 1], K, N, seed=80 + mode + 3 * fmt)
+    print(f"gemm minimum {recipe} fmt={fmt} mode={mode} M={c.M}", flush=True)
+    got = result_f64(c, run_case(c))
+    bad = np.flatnonzero(got.reshape(-1) != c.ref.reshape(-1))
+    assert bad.size == 0, f"{bad.size} mismatches; first {np.unravel_index(bad[0], got.shape)}: " \
+                          f"got {got.reshape(-1)[bad[0]]} want {c.ref.reshape(-1)[bad[0]]}"
