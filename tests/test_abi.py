@@ -278,3 +278,13 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(ImportError):
         _lib.load()
+
+
+def test_blockwise_contraction_limit():
+    """Blockwise forward / dgrad accept a contraction of up to 65536 (the
+    per-tile weight-scale table) and report UNSUPPORTED beyond it; wgrad's
+    contraction (the tokens of a group) has no such limit."""
+    assert _mm_check(recipe=2, K=65536, lda=65536, ldb=65536) == _lib.OK
+    assert _mm_check(recipe=2, K=65536 + 128, lda=65536 + 128, ldb=65536 + 128) == _lib.UNSUPPORTED
+    assert _mm_check(mode=1, recipe=2, N=65536, lda=65536, ldb=65536) == _lib.OK
+    assert _mm_check(mode=1, recipe=2, N=65536 + 128, lda=65536 + 128, ldb=65536 + 128) == _lib.UNSUPPORTED

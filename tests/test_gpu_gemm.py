@@ -268,3 +268,17 @@ def test_minimum_feature_sizes(recipe, fmt, mode):
     bad = np.flatnonzero(got.reshape(-1) != c.ref.reshape(-1))
     assert bad.size == 0, f"{bad.size} mismatches; first {np.unravel_index(bad[0], got.shape)}: " \
                           f"got {got.reshape(-1)[bad[0]]} want {c.ref.reshape(-1)[bad[0]]}"
+
+
+@pytest.mark.parametrize("mode", [0, 1], ids=["fwd", "dgrad"])
+def test_blockwise_maximum_contraction(mode):
+    """Blockwise forward / dgrad at the largest contraction the library
+    accepts (65536: 512 weight-scale blocks, the whole per-tile table), exact
+    integer operands (|products| <= 64, sums < 2^24: exact in fp32)."""
+    K, N = (65536, 128) if mode == 0 else (128, 65536)
+    c = make_case(mode, "block", 0, 0, [100, 0, 156], K, N, seed=90 + mode)
+    print(f"gemm blockwise max contraction mode={mode} M={c.M}", flush=True)
+    got = result_f64(c, run_case(c))
+    bad = np.flatnonzero(got.reshape(-1) != c.ref.reshape(-1))
+    assert bad.size == 0, f"{bad.size} mismatches; first {np.unravel_index(bad[0], got.shape)}: " \
+                          f"got {got.reshape(-1)[bad[0]]} want {c.ref.reshape(-1)[bad[0]]}"
