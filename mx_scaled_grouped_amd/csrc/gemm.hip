@@ -9,7 +9,8 @@
 //   DGRAD i = token, j = k, l = n; B = n-major weight codes of expert g
 //   WGRAD i = k, j = n, l = padded tokens of group g (column-wise codes)
 //
-// gfx950 design: a 256-thread workgroup (4 waves, 2 x 2) computes a
+// gfx950 design: a 256-thread workgroup (4 waves, 2 x 2; blockwise: 8
+// waves, 4 x 2, two per SIMD) computes a
 // 256 x BN output tile; each wave owns 128 x BN/2 as 4 x (BN/64) MFMA
 // 32x32x64 FP8 sub-tiles (v_mfma_scale_f32_32x32x64_f8f6f4). The
 // contraction runs in 64-wide stages through a ring of four LDS buffers:
@@ -204,14 +205,22 @@ struct Frags {
 // MFMA operand format code (cbsz / blgp) of an element format
 __host__ __device__ constexpr int mfma_fmt(int f) { return f == kE2M1 ? 4 : f; }
 
+// waves per workgroup: blockwise runs two waves per SIMD, so that one
+// wave's per-block promotion (VALU) issues while the other's MFMAs run
+template <int RECIPE>
+constexpr int gemm_waves() { return RECIPE == kBlockwise ? 8 : 4; }
+
 template <int MODE, int RECIPE, int FA, int FB, int BN>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
-  constexpr int NT = 256;            // threads: 4 waves, 2 along i (128 rows each) x 2 along j
+__global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel(GemmArgs a) {
+  constexpr int NW = gemm_waves<RECIPE>();
+  constexpr int NT = 64 * NW;        // threads
+  constexpr int WI = NW / 2;         // waves along i (2 along j)
+  constexpr int WM = GBM / WI;       // wave tile height along i
   constexpr int WN = BN / 2;         // wave tile width along j
   constexpr int NI = WN / 32;        // 32-wide sub-tiles along j per wave
-  constexpr int MI = 4;              // 32-high sub-tiles along i per wave (128 rows)
-  constexpr int AQ = GBM / 16 / 4;   // 1 KB copy groups (8 row pairs) of A per wave per stage
-  constexpr int BQ = BN / 16 / 4;    // of B
+  constexpr int MI = WM / 32;        // 32-high sub-tiles along i per wave
+  constexpr int AQ = GBM / 16 / NW;  // 1 KB copy groups (8 row pairs) of A per wave per stage
+  constexpr int BQ = BN / 16 / NW;   // of B
   constexpr bool BLK = RECIPE == kBlockwise;
   constexpr bool MX = RECIPE == kMx;
   // MXFP4: two e2m1 codes per byte, so a 64-byte stage is 128 contraction
@@ -323,6 +332,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
   // whole contraction (forward / dgrad) go to LDS once
   const float *sa_src = nullptr, *sb_src = nullptr;
   const bool b_wave = wave < BN / 64;   // copies B-row scale words / scales
+  const bool a_wave = wave < GBM / 64;  // copies A-row scales (blockwise)
   if (BLK) {
     const int r = wave * 64 + lane;
     sa_src = reinterpret_cast<const float *>(a.a_scales) + arow(r) * (sa_row / SBLK) + l0 / SBLK;
@@ -391,7 +401,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
           dma4(real && b_wave ? (const void *)(mxb + w * mxb_word) : (const void *)usrc,
                b_wave ? mb + wave * 64 : dmy);
       } else {
-        if constexpr (C == 0) dma4(real ? sa_src + (kt >> 1) : zsrc4, sa + wave * 64);
+        if constexpr (C == 0)
+          dma4(real && a_wave ? sa_src + (kt >> 1) : zsrc4, a_wave ? sa + wave * 64 : (float *)dmy);
         else dma4(real && b_wave ? sb_src + (kt >> 1) : zsrc4, b_wave ? sb + wave * 64 : (float *)dmy);
       }
     } else if constexpr (C < NSC + AQ) {
@@ -445,7 +456,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
                        const uint32_t *mb) {
     constexpr int U = decltype(u)::value;
     if constexpr (U < MI) {
-      f.a[U] = frag(as, wi * 128 + U * 32 + l32, h);
+      f.a[U] = frag(as, wi * WM + U * 32 + l32, h);
     } else if constexpr (U < MI + NI) {
       f.b[U - MI] = frag(bs, wj * WN + (U - MI) * 32 + l32, h);
     } else if constexpr (MX) {
@@ -463,7 +474,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
   auto read_frags = [&](Frags<MI, NI> &f, const uint8_t *as, const uint8_t *bs, const uint32_t *ma,
                         const uint32_t *mb) {
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) f.a[mi] = frag(as, wi * 128 + mi * 32 + l32, h);
+    for (int mi = 0; mi < MI; ++mi) f.a[mi] = frag(as, wi * WM + mi * 32 + l32, h);
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) f.b[ni] = frag(bs, wj * WN + ni * 32 + l32, h);
     if (MX) {
@@ -530,7 +541,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
       float sa[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float4 v4 = *reinterpret_cast<const float4 *>(&sa_l[wi * 128 + mi * 32 + q * 8 + h * 4]);
+        const float4 v4 = *reinterpret_cast<const float4 *>(&sa_l[wi * WM + mi * 32 + q * 8 + h * 4]);
         sa[q * 4 + 0] = v4.x;
         sa[q * 4 + 1] = v4.y;
         sa[q * 4 + 2] = v4.z;
@@ -640,7 +651,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
   constexpr int STR = WN + 8;          // LDS row stride in floats
   constexpr int CPR = WN / 8;          // 8-float chunks per row
   constexpr int CPL = 16 * CPR / 64;   // chunks per lane per half slab
-  uint8_t *creg = wave == 0 ? As0 : wave == 1 ? As1 : wave == 2 ? As2 : As3;
+  // (eight waves: two slabs in each A stage buffer)
+  const int cw = NW == 4 ? wave : wave >> 1;
+  uint8_t *creg = (cw == 0 ? As0 : cw == 1 ? As1 : cw == 2 ? As2 : As3) +
+                  (NW == 4 ? 0 : (wave & 1) * (GBM * GBK / 2));
   float *cb = reinterpret_cast<float *>(creg);
   const int64_t jw = j0 + wj * WN;
 #pragma unroll
@@ -657,7 +671,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
       for (int k = 0; k < CPL; ++k) {
         const int id = k * 64 + lane;
         const int r = id / CPR, c8 = id % CPR;
-        const int64_t i = i0 + wi * 128 + mi * 32 + hs * 16 + r;
+        const int64_t i = i0 + wi * WM + mi * 32 + hs * 16 + r;
         const int64_t j = jw + c8 * 8;
         const float4 x0 = *reinterpret_cast<const float4 *>(&cb[r * STR + c8 * 8]);
         const float4 x1 = *reinterpret_cast<const float4 *>(&cb[r * STR + c8 * 8 + 4]);
@@ -720,7 +734,7 @@ static hipError_t launch_cfg(const GemmArgs &a0, hipStream_t st) {
     const int64_t persistent = (int64_t)(ncu / 8) * 8;
     grid = nblocks < persistent ? nblocks : persistent;
   }
-  grouped_gemm_kernel<MODE, RECIPE, FA, FB, BN><<<(unsigned)grid, 256, 0, st>>>(a);
+  grouped_gemm_kernel<MODE, RECIPE, FA, FB, BN><<<(unsigned)grid, 64 * gemm_waves<RECIPE>(), 0, st>>>(a);
   return hipGetLastError();
 }
 
