@@ -11,8 +11,8 @@
 //
 // gfx950 design: a 256-thread workgroup (4 waves, 2 x 2; blockwise: 8
 // waves, 4 x 2, two per SIMD) computes a
-// 256 x BN output tile; each wave owns 128 x BN/2 as 4 x (BN/64) MFMA
-// 32x32x64 FP8 sub-tiles (v_mfma_scale_f32_32x32x64_f8f6f4). The
+// 256 x BN output tile; each wave owns (256 / waves along i) x BN/2 as
+// 32 x 32 MFMA sub-tiles (v_mfma_scale_f32_32x32x64_f8f6f4). The
 // contraction runs in 64-wide stages through a ring of four LDS buffers:
 // global_load_lds_dwordx4 copies (no staging registers) land XOR-swizzled
 // 16-byte chunks (bank-conflict-free fragment reads) three stages ahead of
@@ -442,7 +442,7 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
       for (int ni = 0; ni < NI; ++ni) {
         if (BLK) {
           asm volatile("" ::"v"(acc[mi][ni]));
-          asm volatile("" ::"a"(part[mi][ni]));
+          asm volatile("" ::"v"(part[mi][ni]));  // in VGPRs: promoted without AGPR reads
         } else {
           asm volatile("" ::"a"(acc[mi][ni]));
         }
