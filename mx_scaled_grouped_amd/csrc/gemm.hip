@@ -433,7 +433,9 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
   using W2 = std::integral_constant<int, 2>;
 
   // an empty asm use of every accumulator: keeps the stage's MFMAs issued
-  // before the next wait (and the accumulators in AGPRs)
+  // before the next wait, and each accumulator in its register file (AGPRs;
+  // blockwise: the totals and the block partials in VGPRs, so the promotion
+  // reads the partials directly)
   auto pin_acc = [&]() {
 #if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
@@ -442,7 +444,7 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
       for (int ni = 0; ni < NI; ++ni) {
         if (BLK) {
           asm volatile("" ::"v"(acc[mi][ni]));
-          asm volatile("" ::"v"(part[mi][ni]));  // in VGPRs: promoted without AGPR reads
+          asm volatile("" ::"v"(part[mi][ni]));
         } else {
           asm volatile("" ::"a"(acc[mi][ni]));
         }
