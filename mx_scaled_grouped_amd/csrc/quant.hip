@@ -149,6 +149,7 @@ struct TileArgs {
   const int32_t *row_index;  // optional gather: routed row i is x row row_index[i]
   int64_t src_rows;          // rows of x when row_index is given
   int32_t *status;           // optional status word (non-finite inputs)
+  int32_t rgroup;            // row tiles per launch-order group (>= 1)
 };
 
 // Padded start of the tile and its source rows. Returns false if the tile is
@@ -213,11 +214,24 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int64_t b = blockIdx.z;
-  // grid.x = row tiles x feature tiles, feature tiles fastest: consecutive
-  // workgroups read the 256-byte pieces of the same 128 rows (contiguous memory)
+  // grid.x = row tiles x feature tiles, in groups of `rgroup` row tiles: the
+  // feature tile runs slowest within a group, the row tile fastest. With
+  // rgroup = 1 consecutive workgroups read the 256-byte pieces of the same 128
+  // rows; with rgroup > 1 they also write adjacent 128-position pieces of the
+  // same column-wise feature rows.
   const int nft = (int)(a.C / QT);
-  const int ftile = (int)(blockIdx.x % (unsigned)nft);
-  const int64_t rtile = blockIdx.x / (unsigned)nft;
+  int ftile;
+  int64_t rtile;
+  {
+    const int64_t nrt = gridDim.x / (unsigned)nft;
+    const int64_t per = (int64_t)a.rgroup * nft;
+    const int64_t grp = blockIdx.x / per;
+    const int64_t within = blockIdx.x - grp * per;
+    const int64_t g0 = grp * a.rgroup;
+    const int gs = (int)(nrt - g0 < a.rgroup ? nrt - g0 : a.rgroup);
+    ftile = (int)(within / gs);
+    rtile = g0 + within % gs;
+  }
   const int64_t c0 = (int64_t)ftile * QT;
   const uint16_t *x = a.x + b * a.x_bstride;
 
@@ -556,6 +570,15 @@ static int tiles_of(int64_t n) { return (int)((n + QT - 1) / QT); }
 // later pass anyway, so the tile pass streams them past it
 constexpr int64_t kStreamBytes = (int64_t)256 << 20;
 
+// Launch-order group (row tiles) of a weight pass with k-major output. A group
+// of g row tiles makes the workgroups in flight together write g adjacent
+// 128-position pieces of each k-major row instead of one, which lets the
+// scattered column-wise writes use HBM better. Measured per pass (weights of
+// the Mixtral, DeepSeek and Llama4 shapes): 16 is best when the bf16 row
+// stride is not a multiple of 32 KiB, and slower than 8 when it is (then the
+// half-width row slices in flight read fewer distinct channel offsets).
+static int weight_col_group(int64_t C) { return (C * 2) % 32768 == 0 ? 8 : 16; }
+
 hipError_t launch_zero(float *p, int n, hipStream_t st) {
   zero_f32_kernel<<<(n + 255) / 256, 256, 0, st>>>(p, n);
   return hipGetLastError();
@@ -643,6 +666,7 @@ hipError_t launch_quantize_act(const QuantActParams &p, hipStream_t st) {
   a.src_rows = p.src_rows;
   a.status = p.status;
   const bool row = p.row_codes != nullptr, col = p.col_codes != nullptr;
+  a.rgroup = 1;  // token passes: feature tile fastest (measured best)
   // at least one tile: an empty tensor still gets its tensor scale written
   int64_t ytiles = col ? p.ld / QT : tiles_of(p.M);
   if (ytiles == 0) ytiles = 1;
@@ -695,6 +719,7 @@ hipError_t launch_quantize_weight(const QuantWeightParams &p, hipStream_t st) {
     a.col_scales = p.kmajor_scales;
   }
   const bool row = p.nmajor_codes != nullptr, col = p.kmajor_codes != nullptr;
+  a.rgroup = col ? weight_col_group(p.N) : 1;
   const int64_t tiles = (p.K / QT) * (p.N / QT);
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
   dim3 grid((unsigned)tiles, 1, (unsigned)p.E);
