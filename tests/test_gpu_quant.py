@@ -285,6 +285,29 @@ def test_weight_layouts(recipe, fmt):
         assert_bits_equal(host(q.amax), ref["amax"], "amax")
 
 
+# Weight passes with k-major output launch their tiles in groups of row tiles
+# (16, or 8 when the bf16 row stride is a multiple of 32 KiB). These shapes
+# have several full groups and a partial last one, for both group sizes.
+@pytest.mark.parametrize("shape,recipe,fmt", [
+    ((2, 128 * 37, 256), "tw", 0), ((2, 128 * 37, 256), "block", 1), ((2, 128 * 37, 256), "mx", 0),
+    ((2, 128 * 37, 256), "mx", 2), ((1, 128 * 19, 16384), "tw", 0), ((1, 128 * 11, 16384), "mx", 1)],
+    ids=["g16-tw", "g16-block", "g16-mx", "g16-mxfp4", "g8-tw", "g8-mx"])
+def test_weight_tile_groups(shape, recipe, fmt):
+    api = _api()
+    w = W.normal_bf16(108, 0, shape, std=0.02)
+    w[-1, -1, -1] = W.bf16_bits(np.float32([-2.5]))[0]      # outlier in the last tile
+    print(f"quantize_weight {shape} {recipe} fmt={fmt}", flush=True)
+    ref = OQ.quantize_weight(w, recipe, FMT_OBJ[fmt])
+    q = api.quantize_weight(to_dev_u16(w), recipe, fmt)
+    assert_bits_equal(codes_of(q.kmajor_codes, fmt), ref["kmajor_codes"], "k-major codes")
+    assert_bits_equal(codes_of(q.nmajor_codes, fmt), ref["nmajor_codes"], "n-major codes")
+    assert_bits_equal(scales_host(q.kmajor_scales, recipe), ref["kmajor_scales"], "k-major scales")
+    assert_bits_equal(scales_host(q.nmajor_scales, recipe), ref["nmajor_scales"], "n-major scales")
+    # k-major only (the forward-only weight pass) uses the same tile order
+    qk = api.quantize_weight(to_dev_u16(w), recipe, fmt, nmajor=False)
+    assert_bits_equal(codes_of(qk.kmajor_codes, fmt), ref["kmajor_codes"], "k-major-only codes")
+
+
 # ---------------------------------------------------------------------------
 # delayed scaling
 
