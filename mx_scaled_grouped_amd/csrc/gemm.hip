@@ -68,6 +68,7 @@ struct GemmArgs {
   int jtiles;
   int nblocks;           // tiles (slots x jtiles, or E x slots x jtiles)
   int accumulate;
+  int stream_out;        // FWD / DGRAD: write the bf16 output with streaming stores
 };
 
 // Workgroup bid runs on XCD bid % 8. Logical tiles are handed to the XCDs in
@@ -700,7 +701,11 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
             o.y = f32_to_bf16_bits(x0.z * scale) | (f32_to_bf16_bits(x0.w * scale) << 16);
             o.z = f32_to_bf16_bits(x1.x * scale) | (f32_to_bf16_bits(x1.y * scale) << 16);
             o.w = f32_to_bf16_bits(x1.z * scale) | (f32_to_bf16_bits(x1.w * scale) << 16);
-            *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(a.out) + i * a.ldo + j) = o;
+            uint16_t *dst = reinterpret_cast<uint16_t *>(a.out) + i * a.ldo + j;
+            if (a.stream_out)
+              store16_stream(dst, o);
+            else
+              *reinterpret_cast<uint4 *>(dst) = o;
           }
         }
       }
@@ -779,6 +784,13 @@ hipError_t launch_grouped_mm(const GemmParams &p, hipStream_t st) {
   a.M = p.M;
   a.E = p.E;
   a.accumulate = p.accumulate;
+  // A bf16 output larger than the 256 MiB last-level cache leaves with
+  // streaming stores, so that it does not evict the operand lines other tiles
+  // re-read (measured: forward / dgrad up to 4.5% faster on such outputs;
+  // streaming stores of wgrad's fp32 output were slower, up to 35%, and it
+  // keeps plain stores).
+  const int64_t out_cols = p.mode == kFwd ? p.N : p.K;
+  a.stream_out = p.M * out_cols * 2 > ((int64_t)256 << 20);
   if (p.mode == kFwd) {
     a.I = p.M;
     a.J = p.N;

@@ -282,3 +282,18 @@ def test_blockwise_maximum_contraction(mode):
     bad = np.flatnonzero(got.reshape(-1) != c.ref.reshape(-1))
     assert bad.size == 0, f"{bad.size} mismatches; first {np.unravel_index(bad[0], got.shape)}: " \
                           f"got {got.reshape(-1)[bad[0]]} want {c.ref.reshape(-1)[bad[0]]}"
+
+
+@pytest.mark.parametrize("mode", [0, 1], ids=["fwd", "dgrad"])
+def test_streaming_output_exact(mode):
+    """A bf16 output above 256 MiB (8200 x 16384) is written with streaming
+    stores: every element must still match the oracle exactly (integer
+    operands, exact in fp32 and in bf16)."""
+    K, N = (128, 16384) if mode == 0 else (16384, 128)
+    c = make_case(mode, "tw", 0, 0, [4100, 0, 4100], K, N, seed=120 + mode)
+    assert c.M * (N if mode == 0 else K) * 2 > (256 << 20)
+    print(f"gemm streaming output mode={mode} M={c.M} K={K} N={N}", flush=True)
+    got = result_f64(c, run_case(c))
+    bad = np.flatnonzero(got.reshape(-1) != c.ref.reshape(-1))
+    assert bad.size == 0, f"{bad.size} mismatches; first {np.unravel_index(bad[0], got.shape)}: " \
+                          f"got {got.reshape(-1)[bad[0]]} want {c.ref.reshape(-1)[bad[0]]}"
