@@ -321,8 +321,9 @@ def measured_traffic(workload):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path shards by expert, "
-              "see the design notes", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); across GPUs the path "
+              "would shard by expert, each GPU running this step on its own experts' groups",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     from mx_scaled_grouped_amd import api, workloads as W

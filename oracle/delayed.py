@@ -3,8 +3,8 @@
 The pages fix only the knobs: the Megatron-LM FP8-vs-BF16 MoE bug report
 reproduces with ``--fp8-amax-compute-algo max --fp8-amax-history-len
 1024`` (reproduction steps), and the Transformer Engine issue names the
-"delayed" recipe. The order of operations is a reading (listed in the
-design notes):
+"delayed" recipe. The order of operations is a reading, where the pages
+are silent:
 
 1. step t quantizes with the (s, inv) held by the state, which come from
    steps before t, and records the amax of the tensor it quantized;

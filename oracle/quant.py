@@ -18,8 +18,7 @@ Sources on the pages (none of them prints a formula):
   single-grouped-weight PR, fix 1 (the MXFP8 GroupedTensor listing).
 * MXFP8 with e4m3 elements: the same PR's coverage table.
 
-Readings taken where the pages are silent (each one is listed in the
-design notes of this repository):
+Readings taken where the pages are silent:
 
 * a scaling unit's scale is ``s = fp32(amax / fmax)`` (the stored
   dequantization multiplier, ``scale_inv`` in the PR's naming) and the
