@@ -347,6 +347,13 @@ def grouped_mm(mode: int, recipe: str, fmt_a, fmt_b, E: int, M: int, K: int, N: 
     return out
 
 
+def batch_group_ends(E: int, m: int, device) -> torch.Tensor:
+    """Group ends of a 3-D (batched) token operand [E, m, C], e.g. the
+    shared-expert case: its [E*m, C] view is E equal groups with ends m, 2m,
+    ..., E*m, so quantize_act and grouped_mm take it unchanged (int32 [E])."""
+    return torch.arange(1, E + 1, dtype=torch.int32, device=device) * int(m)
+
+
 def grouped_mm_fwd(qa: QuantAct, qw: QuantWeight, group_ends: torch.Tensor,
                    out: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Y [M, N] (bf16) = A_g @ W_g per group, from row-wise A and k-major W."""

@@ -297,3 +297,39 @@ def test_streaming_output_exact(mode):
     bad = np.flatnonzero(got.reshape(-1) != c.ref.reshape(-1))
     assert bad.size == 0, f"{bad.size} mismatches; first {np.unravel_index(bad[0], got.shape)}: " \
                           f"got {got.reshape(-1)[bad[0]]} want {c.ref.reshape(-1)[bad[0]]}"
+
+
+@pytest.mark.parametrize("recipe", ["tw", "mx"])
+@pytest.mark.parametrize("mode", [0, 1, 2], ids=["fwd", "dgrad", "wgrad"])
+def test_batched_3d_operand(recipe, mode):
+    """A 3-D (batched) token operand [E, m, C] runs as its [E*m, C] view with
+    E equal groups (api.batch_group_ends). Checked exactly against a batched
+    product of the dequantized 3-D operands (np.matmul over the batch axis),
+    not against the grouped oracle; m = 200 leaves each group's column-wise
+    rows padded to 256."""
+    E, m, K, N = 3, 200, 256, 384
+    F = FMT_OBJ[0]
+    c = make_case(mode, recipe, 0, 0, [m] * E, K, N, seed=130 + mode)
+    ends = _api().batch_group_ends(E, m, "cuda")
+    assert np.array_equal(host(ends), c.ge)
+    print(f"gemm batched 3-D {recipe} mode={mode} E={E} m={m}", flush=True)
+    got = result_f64(c, run_case(c))
+    if mode == 0:
+        A3 = OG.deq_act_rows(c.a, c.sa, recipe, F).reshape(E, m, K)
+        Wd = OG.deq_weight({"kmajor_codes": c.b, "kmajor_scales": c.sb}, recipe, F, "k")
+        ref = OG.round_bf16(np.matmul(A3, Wd).reshape(E * m, N))
+    elif mode == 1:
+        D3 = OG.deq_act_rows(c.a, c.sa, recipe, F).reshape(E, m, N)
+        Wd = OG.deq_weight({"nmajor_codes": c.b, "nmajor_scales": c.sb}, recipe, F, "n")
+        ref = OG.round_bf16(np.matmul(D3, Wd.transpose(0, 2, 1)).reshape(E * m, K))
+    else:
+        Rp = int(c.padded[-1])
+        blk = Rp // 32
+        sa = c.sa if recipe == "tw" else c.sa[:, :blk]
+        sb = c.sb if recipe == "tw" else c.sb[:, :blk]
+        A3 = OG.unpad_cols(OG.deq_act_cols(c.a[:, :Rp], sa, recipe, F), c.padded, c.ge).reshape(E, m, K)
+        D3 = OG.unpad_cols(OG.deq_act_cols(c.b[:, :Rp], sb, recipe, F), c.padded, c.ge).reshape(E, m, N)
+        ref = OG.round_f32(np.matmul(A3.transpose(0, 2, 1), D3))
+    bad = np.flatnonzero(got.reshape(-1) != ref.reshape(-1))
+    assert bad.size == 0, f"{bad.size} mismatches; first {np.unravel_index(bad[0], got.shape)}: " \
+                          f"got {got.reshape(-1)[bad[0]]} want {ref.reshape(-1)[bad[0]]}"

@@ -79,3 +79,11 @@ def test_mx_shape_errors():
         api.pack_mx_scales(torch.zeros(3, 6, dtype=torch.uint8))
     with pytest.raises(ValueError):
         api.unpack_mx_scales(torch.zeros(2, 3, 2, dtype=torch.uint8))
+
+
+def test_batch_group_ends():
+    # a 3-D [E, m, C] operand is E equal groups of its [E*m, C] view
+    e = api.batch_group_ends(4, 200, "cpu")
+    assert e.dtype == torch.int32
+    assert e.tolist() == [200, 400, 600, 800]
+    assert api.batch_group_ends(2, 0, "cpu").tolist() == [0, 0]
