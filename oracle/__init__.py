@@ -17,6 +17,9 @@ It is written for plain correctness, in numpy, from definitions:
 * ``delayed``  the delayed-scaling state (amax history, max algorithm).
 * ``gemm``     dequantization and the grouped GEMM (forward, dgrad, wgrad)
   in float64, bf16 rounding of outputs, relative Frobenius error, SQNR.
+* ``swiglu``   the SwiGLU activation between the two GEMMs in reproducible
+  fp32 (correctly rounded operations only), rounded to bf16: the reference
+  for the fused SwiGLU-then-quantize step, which no kernel takes yet.
 
 Every function states the passage of the source pages it follows. The
 pages name the recipes and formats but print no formula beyond
@@ -24,4 +27,4 @@ pages name the recipes and formats but print no formula beyond
 stated in the function's docstring. Functions without an independent
 pin are marked "parity unpinned" (there are none at present).
 """
-from . import formats, quant, delayed, gemm  # noqa: F401
+from . import formats, quant, delayed, gemm, swiglu  # noqa: F401
