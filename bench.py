@@ -240,6 +240,43 @@ def attainable_ms(spec, group_sizes, modes, peak_tflops=PEAK_FP8_TFLOPS, code_by
     return out
 
 
+def swiglu_quant_rate(torch, api, step, spec, R):
+    """The fused SwiGLU + quantization of the down-projection input, timed
+    on its own after the step (the step's down-projection input is an input
+    of the configuration): a random gate/up output [R, 2F] -> the step's
+    layouts of silu(gate) * up [R, F]. None for tensorwise (not built) and
+    for workloads without a down projection."""
+    if step.recipe == "tw" or "dn" not in spec.gemms:
+        return None
+    F = spec.gemm_shape("dn")[0]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    h = torch.randn(R, 2 * F, generator=g, device="cuda").to(torch.bfloat16)
+    kw = {}
+    if step.recipe == "dl":
+        kw = dict(state=api.DelayedState.create(1, 0, 16), unit=0)
+    q = api.quantize_act(h, step.recipe, step.fa, step.ge, rowwise=True, colwise=step.bwd,
+                         swiglu=True, **kw)
+    n = 10
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n):
+        api.quantize_act(h, step.recipe, step.fa, step.ge, rowwise=True, colwise=step.bwd,
+                         swiglu=True, out=q, **kw)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    code = 0.5 if step.fp4 else 1.0
+    per_layout = {"dl": code, "block": code + 4 / 128, "mx": code + 1 / 32}[step.recipe]
+    nbytes = R * F * (4.0 + (2 if step.bwd else 1) * per_layout)   # reads gate and up (bf16)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del h, q
+    return {"rows": R, "F": F, "ms": round(ms, 4), "gbs": round(gbs, 1),
+            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def percentiles(v):
     """p10, median, p90 of a list of per-call times (ms)."""
     import numpy as np
@@ -410,6 +447,7 @@ def main():
     copy_gbs = copy_rate(lambda: api.stream_copy(src, dst))
     torch_copy_gbs = copy_rate(lambda: dst.copy_(src))
     del src, dst
+    swiglu = swiglu_quant_rate(torch, api, step, spec, R)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -459,6 +497,7 @@ def main():
             "gemm_ms_total": round(gemm_total_ms, 4),
             "quant_ms_total": round(quant_total_ms, 4),
             "wall_s": round(wall, 3),
+            "swiglu_quant": swiglu,
         },
     }
     print(json.dumps(out), flush=True)

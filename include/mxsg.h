@@ -206,6 +206,29 @@ mxsg_status mxsg_quantize_act(const void *x, int64_t M, int64_t C, int32_t recip
                               const float *dl_inv, int32_t *status_word, mxsg_stream_t stream);
 
 /*
+ * mxsg_quantize_act applied to the SwiGLU activation of a gate/up GEMM
+ * output, fused so the activation is never written: x is bf16 [M, 2C]
+ * (device, row stride 2C); for columns c < C the quantized element is
+ * silu(x[m, c]) * x[m, C + c], silu(g) = g / (1 + exp(-g)), the SwiGLU that
+ * Mixtral's experts apply between the two GEMMs (the Megatron-LM FP8-vs-BF16
+ * MoE bug report's model; the pages print no formula). The activation is
+ * computed from correctly rounded fp32 operations only, in a fixed order
+ * (exp: argument clamped to [-87, 89], Cody-Waite reduction with a two-part
+ * ln 2, degree-7 Taylor polynomial, exact power-of-two scaling; then one add,
+ * one IEEE division, one multiply), rounded to nearest even bf16, and
+ * quantized exactly as mxsg_quantize_act quantizes a bf16 tensor [M, C]:
+ * every output, layout, size (mxsg_quantize_act_sizes with C) and rule is
+ * that call's. Delayed, blockwise and MX recipes only: tensorwise returns
+ * MXSG_UNSUPPORTED (its amax pass would need the activation too).
+ */
+mxsg_status mxsg_quantize_act_swiglu(const void *x, int64_t M, int64_t C, int32_t recipe,
+                                     int32_t fmt, int32_t E, const int32_t *group_ends,
+                                     void *row_codes, void *row_scales, void *col_codes,
+                                     void *col_scales, int64_t ld, int32_t *padded_starts,
+                                     float *amax, const float *dl_scale, const float *dl_inv,
+                                     int32_t *status_word, mxsg_stream_t stream);
+
+/*
  * mxsg_quantize_act on routed rows gathered from a token tensor: x is
  * [T, C] (one row per token) and routed row i, i < M, is x row
  * row_index[i] (int32 [M], device). This is the MoE dispatch permutation

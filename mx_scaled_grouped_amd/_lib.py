@@ -31,6 +31,8 @@ SIGNATURES = {
                                      _i32]),
     "mxsg_quantize_act": (_i32, [_c_p, _i64, _i64, _i32, _i32, _i32, _c_p, _c_p, _c_p, _c_p, _c_p,
                                  _i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
+    "mxsg_quantize_act_swiglu": (_i32, [_c_p, _i64, _i64, _i32, _i32, _i32, _c_p, _c_p, _c_p, _c_p,
+                                        _c_p, _i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "mxsg_quantize_act_gather": (_i32, [_c_p, _i64, _c_p, _i64, _i64, _i32, _i32, _i32, _c_p, _c_p,
                                         _c_p, _c_p, _c_p, _i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "mxsg_quantize_weight": (_i32, [_c_p, _i32, _i64, _i64, _i32, _i32, _c_p, _c_p, _c_p, _c_p,

@@ -199,7 +199,7 @@ def quantize_act(x: torch.Tensor, recipe: str, fmt, group_ends: Optional[torch.T
                  state: Optional[DelayedState] = None, unit: int = 0,
                  out: Optional[QuantAct] = None,
                  row_index: Optional[torch.Tensor] = None,
-                 status: Optional[torch.Tensor] = None) -> QuantAct:
+                 status: Optional[torch.Tensor] = None, swiglu: bool = False) -> QuantAct:
     """Quantize a token-major bf16 tensor [M, C] (mxsg_quantize_act).
 
     recipe "dl" takes its scale from ``state`` unit ``unit`` and records
@@ -209,10 +209,19 @@ def quantize_act(x: torch.Tensor, recipe: str, fmt, group_ends: Optional[torch.T
     x[row_index] of a token tensor x [T, C], gathered inside the kernel
     (mxsg_quantize_act_gather). ``status`` (int32 [1], device) receives the
     MXSG_STATUS_* bits of malformed group ends and non-finite inputs.
+    With ``swiglu`` x is a gate/up output [M, 2C] and the quantized tensor
+    is its SwiGLU activation silu(gate) * up [M, C]
+    (mxsg_quantize_act_swiglu; not with ``row_index``).
     """
     x = _bits16(x)
     _check_dev(x, group_ends, row_index, status)
     T, C = x.shape
+    if swiglu:
+        if row_index is not None:
+            raise ValueError("swiglu takes routed rows in order (no row_index)")
+        if C % 2:
+            raise ValueError("a gate/up output has an even number of columns")
+        C //= 2
     if row_index is not None:
         if row_index.dtype != torch.int32 or row_index.dim() != 1:
             raise TypeError("row_index must be a 1-D int32 tensor")
@@ -256,7 +265,9 @@ def quantize_act(x: torch.Tensor, recipe: str, fmt, group_ends: Optional[torch.T
     outs = (E, _ptr(group_ends), _ptr(q.row_codes), _ptr(q.row_scales), _ptr(q.col_codes),
             _ptr(q.col_scales), q.ld, _ptr(q.padded_starts), _ptr(amax), _ptr(dls), _ptr(dli),
             _ptr(_status_word(status)), _stream())
-    if row_index is None:
+    if swiglu:
+        _lib.call("mxsg_quantize_act_swiglu", _ptr(x), M, C, RECIPES[recipe], f, *outs)
+    elif row_index is None:
         _lib.call("mxsg_quantize_act", _ptr(x), M, C, RECIPES[recipe], f, *outs)
     else:
         _lib.call("mxsg_quantize_act_gather", _ptr(x), T, _ptr(row_index), M, C, RECIPES[recipe],

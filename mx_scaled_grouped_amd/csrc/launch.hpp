@@ -23,6 +23,7 @@ struct QuantActParams {
   const int32_t *row_index;  // optional: routed row i is x row row_index[i]
   int64_t src_rows;          // rows of x when row_index is given
   int32_t *status;           // optional device status word (MXSG_STATUS_* bits)
+  int32_t swiglu;            // x is a gate/up output [M, 2C]: quantize silu(gate) * up
 };
 
 struct QuantWeightParams {

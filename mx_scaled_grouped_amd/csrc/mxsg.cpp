@@ -84,9 +84,11 @@ static mxsg_status quantize_act_impl(const char *fn, const void *x, int64_t T,
                                      void *col_codes, void *col_scales, int64_t ld,
                                      int32_t *padded_starts, float *amax, const float *dl_scale,
                                      const float *dl_inv, int32_t *status_word,
-                                     mxsg_stream_t stream) {
+                                     mxsg_stream_t stream, bool swiglu = false) {
   mxsg_status st = act_shape(fn, M, C, recipe, fmt);
   if (st != MXSG_OK) return st;
+  REQUIRE(!swiglu || recipe != MXSG_RECIPE_TENSORWISE, MXSG_UNSUPPORTED,
+          "%s: tensorwise scaling of the SwiGLU activation is not built", fn);
   REQUIRE(row_codes || col_codes, MXSG_INVALID_ARGUMENT, "%s: no output requested", fn);
   REQUIRE(M == 0 || x, MXSG_INVALID_ARGUMENT, "%s: x is NULL", fn);
   if (row_index || T != M) {  // gathered rows: an index per routed row into x [T, C]
@@ -140,6 +142,7 @@ static mxsg_status quantize_act_impl(const char *fn, const void *x, int64_t T,
   p.row_index = row_index;
   p.src_rows = T;
   p.status = status_word;
+  p.swiglu = swiglu ? 1 : 0;
   if (status_word && group_ends && E >= 1) {
     const hipError_t e = mxsg::launch_check_ends(group_ends, E, M, status_word, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return from_hip(e, fn);
@@ -220,6 +223,17 @@ mxsg_status mxsg_quantize_act(const void *x, int64_t M, int64_t C, int32_t recip
   return quantize_act_impl("quantize_act", x, M, nullptr, M, C, recipe, fmt, E, group_ends,
                            row_codes, row_scales, col_codes, col_scales, ld, padded_starts, amax,
                            dl_scale, dl_inv, status_word, stream);
+}
+
+mxsg_status mxsg_quantize_act_swiglu(const void *x, int64_t M, int64_t C, int32_t recipe,
+                                     int32_t fmt, int32_t E, const int32_t *group_ends,
+                                     void *row_codes, void *row_scales, void *col_codes,
+                                     void *col_scales, int64_t ld, int32_t *padded_starts,
+                                     float *amax, const float *dl_scale, const float *dl_inv,
+                                     int32_t *status_word, mxsg_stream_t stream) {
+  return quantize_act_impl("quantize_act_swiglu", x, M, nullptr, M, C, recipe, fmt, E, group_ends,
+                           row_codes, row_scales, col_codes, col_scales, ld, padded_starts, amax,
+                           dl_scale, dl_inv, status_word, stream, true);
 }
 
 mxsg_status mxsg_quantize_act_gather(const void *x, int64_t T, const int32_t *row_index, int64_t M,

@@ -150,7 +150,56 @@ struct TileArgs {
   int64_t src_rows;          // rows of x when row_index is given
   int32_t *status;           // optional status word (non-finite inputs)
   int32_t rgroup;            // row tiles per launch-order group (>= 1)
+  int32_t swiglu;            // x is a gate/up output [rows, 2C]: quantize silu(gate) * up
 };
+
+// ---------------------------------------------------------------------------
+// SwiGLU between the expert GEMMs, from correctly rounded fp32 operations
+// only (no contraction into FMAs), so that every bit of the bf16 activation
+// is defined: exp by Cody-Waite reduction with a two-part ln 2 and a degree-7
+// Taylor polynomial (Horner), an exact power-of-two scaling, then one add and
+// one IEEE division for silu(g) = g / (1 + exp(-g)), one multiply by the up
+// value and round-to-nearest-even to bf16. The argument of exp is clamped to
+// [-87, 89]: below, 1 + exp(-g) is 1 in fp32 anyway and the clamp keeps
+// subnormals out; above, the result overflows to +inf as the true one does.
+__device__ __forceinline__ float exp_rn(float x) {
+  // plain operators under contract(off): each one is a separately rounded
+  // IEEE fp32 operation (the _rn helpers may still be fused after inlining)
+#pragma clang fp contract(off)
+  if (x != x) return x;
+  constexpr float kLog2e = (float)1.4426950408889634;
+  constexpr float kLn2Hi = (float)0.693145751953125;   // 16 significant bits
+  constexpr float kLn2Lo = (float)(0.6931471805599453 - 0.693145751953125);
+  const float xc = fminf(fmaxf(x, -87.0f), 89.0f);
+  const float n = rintf(xc * kLog2e);
+  const float r = (xc - n * kLn2Hi) - n * kLn2Lo;
+  float p = (float)(1.0 / 5040);
+  p = p * r + (float)(1.0 / 720);
+  p = p * r + (float)(1.0 / 120);
+  p = p * r + (float)(1.0 / 24);
+  p = p * r + (float)(1.0 / 6);
+  p = p * r + 0.5f;
+  p = p * r + 1.0f;
+  p = p * r + 1.0f;
+  return ldexpf(p, (int)n);
+}
+
+// bf16 bits of silu(g) * u for bf16 g, u
+__device__ __forceinline__ uint32_t swiglu_bf16(float g, float u) {
+#pragma clang fp contract(off)
+  const float s = __fdiv_rn(g, 1.0f + exp_rn(-g));
+  return f32_to_bf16_bits(s * u);
+}
+
+// eight activations (one 16-byte chunk) from a gate chunk and an up chunk
+__device__ __forceinline__ uint4 swiglu8(uint4 g, uint4 u) {
+  uint4 r;
+  r.x = swiglu_bf16(bf16_lo(g.x), bf16_lo(u.x)) | (swiglu_bf16(bf16_hi(g.x), bf16_hi(u.x)) << 16);
+  r.y = swiglu_bf16(bf16_lo(g.y), bf16_lo(u.y)) | (swiglu_bf16(bf16_hi(g.y), bf16_hi(u.y)) << 16);
+  r.z = swiglu_bf16(bf16_lo(g.z), bf16_lo(u.z)) | (swiglu_bf16(bf16_hi(g.z), bf16_hi(u.z)) << 16);
+  r.w = swiglu_bf16(bf16_lo(g.w), bf16_lo(u.w)) | (swiglu_bf16(bf16_hi(g.w), bf16_hi(u.w)) << 16);
+  return r;
+}
 
 // Padded start of the tile and its source rows. Returns false if the tile is
 // past the last group. Uses LDS `scan` (>= 65 ints).
@@ -269,14 +318,30 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
   const int cq = t & 15;   // chunk within the row (8 features)
   const int rq = t >> 4;   // row offset within a 16-row slab
   uint4 v[8];
+  if (a.swiglu) {
+    // gate/up rows of 2C: gate at column c, up at column C + c
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int r = u * 16 + rq;
-    if (r < nvalid) {
-      const uint16_t *src = x + source_row(a.row_index, a.src_rows, src0 + r) * a.C + c0 + cq * 8;
-      v[u] = a.stream_x ? load16_stream(src) : *reinterpret_cast<const uint4 *>(src);
-    } else {
-      v[u] = make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < 8; ++u) {
+      const int r = u * 16 + rq;
+      if (r < nvalid) {
+        const uint16_t *src = x + (src0 + r) * (2 * a.C) + c0 + cq * 8;
+        const uint4 gv = a.stream_x ? load16_stream(src) : *reinterpret_cast<const uint4 *>(src);
+        const uint4 uv = a.stream_x ? load16_stream(src + a.C) : *reinterpret_cast<const uint4 *>(src + a.C);
+        v[u] = swiglu8(gv, uv);
+      } else {
+        v[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = u * 16 + rq;
+      if (r < nvalid) {
+        const uint16_t *src = x + source_row(a.row_index, a.src_rows, src0 + r) * a.C + c0 + cq * 8;
+        v[u] = a.stream_x ? load16_stream(src) : *reinterpret_cast<const uint4 *>(src);
+      } else {
+        v[u] = make_uint4(0, 0, 0, 0);
+      }
     }
   }
 
@@ -667,6 +732,8 @@ hipError_t launch_quantize_act(const QuantActParams &p, hipStream_t st) {
   a.status = p.status;
   const bool row = p.row_codes != nullptr, col = p.col_codes != nullptr;
   a.rgroup = 1;  // token passes: feature tile fastest (measured best)
+  a.swiglu = p.swiglu;
+  if (p.swiglu) a.stream_x = p.M * p.C * 4 > kStreamBytes;
   // at least one tile: an empty tensor still gets its tensor scale written
   int64_t ytiles = col ? p.ld / QT : tiles_of(p.M);
   if (ytiles == 0) ytiles = 1;

@@ -19,7 +19,7 @@ It is written for plain correctness, in numpy, from definitions:
   in float64, bf16 rounding of outputs, relative Frobenius error, SQNR.
 * ``swiglu``   the SwiGLU activation between the two GEMMs in reproducible
   fp32 (correctly rounded operations only), rounded to bf16: the reference
-  for the fused SwiGLU-then-quantize step, which no kernel takes yet.
+  for the fused SwiGLU-then-quantize pass.
 
 Every function states the passage of the source pages it follows. The
 pages name the recipes and formats but print no formula beyond

@@ -1,6 +1,6 @@
 """SwiGLU between the two expert GEMMs, in reproducible fp32 (test
-infrastructure, for the fused "SwiGLU then quantize the down-projection
-input" step; no HIP kernel takes this step yet).
+infrastructure: the reference for the fused "SwiGLU, then quantize the
+down-projection input" pass).
 
 Source: the Megatron-LM MoE bug report trains Mixtral 8x7B, whose experts
 apply SwiGLU between the gate/up GEMM and the down GEMM (its reproduction
