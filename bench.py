@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="mixtral-dl", choices=sorted(WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-swiglu", action="store_true",
+                   help="skip the separate timing of the fused SwiGLU quantization")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (five times); "
                         "used to scale the HBM traffic counters")
@@ -447,7 +449,7 @@ def main():
     copy_gbs = copy_rate(lambda: api.stream_copy(src, dst))
     torch_copy_gbs = copy_rate(lambda: dst.copy_(src))
     del src, dst
-    swiglu = swiglu_quant_rate(torch, api, step, spec, R)
+    swiglu = None if args.no_swiglu else swiglu_quant_rate(torch, api, step, spec, R)
 
     cpu = None
     if not args.no_cpu_baseline:
