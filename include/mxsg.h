@@ -219,7 +219,9 @@ mxsg_status mxsg_quantize_act(const void *x, int64_t M, int64_t C, int32_t recip
  * quantized exactly as mxsg_quantize_act quantizes a bf16 tensor [M, C]:
  * every output, layout, size (mxsg_quantize_act_sizes with C) and rule is
  * that call's. Delayed, blockwise and MX recipes only: tensorwise returns
- * MXSG_UNSUPPORTED (its amax pass would need the activation too).
+ * MXSG_UNSUPPORTED (its amax pass would need the activation too). The
+ * status word's MXSG_STATUS_NONFINITE bit reports a NaN or Inf activation
+ * (a non-finite gate/up input, or a product that overflows).
  */
 mxsg_status mxsg_quantize_act_swiglu(const void *x, int64_t M, int64_t C, int32_t recipe,
                                      int32_t fmt, int32_t E, const int32_t *group_ends,
