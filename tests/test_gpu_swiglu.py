@@ -85,3 +85,29 @@ def test_swiglu_tensorwise_is_rejected():
     h = W.normal_bf16(170, 0, (8, 256), std=1.0)
     with pytest.raises(Exception):
         api.quantize_act(to_dev_u16(h), "tw", 0, None, rowwise=True, swiglu=True)
+
+
+@pytest.mark.parametrize("recipe,fmt", [("dl", 0), ("block", 0), ("mx", 0)])
+def test_swiglu_status_word(recipe, fmt):
+    """The non-finite bit reports a NaN or Inf activation: a NaN gate, an
+    infinite gate times a zero up value (NaN), and nothing for finite inputs."""
+    api = _api()
+    sizes = [100, 28]
+    C = 128
+    ge = to_dev(W.group_ends_from_sizes(sizes))
+    kw = {}
+    if recipe == "dl":
+        kw = dict(state=api.DelayedState.create(1, fmt, 4), unit=0)
+    for poison, expect in ((None, 0), ((5, 3, 0x7FC0, None), api.STATUS_NONFINITE),
+                           ((77, 100, 0x7F80, 0x0000), api.STATUS_NONFINITE)):
+        h = W.normal_bf16(180, 0, (sum(sizes), 2 * C), std=1.0)
+        if poison is not None:
+            r, c, gbits, ubits = poison
+            h[r, c] = gbits
+            if ubits is not None:
+                h[r, C + c] = ubits
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        api.quantize_act(to_dev_u16(h), recipe, fmt, ge, rowwise=True, colwise=True, swiglu=True,
+                         status=status, **kw)
+        got = int(host(status)[0])
+        assert got == expect, (poison, got, expect)
