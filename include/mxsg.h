@@ -3,10 +3,11 @@
  *
  * What it computes. The float8 MoE training pages describe one hot path:
  * quantize the routed-row activations, the expert weights and the output
- * gradients to FP8 ("dynamic quant + scaled grouped mm", torchao float8 MoE
- * training PR, Summary), then run a grouped matmul over per-expert token
- * groups for the forward pass and both backward products (the same PR's
- * Testing section checks outputs, input gradients and parameter gradients).
+ * gradients to FP8 at run time from their current amax (torchao float8 MoE
+ * training PR, Summary), then run a scaled grouped matmul over per-expert
+ * token groups for the forward pass and both backward products (the same
+ * PR's Testing section checks outputs, input gradients and parameter
+ * gradients).
  * Recipes: tensorwise dynamic; delayed with an amax history and the "max"
  * algorithm (Megatron-LM FP8-vs-BF16 MoE bug report, reproduction flags);
  * DeepSeek-style 1x128 / 128x1 / 128x128 blockwise with fp32 scales

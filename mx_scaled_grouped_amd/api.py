@@ -47,6 +47,22 @@ def _check_dev(*ts):
                 raise ValueError("tensors must be contiguous")
 
 
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _need(t: Optional[torch.Tensor], nbytes: int, what: str, dtype=None) -> None:
+    """The C ABI takes bare pointers, so the binding checks every buffer it
+    passes: a buffer smaller than the call writes or reads would be an
+    out-of-bounds access on the device."""
+    if t is None:
+        raise ValueError(f"{what} is missing")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype}, got {t.dtype}")
+    if _nbytes(t) < nbytes:
+        raise ValueError(f"{what} holds {_nbytes(t)} bytes, the call needs {nbytes}")
+
+
 def _bits16(x: torch.Tensor) -> torch.Tensor:
     if x.dtype == torch.bfloat16:
         return x
@@ -179,6 +195,33 @@ class DelayedState:
             getattr(self, k).copy_(v)
 
 
+def _check_quant_act_out(q: "QuantAct", recipe: str, f: int, M: int, C: int, E: int,
+                         rowwise: bool, colwise: bool) -> None:
+    """A reused QuantAct must describe the same call: same recipe, format
+    and shape, the requested layouts present, and every buffer at least the
+    size mxsg_quantize_act_sizes gives."""
+    if (q.recipe, q.fmt, q.M, q.C) != (recipe, f, M, C):
+        raise ValueError(f"out was made for recipe={q.recipe} fmt={q.fmt} M={q.M} C={q.C}, "
+                         f"the call has recipe={recipe} fmt={f} M={M} C={C}")
+    nb = quantize_act_sizes(M, C, recipe, f, E if colwise else 0)
+    sdt = torch.uint8 if recipe == "mx" else torch.float32
+    if rowwise:
+        _need(q.row_codes, nb[0], "out.row_codes", torch.uint8)
+        _need(q.row_scales, nb[1], "out.row_scales", sdt)
+    elif q.row_codes is not None:
+        raise ValueError("out holds row-wise codes but the call asks for none")
+    if colwise:
+        if q.ld != padded_capacity(M, E):
+            raise ValueError(f"out.ld={q.ld} was made for another group count (need {padded_capacity(M, E)})")
+        _need(q.col_codes, nb[2], "out.col_codes", torch.uint8)
+        _need(q.col_scales, nb[3], "out.col_scales", sdt)
+        _need(q.padded_starts, nb[4], "out.padded_starts", torch.int32)
+    elif q.col_codes is not None:
+        raise ValueError("out holds column-wise codes but the call asks for none")
+    if recipe == "tw":
+        _need(q.amax, 4, "out.amax", torch.float32)
+
+
 @dataclasses.dataclass
 class QuantAct:
     recipe: str
@@ -232,10 +275,14 @@ def quantize_act(x: torch.Tensor, recipe: str, fmt, group_ends: Optional[torch.T
     dev = x.device
     blk = _scale_blocks(recipe)
     E = int(group_ends.numel()) if group_ends is not None else 0
+    if colwise and group_ends is None:
+        raise ValueError("column-wise output needs group_ends")
+    if group_ends is not None and group_ends.dtype != torch.int32:
+        raise TypeError("group_ends must be int32")
     q = out
-    if q is None:
-        if colwise and group_ends is None:
-            raise ValueError("column-wise output needs group_ends")
+    if q is not None:
+        _check_quant_act_out(q, recipe, f, M, C, E, rowwise, colwise)
+    else:
         q = QuantAct(recipe, f, M, C)
         sdt = torch.uint8 if recipe == "mx" else torch.float32
         nb = quantize_act_sizes(M, C, recipe, f, E if colwise else 0)
@@ -259,6 +306,8 @@ def quantize_act(x: torch.Tensor, recipe: str, fmt, group_ends: Optional[torch.T
     if recipe == "dl":
         if state is None:
             raise ValueError("recipe 'dl' needs a DelayedState")
+        if not 0 <= unit < state.units:
+            raise ValueError(f"unit {unit} outside the state's {state.units} units")
         amax = state.amax[unit:unit + 1]
         dls = state.scale[unit:unit + 1]
         dli = state.inv[unit:unit + 1]
@@ -273,6 +322,27 @@ def quantize_act(x: torch.Tensor, recipe: str, fmt, group_ends: Optional[torch.T
         _lib.call("mxsg_quantize_act_gather", _ptr(x), T, _ptr(row_index), M, C, RECIPES[recipe],
                   f, *outs)
     return q
+
+
+def _check_quant_weight_out(q: "QuantWeight", recipe: str, f: int, E: int, K: int, N: int,
+                            kmajor: bool, nmajor: bool) -> None:
+    """A reused QuantWeight must describe the same call (recipe, format,
+    E, K, N, the requested layouts) with buffers of at least the sizes
+    mxsg_quantize_weight_sizes gives."""
+    if (q.recipe, q.fmt, q.E, q.K, q.N) != (recipe, f, E, K, N):
+        raise ValueError(f"out was made for recipe={q.recipe} fmt={q.fmt} E={q.E} K={q.K} N={q.N}, "
+                         f"the call has recipe={recipe} fmt={f} E={E} K={K} N={N}")
+    nb = quantize_weight_sizes(E, K, N, recipe, f)
+    sdt = torch.uint8 if recipe == "mx" else torch.float32
+    for want, codes, scales, i, name in ((kmajor, q.kmajor_codes, q.kmajor_scales, 0, "kmajor"),
+                                         (nmajor, q.nmajor_codes, q.nmajor_scales, 2, "nmajor")):
+        if want:
+            _need(codes, nb[i], f"out.{name}_codes", torch.uint8)
+            _need(scales, nb[i + 1], f"out.{name}_scales", sdt)
+        elif codes is not None:
+            raise ValueError(f"out holds {name} codes but the call asks for none")
+    if recipe == "tw":
+        _need(q.amax, 4 * E, "out.amax", torch.float32)
 
 
 @dataclasses.dataclass
@@ -301,7 +371,9 @@ def quantize_weight(w: torch.Tensor, recipe: str, fmt, kmajor: bool = True, nmaj
     f = FMT[fmt]
     dev = w.device
     q = out
-    if q is None:
+    if q is not None:
+        _check_quant_weight_out(q, recipe, f, E, K, N, kmajor, nmajor)
+    else:
         q = QuantWeight(recipe, f, E, K, N)
         nb = quantize_weight_sizes(E, K, N, recipe, f)
         epb = elems_per_byte(f)
@@ -325,6 +397,8 @@ def quantize_weight(w: torch.Tensor, recipe: str, fmt, kmajor: bool = True, nmaj
     if recipe == "dl":
         if state is None:
             raise ValueError("recipe 'dl' needs a DelayedState")
+        if not (0 <= unit and unit + E <= state.units):
+            raise ValueError(f"units {unit}..{unit + E - 1} outside the state's {state.units} units")
         amax = state.amax[unit:unit + E]
         dls = state.scale[unit:unit + E]
         dli = state.inv[unit:unit + E]
@@ -335,6 +409,40 @@ def quantize_weight(w: torch.Tensor, recipe: str, fmt, kmajor: bool = True, nmaj
     return q
 
 
+def _check_gemm_buffers(mode, recipe, fa, E, M, K, N, group_ends, a, a_scales, lda, b, b_scales, ldb,
+                        padded_starts, out) -> None:
+    """Sizes and dtypes of every buffer of a grouped_mm call (the layouts of
+    mxsg.h): codes, scales, group ends, padded starts and the output."""
+    epb = 2 if fa == E2M1 else 1
+    _need(group_ends, 4 * E, "group_ends", torch.int32)
+    if mode == MODE_WGRAD:
+        a_rows, b_rows = K, N                         # column-wise codes [K, lda], [N, ldb]
+        a_units, b_units = (K, lda * epb), (N, ldb * epb)
+        _need(padded_starts, 4 * (E + 1), "padded_starts", torch.int32)
+        out_bytes, out_dt = 4 * E * K * N, torch.float32
+    else:
+        L = K if mode == MODE_FWD else N             # contraction elements
+        J = N if mode == MODE_FWD else K
+        a_rows, b_rows = M + (M & 1), E * J
+        a_units, b_units = (M, L), (E * J, L)
+        out_bytes, out_dt = 2 * M * J, torch.bfloat16
+    _need(a, a_rows * lda, "A codes", torch.uint8)
+    _need(b, b_rows * ldb, "B codes", torch.uint8)
+    if recipe in ("tw", "dl"):
+        _need(a_scales, 4, "A scales", torch.float32)
+        _need(b_scales, 4 * (1 if mode == MODE_WGRAD else E), "B scales", torch.float32)
+    else:
+        blk, per = (128, 4) if recipe == "block" else (32, 1)
+        sdt = torch.float32 if recipe == "block" else torch.uint8
+        _need(a_scales, a_units[0] * (a_units[1] // blk) * per, "A scales", sdt)
+        if recipe == "block" and mode != MODE_WGRAD:   # 128x128 weight tiles
+            _need(b_scales, 4 * E * (K // 128) * (N // 128), "B scales", sdt)
+        else:
+            _need(b_scales, b_units[0] * (b_units[1] // blk) * per, "B scales", sdt)
+    if out is not None:
+        _need(out, out_bytes, "out", out_dt)
+
+
 def grouped_mm(mode: int, recipe: str, fmt_a, fmt_b, E: int, M: int, K: int, N: int,
                group_ends: torch.Tensor, a: torch.Tensor, a_scales: torch.Tensor, lda: int,
                b: torch.Tensor, b_scales: torch.Tensor, ldb: int,
@@ -343,6 +451,8 @@ def grouped_mm(mode: int, recipe: str, fmt_a, fmt_b, E: int, M: int, K: int, N: 
     """Raw grouped GEMM call (mxsg_grouped_mm); see the helpers below.
     ``status`` (int32 [1], device) receives the MXSG_STATUS_ENDS_* bits."""
     _check_dev(group_ends, a, a_scales, b, b_scales, padded_starts, out, status)
+    _check_gemm_buffers(mode, recipe, FMT[fmt_a], E, M, K, N, group_ends, a, a_scales, lda, b,
+                        b_scales, ldb, padded_starts, out)
     dev = a.device
     if out is None:
         if mode == MODE_FWD:

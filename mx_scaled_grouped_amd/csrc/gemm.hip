@@ -1,7 +1,8 @@
 // Grouped FP8 GEMM for the MoE expert layer: forward, dgrad and wgrad over
 // per-expert token groups (the grouped_mm that the torchao float8 MoE
-// training PR overrides with "dynamic quant + scaled grouped mm", and the
-// backward products its Testing section checks).
+// training PR replaces, in its Summary, by run-time quantization followed
+// by a scaled grouped matmul, and the backward products its Testing section
+// checks).
 //
 // Every mode is written as C[i, j] = sum_l A[i, l] * B[j, l] with both FP8
 // code operands contiguous along the contraction index l:

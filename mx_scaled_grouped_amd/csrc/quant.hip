@@ -11,10 +11,10 @@
 // 128 features). Row-wise units (1x128, 1x32) are reduced across the 16 (or
 // 4) lanes that hold one row; the tile is staged in LDS and re-read by
 // columns for the column-wise units (128x1, 32x1), whose codes are written
-// through an LDS code tile as 128-byte rows of the transposed output. This
-// is the "128x1 block scaling and transpose in shared memory" of the
-// Transformer Engine blockwise issue's design note, with the partial-block
-// zero fill it describes: a tile that runs past a group's last token reads
+// through an LDS code tile as 128-byte rows of the transposed output. The
+// Transformer Engine blockwise issue's design note does the same: column
+// (128x1) scaling with the transpose staged on chip rather than through a
+// high-precision copy in memory, and a zero fill of partial blocks: a tile that runs past a group's last token reads
 // zeros there, so padding never raises an amax and its codes are 0x00.
 //
 // Column-wise tiles are laid out in padded token space: group g owns padded

@@ -2,8 +2,8 @@
 
 What is computed (the problem statement of the pages): per-expert token
 groups [o_{g-1}, o_g) of a routed-row matrix, each multiplied by its own
-expert's weight - the "grouped_mm" that the torchao float8 MoE PR
-overrides with "dynamic quant + scaled grouped mm" (Summary), the
+expert's weight - the ``grouped_mm`` that the torchao float8 MoE PR
+replaces by run-time quantization and a scaled grouped matmul (Summary), the
 TEGroupedMLP / ``--moe-grouped-gemm`` path of the Megatron-LM bug report,
 and equivalently the per-expert loop of SequentialMLP that report runs.
 The backward (input gradients and parameter gradients) is the one the

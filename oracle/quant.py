@@ -2,8 +2,9 @@
 
 Sources on the pages (none of them prints a formula):
 
-* "dynamic quant + scaled grouped mm": the torchao float8 MoE training
-  PR, Summary - quantize each operand from the amax of the current tensor.
+* run-time quantization ahead of a scaled grouped matmul: the torchao
+  float8 MoE training PR, Summary - each operand is quantized from the amax
+  of the current tensor.
 * delayed scaling with ``--fp8-amax-compute-algo max`` and
   ``--fp8-amax-history-len 1024``: the Megatron-LM FP8-vs-BF16 MoE bug
   report, reproduction steps (see ``delayed``).

@@ -241,3 +241,37 @@ def test_structural_empty_group_and_permutation():
     assert np.array_equal(Yp, Y[rows])
     dWp = G.grouped_wgrad(af[rows], df[rows], ge_p, 3)
     assert np.array_equal(dWp, dW[perm])
+
+
+def test_rel_fro_hand_cases():
+    """||y - ref||_F / ||ref||_F on cases worked by hand: a 3-4-5 triangle
+    (a missing square root gives 0.01 instead of 0.1, a swapped denominator
+    0.5/||y|| instead of 0.5/||ref||), a matrix and a 3-D (weight-gradient
+    shaped) array, and the zero conventions."""
+    ref = np.array([[3.0, 0.0], [0.0, 4.0]])          # ||ref||_F = 5
+    y = ref + np.array([[0.0, 0.5], [0.0, 0.0]])      # ||y - ref||_F = 0.5
+    assert G.rel_fro(y, ref) == 0.1
+    # the error is measured relative to the reference, not to y
+    assert G.rel_fro(2 * ref, ref) == 1.0
+    assert G.rel_fro(ref, 2 * ref) == 0.5
+    # every element of a 3-D array counts: ||(1,2,2)|| = 3 over two experts
+    ref3 = np.zeros((2, 2, 2))
+    ref3[0, 0, 0], ref3[1, 1, 0], ref3[1, 1, 1] = 1.0, 2.0, 2.0
+    y3 = ref3.copy()
+    y3[1, 0, 1] = 0.75                                # error 0.75 -> 0.25
+    assert G.rel_fro(y3, ref3) == 0.25
+    assert G.rel_fro(np.zeros(3), np.zeros(3)) == 0.0
+    assert G.rel_fro(np.ones(3), np.zeros(3)) == float("inf")
+
+
+@pytest.mark.parametrize("k", [1, 7, 10, 23, 40])
+def test_rel_fro_and_sqnr_power_of_two_perturbation(k):
+    """ref * (1 + 2^-k) differs from ref by exactly ref * 2^-k (small
+    integers, so every value is exact in float64), hence rel_fro is exactly
+    2^-k and SQNR exactly 20 k log10(2) dB, whatever the shape or sign."""
+    rng = np.random.default_rng(k)
+    ref = rng.integers(-100, 101, size=(17, 9)).astype(np.float64)
+    y = ref * (1.0 + 2.0 ** -k)
+    assert G.rel_fro(y, ref) == 2.0 ** -k
+    assert abs(G.sqnr_db(ref, y) - 20.0 * k * math.log10(2.0)) < 1e-9
+    assert G.sqnr_db(ref, ref) == float("inf")
