@@ -246,9 +246,9 @@ def swiglu_quant_rate(torch, api, step, spec, R):
     """The fused SwiGLU + quantization of the down-projection input, timed
     on its own after the step (the step's down-projection input is an input
     of the configuration): a random gate/up output [R, 2F] -> the step's
-    layouts of silu(gate) * up [R, F]. None for tensorwise (not built) and
-    for workloads without a down projection."""
-    if step.recipe == "tw" or "dn" not in spec.gemms:
+    layouts of silu(gate) * up [R, F]. None for workloads without a down
+    projection."""
+    if "dn" not in spec.gemms:
         return None
     F = spec.gemm_shape("dn")[0]
     g = torch.Generator(device="cuda")
@@ -271,8 +271,9 @@ def swiglu_quant_rate(torch, api, step, spec, R):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
     code = 0.5 if step.fp4 else 1.0
-    per_layout = {"dl": code, "block": code + 4 / 128, "mx": code + 1 / 32}[step.recipe]
-    nbytes = R * F * (4.0 + (2 if step.bwd else 1) * per_layout)   # reads gate and up (bf16)
+    per_layout = {"tw": code, "dl": code, "block": code + 4 / 128, "mx": code + 1 / 32}[step.recipe]
+    read = 8.0 if step.recipe == "tw" else 4.0      # gate and up (bf16); tensorwise reads them twice (amax pass)
+    nbytes = R * F * (read + (2 if step.bwd else 1) * per_layout)
     gbs = nbytes / (ms * 1e-3) / 1e9
     del h, q
     return {"rows": R, "F": F, "ms": round(ms, 4), "gbs": round(gbs, 1),

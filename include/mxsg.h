@@ -209,20 +209,19 @@ mxsg_status mxsg_quantize_act(const void *x, int64_t M, int64_t C, int32_t recip
 /*
  * mxsg_quantize_act applied to the SwiGLU activation of a gate/up GEMM
  * output, fused so the activation is never written: x is bf16 [M, 2C]
- * (device, row stride 2C); for columns c < C the quantized element is
- * silu(x[m, c]) * x[m, C + c], silu(g) = g / (1 + exp(-g)), the SwiGLU that
- * Mixtral's experts apply between the two GEMMs (the Megatron-LM FP8-vs-BF16
- * MoE bug report's model; the pages print no formula). The activation is
- * computed from correctly rounded fp32 operations only, in a fixed order
- * (exp: argument clamped to [-87, 89], Cody-Waite reduction with a two-part
- * ln 2, degree-7 Taylor polynomial, exact power-of-two scaling; then one add,
- * one IEEE division, one multiply), rounded to nearest even bf16, and
- * quantized exactly as mxsg_quantize_act quantizes a bf16 tensor [M, C]:
- * every output, layout, size (mxsg_quantize_act_sizes with C) and rule is
- * that call's. Delayed, blockwise and MX recipes only: tensorwise returns
- * MXSG_UNSUPPORTED (its amax pass would need the activation too). The
- * status word's MXSG_STATUS_NONFINITE bit reports a NaN or Inf activation
- * (a non-finite gate/up input, or a product that overflows).
+ * (device, row stride 2C); for columns c < C the quantized element is the
+ * bf16 value nearest to silu(x[m, c]) * x[m, C + c] (ties to even; the
+ * exact real value, so the result is correctly rounded), with
+ * silu(g) = g / (1 + exp(-g)): the SwiGLU that Mixtral's experts apply
+ * between the two GEMMs (the Megatron-LM FP8-vs-BF16 MoE bug report's
+ * model, reproduction steps; the pages print no formula). That bf16 tensor
+ * [M, C] is then quantized exactly as mxsg_quantize_act quantizes a bf16
+ * tensor: every output, layout, size (mxsg_quantize_act_sizes with C) and
+ * rule is that call's. Tensorwise scaling first reads gate and up once to
+ * take the activation's amax (written to amax[0]). NaN / Inf inputs follow
+ * the formula in IEEE arithmetic (g = -inf gives NaN); the status word's
+ * MXSG_STATUS_NONFINITE bit reports a NaN or Inf activation (a non-finite
+ * gate/up input, or a product past the bf16 range).
  */
 mxsg_status mxsg_quantize_act_swiglu(const void *x, int64_t M, int64_t C, int32_t recipe,
                                      int32_t fmt, int32_t E, const int32_t *group_ends,
@@ -372,6 +371,25 @@ mxsg_status mxsg_grouped_mm_check(int32_t mode, int32_t recipe, int32_t fmt_a, i
  */
 mxsg_status mxsg_cast_sweep(uint32_t start_bits, int64_t n, int32_t fmt, void *out,
                             mxsg_stream_t stream);
+
+/*
+ * The SwiGLU activation on its own: y[m, c] = the bf16 value nearest to
+ * silu(x[m, c]) * x[m, C + c] (the activation mxsg_quantize_act_swiglu
+ * quantizes), for x bf16 [M, 2C] and y bf16 [M, C], both row-major device
+ * arrays, 16-byte aligned, C a positive multiple of 8. For callers that
+ * keep the bf16 activation (e.g. for the backward pass of the SwiGLU).
+ */
+mxsg_status mxsg_swiglu(const void *x, int64_t M, int64_t C, void *y, mxsg_stream_t stream);
+
+/*
+ * The fp32 sigmoid that the SwiGLU kernels evaluate first, for every bf16
+ * bit pattern g: out[g] (fp32 [65536], device) = that value for the gate
+ * g. The kernels rely on its relative error being at most 2^-21 for
+ * |g| <= 64 (they recompute in fp64 elsewhere and near bf16 rounding
+ * midpoints); this call lets a caller check that bound on every input.
+ * Outputs for |g| > 64 or non-finite g are unspecified.
+ */
+mxsg_status mxsg_sigmoid_sweep(float *out, mxsg_stream_t stream);
 
 /*
  * Device-to-device copy of `bytes` (a multiple of 16; both pointers 16-byte

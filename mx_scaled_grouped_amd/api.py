@@ -513,6 +513,32 @@ def cast_sweep(start_bits: int, n: int, fmt, out: Optional[torch.Tensor] = None)
     return out
 
 
+def swiglu(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The bf16 SwiGLU activation [M, C] of a gate/up output x [M, 2C]
+    (mxsg_swiglu): the value nearest to silu(gate) * up, ties to even."""
+    x = _bits16(x)
+    _check_dev(x, out)
+    M, C2 = x.shape
+    if C2 % 16:
+        raise ValueError("a gate/up output needs 2C columns with C a multiple of 8")
+    C = C2 // 2
+    if out is None:
+        out = torch.empty(M, C, dtype=torch.bfloat16, device=x.device)
+    _need(out, 2 * M * C, "out")
+    if out.element_size() != 2:
+        raise TypeError("out must be a 16-bit (bf16) tensor")
+    _lib.call("mxsg_swiglu", _ptr(x), M, C, _ptr(out), _stream())
+    return out
+
+
+def sigmoid_sweep() -> torch.Tensor:
+    """The device's fast-path fp32 sigmoid of every bf16 bit pattern
+    (mxsg_sigmoid_sweep): float32 [65536]."""
+    out = torch.empty(65536, dtype=torch.float32, device="cuda")
+    _lib.call("mxsg_sigmoid_sweep", _ptr(out), _stream())
+    return out
+
+
 def stream_copy(src: torch.Tensor, dst: torch.Tensor) -> None:
     """Device copy of src's bytes into dst (mxsg_stream_copy): the HBM
     reference rate for the quantization passes."""

@@ -87,8 +87,6 @@ static mxsg_status quantize_act_impl(const char *fn, const void *x, int64_t T,
                                      mxsg_stream_t stream, bool swiglu = false) {
   mxsg_status st = act_shape(fn, M, C, recipe, fmt);
   if (st != MXSG_OK) return st;
-  REQUIRE(!swiglu || recipe != MXSG_RECIPE_TENSORWISE, MXSG_UNSUPPORTED,
-          "%s: tensorwise scaling of the SwiGLU activation is not built", fn);
   REQUIRE(row_codes || col_codes, MXSG_INVALID_ARGUMENT, "%s: no output requested", fn);
   REQUIRE(M == 0 || x, MXSG_INVALID_ARGUMENT, "%s: x is NULL", fn);
   if (row_index || T != M) {  // gathered rows: an index per routed row into x [T, C]
@@ -387,6 +385,23 @@ mxsg_status mxsg_cast_sweep(uint32_t start_bits, int64_t n, int32_t fmt, void *o
   return from_hip(mxsg::launch_cast_sweep(start_bits, n, fmt, static_cast<uint8_t *>(out),
                                           static_cast<hipStream_t>(stream)),
                   "cast_sweep");
+}
+
+mxsg_status mxsg_swiglu(const void *x, int64_t M, int64_t C, void *y, mxsg_stream_t stream) {
+  REQUIRE(M >= 0 && C > 0 && C % 8 == 0, MXSG_BAD_SHAPE,
+          "swiglu: M=%lld C=%lld (C must be a positive multiple of 8)", (long long)M, (long long)C);
+  REQUIRE(M <= ((int64_t)1 << 31) - 1 && C <= ((int64_t)1 << 31) - 1, MXSG_BAD_SHAPE, "swiglu: too large");
+  REQUIRE(M == 0 || (x && y), MXSG_INVALID_ARGUMENT, "swiglu: NULL pointer");
+  REQUIRE(((uintptr_t)x | (uintptr_t)y) % 16 == 0, MXSG_INVALID_ARGUMENT,
+          "swiglu: pointers must be 16-byte aligned");
+  return from_hip(mxsg::launch_swiglu(static_cast<const uint16_t *>(x), M, C, static_cast<uint16_t *>(y),
+                                      static_cast<hipStream_t>(stream)),
+                  "swiglu");
+}
+
+mxsg_status mxsg_sigmoid_sweep(float *out, mxsg_stream_t stream) {
+  REQUIRE(out, MXSG_INVALID_ARGUMENT, "sigmoid_sweep: out is NULL");
+  return from_hip(mxsg::launch_sigmoid_sweep(out, static_cast<hipStream_t>(stream)), "sigmoid_sweep");
 }
 
 mxsg_status mxsg_stream_copy(const void *src, void *dst, int64_t bytes, mxsg_stream_t stream) {

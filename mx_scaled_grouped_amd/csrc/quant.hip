@@ -154,51 +154,167 @@ struct TileArgs {
 };
 
 // ---------------------------------------------------------------------------
-// SwiGLU between the expert GEMMs, from correctly rounded fp32 operations
-// only (no contraction into FMAs), so that every bit of the bf16 activation
-// is defined: exp by Cody-Waite reduction with a two-part ln 2 and a degree-7
-// Taylor polynomial (Horner), an exact power-of-two scaling, then one add and
-// one IEEE division for silu(g) = g / (1 + exp(-g)), one multiply by the up
-// value and round-to-nearest-even to bf16. The argument of exp is clamped to
-// [-87, 89]: below, 1 + exp(-g) is 1 in fp32 anyway and the clamp keeps
-// subnormals out; above, the result overflows to +inf as the true one does.
-__device__ __forceinline__ float exp_rn(float x) {
-  // plain operators under contract(off): each one is a separately rounded
-  // IEEE fp32 operation (the _rn helpers may still be fused after inlining)
-#pragma clang fp contract(off)
-  if (x != x) return x;
-  constexpr float kLog2e = (float)1.4426950408889634;
-  constexpr float kLn2Hi = (float)0.693145751953125;   // 16 significant bits
-  constexpr float kLn2Lo = (float)(0.6931471805599453 - 0.693145751953125);
-  const float xc = fminf(fmaxf(x, -87.0f), 89.0f);
-  const float n = rintf(xc * kLog2e);
-  const float r = (xc - n * kLn2Hi) - n * kLn2Lo;
-  float p = (float)(1.0 / 5040);
-  p = p * r + (float)(1.0 / 720);
-  p = p * r + (float)(1.0 / 120);
-  p = p * r + (float)(1.0 / 24);
-  p = p * r + (float)(1.0 / 6);
-  p = p * r + 0.5f;
-  p = p * r + 1.0f;
-  p = p * r + 1.0f;
-  return ldexpf(p, (int)n);
+// SwiGLU between the expert GEMMs: the bf16 value nearest to the exact
+// silu(g) * u (ties to even), silu(g) = g * sigmoid(g), for bf16 g and u.
+// For finite g != 0 and u != 0 that value is transcendental, hence never a
+// bf16 midpoint, so the rounding is well defined.
+//
+// Fast path, fp32. With a = |g| <= 64, e = exp(-a) = 2^-(a log2 e) is taken
+// as 2^-n * 2^-f: n = rint(a * kL2eHi) (an exact product: a has 8 significant
+// bits, kL2eHi 15), f = (a * kL2eHi - n) + a * kL2eLo (|f| <= 0.51, the
+// difference exact), 2^-f from v_exp_f32 and 2^-n from an exact ldexp. Then
+// sigmoid(a) = 1 / (1 + e) and sigmoid(-a) = e / (1 + e) with v_rcp_f32, and
+// p = fl(g * u) * sigmoid(g), where g * u is exact (8 x 8 significant bits).
+// Error budget in units of 2^-23 relative: e 1.1 (exp2 1 ulp, argument
+// rounding 0.1), 1 + e 1.05, reciprocal 1, e * r 0.5: sigmoid <= 3.7, so
+// with the last product p is within 4.2 * 2^-23 of the exact value, under
+// 9 units in the last place of p's own binade. mxsg_sigmoid_sweep exposes
+// the fast sigmoid so that its error can be checked on all 65536 bf16
+// gates (bound used below: 2^-21, i.e. p within 9 ulps). Rounding p to bf16
+// then gives the correctly rounded result unless p's low 16 bits lie within
+// kTieUlps of 0x8000 (a bf16 midpoint). Those elements, and all outside the
+// fast path's range (|g| > 64, zero, subnormal-range or overflowing p, NaN,
+// Inf), take the fp64 path below.
+constexpr float kL2eHi = 1.44268798828125f;          // log2(e) to 15 significant bits
+constexpr float kL2eLo = 7.052607543300837e-06f;     // log2(e) - kL2eHi
+constexpr int kTieUlps = 16;
+
+// fast sigmoid(g) for |g| <= 64 (fp32; see above)
+__device__ __forceinline__ float sigmoid_fast(float g) {
+  const float a = __builtin_fabsf(g);
+  const float xh = a * kL2eHi;                                  // exact
+  const float n = __builtin_rintf(xh);
+  const float f = __builtin_fmaf(a, kL2eLo, xh - n);            // xh - n exact
+  const float e = __builtin_ldexpf(__builtin_amdgcn_exp2f(-f), -(int)n);
+  const float r = __builtin_amdgcn_rcpf(1.0f + e);
+  return g >= 0.0f ? r : e * r;
 }
 
-// bf16 bits of silu(g) * u for bf16 g, u
-__device__ __forceinline__ uint32_t swiglu_bf16(float g, float u) {
-#pragma clang fp contract(off)
-  const float s = __fdiv_rn(g, 1.0f + exp_rn(-g));
-  return f32_to_bf16_bits(s * u);
+// fp64 path: the same formula in double (relative error < 2^-50), rounded to
+// bf16 directly from the double. When that double lies within 2^-45 of a
+// bf16 midpoint M, the side of M is decided from exact relations instead.
+// With P = |g * u| (exact) and |silu(g) * u| = P / (1 + exp(-g)):
+//   P <= M                 -> below M (the sigmoid is < 1);
+//   else below M iff P - 2M < M expm1(-g), used for |g| < 1 (sigmoid in
+//     (0.27, 0.73), so M < P < 4M and P - 2M is exact; expm1 keeps the
+//     small difference 1 - exp(-g) that exp itself would round away);
+//   else for g >= 1 iff P - M < M exp(-g) (P <= 2M: P - M exact), and for
+//     g <= -1 iff P - M < M exp(|g|).
+// (Only a value within ~2^-50 of M itself, which needs more than double
+// precision, could still be misjudged.)
+__device__ __attribute__((noinline)) uint32_t swiglu_bf16_fp64(float gf, float uf) {
+  const double g = gf, u = uf;
+  const double a = __builtin_fabs(g);
+  const double e = exp(-a);
+  const double sig = g >= 0.0 ? 1.0 / (1.0 + e) : e / (1.0 + e);
+  const double p = (g * u) * sig;
+  const uint32_t sign = __builtin_signbit(p) ? 0x8000u : 0u;
+  const double ap = __builtin_fabs(p);
+  if (!(ap == ap)) return 0x7FC0u | sign;                      // NaN
+  if (ap == __builtin_inf()) return 0x7F80u | sign;
+  if (ap == 0.0) return sign;
+  int ex;
+  (void)__builtin_frexp(ap, &ex);                               // ap in [2^(ex-1), 2^ex)
+  const int eb = ex - 1 < -126 ? -126 : ex - 1;
+  const double q = __builtin_ldexp(1.0, eb - 7);                // bf16 spacing around ap
+  const double t = ap / q;                                      // exact
+  const double k = __builtin_floor(t);
+  const double frac = t - k;
+  bool up;
+  if (__builtin_fabs(frac - 0.5) * q > 0x1p-45 * ap) {
+    up = frac > 0.5;
+  } else {
+    const double P = __builtin_fabs(g * u), M = (k + 0.5) * q;
+    bool below;
+    if (P <= M) below = true;
+    else if (a < 1.0) below = P - 2.0 * M < M * expm1(-g);
+    else if (g > 0.0) below = P - M < M * e;
+    else below = P - M < M * exp(a);
+    up = !below;
+  }
+  const float r = (float)((up ? k + 1.0 : k) * q);             // exact, or +inf past the bf16 range
+  return (__float_as_uint(r) >> 16) | sign;
+}
+
+// bf16 bits of the activation; *tie = true when the fp64 path must decide
+__device__ __forceinline__ uint32_t swiglu_fast(float g, float u, bool &redo) {
+  const float p = (g * u) * sigmoid_fast(g);
+  const uint32_t b = __float_as_uint(p);
+  const uint32_t ex = (b >> 23) & 0xFFu;
+  const int lo = (int)(b & 0xFFFFu) - 0x8000;
+  redo = !(__builtin_fabsf(g) <= 64.0f) || ex < 24u || ex > 253u || (lo <= kTieUlps && lo >= -kTieUlps);
+  return (b + 0x8000u) >> 16;                                   // nearest (not a tie here)
 }
 
 // eight activations (one 16-byte chunk) from a gate chunk and an up chunk
 __device__ __forceinline__ uint4 swiglu8(uint4 g, uint4 u) {
-  uint4 r;
-  r.x = swiglu_bf16(bf16_lo(g.x), bf16_lo(u.x)) | (swiglu_bf16(bf16_hi(g.x), bf16_hi(u.x)) << 16);
-  r.y = swiglu_bf16(bf16_lo(g.y), bf16_lo(u.y)) | (swiglu_bf16(bf16_hi(g.y), bf16_hi(u.y)) << 16);
-  r.z = swiglu_bf16(bf16_lo(g.z), bf16_lo(u.z)) | (swiglu_bf16(bf16_hi(g.z), bf16_hi(u.z)) << 16);
-  r.w = swiglu_bf16(bf16_lo(g.w), bf16_lo(u.w)) | (swiglu_bf16(bf16_hi(g.w), bf16_hi(u.w)) << 16);
-  return r;
+  const uint32_t gw[4] = {g.x, g.y, g.z, g.w}, uw[4] = {u.x, u.y, u.z, u.w};
+  uint32_t o[4];
+  uint32_t redo = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    bool r0, r1;
+    const uint32_t lo = swiglu_fast(bf16_lo(gw[i]), bf16_lo(uw[i]), r0);
+    const uint32_t hi = swiglu_fast(bf16_hi(gw[i]), bf16_hi(uw[i]), r1);
+    o[i] = lo | (hi << 16);
+    redo |= (r0 ? 1u : 0u) << (2 * i);
+    redo |= (r1 ? 1u : 0u) << (2 * i + 1);
+  }
+  if (redo) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (redo & (1u << (2 * i)))
+        o[i] = (o[i] & 0xFFFF0000u) | swiglu_bf16_fp64(bf16_lo(gw[i]), bf16_lo(uw[i]));
+      if (redo & (2u << (2 * i)))
+        o[i] = (o[i] & 0x0000FFFFu) | (swiglu_bf16_fp64(bf16_hi(gw[i]), bf16_hi(uw[i])) << 16);
+    }
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// amax of the SwiGLU activation of x [M, 2C] (tensorwise scaling of a fused
+// SwiGLU operand): 16-byte chunks of the gate half, each with its up chunk;
+// the result is max-reduced into *amax_bits (starts at 0).
+__global__ __launch_bounds__(256) void amax_swiglu_kernel(const uint16_t *__restrict__ x, int64_t M,
+                                                          int64_t C, uint32_t *__restrict__ amax_bits,
+                                                          int32_t *__restrict__ status) {
+  const int64_t cpr = C / 8;  // chunks per row
+  const int64_t n = M * cpr;
+  uint32_t m = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / cpr, c = (i - r * cpr) * 8;
+    const uint16_t *src = x + r * 2 * C + c;
+    m = absmax_bits8(swiglu8(*reinterpret_cast<const uint4 *>(src), *reinterpret_cast<const uint4 *>(src + C)), m);
+  }
+  m = wave_max_u32(m);
+  __shared__ uint32_t red[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = umax(umax(red[0], red[1]), umax(red[2], red[3]));
+    if (m) atomic_max_bits(amax_bits, m << 16);
+    flag_nonfinite(status, m);
+  }
+}
+
+// the SwiGLU activation itself: y [M, C] bf16 from x [M, 2C], one 16-byte
+// output chunk per thread
+__global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t *__restrict__ x, int64_t M, int64_t C,
+                                                     uint16_t *__restrict__ y) {
+  const int64_t cpr = C / 8;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= M * cpr) return;
+  const int64_t r = i / cpr, c = (i - r * cpr) * 8;
+  const uint16_t *src = x + r * 2 * C + c;
+  *reinterpret_cast<uint4 *>(y + r * C + c) =
+      swiglu8(*reinterpret_cast<const uint4 *>(src), *reinterpret_cast<const uint4 *>(src + C));
+}
+
+// the fast-path sigmoid of every bf16 bit pattern (65536 outputs)
+__global__ __launch_bounds__(256) void sigmoid_sweep_kernel(float *__restrict__ out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < 65536) out[i] = sigmoid_fast(bf16_lo((uint32_t)i));
 }
 
 // Padded start of the tile and its source rows. Returns false if the tile is
@@ -692,9 +808,34 @@ static hipError_t tile_by_recipe(int recipe, const TileArgs &a, bool row, bool c
   }
 }
 
+hipError_t launch_swiglu(const uint16_t *x, int64_t M, int64_t C, uint16_t *y, hipStream_t st) {
+  const int64_t n = M * (C / 8);
+  if (n == 0) return hipSuccess;
+  swiglu_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(x, M, C, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_sigmoid_sweep(float *out, hipStream_t st) {
+  sigmoid_sweep_kernel<<<256, 256, 0, st>>>(out);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize_act(const QuantActParams &p, hipStream_t st) {
   hipError_t e;
-  if (p.recipe == kTensorwise) {
+  if (p.recipe == kTensorwise && p.swiglu) {
+    // the amax is that of the activation, computed from gate and up
+    e = launch_zero(p.amax, 1, st);
+    if (e != hipSuccess) return e;
+    const int64_t n = p.M * (p.C / 8);
+    if (n > 0) {
+      int64_t blocks = (n + 256 * 8 - 1) / (256 * 8);
+      blocks = blocks > 4096 ? 4096 : (blocks < 1 ? 1 : blocks);
+      amax_swiglu_kernel<<<(unsigned)blocks, 256, 0, st>>>(p.x, p.M, p.C, reinterpret_cast<uint32_t *>(p.amax),
+                                                           p.status);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  } else if (p.recipe == kTensorwise) {
     if (p.row_index) {
       e = launch_zero(p.amax, 1, st);
       if (e != hipSuccess) return e;

@@ -1,81 +1,123 @@
-"""SwiGLU between the two expert GEMMs, in reproducible fp32 (test
-infrastructure: the reference for the fused "SwiGLU, then quantize the
-down-projection input" pass).
+"""SwiGLU between the two expert GEMMs (test infrastructure: the reference
+for the fused "SwiGLU, then quantize the down-projection input" pass and
+for the plain SwiGLU kernel).
 
-Source: the Megatron-LM MoE bug report trains Mixtral 8x7B, whose experts
-apply SwiGLU between the gate/up GEMM and the down GEMM (its reproduction
-steps); the pages print no formula for it. Readings taken here:
+Source: the Megatron-LM MoE bug report ("Loss difference when training with
+FP8 vs. BF16 MoE", reproduction steps) trains Mixtral 8x7B, whose experts
+apply SwiGLU between the gate/up GEMM and the down GEMM; the pages print no
+formula for it. Readings taken here:
 
 * the gate/up GEMM output ``h`` has 2F columns: the first F are the gate
-  ``g``, the last F the up projection ``u`` (the split of a fused gate/up
-  weight into two halves), and the activation is ``silu(g) * u`` with
-  ``silu(g) = g / (1 + exp(-g))``;
-* the activation is produced in bf16 (the dtype of the tensors between the
-  GEMMs), rounded to nearest even from the fp32 product, and quantized from
-  those bf16 values like any other activation;
-* so that a device implementation can match every bit, the fp32 value is
-  defined by correctly rounded fp32 operations only, in this order (no
-  fused multiply-adds): an exponential by Cody-Waite range reduction with a
-  two-part ln 2 and a degree-7 Taylor polynomial in Horner form, scaled by
-  an exact power of two; then one add and one IEEE division for SiLU, and
-  one multiply by ``u``. The exponential's argument is clamped to
-  [-87, 89] first: below, the true result would be subnormal (SiLU's
-  ``1 + exp(-g)`` is then 1 in fp32 anyway); above, it overflows to +inf as
-  the true one does. NaN stays NaN, and ``g = -inf`` gives NaN (IEEE
-  ``-inf / inf``).
+  ``g``, the last F the up projection ``u`` (the two halves of a fused
+  gate/up weight), and the activation is ``silu(g) * u`` with
+  ``silu(g) = g * sigmoid(g) = g / (1 + exp(-g))``;
+* the activation is the bf16 value nearest to the exact real number
+  ``silu(g) * u`` (ties to even), i.e. a correctly rounded bf16 result.
+  For finite bf16 ``g != 0`` and ``u != 0`` that number is transcendental
+  (``exp`` of a nonzero rational is), so it is never a bf16 midpoint and
+  the rounding is unambiguous; ``g == 0`` or ``u == 0`` gives a signed
+  zero. NaN and infinite inputs follow float64 arithmetic on the same
+  formula (``g = -inf`` gives NaN, as ``-inf * 0``).
 
-numpy float32 arithmetic is IEEE single with round-to-nearest-even, so each
-step below is the correctly rounded operation it names. The tests pin the
-exponential and SiLU to their float64 definitions within a few fp32 ulps,
-and the bf16 activation to the float64 textbook value away from bf16
-rounding boundaries.
+How it is computed: the formula in float64 (relative error below 2^-50),
+rounded directly to bf16 (``gemm.round_bf16``, no float32 step); where that
+float64 value lies within 2^-40 of its size from a bf16 rounding midpoint,
+the element is recomputed with Python's ``decimal`` module at 120 digits
+(its ``exp`` is correctly rounded at that precision) and rounded by exact
+comparison with the midpoint. Nothing here is tuned to any device
+algorithm.
 """
 from __future__ import annotations
+
+import decimal
+import math
 
 import numpy as np
 
 from .gemm import round_bf16
 
-_F = np.float32
-
-LOG2E = _F(1.4426950408889634)                    # fp32 nearest of log2(e)
-LN2_HI = _F(0.693145751953125)                    # 16 significant bits: n * LN2_HI exact for |n| <= 256
-LN2_LO = _F(0.6931471805599453 - 0.693145751953125)
-# 1/7!, 1/6!, ..., 1/1!, 1/0! as fp32, highest degree first
-TAYLOR = [_F(1.0 / 5040), _F(1.0 / 720), _F(1.0 / 120), _F(1.0 / 24), _F(1.0 / 6), _F(0.5), _F(1.0), _F(1.0)]
-EXP_LO, EXP_HI = _F(-87.0), _F(89.0)
+TIE_REL = 2.0 ** -40       # float64 values this close to a bf16 midpoint are recomputed exactly
+_PREC = 120                # decimal digits (2^-133, the bf16 subnormal quantum, has 93)
 
 
-def exp_f32(x) -> np.ndarray:
-    """fp32 exp(x) by the operation sequence stated in the module docstring."""
-    x = np.asarray(x, np.float32)
-    nan = np.isnan(x)
-    xc = np.clip(np.where(nan, _F(0), x), EXP_LO, EXP_HI).astype(np.float32)
-    n = np.rint(xc * LOG2E).astype(np.float32)             # nearest integer, ties to even
-    r = ((xc - n * LN2_HI) - n * LN2_LO).astype(np.float32)
-    p = TAYLOR[0] * np.ones_like(r)
-    for c in TAYLOR[1:]:
-        p = (p * r).astype(np.float32)
-        p = (p + c).astype(np.float32)
-    with np.errstate(over="ignore"):
-        y = np.ldexp(p, n.astype(np.int32)).astype(np.float32)
-    return np.where(nan, _F(np.nan), y).astype(np.float32)
-
-
-def silu_f32(g) -> np.ndarray:
-    """fp32 g / (1 + exp(-g)) (one add, one IEEE division)."""
-    g = np.asarray(g, np.float32)
-    d = (_F(1.0) + exp_f32(-g)).astype(np.float32)
+def sigmoid_f64(g) -> np.ndarray:
+    """sigmoid(g) = 1 / (1 + exp(-g)) in float64, evaluated as
+    exp(g) / (1 + exp(g)) for g < 0 (the same value, without overflow)."""
+    g = np.asarray(g, np.float64)
+    e = np.exp(-np.abs(g))
     with np.errstate(invalid="ignore"):
-        return (g / d).astype(np.float32)
+        return np.where(g >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def silu_f64(g) -> np.ndarray:
+    """silu(g) = g * sigmoid(g) in float64."""
+    g = np.asarray(g, np.float64)
+    with np.errstate(invalid="ignore"):
+        return g * sigmoid_f64(g)
+
+
+def _bf16_quantum(a: np.ndarray) -> np.ndarray:
+    """Spacing of the bf16 values around |a| (8 significant bits; a fixed
+    2^-133 below the smallest normal 2^-126)."""
+    e = np.frexp(a)[1] - 1                       # a in [2^e, 2^(e+1))
+    return np.ldexp(1.0, np.maximum(e, -126) - 7)
+
+
+def near_midpoint(p) -> np.ndarray:
+    """True where the float64 value p lies within TIE_REL * |p| of a bf16
+    rounding midpoint (where its own rounding error could decide the
+    bf16 result)."""
+    p = np.asarray(p, np.float64)
+    a = np.abs(p)
+    ok = np.isfinite(a) & (a > 0)
+    q = _bf16_quantum(np.where(ok, a, 1.0))
+    t = np.where(ok, a, 1.0) / q
+    frac = t - np.floor(t)
+    return ok & (np.abs(frac - 0.5) * q <= TIE_REL * np.where(ok, a, 1.0))
+
+
+def swiglu_exact_bf16(g: float, u: float) -> float:
+    """The bf16 value nearest to silu(g) * u for finite g, u, by exact
+    decimal arithmetic (returned as a float)."""
+    if g == 0 or u == 0:
+        return float(np.float64(g) * 0.5 * np.float64(u))       # signed zero, as IEEE gives it
+    ctx = decimal.Context(prec=_PREC)
+    D = decimal.Decimal
+    gd, ud = D(float(g)), D(float(u))
+    if g >= 0:
+        p = ctx.divide(ctx.multiply(gd, ud), ctx.add(D(1), ctx.exp(ctx.minus(gd))))
+    else:
+        eg = ctx.exp(gd)
+        p = ctx.divide(ctx.multiply(ctx.multiply(gd, ud), eg), ctx.add(D(1), eg))
+    a = ctx.copy_abs(p)                       # every step in the 120-digit context
+    approx = float(a)
+    q = float(_bf16_quantum(np.float64(approx)))
+    k = math.floor(ctx.divide(a, D(q)))
+    mid = ctx.multiply(ctx.add(D(k), D("0.5")), D(q))           # exact: q is a power of two
+    if a == mid:
+        # only when exp(-g) is below the working precision (g beyond ~276),
+        # 1 + exp(-g) rounds to 1 and |g u| (exact) is the midpoint itself;
+        # the true |silu(g) * u| = |g u| sigmoid(g) is strictly smaller, since
+        # sigmoid(g) < 1, so it rounds toward zero
+        assert g > 0 and ctx.copy_abs(ctx.multiply(gd, ud)) == mid, "silu(g) * u is never a bf16 midpoint"
+        r = k * q
+    else:
+        r = (k + 1) * q if a > mid else k * q
+    if abs(r) >= 2.0 ** 128:                  # past the largest bf16: rounds to infinity
+        r = math.inf
+    return math.copysign(r, float(p))
 
 
 def swiglu_bf16(h) -> np.ndarray:
     """Activation [M, F] (bf16 values as float64) of a gate/up output h
     [M, 2F] given as float values (bf16-representable)."""
-    h = np.asarray(h, np.float32)
+    h = np.asarray(h, np.float64)
     F = h.shape[-1] // 2
     g, u = h[..., :F], h[..., F:]
     with np.errstate(invalid="ignore", over="ignore"):
-        a = (silu_f32(g) * u).astype(np.float32)
-    return round_bf16(a.astype(np.float64))
+        p = silu_f64(g) * u
+    out = round_bf16(p)
+    amb = near_midpoint(p) & np.isfinite(g) & np.isfinite(u)
+    for idx in zip(*np.nonzero(amb)):
+        out[idx] = swiglu_exact_bf16(float(g[idx]), float(u[idx]))
+    return out
