@@ -53,6 +53,9 @@ def parse():
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (five times); "
                         "used to scale the HBM traffic counters")
+    p.add_argument("--micro-batches", type=int, default=4, metavar="M",
+                   help="also time optimizer steps of M micro-batches that quantize the weights once "
+                        "and reuse them (0: skip)")
     p.add_argument("--cpu-sample-rows", type=int, default=1024)
     p.add_argument("--cpu-sample-cols", type=int, default=28672)
     return p.parse_args()
@@ -62,14 +65,21 @@ def parse():
 # synthetic inputs (generated on the GPU with torch's seeded generator; the
 # distributions and routing follow mx_scaled_grouped_amd.workloads)
 
-def make_inputs(cid, torch, W, sets=2):
+def make_inputs(cid, torch, W, api, sets=2):
+    """Seeded inputs on the GPU: the top-k expert choices (device int32
+    [T, k]), the weights and `sets` sets of activations and gradients. The
+    routed rows of the gate/up input are gathered from the token rows by the
+    step itself (routing kernel, then the gathering quantizer); `a_gu`, an
+    explicit gathered copy made here with the device routing, is for checks
+    and for callers that want the gathered tensor."""
     spec = W.SPECS[cid]
-    r = W.routing_for(cid)
+    topk = W.routing_for(cid)
     dev = "cuda"
     g = torch.Generator(device=dev)
     g.manual_seed(1000 + cid)
-    R = r.rows
-    row_token = torch.from_numpy(r.row_token).to(dev)
+    R = topk.rows
+    ids = torch.from_numpy(topk.expert_ids).to(dev)
+    row_token = api.route(ids, spec.experts).row_index
 
     def normal(shape, std):
         t = torch.randn(shape, generator=g, device=dev, dtype=torch.float32)
@@ -78,10 +88,12 @@ def make_inputs(cid, torch, W, sets=2):
         return t.to(torch.bfloat16)
 
     def outliers(t):
+        # 0.1% of the elements, drawn without replacement, multiplied by 50
         if cid not in (5, 6):
             return t
         flat = t.view(-1)
-        idx = torch.randint(0, flat.numel(), (max(1, flat.numel() // 1000),), generator=g, device=dev)
+        n = flat.numel()
+        idx = torch.randperm(n, generator=g, device=dev)[:max(1, n // 1000)]
         flat[idx] = (flat[idx].float() * 50.0).to(torch.bfloat16)
         return t
 
@@ -92,26 +104,27 @@ def make_inputs(cid, torch, W, sets=2):
         weights["dn"] = normal((spec.experts, dn_k, dn_n), 0.02)
     sets_out = []
     for s in range(sets):
-        drift = 1.01 ** s if cid == 3 else 1.0
-        x = outliers(normal((spec.tokens, gu_k), drift))
-        # x_gu: the token tensor the step quantizes through the routing index
-        # (gather fused into the quantization); a_gu: the same routed rows as
-        # an explicit copy, for checks against the oracle
-        d = {"x_gu": x, "a_gu": x.index_select(0, row_token).contiguous()}
+        sets_out.append(make_set(cid, spec, R, s, normal, outliers, row_token))
+    return spec, topk, ids, weights, sets_out
+
+
+def make_set(cid, spec, R, s, normal, outliers, row_token):
+    """One input set (drift 1.01^s for the delayed-scaling workload)."""
+    gu_k, gu_n = spec.gemm_shape("gu")
+    dn_k, dn_n = spec.gemm_shape("dn")
+    drift = 1.01 ** s if cid == 3 else 1.0
+    x = outliers(normal((spec.tokens, gu_k), drift))
+    # x_gu: the token tensor the step quantizes through the routing index
+    # (gather fused into the quantization); a_gu: the same routed rows as
+    # an explicit copy
+    d = {"x_gu": x, "a_gu": x.index_select(0, row_token).contiguous()}
+    if "dn" in spec.gemms:
+        d["a_dn"] = outliers(normal((R, dn_k), drift))
+    if "dgrad" in spec.modes:
+        d["dy_gu"] = normal((R, gu_n), 2.0 ** -10)
         if "dn" in spec.gemms:
-            d["a_dn"] = outliers(normal((R, dn_k), drift))
-        if "dgrad" in spec.modes:
-            d["dy_gu"] = normal((R, gu_n), 2.0 ** -10)
-            if "dn" in spec.gemms:
-                d["dy_dn"] = normal((R, dn_n), 2.0 ** -10)
-        sets_out.append(d)
-    ge = torch.from_numpy(r.group_ends).to(dev)
-    return spec, r, ge, weights, sets_out
-
-
-def routing_index(r, torch):
-    """int32 routed-row -> token index on the GPU (the gather of the gate/up input)."""
-    return torch.from_numpy(r.row_token.astype("int32")).to("cuda")
+            d["dy_dn"] = normal((R, dn_n), 2.0 ** -10)
+    return d
 
 
 # ---------------------------------------------------------------------------
@@ -120,9 +133,14 @@ class Step:
     """One pass of the hot path; every call's duration is recorded with HIP
     events on the stream the kernels run on (torch's current stream)."""
 
-    def __init__(self, torch, api, spec, ge, weights, recipe, row_index=None):
-        self.torch, self.api, self.spec, self.ge, self.weights = torch, api, spec, ge, weights
-        self.row_index = row_index   # routed row -> token; None: a_gu is already gathered
+    def __init__(self, torch, api, spec, ids, weights, recipe, gather=True):
+        self.torch, self.api, self.spec, self.weights = torch, api, spec, weights
+        self.ids = ids               # top-k expert choices, int32 [T, k] on the device
+        # the routing buffers (group ends, routed row -> token), refilled by
+        # the routing kernel at the start of every step
+        self.rt = api.route(ids, spec.experts)
+        self.ge = self.rt.group_ends
+        self.gather = gather         # False: quantize the explicit gathered copy a_gu
         # "mxfp4" is the MX recipe with e2m1 elements for every operand
         self.recipe = "mx" if recipe == "mxfp4" else recipe
         if recipe == "mxfp4":
@@ -156,28 +174,49 @@ class Step:
         return r
 
     def run(self, data, timing=None):
-        api, spec, r = self.api, self.spec, self.recipe
+        """One step: one batch through the whole path (weights quantized)."""
+        self.optimizer_step([data], timing)
+
+    def optimizer_step(self, datas, timing=None):
+        """One optimizer step over len(datas) micro-batches: the expert
+        weights change only at the optimizer step, so they are quantized
+        (both layouts) once, before the first micro-batch, and every
+        micro-batch reuses them; wgrad accumulates into the fp32 main
+        gradient after the first micro-batch; the delayed-scaling state is
+        updated once, after the last (its activation / gradient amaxes are
+        then the maxima over the micro-batches)."""
         self.timing = timing
+        for b, data in enumerate(datas):
+            self._micro_batch(data, first=b == 0)
+        if self.recipe == "dl":
+            self._t("delayed_update", lambda: (self.st_f.update(), self.st_g.update()))
+        self.timing = None
+
+    def _micro_batch(self, data, first):
+        api, spec, r = self.api, self.spec, self.recipe
         bwd = self.bwd
+        self._t("route", lambda: api.route(self.ids, spec.experts, out=self.rt))
         for gi, which in enumerate(spec.gemms):
             K, N = spec.gemm_shape(which)
             a, w = data["a_" + which], self.weights[which]
             kw = {}
             if r == "dl":
                 kw = dict(state=self.st_f, unit=gi)
-            if which == "gu" and self.row_index is not None:
+            if which == "gu" and self.gather:
                 # the routed rows are gathered from the tokens inside the kernel
                 a = data["x_gu"]
-                kw["row_index"] = self.row_index
+                kw["row_index"] = self.rt.row_index
             qa = self._t(f"quant_a_{which}", lambda: api.quantize_act(
                 a, r, self.fa, self.ge, rowwise=True, colwise=bwd, out=self.q.get("a_" + which), **kw))
             self.q["a_" + which] = qa
             kw = {}
             if r == "dl":
                 kw = dict(state=self.st_f, unit=len(spec.gemms) + gi * self.E)
-            qw = self._t(f"quant_w_{which}", lambda: api.quantize_weight(
-                w, r, self.fw, kmajor=True, nmajor=bwd, out=self.q.get("w_" + which), **kw))
-            self.q["w_" + which] = qw
+            if first:
+                qw = self._t(f"quant_w_{which}", lambda: api.quantize_weight(
+                    w, r, self.fw, kmajor=True, nmajor=bwd, out=self.q.get("w_" + which), **kw))
+                self.q["w_" + which] = qw
+            qw = self.q["w_" + which]
             self.out["y_" + which] = self._t(f"gemm_fwd_{which}", lambda: api.grouped_mm_fwd(
                 qa, qw, self.ge, out=self.out.get("y_" + which)))
             if bwd:
@@ -189,10 +228,7 @@ class Step:
                 self.out["da_" + which] = self._t(f"gemm_dgrad_{which}", lambda: api.grouped_mm_dgrad(
                     qd, qw, self.ge, out=self.out.get("da_" + which)))
                 self.out["dw_" + which] = self._t(f"gemm_wgrad_{which}", lambda: api.grouped_mm_wgrad(
-                    qa, qd, self.ge, out=self.out.get("dw_" + which)))
-        if r == "dl":
-            self._t("delayed_update", lambda: (self.st_f.update(), self.st_g.update()))
-        self.timing = None
+                    qa, qd, self.ge, out=self.out.get("dw_" + which), accumulate=not first))
 
     def work(self, R):
         """Algorithmic GEMM FLOPs and quantization bytes per call name."""
@@ -280,6 +316,36 @@ def swiglu_quant_rate(torch, api, step, spec, R):
             "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
+def persistent_weights_rate(torch, step, sets, micro, step_flops, ms_step, quant_ms):
+    """Optimizer steps of `micro` micro-batches with the weights quantized
+    once per step (the persistent quantized weights of gradient
+    accumulation), timed after the main loop: 1 untimed and 3 timed
+    optimizer steps, micro-batches cycling through the input sets."""
+    datas = [sets[i % len(sets)] for i in range(micro)]
+    step.optimizer_step(datas)
+    timing = []
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    n = 3
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n):
+        step.optimizer_step(datas, timing=timing)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    wq = sum(a.elapsed_time(b) for name, a, b in timing if name.startswith("quant_w")) / n
+    wq_step = sum(v for k, v in quant_ms.items() if k.startswith("quant_w"))
+    return {"micro_batches": micro, "ms_per_optimizer_step": round(ms, 4),
+            "ms_per_micro_batch": round(ms / micro, 4),
+            "tflops": round(step_flops * micro / (ms * 1e-3) / 1e12, 2),
+            "weight_quant_ms_per_optimizer_step": round(wq, 4),
+            "ms_per_step_weights_quantized_every_step": round(ms_step, 4),
+            "weight_quant_ms_every_step": round(wq_step, 4),
+            "note": "wgrad accumulates into fp32 after the first micro-batch; delayed update once per "
+                    "optimizer step"}
+
+
 def percentiles(v):
     """p10, median, p90 of a list of per-call times (ms)."""
     import numpy as np
@@ -300,11 +366,12 @@ def cpu_baseline(cid, rows, cols):
         threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
+    from oracle import routing as OR
     spec = W.SPECS[cid]
-    r = W.routing_for(cid)
+    topk = W.routing_for(cid)
     K, N = spec.gemm_shape("gu")
     N = min(N, cols)
-    m = min(rows, int(r.group_sizes[0]))
+    m = min(rows, int(OR.route(topk.expert_ids, topk.n_experts)["group_ends"][0]))
     rec = {"tw": "tw", "dl": "dl", "block": "block", "mx": "mx", "mxfp4": "mx"}[spec.recipe]
     fq = OF.E2M1 if spec.recipe == "mxfp4" else OF.E4M3     # activations and weights
     a = W.normal_bf16(cid, W.T_X, (m, K))
@@ -380,9 +447,10 @@ def main():
 
     cid = WORKLOADS[args.workload]
     print(f"# generating inputs for {W.SPECS[cid].name}", file=sys.stderr, flush=True)
-    spec, routing, ge, weights, sets = make_inputs(cid, torch, W)
-    R = routing.rows
-    step = Step(torch, api, spec, ge, weights, spec.recipe, row_index=routing_index(routing, torch))
+    spec, topk, ids, weights, sets = make_inputs(cid, torch, W, api)
+    R = topk.rows
+    step = Step(torch, api, spec, ids, weights, spec.recipe)
+    group_sizes = torch.diff(step.ge.long(), prepend=step.ge.new_zeros(1).long()).cpu().numpy()
     torch.cuda.synchronize()
     print("# warmup", file=sys.stderr, flush=True)
     for i in range(args.warmup):
@@ -413,6 +481,7 @@ def main():
 
     gemm_ms = {k: sum(v) / len(v) for k, v in per.items() if k.startswith("gemm")}
     quant_ms = {k: sum(v) / len(v) for k, v in per.items() if k.startswith("quant")}
+    route_ms = sum(per["route"]) / len(per["route"])
     gemm_tflops = {k: flops[k] / (gemm_ms[k] * 1e-3) / 1e12 for k in gemm_ms}
     quant_gbs = {k: byts[k] / (quant_ms[k] * 1e-3) / 1e9 for k in quant_ms}
     gemm_total_ms = sum(gemm_ms.values())
@@ -423,7 +492,7 @@ def main():
     achieved = step_flops / (gemm_total_ms * 1e-3) / 1e12
     quant_agg = sum(byts.values()) / (quant_total_ms * 1e-3) / 1e9
     peak = PEAK_FP4_TFLOPS if step.fp4 else PEAK_FP8_TFLOPS
-    att = attainable_ms(spec, routing.group_sizes, spec.modes, peak, 0.5 if step.fp4 else 1.0)
+    att = attainable_ms(spec, group_sizes, spec.modes, peak, 0.5 if step.fp4 else 1.0)
     att_frac = {k: att[k] / gemm_ms[k] for k in gemm_ms}
     att_total = sum(att[k] for k in gemm_ms) / gemm_total_ms
 
@@ -451,6 +520,10 @@ def main():
     torch_copy_gbs = copy_rate(lambda: dst.copy_(src))
     del src, dst
     swiglu = None if args.no_swiglu else swiglu_quant_rate(torch, api, step, spec, R)
+    persistent = None
+    if args.micro_batches > 1:
+        persistent = persistent_weights_rate(torch, step, sets, args.micro_batches, step_flops, ms_step,
+                                             quant_ms)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -474,7 +547,7 @@ def main():
         "config": {"workload": spec.name, "experts": spec.experts, "tokens": spec.tokens,
                    "topk": spec.topk, "routed_rows": R, "hidden": spec.hidden, "ffn": spec.ffn,
                    "recipe": spec.recipe, "modes": list(spec.modes),
-                   "group_sizes": [int(x) for x in routing.group_sizes]},
+                   "group_sizes": [int(x) for x in group_sizes]},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(args.workload),
@@ -497,10 +570,12 @@ def main():
             "gemm_attainable_frac": {k: round(v, 4) for k, v in att_frac.items()},
             "gemm_attainable_frac_total": round(att_total, 4),
             "call_ms_p10_p50_p90": {k: percentiles(v) for k, v in per.items()},
+            "route_ms": round(route_ms, 4),
             "gemm_ms_total": round(gemm_total_ms, 4),
             "quant_ms_total": round(quant_total_ms, 4),
             "wall_s": round(wall, 3),
             "swiglu_quant": swiglu,
+            "persistent_weights": persistent,
         },
     }
     print(json.dumps(out), flush=True)

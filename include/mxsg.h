@@ -106,6 +106,7 @@ typedef int32_t mxsg_status;
 #define MXSG_STATUS_ENDS_RANGE 2      /* some group end outside [0, M] */
 #define MXSG_STATUS_ENDS_TOTAL 4      /* group_ends[E-1] != M (rows not covered exactly) */
 #define MXSG_STATUS_NONFINITE 8       /* an amax reduction met a NaN or Inf input element */
+#define MXSG_STATUS_BAD_EXPERT 16     /* mxsg_route met an expert id outside [0, E) */
 
 /* recipes */
 #define MXSG_RECIPE_TENSORWISE 0 /* one unit per 2-D tensor (per expert for weights), dynamic amax */
@@ -169,6 +170,32 @@ mxsg_status mxsg_quantize_act_sizes(int64_t M, int64_t C, int32_t recipe, int32_
  */
 mxsg_status mxsg_quantize_weight_sizes(int32_t E, int64_t K, int64_t N, int32_t recipe,
                                        int32_t fmt, int64_t bytes[4]);
+
+/*
+ * Routing permutation of the MoE dispatch, on the device. expert_ids is
+ * int32 [T, k] (device): the k experts token t was routed to (top-k
+ * choices, in choice order). Writes
+ *   group_ends int32 [E]: cumulative row ends of the expert groups, i.e.
+ *     group_ends[e] = number of choices with an id <= e (ids in [0, E));
+ *   row_index  int32 [T * k]: routed row i -> its token, rows grouped by
+ *     expert in ascending id and, within an expert, in (token, choice)
+ *     order (a stable order of the choices by expert id);
+ *   slot_row   int32 [T * k] (optional, NULL = not written): choice
+ *     t * k + j -> its routed row (the inverse map, for returning expert
+ *     outputs to their tokens).
+ * The result is the input the grouped GEMM and mxsg_quantize_act_gather
+ * take (row_index, group_ends with M = T * k): the pages hand the grouped
+ * matmul rows grouped by routed expert with cumulative offsets (torchao
+ * float8 MoE training PR, Summary and Limitations; Megatron-LM FP8-vs-BF16
+ * MoE bug report, additional context on TEGroupedMLP's per-expert inputs).
+ * A choice with an id outside [0, E) is not routed: it sets
+ * MXSG_STATUS_BAD_EXPERT in status_word (optional), its slot_row entry is
+ * -1, and the rows past group_ends[E-1] are filled with -1 (which the
+ * gather quantizer clamps to token 0; those rows lie outside every group).
+ * Limits: T * k < 2^31, 1 <= E <= 2^20. Uses no scratch memory.
+ */
+mxsg_status mxsg_route(const int32_t *expert_ids, int64_t T, int32_t k, int32_t E, int32_t *group_ends,
+                       int32_t *row_index, int32_t *slot_row, int32_t *status_word, mxsg_stream_t stream);
 
 /*
  * Quantize a token-major tensor x [M, C] (routed-row activations or output

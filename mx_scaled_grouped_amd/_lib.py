@@ -41,6 +41,7 @@ SIGNATURES = {
     "mxsg_grouped_mm": (_i32, [_i32, _i32, _i32, _i32, _i32, _i64, _i64, _i64, _c_p, _c_p, _c_p,
                                _c_p, _i64, _c_p, _c_p, _i64, _c_p, _i32, _c_p, _c_p]),
     "mxsg_cast_sweep": (_i32, [_u32, _i64, _i32, _c_p, _c_p]),
+    "mxsg_route": (_i32, [_c_p, _i64, _i32, _i32, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "mxsg_swiglu": (_i32, [_c_p, _i64, _i64, _c_p, _c_p]),
     "mxsg_sigmoid_sweep": (_i32, [_c_p, _c_p]),
     "mxsg_stream_copy": (_i32, [_c_p, _c_p, _i64, _c_p]),

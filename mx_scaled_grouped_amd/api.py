@@ -123,6 +123,7 @@ def pack_mx_scales(t: torch.Tensor) -> torch.Tensor:
 
 # status word bits (mxsg.h)
 STATUS_ENDS_DECREASING, STATUS_ENDS_RANGE, STATUS_ENDS_TOTAL, STATUS_NONFINITE = 1, 2, 4, 8
+STATUS_BAD_EXPERT = 16
 
 
 def _status_word(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
@@ -156,6 +157,38 @@ def _buffer(nbytes: int, dtype: torch.dtype, cols: int, dev) -> torch.Tensor:
     n = nbytes // torch.empty(0, dtype=dtype).element_size()
     t = torch.empty(n, dtype=dtype, device=dev)
     return t.view(-1, cols) if cols else t
+
+
+@dataclasses.dataclass
+class Route:
+    """Device routing of top-k choices (mxsg_route)."""
+    group_ends: torch.Tensor                 # int32 [E]
+    row_index: torch.Tensor                  # int32 [T * k]: routed row -> token
+    slot_row: Optional[torch.Tensor] = None  # int32 [T * k]: choice -> routed row
+
+
+def route(expert_ids: torch.Tensor, E: int, slot_row: bool = False, out: Optional[Route] = None,
+          status: Optional[torch.Tensor] = None) -> Route:
+    """Group the routed rows by expert on the device (mxsg_route).
+    ``expert_ids`` is int32 [T, k]; rows are ordered by expert, then token,
+    then choice. ``out`` reuses a previous Route's buffers."""
+    _check_dev(expert_ids, status)
+    if expert_ids.dtype != torch.int32 or expert_ids.dim() != 2:
+        raise TypeError("expert_ids must be a 2-D int32 tensor [T, k]")
+    T, k = expert_ids.shape
+    dev = expert_ids.device
+    if out is None:
+        out = Route(torch.empty(E, dtype=torch.int32, device=dev),
+                    torch.empty(T * k, dtype=torch.int32, device=dev),
+                    torch.empty(T * k, dtype=torch.int32, device=dev) if slot_row else None)
+    _check_dev(out.group_ends, out.row_index, out.slot_row)
+    _need(out.group_ends, 4 * E, "out.group_ends", torch.int32)
+    _need(out.row_index, 4 * T * k, "out.row_index", torch.int32)
+    if slot_row:
+        _need(out.slot_row, 4 * T * k, "out.slot_row", torch.int32)
+    _lib.call("mxsg_route", _ptr(expert_ids), T, k, E, _ptr(out.group_ends), _ptr(out.row_index),
+              _ptr(out.slot_row) if slot_row else None, _ptr(_status_word(status)), _stream())
+    return out
 
 
 @dataclasses.dataclass

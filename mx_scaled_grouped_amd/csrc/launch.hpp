@@ -62,6 +62,8 @@ hipError_t launch_quantize_weight(const QuantWeightParams &p, hipStream_t st);
 hipError_t launch_delayed_update(float *hist, int32_t *pos, float *amax, float *scale, float *inv,
                                  int units, int L, int fmt, hipStream_t st);
 hipError_t launch_cast_sweep(uint32_t start, int64_t n, int fmt, uint8_t *out, hipStream_t st);
+hipError_t launch_route(const int32_t *ids, int64_t T, int k, int E, int32_t *ends, int32_t *row_index,
+                        int32_t *slot_row, int32_t *status, hipStream_t st);
 hipError_t launch_swiglu(const uint16_t *x, int64_t M, int64_t C, uint16_t *y, hipStream_t st);
 hipError_t launch_sigmoid_sweep(float *out, hipStream_t st);
 hipError_t launch_stream_copy(const void *src, void *dst, int64_t bytes, hipStream_t st);

@@ -387,6 +387,18 @@ mxsg_status mxsg_cast_sweep(uint32_t start_bits, int64_t n, int32_t fmt, void *o
                   "cast_sweep");
 }
 
+mxsg_status mxsg_route(const int32_t *expert_ids, int64_t T, int32_t k, int32_t E, int32_t *group_ends,
+                       int32_t *row_index, int32_t *slot_row, int32_t *status_word, mxsg_stream_t stream) {
+  REQUIRE(T >= 0 && k >= 1 && E >= 1 && E <= (1 << 20), MXSG_INVALID_ARGUMENT,
+          "route: T=%lld k=%d E=%d", (long long)T, k, E);
+  REQUIRE(T <= (((int64_t)1 << 31) - 1) / k, MXSG_BAD_SHAPE, "route: T * k must be below 2^31");
+  REQUIRE(group_ends, MXSG_INVALID_ARGUMENT, "route: group_ends is NULL");
+  REQUIRE(T == 0 || (expert_ids && row_index), MXSG_INVALID_ARGUMENT, "route: NULL pointer");
+  return from_hip(mxsg::launch_route(expert_ids, T, k, E, group_ends, row_index, slot_row, status_word,
+                                     static_cast<hipStream_t>(stream)),
+                  "route");
+}
+
 mxsg_status mxsg_swiglu(const void *x, int64_t M, int64_t C, void *y, mxsg_stream_t stream) {
   REQUIRE(M >= 0 && C > 0 && C % 8 == 0, MXSG_BAD_SHAPE,
           "swiglu: M=%lld C=%lld (C must be a positive multiple of 8)", (long long)M, (long long)C);

@@ -8,6 +8,9 @@ CPU oracle (through the tests) and the HIP path can be fed from it.
 Every tensor is drawn with ``numpy.random.default_rng(SeedSequence([cid,
 tensor_id, step]))`` as float32, then rounded to bf16 (round to nearest
 even) and returned as uint16 bit patterns, the exact bits both sides see.
+Routing is drawn as each token's top-k expert choices; grouping the routed
+rows by expert is a step of the path (the device kernel, checked against
+the oracle), not done here.
 
 Workload shapes follow the problem statement of the float8 MoE training
 pages: a tiny four-expert case, a Mixtral-8x7B-shaped expert FFN (the
@@ -66,34 +69,28 @@ def normal_bf16(cid: int, tid: int, shape, std: float = 1.0, step: int = 0,
 
 
 @dataclasses.dataclass
-class Routing:
-    """Token -> expert assignment, sorted into expert-contiguous rows."""
+class TopK:
+    """Top-k expert choices of every token (the router's output, before the
+    routed rows are grouped by expert)."""
     n_tokens: int
     n_experts: int
-    row_token: np.ndarray    # int64 [R]: source token of each routed row
-    group_ends: np.ndarray   # int32 [E]: cumulative row ends (offs[E-1] == R)
+    expert_ids: np.ndarray   # int32 [T, k], in choice order
+
+    @property
+    def k(self) -> int:
+        return int(self.expert_ids.shape[1])
 
     @property
     def rows(self) -> int:
-        return int(self.row_token.shape[0])
-
-    @property
-    def group_sizes(self) -> np.ndarray:
-        return np.diff(np.concatenate([[0], self.group_ends.astype(np.int64)]))
-
-
-def _sort_rows(tok: np.ndarray, exp: np.ndarray, n_experts: int, n_tokens: int) -> Routing:
-    order = np.lexsort((tok, exp))            # stable by (expert, token)
-    counts = np.bincount(exp, minlength=n_experts)
-    return Routing(n_tokens, n_experts, tok[order].astype(np.int64),
-                   np.cumsum(counts).astype(np.int32))
+        return self.n_tokens * self.k
 
 
 def route_topk(cid: int, n_tokens: int, n_experts: int, k: int,
-               masked=(), uniform: bool = False) -> Routing:
+               masked=(), uniform: bool = False) -> TopK:
     """Top-k routing. uniform: k distinct experts uniformly at random;
     otherwise the k largest of N(0,1) logits (softmax does not change the
-    order), with ``masked`` experts never chosen. Ties go to the lower id."""
+    order), with ``masked`` experts never chosen. Ties go to the lower id.
+    Choices are listed by descending key."""
     rng = _rng(cid, T_LOGITS)
     if uniform:
         keys = rng.random((n_tokens, n_experts))
@@ -103,18 +100,16 @@ def route_topk(cid: int, n_tokens: int, n_experts: int, k: int,
         keys[:, e] = -np.inf
     # descending by key, ascending by expert id on ties
     order = np.lexsort((np.broadcast_to(np.arange(n_experts), keys.shape), -keys), axis=1)
-    chosen = order[:, :k]
-    tok = np.repeat(np.arange(n_tokens), k)
-    return _sort_rows(tok, chosen.reshape(-1), n_experts, n_tokens)
+    return TopK(n_tokens, n_experts, np.ascontiguousarray(order[:, :k]).astype(np.int32))
 
 
-def route_zipf(cid: int, n_tokens: int, n_experts: int, alpha: float) -> Routing:
+def route_zipf(cid: int, n_tokens: int, n_experts: int, alpha: float) -> TopK:
     """Top-1 routing with P(e) proportional to (e+1)^-alpha."""
     rng = _rng(cid, T_ROUTE)
     p = (np.arange(1, n_experts + 1, dtype=np.float64)) ** (-alpha)
     p /= p.sum()
     exp = rng.choice(n_experts, size=n_tokens, p=p)
-    return _sort_rows(np.arange(n_tokens), exp, n_experts, n_tokens)
+    return TopK(n_tokens, n_experts, exp.reshape(-1, 1).astype(np.int32))
 
 
 def group_ends_from_sizes(sizes) -> np.ndarray:
@@ -164,7 +159,8 @@ SPECS: Dict[int, WorkloadSpec] = {
 C4_MASKED = (0, 21, 42, 63)
 
 
-def routing_for(cid: int) -> Routing:
+def routing_for(cid: int) -> TopK:
+    """The workload's top-k expert choices."""
     s = SPECS[cid]
     if cid == 1:
         return route_topk(cid, s.tokens, s.experts, s.topk, uniform=True)
@@ -177,24 +173,26 @@ def routing_for(cid: int) -> Routing:
     raise KeyError(cid)
 
 
-def activation_bf16(cid: int, which: str, routing: Routing, step: int = 0) -> np.ndarray:
-    """Routed-row activation of GEMM ``which`` ("gu" input A1 or "dn" input A2).
-
-    A1 gathers token rows of x [tokens, hidden]; A2 is drawn per routed row.
-    C3 scales both by 1.01**step (drift), C5 multiplies 0.1% of elements by 50.
-    """
+def token_activation(cid: int, step: int = 0) -> np.ndarray:
+    """Token rows x [tokens, hidden] of the gate/up GEMM input (before the
+    routed rows are gathered). C3 scales by 1.01**step (drift), C5/C6
+    multiply 0.1% of elements by 50."""
     s = SPECS[cid]
-    K = s.gemm_shape(which)[0]
-    tid = T_X if which == "gu" else T_A2
     std = 1.01 ** step if cid == 3 else 1.0
-    if which == "gu":
-        x = normal_bf16(cid, tid, (s.tokens, K), std=std, step=step)
-        if cid in (5, 6):
-            x = _outliers(cid, tid, x)
-        return x[routing.row_token]
-    a = normal_bf16(cid, tid, (routing.rows, K), std=std, step=step)
+    x = normal_bf16(cid, T_X, (s.tokens, s.hidden), std=std, step=step)
     if cid in (5, 6):
-        a = _outliers(cid, tid, a)
+        x = _outliers(cid, T_X, x)
+    return x
+
+
+def down_activation(cid: int, rows: int, step: int = 0) -> np.ndarray:
+    """Routed-row input of the down GEMM [rows, ffn], drawn per row (same
+    drift and outliers as the token rows)."""
+    s = SPECS[cid]
+    std = 1.01 ** step if cid == 3 else 1.0
+    a = normal_bf16(cid, T_A2, (rows, s.ffn), std=std, step=step)
+    if cid in (5, 6):
+        a = _outliers(cid, T_A2, a)
     return a
 
 
@@ -216,11 +214,11 @@ def weight_bf16(cid: int, which: str) -> np.ndarray:
     return normal_bf16(cid, T_W1 if which == "gu" else T_W2, (s.experts, K, N), std=0.02)
 
 
-def grad_bf16(cid: int, which: str, routing: Routing, step: int = 0) -> np.ndarray:
-    """Output gradient dY [R, N] = N(0,1) * 2^-10 (a power of two keeps scale equivariance)."""
+def grad_bf16(cid: int, which: str, rows: int, step: int = 0) -> np.ndarray:
+    """Output gradient dY [rows, N] = N(0,1) * 2^-10 (a power of two keeps scale equivariance)."""
     s = SPECS[cid]
     N = s.gemm_shape(which)[1]
-    return normal_bf16(cid, T_DY1 if which == "gu" else T_DY2, (routing.rows, N),
+    return normal_bf16(cid, T_DY1 if which == "gu" else T_DY2, (rows, N),
                        std=2.0 ** -10, step=step)
 
 

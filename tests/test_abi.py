@@ -45,8 +45,9 @@ def test_status_bits_match_header():
     text = open(HEADER).read()
     bits = {k: int(v) for k, v in re.findall(r"#define MXSG_STATUS_(\w+) (\d+)", text)}
     assert bits == {"ENDS_DECREASING": api.STATUS_ENDS_DECREASING, "ENDS_RANGE": api.STATUS_ENDS_RANGE,
-                    "ENDS_TOTAL": api.STATUS_ENDS_TOTAL, "NONFINITE": api.STATUS_NONFINITE}
-    assert len(set(bits.values())) == 4 and all(v & (v - 1) == 0 for v in bits.values())
+                    "ENDS_TOTAL": api.STATUS_ENDS_TOTAL, "NONFINITE": api.STATUS_NONFINITE,
+                    "BAD_EXPERT": api.STATUS_BAD_EXPERT}
+    assert len(set(bits.values())) == 5 and all(v & (v - 1) == 0 for v in bits.values())
 
 
 def test_all_symbols_exported():
@@ -288,3 +289,26 @@ def test_blockwise_contraction_limit():
     assert _mm_check(recipe=2, K=65536 + 128, lda=65536 + 128, ldb=65536 + 128) == _lib.UNSUPPORTED
     assert _mm_check(mode=1, recipe=2, N=65536, lda=65536, ldb=65536) == _lib.OK
     assert _mm_check(mode=1, recipe=2, N=65536 + 128, lda=65536 + 128, ldb=65536 + 128) == _lib.UNSUPPORTED
+
+
+def test_route_validation():
+    """mxsg_route rejects bad sizes and missing outputs before any launch."""
+    st = _lib.status_of
+    p = ctypes.c_void_p(16)
+    assert st("mxsg_route", p, 10, 0, 4, p, p, None, None, None) == _lib.INVALID_ARGUMENT      # k = 0
+    assert st("mxsg_route", p, 10, 2, 0, p, p, None, None, None) == _lib.INVALID_ARGUMENT      # E = 0
+    assert st("mxsg_route", p, -1, 2, 4, p, p, None, None, None) == _lib.INVALID_ARGUMENT      # T < 0
+    assert st("mxsg_route", p, 1 << 30, 2, 4, p, p, None, None, None) == _lib.BAD_SHAPE        # T k >= 2^31
+    assert st("mxsg_route", p, 10, 2, 4, None, p, None, None, None) == _lib.INVALID_ARGUMENT   # no group_ends
+    assert st("mxsg_route", None, 10, 2, 4, p, p, None, None, None) == _lib.INVALID_ARGUMENT   # no ids
+    assert st("mxsg_route", p, 10, 2, 4, p, None, None, None, None) == _lib.INVALID_ARGUMENT   # no row_index
+
+
+def test_swiglu_and_sweep_validation():
+    st = _lib.status_of
+    p = ctypes.c_void_p(16)
+    assert st("mxsg_swiglu", p, 4, 12, p, None) == _lib.BAD_SHAPE             # C not a multiple of 8
+    assert st("mxsg_swiglu", p, -1, 8, p, None) == _lib.BAD_SHAPE
+    assert st("mxsg_swiglu", None, 4, 8, p, None) == _lib.INVALID_ARGUMENT
+    assert st("mxsg_swiglu", ctypes.c_void_p(8), 4, 8, p, None) == _lib.INVALID_ARGUMENT   # misaligned
+    assert st("mxsg_sigmoid_sweep", None, None) == _lib.INVALID_ARGUMENT

@@ -26,6 +26,7 @@ from oracle import quant as OQ
 from oracle import formats as OF
 from oracle import gemm as OG
 from oracle.delayed import DelayedState as ODelayed
+from oracle import routing as OR
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="no GPU")]
 
@@ -73,22 +74,34 @@ def _run(name):
     from mx_scaled_grouped_amd import api, workloads as W
     cid = bench.WORKLOADS[name]
     print(f"[fullsize] {name}: generating inputs", flush=True)
-    spec, routing, ge_t, weights, sets = bench.make_inputs(cid, torch, W)
-    step = bench.Step(torch, api, spec, ge_t, weights, spec.recipe,
-                      row_index=bench.routing_index(routing, torch))
+    spec, topk, ids, weights, sets = bench.make_inputs(cid, torch, W, api)
+    step = bench.Step(torch, api, spec, ids, weights, spec.recipe)
     step.run(sets[0])
     step.run(sets[1])
     torch.cuda.synchronize()
     print(f"[fullsize] {name}: two steps done", flush=True)
-    st = {"spec": spec, "ge": routing.group_ends.astype(np.int64), "step": step,
+    # the step's device routing is the oracle's grouping of the same choices;
+    # the oracle side uses its own routing (and gathers the token rows itself)
+    ro = OR.route(topk.expert_ids, spec.experts)
+    assert np.array_equal(_np(step.rt.group_ends).astype(np.int64), ro["group_ends"]), "group ends"
+    assert np.array_equal(_np(step.rt.row_index).astype(np.int64), ro["row_index"]), "routed row order"
+    st = {"spec": spec, "ge": ro["group_ends"], "row_index": ro["row_index"], "step": step,
           "weights": weights, "sets": sets, "recipe": step.recipe}
     if spec.recipe == "dl":
-        st["scales"] = _oracle_delayed(step, spec, weights, sets)
+        st["scales"] = _oracle_delayed(step, spec, weights, sets, st["row_index"])
     _cache[name] = st
     return st
 
 
-def _oracle_delayed(step, spec, weights, sets):
+def _act(d, which, row_index):
+    """Host bf16 bits of a step's routed activation: the gate/up input is the
+    token rows gathered with the oracle's routing."""
+    if which == "gu":
+        return _bits(d["x_gu"])[row_index]
+    return _bits(d["a_" + which])
+
+
+def _oracle_delayed(step, spec, weights, sets, row_index):
     """Replay the delayed-scaling state in the oracle over both steps; check the
     GPU state after them; return the (s, inv) each unit used in step 2."""
     ng, E = len(spec.gemms), spec.experts
@@ -102,7 +115,7 @@ def _oracle_delayed(step, spec, weights, sets):
     used = None
     for s in (0, 1):
         d = sets[s]
-        a_amax = [OQ.amax_of(OQ.bf16_to_f32(_bits(d["a_" + wh]))) for wh in spec.gemms]
+        a_amax = [OQ.amax_of(OQ.bf16_to_f32(_act(d, wh, row_index))) for wh in spec.gemms]
         g_amax = [OQ.amax_of(OQ.bf16_to_f32(_bits(d["dy_" + wh]))) for wh in spec.gemms]
         if s == 1:
             used = {"f": (sf.s.copy(), sf.inv.copy()), "g": (sg.s.copy(), sg.inv.copy())}
@@ -203,7 +216,7 @@ def check_forward(name, which):
     spec, step, ge = st["spec"], st["step"], st["ge"]
     K, N = spec.gemm_shape(which)
     fa = FMT[step.fa]
-    a_bits = _bits(st["sets"][1]["a_" + which])
+    a_bits = _act(st["sets"][1], which, st["row_index"])
     w_bits = _bits(st["weights"][which])
     rows, ge_s = _row_sample(ge, 11)
     ncols, nblk = _block_sample(N, 12)
@@ -270,7 +283,7 @@ def check_wgrad(name, which):
     K, N = spec.gemm_shape(which)
     E = spec.experts
     fa, fg = FMT[step.fa], FMT[step.fg]
-    a_bits = _bits(st["sets"][1]["a_" + which])
+    a_bits = _act(st["sets"][1], which, st["row_index"])
     d_bits = _bits(st["sets"][1]["dy_" + which])
     kcols, _ = _block_sample(K, 31)
     ncols, _ = _block_sample(N, 32)

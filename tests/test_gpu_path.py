@@ -85,11 +85,14 @@ def run_path(a, w, dy, ge, recipe, fa, fw, fg, modes, sqnr_min=25.0):
 def test_tiny_config_full():
     """The tiny workload (4 experts, hidden 256, ffn 512, 512 tokens top-2,
     tensorwise e4m3, forward) end to end at its real size."""
-    r = W.routing_for(1)
-    a = W.activation_bf16(1, "gu", r)
+    from oracle import routing as OR
+    topk = W.routing_for(1)
+    r = OR.route(topk.expert_ids, topk.n_experts)
+    a = W.token_activation(1)[r["row_index"]]
     w = W.weight_bf16(1, "gu")
-    print(f"tiny config: rows={r.rows} groups={r.group_sizes.tolist()}", flush=True)
-    run_path(a, w, None, r.group_ends, "tw", 0, 0, 0, ("fwd",))
+    ge = r["group_ends"].astype(np.int32)
+    print(f"tiny config: rows={topk.rows} group ends={ge.tolist()}", flush=True)
+    run_path(a, w, None, ge, "tw", 0, 0, 0, ("fwd",))
 
 
 @pytest.mark.parametrize("recipe,fg", [("tw", 1), ("block", 0), ("mx", 0)])
