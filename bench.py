@@ -65,65 +65,65 @@ def parse():
 # synthetic inputs (generated on the GPU with torch's seeded generator; the
 # distributions and routing follow mx_scaled_grouped_amd.workloads)
 
+def _normal(torch, g, shape, std):
+    """bf16 N(0, std^2) draws on the GPU from generator g."""
+    t = torch.randn(shape, generator=g, device="cuda", dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    return t.to(torch.bfloat16)
+
+
+def _outliers(torch, g, cid, t):
+    """Llama4-shaped workloads: 0.1% of the elements, drawn without
+    replacement, multiplied by 50."""
+    if cid not in (5, 6):
+        return t
+    flat = t.view(-1)
+    n = flat.numel()
+    idx = torch.randperm(n, generator=g, device="cuda")[:max(1, n // 1000)]
+    flat[idx] = (flat[idx].float() * 50.0).to(torch.bfloat16)
+    return t
+
+
 def make_inputs(cid, torch, W, api, sets=2):
     """Seeded inputs on the GPU: the top-k expert choices (device int32
     [T, k]), the weights and `sets` sets of activations and gradients. The
     routed rows of the gate/up input are gathered from the token rows by the
     step itself (routing kernel, then the gathering quantizer); `a_gu`, an
-    explicit gathered copy made here with the device routing, is for checks
-    and for callers that want the gathered tensor."""
+    explicit gathered copy made here with the device routing, is for callers
+    that want the gathered tensor."""
     spec = W.SPECS[cid]
     topk = W.routing_for(cid)
-    dev = "cuda"
-    g = torch.Generator(device=dev)
+    g = torch.Generator(device="cuda")
     g.manual_seed(1000 + cid)
-    R = topk.rows
-    ids = torch.from_numpy(topk.expert_ids).to(dev)
+    ids = torch.from_numpy(topk.expert_ids).to("cuda")
     row_token = api.route(ids, spec.experts).row_index
-
-    def normal(shape, std):
-        t = torch.randn(shape, generator=g, device=dev, dtype=torch.float32)
-        if std != 1.0:
-            t.mul_(std)
-        return t.to(torch.bfloat16)
-
-    def outliers(t):
-        # 0.1% of the elements, drawn without replacement, multiplied by 50
-        if cid not in (5, 6):
-            return t
-        flat = t.view(-1)
-        n = flat.numel()
-        idx = torch.randperm(n, generator=g, device=dev)[:max(1, n // 1000)]
-        flat[idx] = (flat[idx].float() * 50.0).to(torch.bfloat16)
-        return t
-
     gu_k, gu_n = spec.gemm_shape("gu")
     dn_k, dn_n = spec.gemm_shape("dn")
-    weights = {"gu": normal((spec.experts, gu_k, gu_n), 0.02)}
+    weights = {"gu": _normal(torch, g, (spec.experts, gu_k, gu_n), 0.02)}
     if "dn" in spec.gemms:
-        weights["dn"] = normal((spec.experts, dn_k, dn_n), 0.02)
-    sets_out = []
-    for s in range(sets):
-        sets_out.append(make_set(cid, spec, R, s, normal, outliers, row_token))
+        weights["dn"] = _normal(torch, g, (spec.experts, dn_k, dn_n), 0.02)
+    sets_out = [make_set(torch, g, cid, spec, topk.rows, s, row_token) for s in range(sets)]
     return spec, topk, ids, weights, sets_out
 
 
-def make_set(cid, spec, R, s, normal, outliers, row_token):
-    """One input set (drift 1.01^s for the delayed-scaling workload)."""
+def make_set(torch, g, cid, spec, R, s, row_token):
+    """Input set s (activations scaled by 1.01^s for the delayed-scaling
+    workload, whose activations drift from step to step)."""
     gu_k, gu_n = spec.gemm_shape("gu")
     dn_k, dn_n = spec.gemm_shape("dn")
     drift = 1.01 ** s if cid == 3 else 1.0
-    x = outliers(normal((spec.tokens, gu_k), drift))
+    x = _outliers(torch, g, cid, _normal(torch, g, (spec.tokens, gu_k), drift))
     # x_gu: the token tensor the step quantizes through the routing index
     # (gather fused into the quantization); a_gu: the same routed rows as
     # an explicit copy
     d = {"x_gu": x, "a_gu": x.index_select(0, row_token).contiguous()}
     if "dn" in spec.gemms:
-        d["a_dn"] = outliers(normal((R, dn_k), drift))
+        d["a_dn"] = _outliers(torch, g, cid, _normal(torch, g, (R, dn_k), drift))
     if "dgrad" in spec.modes:
-        d["dy_gu"] = normal((R, gu_n), 2.0 ** -10)
+        d["dy_gu"] = _normal(torch, g, (R, gu_n), 2.0 ** -10)
         if "dn" in spec.gemms:
-            d["dy_dn"] = normal((R, dn_n), 2.0 ** -10)
+            d["dy_dn"] = _normal(torch, g, (R, dn_n), 2.0 ** -10)
     return d
 
 

@@ -67,6 +67,19 @@ def amax_of(x_f32) -> np.float32:
     return np.float32(np.max(np.abs(x)))
 
 
+def amax_of_bf16_bits(bits, chunk: int = 1 << 24) -> np.float32:
+    """max |x| over bf16 bit patterns of finite values, exactly, without
+    widening to float32: a finite bf16 value's magnitude is ordered as its
+    low 15 bits (exponent above mantissa), so the largest magnitude is the
+    value of the largest masked pattern. Chunked, for tensors of billions of
+    elements."""
+    b = np.asarray(bits, np.uint16).reshape(-1)
+    m = np.uint16(0)
+    for i in range(0, b.size, chunk):
+        m = max(m, np.max(b[i:i + chunk] & np.uint16(0x7FFF)))
+    return np.float32(bf16_to_f32(np.array([m], np.uint16))[0])
+
+
 def fp32_scale_pair(amax, fmt: Fp8Format):
     """(s, inv) as float32 for the fp32-scaled recipes: s = amax/fmax, inv = fmax/amax.
 

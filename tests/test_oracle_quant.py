@@ -334,3 +334,16 @@ def test_delayed_saturation_count():
         if t >= 1:
             assert n_sat >= over >= at
         st.update(q["amax"])
+
+
+def test_amax_of_bf16_bits_matches_amax_of_values():
+    """The bit-pattern amax equals max |x| of the widened values, including
+    subnormals, signed zeros, the largest finite bf16 and chunk edges."""
+    rng = np.random.default_rng(12)
+    for n, chunk in ((1, 4), (1000, 7), (4096, 1 << 24)):
+        x = rng.standard_normal(n).astype(np.float32) * np.float32(10.0) ** rng.integers(-40, 38, n).astype(np.float32)
+        b = W.bf16_bits(np.nan_to_num(x, posinf=1e38, neginf=-1e38))
+        assert Q.amax_of_bf16_bits(b, chunk) == Q.amax_of(Q.bf16_to_f32(b))
+    special = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x7F7F, 0xFF7F, 0x3F80], np.uint16)
+    assert Q.amax_of_bf16_bits(special) == Q.amax_of(Q.bf16_to_f32(special)) == Q.bf16_to_f32(np.uint16(0x7F7F))
+    assert Q.amax_of_bf16_bits(np.array([0x8000, 0x0000], np.uint16)) == 0
