@@ -216,7 +216,7 @@ __host__ __device__ constexpr int mfma_fmt(int f) { return f == kE2M1 ? 4 : f; }
 template <int RECIPE>
 constexpr int gemm_waves() { return RECIPE == kBlockwise ? 8 : 4; }
 
-template <int MODE, int RECIPE, int FA, int FB, int BN>
+template <int MODE, int RECIPE, int FA, int FB, int BN, bool ACC>
 __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel(GemmArgs a) {
   constexpr int NW = gemm_waves<RECIPE>();
   constexpr int NT = 64 * NW;        // threads
@@ -655,9 +655,9 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
     const float sb = reinterpret_cast<const float *>(a.b_scales)[MODE == kWgrad ? 0 : g];
     scale = sa * sb;
   }
-  if (MODE == kWgrad && a.accumulate && nsteps == 0) continue;  // empty group: dW_g unchanged
+  if (ACC && nsteps == 0) continue;  // empty group: dW_g unchanged
   constexpr int STR = WN + 8;          // LDS row stride in floats
-  constexpr int CPR = WN / 8;          // 8-float chunks per row
+  constexpr int CPR = WN / 8;          // 8-value chunks per row (bf16 outputs: 16 bytes)
   constexpr int CPL = 16 * CPR / 64;   // chunks per lane per half slab
   // (eight waves: two slabs in each A stage buffer)
   const int cw = NW == 4 ? wave : wave >> 1;
@@ -675,6 +675,42 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
         for (int v = 8 * hs; v < 8 * hs + 8; ++v)
           cb[(((v >> 2) & 1) * 8 + h * 4 + (v & 3)) * STR + ni * 32 + l32] = acc[mi][ni][v];
       __builtin_amdgcn_wave_barrier();
+      if constexpr (MODE == kWgrad) {
+        // fp32 dW: 16-byte chunks, WN / 4 per row, so that one store
+        // instruction writes whole 512-byte pieces of two rows (measured 4-6%
+        // faster for wgrad than two interleaved 16-byte halves of 32-byte
+        // chunks). Accumulating (a separate kernel instance, so the plain
+        // one keeps its registers): every old value is loaded before the
+        // first store, so no load waits behind an earlier store.
+        constexpr int CPR4 = WN / 4;
+        constexpr int CPL4 = 16 * CPR4 / 64;
+        float4 old[ACC ? CPL4 : 1];
+        if constexpr (ACC) {
+#pragma unroll
+          for (int k = 0; k < CPL4; ++k) {
+            const int id = k * 64 + lane;
+            const int64_t i = i0 + wi * WM + mi * 32 + hs * 16 + id / CPR4;
+            const int64_t j = jw + (id % CPR4) * 4;
+            old[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (i >= ilo && i < ihi && j < a.J)
+              old[k] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.out) +
+                                                         ((int64_t)g * a.I + i) * a.ldo + j);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < CPL4; ++k) {
+          const int id = k * 64 + lane;
+          const int r = id / CPR4, c4 = id % CPR4;
+          const int64_t i = i0 + wi * WM + mi * 32 + hs * 16 + r;
+          const int64_t j = jw + c4 * 4;
+          const float4 x = *reinterpret_cast<const float4 *>(&cb[r * STR + c4 * 4]);
+          if (i >= ilo && i < ihi && j < a.J) {  // J % 128 == 0: a chunk is all in or all out
+            float4 y = make_float4(x.x * scale, x.y * scale, x.z * scale, x.w * scale);
+            if constexpr (ACC) y = make_float4(y.x + old[k].x, y.y + old[k].y, y.z + old[k].z, y.w + old[k].w);
+            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.out) + ((int64_t)g * a.I + i) * a.ldo + j) = y;
+          }
+        }
+      } else {
 #pragma unroll
       for (int k = 0; k < CPL; ++k) {
         const int id = k * 64 + lane;
@@ -684,31 +720,18 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
         const float4 x0 = *reinterpret_cast<const float4 *>(&cb[r * STR + c8 * 8]);
         const float4 x1 = *reinterpret_cast<const float4 *>(&cb[r * STR + c8 * 8 + 4]);
         if (i >= ilo && i < ihi && j < a.J) {  // J % 128 == 0: a chunk is all in or all out
-          if (MODE == kWgrad) {
-            float4 y0 = make_float4(x0.x * scale, x0.y * scale, x0.z * scale, x0.w * scale);
-            float4 y1 = make_float4(x1.x * scale, x1.y * scale, x1.z * scale, x1.w * scale);
-            float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.out) +
-                                                     ((int64_t)g * a.I + i) * a.ldo + j);
-            if (a.accumulate) {
-              const float4 o0 = dst[0], o1 = dst[1];
-              y0 = make_float4(y0.x + o0.x, y0.y + o0.y, y0.z + o0.z, y0.w + o0.w);
-              y1 = make_float4(y1.x + o1.x, y1.y + o1.y, y1.z + o1.z, y1.w + o1.w);
-            }
-            dst[0] = y0;
-            dst[1] = y1;
-          } else {
-            uint4 o;
-            o.x = f32_to_bf16_bits(x0.x * scale) | (f32_to_bf16_bits(x0.y * scale) << 16);
-            o.y = f32_to_bf16_bits(x0.z * scale) | (f32_to_bf16_bits(x0.w * scale) << 16);
-            o.z = f32_to_bf16_bits(x1.x * scale) | (f32_to_bf16_bits(x1.y * scale) << 16);
-            o.w = f32_to_bf16_bits(x1.z * scale) | (f32_to_bf16_bits(x1.w * scale) << 16);
-            uint16_t *dst = reinterpret_cast<uint16_t *>(a.out) + i * a.ldo + j;
-            if (a.stream_out)
-              store16_stream(dst, o);
-            else
-              *reinterpret_cast<uint4 *>(dst) = o;
-          }
+          uint4 o;
+          o.x = f32_to_bf16_bits(x0.x * scale) | (f32_to_bf16_bits(x0.y * scale) << 16);
+          o.y = f32_to_bf16_bits(x0.z * scale) | (f32_to_bf16_bits(x0.w * scale) << 16);
+          o.z = f32_to_bf16_bits(x1.x * scale) | (f32_to_bf16_bits(x1.y * scale) << 16);
+          o.w = f32_to_bf16_bits(x1.z * scale) | (f32_to_bf16_bits(x1.w * scale) << 16);
+          uint16_t *dst = reinterpret_cast<uint16_t *>(a.out) + i * a.ldo + j;
+          if (a.stream_out)
+            store16_stream(dst, o);
+          else
+            *reinterpret_cast<uint4 *>(dst) = o;
         }
+      }
       }
       __builtin_amdgcn_wave_barrier();
     }
@@ -746,7 +769,10 @@ static hipError_t launch_cfg(const GemmArgs &a0, hipStream_t st) {
     const int64_t persistent = (int64_t)(ncu / 8) * 8;
     grid = nblocks < persistent ? nblocks : persistent;
   }
-  grouped_gemm_kernel<MODE, RECIPE, FA, FB, BN><<<(unsigned)grid, 64 * gemm_waves<RECIPE>(), 0, st>>>(a);
+  if (MODE == kWgrad && a.accumulate)
+    grouped_gemm_kernel<MODE, RECIPE, FA, FB, BN, true><<<(unsigned)grid, 64 * gemm_waves<RECIPE>(), 0, st>>>(a);
+  else
+    grouped_gemm_kernel<MODE, RECIPE, FA, FB, BN, false><<<(unsigned)grid, 64 * gemm_waves<RECIPE>(), 0, st>>>(a);
   return hipGetLastError();
 }
 
