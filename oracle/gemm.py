@@ -27,8 +27,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import Fp8Format, decode, e8m0_value
-from .quant import BLOCK, MX_BLOCK, group_starts
+from .formats import Fp8Format, E4M3, decode, e8m0_value
+from .quant import BLOCK, MX_BLOCK, NV_BLOCK, group_starts
 
 
 # ---- dequantization --------------------------------------------------------
@@ -39,9 +39,13 @@ def _expand(scales, rows: int, cols: int, blk: int) -> np.ndarray:
 
 
 def deq_act_rows(codes, scales, recipe: str, fmt: Fp8Format) -> np.ndarray:
-    """float64 [M, C] of a row-wise quantized token tensor."""
+    """float64 [M, C] of a row-wise quantized token tensor. For nvfp4,
+    ``scales`` is (e4m3 block codes [M, C/16], tensor scale)."""
     v = decode(codes, fmt)
     M, C = v.shape
+    if recipe == "nvfp4":
+        blocks, s_t = scales
+        return v * _expand(decode(blocks, E4M3), M, C, NV_BLOCK) * float(np.asarray(s_t).reshape(-1)[0])
     if recipe in ("tw", "dl"):
         return v * float(np.asarray(scales).reshape(-1)[0])
     if recipe == "block":
@@ -68,7 +72,10 @@ def deq_weight(q: dict, recipe: str, fmt: Fp8Format, layout: str) -> np.ndarray:
         scales = q["nmajor_scales"]
     v = decode(codes, fmt)
     E = v.shape[0]
-    if recipe in ("tw", "dl"):
+    if recipe == "nvfp4":
+        s_t = np.asarray(q["tensor_scale"], np.float64).reshape(E, 1, 1)
+        d = v * np.repeat(decode(scales, E4M3), NV_BLOCK, axis=2) * s_t
+    elif recipe in ("tw", "dl"):
         d = v * np.asarray(scales, np.float64).reshape(E, 1, 1)
     elif recipe == "block":
         s = np.asarray(scales, np.float64)              # [E, K/128, N/128]

@@ -49,7 +49,9 @@ from .formats import Fp8Format, encode_sat_rne, E8M0_BIAS
 
 BLOCK = 128      # DeepSeek-style block length (the Transformer Engine issue's block size)
 MX_BLOCK = 32    # MXFP8 block length (OCP MX v1.0)
-RECIPES = ("tw", "dl", "block", "mx")
+NV_BLOCK = 16    # NVFP4 block length (16 e2m1 elements share an e4m3 scale)
+NV_TENSOR_DEN = 2688.0   # 6 * 448: the largest e2m1 value times the largest e4m3 value
+RECIPES = ("tw", "dl", "block", "mx", "nvfp4")
 
 
 def bf16_to_f32(b) -> np.ndarray:
@@ -133,6 +135,86 @@ def cast(x_f32, inv, fmt: Fp8Format) -> np.ndarray:
     return encode_sat_rne(prod, fmt)
 
 
+# ---- NVFP4: e2m1 elements, e4m3 scale per 16 elements, fp32 scale per tensor ----
+#
+# The single-grouped-weight PR tests an NVFP4 recipe next to MXFP8 and MXFP4
+# (coverage table: fp4 = e2m1 with the nvfp4 recipe). The pages give no
+# formula; the reading taken (the two-level scheme of the public NVFP4
+# format, each step one IEEE fp32 operation):
+#   tensor unit (an activation tensor; one expert of a weight): amax_t,
+#     s_t = fp32(amax_t / 2688), or 1 when amax_t == 0;
+#   block of 16 consecutive elements along the contraction dim: amax_b,
+#     t_b = fp32(fp32(amax_b / 6) / s_t), block code sb = e4m3 sat_rne(t_b),
+#     D = value(sb), M_b = fp32(D * s_t), inv_b = fp32(1 / M_b) (0 when
+#     M_b == 0 or 1 / M_b overflows);
+#   element code q = e2m1 sat_rne(fp32(x * inv_b));
+#   value: e2m1(q) * D * s_t (exact; the oracle dequantizes in float64).
+
+def nvfp4_tensor_scale(amax) -> np.ndarray:
+    """s_t = fp32(amax / 2688) per unit (1 for amax == 0)."""
+    a = np.asarray(amax, np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return np.where(a > 0, a / np.float32(NV_TENSOR_DEN), np.float32(1.0)).astype(np.float32)
+
+
+def nvfp4_blocks(xb, s_t):
+    """Codes and e4m3 block codes of blocks along the last axis: xb float32
+    [..., nb, 16] (zero-filled where a block is partial), s_t broadcastable
+    to [..., nb]. Returns (codes u8 [..., nb, 16], block codes u8 [..., nb])."""
+    from .formats import E4M3, E2M1, decode
+    xb = np.asarray(xb, np.float32)
+    am = np.max(np.abs(xb), axis=-1) if xb.shape[-1] else np.zeros(xb.shape[:-1], np.float32)
+    s_t = np.asarray(s_t, np.float32)
+    d6 = (am / np.float32(6.0)).astype(np.float32)
+    t_b = (d6 / s_t).astype(np.float32)
+    sb = encode_sat_rne(t_b, E4M3)
+    D = decode(sb, E4M3).astype(np.float32)
+    m_b = (D * s_t).astype(np.float32)
+    with np.errstate(divide="ignore", over="ignore"):
+        inv = np.where(m_b > 0, np.float32(1.0) / np.where(m_b > 0, m_b, np.float32(1.0)), np.float32(0.0))
+    inv = np.where(np.isfinite(inv), inv, np.float32(0.0)).astype(np.float32)
+    return cast(xb, inv[..., None], E2M1), sb
+
+
+def _nvfp4_act(x, group_ends, rowwise, colwise) -> dict:
+    M, C = x.shape
+    am = amax_of(x)
+    s_t = nvfp4_tensor_scale(am)
+    out = {"amax": np.array([am], np.float32), "tensor_scale": np.array([s_t], np.float32)}
+    if rowwise:
+        codes, sb = nvfp4_blocks(x.reshape(M, C // NV_BLOCK, NV_BLOCK), s_t)
+        out["row_codes"] = codes.reshape(M, C)
+        out["row_scales"] = sb
+    if colwise:
+        check_groups(group_ends, M)
+        P = padded_starts(group_ends)
+        st = group_starts(group_ends)
+        ge = np.asarray(group_ends, dtype=np.int64)
+        Rp = int(P[-1])
+        xp = np.zeros((Rp, C), np.float32)                 # padded token layout, zero fill
+        for g in range(len(P) - 1):
+            m = int(ge[g] - st[g])
+            xp[P[g]:P[g] + m] = x[st[g]:st[g] + m]
+        # 16x1 blocks along the padded tokens; a group's first token starts a block
+        codes, sb = nvfp4_blocks(xp.T.reshape(C, Rp // NV_BLOCK, NV_BLOCK), s_t)
+        out["padded_starts"] = P
+        out["col_codes"] = codes.reshape(C, Rp)
+        out["col_scales"] = sb
+    return out
+
+
+def _nvfp4_weight(w) -> dict:
+    E, K, N = w.shape
+    am = np.array([amax_of(w[e]) for e in range(E)], np.float32)
+    s_t = nvfp4_tensor_scale(am)
+    cn, sn = nvfp4_blocks(w.reshape(E, K, N // NV_BLOCK, NV_BLOCK), s_t[:, None, None])
+    wt = np.ascontiguousarray(w.transpose(0, 2, 1))                  # [E, N, K]
+    ck, sk = nvfp4_blocks(wt.reshape(E, N, K // NV_BLOCK, NV_BLOCK), s_t[:, None, None])
+    return {"amax": am, "tensor_scale": s_t,
+            "nmajor_codes": cn.reshape(E, K, N), "nmajor_scales": sn,
+            "kmajor_codes": ck.reshape(E, N, K), "kmajor_scales": sk}
+
+
 # ---- group layout -----------------------------------------------------------
 
 def group_starts(group_ends) -> np.ndarray:
@@ -163,11 +245,13 @@ def quantize_act(x_bf16, recipe: str, fmt: Fp8Format, group_ends=None,
                  dl_scale: Optional[tuple] = None) -> dict:
     """Quantize a token-major tensor [M, C] (C = the feature dimension).
 
-    Returns a dict with ``amax`` (tw/dl), ``row_codes`` [M, C] u8 and
+    Returns a dict with ``amax`` (tw/dl/nvfp4), ``row_codes`` [M, C] u8 and
     ``row_scales``; with colwise also ``padded_starts`` [E+1],
     ``col_codes`` [C, P_E] u8 and ``col_scales``. Scale layouts:
     tw/dl: float32 [1]; block: rows [M, C/128], cols [C, P_E/128];
-    mx: uint8 E8M0 rows [M, C/32], cols [C, P_E/32].
+    mx: uint8 E8M0 rows [M, C/32], cols [C, P_E/32]; nvfp4 (e2m1 codes):
+    uint8 e4m3 block codes rows [M, C/16], cols [C, P_E/16], plus
+    ``tensor_scale`` float32 [1].
     dl_scale = (s, inv) float32 from the delayed-scaling state.
     """
     x_bf16 = np.asarray(x_bf16, dtype=np.uint16)
@@ -178,6 +262,8 @@ def quantize_act(x_bf16, recipe: str, fmt: Fp8Format, group_ends=None,
     if C % BLOCK != 0:
         raise ValueError("feature dim must be a multiple of 128")
     x = bf16_to_f32(x_bf16)
+    if recipe == "nvfp4":
+        return _nvfp4_act(x, group_ends, rowwise, colwise)
     out = {}
     if recipe in ("tw", "dl"):
         am = amax_of(x)
@@ -288,7 +374,9 @@ def quantize_weight(w_bf16, recipe: str, fmt: Fp8Format, dl_scale=None) -> dict:
     scales: tw/dl: float32 [E] for both (and ``amax`` [E]); block: 128x128
     tiles, float32 [E, K/128, N/128] for both (one code set, two layouts);
     mx: two code sets, ``kmajor_scales`` [E, N, K/32] (blocks along K) and
-    ``nmajor_scales`` [E, K, N/32] (blocks along N).
+    ``nmajor_scales`` [E, K, N/32] (blocks along N); nvfp4: two e2m1 code
+    sets with e4m3 block codes [E, N, K/16] and [E, K, N/16] and
+    ``tensor_scale`` float32 [E] (one per expert, shared by both).
     dl_scale = (s[E], inv[E]) from the delayed-scaling state.
     """
     w_bf16 = np.asarray(w_bf16, dtype=np.uint16)
@@ -296,6 +384,8 @@ def quantize_weight(w_bf16, recipe: str, fmt: Fp8Format, dl_scale=None) -> dict:
     if K % BLOCK or N % BLOCK:
         raise ValueError("K and N must be multiples of 128")
     w = bf16_to_f32(w_bf16)
+    if recipe == "nvfp4":
+        return _nvfp4_weight(w)
     out = {}
     if recipe in ("tw", "dl"):
         am = np.array([amax_of(w[e]) for e in range(E)], np.float32)

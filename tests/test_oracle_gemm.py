@@ -25,6 +25,8 @@ def _unit_scale_act(q, recipe, r, c, layout="row"):
         return float(sc[0])
     if recipe == "block":
         return float(sc[r][c // 128])
+    if recipe == "nvfp4":
+        return F.decode_value(F.E4M3, int(sc[r][c // 16])) * float(q["tensor_scale"][0])
     return 2.0 ** (int(sc[r][c // 32]) - 127)
 
 
@@ -33,14 +35,24 @@ def _unit_scale_w(q, recipe, e, k, n, layout):
         return float(q["kmajor_scales"][e])
     if recipe == "block":
         return float(q["kmajor_scales"][e][k // 128][n // 128])
+    if recipe == "nvfp4":
+        b = q["kmajor_scales"][e][n][k // 16] if layout == "k" else q["nmajor_scales"][e][k][n // 16]
+        return F.decode_value(F.E4M3, int(b)) * float(q["tensor_scale"][e])
     if layout == "k":
         return 2.0 ** (int(q["kmajor_scales"][e][n][k // 32]) - 127)
     return 2.0 ** (int(q["nmajor_scales"][e][k][n // 32]) - 127)
 
 
+def _sc(q, key, recipe):
+    """The scales argument of the oracle's dequantization (nvfp4: block codes
+    and the tensor scale)."""
+    return (q[key], q["tensor_scale"]) if recipe == "nvfp4" else q[key]
+
+
 @pytest.mark.parametrize("recipe,fa,fg", [("tw", F.E4M3, F.E5M2), ("block", F.E4M3, F.E4M3),
-                                          ("mx", F.E4M3, F.E4M3), ("mx", F.E2M1, F.E2M1)],
-                         ids=["tw", "block", "mx", "mxfp4"])
+                                          ("mx", F.E4M3, F.E4M3), ("mx", F.E2M1, F.E2M1),
+                                          ("nvfp4", F.E2M1, F.E2M1)],
+                         ids=["tw", "block", "mx", "mxfp4", "nvfp4"])
 def test_brute_force_tiny(recipe, fa, fg):
     """Forward, dgrad and wgrad of E=3, m = {0, 5, 13}, K=N=128 by triple loops."""
     sizes = [0, 5, 13]
@@ -73,7 +85,7 @@ def test_brute_force_tiny(recipe, fa, fg):
     Wnq = [[[Wn(e, k, n) for n in range(N)] for k in range(K)] for e in range(E)]
 
     # forward
-    Y = G.grouped_fwd(G.deq_act_rows(qa["row_codes"], qa["row_scales"], recipe, fa),
+    Y = G.grouped_fwd(G.deq_act_rows(qa["row_codes"], _sc(qa, "row_scales", recipe), recipe, fa),
                       G.deq_weight(qw, recipe, fa, "k"), ge)
     for r in range(R):
         g = group_of[r]
@@ -81,7 +93,7 @@ def test_brute_force_tiny(recipe, fa, fg):
             want = math.fsum(Aq[r][k] * Wkq[g][k][n] for k in range(K))
             assert abs(Y[r, n] - want) <= 1e-12 * (abs(want) + 1e-30), (r, n)
     # dgrad
-    dA = G.grouped_dgrad(G.deq_act_rows(qd["row_codes"], qd["row_scales"], recipe, fg),
+    dA = G.grouped_dgrad(G.deq_act_rows(qd["row_codes"], _sc(qd, "row_scales", recipe), recipe, fg),
                          G.deq_weight(qw, recipe, fa, "n"), ge)
     for r in range(R):
         g = group_of[r]
@@ -89,8 +101,10 @@ def test_brute_force_tiny(recipe, fa, fg):
             want = math.fsum(Dq[r][n] * Wnq[g][k][n] for n in range(N))
             assert abs(dA[r, k] - want) <= 1e-12 * (abs(want) + 1e-30), (r, k)
     # wgrad from the column-wise (padded, transposed) operands
-    At = G.unpad_cols(G.deq_act_cols(qa["col_codes"], qa["col_scales"], recipe, fa), qa["padded_starts"], ge)
-    Dt = G.unpad_cols(G.deq_act_cols(qd["col_codes"], qd["col_scales"], recipe, fg), qd["padded_starts"], ge)
+    At = G.unpad_cols(G.deq_act_cols(qa["col_codes"], _sc(qa, "col_scales", recipe), recipe, fa),
+                      qa["padded_starts"], ge)
+    Dt = G.unpad_cols(G.deq_act_cols(qd["col_codes"], _sc(qd, "col_scales", recipe), recipe, fg),
+                      qd["padded_starts"], ge)
     dW = G.grouped_wgrad(At, Dt, ge, E)
     for e in range(E):
         rows = range(st[e], st[e] + sizes[e])
@@ -112,6 +126,8 @@ def _col_val(q, recipe, fmt, g, j, c):
         s = float(q["col_scales"][0])
     elif recipe == "block":
         s = float(q["col_scales"][c][p // 128])
+    elif recipe == "nvfp4":
+        s = F.decode_value(F.E4M3, int(q["col_scales"][c][p // 16])) * float(q["tensor_scale"][0])
     else:
         s = 2.0 ** (int(q["col_scales"][c][p // 32]) - 127)
     return F.decode_value(fmt, int(code)) * s
