@@ -113,6 +113,7 @@ typedef int32_t mxsg_status;
 #define MXSG_RECIPE_DELAYED 1    /* as tensorwise, scale taken from a delayed-scaling state */
 #define MXSG_RECIPE_BLOCKWISE 2  /* tokens 1x128 rows / 128x1 columns; weights 128x128 tiles */
 #define MXSG_RECIPE_MX 3         /* 32-element blocks, E8M0 scales */
+#define MXSG_RECIPE_NVFP4 4      /* e2m1 elements; e4m3 scale per 16 elements; fp32 scale per tensor */
 
 /* element formats */
 #define MXSG_FMT_E4M3 0

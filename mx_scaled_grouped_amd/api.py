@@ -26,7 +26,7 @@ FMT = {"e4m3": E4M3, "e5m2": E5M2, "e2m1": E2M1, E4M3: E4M3, E5M2: E5M2, E2M1: E
 def elems_per_byte(fmt) -> int:
     """Elements per code byte: 2 for 4-bit e2m1 (MXFP4), else 1."""
     return 2 if FMT[fmt] == E2M1 else 1
-RECIPES = {"tw": 0, "dl": 1, "block": 2, "mx": 3}
+RECIPES = {"tw": 0, "dl": 1, "block": 2, "mx": 3, "nvfp4": 4}
 MODE_FWD, MODE_DGRAD, MODE_WGRAD = 0, 1, 2
 
 
@@ -136,6 +136,71 @@ def _scale_blocks(recipe: str) -> int:
     return {"block": 128, "mx": 32}.get(recipe, 0)
 
 
+def _scale_dtype(recipe: str) -> torch.dtype:
+    """E8M0 (MX) and e4m3 (NVFP4) scale codes are bytes; the rest fp32."""
+    return torch.uint8 if recipe in ("mx", "nvfp4") else torch.float32
+
+
+# NVFP4 code order inside each 128-element (64-byte) piece of a row: the 8
+# elements 16 s + 8 h .. + 7 (k16 step s, half h) form the dword at byte
+# 32 (s // 4) + 16 h + 4 (s % 4) (mxsg.h, Layouts).
+def _nv_nibble_order() -> torch.Tensor:
+    """nibble position of logical element e of a 128-element piece"""
+    pos = []
+    for e in range(128):
+        st, h, i = e // 16, (e // 8) % 2, e % 8
+        byte = 32 * (st // 4) + 16 * h + 4 * (st % 4) + i // 2
+        pos.append(2 * byte + i % 2)
+    return torch.tensor(pos, dtype=torch.long)
+
+
+def unpack_nvfp4_codes(t: torch.Tensor, rows: Optional[int] = None) -> torch.Tensor:
+    """Row-major e2m1 codes [..., rows, L], one per uint8, from NVFP4 code
+    bytes [..., Rp, L/2] (pair-interleaved rows, NVFP4 nibble order)."""
+    b = unpack_codes(t, rows)
+    nib = torch.stack([b & 0xF, b >> 4], dim=-1).reshape(*b.shape[:-1], -1)       # nibbles in storage order
+    L = nib.shape[-1]
+    idx = _nv_nibble_order().to(nib.device)
+    piece = nib.reshape(*nib.shape[:-1], L // 128, 128)
+    return piece.index_select(-1, idx).reshape(*nib.shape[:-1], L)
+
+
+def pack_nvfp4_codes(codes: torch.Tensor) -> torch.Tensor:
+    """NVFP4 code bytes [..., R + R % 2, L/2] (pair-interleaved rows, NVFP4
+    nibble order) from row-major e2m1 codes [..., R, L], one per uint8."""
+    *lead, r, L = codes.shape
+    if L % 128:
+        raise ValueError(f"row length {L} is not a multiple of 128")
+    pos = _nv_nibble_order().to(codes.device)
+    piece = codes.reshape(*lead, r, L // 128, 128)
+    stored = torch.empty_like(piece)
+    stored[..., pos] = piece                                    # element e goes to nibble position pos[e]
+    nib = stored.reshape(*lead, r, L // 2, 2)
+    return pack_codes((nib[..., 0] | (nib[..., 1] << 4)).contiguous())
+
+
+def pack_nvfp4_scales(blocks: torch.Tensor, tensor_scales: torch.Tensor) -> torch.Tensor:
+    """An NVFP4 scale buffer (uint8) from e4m3 block codes [units, rows, L/16]
+    and fp32 tensor scales [units]: each unit's codes piece-major
+    [L/128, rows, 8], then the tensor scales."""
+    units, rows, nb = blocks.shape
+    pm = blocks.reshape(units, rows, nb // 8, 8).transpose(1, 2).reshape(-1)
+    ts = tensor_scales.to(torch.float32).contiguous().view(torch.uint8)
+    return torch.cat([pm.to(torch.uint8), ts.to(pm.device)])
+
+
+def nvfp4_scales(t: torch.Tensor, rows: int, L: int, units: int = 1):
+    """(e4m3 block codes [units, rows, L/16], tensor scales float32 [units])
+    of an NVFP4 scale buffer: each unit's block codes piece-major
+    ([L/128, rows, 8]), the units' codes one after another, then the fp32
+    tensor scales."""
+    flat = t.reshape(-1)
+    n = rows * (L // 16)
+    blocks = flat[:units * n].reshape(units, L // 128, rows, 8).transpose(1, 2).reshape(units, rows, L // 16)
+    ts = flat[units * n:units * n + 4 * units].view(torch.float32)
+    return blocks, ts
+
+
 def quantize_act_sizes(M: int, C: int, recipe: str, fmt=E4M3, E: int = 0) -> List[int]:
     """Byte sizes [row_codes, row_scales, col_codes, col_scales,
     padded_starts] of mxsg_quantize_act's outputs (E = 0: row-wise only)."""
@@ -237,7 +302,7 @@ def _check_quant_act_out(q: "QuantAct", recipe: str, f: int, M: int, C: int, E: 
         raise ValueError(f"out was made for recipe={q.recipe} fmt={q.fmt} M={q.M} C={q.C}, "
                          f"the call has recipe={recipe} fmt={f} M={M} C={C}")
     nb = quantize_act_sizes(M, C, recipe, f, E if colwise else 0)
-    sdt = torch.uint8 if recipe == "mx" else torch.float32
+    sdt = _scale_dtype(recipe)
     if rowwise:
         _need(q.row_codes, nb[0], "out.row_codes", torch.uint8)
         _need(q.row_scales, nb[1], "out.row_scales", sdt)
@@ -251,7 +316,7 @@ def _check_quant_act_out(q: "QuantAct", recipe: str, f: int, M: int, C: int, E: 
         _need(q.padded_starts, nb[4], "out.padded_starts", torch.int32)
     elif q.col_codes is not None:
         raise ValueError("out holds column-wise codes but the call asks for none")
-    if recipe == "tw":
+    if recipe in ("tw", "nvfp4"):
         _need(q.amax, 4, "out.amax", torch.float32)
 
 
@@ -317,7 +382,7 @@ def quantize_act(x: torch.Tensor, recipe: str, fmt, group_ends: Optional[torch.T
         _check_quant_act_out(q, recipe, f, M, C, E, rowwise, colwise)
     else:
         q = QuantAct(recipe, f, M, C)
-        sdt = torch.uint8 if recipe == "mx" else torch.float32
+        sdt = _scale_dtype(recipe)
         nb = quantize_act_sizes(M, C, recipe, f, E if colwise else 0)
         epb = elems_per_byte(f)
         if rowwise:
@@ -332,7 +397,7 @@ def quantize_act(x: torch.Tensor, recipe: str, fmt, group_ends: Optional[torch.T
             if recipe == "mx":  # word-major [ld/128, C, 4]
                 q.col_scales = q.col_scales.view(q.ld // 128, C, 4)
             q.padded_starts = _buffer(nb[4], torch.int32, 0, dev)
-        if recipe == "tw":
+        if recipe in ("tw", "nvfp4"):
             q.amax = torch.empty(1, dtype=torch.float32, device=dev)
     amax = q.amax
     dls = dli = None
@@ -366,7 +431,7 @@ def _check_quant_weight_out(q: "QuantWeight", recipe: str, f: int, E: int, K: in
         raise ValueError(f"out was made for recipe={q.recipe} fmt={q.fmt} E={q.E} K={q.K} N={q.N}, "
                          f"the call has recipe={recipe} fmt={f} E={E} K={K} N={N}")
     nb = quantize_weight_sizes(E, K, N, recipe, f)
-    sdt = torch.uint8 if recipe == "mx" else torch.float32
+    sdt = _scale_dtype(recipe)
     for want, codes, scales, i, name in ((kmajor, q.kmajor_codes, q.kmajor_scales, 0, "kmajor"),
                                          (nmajor, q.nmajor_codes, q.nmajor_scales, 2, "nmajor")):
         if want:
@@ -374,7 +439,7 @@ def _check_quant_weight_out(q: "QuantWeight", recipe: str, f: int, E: int, K: in
             _need(scales, nb[i + 1], f"out.{name}_scales", sdt)
         elif codes is not None:
             raise ValueError(f"out holds {name} codes but the call asks for none")
-    if recipe == "tw":
+    if recipe in ("tw", "nvfp4"):
         _need(q.amax, 4 * E, "out.amax", torch.float32)
 
 
@@ -414,6 +479,9 @@ def quantize_weight(w: torch.Tensor, recipe: str, fmt, kmajor: bool = True, nmaj
             ks = ns = _buffer(nb[1], torch.float32, 0, dev)
         elif recipe == "block":
             ks = ns = _buffer(nb[1], torch.float32, N // 128, dev).view(E, K // 128, N // 128)
+        elif recipe == "nvfp4":  # block codes [E, K/128, N, 8] / [E, N/128, K, 8], then fp32 [E]
+            ks = _buffer(nb[1], torch.uint8, 0, dev)
+            ns = _buffer(nb[3], torch.uint8, 0, dev)
         else:  # word-major per expert: [E, K/128, N, 4] and [E, N/128, K, 4]
             ks = _buffer(nb[1], torch.uint8, 0, dev).view(E, K // 128, N, 4)
             ns = _buffer(nb[3], torch.uint8, 0, dev).view(E, N // 128, K, 4)
@@ -423,7 +491,7 @@ def quantize_weight(w: torch.Tensor, recipe: str, fmt, kmajor: bool = True, nmaj
         if nmajor:
             q.nmajor_codes = _buffer(nb[2], torch.uint8, N // epb, dev).view(E, K, N // epb)
             q.nmajor_scales = ns
-        if recipe == "tw":
+        if recipe in ("tw", "nvfp4"):
             q.amax = torch.empty(E, dtype=torch.float32, device=dev)
     amax = q.amax
     dls = dli = None
@@ -464,6 +532,10 @@ def _check_gemm_buffers(mode, recipe, fa, E, M, K, N, group_ends, a, a_scales, l
     if recipe in ("tw", "dl"):
         _need(a_scales, 4, "A scales", torch.float32)
         _need(b_scales, 4 * (1 if mode == MODE_WGRAD else E), "B scales", torch.float32)
+    elif recipe == "nvfp4":      # e4m3 block codes per 16 elements, then the fp32 tensor scale(s)
+        _need(a_scales, a_units[0] * (a_units[1] // 16) + 4, "A scales", torch.uint8)
+        _need(b_scales, b_units[0] * (b_units[1] // 16) + 4 * (1 if mode == MODE_WGRAD else E), "B scales",
+              torch.uint8)
     else:
         blk, per = (128, 4) if recipe == "block" else (32, 1)
         sdt = torch.float32 if recipe == "block" else torch.uint8

@@ -14,7 +14,7 @@
 
 namespace mxsg {
 
-enum Recipe : int { kTensorwise = 0, kDelayed = 1, kBlockwise = 2, kMx = 3, kTile128 = 4 };
+enum Recipe : int { kTensorwise = 0, kDelayed = 1, kBlockwise = 2, kMx = 3, kNvfp4 = 4, kTile128 = 5 };
 enum Format : int { kE4M3 = 0, kE5M2 = 1, kE2M1 = 2 };
 enum Mode : int { kFwd = 0, kDgrad = 1, kWgrad = 2 };
 
@@ -150,6 +150,37 @@ __device__ __forceinline__ float exp2_neg(int k) {
   if (e >= 1) return __uint_as_float((uint32_t)e << 23);
   return __uint_as_float(1u << (22 + e));  // e == 0: 2^-127
 }
+
+// NVFP4 (e2m1 elements; an e4m3 scale per 16 elements along the contraction
+// dim; an fp32 scale per tensor unit). Tensor decode scale s_t = fp32(amax /
+// 2688) (6 * 448, the e2m1 maximum times the e4m3 maximum), 1 for amax == 0.
+constexpr float kNvTensorDen = 2688.0f;
+__device__ __forceinline__ float nv_tensor_scale(float amax) {
+  return amax > 0.0f ? __fdiv_rn(amax, kNvTensorDen) : 1.0f;
+}
+
+// A 16-element block's e4m3 scale code and the element multiplier:
+// t = fp32(fp32(amax / 6) / s_t), code = saturating RNE e4m3 of t,
+// M = fp32(value(code) * s_t), inv = fp32(1 / M) (0 when M == 0 or 1 / M
+// overflows), each an IEEE fp32 operation.
+__device__ __forceinline__ uint32_t nv_block_scale(float amax, float s_t, float &inv) {
+  const float t = __fdiv_rn(__fdiv_rn(amax, 6.0f), s_t);
+  const float tc = __builtin_fminf(t, 448.0f);                  // t >= 0; saturate
+  const uint32_t code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(tc, tc, 0, false) & 0xFFu;
+  const float d = __builtin_amdgcn_cvt_f32_fp8((int)code, 0);   // exact decode
+  const float m = d * s_t;
+  const float r = __fdiv_rn(1.0f, m);
+  inv = (m > 0.0f && r < __builtin_inff()) ? r : 0.0f;
+  return code;
+}
+
+// NVFP4 code order inside each 128-element (64-byte) piece of a row: the 8
+// elements 16 s + 8 h .. 16 s + 8 h + 7 (k16 step s, half h) form the dword
+// at byte 32 (s / 4) + 16 h + 4 (s % 4), so that the 16-byte chunks h and
+// 2 + h of a piece hold, for MFMA lane half h, its 8 k-values of each of the
+// piece's 8 steps (measured operand layout of the 32x32x16 f16 MFMA: lane
+// half h holds k in [8h, 8h + 8) of a step).
+__device__ __forceinline__ int nv_dword_off(int s, int h) { return ((s & 4) << 3) + 16 * h + 4 * (s & 3); }
 
 // wave-wide max of a uint (64 lanes)
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {

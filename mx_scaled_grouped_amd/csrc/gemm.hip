@@ -70,6 +70,7 @@ struct GemmArgs {
   int nblocks;           // tiles (slots x jtiles, or E x slots x jtiles)
   int accumulate;
   int stream_out;        // FWD / DGRAD: write the bf16 output with streaming stores
+  int64_t sa_tail, sb_tail;  // NVFP4: byte offset of the fp32 tensor scales in the scale buffers
 };
 
 // Workgroup bid runs on XCD bid % 8. Logical tiles are handed to the XCDs in
@@ -740,15 +741,307 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// NVFP4 grouped GEMM: e2m1 codes with an e4m3 scale per 16 contraction
+// elements and an fp32 scale per tensor (the NVFP4 rows of the Megatron-LM
+// single-grouped-weight PR's coverage table). gfx950's scaled MFMAs take
+// only power-of-two (E8M0) scales per 32 elements, so the block scale cannot
+// ride on them; instead each lane turns its codes into f16 operands: the
+// code pairs decode exactly to f16 (v_cvt_scalef32_pk_f16_fp4, scale 1) and
+// a packed f16 multiply by the block scale is exact too (an e2m1 value has
+// 2 significant bits and an e4m3 scale 4, and every product lies in
+// [2^-10, 2688], inside f16's normal range; all three facts measured on the
+// device for all codes and scales). The f16 products then go through the
+// 32x32x16 f16 MFMA with fp32 accumulation, and the two tensor scales
+// multiply the accumulators in the epilogue. The tile, the XCD mapping, the
+// persistent grid and the direct-to-LDS ring of 64-byte (128-element) stages
+// are those of grouped_gemm_kernel; a stage is one 128-element piece of each
+// row, whose 8 e4m3 block codes per row arrive beside it, and whose codes
+// are stored so that the 16-byte chunks a lane reads hold, for its half of
+// the MFMA's k range, the 8 elements of each of the stage's 8 k16 steps.
+typedef _Float16 nv_v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 nv_v8h __attribute__((ext_vector_type(8)));
+
+// 8 e2m1 codes (one dword, element 2i in the low nibble of byte i) times the
+// block scale dd (both halves equal): the f16 MFMA operand of one lane
+__device__ __forceinline__ nv_v8h nv_operand(uint32_t x, nv_v2h dd) {
+  const nv_v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 0) * dd;
+  const nv_v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 1) * dd;
+  const nv_v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 2) * dd;
+  const nv_v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 3) * dd;
+  return nv_v8h{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// a row's 8 block scales of one stage (two dwords of e4m3 codes) as f16 pairs
+struct NvScale {
+  nv_v2h p[4];
+};
+__device__ __forceinline__ NvScale nv_scales(uint2 w) {
+  NvScale r;
+  r.p[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, false);
+  r.p[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, true);
+  r.p[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, false);
+  r.p[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, true);
+  return r;
+}
+template <int S>
+__device__ __forceinline__ nv_v2h nv_dd(const NvScale &r) {
+  return __builtin_shufflevector(r.p[S >> 1], r.p[S >> 1], S & 1, S & 1);
+}
+
+template <int MODE, bool ACC>
+__global__ __launch_bounds__(256) void nvfp4_gemm_kernel(GemmArgs a) {
+  constexpr int NW = 4, BN = 256, WM = 128, WN = 128, MI = 4, NI = 4;
+  constexpr int AQ = GBM / 16 / NW, BQ = BN / 16 / NW;   // 1 KB copy groups of codes per wave per stage
+  constexpr int OPS = 4 + AQ + BQ;                        // + two scale dwords of A rows and two of B rows
+  __shared__ __attribute__((aligned(1024))) uint8_t As[4][GBM * GBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t Bs[4][BN * GBK];
+  // per stage buffer: the 8 block-scale bytes of every tile row, row r at dwords 2r, 2r + 1
+  __shared__ __attribute__((aligned(16))) uint32_t nA[4][2 * GBM];
+  __shared__ __attribute__((aligned(16))) uint32_t nB[4][2 * BN];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wi = wave >> 1, wj = wave & 1;
+  const int h = lane >> 5, l32 = lane & 31;
+  const uint8_t *zsrc = reinterpret_cast<const uint8_t *>(kZeroSrc) + lane * 16;
+  const uint32_t *zsrc4 = kZeroSrc + lane;
+
+  for (int vb = blockIdx.x; vb < a.nblocks; vb += gridDim.x) {
+    const int lid = xcd_remap<32>(vb, a.nblocks);
+    int g = 0;
+    int64_t i0 = 0, ilo = 0, ihi = 0, j0 = 0, l0 = 0;
+    int nsteps = 0;
+    if (MODE == kWgrad) {
+      const int per_g = a.slots * a.jtiles;
+      g = lid / per_g;
+      int it, jt;
+      raster(lid - g * per_g, a.slots, a.jtiles, it, jt);
+      i0 = (int64_t)it * GBM;
+      j0 = (int64_t)jt * BN;
+      ilo = i0;
+      ihi = a.I < i0 + GBM ? a.I : i0 + GBM;
+      int64_t p_lo = a.pstarts[g], p_hi = a.pstarts[g + 1];
+      const int64_t cap = (a.lda < a.ldb ? a.lda : a.ldb) * 2;   // token positions
+      p_lo = p_lo < 0 ? 0 : (p_lo > cap ? cap : p_lo);
+      p_hi = p_hi < p_lo ? p_lo : (p_hi > cap ? cap : p_hi);
+      l0 = p_lo & ~(int64_t)127;
+      nsteps = (int)((p_hi - l0) / 128);
+    } else {
+      int slot, jt;
+      raster(lid, a.slots, a.jtiles, slot, jt);
+      j0 = (int64_t)jt * BN;
+      if (!locate_row_tile(a, slot, g, i0, ilo, ihi)) continue;
+      l0 = 0;
+      nsteps = (int)(a.L / GBK);
+    }
+
+    // code copies: as in grouped_gemm_kernel (64-byte stages of row pairs)
+    const int64_t lb = l0 / 128;   // first stage: 128 contraction elements per stage
+    const uint8_t *abase = a.a + (i0 >> 1) * 2 * a.lda + lb * 128;
+    const uint8_t *bbase = a.b + (MODE == kWgrad ? 0 : (int64_t)g * a.b_gstride) + (j0 >> 1) * 2 * a.ldb + lb * 128;
+    const int apmax = (int)(((ihi - 1) >> 1) - (i0 >> 1));
+    const int64_t jlim = (a.J - j0) < BN ? (a.J - j0) : BN;
+    const int bpmax = (int)((jlim - 1) >> 1);
+    uint32_t aoff[AQ], boff[BQ];
+#pragma unroll
+    for (int q = 0; q < AQ; ++q) {
+      const int row = (wave * AQ + q) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      const int pr = (row >> 1) < apmax ? (row >> 1) : apmax;
+      aoff[q] = (uint32_t)(pr * 2 * (int32_t)a.lda + (row & 1) * 64 + c * 16);
+    }
+#pragma unroll
+    for (int q = 0; q < BQ; ++q) {
+      const int row = (wave * BQ + q) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      const int pr = (row >> 1) < bpmax ? (row >> 1) : bpmax;
+      boff[q] = (uint32_t)(pr * 2 * (int32_t)a.ldb + (row & 1) * 64 + c * 16);
+    }
+    // block-scale copies: LDS dword d = 256 c + 64 wave + lane of a stage
+    // buffer is dword d % 2 of tile row d / 2; block scales are piece-major,
+    // [pieces, rows, 8 bytes], so a stage's bytes of consecutive rows are
+    // consecutive in memory
+    const int64_t RA = MODE == kWgrad ? a.I : a.M, RB = a.J;
+    const uint8_t *nsa[2], *nsb[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int d = c * 256 + wave * 64 + lane;
+      const int r = d >> 1;
+      const int64_t ia = i0 + r, jb = j0 + (r < jlim ? r : jlim - 1);
+      const int64_t ra = ia < ilo ? ilo : (ia >= ihi ? ihi - 1 : ia);
+      nsa[c] = reinterpret_cast<const uint8_t *>(a.a_scales) + (lb * RA + ra) * 8 + (d & 1) * 4;
+      nsb[c] = reinterpret_cast<const uint8_t *>(a.b_scales) + (MODE == kWgrad ? 0 : (int64_t)g * a.bs_gstride) +
+               (lb * RB + jb) * 8 + (d & 1) * 4;
+    }
+    // stage kt into buffer kt % 4; past the contraction: zero codes and zero
+    // block scales (the operands are then zero). OPS copies per wave always.
+    auto copy = [&](int kt) {
+      const int buf = kt & 3;
+      const bool real = kt < nsteps;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        dma4(real ? (const void *)(nsa[c] + (int64_t)kt * RA * 8) : (const void *)zsrc4, &nA[buf][c * 256 + wave * 64]);
+        dma4(real ? (const void *)(nsb[c] + (int64_t)kt * RB * 8) : (const void *)zsrc4, &nB[buf][c * 256 + wave * 64]);
+      }
+#pragma unroll
+      for (int q = 0; q < AQ; ++q)
+        dma16(real ? abase + (int64_t)kt * 128 + aoff[q] : zsrc, &As[buf][(wave * AQ + q) * 1024]);
+#pragma unroll
+      for (int q = 0; q < BQ; ++q)
+        dma16(real ? bbase + (int64_t)kt * 128 + boff[q] : zsrc, &Bs[buf][(wave * BQ + q) * 1024]);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    v16f acc[MI][NI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
+
+    if (nsteps > 0) {
+      copy(0);
+      copy(1);
+      copy(2);
+    }
+    for (int kt = 0; kt < nsteps; ++kt) {
+      const int buf = kt & 3;
+      // stage kt has landed (kt + 1 and kt + 2 may be in flight); after the
+      // barrier every wave is done with stage kt - 1, whose buffer the
+      // copies of stage kt + 3 reuse
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm<2 * OPS>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      copy(kt + 3);
+      v8i fa[MI], fb[NI];
+      NvScale sa[MI], sb[NI];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const int row = wi * WM + mi * 32 + l32;
+        fa[mi] = frag(As[buf], row, h);
+        sa[mi] = nv_scales(*reinterpret_cast<const uint2 *>(&nA[buf][2 * row]));
+      }
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int row = wj * WN + ni * 32 + l32;
+        fb[ni] = frag(Bs[buf], row, h);
+        sb[ni] = nv_scales(*reinterpret_cast<const uint2 *>(&nB[buf][2 * row]));
+      }
+      [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
+        ([&] {
+          constexpr int S = Ss;
+          nv_v8h ao[MI], bo[NI];
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi) ao[mi] = nv_operand((uint32_t)fa[mi][S], nv_dd<S>(sa[mi]));
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) bo[ni] = nv_operand((uint32_t)fb[ni][S], nv_dd<S>(sb[ni]));
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni)
+              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ao[mi], bo[ni], acc[mi][ni], 0, 0, 0);
+        }(), ...);
+      }(std::make_integer_sequence<int, 8>{});
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // the epilogue's first LDS writes read the last MFMAs' accumulators
+    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" ::: "memory");
+    wait_vm<0>();     // every copy (also past the contraction) has landed
+    __syncthreads();  // every wave is done with the stage buffers
+
+    // ---- epilogue: the tensor scales, then as in grouped_gemm_kernel
+    const float s_a = *reinterpret_cast<const float *>(reinterpret_cast<const uint8_t *>(a.a_scales) + a.sa_tail);
+    const float s_b = reinterpret_cast<const float *>(reinterpret_cast<const uint8_t *>(a.b_scales) +
+                                                      a.sb_tail)[MODE == kWgrad ? 0 : g];
+    const float scale = s_a * s_b;
+    if (ACC && nsteps == 0) continue;  // empty group: dW_g unchanged
+    constexpr int STR = WN + 8;
+    float *cb = reinterpret_cast<float *>(As[wave]);
+    const int64_t jw = j0 + wj * WN;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int v = 8 * hs; v < 8 * hs + 8; ++v)
+            cb[(((v >> 2) & 1) * 8 + h * 4 + (v & 3)) * STR + ni * 32 + l32] = acc[mi][ni][v];
+        __builtin_amdgcn_wave_barrier();
+        if constexpr (MODE == kWgrad) {
+          constexpr int CPR4 = WN / 4, CPL4 = 16 * CPR4 / 64;
+          float4 old[ACC ? CPL4 : 1];
+          if constexpr (ACC) {
+#pragma unroll
+            for (int k = 0; k < CPL4; ++k) {
+              const int id = k * 64 + lane;
+              const int64_t i = i0 + wi * WM + mi * 32 + hs * 16 + id / CPR4;
+              const int64_t j = jw + (id % CPR4) * 4;
+              old[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+              if (i >= ilo && i < ihi && j < a.J)
+                old[k] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.out) +
+                                                           ((int64_t)g * a.I + i) * a.ldo + j);
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < CPL4; ++k) {
+            const int id = k * 64 + lane;
+            const int r = id / CPR4, c4 = id % CPR4;
+            const int64_t i = i0 + wi * WM + mi * 32 + hs * 16 + r;
+            const int64_t j = jw + c4 * 4;
+            const float4 x = *reinterpret_cast<const float4 *>(&cb[r * STR + c4 * 4]);
+            if (i >= ilo && i < ihi && j < a.J) {
+              float4 y = make_float4(x.x * scale, x.y * scale, x.z * scale, x.w * scale);
+              if constexpr (ACC) y = make_float4(y.x + old[k].x, y.y + old[k].y, y.z + old[k].z, y.w + old[k].w);
+              *reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.out) + ((int64_t)g * a.I + i) * a.ldo + j) = y;
+            }
+          }
+        } else {
+          constexpr int CPR = WN / 8, CPL = 16 * CPR / 64;
+#pragma unroll
+          for (int k = 0; k < CPL; ++k) {
+            const int id = k * 64 + lane;
+            const int r = id / CPR, c8 = id % CPR;
+            const int64_t i = i0 + wi * WM + mi * 32 + hs * 16 + r;
+            const int64_t j = jw + c8 * 8;
+            const float4 x0 = *reinterpret_cast<const float4 *>(&cb[r * STR + c8 * 8]);
+            const float4 x1 = *reinterpret_cast<const float4 *>(&cb[r * STR + c8 * 8 + 4]);
+            if (i >= ilo && i < ihi && j < a.J) {
+              uint4 o;
+              o.x = f32_to_bf16_bits(x0.x * scale) | (f32_to_bf16_bits(x0.y * scale) << 16);
+              o.y = f32_to_bf16_bits(x0.z * scale) | (f32_to_bf16_bits(x0.w * scale) << 16);
+              o.z = f32_to_bf16_bits(x1.x * scale) | (f32_to_bf16_bits(x1.y * scale) << 16);
+              o.w = f32_to_bf16_bits(x1.z * scale) | (f32_to_bf16_bits(x1.w * scale) << 16);
+              uint16_t *dst = reinterpret_cast<uint16_t *>(a.out) + i * a.ldo + j;
+              if (a.stream_out)
+                store16_stream(dst, o);
+              else
+                *reinterpret_cast<uint4 *>(dst) = o;
+            }
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+    __syncthreads();  // the staging buffers are free before the next tile's copies land
+  }
+}
+
 // ---------------------------------------------------------------------------
 
-template <int MODE, int RECIPE, int FA, int FB>
-static hipError_t launch_cfg(const GemmArgs &a0, hipStream_t st) {
-  constexpr int BN = RECIPE == kBlockwise ? 128 : 256;
-  GemmArgs a = a0;
+// Tile counts of a launch with BN-wide tiles: a.jtiles, a.slots, a.nblocks.
+// False when there is nothing to launch (a.nblocks = 0) or too many tiles
+// (a.nblocks = -1).
+template <int BN>
+static bool plan_grid(int mode, GemmArgs &a) {
   a.jtiles = (int)((a.J + BN - 1) / BN);
   int64_t nblocks;
-  if (MODE == kWgrad) {
+  if (mode == kWgrad) {
     a.slots = (int)((a.I + GBM - 1) / GBM);
     nblocks = (int64_t)a.E * a.slots * a.jtiles;
   } else {
@@ -757,11 +1050,17 @@ static hipError_t launch_cfg(const GemmArgs &a0, hipStream_t st) {
     a.slots = (int)((a.M + 2 * (int64_t)a.E + GBM - 1) / GBM) + a.E;
     nblocks = (int64_t)a.slots * a.jtiles;
   }
-  if (nblocks == 0) return hipSuccess;
-  if (nblocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (nblocks > 0x7fffffff) {
+    a.nblocks = -1;
+    return false;
+  }
   a.nblocks = (int)nblocks;
-  // one workgroup per CU (the LDS ring allows one), rounded down to whole
-  // rounds of the 8 XCDs; each loops over its share of the tiles
+  return nblocks > 0;
+}
+
+// one workgroup per CU (the LDS ring allows one), rounded down to whole
+// rounds of the 8 XCDs; each loops over its share of the tiles
+static unsigned persistent_grid(int nblocks) {
   int64_t grid = nblocks;
   int dev = 0, ncu = 0;
   if (hipGetDevice(&dev) == hipSuccess &&
@@ -769,10 +1068,19 @@ static hipError_t launch_cfg(const GemmArgs &a0, hipStream_t st) {
     const int64_t persistent = (int64_t)(ncu / 8) * 8;
     grid = nblocks < persistent ? nblocks : persistent;
   }
+  return (unsigned)grid;
+}
+
+template <int MODE, int RECIPE, int FA, int FB>
+static hipError_t launch_cfg(const GemmArgs &a0, hipStream_t st) {
+  constexpr int BN = RECIPE == kBlockwise ? 128 : 256;
+  GemmArgs a = a0;
+  if (!plan_grid<BN>(MODE, a)) return a.nblocks < 0 ? hipErrorInvalidValue : hipSuccess;
+  const unsigned grid = persistent_grid(a.nblocks);
   if (MODE == kWgrad && a.accumulate)
-    grouped_gemm_kernel<MODE, RECIPE, FA, FB, BN, true><<<(unsigned)grid, 64 * gemm_waves<RECIPE>(), 0, st>>>(a);
+    grouped_gemm_kernel<MODE, RECIPE, FA, FB, BN, true><<<grid, 64 * gemm_waves<RECIPE>(), 0, st>>>(a);
   else
-    grouped_gemm_kernel<MODE, RECIPE, FA, FB, BN, false><<<(unsigned)grid, 64 * gemm_waves<RECIPE>(), 0, st>>>(a);
+    grouped_gemm_kernel<MODE, RECIPE, FA, FB, BN, false><<<grid, 64 * gemm_waves<RECIPE>(), 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -787,11 +1095,24 @@ static hipError_t launch_fmt(const GemmArgs &a, int fa, int fb, hipStream_t st) 
 }
 
 template <int MODE>
+static hipError_t launch_nvfp4(const GemmArgs &a0, hipStream_t st) {
+  GemmArgs a = a0;
+  if (!plan_grid<256>(MODE, a)) return a.nblocks < 0 ? hipErrorInvalidValue : hipSuccess;
+  const unsigned grid = persistent_grid(a.nblocks);
+  if (MODE == kWgrad && a.accumulate)
+    nvfp4_gemm_kernel<MODE, true><<<grid, 256, 0, st>>>(a);
+  else
+    nvfp4_gemm_kernel<MODE, false><<<grid, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+template <int MODE>
 static hipError_t launch_recipe(const GemmArgs &a, int recipe, int fa, int fb, hipStream_t st) {
   switch (recipe) {
     case kTensorwise:
     case kDelayed: return launch_fmt<MODE, kTensorwise>(a, fa, fb, st);
     case kBlockwise: return launch_fmt<MODE, kBlockwise>(a, fa, fb, st);
+    case kNvfp4: return launch_nvfp4<MODE>(a, st);
     default: return launch_fmt<MODE, kMx>(a, fa, fb, st);
   }
 }
@@ -826,6 +1147,9 @@ hipError_t launch_grouped_mm(const GemmParams &p, hipStream_t st) {
     a.b_gstride = p.N * p.ldb;
     // blockwise weight scales [E, K/128, N/128]: l-block = k, j-block = n
     a.bs_gstride = p.recipe == kMx ? p.N * (p.K / 32) : (p.K / SBLK) * (p.N / SBLK);
+    if (p.recipe == kNvfp4) a.bs_gstride = p.N * (p.K / 16);   // block-code bytes per expert
+    a.sa_tail = p.M * (p.K / 16);
+    a.sb_tail = (int64_t)p.E * p.N * (p.K / 16);
     a.sb_l = p.N / SBLK;
     a.sb_j = 1;
     return launch_recipe<kFwd>(a, p.recipe, p.fmt_a, p.fmt_b, st);
@@ -838,6 +1162,9 @@ hipError_t launch_grouped_mm(const GemmParams &p, hipStream_t st) {
     a.b_gstride = p.K * p.ldb;
     // same [E, K/128, N/128] array: l-block = n, j-block = k
     a.bs_gstride = p.recipe == kMx ? p.K * (p.N / 32) : (p.K / SBLK) * (p.N / SBLK);
+    if (p.recipe == kNvfp4) a.bs_gstride = p.K * (p.N / 16);
+    a.sa_tail = p.M * (p.N / 16);
+    a.sb_tail = (int64_t)p.E * p.K * (p.N / 16);
     a.sb_l = 1;
     a.sb_j = p.N / SBLK;
     return launch_recipe<kDgrad>(a, p.recipe, p.fmt_a, p.fmt_b, st);
@@ -846,6 +1173,8 @@ hipError_t launch_grouped_mm(const GemmParams &p, hipStream_t st) {
   a.J = p.N;
   a.L = 0;
   a.ldo = p.N;
+  a.sa_tail = p.K * (p.lda * epb / 16);
+  a.sb_tail = p.N * (p.ldb * epb / 16);
   return launch_recipe<kWgrad>(a, p.recipe, p.fmt_a, p.fmt_b, st);
 }
 

@@ -34,7 +34,12 @@ mxsg_status from_hip(hipError_t e, const char *what) {
   return fail(MXSG_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
 }
 
-bool recipe_ok(int32_t r) { return r >= MXSG_RECIPE_TENSORWISE && r <= MXSG_RECIPE_MX; }
+bool recipe_ok(int32_t r) { return r >= MXSG_RECIPE_TENSORWISE && r <= MXSG_RECIPE_NVFP4; }
+// e2m1 elements exist for the MX and NVFP4 recipes; NVFP4 has e2m1 elements only
+bool fmt_recipe_ok(int32_t fmt, int32_t recipe) {
+  if (recipe == MXSG_RECIPE_NVFP4) return fmt == MXSG_FMT_E2M1;
+  return fmt != MXSG_FMT_E2M1 || recipe == MXSG_RECIPE_MX;
+}
 bool fmt_ok(int32_t f) { return f == MXSG_FMT_E4M3 || f == MXSG_FMT_E5M2 || f == MXSG_FMT_E2M1; }
 bool fp8_fmt(int32_t f) { return f == MXSG_FMT_E4M3 || f == MXSG_FMT_E5M2; }
 // contraction / feature elements per code byte
@@ -50,8 +55,8 @@ int64_t elems_per_byte(int32_t f) { return f == MXSG_FMT_E2M1 ? 2 : 1; }
 mxsg_status act_shape(const char *fn, int64_t M, int64_t C, int32_t recipe, int32_t fmt) {
   REQUIRE(recipe_ok(recipe), MXSG_INVALID_ARGUMENT, "%s: unknown recipe %d", fn, recipe);
   REQUIRE(fmt_ok(fmt), MXSG_INVALID_ARGUMENT, "%s: unknown format %d", fn, fmt);
-  REQUIRE(fmt != MXSG_FMT_E2M1 || recipe == MXSG_RECIPE_MX, MXSG_UNSUPPORTED,
-          "%s: e2m1 codes need the MX recipe", fn);
+  REQUIRE(fmt_recipe_ok(fmt, recipe), MXSG_UNSUPPORTED,
+          "%s: e2m1 codes go with the MX or NVFP4 recipe, and NVFP4 with e2m1 only", fn);
   REQUIRE(M >= 0 && C > 0, MXSG_INVALID_ARGUMENT, "%s: M=%lld C=%lld", fn, (long long)M,
           (long long)C);
   REQUIRE(C % 128 == 0, MXSG_BAD_SHAPE, "%s: C=%lld is not a multiple of 128", fn, (long long)C);
@@ -64,8 +69,8 @@ mxsg_status weight_shape(const char *fn, int32_t E, int64_t K, int64_t N, int32_
                          int32_t fmt) {
   REQUIRE(recipe_ok(recipe), MXSG_INVALID_ARGUMENT, "%s: unknown recipe %d", fn, recipe);
   REQUIRE(fmt_ok(fmt), MXSG_INVALID_ARGUMENT, "%s: unknown format %d", fn, fmt);
-  REQUIRE(fmt != MXSG_FMT_E2M1 || recipe == MXSG_RECIPE_MX, MXSG_UNSUPPORTED,
-          "%s: e2m1 codes need the MX recipe", fn);
+  REQUIRE(fmt_recipe_ok(fmt, recipe), MXSG_UNSUPPORTED,
+          "%s: e2m1 codes go with the MX or NVFP4 recipe, and NVFP4 with e2m1 only", fn);
   REQUIRE(E >= 1 && K > 0 && N > 0, MXSG_INVALID_ARGUMENT, "%s: E=%d K=%lld N=%lld", fn, E,
           (long long)K, (long long)N);
   REQUIRE(K % 128 == 0 && N % 128 == 0, MXSG_BAD_SHAPE,
@@ -94,7 +99,8 @@ static mxsg_status quantize_act_impl(const char *fn, const void *x, int64_t T,
     REQUIRE(T >= 0 && T <= ((int64_t)1 << 31) - 1 && (M == 0 || T > 0), MXSG_BAD_SHAPE,
             "%s: x has %lld rows for %lld routed rows", fn, (long long)T, (long long)M);
   }
-  const bool scaled_unit = recipe == MXSG_RECIPE_BLOCKWISE || recipe == MXSG_RECIPE_MX;
+  const bool scaled_unit =
+      recipe == MXSG_RECIPE_BLOCKWISE || recipe == MXSG_RECIPE_MX || recipe == MXSG_RECIPE_NVFP4;
   if (row_codes && scaled_unit)
     REQUIRE(row_scales, MXSG_INVALID_ARGUMENT, "%s: row_scales is NULL", fn);
   if (col_codes) {
@@ -108,7 +114,7 @@ static mxsg_status quantize_act_impl(const char *fn, const void *x, int64_t T,
     if (scaled_unit)
       REQUIRE(col_scales, MXSG_INVALID_ARGUMENT, "%s: col_scales is NULL", fn);
   }
-  if (recipe == MXSG_RECIPE_TENSORWISE || recipe == MXSG_RECIPE_DELAYED)
+  if (recipe == MXSG_RECIPE_TENSORWISE || recipe == MXSG_RECIPE_DELAYED || recipe == MXSG_RECIPE_NVFP4)
     REQUIRE(amax, MXSG_INVALID_ARGUMENT, "%s: amax is NULL", fn);
   if (recipe == MXSG_RECIPE_DELAYED)
     REQUIRE(dl_scale && dl_inv, MXSG_INVALID_ARGUMENT, "%s: dl_scale/dl_inv NULL", fn);
@@ -180,6 +186,7 @@ mxsg_status mxsg_quantize_act_sizes(int64_t M, int64_t C, int32_t recipe, int32_
   auto scale_bytes = [recipe](int64_t rows, int64_t n) -> int64_t {
     if (recipe == MXSG_RECIPE_BLOCKWISE) return rows * (n / 128) * 4;
     if (recipe == MXSG_RECIPE_MX) return rows * (n / 32);
+    if (recipe == MXSG_RECIPE_NVFP4) return rows * (n / 16) + 4;   // block codes, then the tensor scale
     return 4;
   };
   const int64_t epb = elems_per_byte(fmt);
@@ -207,6 +214,7 @@ mxsg_status mxsg_quantize_weight_sizes(int32_t E, int64_t K, int64_t N, int32_t 
   switch (recipe) {
     case MXSG_RECIPE_BLOCKWISE: bytes[1] = bytes[3] = (int64_t)E * (K / 128) * (N / 128) * 4; break;
     case MXSG_RECIPE_MX: bytes[1] = bytes[3] = elems / 32; break;
+    case MXSG_RECIPE_NVFP4: bytes[1] = bytes[3] = elems / 16 + 4 * (int64_t)E; break;
     default: bytes[1] = bytes[3] = (int64_t)E * 4; break;
   }
   g_err[0] = 0;
@@ -257,7 +265,7 @@ mxsg_status mxsg_quantize_weight(const void *w, int32_t E, int64_t K, int64_t N,
   REQUIRE(kmajor_codes || nmajor_codes, MXSG_INVALID_ARGUMENT, "quantize_weight: no output");
   if (kmajor_codes) REQUIRE(kmajor_scales, MXSG_INVALID_ARGUMENT, "quantize_weight: kmajor_scales NULL");
   if (nmajor_codes) REQUIRE(nmajor_scales, MXSG_INVALID_ARGUMENT, "quantize_weight: nmajor_scales NULL");
-  if (recipe == MXSG_RECIPE_TENSORWISE || recipe == MXSG_RECIPE_DELAYED)
+  if (recipe == MXSG_RECIPE_TENSORWISE || recipe == MXSG_RECIPE_DELAYED || recipe == MXSG_RECIPE_NVFP4)
     REQUIRE(amax, MXSG_INVALID_ARGUMENT, "quantize_weight: amax is NULL");
   if (recipe == MXSG_RECIPE_DELAYED)
     REQUIRE(dl_scale && dl_inv, MXSG_INVALID_ARGUMENT, "quantize_weight: dl_scale/dl_inv NULL");
@@ -305,8 +313,8 @@ mxsg_status mxsg_grouped_mm_check(int32_t mode, int32_t recipe, int32_t fmt_a, i
           "grouped_mm: e5m2 x e5m2 is not built");
   REQUIRE((fmt_a == MXSG_FMT_E2M1) == (fmt_b == MXSG_FMT_E2M1), MXSG_UNSUPPORTED,
           "grouped_mm: 4-bit operands are built only against 4-bit operands");
-  REQUIRE(fmt_a != MXSG_FMT_E2M1 || recipe == MXSG_RECIPE_MX, MXSG_UNSUPPORTED,
-          "grouped_mm: e2m1 operands need the MX recipe");
+  REQUIRE(fmt_recipe_ok(fmt_a, recipe) && fmt_recipe_ok(fmt_b, recipe), MXSG_UNSUPPORTED,
+          "grouped_mm: e2m1 operands go with the MX or NVFP4 recipe, and NVFP4 with e2m1 only");
   const int64_t epb = elems_per_byte(fmt_a);
   REQUIRE(E >= 1 && M >= 0 && K > 0 && N > 0, MXSG_INVALID_ARGUMENT,
           "grouped_mm: E=%d M=%lld K=%lld N=%lld", E, (long long)M, (long long)K, (long long)N);

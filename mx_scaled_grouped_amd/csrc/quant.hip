@@ -151,6 +151,7 @@ struct TileArgs {
   int32_t *status;           // optional status word (non-finite inputs)
   int32_t rgroup;            // row tiles per launch-order group (>= 1)
   int32_t swiglu;            // x is a gate/up output [rows, 2C]: quantize silu(gate) * up
+  int64_t rs_tail, cs_tail;  // NVFP4: byte offset of the fp32 tensor scales in row_scales / col_scales
 };
 
 // ---------------------------------------------------------------------------
@@ -365,7 +366,8 @@ __device__ bool locate_padded_tile(const TileArgs &a, int64_t p0, int64_t &src0,
 template <int RECIPE, int FMT, bool ROW, bool COL>
 __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
   // 4-bit codes (MXFP4) exist for the MX recipe only; two codes per byte
-  static_assert(FMT != kE2M1 || RECIPE == kMx, "e2m1 codes are MX-scaled");
+  static_assert(FMT != kE2M1 || RECIPE == kMx || RECIPE == kNvfp4, "e2m1 codes are MX- or NVFP4-scaled");
+  static_assert(RECIPE != kNvfp4 || FMT == kE2M1, "NVFP4 elements are e2m1");
   constexpr bool FP4 = FMT == kE2M1;
   __shared__ __attribute__((aligned(16))) uint16_t tile[QT * QT];       // bf16, row stride 256 B
   // codes [feature][pos] of the column-wise output, in the same LDS as the
@@ -402,6 +404,11 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
 
   // the tensor scale (tensorwise / delayed) is written first, so that it is
   // there even when no tile holds a row (an empty tensor or empty groups)
+  if (RECIPE == kNvfp4 && blockIdx.x == 0 && t == 0) {
+    const float st = nv_tensor_scale(a.amax[b]);
+    if (a.row_scales) reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(a.row_scales) + a.rs_tail)[b] = st;
+    if (a.col_scales) reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(a.col_scales) + a.cs_tail)[b] = st;
+  }
   if ((RECIPE == kTensorwise || RECIPE == kDelayed) && blockIdx.x == 0 &&
       t == 0) {
     float s0 = 1.0f, i0 = 1.0f;
@@ -465,6 +472,8 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
   float t_s = 1.0f, t_inv = 1.0f;
   if (RECIPE == kTensorwise) {
     scale_pair<FMT>(a.amax[b], t_s, t_inv);
+  } else if (RECIPE == kNvfp4) {
+    t_s = nv_tensor_scale(a.amax[b]);
   } else if (RECIPE == kDelayed) {
     t_s = a.dl_scale[b];
     t_inv = a.dl_inv[b];
@@ -513,6 +522,15 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
         if (cq == 0 && r < nvalid)
           reinterpret_cast<float *>(a.row_scales)[b * a.rs_bstride + (src0 + r) * (a.C / QT) +
                                                   ftile] = s;
+      } else if (RECIPE == kNvfp4) {  // 1x16: the 2 lanes holding 16 features
+        uint32_t m = absmax_bits8(v[u], 0);
+        m = umax(m, (uint32_t)__shfl_xor((int)m, 1, 64));
+        if ((cq & 1) == 0) flag_nonfinite(a.status, m);
+        const uint32_t code = nv_block_scale(bits_to_amax(m), t_s, inv);
+        // piece-major: 8 scale bytes per row per 128-element piece, rows consecutive
+        if ((cq & 1) == 0 && r < nvalid)
+          reinterpret_cast<uint8_t *>(a.row_scales)[b * a.rs_bstride + ((c0 / QT) * a.rows + src0 + r) * 8 +
+                                                    (cq >> 1)] = (uint8_t)code;
       } else if (RECIPE == kMx) {  // 1x32: the 4 lanes holding 32 features
         uint32_t m = absmax_bits8(v[u], 0);
         m = umax(m, (uint32_t)__shfl_xor((int)m, 1, 64));
@@ -528,8 +546,9 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
       if (r < nvalid) {
         if constexpr (FP4) {
           const uint32_t q = cvt8_e2m1(v[u], inv);
-          *reinterpret_cast<uint32_t *>(a.row_codes + b * a.row_bstride +
-                                        pi_off(src0 + r, (c0 + cq * 8) / 2, a.C / 2)) = q;
+          // MXFP4: elements in order; NVFP4: the dword of (step cq / 2, half cq % 2)
+          const int64_t col = RECIPE == kNvfp4 ? c0 / 2 + nv_dword_off(cq >> 1, cq & 1) : (c0 + cq * 8) / 2;
+          *reinterpret_cast<uint32_t *>(a.row_codes + b * a.row_bstride + pi_off(src0 + r, col, a.C / 2)) = q;
         } else {
           const uint2 q = cvt8<FMT>(v[u], inv);
           store8_stream(a.row_codes + b * a.row_bstride + pi_off(src0 + r, c0 + cq * 8, a.C), q);
@@ -556,6 +575,25 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
   for (int i = 0; i < 32; ++i) w[i] = *reinterpret_cast<const uint32_t *>(&tile[(q * 32 + i) * QT + fp * 2]);
 
   float inv0 = t_inv, inv1 = t_inv;
+  float nvi[2][2];  // NVFP4: multipliers of [feature 2fp, 2fp + 1][block 2q, 2q + 1]
+  if (RECIPE == kNvfp4) {  // 16x1 units: two per quarter column
+    uint32_t m[2][2] = {{0, 0}, {0, 0}};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      m[0][i >> 4] = umax(m[0][i >> 4], w[i] & 0x7fffu);
+      m[1][i >> 4] = umax(m[1][i >> 4], (w[i] >> 16) & 0x7fffu);
+    }
+    flag_nonfinite(a.status, umax(umax(m[0][0], m[0][1]), umax(m[1][0], m[1][1])));
+    uint8_t *cs = reinterpret_cast<uint8_t *>(a.col_scales) + b * a.cs_bstride;
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t code = nv_block_scale(bits_to_amax(m[f][k]), t_s, nvi[f][k]);
+        // piece-major [ld/128, C, 8]: piece p0/128, feature row c, block 2q + k
+        cs[((p0 / QT) * a.C + c0 + 2 * fp + f) * 8 + 2 * q + k] = (uint8_t)code;
+      }
+  }
   if (RECIPE == kBlockwise || RECIPE == kMx) {
     uint32_t m0 = 0, m1 = 0;
 #pragma unroll
@@ -605,21 +643,34 @@ __global__ __launch_bounds__(QTHREADS) void tile_quant_kernel(TileArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t *wj = &w[8 * j];
+      // NVFP4: rows 16k .. 16k + 15 of the quarter share block 2q + k
+      const float i0 = RECIPE == kNvfp4 ? nvi[0][j >> 1] : inv0;
+      const float i1 = RECIPE == kNvfp4 ? nvi[1][j >> 1] : inv1;
       uint32_t x = 0, y = 0;
-      x = e2m1_pk<0>(x, bf16_lo(wj[0]) * inv0, bf16_lo(wj[1]) * inv0);
-      x = e2m1_pk<1>(x, bf16_lo(wj[2]) * inv0, bf16_lo(wj[3]) * inv0);
-      x = e2m1_pk<2>(x, bf16_lo(wj[4]) * inv0, bf16_lo(wj[5]) * inv0);
-      x = e2m1_pk<3>(x, bf16_lo(wj[6]) * inv0, bf16_lo(wj[7]) * inv0);
-      y = e2m1_pk<0>(y, bf16_hi(wj[0]) * inv1, bf16_hi(wj[1]) * inv1);
-      y = e2m1_pk<1>(y, bf16_hi(wj[2]) * inv1, bf16_hi(wj[3]) * inv1);
-      y = e2m1_pk<2>(y, bf16_hi(wj[4]) * inv1, bf16_hi(wj[5]) * inv1);
-      y = e2m1_pk<3>(y, bf16_hi(wj[6]) * inv1, bf16_hi(wj[7]) * inv1);
+      x = e2m1_pk<0>(x, bf16_lo(wj[0]) * i0, bf16_lo(wj[1]) * i0);
+      x = e2m1_pk<1>(x, bf16_lo(wj[2]) * i0, bf16_lo(wj[3]) * i0);
+      x = e2m1_pk<2>(x, bf16_lo(wj[4]) * i0, bf16_lo(wj[5]) * i0);
+      x = e2m1_pk<3>(x, bf16_lo(wj[6]) * i0, bf16_lo(wj[7]) * i0);
+      y = e2m1_pk<0>(y, bf16_hi(wj[0]) * i1, bf16_hi(wj[1]) * i1);
+      y = e2m1_pk<1>(y, bf16_hi(wj[2]) * i1, bf16_hi(wj[3]) * i1);
+      y = e2m1_pk<2>(y, bf16_hi(wj[4]) * i1, bf16_hi(wj[5]) * i1);
+      y = e2m1_pk<3>(y, bf16_hi(wj[6]) * i1, bf16_hi(wj[7]) * i1);
       d0[j] = x;
       d1[j] = y;
     }
-    *reinterpret_cast<uint4 *>(&ctile[(2 * fp) * CODE_LD4 + q * 16]) = make_uint4(d0[0], d0[1], d0[2], d0[3]);
-    *reinterpret_cast<uint4 *>(&ctile[(2 * fp + 1) * CODE_LD4 + q * 16]) =
-        make_uint4(d1[0], d1[1], d1[2], d1[3]);
+    if constexpr (RECIPE == kNvfp4) {
+      // dword j of this quarter = rows 32q + 8j .. + 7 = step 2q + j / 2, half j % 2
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int off = nv_dword_off(2 * q + (j >> 1), j & 1);
+        *reinterpret_cast<uint32_t *>(&ctile[(2 * fp) * CODE_LD4 + off]) = d0[j];
+        *reinterpret_cast<uint32_t *>(&ctile[(2 * fp + 1) * CODE_LD4 + off]) = d1[j];
+      }
+    } else {
+      *reinterpret_cast<uint4 *>(&ctile[(2 * fp) * CODE_LD4 + q * 16]) = make_uint4(d0[0], d0[1], d0[2], d0[3]);
+      *reinterpret_cast<uint4 *>(&ctile[(2 * fp + 1) * CODE_LD4 + q * 16]) =
+          make_uint4(d1[0], d1[1], d1[2], d1[3]);
+    }
     __syncthreads();
     // 128 feature rows x 64 bytes; 4 lanes per row
 #pragma unroll
@@ -804,7 +855,8 @@ static hipError_t tile_by_recipe(int recipe, const TileArgs &a, bool row, bool c
     case kDelayed: return tile_dispatch<kDelayed, FMT>(a, row, col, grid, st);
     case kBlockwise: return tile_dispatch<kBlockwise, FMT>(a, row, col, grid, st);
     case kMx: return tile_dispatch<kMx, FMT>(a, row, col, grid, st);
-    default: return tile_dispatch<kTile128, FMT>(a, row, col, grid, st);
+    case kTile128: return tile_dispatch<kTile128, FMT>(a, row, col, grid, st);
+    default: return hipErrorInvalidValue;  // NVFP4 has e2m1 elements only
   }
 }
 
@@ -822,7 +874,9 @@ hipError_t launch_sigmoid_sweep(float *out, hipStream_t st) {
 
 hipError_t launch_quantize_act(const QuantActParams &p, hipStream_t st) {
   hipError_t e;
-  if (p.recipe == kTensorwise && p.swiglu) {
+  // tensorwise and NVFP4 (its tensor scale) need the tensor's amax first
+  const bool tensor_amax = p.recipe == kTensorwise || p.recipe == kNvfp4;
+  if (tensor_amax && p.swiglu) {
     // the amax is that of the activation, computed from gate and up
     e = launch_zero(p.amax, 1, st);
     if (e != hipSuccess) return e;
@@ -835,7 +889,7 @@ hipError_t launch_quantize_act(const QuantActParams &p, hipStream_t st) {
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-  } else if (p.recipe == kTensorwise) {
+  } else if (tensor_amax) {
     if (p.row_index) {
       e = launch_zero(p.amax, 1, st);
       if (e != hipSuccess) return e;
@@ -875,20 +929,24 @@ hipError_t launch_quantize_act(const QuantActParams &p, hipStream_t st) {
   a.rgroup = 1;  // token passes: feature tile fastest (measured best)
   a.swiglu = p.swiglu;
   if (p.swiglu) a.stream_x = p.M * p.C * 4 > kStreamBytes;
+  a.rs_tail = p.M * (p.C / 16);      // NVFP4: the tensor scale follows the block scales
+  a.cs_tail = p.C * (p.ld / 16);
   // at least one tile: an empty tensor still gets its tensor scale written
   int64_t ytiles = col ? p.ld / QT : tiles_of(p.M);
   if (ytiles == 0) ytiles = 1;
   const int64_t tiles = ytiles * (p.C / QT);
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
   dim3 grid((unsigned)tiles, 1, 1);
-  if (p.fmt == kE2M1) return tile_dispatch<kMx, kE2M1>(a, row, col, grid, st);
+  if (p.fmt == kE2M1)
+    return p.recipe == kNvfp4 ? tile_dispatch<kNvfp4, kE2M1>(a, row, col, grid, st)
+                              : tile_dispatch<kMx, kE2M1>(a, row, col, grid, st);
   return p.fmt == kE4M3 ? tile_by_recipe<kE4M3>(p.recipe, a, row, col, grid, st)
                         : tile_by_recipe<kE5M2>(p.recipe, a, row, col, grid, st);
 }
 
 hipError_t launch_quantize_weight(const QuantWeightParams &p, hipStream_t st) {
   hipError_t e;
-  if (p.recipe == kTensorwise) {
+  if (p.recipe == kTensorwise || p.recipe == kNvfp4) {
     e = launch_amax(p.w, p.E, p.K * p.N, p.amax, p.status, st);
     if (e != hipSuccess) return e;
   }
@@ -922,6 +980,13 @@ hipError_t launch_quantize_weight(const QuantWeightParams &p, hipStream_t st) {
     a.col_scales = p.kmajor_scales;  // [E, N, K/32]
     a.rs_bstride = p.K * (p.N / 32);
     a.cs_bstride = p.N * (p.K / 32);
+  } else if (recipe == kNvfp4) {
+    a.row_scales = p.nmajor_scales;  // [E, N/128, K, 8] block codes, then fp32 [E]
+    a.col_scales = p.kmajor_scales;  // [E, K/128, N, 8] block codes, then fp32 [E]
+    a.rs_bstride = p.K * (p.N / 16);
+    a.cs_bstride = p.N * (p.K / 16);
+    a.rs_tail = (int64_t)p.E * a.rs_bstride;
+    a.cs_tail = (int64_t)p.E * a.cs_bstride;
   } else {
     a.row_scales = p.nmajor_scales;  // [E]
     a.col_scales = p.kmajor_scales;
@@ -931,7 +996,9 @@ hipError_t launch_quantize_weight(const QuantWeightParams &p, hipStream_t st) {
   const int64_t tiles = (p.K / QT) * (p.N / QT);
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
   dim3 grid((unsigned)tiles, 1, (unsigned)p.E);
-  if (p.fmt == kE2M1) return tile_dispatch<kMx, kE2M1>(a, row, col, grid, st);
+  if (p.fmt == kE2M1)
+    return recipe == kNvfp4 ? tile_dispatch<kNvfp4, kE2M1>(a, row, col, grid, st)
+                            : tile_dispatch<kMx, kE2M1>(a, row, col, grid, st);
   return p.fmt == kE4M3 ? tile_by_recipe<kE4M3>(recipe, a, row, col, grid, st)
                         : tile_by_recipe<kE5M2>(recipe, a, row, col, grid, st);
 }

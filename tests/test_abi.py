@@ -189,7 +189,8 @@ def test_quantize_act_sizes(M, C, E):
 def test_quantize_act_sizes_validation():
     assert _act_sizes(16, 200, 0, 1)[0] == _lib.BAD_SHAPE
     assert _act_sizes(-1, 128, 0, 1)[0] == _lib.INVALID_ARGUMENT
-    assert _act_sizes(16, 128, 4, 1)[0] == _lib.INVALID_ARGUMENT
+    assert _act_sizes(16, 128, 5, 1)[0] == _lib.INVALID_ARGUMENT      # no recipe 5
+    assert _act_sizes(16, 128, 4, 1)[0] == _lib.UNSUPPORTED           # NVFP4 takes e2m1 elements only
     assert _act_sizes(16, 128, 0, -1)[0] == _lib.INVALID_ARGUMENT
     assert _act_sizes(1 << 31, 128, 0, 1)[0] == _lib.BAD_SHAPE
     assert _lib.status_of("mxsg_quantize_act_sizes", 16, 128, 0, 0, 1, None) == _lib.INVALID_ARGUMENT
@@ -221,6 +222,21 @@ def test_quantize_weight_sizes_validation():
     assert _qw(K=130) == _w_sizes(2, 130, 256, 0)[0]
     assert _w_sizes(2, 256, 256, 2, fmt=2)[0] == _lib.UNSUPPORTED
     assert _w_sizes(2, 256, 384, 3, fmt=2)[1] == [2 * 256 * 384 // 2, 2 * 256 * 384 // 32] * 2
+    # NVFP4: half-byte codes; e4m3 block codes per 16 elements, then one fp32 tensor scale per expert
+    assert _w_sizes(2, 256, 384, 4, fmt=2)[1] == [2 * 256 * 384 // 2, 2 * 256 * 384 // 16 + 8] * 2
+    assert _w_sizes(2, 256, 384, 4, fmt=0)[0] == _lib.UNSUPPORTED
+
+
+def test_nvfp4_act_sizes():
+    M, C, E = 7, 256, 3
+    ld = _lib.load().mxsg_padded_capacity(M, E)
+    st, b = _act_sizes(M, C, 4, E, fmt=2)
+    assert st == _lib.OK
+    assert b == [(M + 1) * C // 2, M * C // 16 + 4, C * ld // 2, C * ld // 16 + 4, 4 * (E + 1)]
+    # grouped GEMM: NVFP4 needs e2m1 on both sides, and e2m1 no other recipe than MX / NVFP4
+    assert _mm_check(recipe=4, fa=2, fb=2, lda=128, ldb=128) == _lib.OK
+    assert _mm_check(recipe=4, fa=0, fb=0) == _lib.UNSUPPORTED
+    assert _mm_check(recipe=2, fa=2, fb=2, lda=128, ldb=128) == _lib.UNSUPPORTED
 
 
 def _mm_check(**kw):
