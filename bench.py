@@ -29,6 +29,7 @@ sys.path.insert(0, HERE)
 
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
 PEAK_FP4_TFLOPS = 10100.0      # MI355X dense FP4 / FP6 MFMA
+PEAK_F16_TFLOPS = 2500.0       # MI355X dense FP16 / BF16 MFMA (the NVFP4 GEMM's arithmetic)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 GEMM_SOURCE = os.path.join(HERE, "mx_scaled_grouped_amd", "csrc", "gemm.hip")
 
@@ -38,6 +39,7 @@ WORKLOADS = {
     "deepseek-block": 4,
     "llama4-mx": 5,
     "llama4-mxfp4": 6,
+    "llama4-nvfp4": 7,
 }
 
 
@@ -76,7 +78,7 @@ def _normal(torch, g, shape, std):
 def _outliers(torch, g, cid, t):
     """Llama4-shaped workloads: 0.1% of the elements, drawn without
     replacement, multiplied by 50."""
-    if cid not in (5, 6):
+    if cid not in (5, 6, 7):
         return t
     flat = t.view(-1)
     n = flat.numel()
@@ -141,14 +143,15 @@ class Step:
         self.rt = api.route(ids, spec.experts)
         self.ge = self.rt.group_ends
         self.gather = gather         # False: quantize the explicit gathered copy a_gu
-        # "mxfp4" is the MX recipe with e2m1 elements for every operand
+        # "mxfp4" is the MX recipe with e2m1 elements for every operand;
+        # NVFP4 has e2m1 elements only
         self.recipe = "mx" if recipe == "mxfp4" else recipe
-        if recipe == "mxfp4":
+        if recipe in ("mxfp4", "nvfp4"):
             self.fa = self.fw = self.fg = 2
         else:
             self.fa, self.fw = 0, 0
             self.fg = 1 if recipe == "dl" else 0     # hybrid: e5m2 gradients
-        self.fp4 = recipe == "mxfp4"
+        self.fp4 = recipe in ("mxfp4", "nvfp4")
         self.E = spec.experts
         self.bwd = "dgrad" in spec.modes
         self.q = {}        # reused quantized outputs
@@ -234,9 +237,8 @@ class Step:
         """Algorithmic GEMM FLOPs and quantization bytes per call name."""
         spec, r = self.spec, self.recipe
         flops, byts = {}, {}
-        code = 0.5 if self.fp4 else 1.0      # bytes per element of one code layout
-        per_layout = {"tw": code, "dl": code, "block": code + 4 / 128, "mx": code + 1 / 32}[r]
-        read = {"tw": 4.0, "dl": 2.0, "block": 2.0, "mx": 2.0}[r]   # tw reads twice (amax pass)
+        per_layout = layout_bytes(r, self.fp4)
+        read = 4.0 if r in ("tw", "nvfp4") else 2.0   # tw and nvfp4 read twice (tensor amax pass)
         w_layout = {"block": 1.0 + 4 / 16384}.get(r, per_layout)
         for which in spec.gemms:
             K, N = spec.gemm_shape(which)
@@ -250,6 +252,25 @@ class Step:
                 flops[f"gemm_wgrad_{which}"] = f
                 byts[f"quant_dy_{which}"] = R * N * (read + 2 * per_layout)
         return flops, byts
+
+
+def layout_bytes(recipe, fp4):
+    """Algorithmic bytes per element of one quantized layout: the code plus
+    its share of the scales (fp32 per 128 for blockwise, one E8M0 byte per
+    32 for MX, one e4m3 byte per 16 for NVFP4)."""
+    code = 0.5 if fp4 else 1.0
+    return {"tw": code, "dl": code, "block": code + 4 / 128, "mx": code + 1 / 32,
+            "nvfp4": code + 1 / 16}[recipe]
+
+
+def gemm_peak(step):
+    """(dense MFMA peak in TFLOP/s, the kernel's arithmetic) of the step's
+    grouped GEMM."""
+    if step.recipe == "nvfp4":
+        return PEAK_F16_TFLOPS, "f16 MFMA over exactly dequantized NVFP4 operands"
+    if step.fp4:
+        return PEAK_FP4_TFLOPS, "fp4 scaled MFMA"
+    return PEAK_FP8_TFLOPS, "fp8 scaled MFMA"
 
 
 def attainable_ms(spec, group_sizes, modes, peak_tflops=PEAK_FP8_TFLOPS, code_bytes=1.0):
@@ -306,9 +327,9 @@ def swiglu_quant_rate(torch, api, step, spec, R):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
-    code = 0.5 if step.fp4 else 1.0
-    per_layout = {"tw": code, "dl": code, "block": code + 4 / 128, "mx": code + 1 / 32}[step.recipe]
-    read = 8.0 if step.recipe == "tw" else 4.0      # gate and up (bf16); tensorwise reads them twice (amax pass)
+    per_layout = layout_bytes(step.recipe, step.fp4)
+    # gate and up (bf16); tensorwise and NVFP4 read them twice (amax pass)
+    read = 8.0 if step.recipe in ("tw", "nvfp4") else 4.0
     nbytes = R * F * (read + (2 if step.bwd else 1) * per_layout)
     gbs = nbytes / (ms * 1e-3) / 1e9
     del h, q
@@ -372,8 +393,11 @@ def cpu_baseline(cid, rows, cols):
     K, N = spec.gemm_shape("gu")
     N = min(N, cols)
     m = min(rows, int(OR.route(topk.expert_ids, topk.n_experts)["group_ends"][0]))
-    rec = {"tw": "tw", "dl": "dl", "block": "block", "mx": "mx", "mxfp4": "mx"}[spec.recipe]
-    fq = OF.E2M1 if spec.recipe == "mxfp4" else OF.E4M3     # activations and weights
+    rec = {"tw": "tw", "dl": "dl", "block": "block", "mx": "mx", "mxfp4": "mx", "nvfp4": "nvfp4"}[spec.recipe]
+    fq = OF.E2M1 if spec.recipe in ("mxfp4", "nvfp4") else OF.E4M3     # activations and weights
+
+    def sc(q, key):
+        return (q[key], q["tensor_scale"]) if rec == "nvfp4" else q[key]
     a = W.normal_bf16(cid, W.T_X, (m, K))
     w = W.normal_bf16(cid, W.T_W1, (1, K, N), std=0.02, chunk_rows=256)
     ge = np.array([m], np.int32)
@@ -383,17 +407,17 @@ def cpu_baseline(cid, rows, cols):
     t0 = time.perf_counter()
     qa = OQ.quantize_act(a, rec, fq, ge, rowwise=True, colwise=bwd, dl_scale=dl)
     qw = OQ.quantize_weight(w, rec, fq, dl_scale=(np.ones(1, np.float32), np.ones(1, np.float32)))
-    A = OG.deq_act_rows(qa["row_codes"], qa["row_scales"], rec, fq)
+    A = OG.deq_act_rows(qa["row_codes"], sc(qa, "row_scales"), rec, fq)
     Y = OG.round_bf16(OG.grouped_fwd(A, OG.deq_weight(qw, rec, fq, "k"), ge))
     flops = 2.0 * m * K * N
     if bwd:
         dy = W.normal_bf16(cid, W.T_DY1, (m, N), std=2.0 ** -10)
         qd = OQ.quantize_act(dy, rec, fg, ge, rowwise=True, colwise=True, dl_scale=dl)
-        D = OG.deq_act_rows(qd["row_codes"], qd["row_scales"], rec, fg)
+        D = OG.deq_act_rows(qd["row_codes"], sc(qd, "row_scales"), rec, fg)
         dA = OG.round_bf16(OG.grouped_dgrad(D, OG.deq_weight(qw, rec, fq, "n"), ge))
         P = qa["padded_starts"]
-        At = OG.unpad_cols(OG.deq_act_cols(qa["col_codes"], qa["col_scales"], rec, fq), P, ge)
-        Dt = OG.unpad_cols(OG.deq_act_cols(qd["col_codes"], qd["col_scales"], rec, fg), P, ge)
+        At = OG.unpad_cols(OG.deq_act_cols(qa["col_codes"], sc(qa, "col_scales"), rec, fq), P, ge)
+        Dt = OG.unpad_cols(OG.deq_act_cols(qd["col_codes"], sc(qd, "col_scales"), rec, fg), P, ge)
         dW = OG.round_f32(OG.grouped_wgrad(At, Dt, ge, 1))
         flops *= 3
     dt = time.perf_counter() - t0
@@ -491,8 +515,8 @@ def main():
     launches = len(gemm_ms)
     achieved = step_flops / (gemm_total_ms * 1e-3) / 1e12
     quant_agg = sum(byts.values()) / (quant_total_ms * 1e-3) / 1e9
-    peak = PEAK_FP4_TFLOPS if step.fp4 else PEAK_FP8_TFLOPS
-    att = attainable_ms(spec, group_sizes, spec.modes, peak, 0.5 if step.fp4 else 1.0)
+    peak, arith = gemm_peak(step)
+    att = attainable_ms(spec, group_sizes, spec.modes, peak, layout_bytes(step.recipe, step.fp4))
     att_frac = {k: att[k] / gemm_ms[k] for k in gemm_ms}
     att_total = sum(att[k] for k in gemm_ms) / gemm_total_ms
 
@@ -541,7 +565,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("fp4(e2m1) codes with E8M0 block scales" if step.fp4 else "fp8(e4m3/e5m2) codes")
+        "dtype": {"nvfp4": "fp4(e2m1) codes with e4m3 block scales and fp32 tensor scales",
+                  "mx": "fp4(e2m1) codes with E8M0 block scales" if step.fp4 else "fp8(e4m3) codes with E8M0 block scales"
+                  }.get(step.recipe, "fp8(e4m3/e5m2) codes")
                  + ", fp32 accumulate, bf16/fp32 out",
         "data": "synthetic (seeded torch generator on the GPU; routing seeded numpy)",
         "config": {"workload": spec.name, "experts": spec.experts, "tokens": spec.tokens,
@@ -551,7 +577,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(args.workload),
-                     "kernel": "grouped_gemm_kernel (every GEMM launch of a step)",
+                     "kernel": ("nvfp4_gemm_kernel" if step.recipe == "nvfp4" else "grouped_gemm_kernel")
+                               + " (every GEMM launch of a step)",
+                     "arithmetic": arith,
                      "launches_per_step": launches,
                      "flops_per_launch": step_flops / launches,
                      "avg_launch_ms": round(gemm_total_ms / launches, 4)},

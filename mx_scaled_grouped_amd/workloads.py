@@ -125,7 +125,7 @@ class WorkloadSpec:
     topk: int
     hidden: int            # K of the gate/up GEMM
     ffn: int               # per-expert FFN width
-    recipe: str            # "tw", "dl", "block", "mx", "mxfp4" (MX with e2m1 elements)
+    recipe: str            # "tw", "dl", "block", "mx", "mxfp4" (MX with e2m1 elements), "nvfp4"
     modes: tuple           # subset of ("fwd", "dgrad", "wgrad")
     gemms: tuple           # ("gu",) or ("gu", "dn")
     steps: int = 1
@@ -154,6 +154,9 @@ SPECS: Dict[int, WorkloadSpec] = {
     # the MXFP4 variant of the same shapes: e2m1 elements for every operand
     6: WorkloadSpec(6, "llama4-scout-experts-mxfp4", 16, 16384, 1, 5120, 8192, "mxfp4",
                     ("fwd", "dgrad", "wgrad"), ("gu", "dn")),
+    # the NVFP4 variant: e2m1 elements, e4m3 scale per 16, fp32 per tensor
+    7: WorkloadSpec(7, "llama4-scout-experts-nvfp4", 16, 16384, 1, 5120, 8192, "nvfp4",
+                    ("fwd", "dgrad", "wgrad"), ("gu", "dn")),
 }
 
 C4_MASKED = (0, 21, 42, 63)
@@ -168,8 +171,8 @@ def routing_for(cid: int) -> TopK:
         return route_topk(2, s.tokens, s.experts, s.topk)   # C3 reuses C2's routing
     if cid == 4:
         return route_topk(cid, s.tokens, s.experts, s.topk, masked=C4_MASKED)
-    if cid in (5, 6):
-        return route_zipf(5, s.tokens, s.experts, 1.1)   # C6 reuses C5's routing
+    if cid in (5, 6, 7):
+        return route_zipf(5, s.tokens, s.experts, 1.1)   # the FP4 variants reuse C5's routing
     raise KeyError(cid)
 
 
@@ -180,7 +183,7 @@ def token_activation(cid: int, step: int = 0) -> np.ndarray:
     s = SPECS[cid]
     std = 1.01 ** step if cid == 3 else 1.0
     x = normal_bf16(cid, T_X, (s.tokens, s.hidden), std=std, step=step)
-    if cid in (5, 6):
+    if cid in (5, 6, 7):
         x = _outliers(cid, T_X, x)
     return x
 
@@ -191,7 +194,7 @@ def down_activation(cid: int, rows: int, step: int = 0) -> np.ndarray:
     s = SPECS[cid]
     std = 1.01 ** step if cid == 3 else 1.0
     a = normal_bf16(cid, T_A2, (rows, s.ffn), std=std, step=step)
-    if cid in (5, 6):
+    if cid in (5, 6, 7):
         a = _outliers(cid, T_A2, a)
     return a
 

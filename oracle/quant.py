@@ -176,9 +176,9 @@ def nvfp4_blocks(xb, s_t):
     return cast(xb, inv[..., None], E2M1), sb
 
 
-def _nvfp4_act(x, group_ends, rowwise, colwise) -> dict:
+def _nvfp4_act(x, group_ends, rowwise, colwise, tensor_amax=None) -> dict:
     M, C = x.shape
-    am = amax_of(x)
+    am = amax_of(x) if tensor_amax is None else np.float32(tensor_amax)
     s_t = nvfp4_tensor_scale(am)
     out = {"amax": np.array([am], np.float32), "tensor_scale": np.array([s_t], np.float32)}
     if rowwise:
@@ -203,9 +203,10 @@ def _nvfp4_act(x, group_ends, rowwise, colwise) -> dict:
     return out
 
 
-def _nvfp4_weight(w) -> dict:
+def _nvfp4_weight(w, tensor_amax=None) -> dict:
     E, K, N = w.shape
-    am = np.array([amax_of(w[e]) for e in range(E)], np.float32)
+    am = (np.array([amax_of(w[e]) for e in range(E)], np.float32) if tensor_amax is None
+          else np.asarray(tensor_amax, np.float32).reshape(E))
     s_t = nvfp4_tensor_scale(am)
     cn, sn = nvfp4_blocks(w.reshape(E, K, N // NV_BLOCK, NV_BLOCK), s_t[:, None, None])
     wt = np.ascontiguousarray(w.transpose(0, 2, 1))                  # [E, N, K]
@@ -242,7 +243,7 @@ def check_groups(group_ends, M: int):
 
 def quantize_act(x_bf16, recipe: str, fmt: Fp8Format, group_ends=None,
                  rowwise: bool = True, colwise: bool = False,
-                 dl_scale: Optional[tuple] = None) -> dict:
+                 dl_scale: Optional[tuple] = None, tensor_amax=None) -> dict:
     """Quantize a token-major tensor [M, C] (C = the feature dimension).
 
     Returns a dict with ``amax`` (tw/dl/nvfp4), ``row_codes`` [M, C] u8 and
@@ -253,6 +254,8 @@ def quantize_act(x_bf16, recipe: str, fmt: Fp8Format, group_ends=None,
     uint8 e4m3 block codes rows [M, C/16], cols [C, P_E/16], plus
     ``tensor_scale`` float32 [1].
     dl_scale = (s, inv) float32 from the delayed-scaling state.
+    tensor_amax (nvfp4): the tensor unit's amax when x is a sample of a
+    larger tensor (the tensor scale is that of the whole tensor).
     """
     x_bf16 = np.asarray(x_bf16, dtype=np.uint16)
     M, C = x_bf16.shape
@@ -263,7 +266,7 @@ def quantize_act(x_bf16, recipe: str, fmt: Fp8Format, group_ends=None,
         raise ValueError("feature dim must be a multiple of 128")
     x = bf16_to_f32(x_bf16)
     if recipe == "nvfp4":
-        return _nvfp4_act(x, group_ends, rowwise, colwise)
+        return _nvfp4_act(x, group_ends, rowwise, colwise, tensor_amax)
     out = {}
     if recipe in ("tw", "dl"):
         am = amax_of(x)
@@ -366,7 +369,7 @@ def _block_codes(xb, am, recipe, fmt):
 
 # ---- weights [E, K, N] ----------------------------------------------------
 
-def quantize_weight(w_bf16, recipe: str, fmt: Fp8Format, dl_scale=None) -> dict:
+def quantize_weight(w_bf16, recipe: str, fmt: Fp8Format, dl_scale=None, tensor_amax=None) -> dict:
     """Quantize expert weights [E, K, N] (K contracts in forward, N in dgrad).
 
     Returns ``kmajor_codes`` [E, N, K] (forward operand, contiguous along K),
@@ -385,7 +388,7 @@ def quantize_weight(w_bf16, recipe: str, fmt: Fp8Format, dl_scale=None) -> dict:
         raise ValueError("K and N must be multiples of 128")
     w = bf16_to_f32(w_bf16)
     if recipe == "nvfp4":
-        return _nvfp4_weight(w)
+        return _nvfp4_weight(w, tensor_amax)
     out = {}
     if recipe in ("tw", "dl"):
         am = np.array([amax_of(w[e]) for e in range(E)], np.float32)

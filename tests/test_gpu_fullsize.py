@@ -7,11 +7,12 @@ sampled outputs: every group's first two and last two rows plus random
 rows in between, and whole 128-wide blocks of the feature dimensions (the
 first, the last and a random one). Quantization of a sample is exactly
 the quantization of the full tensor restricted to it because
-  * tensorwise / delayed scales come from the amax of the FULL tensor,
-    computed by the oracle (tensorwise: current amax; delayed: the
-    oracle's own amax-history state after the previous step), and the
-    sampled rows/columns are cast with that scale;
-  * 1x128 / 1x32 row blocks lie inside one row and 128x1 / 32x1 column
+  * tensorwise / delayed scales and the NVFP4 tensor scales come from the
+    amax of the FULL tensor, computed by the oracle (tensorwise and NVFP4:
+    current amax; delayed: the oracle's own amax-history state after the
+    previous step), and the sampled rows/columns are cast with that scale;
+  * 1x128 / 1x32 / 1x16 row blocks lie inside one row and 128x1 / 32x1 /
+    16x1 column
     blocks inside one column, and the weight's 128x128 tiles inside a
     sampled 128-block; group boundaries are kept because whole columns are
     taken for the column-wise layout.
@@ -43,7 +44,7 @@ def _codes(t, fmt):
     c = _np(t)
     return OF.unpack_nibbles(c) if fmt is OF.E2M1 else c
 TOL = 1e-3
-WORKLOADS = ["mixtral-tw", "mixtral-dl", "deepseek-block", "llama4-mx", "llama4-mxfp4"]
+WORKLOADS = ["mixtral-tw", "mixtral-dl", "deepseek-block", "llama4-mx", "llama4-mxfp4", "llama4-nvfp4"]
 
 _cache = {}
 
@@ -67,6 +68,27 @@ def _take(t, *idx):
     for d, ix in idx:
         t = t.index_select(d, torch.from_numpy(np.asarray(ix, np.int64)).to(t.device))
     return t
+
+
+def _sel_codes(t, rec, fmt, *idx):
+    """Host codes (one per uint8) of the rows / columns idx of device codes;
+    NVFP4 codes sit in their own nibble order inside each 128-element piece."""
+    if rec == "nvfp4":
+        from mx_scaled_grouped_amd import api
+        return _np(_take(api.unpack_nvfp4_codes(t), *idx))
+    return _codes(_take(_unpack(t), *idx), fmt)
+
+
+def _nv_scales(t, rows, L, units=1):
+    """(host e4m3 block codes [units, rows, L/16], host fp32 tensor scales)."""
+    from mx_scaled_grouped_amd import api
+    b, ts = api.nvfp4_scales(t, rows, L, units)
+    return _np(b), _np(ts)
+
+
+def _deq_sc(r, key, rec):
+    """The oracle's scales of r[key] as its dequantization takes them."""
+    return (r[key], r["tensor_scale"]) if rec == "nvfp4" else r[key]
 
 
 def _run(name):
@@ -156,30 +178,35 @@ def _block_sample(D, seed, blk=128):
 
 
 def _act_scale(st, which, kind, x_bits, fmt):
-    """(recipe the oracle runs on the sample, dl_scale) for an activation/gradient."""
+    """(recipe the oracle runs on the sample, its keyword arguments) for an
+    activation/gradient: the full tensor's scale or amax."""
     r = st["recipe"]
     if r == "tw":
-        return "dl", OQ.fp32_scale_pair(OQ.amax_of(OQ.bf16_to_f32(x_bits)), fmt)
+        return "dl", {"dl_scale": OQ.fp32_scale_pair(OQ.amax_of_bf16_bits(x_bits), fmt)}
+    if r == "nvfp4":
+        return r, {"tensor_amax": OQ.amax_of_bf16_bits(x_bits)}
     if r == "dl":
         spec = st["spec"]
         gi = spec.gemms.index(which)
         s, inv = st["scales"][kind]
-        return "dl", (s[gi], inv[gi])
-    return r, None
+        return "dl", {"dl_scale": (s[gi], inv[gi])}
+    return r, {}
 
 
 def _w_scale(st, which, w_bits, fmt):
     r = st["recipe"]
     E = w_bits.shape[0]
-    if r == "tw":
-        am = np.array([OQ.amax_of(OQ.bf16_to_f32(w_bits[e])) for e in range(E)], np.float32)
-        return "dl", OQ.fp32_scale_pair(am, fmt)
+    if r in ("tw", "nvfp4"):
+        am = np.array([OQ.amax_of_bf16_bits(w_bits[e]) for e in range(E)], np.float32)
+        if r == "nvfp4":
+            return r, {"tensor_amax": am}
+        return "dl", {"dl_scale": OQ.fp32_scale_pair(am, fmt)}
     if r == "dl":
         spec = st["spec"]
         u0 = len(spec.gemms) + spec.gemms.index(which) * E
         s, inv = st["scales"]["f"]
-        return "dl", (s[u0:u0 + E], inv[u0:u0 + E])
-    return r, None
+        return "dl", {"dl_scale": (s[u0:u0 + E], inv[u0:u0 + E])}
+    return r, {}
 
 
 def _sc(t, rec):
@@ -190,12 +217,19 @@ def _sc(t, rec):
     return _np(t)
 
 
-def _check_scales_rows(gpu_scales, ora_scales, rec, sel, what):
-    g = _sc(gpu_scales, rec)
+def _check_scales_rows(q, r, rec, sel, what):
+    """Row-wise scales of a quantized token tensor q at rows sel against the
+    oracle's r."""
+    if rec == "nvfp4":
+        b, ts = _nv_scales(q.row_scales, q.M, q.C)
+        assert_bits_equal(b[0][sel], r["row_scales"], what + " (e4m3 blocks)")
+        assert_bits_equal(ts, r["tensor_scale"], what + " (tensor scale)")
+        return
+    g = _sc(q.row_scales, rec)
     if rec == "dl":
-        assert_bits_equal(g.reshape(-1)[:1], np.asarray(ora_scales, np.float32).reshape(-1)[:1], what)
+        assert_bits_equal(g.reshape(-1)[:1], np.asarray(r["row_scales"], np.float32).reshape(-1)[:1], what)
     else:
-        assert_bits_equal(g[sel], ora_scales, what)
+        assert_bits_equal(g[sel], r["row_scales"], what)
 
 
 def _check_err(got, ref, ge_s, what):
@@ -246,25 +280,29 @@ def forward_check(st, which, data, name):
     w_bits = _bits(st["weights"][which])
     rows, ge_s = _row_sample(ge, 11)
     ncols, nblk = _block_sample(N, 12)
-    rec, dls = _act_scale(st, which, "f", a_bits, fa)
-    ra = OQ.quantize_act(a_bits[rows], rec, fa, dl_scale=dls)
+    rec, kw = _act_scale(st, which, "f", a_bits, fa)
+    ra = OQ.quantize_act(a_bits[rows], rec, fa, **kw)
     qa = step.q["a_" + which]
-    assert_bits_equal(_codes(_take(_unpack(qa.row_codes), (0, rows)), fa), ra["row_codes"], "activation codes")
-    _check_scales_rows(qa.row_scales, ra["row_scales"], rec, rows, "activation scales")
+    assert_bits_equal(_sel_codes(qa.row_codes, rec, fa, (0, rows)), ra["row_codes"], "activation codes")
+    _check_scales_rows(qa, ra, rec, rows, "activation scales")
     fw = FMT[step.fw]
-    wrec, wdl = _w_scale(st, which, w_bits, fw)
-    rw = OQ.quantize_weight(np.ascontiguousarray(w_bits[:, :, ncols]), wrec, fw, dl_scale=wdl)
+    wrec, wkw = _w_scale(st, which, w_bits, fw)
+    rw = OQ.quantize_weight(np.ascontiguousarray(w_bits[:, :, ncols]), wrec, fw, **wkw)
     qw = step.q["w_" + which]
-    assert_bits_equal(_codes(_take(_unpack(qw.kmajor_codes), (1, ncols)), fw), rw["kmajor_codes"],
+    assert_bits_equal(_sel_codes(qw.kmajor_codes, wrec, fw, (1, ncols)), rw["kmajor_codes"],
                       "weight k-major codes")
-    ks = _sc(qw.kmajor_scales, wrec)
-    if wrec == "dl":
-        assert_bits_equal(ks, rw["kmajor_scales"], "weight scales")
+    if wrec == "nvfp4":
+        b, ts = _nv_scales(qw.kmajor_scales, N, K, qw.E)
+        assert_bits_equal(b[:, ncols, :], rw["kmajor_scales"], "weight e4m3 blocks (k-major)")
+        assert_bits_equal(ts, rw["tensor_scale"], "weight tensor scales")
+    elif wrec == "dl":
+        assert_bits_equal(_sc(qw.kmajor_scales, wrec), rw["kmajor_scales"], "weight scales")
     elif wrec == "block":
-        assert_bits_equal(ks[:, :, nblk], rw["kmajor_scales"], "weight tile scales")
+        assert_bits_equal(_sc(qw.kmajor_scales, wrec)[:, :, nblk], rw["kmajor_scales"], "weight tile scales")
     else:
-        assert_bits_equal(ks[:, ncols, :], rw["kmajor_scales"], "weight MX scales (k blocks)")
-    ref = OG.round_bf16(OG.grouped_fwd(OG.deq_act_rows(ra["row_codes"], ra["row_scales"], rec, fa),
+        assert_bits_equal(_sc(qw.kmajor_scales, wrec)[:, ncols, :], rw["kmajor_scales"],
+                          "weight MX scales (k blocks)")
+    ref = OG.round_bf16(OG.grouped_fwd(OG.deq_act_rows(ra["row_codes"], _deq_sc(ra, "row_scales", rec), rec, fa),
                                        OG.deq_weight(rw, wrec, fw, "k"), ge_s))
     y = step.out["y_" + which]
     got = OG.bf16_bits_to_f64(_bits(_take(y, (0, rows), (1, ncols))))
@@ -286,23 +324,27 @@ def dgrad_check(st, which, data, name):
     w_bits = _bits(st["weights"][which])
     rows, ge_s = _row_sample(ge, 21)
     kcols, kblk = _block_sample(K, 22)
-    rec, dls = _act_scale(st, which, "g", d_bits, fg)
-    rd = OQ.quantize_act(d_bits[rows], rec, fg, dl_scale=dls)
+    rec, kw = _act_scale(st, which, "g", d_bits, fg)
+    rd = OQ.quantize_act(d_bits[rows], rec, fg, **kw)
     qd = step.q["dy_" + which]
-    assert_bits_equal(_codes(_take(_unpack(qd.row_codes), (0, rows)), fg), rd["row_codes"], "gradient codes")
-    _check_scales_rows(qd.row_scales, rd["row_scales"], rec, rows, "gradient scales")
+    assert_bits_equal(_sel_codes(qd.row_codes, rec, fg, (0, rows)), rd["row_codes"], "gradient codes")
+    _check_scales_rows(qd, rd, rec, rows, "gradient scales")
     fw = FMT[step.fw]
-    wrec, wdl = _w_scale(st, which, w_bits, fw)
-    rw = OQ.quantize_weight(np.ascontiguousarray(w_bits[:, kcols, :]), wrec, fw, dl_scale=wdl)
+    wrec, wkw = _w_scale(st, which, w_bits, fw)
+    rw = OQ.quantize_weight(np.ascontiguousarray(w_bits[:, kcols, :]), wrec, fw, **wkw)
     qw = step.q["w_" + which]
-    assert_bits_equal(_codes(_take(_unpack(qw.nmajor_codes), (1, kcols)), fw), rw["nmajor_codes"],
+    assert_bits_equal(_sel_codes(qw.nmajor_codes, wrec, fw, (1, kcols)), rw["nmajor_codes"],
                       "weight n-major codes")
-    ns = _sc(qw.nmajor_scales, wrec)
-    if wrec == "block":
-        assert_bits_equal(ns[:, kblk, :], rw["nmajor_scales"], "weight tile scales")
+    if wrec == "nvfp4":
+        b, ts = _nv_scales(qw.nmajor_scales, K, N, qw.E)
+        assert_bits_equal(b[:, kcols, :], rw["nmajor_scales"], "weight e4m3 blocks (n-major)")
+        assert_bits_equal(ts, rw["tensor_scale"], "weight tensor scales (n-major)")
+    elif wrec == "block":
+        assert_bits_equal(_sc(qw.nmajor_scales, wrec)[:, kblk, :], rw["nmajor_scales"], "weight tile scales")
     elif wrec == "mx":
-        assert_bits_equal(ns[:, kcols, :], rw["nmajor_scales"], "weight MX scales (n blocks)")
-    ref = OG.round_bf16(OG.grouped_dgrad(OG.deq_act_rows(rd["row_codes"], rd["row_scales"], rec, fg),
+        assert_bits_equal(_sc(qw.nmajor_scales, wrec)[:, kcols, :], rw["nmajor_scales"],
+                          "weight MX scales (n blocks)")
+    ref = OG.round_bf16(OG.grouped_dgrad(OG.deq_act_rows(rd["row_codes"], _deq_sc(rd, "row_scales", rec), rec, fg),
                                          OG.deq_weight(rw, wrec, fw, "n"), ge_s))
     da = step.out["da_" + which]
     got = OG.bf16_bits_to_f64(_bits(_take(da, (0, rows), (1, kcols))))
@@ -329,20 +371,24 @@ def wgrad_check(st, which, data, name):
     sides = []
     for x_bits, cols, fmt, kind, q, tag in ((a_bits, kcols, fa, "f", qa, "activation"),
                                             (d_bits, ncols, fg, "g", qd, "gradient")):
-        rec, dls = _act_scale(st, which, kind, x_bits, fmt)
+        rec, kw = _act_scale(st, which, kind, x_bits, fmt)
         rc = OQ.quantize_act(np.ascontiguousarray(x_bits[:, cols]), rec, fmt, ge, rowwise=False,
-                             colwise=True, dl_scale=dls)
+                             colwise=True, **kw)
         P = rc["padded_starts"]
         assert np.array_equal(_np(q.padded_starts).astype(np.int64), P), tag + " padded starts"
-        cc = _codes(_take(_unpack(q.col_codes), (0, cols)), fmt)
+        cc = _sel_codes(q.col_codes, rec, fmt, (0, cols))
         assert_bits_equal(cc[:, :P[-1]], rc["col_codes"], tag + " column codes")
-        cs = _sc(q.col_scales, rec)
-        if rec == "dl":
-            assert_bits_equal(cs[:1], rc["col_scales"], tag + " column scale")
+        if rec == "nvfp4":
+            b, ts = _nv_scales(q.col_scales, q.C, q.ld)
+            assert_bits_equal(b[0][cols][:, :P[-1] // 16], rc["col_scales"], tag + " column e4m3 blocks")
+            assert_bits_equal(ts, rc["tensor_scale"], tag + " column tensor scale")
+        elif rec == "dl":
+            assert_bits_equal(_sc(q.col_scales, rec)[:1], rc["col_scales"], tag + " column scale")
         else:
             blk = 128 if rec == "block" else 32
-            assert_bits_equal(cs[cols][:, :P[-1] // blk], rc["col_scales"], tag + " column scales")
-        deq = OG.unpad_cols(OG.deq_act_cols(rc["col_codes"], rc["col_scales"], rec, fmt), P, ge)
+            assert_bits_equal(_sc(q.col_scales, rec)[cols][:, :P[-1] // blk], rc["col_scales"],
+                              tag + " column scales")
+        deq = OG.unpad_cols(OG.deq_act_cols(rc["col_codes"], _deq_sc(rc, "col_scales", rec), rec, fmt), P, ge)
         sides.append(deq)
     ref = OG.round_f32(OG.grouped_wgrad(sides[0], sides[1], ge, E))
     dw = _np(_take(step.out["dw_" + which], (1, kcols), (2, ncols))).astype(np.float64)
