@@ -423,8 +423,20 @@ def cpu_baseline(cid, rows, cols):
     dt = time.perf_counter() - t0
     mode = "fwd+dgrad+wgrad" if bwd else "fwd"
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"expert 0 gate/up GEMM, {m} routed rows x K={K} x N={N}, {mode}, "
                       f"oracle quantization + float64 GEMMs, {dt:.1f} s"}
+
+
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def measured_traffic(workload):
@@ -540,6 +552,8 @@ def main():
         torch.cuda.synchronize()
         return 2 * n_copy * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
 
+    # the engine clock under matrix-core load, right after the timed steps
+    clock = api.clock_probe(iters=400000)
     copy_gbs = copy_rate(lambda: api.stream_copy(src, dst))
     torch_copy_gbs = copy_rate(lambda: dst.copy_(src))
     del src, dst
@@ -582,7 +596,12 @@ def main():
                      "arithmetic": arith,
                      "launches_per_step": launches,
                      "flops_per_launch": step_flops / launches,
-                     "avg_launch_ms": round(gemm_total_ms / launches, 4)},
+                     "avg_launch_ms": round(gemm_total_ms / launches, 4),
+                     # the peak is quoted at 2.4 GHz; the same peak at the clock measured
+                     # under matrix-core load
+                     "sclk_mhz_measured": round(clock["mhz_median"], 1),
+                     "peak_at_measured_sclk": round(peak * clock["mhz_median"] / 2400.0, 1),
+                     "frac_at_measured_sclk": round(achieved / (peak * clock["mhz_median"] / 2400.0), 4)},
         "cpu_baseline": cpu,
         "breakdown": {
             "gemm_ms": {k: round(v, 4) for k, v in gemm_ms.items()},
@@ -603,6 +622,7 @@ def main():
             "quant_ms_total": round(quant_total_ms, 4),
             "wall_s": round(wall, 3),
             "swiglu_quant": swiglu,
+            "clock_probe": clock,
             "persistent_weights": persistent,
         },
     }

@@ -427,6 +427,22 @@ mxsg_status mxsg_sigmoid_sweep(float *out, mxsg_stream_t stream);
  */
 mxsg_status mxsg_stream_copy(const void *src, void *dst, int64_t bytes, mxsg_stream_t stream);
 
+/*
+ * Clock probe, also not a step of the method: `blocks` workgroups of 256
+ * threads keep the matrix cores busy with bf16 MFMAs for `iters` rounds (a
+ * round is 4 MFMAs of 32x32x16 per wave); lane 0 of each workgroup writes
+ * out[4 b + 0] = core clock cycles and out[4 b + 1] = wall-clock ticks
+ * elapsed over its rounds, out[4 b + 2..3] = 0 (out: uint64 [4 blocks],
+ * device). cycles / (ticks / wall rate) is the engine clock under matrix
+ * load, which the dense MFMA peaks (quoted at 2.4 GHz) can be scaled by.
+ * blocks in [0, 2^20], iters >= 0.
+ */
+mxsg_status mxsg_clock_probe(int32_t blocks, int32_t iters, uint64_t *out, mxsg_stream_t stream);
+
+/* The constant rate of the wall clock the probe reads, in kHz, of the
+ * current device. */
+mxsg_status mxsg_wall_clock_rate_khz(int32_t *khz);
+
 #ifdef __cplusplus
 }
 #endif

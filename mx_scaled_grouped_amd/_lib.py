@@ -45,6 +45,8 @@ SIGNATURES = {
     "mxsg_swiglu": (_i32, [_c_p, _i64, _i64, _c_p, _c_p]),
     "mxsg_sigmoid_sweep": (_i32, [_c_p, _c_p]),
     "mxsg_stream_copy": (_i32, [_c_p, _c_p, _i64, _c_p]),
+    "mxsg_clock_probe": (_i32, [_i32, _i32, _c_p, _c_p]),
+    "mxsg_wall_clock_rate_khz": (_i32, [_c_p]),
 }
 
 _lib = None

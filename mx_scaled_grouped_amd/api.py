@@ -652,3 +652,23 @@ def stream_copy(src: torch.Tensor, dst: torch.Tensor) -> None:
     if dst.numel() * dst.element_size() < n:
         raise ValueError("dst is smaller than src")
     _lib.call("mxsg_stream_copy", _ptr(src), _ptr(dst), n, _stream())
+
+
+def clock_probe(iters: int = 200000, blocks: int = 0) -> dict:
+    """The engine clock under matrix-core load (mxsg_clock_probe): `blocks`
+    workgroups (default 4 per compute unit) of bf16 MFMAs for `iters`
+    rounds; returns the median, min and max over workgroups of core cycles
+    per second, in MHz. Synchronizes the device."""
+    if blocks <= 0:
+        blocks = 4 * torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    out = torch.zeros(4 * blocks, dtype=torch.int64, device="cuda")
+    khz = ctypes.c_int32(0)
+    _lib.call("mxsg_wall_clock_rate_khz", ctypes.addressof(khz))
+    _lib.call("mxsg_clock_probe", blocks, iters, _ptr(out), _stream())
+    t = out.view(blocks, 4).cpu()
+    if int(t[:, 2].sum()) != 0:
+        raise RuntimeError("clock_probe: non-finite accumulation")
+    cyc, ticks = t[:, 0].double(), t[:, 1].double().clamp(min=1)
+    mhz = (cyc / (ticks / (khz.value * 1e3))) / 1e6
+    return {"mhz_median": float(mhz.median()), "mhz_min": float(mhz.min()), "mhz_max": float(mhz.max()),
+            "wall_clock_khz": int(khz.value), "blocks": blocks, "iters": iters}

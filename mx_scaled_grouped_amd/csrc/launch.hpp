@@ -67,6 +67,7 @@ hipError_t launch_route(const int32_t *ids, int64_t T, int k, int E, int32_t *en
 hipError_t launch_swiglu(const uint16_t *x, int64_t M, int64_t C, uint16_t *y, hipStream_t st);
 hipError_t launch_sigmoid_sweep(float *out, hipStream_t st);
 hipError_t launch_stream_copy(const void *src, void *dst, int64_t bytes, hipStream_t st);
+hipError_t launch_clock_probe(int blocks, int iters, uint64_t *out, hipStream_t st);
 hipError_t launch_grouped_mm(const GemmParams &p, hipStream_t st);
 // ORs MXSG_STATUS_ENDS_* bits into *status for malformed group ends
 hipError_t launch_check_ends(const int32_t *ends, int E, int64_t M, int32_t *status, hipStream_t st);

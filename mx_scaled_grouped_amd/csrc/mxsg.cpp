@@ -434,4 +434,20 @@ mxsg_status mxsg_stream_copy(const void *src, void *dst, int64_t bytes, mxsg_str
                   "stream_copy");
 }
 
+mxsg_status mxsg_clock_probe(int32_t blocks, int32_t iters, uint64_t *out, mxsg_stream_t stream) {
+  REQUIRE(blocks >= 0 && blocks <= (1 << 20) && iters >= 0, MXSG_INVALID_ARGUMENT,
+          "clock_probe: blocks=%d must be in [0, 2^20], iters=%d non-negative", blocks, iters);
+  REQUIRE(blocks == 0 || out, MXSG_INVALID_ARGUMENT, "clock_probe: out is NULL");
+  return from_hip(mxsg::launch_clock_probe(blocks, iters, out, static_cast<hipStream_t>(stream)),
+                  "clock_probe");
+}
+
+mxsg_status mxsg_wall_clock_rate_khz(int32_t *khz) {
+  REQUIRE(khz, MXSG_INVALID_ARGUMENT, "wall_clock_rate_khz: khz is NULL");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(khz, hipDeviceAttributeWallClockRate, dev);
+  return from_hip(e, "wall_clock_rate_khz");
+}
+
 }  // extern "C"

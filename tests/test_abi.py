@@ -288,6 +288,11 @@ def test_delayed_and_sweep_validation():
     assert _lib.status_of("mxsg_stream_copy", FAKE, FAKE, 24, None) == _lib.INVALID_ARGUMENT
     assert _lib.status_of("mxsg_stream_copy", None, FAKE, 32, None) == _lib.INVALID_ARGUMENT
     assert _lib.status_of("mxsg_stream_copy", FAKE + 8, FAKE, 32, None) == _lib.INVALID_ARGUMENT
+    assert _lib.status_of("mxsg_clock_probe", -1, 10, FAKE, None) == _lib.INVALID_ARGUMENT
+    assert _lib.status_of("mxsg_clock_probe", 4, -1, FAKE, None) == _lib.INVALID_ARGUMENT
+    assert _lib.status_of("mxsg_clock_probe", 4, 10, None, None) == _lib.INVALID_ARGUMENT
+    assert _lib.status_of("mxsg_clock_probe", (1 << 20) + 1, 10, FAKE, None) == _lib.INVALID_ARGUMENT
+    assert _lib.status_of("mxsg_wall_clock_rate_khz", None) == _lib.INVALID_ARGUMENT
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

@@ -74,6 +74,16 @@ def test_stream_copy():
         assert int(dst[n:].count_nonzero()) == 0, n
 
 
+def test_clock_probe():
+    """The engine clock under matrix-core load is a plausible engine clock
+    (the chip's peak is 2.4 GHz) on every workgroup."""
+    api = _api()
+    c = api.clock_probe(iters=20000)
+    print(f"clock probe: {c}", flush=True)
+    assert c["wall_clock_khz"] > 0
+    assert 300.0 <= c["mhz_min"] <= c["mhz_median"] <= c["mhz_max"] <= 2600.0, c
+
+
 # ---------------------------------------------------------------------------
 # token tensors
 
