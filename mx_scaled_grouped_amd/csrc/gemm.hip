@@ -14,16 +14,16 @@
 // waves, 4 x 2, two per SIMD) computes a
 // 256 x BN output tile; each wave owns (256 / waves along i) x BN/2 as
 // 32 x 32 MFMA sub-tiles (v_mfma_scale_f32_32x32x64_f8f6f4). The
-// contraction runs in 64-wide stages through a ring of four LDS buffers:
-// global_load_lds_dwordx4 copies (no staging registers) land XOR-swizzled
-// 16-byte chunks (bank-conflict-free fragment reads) three stages ahead of
-// use. The code operands are pair-interleaved, so a stage of 64 bytes over
-// a run of row pairs is whole 128-byte lines. A stage is one barrier: its
-// first two MFMAs are issued before it, and after it every MFMA slot also
-// issues one copy of the stage three ahead and part of the next stage's
-// fragment reads (into a second register set), so the matrix pipe is not
-// left idle while copies go out. Every stage issues the same number of
-// copies (the padding stages of the last ring turn copy from a static zero
+// contraction runs in 64-wide stages through a ring of R LDS buffers (four;
+// blockwise six): global_load_lds_dwordx4 copies (no staging registers)
+// land XOR-swizzled 16-byte chunks (bank-conflict-free fragment reads) R - 1
+// stages ahead of use. The code operands are pair-interleaved, so a stage
+// of 64 bytes over a run of row pairs is whole 128-byte lines. A stage is
+// one barrier: its first two MFMAs are issued before it, and after it every
+// MFMA slot also issues one copy of the stage R - 1 ahead and part of the
+// next stage's fragment reads (into a second register set), so the matrix
+// pipe is not left idle while copies go out. Every stage issues the same
+// number of copies (stages past the contraction copy from a static zero
 // source), so each wait count is a constant and the loop has no branch.
 // The grid is persistent (one workgroup per CU looping over tiles).
 // Tiles never straddle expert groups (row tiles start at a group's first
@@ -217,6 +217,16 @@ __host__ __device__ constexpr int mfma_fmt(int f) { return f == kE2M1 ? 4 : f; }
 template <int RECIPE>
 constexpr int gemm_waves() { return RECIPE == kBlockwise ? 8 : 4; }
 
+// stage buffers in the LDS ring: four for the 256 x 256 tiles (32 KB a
+// stage); six for the blockwise 256 x 128 tile (24 KB a stage, with its
+// scales just inside the 160 KB), whose last stages then run as a partial
+// turn, so a contraction of 22 or 26 stages (hidden or ffn 1408; a group
+// of 1664 padded tokens) computes no padding stage. (Measured: six stages
+// in flight instead of four run the steady state no faster; the copies'
+// cost is in the per-CU fetch path, not in their latency.)
+template <int RECIPE>
+constexpr int gemm_ring() { return RECIPE == kBlockwise ? 6 : 4; }
+
 template <int MODE, int RECIPE, int FA, int FB, int BN, bool ACC>
 __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel(GemmArgs a) {
   constexpr int NW = gemm_waves<RECIPE>();
@@ -240,19 +250,29 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
   static_assert(AQ >= 1 && BQ >= 1 && NI >= 1, "tile shape");
   static_assert(!MX || (MI == 4 && NI == 4 && BN == 256), "MX word layout");
 
-  // four stage buffers of A and B as distinct objects: the compiler then
-  // knows the copies into one buffer do not alias the reads of another
-  __shared__ __attribute__((aligned(1024))) uint8_t As0[GBM * GBK], As1[GBM * GBK], As2[GBM * GBK], As3[GBM * GBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t Bs0[BN * GBK], Bs1[BN * GBK], Bs2[BN * GBK], Bs3[BN * GBK];
-  __shared__ __attribute__((aligned(16))) float sA0[BLK ? GBM : 4], sA1[BLK ? GBM : 4], sA2[BLK ? GBM : 4], sA3[BLK ? GBM : 4];
-  __shared__ __attribute__((aligned(16))) float sB0[BLK ? BN : 4], sB1[BLK ? BN : 4], sB2[BLK ? BN : 4], sB3[BLK ? BN : 4];
+  // the ring's stage buffers of A and B codes (and of their per-stage
+  // scales), always indexed by compile-time constants
+  constexpr int R = gemm_ring<RECIPE>();
+  static_assert(R % 2 == 0, "a blockwise 128-block is two stages");
+  __shared__ __attribute__((aligned(1024))) uint8_t As[R][GBM * GBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t Bs[R][BN * GBK];
+  __shared__ __attribute__((aligned(16))) float sAr[R][BLK ? GBM : 4];
+  __shared__ __attribute__((aligned(16))) float sBr[R][BLK && MODE == kWgrad ? BN : 4];
   __shared__ float sbtab[BLK ? SB_TAB : 1];
+  // blockwise: the promotion factors of the 128-block whose partials are
+  // promoted next, per tile row (forward / dgrad: sA(row) * sB(tile), one
+  // product per row and block; wgrad: sA(row)) and, for wgrad, per tile
+  // column (sB(column))
+  // (one 64-entry slot per wave, so that every wave stores without a
+  // branch; the slots of the waves that copy no scales are never read)
+  __shared__ __attribute__((aligned(16))) float sS[BLK ? 64 * NW : 4];
+  __shared__ __attribute__((aligned(16))) float sSb[BLK && MODE == kWgrad ? 64 * NW : 4];
   __shared__ __attribute__((aligned(256))) uint32_t dmy[64];  // target of filler copies  // blockwise weight scales of this tile's j-block, per l-block
   // MX: per stage buffer, each tile row's E8M0 word (the 32-blocks 4w..4w+3
   // holding the stage's two), stored so the four words one lane needs are
   // contiguous: slot d holds tile row 128 (d / 128) + 32 (d % 4) + (d / 4) % 32
-  __shared__ __attribute__((aligned(16))) uint32_t mA0[MX ? GBM : 4], mA1[MX ? GBM : 4], mA2[MX ? GBM : 4], mA3[MX ? GBM : 4];
-  __shared__ __attribute__((aligned(16))) uint32_t mB0[MX ? BN : 4], mB1[MX ? BN : 4], mB2[MX ? BN : 4], mB3[MX ? BN : 4];
+  __shared__ __attribute__((aligned(16))) uint32_t mAr[R][MX ? GBM : 4];
+  __shared__ __attribute__((aligned(16))) uint32_t mBr[R][MX ? BN : 4];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -294,7 +314,10 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
     l0 = 0;
     nsteps = (int)(a.L / GBK);
   }
-  const int vsteps = (nsteps + 3) & ~3;  // stages rounded up to whole ring turns
+  // stages run: rounded up to whole ring turns (four buffers), or to whole
+  // 128-blocks (six buffers: the last stages then run as a partial turn; with
+  // four, the partial turn's code raised register use past the budget)
+  const int vsteps = R == 4 ? (nsteps + 3) & ~3 : (nsteps + 1) & ~1;
 
   // scale-row strides (contraction elements per row): FWD / DGRAD scales are
   // [rows, L/blk]; WGRAD scales follow the padded column layout, [rows, ld/blk]
@@ -381,7 +404,13 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
   const uint8_t *zsrc = reinterpret_cast<const uint8_t *>(kZeroSrc) + lane * 16;
   const uint32_t *usrc = kUnitScaleSrc + lane;
   const float *zsrc4 = reinterpret_cast<const float *>(kZeroSrc) + lane;
-  __syncthreads();  // sbtab visible
+  // the first stage of the tile promotes a "block -1": zero partials and
+  // zero factors (LDS may hold any bit pattern, Inf or NaN included)
+  if (BLK) {
+    sS[wave * 64 + lane] = 0.0f;
+    if (MODE == kWgrad) sSb[wave * 64 + lane] = 0.0f;
+  }
+  __syncthreads();  // sbtab and the zero factors visible
 
   v16f acc[MI][NI];
 #pragma unroll
@@ -391,6 +420,12 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
   v16f part[BLK ? MI : 1][BLK ? NI : 1];  // blockwise: partial sum of the current 128-block
+#pragma unroll
+  for (int mi = 0; mi < (BLK ? MI : 1); ++mi)
+#pragma unroll
+    for (int ni = 0; ni < (BLK ? NI : 1); ++ni)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) part[mi][ni][v] = 0.0f;
 
   // copy C (0 <= C < OPS) of stage kt into the stage buffers; a stage past
   // the contraction copies zeros (unit E8M0 scales), so the MFMAs of the
@@ -436,8 +471,10 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
-  using W1 = std::integral_constant<int, 1>;
-  using W2 = std::integral_constant<int, 2>;
+  // in a stage's barrier: the next stage's copies have landed (R - 3 later
+  // stages may still be in flight); after the prologue: the first stage's
+  using WR = std::integral_constant<int, R - 3>;
+  using WP = std::integral_constant<int, R - 2>;
 
   // an empty asm use of every accumulator: keeps the stage's MFMAs issued
   // before the next wait, and each accumulator in its register file (AGPRs;
@@ -540,66 +577,103 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
     }
   };
 
-  // blockwise, after the second stage of a 128-block: acc += partial *
-  // sA(row) * sB; sB per column for wgrad, one value per tile (the 128x128
-  // weight tile) otherwise
-  auto promote = [&](const float *sa_l, const float *sb_l, int kt) {
-    const float sbw = MODE == kWgrad ? 0.0f : sbtab[(kt >> 1) & (SB_TAB - 1)];
+  // blockwise promotion of one sub-tile's block partial: acc += partial *
+  // factor, with this lane's 16 rows' factors of sub-tile row mi in s (rows
+  // 8 (v / 4) + 4 h + v % 4 of the 32), times the column's sB for wgrad
+  auto load_factors = [&](int mi, float (&f)[16]) {
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      float sa[16];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 v4 = *reinterpret_cast<const float4 *>(&sa_l[wi * WM + mi * 32 + q * 8 + h * 4]);
-        sa[q * 4 + 0] = v4.x;
-        sa[q * 4 + 1] = v4.y;
-        sa[q * 4 + 2] = v4.z;
-        sa[q * 4 + 3] = v4.w;
-      }
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        const float sbj = MODE == kWgrad ? sb_l[wj * WN + ni * 32 + l32] : sbw;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[mi][ni][v] += part[mi][ni][v] * (sa[v] * sbj);
-      }
+    for (int q = 0; q < 4; ++q) {
+      const float4 v4 = *reinterpret_cast<const float4 *>(&sS[wi * WM + mi * 32 + q * 8 + h * 4]);
+      f[q * 4 + 0] = v4.x;
+      f[q * 4 + 1] = v4.y;
+      f[q * 4 + 2] = v4.z;
+      f[q * 4 + 3] = v4.w;
     }
+  };
+  auto promote_one = [&](int mi, int ni, const float (&f)[16]) {
+    if (MODE == kWgrad) {
+      const float sbj = sSb[wj * WN + ni * 32 + l32];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mi][ni][v] += part[mi][ni][v] * (f[v] * sbj);
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mi][ni][v] += part[mi][ni][v] * f[v];
+    }
+  };
+  // blockwise, in the second stage of a 128-block (its scales are in that
+  // stage's buffers): each wave moves the factors of the rows it copied
+  // into its slot of sS / sSb, read after the next barrier. No branch: a
+  // wave that copied no scale rows re-reads valid ones into a slot nobody
+  // reads (a branch here let the compiler sink this stage's MFMAs below it).
+  auto stash_factors = [&](const float *sa_l, const float *sb_l, int kt) {
+    float v = sa_l[(wave % (GBM / 64)) * 64 + lane];
+    if (MODE != kWgrad) v *= sbtab[(kt >> 1) & (SB_TAB - 1)];
+    sS[wave * 64 + lane] = v;
+    if (MODE == kWgrad) sSb[wave * 64 + lane] = sb_l[(wave % (BN / 64)) * 64 + lane];
   };
 
   // MFMAs of a stage issued before its barrier (their operands are already
   // in registers, so they keep the MFMA pipe busy while the waves sync).
-  // Not for blockwise: there the partials are read back soon after their
-  // MFMAs, and the compiler then placed those reads too close to the MFMAs
-  // (stale values).
-  constexpr int NPRE = BLK ? 0 : 2;
+  // Blockwise: in the second stage of each block only (the first stage's
+  // MFMAs wait for the promotion of the previous block's partials).
+  constexpr int NPRE = 2;
   using C0 = std::integral_constant<int, 0>;
   using CPRE = std::integral_constant<int, NPRE>;
 
-  // ---- main loop: a ring of four stage buffers; stage kt lives in buffer
-  // kt % 4 and its copies are issued three stages ahead. The stage count is
-  // rounded up to whole turns of the ring with zero-filled stages, so the
-  // loop body (four stages) has no conditional MFMAs.
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
+  // ---- main loop: a ring of R stage buffers; stage kt lives in buffer
+  // kt % R and its copies are issued R - 1 stages ahead. The loop body is
+  // one turn of the ring (R stages, no conditional MFMAs).
   Frags<MI, NI> F0, F1;
   {
-    // stage k: wait for stage k+1's copies, barrier, issue stage k+3's
-    // copies, then stage k's MFMAs (fragments read during stage k-1)
-    // interleaved with the reads of stage k+1's fragments
     // stage k: its first NPRE MFMAs (fragments read during stage k-1), wait
     // for stage k+1's copies, barrier, then slot by slot: one MFMA, one copy
-    // of stage k+3, and the fragment reads of stage k+1 spread over the slots
+    // of stage k+R-1, and the fragment reads of stage k+1 spread over the slots
     auto step = [&](int k, Frags<MI, NI> &fc, Frags<MI, NI> &fn, const float *sac, const float *sbc,
                     const uint8_t *an, const uint8_t *bn, const uint32_t *man, const uint32_t *mbn,
                     uint8_t *al, uint8_t *bl, float *sal, float *sbl, uint32_t *mal, uint32_t *mbl,
-                    auto ph) {
+                    auto ph) __attribute__((always_inline)) {
+      if constexpr (BLK && decltype(ph)::value == 0) {
+        // blockwise, first stage of a block: after the barrier, sub-tile by
+        // sub-tile, promote the previous block's partial (VALU) and then
+        // start the new partial with this stage's MFMA, so each sub-tile's
+        // promotion issues while the previous sub-tile's MFMA runs
+        sync_stage(WR{});
+        // the partials were written by the previous stage's MFMAs: pad the
+        // MFMA-result-to-VALU-read distance explicitly (>= 40 wait states)
+        asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        constexpr int NS = MI * NI;
+        float f[16];
+        [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
+          ([&] {
+            constexpr int S = Ss;
+            constexpr int mi = S / NI, ni = S % NI;
+            if constexpr (ni == 0) load_factors(mi, f);
+            promote_one(mi, ni, f);
+            mfma_range(fc, ph, std::integral_constant<int, S>{}, std::integral_constant<int, S + 1>{});
+            if constexpr (S < OPS) copy(std::integral_constant<int, S>{}, k + R - 1, al, bl, sal, sbl, mal, mbl);
+            constexpr int u0 = (NUNIT * S) / NS, u1 = (NUNIT * (S + 1)) / NS;
+            if constexpr (u1 > u0) read_unit(std::integral_constant<int, u0>{}, fn, an, bn, man, mbn);
+            if constexpr (u1 > u0 + 1) read_unit(std::integral_constant<int, u0 + 1>{}, fn, an, bn, man, mbn);
+            __builtin_amdgcn_sched_barrier(0);
+          }(), ...);
+        }(std::make_integer_sequence<int, NS>{});
+        if constexpr (OPS > NS) {
+          [&]<int... Cs>(std::integer_sequence<int, Cs...>) {
+            (copy(std::integral_constant<int, NS + Cs>{}, k + R - 1, al, bl, sal, sbl, mal, mbl), ...);
+          }(std::make_integer_sequence<int, OPS - NS>{});
+        }
+        pin_acc();
+        return;
+      }
       mfma_range(fc, ph, C0{}, CPRE{});
-      sync_stage(W1{});
+      sync_stage(WR{});
       constexpr int NS = MI * NI - NPRE;   // slots
       [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
         ([&] {
           constexpr int S = Ss;
           mfma_range(fc, ph, std::integral_constant<int, NPRE + S>{}, std::integral_constant<int, NPRE + S + 1>{});
-          if constexpr (S < OPS) copy(std::integral_constant<int, S>{}, k + 3, al, bl, sal, sbl, mal, mbl);
+          if constexpr (S < OPS) copy(std::integral_constant<int, S>{}, k + R - 1, al, bl, sal, sbl, mal, mbl);
           constexpr int u0 = (NUNIT * S) / NS, u1 = (NUNIT * (S + 1)) / NS;
           if constexpr (u1 > u0) read_unit(std::integral_constant<int, u0>{}, fn, an, bn, man, mbn);
           if constexpr (u1 > u0 + 1) read_unit(std::integral_constant<int, u0 + 1>{}, fn, an, bn, man, mbn);
@@ -608,44 +682,69 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
       }(std::make_integer_sequence<int, NS>{});
       if constexpr (OPS > NS) {
         [&]<int... Cs>(std::integer_sequence<int, Cs...>) {
-          (copy(std::integral_constant<int, NS + Cs>{}, k + 3, al, bl, sal, sbl, mal, mbl), ...);
+          (copy(std::integral_constant<int, NS + Cs>{}, k + R - 1, al, bl, sal, sbl, mal, mbl), ...);
         }(std::make_integer_sequence<int, OPS - NS>{});
       }
-      if (BLK && decltype(ph)::value == 1) {
-        // a v_mfma_scale 32x32x64 result read back by the VALU needs more
-        // independent cycles than the compiler left in one schedule: pad
-        // explicitly (>= 40 wait states) between the last MFMA of the block
-        // and the reads of its partials
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        promote(sac, sbc, k);
-      }
+      if constexpr (BLK) stash_factors(sac, sbc, k);
       pin_acc();
     };
+    // step J of a ring turn starting at stage kt (a multiple of R): stage
+    // kt + J lives in buffer J, its fragments in F0 (J even) or F1, the
+    // next stage's in buffer J + 1, and its copies go to buffer J - 1
+    auto step_at = [&](auto j, int kt) __attribute__((always_inline)) {
+      constexpr int J = decltype(j)::value;
+      constexpr int cur = J % R, nxt = (J + 1) % R, cpy = (J + R - 1) % R;
+      // (the register sets are named, not selected: a selected reference
+      // would put them in scratch memory)
+      if constexpr (J % 2 == 0)
+        step(kt + J, F0, F1, sAr[cur], sBr[cur], As[nxt], Bs[nxt], mAr[nxt], mBr[nxt], As[cpy], Bs[cpy],
+             sAr[cpy], sBr[cpy], mAr[cpy], mBr[cpy], std::integral_constant<int, 0>{});
+      else
+        step(kt + J, F1, F0, sAr[cur], sBr[cur], As[nxt], Bs[nxt], mAr[nxt], mBr[nxt], As[cpy], Bs[cpy],
+             sAr[cpy], sBr[cpy], mAr[cpy], mBr[cpy], std::integral_constant<int, 1>{});
+    };
     if (vsteps > 0) {
-      load_stage(0, As0, Bs0, sA0, sB0, mA0, mB0);
-      load_stage(1, As1, Bs1, sA1, sB1, mA1, mB1);
-      load_stage(2, As2, Bs2, sA2, sB2, mA2, mB2);
-      sync_stage(W2{});
-      read_frags(F0, As0, Bs0, mA0, mB0);
+      [&]<int... Js>(std::integer_sequence<int, Js...>) {
+        (load_stage(Js, As[Js], Bs[Js], sAr[Js], sBr[Js], mAr[Js], mBr[Js]), ...);
+      }(std::make_integer_sequence<int, R - 1>{});
+      sync_stage(WP{});
+      read_frags(F0, As[0], Bs[0], mAr[0], mBr[0]);
     }
-    for (int kt = 0; kt < vsteps; kt += 4) {
-      step(kt, F0, F1, sA0, sB0, As1, Bs1, mA1, mB1, As3, Bs3, sA3, sB3, mA3, mB3, P0{});
-      step(kt + 1, F1, F0, sA1, sB1, As2, Bs2, mA2, mB2, As0, Bs0, sA0, sB0, mA0, mB0, P1{});
-      step(kt + 2, F0, F1, sA2, sB2, As3, Bs3, mA3, mB3, As1, Bs1, sA1, sB1, mA1, mB1, P0{});
-      step(kt + 3, F1, F0, sA3, sB3, As0, Bs0, mA0, mB0, As2, Bs2, sA2, sB2, mA2, mB2, P1{});
+    int kt = 0;
+    for (; kt + R <= vsteps; kt += R) {
+      [&]<int... Js>(std::integer_sequence<int, Js...>) {
+        (step_at(std::integral_constant<int, Js>{}, kt), ...);
+      }(std::make_integer_sequence<int, R>{});
+    }
+    // six buffers: the last vsteps - kt < R stages (an even count) run as
+    // the first steps of one more turn
+    if constexpr (R > 4) {
+      if (vsteps - kt >= 2) {
+        step_at(std::integral_constant<int, 0>{}, kt);
+        step_at(std::integral_constant<int, 1>{}, kt);
+      }
+      if (vsteps - kt >= 4) {
+        step_at(std::integral_constant<int, 2>{}, kt);
+        step_at(std::integral_constant<int, 3>{}, kt);
+      }
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (!BLK) {
-    // the epilogue's first LDS writes take the last MFMA's accumulators
-    // straight from AGPRs: keep >= 40 wait states between them (blockwise
-    // pads every ring turn)
-    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" ::: "memory");
-  }
+  // the epilogue's first LDS writes (blockwise: the last promotion) read the
+  // last MFMAs' results: keep >= 40 wait states between them
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" ::: "memory");
   wait_vm<0>();     // the copies of the stages past the contraction have landed
-  __syncthreads();  // every wave is done with the stage buffers
+  __syncthreads();  // every wave is done with the stage buffers (blockwise: sS / sSb written)
+  if constexpr (BLK) {
+    // the last block's partials
+    float f[16];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      load_factors(mi, f);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) promote_one(mi, ni, f);
+    }
+  }
 
   // ---- epilogue: each wave stages 16-row half slabs through its own LDS
   // region, then writes rows of 8 outputs with 16-byte stores. The scale
@@ -662,7 +761,7 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
   constexpr int CPL = 16 * CPR / 64;   // chunks per lane per half slab
   // (eight waves: two slabs in each A stage buffer)
   const int cw = NW == 4 ? wave : wave >> 1;
-  uint8_t *creg = (cw == 0 ? As0 : cw == 1 ? As1 : cw == 2 ? As2 : As3) +
+  uint8_t *creg = As[cw] +
                   (NW == 4 ? 0 : (wave & 1) * (GBM * GBK / 2));
   float *cb = reinterpret_cast<float *>(creg);
   const int64_t jw = j0 + wj * WN;
