@@ -13,7 +13,19 @@
  * DeepSeek-style 1x128 / 128x1 / 128x128 blockwise with fp32 scales
  * (Transformer Engine "FP8BlockQuantizer not work" issue, design note);
  * MXFP8 with 32-element blocks and E8M0 scales (Megatron-LM single grouped
- * weight PR, coverage table). Formats are OCP e4m3 and e5m2.
+ * weight PR, coverage table); the same table's 4-bit rows: MXFP4 (e2m1
+ * elements, E8M0 scales) and NVFP4 (e2m1 elements, an e4m3 scale per 16
+ * elements and an fp32 scale per tensor). Formats are OCP e4m3, e5m2, e2m1.
+ *
+ * Shape of the interface. Every call takes a flat argument list (device
+ * pointers, sizes, enums) instead of descriptor structs, so that each
+ * argument's meaning and ownership is stated where it is declared. The
+ * quantization is four calls (token tensors; tokens gathered through a
+ * routing index; the SwiGLU activation of a gate/up output; the grouped
+ * weight), and the buffer sizes are two pure host queries, one for token
+ * tensors and one for weights. One rule is stricter than the MX block size
+ * needs: MX feature dimensions must be multiples of 128, not 32, so that
+ * one GEMM tile shape serves every recipe.
  *
  * Conventions for every call.
  *  - All array pointers are DEVICE pointers of the current HIP device, owned
@@ -48,7 +60,23 @@
  *    the low nibble of byte i, element 2i + 1 in the high nibble; a row of
  *    L elements is L/2 code bytes. Sign in bit 3; magnitudes 0, 0.5, 1,
  *    1.5, 2, 3, 4, 6 (OCP MX v1.0 element formats); the MX exponent uses
- *    fmax = 6, and MX is the only recipe with e2m1 elements.
+ *    fmax = 6.
+ *  - NVFP4: per tensor (per expert for weights) s_t = fp32(amax / (6 *
+ *    448)), or 1 when amax = 0; per 16 consecutive elements along a row,
+ *    the block scale code b = e4m3 sat_rne(fp32(fp32(amax_16 / 6) / s_t)),
+ *    its multiplier m = fp32(e4m3(b) * s_t), and the element codes
+ *    e2m1 sat_rne(fp32(x * inv)) with inv = fp32(1 / m) (0 when m = 0 or
+ *    the quotient overflows); the value is e2m1(code) * e4m3(b) * s_t. Element codes sit two per byte
+ *    like MXFP4 codes, but inside each 128-element (64-byte) piece of a row
+ *    the 8 elements 16 s + 8 h .. 16 s + 8 h + 7 (s = 0..7, h = 0..1) form
+ *    the little-endian dword at byte 32 (s / 4) + 16 h + 4 (s % 4) of the
+ *    piece (element order within the dword as for MXFP4); pair interleaving
+ *    then applies to the code bytes as for every code matrix. A scale
+ *    buffer of R rows of L elements holds the R * L/16 block codes
+ *    piece-major, byte ((l / 128) * R + r) * 8 + (l % 128) / 16 for element
+ *    (r, l), then the fp32 tensor scale (little-endian) at byte R * L/16; a
+ *    weight's buffer holds the E experts' block codes one after another,
+ *    then the E fp32 tensor scales.
  *  - Code matrices are pair-interleaved: a matrix of R rows of L code bytes
  *    (L a multiple of 64) stores byte (r, l) at offset
  *      (r / 2) * 2L + (l / 64) * 128 + (r % 2) * 64 + (l % 64),
@@ -148,9 +176,11 @@ int64_t mxsg_padded_capacity(int64_t M, int32_t E);
  * e2m1 only with MX) and returns their status. With b = 1 code byte per
  * element (e4m3, e5m2) or 1/2 (e2m1):
  *   bytes[0] row_codes      (M + (M & 1)) * C * b
- *   bytes[1] row_scales     BLOCKWISE 4 * M * C/128, MX M * C/32 (word-major), else 4
+ *   bytes[1] row_scales     BLOCKWISE 4 * M * C/128, MX M * C/32 (word-major),
+ *                           NVFP4 M * C/16 + 4, else 4
  *   bytes[2] col_codes      C * ld * b               (0 when E = 0)
- *   bytes[3] col_scales     BLOCKWISE 4 * C * ld/128, MX C * ld/32 (word-major), else 4
+ *   bytes[3] col_scales     BLOCKWISE 4 * C * ld/128, MX C * ld/32 (word-major),
+ *                           NVFP4 C * ld/16 + 4, else 4
  *   bytes[4] padded_starts  4 * (E + 1)              (0 when E = 0)
  * Units and shape rule: the Transformer Engine "FP8BlockQuantizer not
  * work" issue, design note (1x128 units; the blocked dimension divides by
@@ -165,7 +195,8 @@ mxsg_status mxsg_quantize_act_sizes(int64_t M, int64_t C, int32_t recipe, int32_
  * (b as above):
  *   bytes[0] kmajor_codes, bytes[2] nmajor_codes   E * K * N * b each
  *   bytes[1] kmajor_scales, bytes[3] nmajor_scales BLOCKWISE 4 * E * K/128 * N/128,
- *                                                  MX E * K * N / 32, else 4 * E
+ *                                                  MX E * K * N / 32,
+ *                                                  NVFP4 E * K * N / 16 + 4 * E, else 4 * E
  * Pure host function with the shape rules of mxsg_quantize_weight (K, N
  * multiples of 128; 128x128 weight blocks of the same issue's design note).
  */
@@ -217,6 +248,11 @@ mxsg_status mxsg_route(const int32_t *expert_ids, int64_t T, int32_t k, int32_t 
  *    (both word-major, R = M resp. C); a
  *    32-block made only of padding gets code 127. fmt e2m1 (MXFP4): the
  *    same scales; code rows hold C/2 resp. ld/2 bytes.
+ *  recipe NVFP4 (fmt e2m1 only): amax = max|x| is computed first (amax[0],
+ *    required); row_scales / col_scales are NVFP4 scale buffers (Layouts)
+ *    of R = M rows of C elements resp. R = C rows of ld elements, the
+ *    column-wise 16x1 blocks along the padded tokens starting at each
+ *    group's first token (a block of padding only gets block code 0).
  *
  *  row_codes uint8 [2 * ceil(M/2), C] (C/2 for e2m1), pair-interleaved (NULL: no row-wise
  *    output).
@@ -296,6 +332,10 @@ mxsg_status mxsg_quantize_act_gather(const void *x, int64_t T, const int32_t *ro
  *    [E, N, K/32]; n-major: blocks of 32 along N, nmajor_scales uint8
  *    [E, K, N/32] (each expert's matrix word-major, R = N resp. K). fmt
  *    e2m1: code rows of K/2 resp. N/2 bytes, same scales.
+ *  NVFP4 (fmt e2m1): one tensor scale per expert; amax fp32 [E] (required)
+ *    receives max|W_e|; 16-element blocks along K (k-major) resp. N
+ *    (n-major); each scale buffer is the NVFP4 buffer of the E experts'
+ *    matrices (R = N, L = K resp. R = K, L = N), tensor scales last.
  *  Scale pointers belonging to a non-NULL code pointer are required.
  *  status_word (optional): NaN / Inf weights set MXSG_STATUS_NONFINITE.
  */
@@ -351,9 +391,16 @@ mxsg_status mxsg_delayed_update(float *history, int32_t *pos, float *amax, float
  *     WGRAD a [K, lda/32], b [N, ldb/32], all word-major (the layout
  *     mxsg_quantize_act / mxsg_quantize_weight write); applied inside the
  *     MFMA.
+ *   NVFP4: each operand's NVFP4 scale buffer as its quantize call wrote it
+ *     (FWD: the row-wise buffer of x and the k-major weight buffer; DGRAD:
+ *     of dY and the n-major weight buffer; WGRAD: the column-wise buffers of
+ *     x and dY, whose rows hold ld elements). Each lane decodes its codes
+ *     and multiplies by the block scale exactly in f16 (e2m1 x e4m3 products
+ *     lie in [2^-10, 2688]); the f16 MFMA accumulates in fp32, and the
+ *     epilogue multiplies by the two tensor scales.
  *  fmt_a / fmt_b: element formats of A and B (e4m3 x e4m3, e5m2 x e4m3 and
  *  e4m3 x e5m2 are supported; hybrid training uses e5m2 gradients; e2m1 x
- *  e2m1 with the MX recipe is MXFP4).
+ *  e2m1 with the MX recipe is MXFP4, with the NVFP4 recipe NVFP4).
  *  4-bit operands (e2m1): rows hold two codes per byte, so every row length
  *  above is in code bytes: FWD lda >= K/2 and ldb = K/2, DGRAD lda >= N/2
  *  and ldb = N/2, WGRAD lda, ldb = column-wise code bytes per row (ld/2 of
