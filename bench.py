@@ -439,26 +439,31 @@ def cpu_model():
     return None
 
 
-def measured_traffic(workload):
-    """HBM bytes per grouped-GEMM launch from the committed counter summary
-    (FETCH_SIZE and WRITE_SIZE, calibrated against a plain copy); None when
-    there is no summary for this workload or the GEMM source has changed
-    since the counters were taken."""
+def profile_values(workload):
+    """Machine-read values of the committed counter summary of this
+    workload's grouped GEMM: HBM bytes per launch (FETCH_SIZE and
+    WRITE_SIZE, calibrated against a plain copy) and the time-weighted clock
+    of the GEMM launches (GRBM_GUI_ACTIVE over kernel time). Empty when there
+    is no summary or the GEMM source has changed since the counters were
+    taken."""
     import hashlib
     path = os.path.join(HERE, "profiles", f"grouped_gemm_{workload}.md")
     if not os.path.exists(path):
-        return None
+        return {}
     kv = {}
     for line in open(path):
         if " = " in line:
             k, v = line.strip().split(" = ", 1)
             kv[k] = v
-    if "traffic_bytes_per_launch" not in kv:
-        return None
     src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
     if kv.get("gemm_source_sha256") != src:
-        return None
-    return int(float(kv["traffic_bytes_per_launch"]))
+        return {}
+    out = {}
+    if "traffic_bytes_per_launch" in kv:
+        out["traffic"] = int(float(kv["traffic_bytes_per_launch"]))
+    if "gemm_clock_ghz" in kv:
+        out["clock_ghz"] = float(kv["gemm_clock_ghz"])
+    return out
 
 
 def main():
@@ -528,6 +533,7 @@ def main():
     achieved = step_flops / (gemm_total_ms * 1e-3) / 1e12
     quant_agg = sum(byts.values()) / (quant_total_ms * 1e-3) / 1e9
     peak, arith = gemm_peak(step)
+    prof = profile_values(args.workload)
     att = attainable_ms(spec, group_sizes, spec.modes, peak, layout_bytes(step.recipe, step.fp4))
     att_frac = {k: att[k] / gemm_ms[k] for k in gemm_ms}
     att_total = sum(att[k] for k in gemm_ms) / gemm_total_ms
@@ -590,18 +596,24 @@ def main():
                    "group_sizes": [int(x) for x in group_sizes]},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic(args.workload),
+                     "traffic": prof.get("traffic"),
                      "kernel": ("nvfp4_gemm_kernel" if step.recipe == "nvfp4" else "grouped_gemm_kernel")
                                + " (every GEMM launch of a step)",
                      "arithmetic": arith,
                      "launches_per_step": launches,
                      "flops_per_launch": step_flops / launches,
                      "avg_launch_ms": round(gemm_total_ms / launches, 4),
-                     # the peak is quoted at 2.4 GHz; the same peak at the clock measured
-                     # under matrix-core load
+                     # the peak is quoted at 2.4 GHz. Two measured clocks: the clock probe's
+                     # (bf16 MFMAs on every CU, run right after the timed steps) and the GEMM
+                     # launches' own (PMC, from the committed profile of this source)
                      "sclk_mhz_measured": round(clock["mhz_median"], 1),
+                     "sclk_source": "clock probe: bf16 MFMA load on every CU after the timed steps",
                      "peak_at_measured_sclk": round(peak * clock["mhz_median"] / 2400.0, 1),
-                     "frac_at_measured_sclk": round(achieved / (peak * clock["mhz_median"] / 2400.0), 4)},
+                     "frac_at_measured_sclk": round(achieved / (peak * clock["mhz_median"] / 2400.0), 4),
+                     "gemm_sclk_mhz_pmc": (round(prof["clock_ghz"] * 1000.0, 1) if "clock_ghz" in prof
+                                           else None),
+                     "frac_at_gemm_sclk_pmc": (round(achieved / (peak * prof["clock_ghz"] / 2.4), 4)
+                                               if "clock_ghz" in prof else None)},
         "cpu_baseline": cpu,
         "breakdown": {
             "gemm_ms": {k: round(v, 4) for k, v in gemm_ms.items()},
