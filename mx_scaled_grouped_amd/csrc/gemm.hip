@@ -15,7 +15,7 @@
 // 256 x BN output tile; each wave owns (256 / waves along i) x BN/2 as
 // 32 x 32 MFMA sub-tiles (v_mfma_scale_f32_32x32x64_f8f6f4). The
 // contraction runs in 64-wide stages through a ring of R LDS buffers (four;
-// blockwise six): global_load_lds_dwordx4 copies (no staging registers)
+// blockwise six): direct-to-LDS buffer loads (no staging registers)
 // land XOR-swizzled 16-byte chunks (bank-conflict-free fragment reads) R - 1
 // stages ahead of use. The code operands are pair-interleaved, so a stage
 // of 64 bytes over a run of row pairs is whole 128-byte lines. A stage is
@@ -23,8 +23,8 @@
 // MFMA slot also issues one copy of the stage R - 1 ahead and part of the
 // next stage's fragment reads (into a second register set), so the matrix
 // pipe is not left idle while copies go out. Every stage issues the same
-// number of copies (stages past the contraction copy from a static zero
-// source), so each wait count is a constant and the loop has no branch.
+// number of copies (stages past the contraction read zeros), so each wait
+// count is a constant and the loop has no branch.
 // The grid is persistent (one workgroup per CU looping over tiles).
 // Tiles never straddle expert groups (row tiles start at a group's first
 // row pair; rows of a neighbouring group in the tile are computed and not
@@ -151,9 +151,10 @@ __device__ bool locate_row_tile(const GemmArgs &a, int slot, int &g_out, int64_t
 }
 
 // Read-only copy sources for the stages past a tile's contraction (the ring
-// runs in whole turns of four stages): zero codes and zero blockwise scales,
-// and E8M0 words of four unit scales. Reading them keeps every stage's copy
-// count the same, so no wait depends on the stage.
+// runs in whole turns): zero blockwise scales and NVFP4 block codes, and
+// E8M0 words of four unit scales (codes read zeros through an empty buffer
+// resource). Reading them keeps every stage's copy count the same, so no
+// wait depends on the stage.
 #define MXSG_U7F4 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu
 #define MXSG_U7F16 MXSG_U7F4, MXSG_U7F4, MXSG_U7F4, MXSG_U7F4
 __device__ __attribute__((aligned(1024))) const uint32_t kZeroSrc[256] = {};
@@ -168,13 +169,37 @@ __device__ __attribute__((aligned(256))) const uint32_t kUnitScaleSrc[64] = {MXS
 // different banks.
 __device__ __forceinline__ int swz(int row, int ch) { return row * GBK + ((ch ^ ((row >> 2) & 3)) << 4); }
 
-// Direct global -> LDS copies (global_load_lds_dwordx4 / _dword): lane L of
-// the wave lands at lds + 16 L (or 4 L); M0 holds the LDS byte address.
+// Direct-to-LDS copies (buffer_load_dwordx4 ... lds, global_load_lds_dword(x4)):
+// lane L of the wave lands at lds + 16 L (or 4 L); M0 holds the LDS byte
+// address.
 // Issued through inline asm, so the compiler inserts no waits for them: the
 // main loop counts them itself (vmcnt) before each stage's barrier.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
+// Code copies are buffer loads (buffer_load_dwordx4 ... lds): a buffer
+// resource (base, size, in SGPRs) per operand and tile, a constant 32-bit
+// lane offset and the stage's byte offset in an SGPR, so a copy costs no
+// vector ALU work (a 64-bit address per lane and stage cost three VALU ops:
+// measured 1-4% of GEMM time, most for MXFP4). A stage past the
+// contraction reads through a resource of size 0: every lane is out of
+// range, reads nothing and lands zeros.
+typedef int rsrc_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t num_records) {
+  const uint64_t p = (uint64_t)base;
+  rsrc_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xFFFF));  // stride 0: a raw buffer
+  r[2] = (int)num_records;
+  r[3] = 0x00020000;  // 32-bit data format (raw loads ignore it; it must be valid)
+  return r;
+}
+__device__ __forceinline__ void bdma16(rsrc_t rs, uint32_t voff, uint32_t soff, uint8_t *lds) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rs), "s"(soff), "{m0}"(lds_addr(lds)));
+}
+// The NVFP4 kernel, at its register limit, keeps per-lane 64-bit addresses
+// (global_load_lds_dwordx4): four more SGPRs of buffer resources made the
+// compiler spill them.
 __device__ __forceinline__ void dma16(const uint8_t *src, uint8_t *lds) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_addr(lds)));
 }
@@ -332,6 +357,8 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
   const int64_t lb = l0 / (GBK * EPB);   // first contraction line of the tile
   const uint8_t *abase = a.a + (i0 >> 1) * 2 * a.lda + lb * 128;
   const uint8_t *bbase = a.b + (MODE == kWgrad ? 0 : (int64_t)g * a.b_gstride) + (j0 >> 1) * 2 * a.ldb + lb * 128;
+  const rsrc_t rsA = make_rsrc(abase, 0xFFFFFFFFu), rsB = make_rsrc(bbase, 0xFFFFFFFFu);
+  const rsrc_t rsZ = make_rsrc(kZeroSrc, 0u);
   const int apmax = (int)(((ihi - 1) >> 1) - (i0 >> 1));   // last valid pair, tile-relative
   const int64_t jlim = (a.J - j0) < BN ? (a.J - j0) : BN;
   const int bpmax = (int)((jlim - 1) >> 1);
@@ -401,7 +428,6 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
   // B-side scale row), then the A and B code chunks
   constexpr int NSC = MX ? 2 : (BLK ? (MODE == kWgrad ? 2 : 1) : 0);
   constexpr int OPS = NSC + AQ + BQ;
-  const uint8_t *zsrc = reinterpret_cast<const uint8_t *>(kZeroSrc) + lane * 16;
   const uint32_t *usrc = kUnitScaleSrc + lane;
   const float *zsrc4 = reinterpret_cast<const float *>(kZeroSrc) + lane;
   // the first stage of the tile promotes a "block -1": zero partials and
@@ -449,10 +475,10 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
       }
     } else if constexpr (C < NSC + AQ) {
       constexpr int q = C - NSC;
-      dma16(real ? abase + kt * 128 + aoff[q] : zsrc, as + (wave * AQ + q) * 1024);
+      bdma16(real ? rsA : rsZ, aoff[q], (uint32_t)kt * 128u, as + (wave * AQ + q) * 1024);
     } else {
       constexpr int q = C - NSC - AQ;
-      dma16(real ? bbase + kt * 128 + boff[q] : zsrc, bs + (wave * BQ + q) * 1024);
+      bdma16(real ? rsB : rsZ, boff[q], (uint32_t)kt * 128u, bs + (wave * BQ + q) * 1024);
     }
   };
   auto load_stage = [&](int kt, uint8_t *as, uint8_t *bs, float *sa, float *sb, uint32_t *ma,
@@ -905,7 +931,6 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_kernel(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wi = wave >> 1, wj = wave & 1;
   const int h = lane >> 5, l32 = lane & 31;
-  const uint8_t *zsrc = reinterpret_cast<const uint8_t *>(kZeroSrc) + lane * 16;
   const uint32_t *zsrc4 = kZeroSrc + lane;
 
   for (int vb = blockIdx.x; vb < a.nblocks; vb += gridDim.x) {
@@ -941,6 +966,7 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_kernel(GemmArgs a) {
     const int64_t lb = l0 / 128;   // first stage: 128 contraction elements per stage
     const uint8_t *abase = a.a + (i0 >> 1) * 2 * a.lda + lb * 128;
     const uint8_t *bbase = a.b + (MODE == kWgrad ? 0 : (int64_t)g * a.b_gstride) + (j0 >> 1) * 2 * a.ldb + lb * 128;
+    const uint8_t *zsrc = reinterpret_cast<const uint8_t *>(kZeroSrc) + lane * 16;
     const int apmax = (int)(((ihi - 1) >> 1) - (i0 >> 1));
     const int64_t jlim = (a.J - j0) < BN ? (a.J - j0) : BN;
     const int bpmax = (int)((jlim - 1) >> 1);
@@ -1002,48 +1028,94 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
 
+    // operands of one lane: the raw codes and block scales of a stage, and the
+    // f16 operands of k16 step S in register set S % 2
+    v8i fa[MI], fb[NI];
+    uint2 ra[MI], rb[NI];       // the rows' 8 e4m3 block codes of the stage
+    NvScale sa[MI], sb[NI];     // the same as f16 pairs
+    nv_v8h ao[2][MI], bo[2][NI];
+    // raw unit U of stage buffer `buf` (A sub-tiles 0..MI-1, then B): LDS
+    // reads only, so a run of them is in flight at once
+    auto read_unit = [&](auto u, int buf) __attribute__((always_inline)) {
+      constexpr int U = decltype(u)::value;
+      if constexpr (U < MI) {
+        const int row = wi * WM + U * 32 + l32;
+        fa[U] = frag(As[buf], row, h);
+        ra[U] = *reinterpret_cast<const uint2 *>(&nA[buf][2 * row]);
+      } else {
+        const int row = wj * WN + (U - MI) * 32 + l32;
+        fb[U - MI] = frag(Bs[buf], row, h);
+        rb[U - MI] = *reinterpret_cast<const uint2 *>(&nB[buf][2 * row]);
+      }
+    };
+    // unit U's block scales to f16 (once per stage, before its first decode)
+    auto prep_unit = [&](auto u) __attribute__((always_inline)) {
+      constexpr int U = decltype(u)::value;
+      if constexpr (U < MI)
+        sa[U] = nv_scales(ra[U]);
+      else
+        sb[U - MI] = nv_scales(rb[U - MI]);
+    };
+    // the f16 operand U of k16 step S (into set S % 2)
+    auto decode = [&](auto s, auto u) __attribute__((always_inline)) {
+      constexpr int S = decltype(s)::value, U = decltype(u)::value;
+      if constexpr (U < MI)
+        ao[S % 2][U] = nv_operand((uint32_t)fa[U][S], nv_dd<S>(sa[U]));
+      else
+        bo[S % 2][U - MI] = nv_operand((uint32_t)fb[U - MI][S], nv_dd<S>(sb[U - MI]));
+    };
+    using US = std::make_integer_sequence<int, MI + NI>;
+
+    // prologue: stages 0..2 in flight; once stages 0 and 1 have landed, the
+    // operands of stage 0's first step are read and decoded
     if (nsteps > 0) {
       copy(0);
       copy(1);
       copy(2);
+      wait_vm<1 * OPS>();
+      __syncthreads();
+      [&]<int... Us>(std::integer_sequence<int, Us...>) {
+        (read_unit(std::integral_constant<int, Us>{}, 0), ...);
+        (prep_unit(std::integral_constant<int, Us>{}), ...);
+        (decode(std::integral_constant<int, 0>{}, std::integral_constant<int, Us>{}), ...);
+      }(US{});
     }
     for (int kt = 0; kt < nsteps; ++kt) {
-      const int buf = kt & 3;
-      // stage kt has landed (kt + 1 and kt + 2 may be in flight); after the
-      // barrier every wave is done with stage kt - 1, whose buffer the
-      // copies of stage kt + 3 reuse
+      const int nbuf = (kt + 1) & 3;
+      // stage kt + 1 has landed (kt + 2 may be in flight); after the barrier
+      // every wave is done with stage kt - 1, whose buffer the copies of
+      // stage kt + 3 reuse. The operands of this stage's first step were
+      // decoded during the previous stage.
       __builtin_amdgcn_sched_barrier(0);
-      wait_vm<2 * OPS>();
+      wait_vm<1 * OPS>();
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       copy(kt + 3);
-      v8i fa[MI], fb[NI];
-      NvScale sa[MI], sb[NI];
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        const int row = wi * WM + mi * 32 + l32;
-        fa[mi] = frag(As[buf], row, h);
-        sa[mi] = nv_scales(*reinterpret_cast<const uint2 *>(&nA[buf][2 * row]));
-      }
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        const int row = wj * WN + ni * 32 + l32;
-        fb[ni] = frag(Bs[buf], row, h);
-        sb[ni] = nv_scales(*reinterpret_cast<const uint2 *>(&nB[buf][2 * row]));
-      }
+      // step S's 16 MFMAs, each second one followed by the decode of one
+      // operand of step S + 1; in the last step, the first half reads the
+      // next stage's raw operands (the current ones are dead) and the second
+      // half decodes the next stage's first step
       [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
         ([&] {
           constexpr int S = Ss;
-          nv_v8h ao[MI], bo[NI];
-#pragma unroll
-          for (int mi = 0; mi < MI; ++mi) ao[mi] = nv_operand((uint32_t)fa[mi][S], nv_dd<S>(sa[mi]));
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni) bo[ni] = nv_operand((uint32_t)fb[ni][S], nv_dd<S>(sb[ni]));
-#pragma unroll
-          for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < NI; ++ni)
-              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ao[mi], bo[ni], acc[mi][ni], 0, 0, 0);
+          [&]<int... Xs>(std::integer_sequence<int, Xs...>) {
+            ([&] {
+              constexpr int X = Xs;
+              constexpr int mi = X / NI, ni = X % NI;
+              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ao[S % 2][mi], bo[S % 2][ni], acc[mi][ni], 0, 0, 0);
+              if constexpr (S + 1 < 8) {
+                if constexpr (X % 2 == 1) decode(std::integral_constant<int, S + 1>{}, std::integral_constant<int, X / 2>{});
+              } else {
+                if constexpr (X < MI + NI) {
+                  read_unit(std::integral_constant<int, X>{}, nbuf);
+                } else {
+                  prep_unit(std::integral_constant<int, X - (MI + NI)>{});
+                  decode(std::integral_constant<int, 0>{}, std::integral_constant<int, X - (MI + NI)>{});
+                }
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }(), ...);
+          }(std::make_integer_sequence<int, MI * NI>{});
         }(), ...);
       }(std::make_integer_sequence<int, 8>{});
     }
@@ -1176,10 +1248,14 @@ static hipError_t launch_cfg(const GemmArgs &a0, hipStream_t st) {
   GemmArgs a = a0;
   if (!plan_grid<BN>(MODE, a)) return a.nblocks < 0 ? hipErrorInvalidValue : hipSuccess;
   const unsigned grid = persistent_grid(a.nblocks);
-  if (MODE == kWgrad && a.accumulate)
-    grouped_gemm_kernel<MODE, RECIPE, FA, FB, BN, true><<<grid, 64 * gemm_waves<RECIPE>(), 0, st>>>(a);
-  else
-    grouped_gemm_kernel<MODE, RECIPE, FA, FB, BN, false><<<grid, 64 * gemm_waves<RECIPE>(), 0, st>>>(a);
+  // the accumulating instance exists for wgrad only
+  if constexpr (MODE == kWgrad) {
+    if (a.accumulate) {
+      grouped_gemm_kernel<MODE, RECIPE, FA, FB, BN, true><<<grid, 64 * gemm_waves<RECIPE>(), 0, st>>>(a);
+      return hipGetLastError();
+    }
+  }
+  grouped_gemm_kernel<MODE, RECIPE, FA, FB, BN, false><<<grid, 64 * gemm_waves<RECIPE>(), 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -1198,10 +1274,13 @@ static hipError_t launch_nvfp4(const GemmArgs &a0, hipStream_t st) {
   GemmArgs a = a0;
   if (!plan_grid<256>(MODE, a)) return a.nblocks < 0 ? hipErrorInvalidValue : hipSuccess;
   const unsigned grid = persistent_grid(a.nblocks);
-  if (MODE == kWgrad && a.accumulate)
-    nvfp4_gemm_kernel<MODE, true><<<grid, 256, 0, st>>>(a);
-  else
-    nvfp4_gemm_kernel<MODE, false><<<grid, 256, 0, st>>>(a);
+  if constexpr (MODE == kWgrad) {
+    if (a.accumulate) {
+      nvfp4_gemm_kernel<MODE, true><<<grid, 256, 0, st>>>(a);
+      return hipGetLastError();
+    }
+  }
+  nvfp4_gemm_kernel<MODE, false><<<grid, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
