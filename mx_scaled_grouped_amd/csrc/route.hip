@@ -13,10 +13,11 @@
 // small next to the activations it orders and stays in the L2 caches, so
 // every workgroup reads all of it twice: once to count the entries that
 // precede its expert's group (ids below e) and its own, once to write its
-// rows. Within a pass, chunks of 1024 entries are compacted in order with a
-// wave ballot (lane prefix = popcount of the lower lanes' bits) and one
-// prefix over the 16 wave totals, so the order within a group is the entry
-// order (stable) without any sort. No scratch memory, no atomics on data.
+// rows. In the second pass, chunks of 4096 entries (4 consecutive ones per
+// thread) are compacted in order with a wave prefix sum of the threads' hit
+// counts and one prefix over the 16 wave totals, so the order within a group
+// is the entry order (stable) without any sort; the next chunk's ids load
+// while the current one is compacted. No scratch memory, no atomics on data.
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "mxsg.h"
@@ -56,16 +57,24 @@ __global__ __launch_bounds__(RT) void route_kernel(const int32_t *__restrict__ i
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
 
   // pass 1: entries of lower experts (the group's start) and of this one
+  // (eight independent entries per thread and iteration, so their loads are
+  // in flight together)
   int64_t below = 0, mine = 0;
-  for (int64_t i = t; i < n; i += RT) {
-    const int32_t v = ids[i];
-    const bool valid = v >= 0 && v < E;
-    if (e < E) {
-      below += valid && v < e;
-      mine += v == e;
-    } else {
-      below += valid;
-      mine += !valid;
+  for (int64_t b0 = 0; b0 < n; b0 += (int64_t)RT * 8) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t i = b0 + (int64_t)j * RT + t;
+      if (i < n) {
+        const int32_t v = ids[i];
+        const bool valid = v >= 0 && v < E;
+        if (e < E) {
+          below += valid && v < e;
+          mine += v == e;
+        } else {
+          below += valid;
+          mine += !valid;
+        }
+      }
     }
   }
   block_sum2(below, mine, red);
@@ -78,38 +87,71 @@ __global__ __launch_bounds__(RT) void route_kernel(const int32_t *__restrict__ i
 
   // pass 2: this group's rows in entry order. The invalid-id workgroup marks
   // its entries' inverse map -1 and fills the row slots past the last group
-  // (valid entries .. n) with -1.
+  // (valid entries .. n) with -1. Chunks of RT * PER entries, PER consecutive
+  // entries per thread; the next chunk's ids are loaded before this chunk's
+  // barrier, so their latency overlaps it. (Measured on 98304 choices over
+  // 64 experts: PER = 4 102 us; 1 entry per thread per chunk 147 us; 16
+  // per thread 113 us; four coalesced 1024-entry sub-chunks per barrier 139
+  // us.)
+  constexpr int PER = 4;
+  constexpr int64_t CH = (int64_t)RT * PER;
+  auto load = [&](int64_t base, int32_t (&v)[PER]) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int64_t i = base + (int64_t)t * PER + j;
+      v[j] = i < n ? ids[i] : 0;
+    }
+  };
   int64_t run = 0;
   int buf = 0;
-  for (int64_t base = 0; base < n; base += RT) {
-    const int64_t i = base + t;
-    bool hit = false;
-    if (i < n) {
-      const int32_t v = ids[i];
-      hit = e < E ? v == e : !(v >= 0 && v < E);
+  int32_t cur[PER], nxt[PER];
+  load(0, cur);
+  for (int64_t base = 0; base < n; base += CH) {
+    if (base + CH < n) load(base + CH, nxt);
+    unsigned hits = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int64_t i = base + (int64_t)t * PER + j;
+      const int32_t v = cur[j];
+      const bool hit = i < n && (e < E ? v == e : !(v >= 0 && v < E));
+      hits |= (unsigned)hit << j;
     }
-    const uint64_t m = __ballot(hit);
-    if (lane == 0) wtot[buf][wave] = (int32_t)__popcll(m);
+    // exclusive prefix of the threads' hit counts, in entry order
+    const int c = __popc(hits);
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += u;
+    }
+    if (lane == 63) wtot[buf][wave] = incl;
     __syncthreads();
     int64_t off = 0, tot = 0;
 #pragma unroll
     for (int w = 0; w < RW; ++w) {
-      const int32_t c = wtot[buf][w];
-      off += w < wave ? c : 0;
-      tot += c;
+      const int32_t cw = wtot[buf][w];
+      off += w < wave ? cw : 0;
+      tot += cw;
     }
-    if (hit) {
-      const int64_t pos = below + run + off + __popcll(m & ((1ull << lane) - 1ull));
-      if (e < E) {
-        row_index[pos] = (int32_t)(i / k);
-        if (slot_row) slot_row[i] = (int32_t)pos;
-      } else {
-        row_index[pos] = -1;
-        if (slot_row) slot_row[i] = -1;
+    int64_t pos = below + run + off + (incl - c);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (hits & (1u << j)) {
+        const int64_t i = base + (int64_t)t * PER + j;
+        if (e < E) {
+          row_index[pos] = (int32_t)(i / k);
+          if (slot_row) slot_row[i] = (int32_t)pos;
+        } else {
+          row_index[pos] = -1;
+          if (slot_row) slot_row[i] = -1;
+        }
+        ++pos;
       }
     }
     run += tot;
     buf ^= 1;  // the next chunk's totals go to the other buffer: one barrier per chunk
+#pragma unroll
+    for (int j = 0; j < PER; ++j) cur[j] = nxt[j];
   }
 }
 
