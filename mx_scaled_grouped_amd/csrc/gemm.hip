@@ -868,6 +868,390 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
 
 
 // ---------------------------------------------------------------------------
+// Blockwise grouped GEMM (1x128 / 128x1 token scales, 128x128 weight scales,
+// all fp32; DeepSeek-V3's recipe as the TE issue design note describes it):
+// C[i, j] = sum over 128-blocks b of sA(i, b) * sB(b, j) * P_b[i, j], where
+// P_b is the exact FP8 product over block b.
+//
+// One MFMA per block: v_mfma_scale_f32_16x16x128_f8f6f4 (unit E8M0 scales)
+// contracts a whole 128-long block into a 16 x 16 partial of four registers
+// per lane, which the lane then promotes into its fp32 totals with one FMA
+// per element (the factor sA(i) * sB is one number per lane and sub-tile
+// row: the MFMA is called with the B fragment first, so a lane holds one
+// output row i and four consecutive columns). Small partials let a
+// 256 x 256 tile fit: eight waves (two per SIMD) of 64 x 128, each with
+// 4 x 8 sub-tiles (128 registers of totals, 32 of A fragments for the whole
+// block, 8 per B fragment), so the tile's copy demand per MFMA is that of the
+// tensorwise 256 x 256 tile instead of the 1.5x of a 256 x 128 one.
+//
+// The LDS holds two blocks (four 64-byte stages of A and of B, 128 KB) and
+// the block loop is block-major: at a block's barrier its data has landed and
+// every wave is done with the block before, whose buffers then receive the
+// next block's copies (direct-to-LDS buffer loads, one block ahead). Each
+// wave walks its sub-tiles column by column (8 columns of 4 MFMAs), reading
+// the next column's B fragment while the current one runs; a sub-tile's
+// promotion is issued two MFMAs after its own, when its partial has certainly
+// been written. The last column of a block runs after the next block's
+// barrier, on fragments already in registers, while the new block's A
+// fragments arrive.
+__device__ __forceinline__ int64_t uni64(int64_t v) {
+  const uint64_t u = (uint64_t)v;
+  return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(u >> 32)) << 32) |
+                   (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u));
+}
+
+template <int MODE, int FA, int FB, bool ACC>
+__global__ __launch_bounds__(512) void blockwise_gemm_kernel(GemmArgs a) {
+  constexpr int NW = 8;
+  constexpr int BN = 256;
+  constexpr int WM = 64, WN = 128;  // wave tile: 4 waves along i, 2 along j
+  constexpr int AQ = GBM / 16 / NW, BQ = BN / 16 / NW;  // 1 KB copy groups per wave and stage
+  constexpr bool WG = MODE == kWgrad;
+  typedef float v4f __attribute__((ext_vector_type(4)));
+
+  __shared__ __attribute__((aligned(1024))) uint8_t As[4][GBM * GBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t Bs[4][BN * GBK];
+  __shared__ __attribute__((aligned(16))) float sAr[2][GBM];          // per-row A scales of a block
+  __shared__ __attribute__((aligned(16))) float sBr[2][WG ? BN : 64];  // wgrad: per-column B scales
+  __shared__ float sbtab[WG ? 1 : 2 * SB_TAB];  // FWD / DGRAD: sB of the tile's two j-blocks, per block
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wi = wave & 3, wj = wave >> 2;
+  const int l16 = lane & 15, g4 = lane >> 4;
+
+  for (int vb = blockIdx.x; vb < a.nblocks; vb += gridDim.x) {
+    const int lid = xcd_remap<32>(vb, a.nblocks);
+    int g = 0;
+    int64_t i0 = 0, ilo = 0, ihi = 0, j0 = 0, l0 = 0;
+    int nsteps = 0;
+    if (WG) {
+      const int per_g = a.slots * a.jtiles;
+      g = lid / per_g;
+      int it, jt;
+      raster(lid - g * per_g, a.slots, a.jtiles, it, jt);
+      i0 = (int64_t)it * GBM;
+      j0 = (int64_t)jt * BN;
+      ilo = i0;
+      ihi = a.I < i0 + GBM ? a.I : i0 + GBM;
+      int64_t p_lo = a.pstarts[g], p_hi = a.pstarts[g + 1];
+      const int64_t cap = a.lda < a.ldb ? a.lda : a.ldb;  // token positions
+      p_lo = p_lo < 0 ? 0 : (p_lo > cap ? cap : p_lo);
+      p_hi = p_hi < p_lo ? p_lo : (p_hi > cap ? cap : p_hi);
+      l0 = p_lo & ~(int64_t)127;  // padded starts are 128-aligned
+      nsteps = (int)(((p_hi - l0) / 128) * 2);
+    } else {
+      int slot, jt;
+      raster(lid, a.slots, a.jtiles, slot, jt);
+      j0 = (int64_t)jt * BN;
+      if (!locate_row_tile(a, slot, g, i0, ilo, ihi)) continue;
+      // (read from LDS: wave-uniform values the compiler would keep in VGPRs)
+      g = __builtin_amdgcn_readfirstlane(g);
+      i0 = uni64(i0);
+      ilo = uni64(ilo);
+      ihi = uni64(ihi);
+      nsteps = (int)(a.L / GBK);
+    }
+    const int nblk = nsteps >> 1;  // 128-blocks of the contraction
+    const int64_t sa_row = WG ? a.lda : a.L;  // contraction elements per scale row
+    const int64_t sb_row = WG ? a.ldb : a.L;
+
+    // copy offsets: as in grouped_gemm_kernel (pairs past the last valid one
+    // re-read it)
+    const int64_t lb = l0 / GBK;
+    const uint8_t *abase = a.a + (i0 >> 1) * 2 * a.lda + lb * 128;
+    const uint8_t *bbase = a.b + (WG ? 0 : (int64_t)g * a.b_gstride) + (j0 >> 1) * 2 * a.ldb + lb * 128;
+    const rsrc_t rsA = make_rsrc(abase, 0xFFFFFFFFu), rsB = make_rsrc(bbase, 0xFFFFFFFFu);
+    const rsrc_t rsZ = make_rsrc(kZeroSrc, 0u);
+    const int apmax = (int)(((ihi - 1) >> 1) - (i0 >> 1));
+    const int64_t jlim = (a.J - j0) < BN ? (a.J - j0) : BN;
+    const int bpmax = (int)((jlim - 1) >> 1);
+    uint32_t aoff[AQ], boff[BQ];
+#pragma unroll
+    for (int q = 0; q < AQ; ++q) {
+      const int row = (wave * AQ + q) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      const int pr = (row >> 1) < apmax ? (row >> 1) : apmax;
+      aoff[q] = (uint32_t)(pr * 2 * (int32_t)a.lda + (row & 1) * 64 + c * 16);
+    }
+#pragma unroll
+    for (int q = 0; q < BQ; ++q) {
+      const int row = (wave * BQ + q) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      const int pr = (row >> 1) < bpmax ? (row >> 1) : bpmax;
+      boff[q] = (uint32_t)(pr * 2 * (int32_t)a.ldb + (row & 1) * 64 + c * 16);
+    }
+    // scale rows: waves 0-3 copy the A scales of tile rows 64w..64w+63 (rows
+    // clamped into the valid ones); wgrad: waves 4-7 the B scales of tile
+    // columns 64(w-4)..; the other waves copy zeros into sBr's spare slot
+    const float *zsrc4 = reinterpret_cast<const float *>(kZeroSrc) + lane;
+    const float *sc_src = zsrc4;
+    float *sc_dst0, *sc_dst1;
+    const bool has_sc = wave < 4 || WG;
+    {
+      const int r = (wave & 3) * 64 + lane;
+      if (wave < 4) {
+        const int64_t i = i0 + r;
+        const int64_t ic = i < ilo ? ilo : (i >= ihi ? ihi - 1 : i);
+        sc_src = reinterpret_cast<const float *>(a.a_scales) + ic * (sa_row / SBLK) + l0 / SBLK;
+        sc_dst0 = &sAr[0][(wave & 3) * 64];
+        sc_dst1 = &sAr[1][(wave & 3) * 64];
+      } else if (WG) {
+        const int64_t j = j0 + (r < jlim ? r : jlim - 1);
+        sc_src = reinterpret_cast<const float *>(a.b_scales) + j * (sb_row / SBLK) + l0 / SBLK;
+        sc_dst0 = &sBr[0][(wave & 3) * 64];
+        sc_dst1 = &sBr[1][(wave & 3) * 64];
+      } else {
+        sc_dst0 = &sBr[0][0];
+        sc_dst1 = &sBr[1][0];
+      }
+    }
+    if (!WG) {
+      // the weight scales of the tile's two j-blocks (the second clamped to
+      // the last one when the tile overhangs J)
+      const int64_t jb0 = j0 / SBLK, jbl = a.J / SBLK - 1;
+      for (int e = t; e < 2 * nblk; e += 64 * NW) {
+        const int h = e >= nblk, lbk = e - h * nblk;
+        const int64_t jb = jb0 + h < jbl ? jb0 + h : jbl;
+        sbtab[h * SB_TAB + lbk] =
+            reinterpret_cast<const float *>(a.b_scales)[(int64_t)g * a.bs_gstride + lbk * a.sb_l + jb * a.sb_j];
+      }
+    }
+
+    // copies of block bb into buffer pair q (stages 2q, 2q + 1); a block
+    // past the contraction copies zeros
+    auto copy_block = [&](int bb, int q) __attribute__((always_inline)) {
+      const bool real = bb < nblk;
+      const rsrc_t ra = real ? rsA : rsZ, rb = real ? rsB : rsZ;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const uint32_t soff = (uint32_t)(2 * bb + s) * 128u;
+#pragma unroll
+        for (int c = 0; c < AQ; ++c) bdma16(ra, aoff[c], soff, &As[2 * q + s][(wave * AQ + c) * 1024]);
+#pragma unroll
+        for (int c = 0; c < BQ; ++c) bdma16(rb, boff[c], soff, &Bs[2 * q + s][(wave * BQ + c) * 1024]);
+      }
+      dma4(real && has_sc ? sc_src + bb : zsrc4, q ? sc_dst1 : sc_dst0);
+    };
+
+    // fragment of sub-tile row `row` for the whole block in pair q: chunk g4
+    // of the row in each of the block's two stages (the MFMA's k order is
+    // the same for both operands, so any fixed assignment of the 128 k to
+    // lanes contracts correctly)
+    auto frag_blk = [&](const uint8_t (*buf)[GBM * GBK], int q, int row) -> v8i {
+      const int o = swz(row, g4);
+      const uint4 x0 = *reinterpret_cast<const uint4 *>(&buf[2 * q][o]);
+      const uint4 x1 = *reinterpret_cast<const uint4 *>(&buf[2 * q + 1][o]);
+      return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    };
+    auto fragA = [&](int q, int mi) { return frag_blk(As, q, wi * WM + mi * 16 + l16); };
+    auto fragB = [&](int q, int ni) { return frag_blk(Bs, q, wj * WN + ni * 16 + l16); };
+    // the four column scales of this lane in column ni of the wave tile (wgrad)
+    auto col_scales = [&](int q, int ni) -> v4f {
+      const float4 v = *reinterpret_cast<const float4 *>(&sBr[q][wj * WN + ni * 16 + 4 * g4]);
+      return v4f{v.x, v.y, v.z, v.w};
+    };
+
+    v4f acc[4][8];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 8; ++ni) acc[mi][ni] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    // registers of the block schedule; zero before the first block, whose
+    // leading "previous column" then adds exact zeros
+    v8i af[4], bfX, bfY;     // A fragments; B fragments of even / odd columns
+    v4f p[4];                // partials, by sub-tile row
+    float fo[4], fn[4];      // promotion factors per sub-tile row: previous block, this block
+    v4f sbX, sbY;            // wgrad: column scales of even / odd columns
+    float sbw = 1.0f;        // FWD / DGRAD: this block's weight scale for the wave's j-block
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      af[m] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      p[m] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      fo[m] = 0.0f;
+      fn[m] = 0.0f;
+    }
+    bfX = af[0];
+    bfY = af[0];
+    sbX = p[0];
+    sbY = p[0];
+
+    auto mma = [&](const v8i &bfr, const v8i &afr) -> v4f {
+      const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr, afr, z, FB, FA, 0, kUnitScale, 0, kUnitScale);
+    };
+    auto promote = [&](v4f &c, const v4f &pp, float f, const v4f &sb) __attribute__((always_inline)) {
+      if constexpr (WG) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) c[v] += (pp[v] * sb[v]) * f;
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) c[v] += pp[v] * f;
+      }
+    };
+
+    // Event E (0..31) of a block iteration: events 0-3 are column 7 of the
+    // previous block (sub-tile rows 0-3), events 4 + 4n + m column n < 7 of
+    // this block, row m. After its MFMA, the event promotes the sub-tile of
+    // event E - 2 and issues reads whose target registers are free by then.
+    auto event = [&](auto e_, int q, auto read_) __attribute__((always_inline)) {
+      constexpr int E = decltype(e_)::value;
+      constexpr bool READ = decltype(read_)::value;  // false: the column after the last block
+      constexpr int N = E < 4 ? 7 : (E - 4) / 4;  // column
+      constexpr int M = E < 4 ? E : (E - 4) % 4;  // sub-tile row
+      if constexpr (N % 2 == 0)
+        p[M] = mma(bfX, af[M]);
+      else
+        p[M] = mma(bfY, af[M]);
+      // next column's B fragment, into the register set of column N - 1
+      // (last read by the previous event's MFMA)
+      if constexpr (E >= 4 && M == 0) {
+        if constexpr ((N + 1) % 2 == 0)
+          bfX = fragB(q, N + 1);
+        else
+          bfY = fragB(q, N + 1);
+      }
+      // promotion of event E - 2
+      if constexpr (E < 2) {
+        promote(acc[2 + E][6], p[2 + E], fo[2 + E], sbX);
+      } else if constexpr (E < 6) {
+        promote(acc[E - 2][7], p[E - 2], fo[E - 2], sbY);
+      } else {
+        constexpr int PN = (E - 6) / 4, PM = (E - 6) % 4;
+        if constexpr (PN % 2 == 0)
+          promote(acc[PM][PN], p[PM], fn[PM], sbX);
+        else
+          promote(acc[PM][PN], p[PM], fn[PM], sbY);
+      }
+      // this block's A fragment of row M, once the previous block's is used
+      if constexpr (E < 4 && READ) af[E] = fragA(q, E);
+      // wgrad: the next column's scales, into the set of column N - 1 (whose
+      // last promotion was just issued)
+      if constexpr (WG && E >= 4 && M == 1) {
+        if constexpr ((N + 1) % 2 == 0)
+          sbX = col_scales(q, N + 1);
+        else
+          sbY = col_scales(q, N + 1);
+      }
+      if constexpr (WG && E == 1 && READ) sbX = col_scales(q, 0);
+      if constexpr (!WG && E == 5) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) fn[m] *= sbw;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    if (nblk > 0) copy_block(0, 0);
+    for (int b = 0; b < nblk; ++b) {
+      const int q = b & 1;
+      // block b has landed (every wave waits for its own copies, then the
+      // barrier), and every wave is done reading block b - 1's buffers
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      bfX = fragB(q, 0);
+      // this block's factors: read now, multiplied at event 5 (first used
+      // at event 6), so that no early MFMA waits for these reads
+      sbw = WG ? 1.0f : sbtab[wj * SB_TAB + b];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) fn[m] = sAr[q][wi * WM + m * 16 + l16];
+      __builtin_amdgcn_sched_barrier(0);
+      event(std::integral_constant<int, 0>{}, q, std::true_type{});
+      event(std::integral_constant<int, 1>{}, q, std::true_type{});
+      copy_block(b + 1, q ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+      [&]<int... Es>(std::integer_sequence<int, Es...>) {
+        (event(std::integral_constant<int, 2 + Es>{}, q, std::true_type{}), ...);
+      }(std::make_integer_sequence<int, 30>{});
+#pragma unroll
+      for (int m = 0; m < 4; ++m) fo[m] = fn[m];
+    }
+    // column 7 of the last block, then its last promotions
+    event(std::integral_constant<int, 0>{}, 0, std::false_type{});
+    event(std::integral_constant<int, 1>{}, 0, std::false_type{});
+    event(std::integral_constant<int, 2>{}, 0, std::false_type{});
+    event(std::integral_constant<int, 3>{}, 0, std::false_type{});
+    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    promote(acc[2][7], p[2], fo[2], sbY);
+    promote(acc[3][7], p[3], fo[3], sbY);
+    wait_vm<0>();
+    __syncthreads();  // every wave is done with the stage buffers
+
+    if (ACC && nsteps == 0) continue;  // empty group: dW_g unchanged
+    // ---- epilogue: each wave stages 16-row slabs (one sub-tile row) in its
+    // own 16 KB of the stage buffers, then writes rows with 16-byte stores
+    constexpr int STR = WN + 4;  // LDS row stride in floats (16-byte rows land on distinct banks)
+    float *cb = reinterpret_cast<float *>(wave < 4 ? As[wave] : Bs[wave - 4]);
+    const int64_t jw = j0 + wj * WN;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+      for (int ni = 0; ni < 8; ++ni)
+        *reinterpret_cast<float4 *>(&cb[l16 * STR + ni * 16 + 4 * g4]) =
+            make_float4(acc[mi][ni][0], acc[mi][ni][1], acc[mi][ni][2], acc[mi][ni][3]);
+      __builtin_amdgcn_wave_barrier();
+      const int64_t ib = i0 + wi * WM + mi * 16;
+      if constexpr (WG) {
+        constexpr int CPR4 = WN / 4;  // float4 chunks per row
+        constexpr int CPL4 = 16 * CPR4 / 64;
+        float4 old[ACC ? CPL4 : 1];
+        if constexpr (ACC) {
+#pragma unroll
+          for (int k = 0; k < CPL4; ++k) {
+            const int id = k * 64 + lane;
+            const int64_t i = ib + id / CPR4, j = jw + (id % CPR4) * 4;
+            old[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (i >= ilo && i < ihi && j < a.J)
+              old[k] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.out) +
+                                                         ((int64_t)g * a.I + i) * a.ldo + j);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < CPL4; ++k) {
+          const int id = k * 64 + lane;
+          const int r = id / CPR4, c4 = id % CPR4;
+          const int64_t i = ib + r, j = jw + c4 * 4;
+          float4 y = *reinterpret_cast<const float4 *>(&cb[r * STR + c4 * 4]);
+          if (i >= ilo && i < ihi && j < a.J) {  // J % 128 == 0: a chunk is all in or all out
+            if constexpr (ACC) y = make_float4(y.x + old[k].x, y.y + old[k].y, y.z + old[k].z, y.w + old[k].w);
+            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.out) + ((int64_t)g * a.I + i) * a.ldo + j) = y;
+          }
+        }
+      } else {
+        constexpr int CPR = WN / 8;  // 8-value (16-byte bf16) chunks per row
+        constexpr int CPL = 16 * CPR / 64;
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+          const int id = k * 64 + lane;
+          const int r = id / CPR, c8 = id % CPR;
+          const int64_t i = ib + r, j = jw + c8 * 8;
+          const float4 x0 = *reinterpret_cast<const float4 *>(&cb[r * STR + c8 * 8]);
+          const float4 x1 = *reinterpret_cast<const float4 *>(&cb[r * STR + c8 * 8 + 4]);
+          if (i >= ilo && i < ihi && j < a.J) {
+            uint4 o;
+            o.x = f32_to_bf16_bits(x0.x) | (f32_to_bf16_bits(x0.y) << 16);
+            o.y = f32_to_bf16_bits(x0.z) | (f32_to_bf16_bits(x0.w) << 16);
+            o.z = f32_to_bf16_bits(x1.x) | (f32_to_bf16_bits(x1.y) << 16);
+            o.w = f32_to_bf16_bits(x1.z) | (f32_to_bf16_bits(x1.w) << 16);
+            uint16_t *dst = reinterpret_cast<uint16_t *>(a.out) + i * a.ldo + j;
+            if (a.stream_out)
+              store16_stream(dst, o);
+            else
+              *reinterpret_cast<uint4 *>(dst) = o;
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();  // the staging buffers are free before the next tile's copies land
+  }
+}
+
+
+// ---------------------------------------------------------------------------
 // NVFP4 grouped GEMM: e2m1 codes with an e4m3 scale per 16 contraction
 // elements and an fp32 scale per tensor (the NVFP4 rows of the Megatron-LM
 // single-grouped-weight PR's coverage table). gfx950's scaled MFMAs take
@@ -1244,10 +1628,20 @@ static unsigned persistent_grid(int nblocks) {
 
 template <int MODE, int RECIPE, int FA, int FB>
 static hipError_t launch_cfg(const GemmArgs &a0, hipStream_t st) {
-  constexpr int BN = RECIPE == kBlockwise ? 128 : 256;
+  constexpr int BN = 256;
   GemmArgs a = a0;
   if (!plan_grid<BN>(MODE, a)) return a.nblocks < 0 ? hipErrorInvalidValue : hipSuccess;
   const unsigned grid = persistent_grid(a.nblocks);
+  if constexpr (RECIPE == kBlockwise) {
+    if constexpr (MODE == kWgrad) {
+      if (a.accumulate) {
+        blockwise_gemm_kernel<MODE, FA, FB, true><<<grid, 512, 0, st>>>(a);
+        return hipGetLastError();
+      }
+    }
+    blockwise_gemm_kernel<MODE, FA, FB, false><<<grid, 512, 0, st>>>(a);
+    return hipGetLastError();
+  } else {
   // the accumulating instance exists for wgrad only
   if constexpr (MODE == kWgrad) {
     if (a.accumulate) {
@@ -1257,6 +1651,7 @@ static hipError_t launch_cfg(const GemmArgs &a0, hipStream_t st) {
   }
   grouped_gemm_kernel<MODE, RECIPE, FA, FB, BN, false><<<grid, 64 * gemm_waves<RECIPE>(), 0, st>>>(a);
   return hipGetLastError();
+  }
 }
 
 template <int MODE, int RECIPE>
