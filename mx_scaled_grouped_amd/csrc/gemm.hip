@@ -1020,19 +1020,26 @@ __global__ __launch_bounds__(512) void blockwise_gemm_kernel(GemmArgs a) {
     }
 
     // copies of block bb into buffer pair q (stages 2q, 2q + 1); a block
-    // past the contraction copies zeros
-    auto copy_block = [&](int bb, int q) __attribute__((always_inline)) {
+    // past the contraction copies zeros. Piece K: the A (K = 0, 2) or B
+    // (K = 1, 3) chunks of stage K / 2, or (K = 4) the scale row.
+    auto copy_piece = [&](int bb, int q, auto k_) __attribute__((always_inline)) {
+      constexpr int K = decltype(k_)::value;
       const bool real = bb < nblk;
-      const rsrc_t ra = real ? rsA : rsZ, rb = real ? rsB : rsZ;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      if constexpr (K < 4) {
+        constexpr int s = K / 2;
         const uint32_t soff = (uint32_t)(2 * bb + s) * 128u;
+        if constexpr (K % 2 == 0) {
+          const rsrc_t ra = real ? rsA : rsZ;
 #pragma unroll
-        for (int c = 0; c < AQ; ++c) bdma16(ra, aoff[c], soff, &As[2 * q + s][(wave * AQ + c) * 1024]);
+          for (int c = 0; c < AQ; ++c) bdma16(ra, aoff[c], soff, &As[2 * q + s][(wave * AQ + c) * 1024]);
+        } else {
+          const rsrc_t rb = real ? rsB : rsZ;
 #pragma unroll
-        for (int c = 0; c < BQ; ++c) bdma16(rb, boff[c], soff, &Bs[2 * q + s][(wave * BQ + c) * 1024]);
+          for (int c = 0; c < BQ; ++c) bdma16(rb, boff[c], soff, &Bs[2 * q + s][(wave * BQ + c) * 1024]);
+        }
+      } else {
+        dma4(real && has_sc ? sc_src + bb : zsrc4, q ? sc_dst1 : sc_dst0);
       }
-      dma4(real && has_sc ? sc_src + bb : zsrc4, q ? sc_dst1 : sc_dst0);
     };
 
     // fragment of sub-tile row `row` for the whole block in pair q: chunk g4
@@ -1142,7 +1149,13 @@ __global__ __launch_bounds__(512) void blockwise_gemm_kernel(GemmArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    if (nblk > 0) copy_block(0, 0);
+    if (nblk > 0) {
+      copy_piece(0, 0, std::integral_constant<int, 0>{});
+      copy_piece(0, 0, std::integral_constant<int, 1>{});
+      copy_piece(0, 0, std::integral_constant<int, 2>{});
+      copy_piece(0, 0, std::integral_constant<int, 3>{});
+      copy_piece(0, 0, std::integral_constant<int, 4>{});
+    }
     for (int b = 0; b < nblk; ++b) {
       const int q = b & 1;
       // block b has landed (every wave waits for its own copies, then the
@@ -1158,13 +1171,18 @@ __global__ __launch_bounds__(512) void blockwise_gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) fn[m] = sAr[q][wi * WM + m * 16 + l16];
       __builtin_amdgcn_sched_barrier(0);
-      event(std::integral_constant<int, 0>{}, q, std::true_type{});
-      event(std::integral_constant<int, 1>{}, q, std::true_type{});
-      copy_block(b + 1, q ^ 1);
-      __builtin_amdgcn_sched_barrier(0);
+      // the next block's copies go out in five pieces, after events 1, 5,
+      // 9, 13 and 17: spread over the MFMAs, they ran 7-10% faster than as
+      // one burst after event 1
       [&]<int... Es>(std::integer_sequence<int, Es...>) {
-        (event(std::integral_constant<int, 2 + Es>{}, q, std::true_type{}), ...);
-      }(std::make_integer_sequence<int, 30>{});
+        ([&] {
+          event(std::integral_constant<int, Es>{}, q, std::true_type{});
+          if constexpr (Es % 4 == 1 && Es / 4 < 5) {
+            copy_piece(b + 1, q ^ 1, std::integral_constant<int, Es / 4>{});
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }(), ...);
+      }(std::make_integer_sequence<int, 32>{});
 #pragma unroll
       for (int m = 0; m < 4; ++m) fo[m] = fn[m];
     }
@@ -1186,6 +1204,11 @@ __global__ __launch_bounds__(512) void blockwise_gemm_kernel(GemmArgs a) {
     constexpr int STR = WN + 4;  // LDS row stride in floats (16-byte rows land on distinct banks)
     float *cb = reinterpret_cast<float *>(wave < 4 ? As[wave] : Bs[wave - 4]);
     const int64_t jw = j0 + wj * WN;
+    // the lane index, opaque to the compiler here: otherwise it computes
+    // every store address before the main loop and spills them, and each
+    // reload from scratch then waits for all earlier stores (vmcnt(0))
+    int lane_e = lane;
+    asm volatile("" : "+v"(lane_e));
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
@@ -1201,7 +1224,7 @@ __global__ __launch_bounds__(512) void blockwise_gemm_kernel(GemmArgs a) {
         if constexpr (ACC) {
 #pragma unroll
           for (int k = 0; k < CPL4; ++k) {
-            const int id = k * 64 + lane;
+            const int id = k * 64 + lane_e;
             const int64_t i = ib + id / CPR4, j = jw + (id % CPR4) * 4;
             old[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             if (i >= ilo && i < ihi && j < a.J)
@@ -1211,7 +1234,7 @@ __global__ __launch_bounds__(512) void blockwise_gemm_kernel(GemmArgs a) {
         }
 #pragma unroll
         for (int k = 0; k < CPL4; ++k) {
-          const int id = k * 64 + lane;
+          const int id = k * 64 + lane_e;
           const int r = id / CPR4, c4 = id % CPR4;
           const int64_t i = ib + r, j = jw + c4 * 4;
           float4 y = *reinterpret_cast<const float4 *>(&cb[r * STR + c4 * 4]);
@@ -1225,7 +1248,7 @@ __global__ __launch_bounds__(512) void blockwise_gemm_kernel(GemmArgs a) {
         constexpr int CPL = 16 * CPR / 64;
 #pragma unroll
         for (int k = 0; k < CPL; ++k) {
-          const int id = k * 64 + lane;
+          const int id = k * 64 + lane_e;
           const int r = id / CPR, c8 = id % CPR;
           const int64_t i = ib + r, j = jw + c8 * 8;
           const float4 x0 = *reinterpret_cast<const float4 *>(&cb[r * STR + c8 * 8]);
