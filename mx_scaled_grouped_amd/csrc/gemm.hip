@@ -10,14 +10,14 @@
 //   DGRAD i = token, j = k, l = n; B = n-major weight codes of expert g
 //   WGRAD i = k, j = n, l = padded tokens of group g (column-wise codes)
 //
-// gfx950 design: a 256-thread workgroup (4 waves, 2 x 2; blockwise: 8
-// waves, 4 x 2, two per SIMD) computes a
-// 256 x BN output tile; each wave owns (256 / waves along i) x BN/2 as
+// gfx950 design (tensorwise, delayed and MX recipes; blockwise scaling has
+// its own kernel, blockwise_gemm_kernel): a 256-thread workgroup (4 waves,
+// 2 x 2) computes a 256 x 256 output tile; each wave owns 128 x 128 as
 // 32 x 32 MFMA sub-tiles (v_mfma_scale_f32_32x32x64_f8f6f4). The
-// contraction runs in 64-wide stages through a ring of R LDS buffers (four;
-// blockwise six): direct-to-LDS buffer loads (no staging registers)
-// land XOR-swizzled 16-byte chunks (bank-conflict-free fragment reads) R - 1
-// stages ahead of use. The code operands are pair-interleaved, so a stage
+// contraction runs in 64-wide stages through a ring of four LDS buffers:
+// direct-to-LDS buffer loads (no staging registers) land XOR-swizzled
+// 16-byte chunks (bank-conflict-free fragment reads) three stages ahead of
+// use. The code operands are pair-interleaved, so a stage
 // of 64 bytes over a run of row pairs is whole 128-byte lines. A stage is
 // one barrier: its first two MFMAs are issued before it, and after it every
 // MFMA slot also issues one copy of the stage R - 1 ahead and part of the
@@ -31,8 +31,7 @@
 // stored); a workgroup finds its group from the device-resident offsets
 // (no host sync). Workgroup ids are remapped so
 // each XCD (and its L2) works on a contiguous run of tiles.
-// Scales: tensorwise / delayed in the epilogue (acc * sA * sB); blockwise
-// by promoting each 128-long block's fp32 partial with sA * sB; MX inside
+// Scales: tensorwise / delayed in the epilogue (acc * sA * sB); MX inside
 // the MFMA through its per-32-element E8M0 scale operands.
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -77,9 +76,8 @@ struct GemmArgs {
 // interleaved chunks of XCHUNK consecutive ids: each XCD gets every 8th chunk
 // (balanced even when groups differ wildly in size), and the tiles an XCD runs
 // together are neighbours in the rasterized order (shared L2 data). Ids past
-// the last full round of 8 chunks map to themselves. XCHUNK is 32 (one tile
-// per CU of an XCD), or 64 for the blockwise 256x128 tiles: measured 3% faster
-// there, neutral to slower for the 256x256 tiles.
+// the last full round of 8 chunks map to themselves. XCHUNK is 32: one tile
+// per CU of an XCD (64 measured neutral to slower for 256x256 tiles).
 template <int XCHUNK>
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   const int round = 8 * XCHUNK;
@@ -237,25 +235,9 @@ struct Frags {
 // MFMA operand format code (cbsz / blgp) of an element format
 __host__ __device__ constexpr int mfma_fmt(int f) { return f == kE2M1 ? 4 : f; }
 
-// waves per workgroup: blockwise runs two waves per SIMD, so that one
-// wave's per-block promotion (VALU) issues while the other's MFMAs run
-template <int RECIPE>
-constexpr int gemm_waves() { return RECIPE == kBlockwise ? 8 : 4; }
-
-// stage buffers in the LDS ring: four for the 256 x 256 tiles (32 KB a
-// stage); six for the blockwise 256 x 128 tile (24 KB a stage, with its
-// scales just inside the 160 KB), whose last stages then run as a partial
-// turn, so a contraction of 22 or 26 stages (hidden or ffn 1408; a group
-// of 1664 padded tokens) computes no padding stage. (Measured: six stages
-// in flight instead of four run the steady state no faster; the copies'
-// cost is in the per-CU fetch path, not in their latency.)
-template <int RECIPE>
-constexpr int gemm_ring() { return RECIPE == kBlockwise ? 6 : 4; }
-
 template <int MODE, int RECIPE, int FA, int FB, int BN, bool ACC>
-__global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel(GemmArgs a) {
-  constexpr int NW = gemm_waves<RECIPE>();
-  constexpr int NT = 64 * NW;        // threads
+__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
+  constexpr int NW = 4;              // waves
   constexpr int WI = NW / 2;         // waves along i (2 along j)
   constexpr int WM = GBM / WI;       // wave tile height along i
   constexpr int WN = BN / 2;         // wave tile width along j
@@ -263,8 +245,8 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
   constexpr int MI = WM / 32;        // 32-high sub-tiles along i per wave
   constexpr int AQ = GBM / 16 / NW;  // 1 KB copy groups (8 row pairs) of A per wave per stage
   constexpr int BQ = BN / 16 / NW;   // of B
-  constexpr bool BLK = RECIPE == kBlockwise;
   constexpr bool MX = RECIPE == kMx;
+  static_assert(RECIPE != kBlockwise, "blockwise scaling runs in blockwise_gemm_kernel");
   // MXFP4: two e2m1 codes per byte, so a 64-byte stage is 128 contraction
   // elements (four 32-blocks, one E8M0 word per row) and each tile takes two
   // MFMAs per stage, on the first and second 32 bytes of the stage
@@ -276,23 +258,11 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
   static_assert(!MX || (MI == 4 && NI == 4 && BN == 256), "MX word layout");
 
   // the ring's stage buffers of A and B codes (and of their per-stage
-  // scales), always indexed by compile-time constants
-  constexpr int R = gemm_ring<RECIPE>();
-  static_assert(R % 2 == 0, "a blockwise 128-block is two stages");
+  // scale words), always indexed by compile-time constants
+  constexpr int R = 4;
   __shared__ __attribute__((aligned(1024))) uint8_t As[R][GBM * GBK];
   __shared__ __attribute__((aligned(1024))) uint8_t Bs[R][BN * GBK];
-  __shared__ __attribute__((aligned(16))) float sAr[R][BLK ? GBM : 4];
-  __shared__ __attribute__((aligned(16))) float sBr[R][BLK && MODE == kWgrad ? BN : 4];
-  __shared__ float sbtab[BLK ? SB_TAB : 1];
-  // blockwise: the promotion factors of the 128-block whose partials are
-  // promoted next, per tile row (forward / dgrad: sA(row) * sB(tile), one
-  // product per row and block; wgrad: sA(row)) and, for wgrad, per tile
-  // column (sB(column))
-  // (one 64-entry slot per wave, so that every wave stores without a
-  // branch; the slots of the waves that copy no scales are never read)
-  __shared__ __attribute__((aligned(16))) float sS[BLK ? 64 * NW : 4];
-  __shared__ __attribute__((aligned(16))) float sSb[BLK && MODE == kWgrad ? 64 * NW : 4];
-  __shared__ __attribute__((aligned(256))) uint32_t dmy[64];  // target of filler copies  // blockwise weight scales of this tile's j-block, per l-block
+  __shared__ __attribute__((aligned(256))) uint32_t dmy[64];  // target of filler copies
   // MX: per stage buffer, each tile row's E8M0 word (the 32-blocks 4w..4w+3
   // holding the stage's two), stored so the four words one lane needs are
   // contiguous: slot d holds tile row 128 (d / 128) + 32 (d % 4) + (d / 4) % 32
@@ -312,7 +282,7 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
   // walking the tiles vb = blockIdx.x, + gridDim.x, ...; the next tile's
   // copies then start as soon as this tile's stores are issued
   for (int vb = blockIdx.x; vb < a.nblocks; vb += gridDim.x) {
-  const int lid = xcd_remap<BLK ? 64 : 32>(vb, a.nblocks);
+  const int lid = xcd_remap<32>(vb, a.nblocks);
   int g = 0;
   int64_t i0 = 0, ilo = 0, ihi = 0, j0 = 0, l0 = 0;
   int nsteps = 0;
@@ -339,15 +309,9 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
     l0 = 0;
     nsteps = (int)(a.L / GBK);
   }
-  // stages run: rounded up to whole ring turns (four buffers), or to whole
-  // 128-blocks (six buffers: the last stages then run as a partial turn; with
-  // four, the partial turn's code raised register use past the budget)
-  const int vsteps = R == 4 ? (nsteps + 3) & ~3 : (nsteps + 1) & ~1;
-
-  // scale-row strides (contraction elements per row): FWD / DGRAD scales are
-  // [rows, L/blk]; WGRAD scales follow the padded column layout, [rows, ld/blk]
-  const int64_t sa_row = (MODE == kWgrad ? a.lda : a.L) * EPB;
-  const int64_t sb_row = (MODE == kWgrad ? a.ldb : a.L) * EPB;
+  // stages run: rounded up to whole ring turns (a partial turn's code raised
+  // register use past the budget)
+  const int vsteps = (nsteps + 3) & ~3;
 
   // ---- per-lane byte offsets of the 16-byte chunks this lane copies. Copy
   // group q of a wave is 8 row pairs (16 rows of the stage tile): lane L
@@ -384,28 +348,7 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
   };
   auto brow = [&](int r) -> int64_t { return j0 + (r < jlim ? r : jlim - 1); };
 
-  // blockwise: per-row A scales (and per-row B scales for wgrad) copied per
-  // stage, wave w copying rows 64w..64w+63; the weight tile scales of the
-  // whole contraction (forward / dgrad) go to LDS once
-  const float *sa_src = nullptr, *sb_src = nullptr;
-  const bool b_wave = wave < BN / 64;   // copies B-row scale words / scales
-  const bool a_wave = wave < GBM / 64;  // copies A-row scales (blockwise)
-  if (BLK) {
-    const int r = wave * 64 + lane;
-    sa_src = reinterpret_cast<const float *>(a.a_scales) + arow(r) * (sa_row / SBLK) + l0 / SBLK;
-    if (MODE == kWgrad && b_wave)
-      sb_src = reinterpret_cast<const float *>(a.b_scales) + brow(r) * (sb_row / SBLK) + l0 / SBLK;
-    if (MODE != kWgrad) {
-      // zeros for the padding blocks of the last ring turn: their partials
-      // are zero, and a zero table entry keeps uninitialized LDS (possibly
-      // an Inf or NaN pattern) out of the product
-      const int64_t jb = j0 / SBLK;
-      for (int lbk = t; lbk < vsteps / 2 && lbk < SB_TAB; lbk += NT)
-        sbtab[lbk] = lbk < nsteps / 2 ? reinterpret_cast<const float *>(
-                                            a.b_scales)[(int64_t)g * a.bs_gstride + lbk * a.sb_l + jb * a.sb_j]
-                                      : 0.0f;
-    }
-  }
+  const bool b_wave = wave < BN / 64;   // copies B-row scale words
   // MX scale words: lane L of wave w copies word slot d = 64w + L (see the
   // slot layout above). The scale matrices are word-major (word w of all
   // rows, then word w + 1), so the words of one stage for a run of rows are
@@ -424,19 +367,11 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
             (l0 / 128) * mxb_word + brow(r) * 4;
   }
   // vector-memory instructions every wave issues per stage (the waits count
-  // them): scale words first (a filler copy into dmy where the wave has no
-  // B-side scale row), then the A and B code chunks
-  constexpr int NSC = MX ? 2 : (BLK ? (MODE == kWgrad ? 2 : 1) : 0);
+  // them): MX scale words first (a filler copy into dmy where the wave has
+  // no B-side scale row), then the A and B code chunks
+  constexpr int NSC = MX ? 2 : 0;
   constexpr int OPS = NSC + AQ + BQ;
   const uint32_t *usrc = kUnitScaleSrc + lane;
-  const float *zsrc4 = reinterpret_cast<const float *>(kZeroSrc) + lane;
-  // the first stage of the tile promotes a "block -1": zero partials and
-  // zero factors (LDS may hold any bit pattern, Inf or NaN included)
-  if (BLK) {
-    sS[wave * 64 + lane] = 0.0f;
-    if (MODE == kWgrad) sSb[wave * 64 + lane] = 0.0f;
-  }
-  __syncthreads();  // sbtab and the zero factors visible
 
   v16f acc[MI][NI];
 #pragma unroll
@@ -445,34 +380,20 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
     for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
-  v16f part[BLK ? MI : 1][BLK ? NI : 1];  // blockwise: partial sum of the current 128-block
-#pragma unroll
-  for (int mi = 0; mi < (BLK ? MI : 1); ++mi)
-#pragma unroll
-    for (int ni = 0; ni < (BLK ? NI : 1); ++ni)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) part[mi][ni][v] = 0.0f;
 
   // copy C (0 <= C < OPS) of stage kt into the stage buffers; a stage past
   // the contraction copies zeros (unit E8M0 scales), so the MFMAs of the
   // padding stages of the last ring turn add nothing. No branches.
-  auto copy = [&](auto c, int kt, uint8_t *as, uint8_t *bs, float *sa, float *sb, uint32_t *ma,
-                  uint32_t *mb) {
+  auto copy = [&](auto c, int kt, uint8_t *as, uint8_t *bs, uint32_t *ma, uint32_t *mb) {
     constexpr int C = decltype(c)::value;
     const bool real = kt < nsteps;
-    if constexpr (C < NSC) {
-      if constexpr (MX) {  // the E8M0 word holding this stage's 32-blocks
-        const int64_t w = (kt * EPB) >> 1;
-        if constexpr (C == 0)
-          dma4(real ? (const void *)(mxa + w * mxa_word) : (const void *)usrc, ma + wave * 64);
-        else
-          dma4(real && b_wave ? (const void *)(mxb + w * mxb_word) : (const void *)usrc,
-               b_wave ? mb + wave * 64 : dmy);
-      } else {
-        if constexpr (C == 0)
-          dma4(real && a_wave ? sa_src + (kt >> 1) : zsrc4, a_wave ? sa + wave * 64 : (float *)dmy);
-        else dma4(real && b_wave ? sb_src + (kt >> 1) : zsrc4, b_wave ? sb + wave * 64 : (float *)dmy);
-      }
+    if constexpr (C < NSC) {  // MX: the E8M0 word holding this stage's 32-blocks
+      const int64_t w = (kt * EPB) >> 1;
+      if constexpr (C == 0)
+        dma4(real ? (const void *)(mxa + w * mxa_word) : (const void *)usrc, ma + wave * 64);
+      else
+        dma4(real && b_wave ? (const void *)(mxb + w * mxb_word) : (const void *)usrc,
+             b_wave ? mb + wave * 64 : dmy);
     } else if constexpr (C < NSC + AQ) {
       constexpr int q = C - NSC;
       bdma16(real ? rsA : rsZ, aoff[q], (uint32_t)kt * 128u, as + (wave * AQ + q) * 1024);
@@ -481,10 +402,9 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
       bdma16(real ? rsB : rsZ, boff[q], (uint32_t)kt * 128u, bs + (wave * BQ + q) * 1024);
     }
   };
-  auto load_stage = [&](int kt, uint8_t *as, uint8_t *bs, float *sa, float *sb, uint32_t *ma,
-                        uint32_t *mb) {
+  auto load_stage = [&](int kt, uint8_t *as, uint8_t *bs, uint32_t *ma, uint32_t *mb) {
     [&]<int... Cs>(std::integer_sequence<int, Cs...>) {
-      (copy(std::integral_constant<int, Cs>{}, kt, as, bs, sa, sb, ma, mb), ...);
+      (copy(std::integral_constant<int, Cs>{}, kt, as, bs, ma, mb), ...);
     }(std::make_integer_sequence<int, OPS>{});
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -503,22 +423,13 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
   using WP = std::integral_constant<int, R - 2>;
 
   // an empty asm use of every accumulator: keeps the stage's MFMAs issued
-  // before the next wait, and each accumulator in its register file (AGPRs;
-  // blockwise: the totals and the block partials in VGPRs, so the promotion
-  // reads the partials directly)
+  // before the next wait, and each accumulator in its register file (AGPRs)
   auto pin_acc = [&]() {
 #if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        if (BLK) {
-          asm volatile("" ::"v"(acc[mi][ni]));
-          asm volatile("" ::"v"(part[mi][ni]));
-        } else {
-          asm volatile("" ::"a"(acc[mi][ni]));
-        }
-      }
+      for (int ni = 0; ni < NI; ++ni) asm volatile("" ::"a"(acc[mi][ni]));
 #endif
   };
 
@@ -562,8 +473,7 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
   };
 
   // MFMAs LO..HI-1 (index mi * NI + ni) of stage kt; PH = the stage's
-  // position in its 128-block (MX: which two bytes of the scale word;
-  // blockwise: 0 starts the partial, 1 continues it)
+  // position in its 128-block (MX: which two bytes of the scale word)
   auto mfma_range = [&](const Frags<MI, NI> &f, auto ph, auto lo, auto hi) {
     constexpr int PH = decltype(ph)::value;
     constexpr int LO = decltype(lo)::value, HI = decltype(hi)::value;
@@ -583,17 +493,6 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
         // lane half h takes byte 2*PH + h of the row's word (shifted by 8h): opsel 2*PH
         acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             f.a[mi], f.b[ni], acc[mi][ni], FA, FB, 2 * PH, f.sa[mi], 2 * PH, f.sb[ni]);
-      } else if (BLK) {
-        if (PH == 0) {
-          v16f z;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) z[v] = 0.0f;
-          part[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              f.a[mi], f.b[ni], z, FA, FB, 0, kUnitScale, 0, kUnitScale);
-        } else {
-          part[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              f.a[mi], f.b[ni], part[mi][ni], FA, FB, 0, kUnitScale, 0, kUnitScale);
-        }
       } else {
         // unit E8M0 scales (127 = 2^0); the scaled form keeps the
         // accumulators in AGPRs
@@ -603,45 +502,8 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
     }
   };
 
-  // blockwise promotion of one sub-tile's block partial: acc += partial *
-  // factor, with this lane's 16 rows' factors of sub-tile row mi in s (rows
-  // 8 (v / 4) + 4 h + v % 4 of the 32), times the column's sB for wgrad
-  auto load_factors = [&](int mi, float (&f)[16]) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 v4 = *reinterpret_cast<const float4 *>(&sS[wi * WM + mi * 32 + q * 8 + h * 4]);
-      f[q * 4 + 0] = v4.x;
-      f[q * 4 + 1] = v4.y;
-      f[q * 4 + 2] = v4.z;
-      f[q * 4 + 3] = v4.w;
-    }
-  };
-  auto promote_one = [&](int mi, int ni, const float (&f)[16]) {
-    if (MODE == kWgrad) {
-      const float sbj = sSb[wj * WN + ni * 32 + l32];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mi][ni][v] += part[mi][ni][v] * (f[v] * sbj);
-    } else {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mi][ni][v] += part[mi][ni][v] * f[v];
-    }
-  };
-  // blockwise, in the second stage of a 128-block (its scales are in that
-  // stage's buffers): each wave moves the factors of the rows it copied
-  // into its slot of sS / sSb, read after the next barrier. No branch: a
-  // wave that copied no scale rows re-reads valid ones into a slot nobody
-  // reads (a branch here let the compiler sink this stage's MFMAs below it).
-  auto stash_factors = [&](const float *sa_l, const float *sb_l, int kt) {
-    float v = sa_l[(wave % (GBM / 64)) * 64 + lane];
-    if (MODE != kWgrad) v *= sbtab[(kt >> 1) & (SB_TAB - 1)];
-    sS[wave * 64 + lane] = v;
-    if (MODE == kWgrad) sSb[wave * 64 + lane] = sb_l[(wave % (BN / 64)) * 64 + lane];
-  };
-
   // MFMAs of a stage issued before its barrier (their operands are already
   // in registers, so they keep the MFMA pipe busy while the waves sync).
-  // Blockwise: in the second stage of each block only (the first stage's
-  // MFMAs wait for the promotion of the previous block's partials).
   constexpr int NPRE = 2;
   using C0 = std::integral_constant<int, 0>;
   using CPRE = std::integral_constant<int, NPRE>;
@@ -654,44 +516,9 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
     // stage k: its first NPRE MFMAs (fragments read during stage k-1), wait
     // for stage k+1's copies, barrier, then slot by slot: one MFMA, one copy
     // of stage k+R-1, and the fragment reads of stage k+1 spread over the slots
-    auto step = [&](int k, Frags<MI, NI> &fc, Frags<MI, NI> &fn, const float *sac, const float *sbc,
-                    const uint8_t *an, const uint8_t *bn, const uint32_t *man, const uint32_t *mbn,
-                    uint8_t *al, uint8_t *bl, float *sal, float *sbl, uint32_t *mal, uint32_t *mbl,
-                    auto ph) __attribute__((always_inline)) {
-      if constexpr (BLK && decltype(ph)::value == 0) {
-        // blockwise, first stage of a block: after the barrier, sub-tile by
-        // sub-tile, promote the previous block's partial (VALU) and then
-        // start the new partial with this stage's MFMA, so each sub-tile's
-        // promotion issues while the previous sub-tile's MFMA runs
-        sync_stage(WR{});
-        // the partials were written by the previous stage's MFMAs: pad the
-        // MFMA-result-to-VALU-read distance explicitly (>= 40 wait states)
-        asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        constexpr int NS = MI * NI;
-        float f[16];
-        [&]<int... Ss>(std::integer_sequence<int, Ss...>) {
-          ([&] {
-            constexpr int S = Ss;
-            constexpr int mi = S / NI, ni = S % NI;
-            if constexpr (ni == 0) load_factors(mi, f);
-            promote_one(mi, ni, f);
-            mfma_range(fc, ph, std::integral_constant<int, S>{}, std::integral_constant<int, S + 1>{});
-            if constexpr (S < OPS) copy(std::integral_constant<int, S>{}, k + R - 1, al, bl, sal, sbl, mal, mbl);
-            constexpr int u0 = (NUNIT * S) / NS, u1 = (NUNIT * (S + 1)) / NS;
-            if constexpr (u1 > u0) read_unit(std::integral_constant<int, u0>{}, fn, an, bn, man, mbn);
-            if constexpr (u1 > u0 + 1) read_unit(std::integral_constant<int, u0 + 1>{}, fn, an, bn, man, mbn);
-            __builtin_amdgcn_sched_barrier(0);
-          }(), ...);
-        }(std::make_integer_sequence<int, NS>{});
-        if constexpr (OPS > NS) {
-          [&]<int... Cs>(std::integer_sequence<int, Cs...>) {
-            (copy(std::integral_constant<int, NS + Cs>{}, k + R - 1, al, bl, sal, sbl, mal, mbl), ...);
-          }(std::make_integer_sequence<int, OPS - NS>{});
-        }
-        pin_acc();
-        return;
-      }
+    auto step = [&](int k, Frags<MI, NI> &fc, Frags<MI, NI> &fn, const uint8_t *an, const uint8_t *bn,
+                    const uint32_t *man, const uint32_t *mbn, uint8_t *al, uint8_t *bl, uint32_t *mal,
+                    uint32_t *mbl, auto ph) __attribute__((always_inline)) {
       mfma_range(fc, ph, C0{}, CPRE{});
       sync_stage(WR{});
       constexpr int NS = MI * NI - NPRE;   // slots
@@ -699,7 +526,7 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
         ([&] {
           constexpr int S = Ss;
           mfma_range(fc, ph, std::integral_constant<int, NPRE + S>{}, std::integral_constant<int, NPRE + S + 1>{});
-          if constexpr (S < OPS) copy(std::integral_constant<int, S>{}, k + R - 1, al, bl, sal, sbl, mal, mbl);
+          if constexpr (S < OPS) copy(std::integral_constant<int, S>{}, k + R - 1, al, bl, mal, mbl);
           constexpr int u0 = (NUNIT * S) / NS, u1 = (NUNIT * (S + 1)) / NS;
           if constexpr (u1 > u0) read_unit(std::integral_constant<int, u0>{}, fn, an, bn, man, mbn);
           if constexpr (u1 > u0 + 1) read_unit(std::integral_constant<int, u0 + 1>{}, fn, an, bn, man, mbn);
@@ -708,10 +535,9 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
       }(std::make_integer_sequence<int, NS>{});
       if constexpr (OPS > NS) {
         [&]<int... Cs>(std::integer_sequence<int, Cs...>) {
-          (copy(std::integral_constant<int, NS + Cs>{}, k + R - 1, al, bl, sal, sbl, mal, mbl), ...);
+          (copy(std::integral_constant<int, NS + Cs>{}, k + R - 1, al, bl, mal, mbl), ...);
         }(std::make_integer_sequence<int, OPS - NS>{});
       }
-      if constexpr (BLK) stash_factors(sac, sbc, k);
       pin_acc();
     };
     // step J of a ring turn starting at stage kt (a multiple of R): stage
@@ -719,58 +545,35 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
     // next stage's in buffer J + 1, and its copies go to buffer J - 1
     auto step_at = [&](auto j, int kt) __attribute__((always_inline)) {
       constexpr int J = decltype(j)::value;
-      constexpr int cur = J % R, nxt = (J + 1) % R, cpy = (J + R - 1) % R;
+      constexpr int nxt = (J + 1) % R, cpy = (J + R - 1) % R;
       // (the register sets are named, not selected: a selected reference
       // would put them in scratch memory)
       if constexpr (J % 2 == 0)
-        step(kt + J, F0, F1, sAr[cur], sBr[cur], As[nxt], Bs[nxt], mAr[nxt], mBr[nxt], As[cpy], Bs[cpy],
-             sAr[cpy], sBr[cpy], mAr[cpy], mBr[cpy], std::integral_constant<int, 0>{});
+        step(kt + J, F0, F1, As[nxt], Bs[nxt], mAr[nxt], mBr[nxt], As[cpy], Bs[cpy], mAr[cpy], mBr[cpy],
+             std::integral_constant<int, 0>{});
       else
-        step(kt + J, F1, F0, sAr[cur], sBr[cur], As[nxt], Bs[nxt], mAr[nxt], mBr[nxt], As[cpy], Bs[cpy],
-             sAr[cpy], sBr[cpy], mAr[cpy], mBr[cpy], std::integral_constant<int, 1>{});
+        step(kt + J, F1, F0, As[nxt], Bs[nxt], mAr[nxt], mBr[nxt], As[cpy], Bs[cpy], mAr[cpy], mBr[cpy],
+             std::integral_constant<int, 1>{});
     };
     if (vsteps > 0) {
       [&]<int... Js>(std::integer_sequence<int, Js...>) {
-        (load_stage(Js, As[Js], Bs[Js], sAr[Js], sBr[Js], mAr[Js], mBr[Js]), ...);
+        (load_stage(Js, As[Js], Bs[Js], mAr[Js], mBr[Js]), ...);
       }(std::make_integer_sequence<int, R - 1>{});
       sync_stage(WP{});
       read_frags(F0, As[0], Bs[0], mAr[0], mBr[0]);
     }
-    int kt = 0;
-    for (; kt + R <= vsteps; kt += R) {
+    for (int kt = 0; kt < vsteps; kt += R) {
       [&]<int... Js>(std::integer_sequence<int, Js...>) {
         (step_at(std::integral_constant<int, Js>{}, kt), ...);
       }(std::make_integer_sequence<int, R>{});
     }
-    // six buffers: the last vsteps - kt < R stages (an even count) run as
-    // the first steps of one more turn
-    if constexpr (R > 4) {
-      if (vsteps - kt >= 2) {
-        step_at(std::integral_constant<int, 0>{}, kt);
-        step_at(std::integral_constant<int, 1>{}, kt);
-      }
-      if (vsteps - kt >= 4) {
-        step_at(std::integral_constant<int, 2>{}, kt);
-        step_at(std::integral_constant<int, 3>{}, kt);
-      }
-    }
   }
   __builtin_amdgcn_sched_barrier(0);
-  // the epilogue's first LDS writes (blockwise: the last promotion) read the
-  // last MFMAs' results: keep >= 40 wait states between them
+  // the epilogue's first LDS writes read the last MFMAs' results: keep >= 40
+  // wait states between them
   asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" ::: "memory");
   wait_vm<0>();     // the copies of the stages past the contraction have landed
-  __syncthreads();  // every wave is done with the stage buffers (blockwise: sS / sSb written)
-  if constexpr (BLK) {
-    // the last block's partials
-    float f[16];
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      load_factors(mi, f);
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) promote_one(mi, ni, f);
-    }
-  }
+  __syncthreads();  // every wave is done with the stage buffers
 
   // ---- epilogue: each wave stages 16-row half slabs through its own LDS
   // region, then writes rows of 8 outputs with 16-byte stores. The scale
@@ -785,11 +588,7 @@ __global__ __launch_bounds__(64 * gemm_waves<RECIPE>()) void grouped_gemm_kernel
   constexpr int STR = WN + 8;          // LDS row stride in floats
   constexpr int CPR = WN / 8;          // 8-value chunks per row (bf16 outputs: 16 bytes)
   constexpr int CPL = 16 * CPR / 64;   // chunks per lane per half slab
-  // (eight waves: two slabs in each A stage buffer)
-  const int cw = NW == 4 ? wave : wave >> 1;
-  uint8_t *creg = As[cw] +
-                  (NW == 4 ? 0 : (wave & 1) * (GBM * GBK / 2));
-  float *cb = reinterpret_cast<float *>(creg);
+  float *cb = reinterpret_cast<float *>(As[wave]);  // this wave's staging region
   const int64_t jw = j0 + wj * WN;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
@@ -1665,15 +1464,15 @@ static hipError_t launch_cfg(const GemmArgs &a0, hipStream_t st) {
     blockwise_gemm_kernel<MODE, FA, FB, false><<<grid, 512, 0, st>>>(a);
     return hipGetLastError();
   } else {
-  // the accumulating instance exists for wgrad only
-  if constexpr (MODE == kWgrad) {
-    if (a.accumulate) {
-      grouped_gemm_kernel<MODE, RECIPE, FA, FB, BN, true><<<grid, 64 * gemm_waves<RECIPE>(), 0, st>>>(a);
-      return hipGetLastError();
+    // the accumulating instance exists for wgrad only
+    if constexpr (MODE == kWgrad) {
+      if (a.accumulate) {
+        grouped_gemm_kernel<MODE, RECIPE, FA, FB, BN, true><<<grid, 256, 0, st>>>(a);
+        return hipGetLastError();
+      }
     }
-  }
-  grouped_gemm_kernel<MODE, RECIPE, FA, FB, BN, false><<<grid, 64 * gemm_waves<RECIPE>(), 0, st>>>(a);
-  return hipGetLastError();
+    grouped_gemm_kernel<MODE, RECIPE, FA, FB, BN, false><<<grid, 256, 0, st>>>(a);
+    return hipGetLastError();
   }
 }
 
