@@ -686,18 +686,51 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
 // The LDS holds two blocks (four 64-byte stages of A and of B, 128 KB) and
 // the block loop is block-major: at a block's barrier its data has landed and
 // every wave is done with the block before, whose buffers then receive the
-// next block's copies (direct-to-LDS buffer loads, one block ahead). Each
-// wave walks its sub-tiles column by column (8 columns of 4 MFMAs), reading
-// the next column's B fragment while the current one runs; a sub-tile's
-// promotion is issued two MFMAs after its own, when its partial has certainly
-// been written. The last column of a block runs after the next block's
-// barrier, on fragments already in registers, while the new block's A
-// fragments arrive.
+// next block's copies (direct-to-LDS buffer loads, one block ahead, in five
+// pieces spread over the block's MFMAs). Each wave walks its sub-tiles column
+// by column (8 columns of 4 MFMAs), reading the next column's B fragment
+// while the current one runs; a sub-tile's promotion is issued two MFMAs
+// after its own, when its partial has certainly been written. The last
+// column of a block runs after the next block's barrier, on fragments
+// already in registers, while the new block's A fragments arrive.
+//
+// Tiles follow one another without a pause: the last block of a tile copies
+// the first block of the workgroup's next tile, and the finished tile's
+// totals leave straight from registers during the next tile's first block,
+// each sub-tile between its last promotion and the first promotion of the
+// new tile (so neither the copy latency of a tile's first block nor the
+// drain of its stores stalls the matrix cores). The accumulating wgrad
+// instance, which must read the old dW before it writes, ends each tile
+// with a staged read-add-write epilogue instead.
 __device__ __forceinline__ int64_t uni64(int64_t v) {
   const uint64_t u = (uint64_t)v;
   return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(u >> 32)) << 32) |
                    (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u));
 }
+__device__ __forceinline__ void bdma4(rsrc_t rs, uint32_t voff, uint32_t soff, void *lds) {
+  asm volatile("buffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rs), "s"(soff), "{m0}"(lds_addr(lds)));
+}
+__device__ __forceinline__ uint32_t clamp_u32(int64_t v) {
+  return v <= 0 ? 0u : (v >= (int64_t)0xFFFFFFFF ? 0xFFFFFFFFu : (uint32_t)v);
+}
+
+// One tile of the blockwise GEMM (all wave-uniform)
+struct BwTile {
+  int i0, ilo, ihi, j0;  // rows [i0, i0 + 256) (valid [ilo, ihi)), columns from j0
+  int l0;                // first contraction element (wgrad: the group's padded start)
+  int g, nblk, valid;
+};
+// A tile's copy sources: buffer resources sized to its valid rows (rows past
+// them read zeros), so the per-lane copy offsets are the same for every tile
+struct BwRes {
+  rsrc_t ra, rb;  // A and B codes from the tile's first row pair and contraction line
+  rsrc_t rs;      // the scales this wave copies: A rows (waves 0-3); waves 4-7: wgrad B columns,
+                  // FWD / DGRAD the weight scales of the tile's two 128-column blocks
+};
+// what the stores of a finished tile need
+struct BwOut {
+  int i0, ilo, ihi, j0, g, valid;
+};
 
 template <int MODE, int FA, int FB, bool ACC>
 __global__ __launch_bounds__(512) void blockwise_gemm_kernel(GemmArgs a) {
@@ -706,13 +739,16 @@ __global__ __launch_bounds__(512) void blockwise_gemm_kernel(GemmArgs a) {
   constexpr int WM = 64, WN = 128;  // wave tile: 4 waves along i, 2 along j
   constexpr int AQ = GBM / 16 / NW, BQ = BN / 16 / NW;  // 1 KB copy groups per wave and stage
   constexpr bool WG = MODE == kWgrad;
+  constexpr bool SEAMLESS = !ACC;  // stores overlap the next tile (see above)
   typedef float v4f __attribute__((ext_vector_type(4)));
 
-  __shared__ __attribute__((aligned(1024))) uint8_t As[4][GBM * GBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t Bs[4][BN * GBK];
+  // stage buffers: AB[0] = A, AB[1] = B, four 64-byte stages each (one
+  // array, so that a wave's staging region is plain address arithmetic)
+  __shared__ __attribute__((aligned(1024))) uint8_t AB[2][4][GBM * GBK];
+  uint8_t (*const As)[GBM * GBK] = AB[0];
+  uint8_t (*const Bs)[BN * GBK] = AB[1];
   __shared__ __attribute__((aligned(16))) float sAr[2][GBM];          // per-row A scales of a block
   __shared__ __attribute__((aligned(16))) float sBr[2][WG ? BN : 64];  // wgrad: per-column B scales
-  __shared__ float sbtab[WG ? 1 : 2 * SB_TAB];  // FWD / DGRAD: sB of the tile's two j-blocks, per block
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -720,7 +756,41 @@ __global__ __launch_bounds__(512) void blockwise_gemm_kernel(GemmArgs a) {
   const int wi = wave & 3, wj = wave >> 2;
   const int l16 = lane & 15, g4 = lane >> 4;
 
-  for (int vb = blockIdx.x; vb < a.nblocks; vb += gridDim.x) {
+  // ---- per-lane copy offsets. Copy group q of a wave is 8 row pairs (16
+  // rows of the stage tile): lane L takes tile row 16q' + L / 4 and lands at
+  // its LDS chunk L % 4, so it reads the global chunk the swizzle puts there.
+  uint32_t aoff[AQ], boff[BQ];
+#pragma unroll
+  for (int q = 0; q < AQ; ++q) {
+    const int row = (wave * AQ + q) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 2) & 3);
+    aoff[q] = (uint32_t)((row >> 1) * 2 * (int32_t)a.lda + (row & 1) * 64 + c * 16);
+  }
+#pragma unroll
+  for (int q = 0; q < BQ; ++q) {
+    const int row = (wave * BQ + q) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 2) & 3);
+    boff[q] = (uint32_t)((row >> 1) * 2 * (int32_t)a.ldb + (row & 1) * 64 + c * 16);
+  }
+  // scales copied with each block: waves 0-3 the A scales of tile rows
+  // 64w..64w+63; waves 4-7 (wgrad) the B scales of tile columns 64(w-4)..,
+  // (FWD / DGRAD) lanes 0 and 1 the weight scales of the tile's two
+  // 128-column blocks, into sBr[q][0..1] (the other lanes read past the
+  // resource: zeros)
+  const int64_t sa_row = WG ? a.lda : a.L;  // contraction elements per row of the scale matrices
+  const int64_t sb_row = WG ? a.ldb : a.L;
+  const uint32_t srow = (uint32_t)((wave < 4 ? sa_row : sb_row) / SBLK) * 4u;  // bytes per scale row
+  const bool wscale = !WG && wave >= 4;  // copies weight scales
+  const uint32_t svoff = wscale ? (uint32_t)lane * (uint32_t)a.sb_j * 4u : (uint32_t)((wave & 3) * 64 + lane) * srow;
+  const uint32_t vstep = wscale ? (uint32_t)a.sb_l * 4u : 0u, sstep = wscale ? 0u : 4u;  // per block
+  float *const sc_dst0 = wave < 4 ? &sAr[0][(wave & 3) * 64] : &sBr[0][WG ? (wave & 3) * 64 : 0];
+  float *const sc_dst1 = wave < 4 ? &sAr[1][(wave & 3) * 64] : &sBr[1][WG ? (wave & 3) * 64 : 0];
+  const rsrc_t rsZ = make_rsrc(kZeroSrc, 0u);
+
+  // ---- tile vb: coordinates and resources; false for an unused FWD / DGRAD
+  // slot (rows of a neighbouring group inside a tile are computed and not
+  // stored)
+  auto setup = [&](int vb, BwTile &T) -> bool {
     const int lid = xcd_remap<32>(vb, a.nblocks);
     int g = 0;
     int64_t i0 = 0, ilo = 0, ihi = 0, j0 = 0, l0 = 0;
@@ -744,7 +814,7 @@ __global__ __launch_bounds__(512) void blockwise_gemm_kernel(GemmArgs a) {
       int slot, jt;
       raster(lid, a.slots, a.jtiles, slot, jt);
       j0 = (int64_t)jt * BN;
-      if (!locate_row_tile(a, slot, g, i0, ilo, ihi)) continue;
+      if (!locate_row_tile(a, slot, g, i0, ilo, ihi)) return false;
       // (read from LDS: wave-uniform values the compiler would keep in VGPRs)
       g = __builtin_amdgcn_readfirstlane(g);
       i0 = uni64(i0);
@@ -752,125 +822,115 @@ __global__ __launch_bounds__(512) void blockwise_gemm_kernel(GemmArgs a) {
       ihi = uni64(ihi);
       nsteps = (int)(a.L / GBK);
     }
-    const int nblk = nsteps >> 1;  // 128-blocks of the contraction
-    const int64_t sa_row = WG ? a.lda : a.L;  // contraction elements per scale row
-    const int64_t sb_row = WG ? a.ldb : a.L;
-
-    // copy offsets: as in grouped_gemm_kernel (pairs past the last valid one
-    // re-read it)
+    T.g = g;
+    T.i0 = (int)i0;  // row and column indices fit in 32 bits (M < 2^31; K, N < 2^31)
+    T.ilo = (int)ilo;
+    T.ihi = (int)ihi;
+    T.j0 = (int)j0;
+    T.l0 = (int)l0;
+    T.nblk = nsteps >> 1;
+    T.valid = 1;
+    return true;
+  };
+  // the copy sources of tile T (zeros when T is not valid)
+  auto resources = [&](const BwTile &T) -> BwRes {
+    BwRes R;
+    R.ra = R.rb = R.rs = rsZ;
+    if (!T.valid) return R;
+    const int64_t i0 = T.i0, ihi = T.ihi, j0 = T.j0, l0 = T.l0;
     const int64_t lb = l0 / GBK;
-    const uint8_t *abase = a.a + (i0 >> 1) * 2 * a.lda + lb * 128;
-    const uint8_t *bbase = a.b + (WG ? 0 : (int64_t)g * a.b_gstride) + (j0 >> 1) * 2 * a.ldb + lb * 128;
-    const rsrc_t rsA = make_rsrc(abase, 0xFFFFFFFFu), rsB = make_rsrc(bbase, 0xFFFFFFFFu);
-    const rsrc_t rsZ = make_rsrc(kZeroSrc, 0u);
-    const int apmax = (int)(((ihi - 1) >> 1) - (i0 >> 1));
     const int64_t jlim = (a.J - j0) < BN ? (a.J - j0) : BN;
-    const int bpmax = (int)((jlim - 1) >> 1);
-    uint32_t aoff[AQ], boff[BQ];
-#pragma unroll
-    for (int q = 0; q < AQ; ++q) {
-      const int row = (wave * AQ + q) * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ ((row >> 2) & 3);
-      const int pr = (row >> 1) < apmax ? (row >> 1) : apmax;
-      aoff[q] = (uint32_t)(pr * 2 * (int32_t)a.lda + (row & 1) * 64 + c * 16);
-    }
-#pragma unroll
-    for (int q = 0; q < BQ; ++q) {
-      const int row = (wave * BQ + q) * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ ((row >> 2) & 3);
-      const int pr = (row >> 1) < bpmax ? (row >> 1) : bpmax;
-      boff[q] = (uint32_t)(pr * 2 * (int32_t)a.ldb + (row & 1) * 64 + c * 16);
-    }
-    // scale rows: waves 0-3 copy the A scales of tile rows 64w..64w+63 (rows
-    // clamped into the valid ones); wgrad: waves 4-7 the B scales of tile
-    // columns 64(w-4)..; the other waves copy zeros into sBr's spare slot
-    const float *zsrc4 = reinterpret_cast<const float *>(kZeroSrc) + lane;
-    const float *sc_src = zsrc4;
-    float *sc_dst0, *sc_dst1;
-    const bool has_sc = wave < 4 || WG;
-    {
-      const int r = (wave & 3) * 64 + lane;
-      if (wave < 4) {
-        const int64_t i = i0 + r;
-        const int64_t ic = i < ilo ? ilo : (i >= ihi ? ihi - 1 : i);
-        sc_src = reinterpret_cast<const float *>(a.a_scales) + ic * (sa_row / SBLK) + l0 / SBLK;
-        sc_dst0 = &sAr[0][(wave & 3) * 64];
-        sc_dst1 = &sAr[1][(wave & 3) * 64];
-      } else if (WG) {
-        const int64_t j = j0 + (r < jlim ? r : jlim - 1);
-        sc_src = reinterpret_cast<const float *>(a.b_scales) + j * (sb_row / SBLK) + l0 / SBLK;
-        sc_dst0 = &sBr[0][(wave & 3) * 64];
-        sc_dst1 = &sBr[1][(wave & 3) * 64];
-      } else {
-        sc_dst0 = &sBr[0][0];
-        sc_dst1 = &sBr[1][0];
-      }
-    }
-    if (!WG) {
-      // the weight scales of the tile's two j-blocks (the second clamped to
-      // the last one when the tile overhangs J)
-      const int64_t jb0 = j0 / SBLK, jbl = a.J / SBLK - 1;
-      for (int e = t; e < 2 * nblk; e += 64 * NW) {
-        const int h = e >= nblk, lbk = e - h * nblk;
-        const int64_t jb = jb0 + h < jbl ? jb0 + h : jbl;
-        sbtab[h * SB_TAB + lbk] =
-            reinterpret_cast<const float *>(a.b_scales)[(int64_t)g * a.bs_gstride + lbk * a.sb_l + jb * a.sb_j];
-      }
-    }
-
-    // copies of block bb into buffer pair q (stages 2q, 2q + 1); a block
-    // past the contraction copies zeros. Piece K: the A (K = 0, 2) or B
-    // (K = 1, 3) chunks of stage K / 2, or (K = 4) the scale row.
-    auto copy_piece = [&](int bb, int q, auto k_) __attribute__((always_inline)) {
-      constexpr int K = decltype(k_)::value;
-      const bool real = bb < nblk;
-      if constexpr (K < 4) {
-        constexpr int s = K / 2;
-        const uint32_t soff = (uint32_t)(2 * bb + s) * 128u;
-        if constexpr (K % 2 == 0) {
-          const rsrc_t ra = real ? rsA : rsZ;
-#pragma unroll
-          for (int c = 0; c < AQ; ++c) bdma16(ra, aoff[c], soff, &As[2 * q + s][(wave * AQ + c) * 1024]);
-        } else {
-          const rsrc_t rb = real ? rsB : rsZ;
-#pragma unroll
-          for (int c = 0; c < BQ; ++c) bdma16(rb, boff[c], soff, &Bs[2 * q + s][(wave * BQ + c) * 1024]);
+    const int64_t apairs = ((ihi - 1) >> 1) - (i0 >> 1) + 1, bpairs = ((jlim - 1) >> 1) + 1;
+    R.ra = make_rsrc(a.a + (i0 >> 1) * 2 * a.lda + lb * 128, clamp_u32(apairs * 2 * a.lda));
+    R.rb = make_rsrc(a.b + (WG ? 0 : (int64_t)T.g * a.b_gstride) + (j0 >> 1) * 2 * a.ldb + lb * 128,
+                     clamp_u32(bpairs * 2 * a.ldb));
+    if (wave < 4)
+      R.rs = make_rsrc(reinterpret_cast<const float *>(a.a_scales) + i0 * (sa_row / SBLK) + l0 / SBLK,
+                       clamp_u32((ihi - i0) * (int64_t)srow));
+    else if (WG)
+      R.rs = make_rsrc(reinterpret_cast<const float *>(a.b_scales) + j0 * (sb_row / SBLK) + l0 / SBLK,
+                       clamp_u32(jlim * (int64_t)srow));
+    else  // weight scales [E, blocks along l, blocks along j] from the tile's first j-block, to the
+          // end of expert g's array (block offsets ride in the lane offset)
+      R.rs = make_rsrc(reinterpret_cast<const float *>(a.b_scales) + (int64_t)T.g * a.bs_gstride +
+                           (j0 / SBLK) * a.sb_j,
+                       clamp_u32((a.bs_gstride - (j0 / SBLK) * a.sb_j) * 4));
+    return R;
+  };
+  // the workgroup's next tile from vb on with a contraction (vb advanced to
+  // it); an empty wgrad group's tiles get dW = 0 on the way (accumulating:
+  // left as they are)
+  auto next_tile = [&](int &vb, BwTile &T) {
+    T.valid = 0;
+    for (; vb < a.nblocks; vb += gridDim.x) {
+      if (!setup(vb, T)) continue;
+      if (T.nblk > 0) return;
+      if (WG && !ACC) {
+        for (int e = t; e < GBM * BN / 4; e += 64 * NW) {
+          const int64_t i = T.i0 + e / (BN / 4), j = T.j0 + (e % (BN / 4)) * 4;
+          if (i < T.ihi && j < a.J)
+            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.out) + ((int64_t)T.g * a.I + i) * a.ldo + j) =
+                make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         }
-      } else {
-        dma4(real && has_sc ? sc_src + bb : zsrc4, q ? sc_dst1 : sc_dst0);
       }
-    };
+      T.valid = 0;
+    }
+  };
 
-    // fragment of sub-tile row `row` for the whole block in pair q: chunk g4
-    // of the row in each of the block's two stages (the MFMA's k order is
-    // the same for both operands, so any fixed assignment of the 128 k to
-    // lanes contracts correctly)
-    auto frag_blk = [&](const uint8_t (*buf)[GBM * GBK], int q, int row) -> v8i {
-      const int o = swz(row, g4);
-      const uint4 x0 = *reinterpret_cast<const uint4 *>(&buf[2 * q][o]);
-      const uint4 x1 = *reinterpret_cast<const uint4 *>(&buf[2 * q + 1][o]);
-      return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-    };
-    auto fragA = [&](int q, int mi) { return frag_blk(As, q, wi * WM + mi * 16 + l16); };
-    auto fragB = [&](int q, int ni) { return frag_blk(Bs, q, wj * WN + ni * 16 + l16); };
-    // the four column scales of this lane in column ni of the wave tile (wgrad)
-    auto col_scales = [&](int q, int ni) -> v4f {
-      const float4 v = *reinterpret_cast<const float4 *>(&sBr[q][wj * WN + ni * 16 + 4 * g4]);
-      return v4f{v.x, v.y, v.z, v.w};
-    };
+  // copy piece K of block bb from sources R into buffer pair q (stages 2q,
+  // 2q+1): the A (K = 0, 2) or B (K = 1, 3) chunks of stage K / 2, or (K = 4)
+  // the scales
+  auto copy_piece = [&](const BwRes &R, int bb, int q, auto k_) __attribute__((always_inline)) {
+    constexpr int K = decltype(k_)::value;
+    if constexpr (K < 4) {
+      constexpr int s = K / 2;
+      const uint32_t soff = (uint32_t)(2 * bb + s) * 128u;
+      if constexpr (K % 2 == 0) {
+#pragma unroll
+        for (int c = 0; c < AQ; ++c) bdma16(R.ra, aoff[c], soff, &As[2 * q + s][(wave * AQ + c) * 1024]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < BQ; ++c) bdma16(R.rb, boff[c], soff, &Bs[2 * q + s][(wave * BQ + c) * 1024]);
+      }
+    } else {
+      // (the weight scales' block offset in the lane offset, the others' in
+      // the scalar offset: an in-range lane offset then always addresses
+      // memory inside the array)
+      bdma4(R.rs, svoff + (uint32_t)bb * vstep, (uint32_t)bb * sstep, q ? sc_dst1 : sc_dst0);
+    }
+  };
 
-    v4f acc[4][8];
+  // fragment of sub-tile row `row` for the whole block in pair q: chunk g4
+  // of the row in each of the block's two stages (the MFMA's k order is
+  // the same for both operands, so any fixed assignment of the 128 k to
+  // lanes contracts correctly)
+  auto frag_blk = [&](const uint8_t (*buf)[GBM * GBK], int q, int row) -> v8i {
+    const int o = swz(row, g4);
+    const uint4 x0 = *reinterpret_cast<const uint4 *>(&buf[2 * q][o]);
+    const uint4 x1 = *reinterpret_cast<const uint4 *>(&buf[2 * q + 1][o]);
+    return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+  };
+  auto fragA = [&](int q, int mi) { return frag_blk(As, q, wi * WM + mi * 16 + l16); };
+  auto fragB = [&](int q, int ni) { return frag_blk(Bs, q, wj * WN + ni * 16 + l16); };
+  // the four column scales of this lane in column ni of the wave tile (wgrad)
+  auto col_scales = [&](int q, int ni) -> v4f {
+    const float4 v = *reinterpret_cast<const float4 *>(&sBr[q][wj * WN + ni * 16 + 4 * g4]);
+    return v4f{v.x, v.y, v.z, v.w};
+  };
+
+  v4f acc[4][8];
+  // registers of the block schedule; zero before a tile's first block, whose
+  // leading "previous column" then adds exact zeros
+  v8i af[4], bfX, bfY;     // A fragments; B fragments of even / odd columns
+  v4f p[4];                // partials, by sub-tile row
+  float fo[4], fn[4];      // promotion factors per sub-tile row: previous block, this block
+  v4f sbX, sbY;            // wgrad: column scales of even / odd columns
+  float sbw = 1.0f;        // FWD / DGRAD: this block's weight scale for the wave's j-block
+  auto reset = [&]() {
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
       for (int ni = 0; ni < 8; ++ni) acc[mi][ni] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    // registers of the block schedule; zero before the first block, whose
-    // leading "previous column" then adds exact zeros
-    v8i af[4], bfX, bfY;     // A fragments; B fragments of even / odd columns
-    v4f p[4];                // partials, by sub-tile row
-    float fo[4], fn[4];      // promotion factors per sub-tile row: previous block, this block
-    v4f sbX, sbY;            // wgrad: column scales of even / odd columns
-    float sbw = 1.0f;        // FWD / DGRAD: this block's weight scale for the wave's j-block
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       af[m] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
@@ -882,183 +942,87 @@ __global__ __launch_bounds__(512) void blockwise_gemm_kernel(GemmArgs a) {
     bfY = af[0];
     sbX = p[0];
     sbY = p[0];
+  };
+  reset();
 
-    auto mma = [&](const v8i &bfr, const v8i &afr) -> v4f {
-      const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr, afr, z, FB, FA, 0, kUnitScale, 0, kUnitScale);
-    };
-    auto promote = [&](v4f &c, const v4f &pp, float f, const v4f &sb) __attribute__((always_inline)) {
-      if constexpr (WG) {
+  auto mma = [&](const v8i &bfr, const v8i &afr) -> v4f {
+    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr, afr, z, FB, FA, 0, kUnitScale, 0, kUnitScale);
+  };
+  auto promote = [&](v4f &c, const v4f &pp, float f, const v4f &sb) __attribute__((always_inline)) {
+    if constexpr (WG) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) c[v] += (pp[v] * sb[v]) * f;
-      } else {
+      for (int v = 0; v < 4; ++v) c[v] += (pp[v] * sb[v]) * f;
+    } else {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) c[v] += pp[v] * f;
-      }
-    };
-
-    // Event E (0..31) of a block iteration: events 0-3 are column 7 of the
-    // previous block (sub-tile rows 0-3), events 4 + 4n + m column n < 7 of
-    // this block, row m. After its MFMA, the event promotes the sub-tile of
-    // event E - 2 and issues reads whose target registers are free by then.
-    auto event = [&](auto e_, int q, auto read_) __attribute__((always_inline)) {
-      constexpr int E = decltype(e_)::value;
-      constexpr bool READ = decltype(read_)::value;  // false: the column after the last block
-      constexpr int N = E < 4 ? 7 : (E - 4) / 4;  // column
-      constexpr int M = E < 4 ? E : (E - 4) % 4;  // sub-tile row
-      if constexpr (N % 2 == 0)
-        p[M] = mma(bfX, af[M]);
-      else
-        p[M] = mma(bfY, af[M]);
-      // next column's B fragment, into the register set of column N - 1
-      // (last read by the previous event's MFMA)
-      if constexpr (E >= 4 && M == 0) {
-        if constexpr ((N + 1) % 2 == 0)
-          bfX = fragB(q, N + 1);
-        else
-          bfY = fragB(q, N + 1);
-      }
-      // promotion of event E - 2
-      if constexpr (E < 2) {
-        promote(acc[2 + E][6], p[2 + E], fo[2 + E], sbX);
-      } else if constexpr (E < 6) {
-        promote(acc[E - 2][7], p[E - 2], fo[E - 2], sbY);
-      } else {
-        constexpr int PN = (E - 6) / 4, PM = (E - 6) % 4;
-        if constexpr (PN % 2 == 0)
-          promote(acc[PM][PN], p[PM], fn[PM], sbX);
-        else
-          promote(acc[PM][PN], p[PM], fn[PM], sbY);
-      }
-      // this block's A fragment of row M, once the previous block's is used
-      if constexpr (E < 4 && READ) af[E] = fragA(q, E);
-      // wgrad: the next column's scales, into the set of column N - 1 (whose
-      // last promotion was just issued)
-      if constexpr (WG && E >= 4 && M == 1) {
-        if constexpr ((N + 1) % 2 == 0)
-          sbX = col_scales(q, N + 1);
-        else
-          sbY = col_scales(q, N + 1);
-      }
-      if constexpr (WG && E == 1 && READ) sbX = col_scales(q, 0);
-      if constexpr (!WG && E == 5) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) fn[m] *= sbw;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    };
-
-    if (nblk > 0) {
-      copy_piece(0, 0, std::integral_constant<int, 0>{});
-      copy_piece(0, 0, std::integral_constant<int, 1>{});
-      copy_piece(0, 0, std::integral_constant<int, 2>{});
-      copy_piece(0, 0, std::integral_constant<int, 3>{});
-      copy_piece(0, 0, std::integral_constant<int, 4>{});
+      for (int v = 0; v < 4; ++v) c[v] += pp[v] * f;
     }
-    for (int b = 0; b < nblk; ++b) {
-      const int q = b & 1;
-      // block b has landed (every wave waits for its own copies, then the
-      // barrier), and every wave is done reading block b - 1's buffers
-      __builtin_amdgcn_sched_barrier(0);
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      bfX = fragB(q, 0);
-      // this block's factors: read now, multiplied at event 5 (first used
-      // at event 6), so that no early MFMA waits for these reads
-      sbw = WG ? 1.0f : sbtab[wj * SB_TAB + b];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) fn[m] = sAr[q][wi * WM + m * 16 + l16];
-      __builtin_amdgcn_sched_barrier(0);
-      // the next block's copies go out in five pieces, after events 1, 5,
-      // 9, 13 and 17: spread over the MFMAs, they ran 7-10% faster than as
-      // one burst after event 1
-      [&]<int... Es>(std::integer_sequence<int, Es...>) {
-        ([&] {
-          event(std::integral_constant<int, Es>{}, q, std::true_type{});
-          if constexpr (Es % 4 == 1 && Es / 4 < 5) {
-            copy_piece(b + 1, q ^ 1, std::integral_constant<int, Es / 4>{});
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }(), ...);
-      }(std::make_integer_sequence<int, 32>{});
-#pragma unroll
-      for (int m = 0; m < 4; ++m) fo[m] = fn[m];
-    }
-    // column 7 of the last block, then its last promotions
-    event(std::integral_constant<int, 0>{}, 0, std::false_type{});
-    event(std::integral_constant<int, 1>{}, 0, std::false_type{});
-    event(std::integral_constant<int, 2>{}, 0, std::false_type{});
-    event(std::integral_constant<int, 3>{}, 0, std::false_type{});
-    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    promote(acc[2][7], p[2], fo[2], sbY);
-    promote(acc[3][7], p[3], fo[3], sbY);
-    wait_vm<0>();
-    __syncthreads();  // every wave is done with the stage buffers
+  };
 
-    if (ACC && nsteps == 0) continue;  // empty group: dW_g unchanged
-    // ---- epilogue: each wave stages 16-row slabs (one sub-tile row) in its
-    // own 16 KB of the stage buffers, then writes rows with 16-byte stores
-    constexpr int STR = WN + 4;  // LDS row stride in floats (16-byte rows land on distinct banks)
-    float *cb = reinterpret_cast<float *>(wave < 4 ? As[wave] : Bs[wave - 4]);
-    const int64_t jw = j0 + wj * WN;
-    // the lane index, opaque to the compiler here: otherwise it computes
-    // every store address before the main loop and spills them, and each
-    // reload from scratch then waits for all earlier stores (vmcnt(0))
-    int lane_e = lane;
-    asm volatile("" : "+v"(lane_e));
+  // A finished tile's totals leave in 16-row slabs (one sub-tile row at a
+  // time) staged in this wave's own 8 KB of buffer pair q1: its copy
+  // destinations there (2 KB in each of the pair's four stage buffers), so no
+  // other wave touches them and the wave's own next copies into the pair come
+  // after its last read. Slab row r lives in stage buffer r / 4 (A0, B0, A1,
+  // B1) at 512 (r % 4), its 16-byte column chunk c at c ^ r (the 16 lanes of
+  // a write, one row each, and of a row read land on distinct banks). Rows
+  // then leave as 16-byte chunks (bf16: 8 columns, rounded to nearest even;
+  // fp32 dW: 4), and the totals are zeroed for the next tile.
+  auto store_tile = [&](const BwOut &P, int q1) __attribute__((always_inline)) {
+    uint8_t *const region = &AB[0][2 * q1][wave * 2048];
+    // the lane index opaque here, so that the addresses are computed now
+    // rather than before the main loop
+    int ll = lane;
+    asm volatile("" : "+v"(ll));
+    const int rl = ll & 15, cg = ll >> 4;
+    const bool jok = (int64_t)P.j0 + wj * WN < a.J;  // J % 128 == 0: the wave's 128 columns are all in or all out
+    auto row_base = [&](int r) -> uint8_t * {
+      // stage buffer r / 4: A0, B0, A1, B1 of the pair
+      return region + ((r >> 2) & 1) * (4 * GBM * GBK) + (r >> 3) * (GBM * GBK) + (r & 3) * 512;
+    };
+    uint8_t *const wrow = row_base(rl);
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
+    for (int m = 0; m < 4; ++m) {
 #pragma unroll
-      for (int ni = 0; ni < 8; ++ni)
-        *reinterpret_cast<float4 *>(&cb[l16 * STR + ni * 16 + 4 * g4]) =
-            make_float4(acc[mi][ni][0], acc[mi][ni][1], acc[mi][ni][2], acc[mi][ni][3]);
+      for (int n = 0; n < 8; ++n) {
+        *reinterpret_cast<float4 *>(wrow + (((n * 4 + cg) ^ rl) << 4)) =
+            make_float4(acc[m][n][0], acc[m][n][1], acc[m][n][2], acc[m][n][3]);
+        acc[m][n] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      }
       __builtin_amdgcn_wave_barrier();
-      const int64_t ib = i0 + wi * WM + mi * 16;
+      asm volatile("" ::: "memory");
+      const int64_t ib = (int64_t)P.i0 + wi * WM + m * 16;
+      const int64_t jw = (int64_t)P.j0 + wj * WN;
       if constexpr (WG) {
-        constexpr int CPR4 = WN / 4;  // float4 chunks per row
-        constexpr int CPL4 = 16 * CPR4 / 64;
-        float4 old[ACC ? CPL4 : 1];
-        if constexpr (ACC) {
 #pragma unroll
-          for (int k = 0; k < CPL4; ++k) {
-            const int id = k * 64 + lane_e;
-            const int64_t i = ib + id / CPR4, j = jw + (id % CPR4) * 4;
-            old[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            if (i >= ilo && i < ihi && j < a.J)
-              old[k] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.out) +
-                                                         ((int64_t)g * a.I + i) * a.ldo + j);
-          }
-        }
-#pragma unroll
-        for (int k = 0; k < CPL4; ++k) {
-          const int id = k * 64 + lane_e;
-          const int r = id / CPR4, c4 = id % CPR4;
-          const int64_t i = ib + r, j = jw + c4 * 4;
-          float4 y = *reinterpret_cast<const float4 *>(&cb[r * STR + c4 * 4]);
-          if (i >= ilo && i < ihi && j < a.J) {  // J % 128 == 0: a chunk is all in or all out
-            if constexpr (ACC) y = make_float4(y.x + old[k].x, y.y + old[k].y, y.z + old[k].z, y.w + old[k].w);
-            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.out) + ((int64_t)g * a.I + i) * a.ldo + j) = y;
-          }
+        for (int k = 0; k < 8; ++k) {
+          const int id = k * 64 + ll, r = id >> 5, c = id & 31;
+          const float4 y = *reinterpret_cast<const float4 *>(row_base(r) + ((c ^ r) << 4));
+          const int64_t i = ib + r;
+          if (jok && i >= P.ilo && i < P.ihi)
+            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.out) + ((int64_t)P.g * a.I + i) * a.ldo + jw +
+                                        c * 4) = y;
         }
       } else {
-        constexpr int CPR = WN / 8;  // 8-value (16-byte bf16) chunks per row
-        constexpr int CPL = 16 * CPR / 64;
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) {
-          const int id = k * 64 + lane_e;
-          const int r = id / CPR, c8 = id % CPR;
-          const int64_t i = ib + r, j = jw + c8 * 8;
-          const float4 x0 = *reinterpret_cast<const float4 *>(&cb[r * STR + c8 * 8]);
-          const float4 x1 = *reinterpret_cast<const float4 *>(&cb[r * STR + c8 * 8 + 4]);
-          if (i >= ilo && i < ihi && j < a.J) {
+        for (int k = 0; k < 4; ++k) {
+          const int id = k * 64 + ll, r = id >> 4, c8 = id & 15;
+          const float4 x0 = *reinterpret_cast<const float4 *>(row_base(r) + (((2 * c8) ^ r) << 4));
+          const float4 x1 = *reinterpret_cast<const float4 *>(row_base(r) + (((2 * c8 + 1) ^ r) << 4));
+          const int64_t i = ib + r;
+          if (jok && i >= P.ilo && i < P.ihi) {
+            typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+            typedef float f2 __attribute__((ext_vector_type(2)));
+            const bf2 b0 = __builtin_convertvector((f2{x0.x, x0.y}), bf2);  // round to nearest even
+            const bf2 b1 = __builtin_convertvector((f2{x0.z, x0.w}), bf2);
+            const bf2 b2 = __builtin_convertvector((f2{x1.x, x1.y}), bf2);
+            const bf2 b3 = __builtin_convertvector((f2{x1.z, x1.w}), bf2);
             uint4 o;
-            o.x = f32_to_bf16_bits(x0.x) | (f32_to_bf16_bits(x0.y) << 16);
-            o.y = f32_to_bf16_bits(x0.z) | (f32_to_bf16_bits(x0.w) << 16);
-            o.z = f32_to_bf16_bits(x1.x) | (f32_to_bf16_bits(x1.y) << 16);
-            o.w = f32_to_bf16_bits(x1.z) | (f32_to_bf16_bits(x1.w) << 16);
-            uint16_t *dst = reinterpret_cast<uint16_t *>(a.out) + i * a.ldo + j;
+            __builtin_memcpy(&o.x, &b0, 4);
+            __builtin_memcpy(&o.y, &b1, 4);
+            __builtin_memcpy(&o.z, &b2, 4);
+            __builtin_memcpy(&o.w, &b3, 4);
+            uint16_t *dst = reinterpret_cast<uint16_t *>(a.out) + i * a.ldo + jw + c8 * 8;
             if (a.stream_out)
               store16_stream(dst, o);
             else
@@ -1067,11 +1031,225 @@ __global__ __launch_bounds__(512) void blockwise_gemm_kernel(GemmArgs a) {
         }
       }
       __builtin_amdgcn_wave_barrier();
+      asm volatile("" ::: "memory");
+    }
+  };
+
+  // Event E (0..31) of a block iteration: events 0-3 are column 7 of the
+  // previous block (sub-tile rows 0-3), events 4 + 4n + m column n < 7 of
+  // this block, row m. After its MFMA, the event promotes the sub-tile of
+  // event E - 2 and issues reads whose target registers are free by then.
+  // In a tile's first block (FIRST) the previous block's column is not this
+  // tile's: events 0-5 run no MFMA and no promotion of it.
+  auto event = [&](auto e_, int q, auto read_, auto first_) __attribute__((always_inline)) {
+    constexpr int E = decltype(e_)::value;
+    constexpr bool READ = decltype(read_)::value;  // false: the column after a tile's last block
+    constexpr bool FIRST = decltype(first_)::value;
+    constexpr int N = E < 4 ? 7 : (E - 4) / 4;  // column
+    constexpr int M = E < 4 ? E : (E - 4) % 4;  // sub-tile row
+    if constexpr (FIRST && E < 4) {
+    } else if constexpr (N % 2 == 0)
+      p[M] = mma(bfX, af[M]);
+    else
+      p[M] = mma(bfY, af[M]);
+    // (kept first: the promotion below reads the partial of two MFMAs ago,
+    // which is written by the time this MFMA issues; issued before it, the
+    // read could come one MFMA after the write and see a stale value)
+    __builtin_amdgcn_sched_barrier(0);
+    // next column's B fragment, into the register set of column N - 1
+    // (last read by the previous event's MFMA)
+    if constexpr (E >= 4 && M == 0) {
+      if constexpr ((N + 1) % 2 == 0)
+        bfX = fragB(q, N + 1);
+      else
+        bfY = fragB(q, N + 1);
+    }
+    // promotion of event E - 2
+    if constexpr (FIRST && E < 6) {
+    } else if constexpr (E < 2) {
+      promote(acc[2 + E][6], p[2 + E], fo[2 + E], sbX);
+    } else if constexpr (E < 6) {
+      promote(acc[E - 2][7], p[E - 2], fo[E - 2], sbY);
+    } else {
+      constexpr int PN = (E - 6) / 4, PM = (E - 6) % 4;
+      if constexpr (PN % 2 == 0)
+        promote(acc[PM][PN], p[PM], fn[PM], sbX);
+      else
+        promote(acc[PM][PN], p[PM], fn[PM], sbY);
+    }
+    // this block's A fragment of row M, once the previous block's is used
+    if constexpr (E < 4 && READ) af[E] = fragA(q, E);
+    // wgrad: the next column's scales, into the set of column N - 1 (whose
+    // last promotion was just issued)
+    if constexpr (WG && E >= 4 && M == 1) {
+      if constexpr ((N + 1) % 2 == 0)
+        sbX = col_scales(q, N + 1);
+      else
+        sbY = col_scales(q, N + 1);
+    }
+    if constexpr (WG && E == 1 && READ) sbX = col_scales(q, 0);
+    if constexpr (!WG && E == 5) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) fn[m] *= sbw;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // a block in buffer pair q; the next block's copies (block nbb from
+  // sources R) go to pair q ^ 1
+  auto run_block = [&](int q, const BwRes &R, int nbb, auto first_) __attribute__((always_inline)) {
+    bfX = fragB(q, 0);
+    // this block's factors: read now, multiplied at event 5 (first used at
+    // event 6), so that no early MFMA waits for these reads
+    if constexpr (!WG) sbw = sBr[q][wj];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) fn[m] = sAr[q][wi * WM + m * 16 + l16];
+    __builtin_amdgcn_sched_barrier(0);
+    // the next block's copies go out in five pieces, after events 1, 5, 9,
+    // 13 and 17: spread over the MFMAs, they ran 7-10% faster than as one
+    // burst after event 1
+    [&]<int... Es>(std::integer_sequence<int, Es...>) {
+      ([&] {
+        event(std::integral_constant<int, Es>{}, q, std::true_type{}, first_);
+        if constexpr (Es % 4 == 1 && Es / 4 < 5) {
+          copy_piece(R, nbb, q ^ 1, std::integral_constant<int, Es / 4>{});
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }(), ...);
+    }(std::make_integer_sequence<int, 32>{});
+#pragma unroll
+    for (int m = 0; m < 4; ++m) fo[m] = fn[m];
+  };
+  // block b has landed (every wave waits for its own copies, then the
+  // barrier), and every wave is done reading the block before's buffers
+  auto block_sync = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // column 7 of a tile's last block and its last promotions
+  auto finish_tile = [&]() __attribute__((always_inline)) {
+    event(std::integral_constant<int, 0>{}, 0, std::false_type{}, std::false_type{});
+    event(std::integral_constant<int, 1>{}, 0, std::false_type{}, std::false_type{});
+    event(std::integral_constant<int, 2>{}, 0, std::false_type{}, std::false_type{});
+    event(std::integral_constant<int, 3>{}, 0, std::false_type{}, std::false_type{});
+    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    promote(acc[2][7], p[2], fo[2], sbY);
+    promote(acc[3][7], p[3], fo[3], sbY);
+  };
+
+  int vb = blockIdx.x;
+  BwTile T, N;
+  BwOut P;
+  next_tile(vb, T);
+  P.valid = 0;
+  int gb = 0;  // blocks run by the workgroup: block gb lives in buffer pair gb & 1
+  // the sources of the next copies: this tile's, from the start of its last
+  // block the next tile's
+  BwRes R = resources(T);
+  if (T.valid) {
+    copy_piece(R, 0, 0, std::integral_constant<int, 0>{});
+    copy_piece(R, 0, 0, std::integral_constant<int, 1>{});
+    copy_piece(R, 0, 0, std::integral_constant<int, 2>{});
+    copy_piece(R, 0, 0, std::integral_constant<int, 3>{});
+    copy_piece(R, 0, 0, std::integral_constant<int, 4>{});
+  }
+  while (T.valid) {
+    // first block: also finds the next tile and (seamless) writes the
+    // previous tile's totals, whose stores then drain under this block's
+    // MFMAs (the next block's wait covers them)
+    block_sync();
+    N.valid = 0;
+    if constexpr (SEAMLESS) {
+      vb += gridDim.x;
+      next_tile(vb, N);
+      if (P.valid) store_tile(P, (gb & 1) ^ 1);  // in the previous block's buffer pair
+    }
+    if (T.nblk == 1) R = resources(N);
+    run_block(gb & 1, R, T.nblk > 1 ? 1 : 0, std::true_type{});
+    ++gb;
+    for (int b = 1; b < T.nblk; ++b) {
+      block_sync();
+      if (b + 1 == T.nblk) R = resources(N);
+      run_block(gb & 1, R, b + 1 < T.nblk ? b + 1 : 0, std::false_type{});
+      ++gb;
+    }
+    finish_tile();  // on registers: overlaps the next barrier's wait
+    if constexpr (SEAMLESS) {
+      P = BwOut{T.i0, T.ilo, T.ihi, T.j0, T.g, 1};
+      T = N;
+      continue;
+    }
+    // ---- accumulating wgrad: dW += C through 16-row slabs staged in each
+    // wave's own 16 KB of the stage buffers
+    wait_vm<0>();
+    __syncthreads();  // every wave is done with the stage buffers
+    {
+      constexpr int STR = WN + 4;  // LDS row stride in floats (16-byte rows land on distinct banks)
+      float *cb = reinterpret_cast<float *>(wave < 4 ? As[wave] : Bs[wave - 4]);
+      const int64_t jw = T.j0 + wj * WN;
+      // the lane index, opaque to the compiler here: otherwise it computes
+      // every address before the main loop and spills them, and each reload
+      // from scratch then waits for all earlier stores (vmcnt(0))
+      int lane_e = lane;
+      asm volatile("" : "+v"(lane_e));
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+        for (int ni = 0; ni < 8; ++ni)
+          *reinterpret_cast<float4 *>(&cb[l16 * STR + ni * 16 + 4 * g4]) =
+              make_float4(acc[mi][ni][0], acc[mi][ni][1], acc[mi][ni][2], acc[mi][ni][3]);
+        __builtin_amdgcn_wave_barrier();
+        const int64_t ib = T.i0 + wi * WM + mi * 16;
+        constexpr int CPR4 = WN / 4;  // float4 chunks per row
+        constexpr int CPL4 = 16 * CPR4 / 64;
+        float4 old[CPL4];
+#pragma unroll
+        for (int k = 0; k < CPL4; ++k) {
+          const int id = k * 64 + lane_e;
+          const int64_t i = ib + id / CPR4, j = jw + (id % CPR4) * 4;
+          old[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+          if (i >= T.ilo && i < T.ihi && j < a.J)
+            old[k] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.out) +
+                                                       ((int64_t)T.g * a.I + i) * a.ldo + j);
+        }
+#pragma unroll
+        for (int k = 0; k < CPL4; ++k) {
+          const int id = k * 64 + lane_e;
+          const int r = id / CPR4, c4 = id % CPR4;
+          const int64_t i = ib + r, j = jw + c4 * 4;
+          const float4 y = *reinterpret_cast<const float4 *>(&cb[r * STR + c4 * 4]);
+          if (i >= T.ilo && i < T.ihi && j < a.J)  // J % 128 == 0: a chunk is all in or all out
+            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.out) + ((int64_t)T.g * a.I + i) * a.ldo + j) =
+                make_float4(y.x + old[k].x, y.y + old[k].y, y.z + old[k].z, y.w + old[k].w);
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
     }
     __syncthreads();  // the staging buffers are free before the next tile's copies land
+    reset();
+    vb += gridDim.x;
+    next_tile(vb, N);
+    T = N;
+    R = resources(T);
+    if (T.valid) {
+      copy_piece(R, 0, gb & 1, std::integral_constant<int, 0>{});
+      copy_piece(R, 0, gb & 1, std::integral_constant<int, 1>{});
+      copy_piece(R, 0, gb & 1, std::integral_constant<int, 2>{});
+      copy_piece(R, 0, gb & 1, std::integral_constant<int, 3>{});
+      copy_piece(R, 0, gb & 1, std::integral_constant<int, 4>{});
+    }
   }
+  if constexpr (SEAMLESS) {
+    if (P.valid) {  // the workgroup's last tile, once every wave is done with the last block's buffers
+      block_sync();
+      store_tile(P, (gb & 1) ^ 1);
+    }
+  }
+  wait_vm<0>();  // no copy into LDS is still in flight when the workgroup ends
 }
-
 
 // ---------------------------------------------------------------------------
 // NVFP4 grouped GEMM: e2m1 codes with an e4m3 scale per 16 contraction

@@ -342,6 +342,10 @@ mxsg_status mxsg_grouped_mm_check(int32_t mode, int32_t recipe, int32_t fmt_a, i
     REQUIRE(recipe != MXSG_RECIPE_BLOCKWISE || L <= 65536, MXSG_UNSUPPORTED,
             "grouped_mm: blockwise contraction %lld > 65536 is not built", (long long)L);
   }
+  // the blockwise kernel keeps row and column indices in 32 bits
+  REQUIRE(recipe != MXSG_RECIPE_BLOCKWISE || (K < ((int64_t)1 << 31) && N < ((int64_t)1 << 31)),
+          MXSG_UNSUPPORTED, "grouped_mm: blockwise K=%lld N=%lld must be below 2^31", (long long)K,
+          (long long)N);
   g_err[0] = 0;
   return MXSG_OK;
 }
