@@ -333,3 +333,28 @@ def test_batched_3d_operand(recipe, mode):
     bad = np.flatnonzero(got.reshape(-1) != ref.reshape(-1))
     assert bad.size == 0, f"{bad.size} mismatches; first {np.unravel_index(bad[0], got.shape)}: " \
                           f"got {got.reshape(-1)[bad[0]]} want {ref.reshape(-1)[bad[0]]}"
+
+
+@pytest.mark.parametrize("mode,accumulate", [(0, False), (1, False), (2, False), (2, True)],
+                         ids=["fwd", "dgrad", "wgrad", "wgrad-accumulate"])
+def test_blockwise_back_to_back_tiles(mode, accumulate):
+    """More tiles than workgroups, so each workgroup runs several tiles back
+    to back (the next tile's first block copied during the previous tile's
+    last, the previous tile's results written during the next tile's first
+    block): 200 groups of 0-400 rows (empty, one-row and ragged ones), a
+    half-empty last column tile (N or K = 384), exact integer operands."""
+    rng = np.random.default_rng(130 + mode)
+    sizes = [int(v) for v in rng.integers(0, 401, size=200)]
+    sizes[3] = 0
+    sizes[7] = 1
+    c = make_case(mode, "block", 0, 0, sizes, 256, 384, seed=131 + mode)
+    print(f"gemm blockwise back-to-back mode={mode} acc={accumulate} M={c.M}", flush=True)
+    if accumulate:
+        init = rng.integers(-64, 65, size=(c.E, c.K, c.N)).astype(np.float32)
+        got = host(run_case(c, out=to_dev(init.copy()), accumulate=True)).astype(np.float64)
+        want = c.ref + init.astype(np.float64)   # integers below 2^24: exact
+    else:
+        got, want = result_f64(c, run_case(c)), c.ref
+    bad = np.flatnonzero(got.reshape(-1) != want.reshape(-1))
+    assert bad.size == 0, f"{bad.size} mismatches; first {np.unravel_index(bad[0], got.shape)}: " \
+                          f"got {got.reshape(-1)[bad[0]]} want {want.reshape(-1)[bad[0]]}"
