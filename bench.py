@@ -374,11 +374,11 @@ def percentiles(v):
 
 
 def cpu_baseline(cid, rows, cols):
-    """The CPU oracle on a bounded sample of the same workload: one expert,
-    `rows` routed rows, the full K and the first `cols` output columns of the
-    gate/up GEMM; quantization
-    of the sampled operands plus the forward (and dgrad, wgrad) float64
-    GEMMs. Reported in TFLOP/s of the sampled GEMMs."""
+    """The CPU oracle on a bounded sample of the same workload: the first
+    expert that has routed rows, at most `rows` of them, the full K and the
+    first `cols` output columns of the gate/up GEMM; quantization of the
+    sampled operands plus the forward (and dgrad, wgrad) float64 GEMMs.
+    Reported in TFLOP/s of the sampled GEMMs."""
     import numpy as np
     from oracle import quant as OQ, gemm as OG, formats as OF
     from mx_scaled_grouped_amd import workloads as W
@@ -392,7 +392,10 @@ def cpu_baseline(cid, rows, cols):
     topk = W.routing_for(cid)
     K, N = spec.gemm_shape("gu")
     N = min(N, cols)
-    m = min(rows, int(OR.route(topk.expert_ids, topk.n_experts)["group_ends"][0]))
+    ends = OR.route(topk.expert_ids, topk.n_experts)["group_ends"].astype(np.int64)
+    sizes = np.diff(np.concatenate([[0], ends]))
+    e = int(np.flatnonzero(sizes)[0])          # the first expert with routed rows
+    m = min(rows, int(sizes[e]))
     rec = {"tw": "tw", "dl": "dl", "block": "block", "mx": "mx", "mxfp4": "mx", "nvfp4": "nvfp4"}[spec.recipe]
     fq = OF.E2M1 if spec.recipe in ("mxfp4", "nvfp4") else OF.E4M3     # activations and weights
 
@@ -424,7 +427,7 @@ def cpu_baseline(cid, rows, cols):
     mode = "fwd+dgrad+wgrad" if bwd else "fwd"
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "cpu_model": cpu_model(),
-            "sample": f"expert 0 gate/up GEMM, {m} routed rows x K={K} x N={N}, {mode}, "
+            "sample": f"expert {e} gate/up GEMM, {m} routed rows x K={K} x N={N}, {mode}, "
                       f"oracle quantization + float64 GEMMs, {dt:.1f} s"}
 
 
