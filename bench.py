@@ -373,12 +373,14 @@ def percentiles(v):
     return [round(float(x), 4) for x in np.percentile(np.asarray(v, dtype=np.float64), [10, 50, 90])]
 
 
-def cpu_baseline(cid, rows, cols):
-    """The CPU oracle on a bounded sample of the same workload: the first
-    expert that has routed rows, at most `rows` of them, the full K and the
-    first `cols` output columns of the gate/up GEMM; quantization of the
-    sampled operands plus the forward (and dgrad, wgrad) float64 GEMMs.
-    Reported in TFLOP/s of the sampled GEMMs."""
+def cpu_baseline(cid, rows, cols, min_seconds=8.0):
+    """The CPU oracle on a bounded sample of the same workload: the gate/up
+    GEMM of the first experts that have routed rows, at most `rows` of each
+    expert's rows, the full K and the first `cols` output columns, expert
+    after expert until `min_seconds` of oracle work have been timed (one
+    expert of the large configurations takes longer than that); quantization
+    of the sampled operands plus the forward (and dgrad, wgrad) float64
+    GEMMs. Reported in TFLOP/s of the sampled GEMMs."""
     import numpy as np
     from oracle import quant as OQ, gemm as OG, formats as OF
     from mx_scaled_grouped_amd import workloads as W
@@ -394,40 +396,52 @@ def cpu_baseline(cid, rows, cols):
     N = min(N, cols)
     ends = OR.route(topk.expert_ids, topk.n_experts)["group_ends"].astype(np.int64)
     sizes = np.diff(np.concatenate([[0], ends]))
-    e = int(np.flatnonzero(sizes)[0])          # the first expert with routed rows
-    m = min(rows, int(sizes[e]))
+    experts = [int(e) for e in np.flatnonzero(sizes)]
     rec = {"tw": "tw", "dl": "dl", "block": "block", "mx": "mx", "mxfp4": "mx", "nvfp4": "nvfp4"}[spec.recipe]
     fq = OF.E2M1 if spec.recipe in ("mxfp4", "nvfp4") else OF.E4M3     # activations and weights
-
-    def sc(q, key):
-        return (q[key], q["tensor_scale"]) if rec == "nvfp4" else q[key]
-    a = W.normal_bf16(cid, W.T_X, (m, K))
-    w = W.normal_bf16(cid, W.T_W1, (1, K, N), std=0.02, chunk_rows=256)
-    ge = np.array([m], np.int32)
     bwd = "dgrad" in spec.modes
     fg = OF.E5M2 if rec == "dl" else fq
     dl = (np.float32(1.0), np.float32(1.0))
-    t0 = time.perf_counter()
-    qa = OQ.quantize_act(a, rec, fq, ge, rowwise=True, colwise=bwd, dl_scale=dl)
-    qw = OQ.quantize_weight(w, rec, fq, dl_scale=(np.ones(1, np.float32), np.ones(1, np.float32)))
-    A = OG.deq_act_rows(qa["row_codes"], sc(qa, "row_scales"), rec, fq)
-    Y = OG.round_bf16(OG.grouped_fwd(A, OG.deq_weight(qw, rec, fq, "k"), ge))
-    flops = 2.0 * m * K * N
-    if bwd:
-        dy = W.normal_bf16(cid, W.T_DY1, (m, N), std=2.0 ** -10)
-        qd = OQ.quantize_act(dy, rec, fg, ge, rowwise=True, colwise=True, dl_scale=dl)
-        D = OG.deq_act_rows(qd["row_codes"], sc(qd, "row_scales"), rec, fg)
-        dA = OG.round_bf16(OG.grouped_dgrad(D, OG.deq_weight(qw, rec, fq, "n"), ge))
-        P = qa["padded_starts"]
-        At = OG.unpad_cols(OG.deq_act_cols(qa["col_codes"], sc(qa, "col_scales"), rec, fq), P, ge)
-        Dt = OG.unpad_cols(OG.deq_act_cols(qd["col_codes"], sc(qd, "col_scales"), rec, fg), P, ge)
-        dW = OG.round_f32(OG.grouped_wgrad(At, Dt, ge, 1))
-        flops *= 3
-    dt = time.perf_counter() - t0
+
+    def sc(q, key):
+        return (q[key], q["tensor_scale"]) if rec == "nvfp4" else q[key]
+    # synthetic operands of the sampled shapes (drawn once, outside the timing)
+    mmax = min(rows, int(sizes.max()))
+    a_all = W.normal_bf16(cid, W.T_X, (mmax, K))
+    w = W.normal_bf16(cid, W.T_W1, (1, K, N), std=0.02, chunk_rows=256)
+    dy_all = W.normal_bf16(cid, W.T_DY1, (mmax, N), std=2.0 ** -10) if bwd else None
+    flops, dt, done, total_rows = 0.0, 0.0, [], 0
+    for e in experts:
+        m = min(rows, int(sizes[e]))
+        a = a_all[:m]
+        ge = np.array([m], np.int32)
+        t0 = time.perf_counter()
+        qa = OQ.quantize_act(a, rec, fq, ge, rowwise=True, colwise=bwd, dl_scale=dl)
+        qw = OQ.quantize_weight(w, rec, fq, dl_scale=(np.ones(1, np.float32), np.ones(1, np.float32)))
+        A = OG.deq_act_rows(qa["row_codes"], sc(qa, "row_scales"), rec, fq)
+        OG.round_bf16(OG.grouped_fwd(A, OG.deq_weight(qw, rec, fq, "k"), ge))
+        f = 2.0 * m * K * N
+        if bwd:
+            qd = OQ.quantize_act(dy_all[:m], rec, fg, ge, rowwise=True, colwise=True, dl_scale=dl)
+            D = OG.deq_act_rows(qd["row_codes"], sc(qd, "row_scales"), rec, fg)
+            OG.round_bf16(OG.grouped_dgrad(D, OG.deq_weight(qw, rec, fq, "n"), ge))
+            P = qa["padded_starts"]
+            At = OG.unpad_cols(OG.deq_act_cols(qa["col_codes"], sc(qa, "col_scales"), rec, fq), P, ge)
+            Dt = OG.unpad_cols(OG.deq_act_cols(qd["col_codes"], sc(qd, "col_scales"), rec, fg), P, ge)
+            OG.round_f32(OG.grouped_wgrad(At, Dt, ge, 1))
+            f *= 3
+        dt += time.perf_counter() - t0
+        flops += f
+        done.append(e)
+        total_rows += m
+        if dt >= min_seconds:
+            break
     mode = "fwd+dgrad+wgrad" if bwd else "fwd"
+    which = f"expert {done[0]}" if len(done) == 1 else f"experts {done[0]}-{done[-1]} ({len(done)})"
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "cpu_model": cpu_model(),
-            "sample": f"expert {e} gate/up GEMM, {m} routed rows x K={K} x N={N}, {mode}, "
+            "sample": f"{which} gate/up GEMM, {total_rows} routed rows (at most {rows} per expert, "
+                      f"synthetic operands of those shapes) x K={K} x N={N}, {mode}, "
                       f"oracle quantization + float64 GEMMs, {dt:.1f} s"}
 
 
