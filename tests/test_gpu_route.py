@@ -57,6 +57,20 @@ def test_repeated_and_invalid_ids():
     _check(ids, 6, expect_bad=True)
 
 
+def test_split_passes_with_invalid_ids():
+    """Enough entries that each expert's rows are written by several
+    workgroups (one per run of chunks), with invalid ids in several runs and
+    an expert whose entries all sit in one run."""
+    rng = np.random.default_rng(21)
+    T, k, E = 20000, 4, 6
+    ids = rng.integers(0, E - 1, size=(T, k))
+    ids[12000:12100, 0] = E - 1                  # expert E-1: one run of entries only
+    for t in (3, 4500, 9100, 15000, 19999):      # invalid ids spread over the runs
+        ids[t, t % k] = -7 if t % 2 else E + 3
+    print(f"route split: T={T} k={k} E={E}", flush=True)
+    _check(ids, E, expect_bad=True)
+
+
 def test_large_random():
     rng = np.random.default_rng(9)
     T, k, E = 131072, 8, 256
