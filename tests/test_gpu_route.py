@@ -21,11 +21,19 @@ def _api():
     return api
 
 
-def _check(ids, E, expect_bad=False):
+def _check(ids, E, expect_bad=False, offset_rows=0):
+    """offset_rows > 0: the ids are a view that starts that many rows into a
+    larger device array (not 16-byte aligned when rows * k * 4 is not)."""
     api = _api()
     ids = np.ascontiguousarray(ids, np.int32)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    r = api.route(to_dev(ids), E, slot_row=True, status=status)
+    if offset_rows:
+        pad = np.zeros((offset_rows, ids.shape[1]), np.int32)
+        dev = to_dev(np.concatenate([pad, ids]))[offset_rows:]
+        assert dev.is_contiguous()
+    else:
+        dev = to_dev(ids)
+    r = api.route(dev, E, slot_row=True, status=status)
     ref = OR.route(ids, E)
     assert np.array_equal(host(r.group_ends).astype(np.int64), ref["group_ends"]), "group ends"
     assert np.array_equal(host(r.row_index).astype(np.int64), ref["row_index"]), "row order"
@@ -69,6 +77,16 @@ def test_split_passes_with_invalid_ids():
         ids[t, t % k] = -7 if t % 2 else E + 3
     print(f"route split: T={T} k={k} E={E}", flush=True)
     _check(ids, E, expect_bad=True)
+
+
+@pytest.mark.parametrize("offset_rows", [1, 3])
+def test_unaligned_ids(offset_rows):
+    """Ids that do not start on a 16-byte boundary (a view one or three rows
+    of three choices into a larger array) take the one-entry-at-a-time count."""
+    rng = np.random.default_rng(30 + offset_rows)
+    ids = rng.integers(0, 5, size=(11111, 3))
+    ids[77, 2] = -1
+    _check(ids, 5, expect_bad=True, offset_rows=offset_rows)
 
 
 def test_large_random():
