@@ -182,7 +182,17 @@ __device__ __forceinline__ int bswz(int row, int ch) { return row * GBK + (bswz_
 // lane L of the wave lands at lds + 16 L (or 4 L); M0 holds the LDS byte
 // address.
 // Issued through inline asm, so the compiler inserts no waits for them: the
-// main loop counts them itself (vmcnt) before each stage's barrier.
+// main loop counts them itself (vmcnt) before each stage's barrier. Nor does
+// it pad the wait states the ISA requires before a vector-memory read of an
+// SGPR (5 after a VALU write of it, such as the v_readlane that reloads a
+// spilled SGPR; 1 after an SALU write of M0). So each copy pads its own: the
+// buffer copies read their soffset through an SALU copy made inside the asm
+// (an SALU read of a VALU-written SGPR is interlocked), which also puts one
+// instruction between the M0 write and the copy, and the per-lane-address
+// copies start with s_nop 0. A spilled buffer resource is not covered this
+// way; the build checks the device assembly for it (asmcheck.py). A
+// timing build whose extra stores moved a v_readlane reload of the soffset
+// right before an unpadded copy lost whole stages of MX operands.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
@@ -204,16 +214,19 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t num_recor
   return r;
 }
 __device__ __forceinline__ void bdma16(rsrc_t rs, uint32_t voff, uint32_t soff, uint8_t *lds) {
-  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rs), "s"(soff), "{m0}"(lds_addr(lds)));
+  uint32_t t;
+  asm volatile("s_mov_b32 %0, %3\n\tbuffer_load_dwordx4 %1, %2, %0 offen lds"
+               : "=&s"(t)
+               : "v"(voff), "s"(rs), "s"(soff), "{m0}"(lds_addr(lds)));
 }
 // The NVFP4 kernel, at its register limit, keeps per-lane 64-bit addresses
 // (global_load_lds_dwordx4): four more SGPRs of buffer resources made the
 // compiler spill them.
 __device__ __forceinline__ void dma16(const uint8_t *src, uint8_t *lds) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_addr(lds)));
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_addr(lds)));
 }
 __device__ __forceinline__ void dma4(const void *src, void *lds) {
-  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds_addr(lds)));
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds_addr(lds)));
 }
 
 // MFMA 32x32x64 f8 operand for one lane: the lane's row, and (measured lane
@@ -719,7 +732,10 @@ __device__ __forceinline__ int64_t uni64(int64_t v) {
                    (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u));
 }
 __device__ __forceinline__ void bdma4(rsrc_t rs, uint32_t voff, uint32_t soff, void *lds) {
-  asm volatile("buffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rs), "s"(soff), "{m0}"(lds_addr(lds)));
+  uint32_t t;  // the soffset through an SALU copy, as in bdma16
+  asm volatile("s_mov_b32 %0, %3\n\tbuffer_load_dword %1, %2, %0 offen lds"
+               : "=&s"(t)
+               : "v"(voff), "s"(rs), "s"(soff), "{m0}"(lds_addr(lds)));
 }
 __device__ __forceinline__ uint32_t clamp_u32(int64_t v) {
   return v <= 0 ? 0u : (v >= (int64_t)0xFFFFFFFF ? 0xFFFFFFFFu : (uint32_t)v);

@@ -1,0 +1,119 @@
+"""The wait-state check over the GEMM kernels' inline-asm LDS copies.
+
+Each case is a hand-written gfx950 assembly fragment with a known answer
+from the ISA's wait-state rules: 5 wait states between a VALU write of an
+SGPR and a vector-memory read of it, 1 between an SALU write of M0 and an
+LDS DMA; ``s_nop N`` is N+1 wait states, any other instruction one.
+"""
+import textwrap
+
+from mx_scaled_grouped_amd import asmcheck
+
+COPY = "buffer_load_dwordx4 v2, s[60:63], s13 offen lds"
+
+
+def _fn(*lines, name="_ZN4test6kernelEv"):
+    body = "\n".join("\t" + x if not x.endswith(":") else x for x in lines)
+    return f"{name}:\n{body}\n.Lfunc_end0:\n"
+
+
+def _found(*lines):
+    return asmcheck.check_text(_fn(*lines))
+
+
+def test_reload_right_before_copy():
+    f = _found("v_readlane_b32 s13, v213, 11", COPY)
+    assert [(x.reg, x.distance, x.needed) for x in f] == [("s13", 0, 5)]
+    assert "v_readlane_b32 s13" in str(f[0])
+
+
+def test_wait_states_count_instructions_and_nops():
+    filler = ["v_mov_b32_e32 v9, v8"] * 4
+    assert [x.distance for x in _found("v_readlane_b32 s13, v1, 0", *filler, COPY)] == [4]
+    assert _found("v_readlane_b32 s13, v1, 0", *filler, "v_mov_b32_e32 v9, v8", COPY) == []
+    assert _found("v_readlane_b32 s13, v1, 0", "s_nop 4", COPY) == []
+    assert [x.distance for x in _found("v_readlane_b32 s13, v1, 0", "s_nop 3", COPY)] == [4]
+
+
+def test_buffer_resource_range_and_vop3_forms():
+    # a write of one register inside s[60:63]
+    assert [x.reg for x in _found("v_readfirstlane_b32 s61, v0", COPY)] == ["s61"]
+    # an SGPR source of a VOP3 op is read, not written
+    assert _found("v_add_u32_e64 v1, s13, v2", COPY) == []
+    # the carry-out of a VOP3b add is written
+    assert [x.reg for x in _found("v_add_co_u32_e64 v1, s[12:13], v2, v3", COPY)] == ["s13"]
+    # a VOP3 compare writes its SGPR pair
+    assert [x.reg for x in _found("v_cmp_gt_u32_e64 s[62:63], v1, v2", COPY)] == ["s62"]
+
+
+def test_m0_written_by_salu():
+    dma = "global_load_lds_dwordx4 v[2:3], off"
+    assert [(x.reg, x.distance, x.needed) for x in _found("s_mov_b32 m0, s5", dma)] == [("m0", 0, 1)]
+    assert _found("s_mov_b32 m0, s5", "s_nop 0", dma) == []
+    # the padded form the helpers emit: the soffset copy separates M0 from the copy
+    assert _found("s_mov_b32 m0, s78", "s_mov_b32 s14, s75", "buffer_load_dwordx4 v2, s[48:51], s14 offen lds") == []
+    # a VALU write of M0 needs the full 5
+    assert [x.distance for x in _found("v_readfirstlane_b32 m0, v7", "s_nop 2", dma)] == [3]
+
+
+def test_salu_copy_of_a_reloaded_soffset():
+    # the reload feeds an SALU copy (interlocked); the copy reads the SALU result
+    assert _found("v_readlane_b32 s75, v213, 3", "s_mov_b32 m0, s78", "s_mov_b32 s14, s75",
+                  "buffer_load_dwordx4 v2, s[48:51], s14 offen lds") == []
+    # an SALU write supersedes an earlier VALU write of the same register
+    assert _found("v_readlane_b32 s13, v1, 0", "s_mov_b32 s13, s5", COPY) == []
+
+
+def test_paths_through_branches():
+    text = _fn(
+        "v_readlane_b32 s13, v1, 0",
+        "s_branch .LBB0_2",
+        ".LBB0_1:",
+        "s_nop 7",
+        ".LBB0_2:",
+        COPY,
+    )
+    f = asmcheck.check_text(text)
+    # reached from the branch (1 wait state for the branch itself); the
+    # fall-through path from .LBB0_1 is clean
+    assert [(x.reg, x.distance) for x in f] == [("s13", 1)]
+    # a loop whose back edge carries the write
+    loop = _fn(
+        ".LBB0_3:",
+        "s_nop 1",
+        COPY,
+        "v_add_co_u32_e64 v4, s[12:13], v4, 1",
+        "s_cbranch_vccnz .LBB0_3",
+    )
+    # s_nop 1 (2) plus the branch (1)
+    assert [(x.reg, x.distance) for x in asmcheck.check_text(loop)] == [("s13", 3)]
+    # a function start has no predecessor
+    assert _found(COPY) == []
+
+
+def test_functions_are_checked_separately():
+    text = _fn("v_readlane_b32 s13, v1, 0", name="_Z1av") + _fn(COPY, name="_Z1bv")
+    assert asmcheck.check_text(text) == []
+    text = _fn("s_endpgm", name="_Z1av") + _fn("v_readlane_b32 s13, v1, 0", COPY, name="_Z1bv")
+    assert [x.kernel for x in asmcheck.check_text(text)] == ["_Z1bv"]
+
+
+def test_compiler_output_shape():
+    # the form clang prints: tab-indented, asm markers, comments, directives
+    text = textwrap.dedent("""\
+        \t.text
+        _ZN4mxsg1kEv:
+        \t.cfi_startproc
+        \ts_mov_b32 m0, s29
+        \tv_readlane_b32 s12, v213, 22      ; spill reload
+        \tv_readlane_b32 s13, v213, 11
+        \t;;#ASMSTART
+        \tbuffer_load_dwordx4 v2, s[60:63], s13 offen lds
+        \t;;#ASMEND
+        \ts_endpgm
+        .Lfunc_end0:
+        \t.size _ZN4mxsg1kEv, .Lfunc_end0-_ZN4mxsg1kEv
+        """)
+    f = asmcheck.check_text(text)
+    assert [(x.reg, x.distance) for x in f] == [("s13", 0)]
+    assert asmcheck.main([]) == 0
