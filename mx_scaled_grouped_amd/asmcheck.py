@@ -1,4 +1,8 @@
-"""Wait-state check of the inline-asm direct-to-LDS copies in device assembly.
+"""Wait-state checks on the GEMM kernels' device assembly.
+
+Two rules the compiler cannot be left to keep, checked on the built code:
+the wait states before the inline-asm direct-to-LDS copies (below), and the
+distance between an MFMA and a non-MFMA read of its result (further down).
 
 The GEMM kernels issue their global->LDS copies (``buffer_load_* ... lds``,
 ``global_load_lds_*``) through inline asm, so that the compiler inserts no
@@ -187,10 +191,127 @@ def check_function(name: str, lines) -> list:
     return findings
 
 
+# ---- reads of MFMA results -------------------------------------------------
+#
+# The compiler's own wait states after v_mfma_scale were seen to be too few
+# for a VALU or LDS read of the result (stale values), so the kernels keep a
+# stricter rule of their own: a non-MFMA instruction reads an MFMA's
+# destination only after at least two further MFMAs have issued (each of
+# them occupies the matrix pipe for its full latency) or after MFMA_READ_WAIT
+# wait states (explicit s_nop padding). This part checks that rule on the
+# built code, along every path, as for the copies above.
+
+MFMA_READ_WAIT = 40
+MFMA_BEHIND = 2
+
+
+def vregs(tok: str) -> set:
+    """VGPR/AGPR names in one operand token: v7, v[4:7], a3, a[0:15]."""
+    tok = tok.strip().rstrip(",")
+    m = re.fullmatch(r"([va])\[(\d+):(\d+)\]", tok)
+    if m:
+        return {f"{m.group(1)}{k}" for k in range(int(m.group(2)), int(m.group(3)) + 1)}
+    if re.fullmatch(r"[va]\d+", tok):
+        return {tok}
+    return set()
+
+
+_STORE = re.compile(r"^(ds_write|ds_store|global_store|buffer_store|flat_store|scratch_store|global_atomic|buffer_atomic|ds_add|ds_max|ds_min)")
+
+
+def vector_reads(ins: str) -> set:
+    """VGPRs/AGPRs an instruction reads (its sources; all operands of a store or LDS copy)."""
+    op = ins.split(None, 1)[0]
+    ops = operands(ins)
+    if op.startswith("s_") or not ops:
+        return set()
+    first = 0 if (_STORE.match(op) or is_lds_copy(ins)) else 1
+    if _VOP3B.match(op):
+        first = 2
+    out = set()
+    for o in ops[first:]:
+        for w in o.split():
+            out |= vregs(w)
+    return out
+
+
+def vector_writes(ins: str) -> set:
+    """VGPRs/AGPRs a non-store instruction writes (its first operand)."""
+    op = ins.split(None, 1)[0]
+    ops = operands(ins)
+    if op.startswith("s_") or not ops or _STORE.match(op) or is_lds_copy(ins):
+        return set()
+    return vregs(ops[0].split()[0])
+
+
+def mfma_dest(ins: str) -> set:
+    if not ins.startswith("v_mfma"):
+        return set()
+    ops = operands(ins)
+    return vregs(ops[0].split()[0]) if ops else set()
+
+
+def check_mfma_reads(name: str, lines) -> list:
+    body = _body(lines)
+    written = set()
+    for k, v in body:
+        if k == "I":
+            written |= mfma_dest(v)
+    if not written:
+        return []
+    label_at = {v: i for i, (k, v) in enumerate(body) if k == "L"}
+    jumps = {}
+    for i, (k, v) in enumerate(body):
+        if k == "I":
+            m = _BRANCH.match(v)
+            if m and m.group(2) in label_at:
+                jumps.setdefault(m.group(2), []).append(i)
+    findings = []
+
+    def walk(pos, reader, reads, dist, behind, seen):
+        i = pos - 1
+        while i >= 0:
+            k, v = body[i]
+            if k == "L":
+                for j in jumps.get(v, ()):
+                    if (j, dist, behind) not in seen:
+                        seen.add((j, dist, behind))
+                        walk(j, reader, reads, dist + 1, behind, seen)
+                if i > 0 and body[i - 1][0] == "I" and _NO_FALLTHROUGH.match(body[i - 1][1]):
+                    return
+                i -= 1
+                continue
+            if dist >= MFMA_READ_WAIT:
+                return
+            if v.startswith("v_mfma"):
+                hit = mfma_dest(v) & reads
+                if hit:
+                    findings.append(Finding(name, reader, v, sorted(hit)[0], dist, MFMA_READ_WAIT))
+                    return
+                behind += 1
+                if behind >= MFMA_BEHIND:
+                    return
+            else:
+                reads = reads - vector_writes(v)  # the read sees this later write
+                if not reads:
+                    return
+            dist += wait_states(v)
+            i -= 1
+
+    for i, (k, v) in enumerate(body):
+        if k != "I" or v.startswith("v_mfma"):
+            continue
+        reads = vector_reads(v) & written
+        if reads:
+            walk(i, v, reads, 0, 0, set())
+    return findings
+
+
 def check_text(text: str) -> list:
     out = []
     for name, lines in split_kernels(text):
         out.extend(check_function(name, lines))
+        out.extend(check_mfma_reads(name, lines))
     return out
 
 

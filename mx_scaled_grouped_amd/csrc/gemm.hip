@@ -1155,13 +1155,28 @@ __global__ __launch_bounds__(512) void blockwise_gemm_kernel(GemmArgs a) {
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
-  // column 7 of a tile's last block and its last promotions
+  // column 7 of a tile's last block (events 0-3 without the next block's
+  // reads) and the last promotions: column 6 rows 2-3, column 7. Out of the
+  // event order, where the compiler (most of all in the accumulating
+  // instance, at its register limit) hoisted promotions above the next MFMA
+  // and sank MFMAs into the epilogue, each read of a partial here is behind
+  // 40 explicit wait states: the partials pass through the padding asm, so
+  // that no promotion (register-only work, which a memory clobber does not
+  // order) moves above it and no MFMA below it.
   auto finish_tile = [&]() __attribute__((always_inline)) {
-    event(std::integral_constant<int, 0>{}, 0, std::false_type{}, std::false_type{});
-    event(std::integral_constant<int, 1>{}, 0, std::false_type{}, std::false_type{});
-    event(std::integral_constant<int, 2>{}, 0, std::false_type{}, std::false_type{});
-    event(std::integral_constant<int, 3>{}, 0, std::false_type{}, std::false_type{});
-    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" ::: "memory");
+    p[0] = mma(bfY, af[0]);
+    p[1] = mma(bfY, af[1]);
+    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7"
+                 : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3])::"memory");
+    __builtin_amdgcn_sched_barrier(0);
+    promote(acc[2][6], p[2], fo[2], sbX);
+    promote(acc[3][6], p[3], fo[3], sbX);
+    promote(acc[0][7], p[0], fo[0], sbY);
+    promote(acc[1][7], p[1], fo[1], sbY);
+    __builtin_amdgcn_sched_barrier(0);
+    p[2] = mma(bfY, af[2]);
+    p[3] = mma(bfY, af[3]);
+    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" : "+v"(p[2]), "+v"(p[3])::"memory");
     __builtin_amdgcn_sched_barrier(0);
     promote(acc[2][7], p[2], fo[2], sbY);
     promote(acc[3][7], p[3], fo[3], sbY);
