@@ -148,18 +148,12 @@ __device__ bool locate_row_tile(const GemmArgs &a, int slot, int &g_out, int64_t
   return s_found != 0;
 }
 
-// Read-only copy sources for the stages past a tile's contraction (the ring
-// runs in whole turns): zero blockwise scales and NVFP4 block codes, and
-// E8M0 words of four unit scales (codes read zeros through an empty buffer
-// resource). Reading them keeps every stage's copy count the same, so no
-// wait depends on the stage.
-#define MXSG_U7F4 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu
-#define MXSG_U7F16 MXSG_U7F4, MXSG_U7F4, MXSG_U7F4, MXSG_U7F4
+// Read-only copy source for the stages past a tile's contraction (the ring
+// runs in whole turns): zero blockwise scales and NVFP4 block codes (the
+// buffer copies, codes and MX scale words, read zeros through an empty
+// resource on it instead). Reading it keeps every stage's copy count the
+// same, so no wait depends on the stage.
 __device__ __attribute__((aligned(1024))) const uint32_t kZeroSrc[256] = {};
-__device__ __attribute__((aligned(256))) const uint32_t kUnitScaleSrc[64] = {MXSG_U7F16, MXSG_U7F16, MXSG_U7F16,
-                                                                           MXSG_U7F16};
-#undef MXSG_U7F16
-#undef MXSG_U7F4
 
 // LDS stage tiles hold rows of GBK = 64 code bytes as four 16-byte chunks;
 // chunk c of row r sits at chunk c ^ ((r >> 2) & 3), so the lanes of a
@@ -216,6 +210,12 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t num_recor
 __device__ __forceinline__ void bdma16(rsrc_t rs, uint32_t voff, uint32_t soff, uint8_t *lds) {
   uint32_t t;
   asm volatile("s_mov_b32 %0, %3\n\tbuffer_load_dwordx4 %1, %2, %0 offen lds"
+               : "=&s"(t)
+               : "v"(voff), "s"(rs), "s"(soff), "{m0}"(lds_addr(lds)));
+}
+__device__ __forceinline__ void bdma4(rsrc_t rs, uint32_t voff, uint32_t soff, void *lds) {
+  uint32_t t;  // the soffset through an SALU copy, as in bdma16
+  asm volatile("s_mov_b32 %0, %3\n\tbuffer_load_dword %1, %2, %0 offen lds"
                : "=&s"(t)
                : "v"(voff), "s"(rs), "s"(soff), "{m0}"(lds_addr(lds)));
 }
@@ -378,24 +378,31 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
   // rows, then word w + 1), so the words of one stage for a run of rows are
   // contiguous: a wave's copy reads four 64-byte runs. The word of stage kt
   // holds the 32-blocks 4w .. 4w+3 with w = l0/128 + (kt * EPB) / 2.
-  const uint8_t *mxa = nullptr, *mxb = nullptr;
-  int64_t mxa_word = 0, mxb_word = 0;  // bytes from one word of a matrix to the next
+  // They are buffer copies like the code chunks: a resource from the tile's
+  // first word, the row's byte offset per lane, the stage's word offset in
+  // an SGPR (no per-lane 64-bit address, and the stage past the contraction
+  // is a scalar select of the empty resource, so the ring turn has no branch).
+  rsrc_t rsMA = rsZ, rsMB = rsZ;
+  uint32_t maoff = 0, mboff = 0, ma_word = 0, mb_word = 0;  // bytes from one word of a matrix to the next
   if (MX) {
     const int d = wave * 64 + lane;
     const int r = (d >> 7) * 128 + (d & 3) * 32 + ((d >> 2) & 31);
-    mxa_word = (MODE == kWgrad ? a.I : a.M) * 4;
-    mxb_word = a.J * 4;
-    mxa = reinterpret_cast<const uint8_t *>(a.a_scales) + (l0 / 128) * mxa_word + arow(r) * 4;
-    if (b_wave)
-      mxb = reinterpret_cast<const uint8_t *>(a.b_scales) + (MODE == kWgrad ? 0 : (int64_t)g * a.bs_gstride) +
-            (l0 / 128) * mxb_word + brow(r) * 4;
+    ma_word = (uint32_t)((MODE == kWgrad ? a.I : a.M) * 4);
+    mb_word = (uint32_t)(a.J * 4);
+    rsMA = make_rsrc(reinterpret_cast<const uint8_t *>(a.a_scales) + (l0 / 128) * (int64_t)ma_word, 0xFFFFFFFFu);
+    maoff = (uint32_t)(arow(r) * 4);
+    if (b_wave) {
+      rsMB = make_rsrc(reinterpret_cast<const uint8_t *>(a.b_scales) +
+                           (MODE == kWgrad ? 0 : (int64_t)g * a.bs_gstride) + (l0 / 128) * (int64_t)mb_word,
+                       0xFFFFFFFFu);
+      mboff = (uint32_t)(brow(r) * 4);
+    }
   }
   // vector-memory instructions every wave issues per stage (the waits count
   // them): MX scale words first (a filler copy into dmy where the wave has
   // no B-side scale row), then the A and B code chunks
   constexpr int NSC = MX ? 2 : 0;
   constexpr int OPS = NSC + AQ + BQ;
-  const uint32_t *usrc = kUnitScaleSrc + lane;
 
   v16f acc[MI][NI];
 #pragma unroll
@@ -406,18 +413,19 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
 
   // copy C (0 <= C < OPS) of stage kt into the stage buffers; a stage past
-  // the contraction copies zeros (unit E8M0 scales), so the MFMAs of the
-  // padding stages of the last ring turn add nothing. No branches.
+  // the contraction copies zero codes (and MX: zero E8M0 words, 2^-127, a
+  // finite factor of those zeros), so the MFMAs of the padding stages of the
+  // last ring turn add exactly nothing. No branches: the empty resource is a
+  // scalar select.
   auto copy = [&](auto c, int kt, uint8_t *as, uint8_t *bs, uint32_t *ma, uint32_t *mb) {
     constexpr int C = decltype(c)::value;
     const bool real = kt < nsteps;
     if constexpr (C < NSC) {  // MX: the E8M0 word holding this stage's 32-blocks
-      const int64_t w = (kt * EPB) >> 1;
+      const uint32_t w = (uint32_t)(kt * EPB) >> 1;
       if constexpr (C == 0)
-        dma4(real ? (const void *)(mxa + w * mxa_word) : (const void *)usrc, ma + wave * 64);
+        bdma4(real ? rsMA : rsZ, maoff, w * ma_word, ma + wave * 64);
       else
-        dma4(real && b_wave ? (const void *)(mxb + w * mxb_word) : (const void *)usrc,
-             b_wave ? mb + wave * 64 : dmy);
+        bdma4(real && b_wave ? rsMB : rsZ, mboff, w * mb_word, b_wave ? mb + wave * 64 : dmy);
     } else if constexpr (C < NSC + AQ) {
       constexpr int q = C - NSC;
       bdma16(real ? rsA : rsZ, aoff[q], (uint32_t)kt * 128u, as + (wave * AQ + q) * 1024);
@@ -730,12 +738,6 @@ __device__ __forceinline__ int64_t uni64(int64_t v) {
   const uint64_t u = (uint64_t)v;
   return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(u >> 32)) << 32) |
                    (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u));
-}
-__device__ __forceinline__ void bdma4(rsrc_t rs, uint32_t voff, uint32_t soff, void *lds) {
-  uint32_t t;  // the soffset through an SALU copy, as in bdma16
-  asm volatile("s_mov_b32 %0, %3\n\tbuffer_load_dword %1, %2, %0 offen lds"
-               : "=&s"(t)
-               : "v"(voff), "s"(rs), "s"(soff), "{m0}"(lds_addr(lds)));
 }
 __device__ __forceinline__ uint32_t clamp_u32(int64_t v) {
   return v <= 0 ? 0u : (v >= (int64_t)0xFFFFFFFF ? 0xFFFFFFFFu : (uint32_t)v);
