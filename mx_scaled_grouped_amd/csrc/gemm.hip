@@ -184,9 +184,10 @@ __device__ __forceinline__ int bswz(int row, int ch) { return row * GBK + (bswz_
 // (an SALU read of a VALU-written SGPR is interlocked), which also puts one
 // instruction between the M0 write and the copy, and the per-lane-address
 // copies start with s_nop 0. A spilled buffer resource is not covered this
-// way; the build checks the device assembly for it (asmcheck.py). A
-// timing build whose extra stores moved a v_readlane reload of the soffset
-// right before an unpadded copy lost whole stages of MX operands.
+// way; the build checks the device assembly for it (asmcheck.py). Without
+// the padding, a few unrelated extra global stores in the kernel were
+// enough to move a v_readlane reload of the soffset right before a copy,
+// which then loaded whole stages of MX operands from a stale offset.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
